@@ -1,0 +1,393 @@
+"""Float64 CPU oracle for scored decode attention, its block side-car and
+heavy-hitter block selection.
+
+TEST INFRASTRUCTURE ONLY. This module is the checker, not the product: only
+``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import it. The HIP library never calls it, and it imports
+nothing from the HIP package (inputs are handed in as numpy arrays).
+
+Everything is computed in float64 with plain numpy, one definition per step,
+in the order the source pages state them:
+
+* Context Optimization (Flash-MoE docs), "FP8 KV Cache / How It Works":
+  E4M3 with 1 sign, 4 exponent and 3 mantissa bits, bias 7, range +-448; a
+  per-position scale ``absmax / 240``; values clipped and quantised to 8 bits;
+  the scale is kept next to the codes.
+* Context Optimization, "Sliding Window Attention / Design": the write slot of
+  a circular cache is ``position mod capacity``.
+* LLM mechanics III (four-slot cache), sections 1, 3 and 5: position ``i``
+  reads ``i-w+1 .. i`` clipped at 0, the current token included; masking is by
+  absolute position, never by slot; processed count, absolute positions and
+  slots are three separate indices.
+* Context views at marginal cost, section 2 (Tier 0 and Tier 1): the
+  post-softmax weights are reduced per span with one add per (row, span); the
+  side-car keeps Attended (this turn), EMA, Cumulative and a 64-turn trajectory
+  ring, O(1) per span per turn.
+* Per-Head Attention as a Scoring Signal, "Scoring granularity, not eviction
+  granularity": the unit that is scored and kept is a (sequence, 16-token
+  block); heads are only a scoring input.
+* Context Optimization, "H2O KV Cache Eviction": post-softmax scores are summed
+  over all query heads (GQA-aware) and over steps; sinks and recent tokens are
+  kept unconditionally and the top scorers among the rest survive.
+
+Readings taken where the pages are silent (each is listed, with its reason, in
+the design notes of the repository): softmax scale ``f32(1/sqrt(d))``; query
+head ``h`` reads KV head ``h // (Hq/Hkv)``; masses are summed over heads and
+over scored layers; a block is ``position // 16``; ``EMA <- a*A + (1-a)*EMA``
+from zero; selection keys are (score descending, block index ascending); the
+recent region is every block that meets the last ``R`` tokens; blocks not yet
+written are never marked evicted.
+
+Parity pins: every function here is checked in ``tests/test_oracle_*.py``
+against facts the pages or mathematics fix (format tables, closed forms,
+brute force, an independent float64 attention, and the pages' printed sizes).
+Nothing in this file is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import itertools
+import math
+
+import numpy as np
+
+# Per-Head Attention as a Scoring Signal: "(sequence, token block) of 16 tokens".
+BLOCK_TOKENS = 16
+# Context views at marginal cost, section 2 Tier 1: "trajCap = 64 turns".
+TRAJ_CAP = 64
+# Context Optimization, FP8 KV Cache: bias 7, range [-448, 448], scale absmax/240.
+E4M3_BIAS = 7
+E4M3_MAX = 448.0
+FP8_SCALE_DIVISOR = 240.0
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 (Context Optimization, "FP8 KV Cache / How It Works")
+# ---------------------------------------------------------------------------
+
+def e4m3_to_float(code: int) -> float:
+    """Value of one E4M3 byte from the format definition: 1 sign bit, 4
+    exponent bits with bias 7, 3 mantissa bits. Exponent field 0 holds the
+    subnormals ``(m/8) * 2**(1-7)``; otherwise ``(1 + m/8) * 2**(e-7)``. The
+    pair exponent 15 / mantissa 7 is NaN (the range stops at 448, so there is no
+    infinity)."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return math.nan
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** (1 - E4M3_BIAS)
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - E4M3_BIAS)
+
+
+def e4m3_table() -> np.ndarray:
+    """All 256 decoded values (float64), NaN at 0x7F and 0xFF."""
+    return np.array([e4m3_to_float(c) for c in range(256)], dtype=np.float64)
+
+
+def e4m3_encode(y: np.ndarray) -> np.ndarray:
+    """Round values to the nearest E4M3 code, ties to even, after clipping to
+    +-448 (the pages clip before quantising). The sign is kept, so -0 gives
+    0x80. Inputs must be finite.
+
+    Step by step: clip |y| to 448; find its binade ``2**e`` (at least 2**-6,
+    the subnormal binade shares the quantum of the lowest normal binade); the
+    grid there has spacing ``2**(e-3)``; ``n = round_half_even(|y| / spacing)``
+    is in [0, 16]; the code is ``(e + 7) * 8 + n - 8``, which also covers the
+    subnormals (e = -6, n < 8 gives code n) and the carry into the next binade
+    (n = 16)."""
+    y = np.asarray(y, dtype=np.float64)
+    if not np.all(np.isfinite(y)):
+        raise ValueError("E4M3 encode: non-finite input is outside the contract")
+    sign = np.signbit(y)
+    a = np.minimum(np.abs(y), E4M3_MAX)
+    _, ex = np.frexp(a)                      # a = f * 2**ex, f in [0.5, 1)
+    e = np.maximum(ex.astype(np.int64) - 1, 1 - E4M3_BIAS)
+    spacing = np.ldexp(1.0, (e - 3).astype(np.int64))
+    n = np.rint(a / spacing)                 # exact division by a power of 2
+    code = (e + E4M3_BIAS) * 8 + n.astype(np.int64) - 8
+    code = np.where(a == 0.0, 0, code)
+    code = code | (sign.astype(np.int64) << 7)
+    return code.astype(np.uint8)
+
+
+def fp8_encode_rows(x: np.ndarray):
+    """Encode each row (one position's ``Hkv*d`` values of K or of V) with its
+    own scale: ``absmax = max|x|``, ``s = f32(absmax / 240)``,
+    ``code = E4M3(f32(x / s))``. A row of zeros gets ``s = 0`` and codes 0x00.
+
+    Division is done in float64 and rounded once to float32, which equals a
+    correctly rounded float32 division (53 >= 2*24 + 2). Returns
+    ``(codes uint8 [rows, n], scales float32 [rows])``."""
+    x = np.asarray(x)
+    if x.dtype != np.float32:
+        raise TypeError("fp8_encode_rows takes float32 rows (bf16 sources are widened exactly first)")
+    x2 = np.atleast_2d(x)
+    if not np.all(np.isfinite(x2)):
+        raise ValueError("FP8 encode: non-finite input is outside the contract")
+    absmax = np.max(np.abs(x2.astype(np.float64)), axis=1)
+    scales = (absmax / FP8_SCALE_DIVISOR).astype(np.float32)
+    codes = np.zeros(x2.shape, dtype=np.uint8)
+    nz = scales > 0
+    if np.any(nz):
+        y = (x2[nz].astype(np.float64) / scales[nz, None].astype(np.float64)).astype(np.float32)
+        codes[nz] = e4m3_encode(y.astype(np.float64))
+    return codes.reshape(x.shape), scales
+
+
+def fp8_decode_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """``value = E4M3(code) * scale`` in float64 (exact: a 4-bit significand
+    times a float32)."""
+    table = e4m3_table()
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    return table[codes] * scales.reshape(scales.shape + (1,) * (codes.ndim - scales.ndim))
+
+
+# ---------------------------------------------------------------------------
+# Which keys a query reads (LLM mechanics III, sections 1, 3, 5)
+# ---------------------------------------------------------------------------
+
+def ring_slot(position: int, capacity: int) -> int:
+    """Context Optimization, Sliding Window Attention: ``cache_pos = len % window_size``."""
+    return position % capacity
+
+
+def key_visible(p: int, i: int, window: int) -> bool:
+    """Absolute position ``p`` is visible to the query at absolute position ``i``
+    when ``p <= i`` and, for a window ``w >= 1``, ``p >= i - w + 1`` (clipped at
+    0 by ``p >= 0``). ``w == 0`` means unlimited."""
+    if window < 0:
+        raise ValueError("invalid window")
+    if p < 0 or p > i:
+        return False
+    return window == 0 or p >= i - window + 1
+
+
+def block_of(position: int) -> int:
+    """Per-Head Attention as a Scoring Signal: the unit is a 16-token block."""
+    return position // BLOCK_TOKENS
+
+
+def block_alive(alive, b: int) -> bool:
+    return True if alive is None else bool(alive[b])
+
+
+# ---------------------------------------------------------------------------
+# Attention with the post-softmax tap
+# ---------------------------------------------------------------------------
+
+def softmax_scale(d: int) -> float:
+    """Reading: the pages do not state the logit scale; the usual ``1/sqrt(d)``
+    is used, rounded once to float32 (the GPU receives the same float32)."""
+    return float(np.float32(1.0 / math.sqrt(d)))
+
+
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
+    """Explicit softmax attention for one decode query of one sequence.
+
+    ``q`` is ``[Hq, d]``; ``K`` and ``V`` are ``[Hkv, n, d]`` holding only the
+    visible keys. Query head ``h`` reads KV head ``h // (Hq // Hkv)``.
+    Returns ``(o [Hq, d], p [Hq, n])`` where ``p`` are the post-softmax weights
+    that the tap reduces."""
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    Hq, d = q.shape
+    Hkv, n, _ = K.shape
+    if Hq % Hkv:
+        raise ValueError("query heads must be a multiple of KV heads")
+    if n == 0:
+        raise ValueError("all-masked row: the query sees no key")
+    G = Hq // Hkv
+    o = np.zeros((Hq, d))
+    p = np.zeros((Hq, n))
+    for h in range(Hq):
+        g = h // G
+        s = (K[g] @ q[h]) * scale
+        e = np.exp(s - np.max(s))
+        p[h] = e / np.sum(e)
+        o[h] = p[h] @ V[g]
+    return o, p
+
+
+def block_mass(p: np.ndarray, positions: np.ndarray, n_blocks: int) -> np.ndarray:
+    """Tier 0 reduction: for every block ``b``, the sum over heads and over the
+    block's visible keys of the post-softmax weight (one add per row and span).
+    ``positions`` are the absolute positions of the columns of ``p``."""
+    p = np.asarray(p, dtype=np.float64)
+    blocks = np.asarray(positions, dtype=np.int64) // BLOCK_TOKENS
+    if blocks.size and (blocks.min() < 0 or blocks.max() >= n_blocks):
+        raise ValueError("block index out of range")
+    mass = np.zeros(n_blocks)
+    for h in range(p.shape[0]):
+        mass += np.bincount(blocks, weights=p[h], minlength=n_blocks)
+    return mass
+
+
+def attend_scored(q, K_all, V_all, positions, i, window, alive, scale, n_blocks):
+    """One (sequence, layer) of the scored decode step.
+
+    ``K_all`` / ``V_all`` are ``[Hkv, n, d]`` for candidate keys at absolute
+    ``positions`` (any order: a linear cache or the slots of a ring). A key is
+    read when it is visible (window rule) and its block is alive. Returns
+    ``(o [Hq, d], mass [n_blocks])`` with the mass summed over query heads."""
+    positions = np.asarray(positions, dtype=np.int64)
+    sel = np.array([key_visible(int(p), i, window) and block_alive(alive, block_of(int(p)))
+                    for p in positions], dtype=bool)
+    o, p = attend(q, np.asarray(K_all)[:, sel], np.asarray(V_all)[:, sel], scale)
+    return o, block_mass(p, positions[sel], n_blocks)
+
+
+# ---------------------------------------------------------------------------
+# Incremental ring cache versus the full masked reference (LLM mechanics III)
+# ---------------------------------------------------------------------------
+
+class RingCache:
+    """A bounded per-sequence cache with three separate indices: the processed
+    count ``next_position``, the absolute position held by each slot, and the
+    slot itself. Writes go to ``position mod capacity``; masking uses the held
+    absolute positions only."""
+
+    def __init__(self, n_kv_heads: int, d: int, capacity: int):
+        if capacity < 1:
+            raise ValueError("capacity must be positive")
+        self.capacity = capacity
+        self.K = np.zeros((n_kv_heads, capacity, d))
+        self.V = np.zeros((n_kv_heads, capacity, d))
+        self.pos_of_slot = np.full(capacity, -1, dtype=np.int64)
+        self.next_position = 0
+
+    def append(self, k: np.ndarray, v: np.ndarray):
+        """Append a chunk ``k, v [Hkv, n, d]`` at the next absolute positions."""
+        n = k.shape[1]
+        positions = np.arange(self.next_position, self.next_position + n)
+        for j, pos in enumerate(positions):
+            s = ring_slot(int(pos), self.capacity)
+            self.K[:, s] = k[:, j]
+            self.V[:, s] = v[:, j]
+            self.pos_of_slot[s] = pos
+        self.next_position += n          # eviction never resets the position
+        return positions
+
+    def attend(self, q, i, window, scale, n_blocks, alive=None, mask_by_slot=False):
+        """Attend the query at absolute position ``i`` over the held slots.
+        ``mask_by_slot=True`` is the deliberately wrong negative control that
+        treats slot indices as positions."""
+        held = self.pos_of_slot >= 0
+        pos = np.where(held, self.pos_of_slot, -1)
+        if mask_by_slot:
+            pos = np.where(held, np.arange(self.capacity), -1)
+        return attend_scored(q, self.K, self.V, pos, i, window, alive, scale, n_blocks)
+
+
+def full_masked_reference(q, K_hist, V_hist, i, window, scale, n_blocks, alive=None):
+    """The full reference: every position ``0..i`` of the history, with the
+    window applied as a mask by absolute position."""
+    n = i + 1
+    return attend_scored(q, K_hist[:, :n], V_hist[:, :n], np.arange(n), i, window, alive,
+                         scale, n_blocks)
+
+
+# ---------------------------------------------------------------------------
+# Side-car (Context views at marginal cost, section 2 Tier 1 and section 3)
+# ---------------------------------------------------------------------------
+
+class SideCar:
+    """Per-block state ``{Attended, EMA, Cumulative, traj[64]}``, all zero at
+    the start, updated once per turn (one decode step)."""
+
+    def __init__(self, n_blocks: int, traj_cap: int = TRAJ_CAP):
+        self.attended = np.zeros(n_blocks)
+        self.ema = np.zeros(n_blocks)
+        self.cum = np.zeros(n_blocks)
+        self.traj = np.zeros((traj_cap, n_blocks))
+        self.step = 0
+
+    def update(self, A: np.ndarray, alpha: float):
+        """Close the turn with this turn's mass ``A``: Attended = A;
+        EMA = alpha*A + (1-alpha)*EMA; Cumulative += A; the trajectory ring
+        slot ``step mod trajCap`` receives A; the turn counter advances."""
+        A = np.asarray(A, dtype=np.float64)
+        self.attended = A.copy()
+        self.ema = alpha * A + (1.0 - alpha) * self.ema
+        self.cum = self.cum + A
+        self.traj[self.step % self.traj.shape[0]] = A
+        self.step += 1
+
+
+# ---------------------------------------------------------------------------
+# Heavy-hitter block selection (Context Optimization, "H2O KV Cache Eviction")
+# ---------------------------------------------------------------------------
+
+def protected_blocks(i: int, recent_tokens: int, sink_tokens: int):
+    """Blocks kept unconditionally: every block meeting the last
+    ``recent_tokens`` positions ``[max(0, i-R+1), i]``, and every block meeting
+    the first ``sink_tokens`` positions."""
+    if recent_tokens < 1:
+        raise ValueError("recent_tokens must be at least 1 (the current token)")
+    if sink_tokens < 0:
+        raise ValueError("sink_tokens must be non-negative")
+    lo = max(0, i - recent_tokens + 1) // BLOCK_TOKENS
+    prot = set(range(lo, i // BLOCK_TOKENS + 1))
+    if sink_tokens > 0:
+        prot |= set(range(0, (min(sink_tokens, i + 1) - 1) // BLOCK_TOKENS + 1))
+    return prot
+
+
+def select_blocks(score, alive, i, budget_blocks, recent_tokens, sink_tokens=0):
+    """Keep = protected blocks, plus the ``budget_blocks`` highest-scoring
+    alive candidates among the other existing blocks ``b <= i // 16``, ordered
+    by score descending and then by block index ascending (lowest index wins a
+    tie). Returns the kept block ids in ascending order."""
+    if budget_blocks < 0:
+        raise ValueError("budget must be non-negative")
+    score = np.asarray(score)
+    n_exist = i // BLOCK_TOKENS + 1
+    prot = protected_blocks(i, recent_tokens, sink_tokens)
+    cand = [b for b in range(n_exist) if block_alive(alive, b) and b not in prot]
+    cand.sort(key=lambda b: (-float(score[b]), b))
+    keep = prot | set(cand[:budget_blocks])
+    return np.array(sorted(keep), dtype=np.int64)
+
+
+def select_blocks_bruteforce(score, alive, i, budget_blocks, recent_tokens, sink_tokens=0):
+    """Small-case check of ``select_blocks``: among all candidate subsets of the
+    allowed size, take the one whose scores, sorted descending, are largest
+    lexicographically, breaking equal score lists by the smallest sorted index
+    list. Exponential; tiny inputs only."""
+    score = np.asarray(score)
+    n_exist = i // BLOCK_TOKENS + 1
+    prot = protected_blocks(i, recent_tokens, sink_tokens)
+    cand = [b for b in range(n_exist) if block_alive(alive, b) and b not in prot]
+    k = min(budget_blocks, len(cand))
+    best = None
+    for sub in itertools.combinations(cand, k):
+        key = (tuple(sorted((-float(score[b]) for b in sub))), tuple(sorted(sub)))
+        if best is None or key < best[0]:
+            best = (key, sub)
+    return np.array(sorted(prot | set(best[1] if best else ())), dtype=np.int64)
+
+
+def keep_mask_after(keep_ids, i, n_blocks):
+    """Alive set for the next step in evict mode: the kept blocks, plus every
+    block not yet written (``b > i // 16``), which cannot have been evicted."""
+    alive = np.zeros(n_blocks, dtype=bool)
+    alive[np.asarray(keep_ids, dtype=np.int64)] = True
+    alive[i // BLOCK_TOKENS + 1:] = True
+    return alive
+
+
+# ---------------------------------------------------------------------------
+# KV memory sizes (Context Optimization, "Memory Budget Calculator")
+# ---------------------------------------------------------------------------
+
+def kv_cache_bytes(n_layers, n_kv_heads, head_dim, bytes_per_elem, positions,
+                   scale_bytes_per_position_per_cache=0):
+    """``layers x 2 (K+V) x kv_heads x head_dim x bytes x positions``, plus the
+    FP8 scale overhead of one scale per position per cache (K and V of each
+    layer)."""
+    elems = n_layers * 2 * n_kv_heads * head_dim * positions
+    return elems * bytes_per_elem + n_layers * 2 * positions * scale_bytes_per_position_per_cache
