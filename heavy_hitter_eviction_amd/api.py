@@ -1,0 +1,274 @@
+"""Thin ctypes binding of libkvs (include/kvs.h).
+
+Argument marshalling only: every computation runs in the library's HIP
+kernels. Tensors are torch device tensors; each call passes their
+``data_ptr()`` and ``torch.cuda.current_stream()`` to the C ABI and raises
+``KvsError`` on a non-zero status. Importing this module loads
+``libkvs.so`` and fails loudly if it has not been built
+(``python -m heavy_hitter_eviction_amd.build``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvs.so")
+
+KVS_OK, KVS_EINVAL, KVS_EDTYPE, KVS_EALIGN, KVS_EWS, KVS_EHIP, KVS_ENOTIMPL = 0, -1, -2, -3, -4, -5, -6
+KVS_F32, KVS_BF16, KVS_FP8_E4M3 = 0, 1, 2
+DTYPE_CODES = {"f32": KVS_F32, "bf16": KVS_BF16, "fp8": KVS_FP8_E4M3}
+TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+
+EXPORTED = (
+    "kvs_cache_bytes", "kvs_encode_fp8", "kvs_append_kv", "kvs_decode_workspace_bytes",
+    "kvs_decode_attn_scored", "kvs_update_sidecar", "kvs_select_blocks", "kvs_status_str",
+    "kvs_version",
+)
+
+
+class KvsError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        super().__init__(f"{call} failed: {status} ({status_str(status)})")
+        self.status = status
+
+
+class Geom(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("capacity", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("ring", ctypes.c_int32), ("n_blocks_max", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+        ("q_dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libkvs.so not built at {LIB_PATH}; run python -m heavy_hitter_eviction_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    G = ctypes.POINTER(Geom)
+    SZP = ctypes.POINTER(ctypes.c_size_t)
+    sig = {
+        "kvs_cache_bytes": [G, SZP, SZP, SZP],
+        "kvs_encode_fp8": [P, I32, I64, I32, P, P, P],
+        "kvs_append_kv": [G, P, P, I32, I32, P, P, P, P, P, P, P, P],
+        "kvs_decode_workspace_bytes": [G, SZP],
+        "kvs_decode_attn_scored": [G, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "kvs_update_sidecar": [P, P, P, P, P, I32, I32, I32, I64, F, P],
+        "kvs_select_blocks": [P, P, P, I32, I32, I32, I32, I32, P, P, P, P],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.kvs_status_str.argtypes = [ctypes.c_int]
+    lib.kvs_status_str.restype = ctypes.c_char_p
+    lib.kvs_version.argtypes = []
+    lib.kvs_version.restype = ctypes.c_char_p
+    return lib
+
+
+LIB = _load()
+
+
+def status_str(status: int) -> str:
+    return LIB.kvs_status_str(int(status)).decode()
+
+
+def version() -> str:
+    return LIB.kvs_version().decode()
+
+
+def _check(status: int, call: str):
+    if status != KVS_OK:
+        raise KvsError(status, call)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch tensor or None")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    if torch.cuda.is_available():
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return None
+
+
+def _device_check(*tensors):
+    for t in tensors:
+        if t is not None and t.device.type != "cuda":
+            raise ValueError("libkvs works on device tensors only")
+
+
+@dataclass(frozen=True)
+class CacheGeom:
+    """Python mirror of ``kvs_geom``."""
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    capacity: int
+    window: int = 0
+    ring: bool = False
+    n_blocks_max: int = 0
+    kv_dtype: str = "bf16"
+    q_dtype: str = "bf16"
+    softmax_scale: float = 0.0
+
+    def c(self) -> Geom:
+        nb = self.n_blocks_max or self.capacity // 16
+        scale = self.softmax_scale or float(torch.tensor(self.head_dim, dtype=torch.float64).rsqrt())
+        return Geom(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim, self.capacity,
+                    self.window, int(self.ring), nb, DTYPE_CODES[self.kv_dtype],
+                    DTYPE_CODES[self.q_dtype], scale)
+
+    @property
+    def nb(self) -> int:
+        return self.n_blocks_max or self.capacity // 16
+
+    @property
+    def words(self) -> int:
+        return (self.nb + 31) // 32
+
+
+def cache_bytes(geom: CacheGeom):
+    kv, sc, pos = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(LIB.kvs_cache_bytes(ctypes.byref(geom.c()), ctypes.byref(kv), ctypes.byref(sc),
+                               ctypes.byref(pos)), "kvs_cache_bytes")
+    return kv.value, sc.value, pos.value
+
+
+def decode_workspace_bytes(geom: CacheGeom) -> int:
+    n = ctypes.c_size_t()
+    _check(LIB.kvs_decode_workspace_bytes(ctypes.byref(geom.c()), ctypes.byref(n)),
+           "kvs_decode_workspace_bytes")
+    return n.value
+
+
+def encode_fp8(src: torch.Tensor, codes: torch.Tensor | None = None, scales: torch.Tensor | None = None,
+               stream=None):
+    """Per-row E4M3 encoding of ``src [rows, n]`` (float32 or bfloat16)."""
+    _device_check(src)
+    if src.dim() != 2:
+        raise ValueError("src must be [rows, row_len]")
+    rows, n = src.shape
+    dt = {torch.float32: KVS_F32, torch.bfloat16: KVS_BF16}.get(src.dtype)
+    if dt is None:
+        raise TypeError("src must be float32 or bfloat16")
+    if codes is None:
+        codes = torch.empty((rows, n), dtype=torch.uint8, device=src.device)
+    if scales is None:
+        scales = torch.empty((rows,), dtype=torch.float32, device=src.device)
+    _check(LIB.kvs_encode_fp8(_ptr(src), dt, rows, n, _ptr(codes), _ptr(scales), _stream(stream)),
+           "kvs_encode_fp8")
+    return codes, scales
+
+
+class KVCache:
+    """One layer's KV cache allocated with the sizes libkvs reports."""
+
+    def __init__(self, geom: CacheGeom, device="cuda"):
+        self.geom = geom
+        kv, sc, pos = cache_bytes(geom)
+        elt = TORCH_DTYPES[geom.kv_dtype]
+        n = kv // torch.empty((), dtype=elt).element_size()
+        self.k = torch.empty(n, dtype=elt, device=device)
+        self.v = torch.empty(n, dtype=elt, device=device)
+        self.k_scale = torch.zeros(sc // 4, dtype=torch.float32, device=device) if sc else None
+        self.v_scale = torch.zeros(sc // 4, dtype=torch.float32, device=device) if sc else None
+        self.pos_of_slot = torch.full((pos // 4,), -1, dtype=torch.int32, device=device) if pos else None
+
+    def append(self, k_rows, v_rows, row_seq, row_pos, stream=None):
+        """Write rows ``[n, Hkv*d]`` at (sequence, absolute position) pairs."""
+        _device_check(k_rows, v_rows, row_seq, row_pos)
+        dt = {torch.float32: KVS_F32, torch.bfloat16: KVS_BF16}.get(k_rows.dtype)
+        if dt is None or v_rows.dtype != k_rows.dtype:
+            raise TypeError("rows must be float32 or bfloat16, K and V alike")
+        if row_seq.dtype != torch.int32 or row_pos.dtype != torch.int32:
+            raise TypeError("row_seq and row_pos must be int32")
+        n = k_rows.shape[0]
+        w = self.geom.n_kv_heads * self.geom.head_dim
+        if k_rows.shape != (n, w) or v_rows.shape != (n, w) or row_seq.numel() != n or row_pos.numel() != n:
+            raise ValueError("row shapes do not match the geometry")
+        g = self.geom.c()
+        _check(LIB.kvs_append_kv(ctypes.byref(g), _ptr(k_rows), _ptr(v_rows), dt, n, _ptr(row_seq),
+                                 _ptr(row_pos), _ptr(self.k), _ptr(self.v), _ptr(self.k_scale),
+                                 _ptr(self.v_scale), _ptr(self.pos_of_slot), _stream(stream)),
+               "kvs_append_kv")
+
+
+def decode_attn_scored(cache: KVCache, q: torch.Tensor, cur_pos: torch.Tensor, out: torch.Tensor,
+                       workspace: torch.Tensor, mass_accum: torch.Tensor | None = None,
+                       keep_mask: torch.Tensor | None = None, stream=None):
+    """One layer of the scored decode step (kvs_decode_attn_scored)."""
+    g = cache.geom
+    _device_check(q, cur_pos, out, workspace, mass_accum, keep_mask)
+    qdt = TORCH_DTYPES[g.q_dtype]
+    if q.dtype != qdt or out.dtype != qdt:
+        raise TypeError("q and out must have the geometry's q dtype")
+    if q.shape != (g.batch, g.n_q_heads, g.head_dim) or out.shape != q.shape:
+        raise ValueError("q/out must be [B, Hq, d]")
+    if cur_pos.dtype != torch.int32 or cur_pos.numel() != g.batch:
+        raise ValueError("cur_pos must be int32 [B]")
+    if mass_accum is not None and (mass_accum.dtype != torch.float32 or mass_accum.numel() != g.batch * g.nb):
+        raise ValueError("mass_accum must be float32 [B, NBmax]")
+    if keep_mask is not None and (keep_mask.dtype != torch.int32 or keep_mask.numel() != g.batch * g.words):
+        raise ValueError("keep_mask must be int32 (bit words) [B, W]")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    gc = g.c()
+    _check(LIB.kvs_decode_attn_scored(ctypes.byref(gc), _ptr(q), _ptr(cache.k), _ptr(cache.v),
+                                      _ptr(cache.k_scale), _ptr(cache.v_scale), _ptr(cache.pos_of_slot),
+                                      _ptr(cur_pos), _ptr(keep_mask), _ptr(out), _ptr(mass_accum),
+                                      _ptr(workspace), ws_bytes, _stream(stream)),
+           "kvs_decode_attn_scored")
+    return out
+
+
+def update_sidecar(mass_accum, attended, ema, cum, traj, step: int, alpha: float, stream=None):
+    """Close one turn: Attended, EMA, Cumulative, trajectory ring; zero the accumulator."""
+    _device_check(mass_accum, attended, ema, cum, traj)
+    B, nb = attended.shape
+    traj_cap = traj.shape[1] if traj is not None else 1
+    for t in (mass_accum, ema, cum):
+        if t.numel() != B * nb or t.dtype != torch.float32:
+            raise ValueError("side-car arrays must be float32 [B, NBmax]")
+    _check(LIB.kvs_update_sidecar(_ptr(mass_accum), _ptr(attended), _ptr(ema), _ptr(cum), _ptr(traj),
+                                  B, nb, traj_cap, int(step), float(alpha), _stream(stream)),
+           "kvs_update_sidecar")
+
+
+def select_blocks(score, cur_pos, budget_blocks: int, recent_tokens: int, sink_tokens: int = 0,
+                  alive=None, keep_mask=None, sel_ids=None, n_sel=None, stream=None):
+    """Heavy-hitter block selection; returns (keep_mask, sel_ids, n_sel)."""
+    _device_check(score, cur_pos, alive)
+    B, nb = score.shape
+    words = (nb + 31) // 32
+    dev = score.device
+    if keep_mask is None:
+        keep_mask = torch.empty((B, words), dtype=torch.int32, device=dev)
+    if sel_ids is None:
+        sel_ids = torch.empty((B, nb), dtype=torch.int32, device=dev)
+    if n_sel is None:
+        n_sel = torch.empty((B,), dtype=torch.int32, device=dev)
+    if score.dtype != torch.float32 or cur_pos.dtype != torch.int32:
+        raise TypeError("score float32, cur_pos int32")
+    if alive is not None and (alive.dtype != torch.int32 or alive.numel() != B * words):
+        raise ValueError("alive must be int32 bit words [B, W]")
+    _check(LIB.kvs_select_blocks(_ptr(score), _ptr(alive), _ptr(cur_pos), B, nb, int(budget_blocks),
+                                 int(recent_tokens), int(sink_tokens), _ptr(keep_mask), _ptr(sel_ids),
+                                 _ptr(n_sel), _stream(stream)),
+           "kvs_select_blocks")
+    return keep_mask, sel_ids, n_sel

@@ -1,0 +1,228 @@
+// libkvs C ABI: argument checking, partition planning and launches.
+// Declarations and the full contract of every entry point are in include/kvs.h.
+
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/kvs.h"
+#include "kvs_internal.h"
+
+namespace {
+
+constexpr int kTileSlots = 16;
+constexpr int kTargetWorkgroups = 2048;  // ~8 per CU on 256 CUs
+constexpr int kMaxTilesPerPart = 256;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int elem_bytes(int dt) { return dt == KVS_F32 ? 4 : dt == KVS_BF16 ? 2 : 1; }
+
+int check_geom(const kvs_geom* g) {
+  if (!g) return KVS_EINVAL;
+  if (g->batch < 1 || g->n_kv_heads < 1 || g->n_q_heads < 1) return KVS_EINVAL;
+  if (g->n_q_heads % g->n_kv_heads) return KVS_EINVAL;
+  if (g->n_q_heads / g->n_kv_heads > 16) return KVS_ENOTIMPL;
+  if (g->capacity < kTileSlots || g->capacity % kTileSlots) return KVS_EINVAL;
+  if (g->window < 0) return KVS_EINVAL;
+  if (g->ring != 0 && g->ring != 1) return KVS_EINVAL;
+  if (g->n_blocks_max < 1) return KVS_EINVAL;
+  if (!g->ring && g->n_blocks_max < g->capacity / kTileSlots) return KVS_EINVAL;
+  if (!(g->softmax_scale > 0.0f) || !isfinite(g->softmax_scale)) return KVS_EINVAL;
+  const int kv = g->kv_dtype, q = g->q_dtype, d = g->head_dim;
+  if (kv != KVS_F32 && kv != KVS_BF16 && kv != KVS_FP8_E4M3) return KVS_EDTYPE;
+  if (kv == KVS_F32) {
+    if (q != KVS_F32) return KVS_EDTYPE;
+    if (d != 16 && d != 64 && d != 128) return KVS_EDTYPE;
+  } else {
+    if (q != KVS_BF16) return KVS_EDTYPE;
+    if (d != 64 && d != 128) return KVS_EDTYPE;
+  }
+  // sizes that must fit the kernels' 32-bit indexing of per-sequence slots
+  if ((int64_t)g->capacity * g->n_kv_heads * d > (int64_t)1 << 40) return KVS_EINVAL;
+  return KVS_OK;
+}
+
+struct Plan {
+  int NT, tpp, nparts, nsub, G;
+  size_t off_m, off_l, off_o, off_e, total;
+  size_t lds_partial;
+};
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+Plan make_plan(const kvs_geom* g) {
+  Plan p{};
+  p.G = g->n_q_heads / g->n_kv_heads;
+  p.NT = g->capacity / kTileSlots;
+  p.nsub = g->ring ? 2 : 1;
+  const int pairs = g->batch * g->n_kv_heads;
+  int ptarget = (kTargetWorkgroups + pairs - 1) / pairs;
+  if (ptarget < 1) ptarget = 1;
+  int tpp = (p.NT + ptarget - 1) / ptarget;
+  if (tpp < 4) tpp = 4;
+  // combine keeps [Hq][P] weights in LDS: bound P so that stays <= 48 KiB
+  const int pmax = 12288 / g->n_q_heads;
+  while ((p.NT + tpp - 1) / tpp > pmax) tpp *= 2;
+  if (tpp > kMaxTilesPerPart) tpp = kMaxTilesPerPart;
+  p.tpp = tpp;
+  p.nparts = (p.NT + tpp - 1) / tpp;
+  const size_t bh = (size_t)g->batch * g->n_q_heads;
+  p.off_m = 0;
+  p.off_l = round256(p.off_m + bh * p.nparts * 4);
+  p.off_o = round256(p.off_l + bh * p.nparts * 4);
+  p.off_e = round256(p.off_o + bh * p.nparts * g->head_dim * 4);
+  p.total = round256(p.off_e + bh * (size_t)p.NT * p.nsub * 4);
+  p.lds_partial = 4 * ((size_t)tpp * p.G * (p.nsub + 1) + 8 * p.G + 4 * (size_t)p.G * g->head_dim);
+  return p;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? KVS_OK : KVS_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* kvs_version(void) { return "libkvs 0.1 (gfx950)"; }
+
+const char* kvs_status_str(int s) {
+  switch (s) {
+    case KVS_OK: return "ok";
+    case KVS_EINVAL: return "invalid argument or geometry";
+    case KVS_EDTYPE: return "unsupported dtype or head-dim combination";
+    case KVS_EALIGN: return "pointer not 16-byte aligned";
+    case KVS_EWS: return "workspace too small";
+    case KVS_EHIP: return "HIP launch failure";
+    case KVS_ENOTIMPL: return "not implemented for this combination";
+    default: return "unknown status";
+  }
+}
+
+int kvs_cache_bytes(const kvs_geom* g, size_t* kv_bytes, size_t* scale_bytes, size_t* pos_bytes) {
+  int st = check_geom(g);
+  if (st) return st;
+  const size_t slots = (size_t)g->batch * g->capacity;
+  if (kv_bytes) *kv_bytes = slots * g->n_kv_heads * g->head_dim * elem_bytes(g->kv_dtype);
+  if (scale_bytes) *scale_bytes = g->kv_dtype == KVS_FP8_E4M3 ? slots * 4 : 0;
+  if (pos_bytes) *pos_bytes = g->ring ? slots * 4 : 0;
+  return KVS_OK;
+}
+
+int kvs_encode_fp8(const void* src, int32_t src_dtype, int64_t n_rows, int32_t row_len,
+                   uint8_t* codes, float* scales, void* stream) {
+  if (src_dtype != KVS_F32 && src_dtype != KVS_BF16) return KVS_EDTYPE;
+  if (n_rows < 0 || row_len < 1 || row_len > 65536) return KVS_EINVAL;
+  if (n_rows == 0) return KVS_OK;
+  if (!src || !codes || !scales) return KVS_EINVAL;
+  if (!aligned16(src) || !aligned16(codes) || !aligned16(scales)) return KVS_EALIGN;
+  return hip_status(kvs::launch_encode_fp8(src, src_dtype == KVS_BF16, n_rows, row_len, codes,
+                                           scales, (hipStream_t)stream));
+}
+
+int kvs_append_kv(const kvs_geom* g, const void* k_rows, const void* v_rows, int32_t src_dtype,
+                  int32_t n_rows, const int32_t* row_seq, const int32_t* row_pos, void* k_cache,
+                  void* v_cache, float* k_scale, float* v_scale, int32_t* pos_of_slot,
+                  void* stream) {
+  int st = check_geom(g);
+  if (st) return st;
+  if (n_rows < 0) return KVS_EINVAL;
+  if (src_dtype != KVS_F32 && src_dtype != KVS_BF16) return KVS_EDTYPE;
+  const bool fp8 = g->kv_dtype == KVS_FP8_E4M3;
+  if (!fp8 && src_dtype != g->kv_dtype) return KVS_EDTYPE;
+  if (fp8 != (k_scale != nullptr) || fp8 != (v_scale != nullptr)) return KVS_EINVAL;
+  if ((g->ring != 0) != (pos_of_slot != nullptr)) return KVS_EINVAL;
+  if (n_rows == 0) return KVS_OK;
+  if (!k_rows || !v_rows || !row_seq || !row_pos || !k_cache || !v_cache) return KVS_EINVAL;
+  const void* ptrs[] = {k_rows, v_rows, row_seq, row_pos, k_cache, v_cache, k_scale, v_scale, pos_of_slot};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KVS_EALIGN;
+  kvs::AppendArgs a{};
+  a.k_rows = k_rows; a.v_rows = v_rows; a.row_seq = row_seq; a.row_pos = row_pos;
+  a.k_cache = k_cache; a.v_cache = v_cache; a.k_scale = k_scale; a.v_scale = v_scale;
+  a.pos_of_slot = pos_of_slot;
+  a.n_rows = n_rows; a.B = g->batch; a.Hkv = g->n_kv_heads; a.D = g->head_dim; a.C = g->capacity;
+  a.ring = g->ring; a.kv = g->kv_dtype == KVS_FP8_E4M3 ? kvs::KV_FP8 : g->kv_dtype == KVS_BF16 ? kvs::KV_BF16 : kvs::KV_F32;
+  a.src_bf16 = src_dtype == KVS_BF16;
+  return hip_status(kvs::launch_append(a, (hipStream_t)stream));
+}
+
+int kvs_decode_workspace_bytes(const kvs_geom* g, size_t* bytes) {
+  int st = check_geom(g);
+  if (st) return st;
+  if (!bytes) return KVS_EINVAL;
+  *bytes = make_plan(g).total;
+  return KVS_OK;
+}
+
+int kvs_decode_attn_scored(const kvs_geom* g, const void* q, const void* k_cache,
+                           const void* v_cache, const float* k_scale, const float* v_scale,
+                           const int32_t* pos_of_slot, const int32_t* cur_pos,
+                           const uint32_t* keep_mask, void* out, float* mass_accum,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_geom(g);
+  if (st) return st;
+  const bool fp8 = g->kv_dtype == KVS_FP8_E4M3;
+  if (!q || !k_cache || !v_cache || !cur_pos || !out || !workspace) return KVS_EINVAL;
+  if (fp8 != (k_scale != nullptr) || fp8 != (v_scale != nullptr)) return KVS_EINVAL;
+  if ((g->ring != 0) != (pos_of_slot != nullptr)) return KVS_EINVAL;
+  if (keep_mask && g->window > 0) return KVS_EINVAL;
+  const void* ptrs[] = {q, k_cache, v_cache, k_scale, v_scale, pos_of_slot, cur_pos, keep_mask, out, mass_accum, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KVS_EALIGN;
+  const Plan p = make_plan(g);
+  if (workspace_bytes < p.total) return KVS_EWS;
+  char* ws = (char*)workspace;
+  kvs::PartialArgs a{};
+  a.q = q; a.k = k_cache; a.v = v_cache; a.ks = k_scale; a.vs = v_scale;
+  a.pos_of_slot = pos_of_slot; a.cur_pos = cur_pos; a.keep = keep_mask;
+  a.ws_m = (float*)(ws + p.off_m); a.ws_l = (float*)(ws + p.off_l);
+  a.ws_o = (float*)(ws + p.off_o); a.ws_e = (float*)(ws + p.off_e);
+  a.B = g->batch; a.Hq = g->n_q_heads; a.Hkv = g->n_kv_heads; a.G = p.G; a.C = g->capacity;
+  a.NT = p.NT; a.window = g->window; a.nbmax = g->n_blocks_max;
+  a.kwords = (g->n_blocks_max + 31) / 32; a.tpp = p.tpp; a.nparts = p.nparts;
+  a.scale_log2 = g->softmax_scale * 1.4426950408889634f;
+  const int kv = fp8 ? kvs::KV_FP8 : g->kv_dtype == KVS_BF16 ? kvs::KV_BF16 : kvs::KV_F32;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = kvs::launch_partial(kv, g->head_dim, a, mass_accum != nullptr, g->ring != 0,
+                                     p.lds_partial, s);
+  if (e != hipSuccess) return KVS_EHIP;
+  kvs::CombineArgs c{};
+  c.ws_m = a.ws_m; c.ws_l = a.ws_l; c.ws_o = a.ws_o; c.ws_e = a.ws_e; c.cur_pos = cur_pos;
+  c.out = out; c.mass = mass_accum;
+  c.B = g->batch; c.Hq = g->n_q_heads; c.D = g->head_dim; c.C = g->capacity; c.NT = p.NT;
+  c.nbmax = g->n_blocks_max; c.tpp = p.tpp; c.nparts = p.nparts;
+  c.n_o_chunks = (g->n_q_heads * g->head_dim + 255) / 256;
+  c.n_mass_chunks = (p.NT + 255) / 256;
+  return hip_status(kvs::launch_combine(c, g->ring != 0, g->q_dtype == KVS_BF16, s));
+}
+
+int kvs_update_sidecar(float* mass_accum, float* attended, float* ema, float* cum, float* traj,
+                       int32_t batch, int32_t n_blocks_max, int32_t traj_cap, int64_t step,
+                       float alpha, void* stream) {
+  if (batch < 1 || n_blocks_max < 1 || traj_cap < 1 || step < 0) return KVS_EINVAL;
+  if (!(alpha >= 0.0f && alpha <= 1.0f)) return KVS_EINVAL;
+  if (!mass_accum || !attended || !ema || !cum) return KVS_EINVAL;
+  const void* ptrs[] = {mass_accum, attended, ema, cum, traj};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KVS_EALIGN;
+  return hip_status(kvs::launch_sidecar(mass_accum, attended, ema, cum, traj, batch, n_blocks_max,
+                                        traj_cap, step, alpha, (hipStream_t)stream));
+}
+
+int kvs_select_blocks(const float* score, const uint32_t* alive, const int32_t* cur_pos,
+                      int32_t batch, int32_t n_blocks_max, int32_t budget_blocks,
+                      int32_t recent_tokens, int32_t sink_tokens, uint32_t* keep_mask,
+                      int32_t* sel_ids, int32_t* n_sel, void* stream) {
+  if (batch < 1 || n_blocks_max < 1) return KVS_EINVAL;
+  if (budget_blocks < 0 || recent_tokens < 1 || sink_tokens < 0) return KVS_EINVAL;
+  if (!score || !cur_pos || !keep_mask || !sel_ids || !n_sel) return KVS_EINVAL;
+  const void* ptrs[] = {score, alive, cur_pos, keep_mask, sel_ids, n_sel};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KVS_EALIGN;
+  kvs::SelectArgs a{};
+  a.score = score; a.alive = alive; a.cur_pos = cur_pos; a.keep = keep_mask; a.sel_ids = sel_ids;
+  a.n_sel = n_sel; a.B = batch; a.nbmax = n_blocks_max; a.kwords = (n_blocks_max + 31) / 32;
+  a.budget = budget_blocks; a.recent = recent_tokens; a.sinks = sink_tokens;
+  return hip_status(kvs::launch_select(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+// Device-side helpers shared by the libkvs kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvs_internal.h"
+
+namespace kvs {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kTile = 16;          // slots per tile == tokens per block
+
+__device__ __forceinline__ float bits_to_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t f32_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// bf16 (stored as the upper 16 bits of a float) to float: exact.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return bits_to_f32(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return bits_to_f32(w & 0xFFFF0000u); }
+
+// float -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = f32_bits(f);
+  uint32_t r = u + 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(r >> 16);
+}
+
+// Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48),
+// using the gfx950 row-swap permutes. The combine order is the same in every
+// lane, so all four rows end up with bit-identical results.
+__device__ __forceinline__ float rows_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(f32_bits(x), f32_bits(x), false, false);
+  x = fmaxf(bits_to_f32(a[0]), bits_to_f32(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(f32_bits(x), f32_bits(x), false, false);
+  return fmaxf(bits_to_f32(b[0]), bits_to_f32(b[1]));
+}
+
+__device__ __forceinline__ float rows_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(f32_bits(x), f32_bits(x), false, false);
+  x = bits_to_f32(a[0]) + bits_to_f32(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(f32_bits(x), f32_bits(x), false, false);
+  return bits_to_f32(b[0]) + bits_to_f32(b[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Wave-uniform "any lane" / "all lanes" votes.
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+__device__ __forceinline__ bool wave_all(bool p) {
+  return __builtin_amdgcn_ballot_w64(p) == __builtin_amdgcn_read_exec();
+}
+
+// ---------------------------------------------------------------------------
+// FP8 E4M3 (OCP: bias 7, no infinity, NaN = 0x7F/0xFF, largest finite 448).
+// Encoding follows the format definition directly: clip to 448, pick the
+// binade (the subnormal range shares the 2^-9 quantum of the lowest binade),
+// scale to an integer grid by a power of two (exact), round half to even.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  const uint32_t u = f32_bits(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = bits_to_f32(u & 0x7FFFFFFFu);
+  uint32_t code;
+  if (a >= 448.0f) {
+    code = 0x7Eu;
+  } else if (a < 0.015625f) {                 // below 2^-6: quantum 2^-9
+    code = (uint32_t)__builtin_rintf(a * 512.0f);          // 0..8, ties to even
+  } else {
+    const int e = (int)((f32_bits(a) >> 23) & 0xFF) - 127;  // -6 .. 8
+    const float n = __builtin_rintf(a * bits_to_f32((uint32_t)(127 + 3 - e) << 23));  // 8..16
+    code = (uint32_t)((e + 7) * 8) + (uint32_t)n - 8u;
+  }
+  return code | sign;
+}
+
+// absmax / 240, correctly rounded (the pages' per-position scale).
+__device__ __forceinline__ float fp8_scale_of(float absmax) { return __fdiv_rn(absmax, 240.0f); }
+
+// Four FP8 codes (one dword) to four bf16 values, exact (E4M3 is a subset of bf16).
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
+  bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  u32x2 r;
+  r[0] = __builtin_bit_cast(uint32_t, lo);
+  r[1] = __builtin_bit_cast(uint32_t, hi);
+  return r;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
+}
+
+}  // namespace kvs

@@ -1,0 +1,75 @@
+// Internal launch interfaces of libkvs (host and device).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvs {
+
+enum : int { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
+
+struct PartialArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* ks;
+  const float* vs;
+  const int32_t* pos_of_slot;
+  const int32_t* cur_pos;
+  const uint32_t* keep;
+  float* ws_m;     // [B][Hq][P]
+  float* ws_l;     // [B][Hq][P]
+  float* ws_o;     // [B][Hq][P][D]
+  float* ws_e;     // [B][Hq][NT][NSUB]
+  int B, Hq, Hkv, G, C, NT, window, nbmax, kwords, tpp, nparts;
+  float scale_log2;
+};
+
+struct CombineArgs {
+  const float* ws_m;
+  const float* ws_l;
+  const float* ws_o;
+  const float* ws_e;
+  const int32_t* cur_pos;
+  void* out;
+  float* mass;
+  int B, Hq, D, C, NT, nbmax, tpp, nparts, n_o_chunks, n_mass_chunks;
+};
+
+hipError_t launch_partial(int kv, int d, const PartialArgs& a, bool scored, bool ring,
+                          size_t lds_bytes, hipStream_t st);
+hipError_t launch_combine(const CombineArgs& a, bool ring, bool q_bf16, hipStream_t st);
+
+hipError_t launch_encode_fp8(const void* src, int src_bf16, int64_t n_rows, int row_len,
+                             uint8_t* codes, float* scales, hipStream_t st);
+
+struct AppendArgs {
+  const void* k_rows;
+  const void* v_rows;
+  const int32_t* row_seq;
+  const int32_t* row_pos;
+  void* k_cache;
+  void* v_cache;
+  float* k_scale;
+  float* v_scale;
+  int32_t* pos_of_slot;
+  int n_rows, B, Hkv, D, C, ring, kv, src_bf16;
+};
+hipError_t launch_append(const AppendArgs& a, hipStream_t st);
+
+hipError_t launch_sidecar(float* mass, float* att, float* ema, float* cum, float* traj, int B,
+                          int nbmax, int traj_cap, int64_t step, float alpha, hipStream_t st);
+
+struct SelectArgs {
+  const float* score;
+  const uint32_t* alive;
+  const int32_t* cur_pos;
+  uint32_t* keep;
+  int32_t* sel_ids;
+  int32_t* n_sel;
+  int B, nbmax, kwords, budget, recent, sinks;
+};
+hipError_t launch_select(const SelectArgs& a, hipStream_t st);
+
+}  // namespace kvs

@@ -1,0 +1,182 @@
+// Block side-car update and heavy-hitter block selection.
+//
+// Side-car (Context views at marginal cost, section 2 Tier 1): per block,
+// Attended (this turn), EMA, Cumulative and a bounded trajectory ring, O(1)
+// per block per turn.
+//
+// Selection (Context Optimization, "H2O KV Cache Eviction"): sinks and recent
+// tokens kept unconditionally; among the remaining alive blocks the
+// highest-scoring ones survive, here at 16-token block granularity (Per-Head
+// Attention as a Scoring Signal: the block is the unit that is kept). The
+// top-k is an exact radix select on 64-bit keys (order-preserving score bits,
+// then the complemented block index), so equal scores go to the lower index
+// and every key is distinct.
+
+#include "kvs_device.h"
+#include "kvs_internal.h"
+
+namespace kvs {
+
+__global__ __launch_bounds__(256) void kvs_sidecar(float* mass, float* att, float* ema, float* cum,
+                                                    float* traj, int B, int nbmax, int traj_cap,
+                                                    int slot, float alpha) {
+  const size_t n = (size_t)B * nbmax;
+  for (size_t x = (size_t)blockIdx.x * 256 + threadIdx.x; x < n; x += (size_t)gridDim.x * 256) {
+    const float A = mass[x];
+    att[x] = A;
+    ema[x] = alpha * A + (1.0f - alpha) * ema[x];
+    cum[x] = cum[x] + A;
+    if (traj) {
+      const size_t b = x / nbmax, blk = x - b * nbmax;
+      traj[(b * traj_cap + slot) * nbmax + blk] = A;
+    }
+    mass[x] = 0.0f;
+  }
+}
+
+hipError_t launch_sidecar(float* mass, float* att, float* ema, float* cum, float* traj, int B,
+                          int nbmax, int traj_cap, int64_t step, float alpha, hipStream_t st) {
+  const size_t n = (size_t)B * nbmax;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(kvs_sidecar, dim3((unsigned)blocks), dim3(256), 0, st, mass, att, ema, cum, traj,
+                     B, nbmax, traj_cap, (int)(step % traj_cap), alpha);
+  return hipGetLastError();
+}
+
+// Order-preserving map of a float to uint32 (-0 and +0 map alike).
+__device__ __forceinline__ uint32_t float_order(float f) {
+  uint32_t u = f32_bits(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t select_key(float score, int blk) {
+  return ((uint64_t)float_order(score) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)blk);
+}
+
+constexpr int kSelThreads = 1024;
+
+// One workgroup per sequence.
+__global__ __launch_bounds__(kSelThreads) void kvs_select(SelectArgs a) {
+  extern __shared__ uint32_t alive_lds[];  // [kwords]: alive bits, staged so keep may alias alive
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t wsum[kSelThreads / 64];
+  __shared__ uint64_t s_prefix, s_mask;
+  __shared__ int s_remaining, s_ncand, s_base;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int i = a.cur_pos[b];
+  const int nexist = min(i / kTile + 1, a.nbmax);
+  const int rlo = max(0, i - a.recent + 1) / kTile;
+  const int rhi = i / kTile;
+  const int shi = a.sinks > 0 ? (min(a.sinks, i + 1) - 1) / kTile : -1;
+  const float* score = a.score + (size_t)b * a.nbmax;
+  const bool have_alive = a.alive != nullptr;
+  if (have_alive)
+    for (int w = tid; w < a.kwords; w += kSelThreads) alive_lds[w] = a.alive[(size_t)b * a.kwords + w];
+
+  auto is_prot = [&](int blk) { return (blk >= rlo && blk <= rhi) || blk <= shi; };
+  auto is_cand = [&](int blk) {
+    if (blk >= nexist || is_prot(blk)) return false;
+    return !have_alive || ((alive_lds[blk >> 5] >> (blk & 31)) & 1u);
+  };
+
+  // candidate count
+  if (tid == 0) s_ncand = 0;
+  __syncthreads();
+  int cnt = 0;
+  for (int blk = tid; blk < nexist; blk += kSelThreads) cnt += is_cand(blk) ? 1 : 0;
+  for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+  if (lane == 0) atomicAdd(&s_ncand, cnt);
+  if (tid == 0) {
+    s_prefix = 0;
+    s_mask = 0;
+  }
+  __syncthreads();
+  const int ncand = s_ncand;
+  const int k = min(a.budget, ncand);
+  if (tid == 0) s_remaining = k;
+  __syncthreads();
+
+  // Radix select of the k-th largest key, 8 bits at a time from the top.
+  const bool take_all = (k == ncand);
+  if (k > 0 && !take_all) {
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      for (int x = tid; x < 256; x += kSelThreads) hist[x] = 0;
+      __syncthreads();
+      const uint64_t prefix = s_prefix, mask = s_mask;
+      for (int blk = tid; blk < nexist; blk += kSelThreads) {
+        if (!is_cand(blk)) continue;
+        const uint64_t key = select_key(score[blk], blk);
+        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xFF], 1u);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int rem = s_remaining;
+        int d = 255;
+        for (; d > 0; --d) {
+          if ((int)hist[d] >= rem) break;
+          rem -= (int)hist[d];
+        }
+        s_remaining = rem;
+        s_prefix = prefix | ((uint64_t)d << shift);
+        s_mask = mask | ((uint64_t)0xFF << shift);
+      }
+      __syncthreads();
+    }
+  }
+  const uint64_t thresh = s_prefix;
+
+  auto kept = [&](int blk) -> bool {
+    if (blk >= nexist) return true;  // not written yet: never evicted
+    if (is_prot(blk)) return true;
+    if (!is_cand(blk) || k == 0) return false;
+    if (take_all) return true;
+    return select_key(score[blk], blk) >= thresh;
+  };
+
+  // keep mask words
+  for (int w = tid; w < a.kwords; w += kSelThreads) {
+    uint32_t word = 0;
+    for (int bit = 0; bit < 32; ++bit) {
+      const int blk = w * 32 + bit;
+      if (blk < a.nbmax && kept(blk)) word |= 1u << bit;
+    }
+    a.keep[(size_t)b * a.kwords + w] = word;
+  }
+
+  // ascending ids of kept existing blocks (stream compaction)
+  if (tid == 0) s_base = 0;
+  __syncthreads();
+  int32_t* ids = a.sel_ids + (size_t)b * a.nbmax;
+  for (int c0 = 0; c0 < nexist; c0 += kSelThreads) {
+    const int blk = c0 + tid;
+    const bool f = blk < nexist && kept(blk);
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(f);
+    const int before = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[wave] = (uint32_t)__builtin_popcountll(bal);
+    __syncthreads();
+    int off = s_base;
+    for (int w = 0; w < wave; ++w) off += (int)wsum[w];
+    if (f) ids[off + before] = blk;
+    __syncthreads();
+    if (tid == 0) {
+      int t = 0;
+      for (int w = 0; w < kSelThreads / 64; ++w) t += (int)wsum[w];
+      s_base += t;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) a.n_sel[b] = s_base;
+}
+
+hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
+  const size_t lds = a.alive ? (size_t)a.kwords * 4 : 0;
+  hipLaunchKernelGGL(kvs_select, dim3(a.B), dim3(kSelThreads), lds, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace kvs

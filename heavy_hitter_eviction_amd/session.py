@@ -1,0 +1,82 @@
+"""A whole scored decode step over L layers, driven through the C ABI.
+
+For every layer: append the new position's K/V (FP8-encoding when the cache
+is FP8), then the scored attention (partial + combine) that adds this layer's
+block masses into ``mass``. After the last layer the side-car closes the turn,
+and the heavy-hitter selection produces the keep mask. In evict mode that
+mask feeds the next step's attention, so dropped blocks are never read again
+(Context Optimization, "H2O KV Cache Eviction"); in score-only mode the full
+context is read and the mask is only reported.
+
+Host code here only sequences library calls and owns torch buffers.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import api
+from .workloads import Workload
+
+
+def geom_of(w: Workload) -> api.CacheGeom:
+    return api.CacheGeom(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
+                         head_dim=w.head_dim, capacity=w.capacity, window=w.window, ring=w.ring,
+                         n_blocks_max=w.n_blocks_max, kv_dtype=w.kv_dtype, q_dtype=w.q_dtype)
+
+
+class ScoredDecoder:
+    def __init__(self, w: Workload, evict: bool = False, device="cuda", layers: int | None = None):
+        self.w = w
+        self.evict = evict
+        self.device = torch.device(device)
+        self.geom = geom_of(w)
+        self.n_layers = w.n_layers if layers is None else layers
+        self.caches = [api.KVCache(self.geom, device) for _ in range(self.n_layers)]
+        ws = api.decode_workspace_bytes(self.geom)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
+        B, nb = w.batch, self.geom.nb
+        f32 = dict(dtype=torch.float32, device=device)
+        self.mass = torch.zeros((B, nb), **f32)
+        self.attended = torch.zeros((B, nb), **f32)
+        self.ema = torch.zeros((B, nb), **f32)
+        self.cum = torch.zeros((B, nb), **f32)
+        self.traj = torch.zeros((B, w.traj_cap, nb), **f32)
+        self.keep = torch.full((B, self.geom.words), -1, dtype=torch.int32, device=device)
+        self.sel_ids = torch.zeros((B, nb), dtype=torch.int32, device=device)
+        self.n_sel = torch.zeros((B,), dtype=torch.int32, device=device)
+        qdt = api.TORCH_DTYPES[w.q_dtype]
+        self.out = [torch.empty((B, w.n_q_heads, w.head_dim), dtype=qdt, device=device)
+                    for _ in range(self.n_layers)]
+        self.row_seq = torch.arange(B, dtype=torch.int32, device=device)
+        self.step_index = 0
+
+    def prefill(self, layer: int, seq: int, k_rows: torch.Tensor, v_rows: torch.Tensor, pos0: int = 0):
+        n = k_rows.shape[0]
+        seqs = torch.full((n,), seq, dtype=torch.int32, device=self.device)
+        pos = torch.arange(pos0, pos0 + n, dtype=torch.int32, device=self.device)
+        self.caches[layer].append(k_rows, v_rows, seqs, pos)
+
+    def attend_layer(self, layer: int, q: torch.Tensor, cur_pos: torch.Tensor, scored: bool = True):
+        keep = self.keep if (self.evict and not self.w.window) else None
+        api.decode_attn_scored(self.caches[layer], q, cur_pos, self.out[layer], self.workspace,
+                               mass_accum=self.mass if scored else None, keep_mask=keep)
+
+    def step(self, q_layers, k_layers, v_layers, cur_pos: torch.Tensor):
+        """One decode step. ``q_layers[l]`` is [B, Hq, d]; ``k_layers[l]`` and
+        ``v_layers[l]`` are the new position's rows [B, Hkv*d]; ``cur_pos`` is
+        the int32 [B] absolute position being written and read."""
+        for l in range(self.n_layers):
+            self.caches[l].append(k_layers[l], v_layers[l], self.row_seq, cur_pos)
+            self.attend_layer(l, q_layers[l], cur_pos)
+        self.close_turn(cur_pos)
+
+    def close_turn(self, cur_pos: torch.Tensor):
+        api.update_sidecar(self.mass, self.attended, self.ema, self.cum, self.traj,
+                           self.step_index, self.w.alpha)
+        if self.w.select:
+            alive = self.keep if self.evict else None
+            api.select_blocks(self.cum, cur_pos, self.w.budget_blocks, self.w.recent_tokens,
+                              self.w.sink_tokens, alive=alive, keep_mask=self.keep,
+                              sel_ids=self.sel_ids, n_sel=self.n_sel)
+        self.step_index += 1

@@ -1,0 +1,238 @@
+/*
+ * kvs.h -- C ABI of libkvs: scored decode attention over a KV cache, with the
+ * per-(sequence, 16-token block) attention-mass tap, the block side-car and
+ * heavy-hitter block selection, for AMD Instinct MI355X (gfx950).
+ *
+ * Every call is asynchronous on the HIP stream it is given (``stream`` is a
+ * hipStream_t; NULL means the null stream). The library never allocates,
+ * frees or synchronises: the caller owns every buffer. Unless stated
+ * otherwise a pointer argument is a DEVICE pointer and must be 16-byte
+ * aligned. Calls return KVS_OK (0) or a negative kvs_status; when a call
+ * returns an error nothing has been launched. No global mutable state: calls
+ * are re-entrant and may be made from several host threads.
+ *
+ * Terms. B sequences; Hq query heads and Hkv KV heads with G = Hq / Hkv
+ * query heads reading each KV head (query head h reads KV head h / G); head
+ * dimension d; C slots per sequence; a block is 16 consecutive absolute
+ * positions (block b = position / 16); NBmax = n_blocks_max block entries per
+ * sequence in every per-block array; W = ceil(NBmax / 32) mask words.
+ */
+#ifndef KVS_H
+#define KVS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef KVS_API
+#define KVS_API __attribute__((visibility("default")))
+#endif
+
+/* Status codes. */
+typedef enum {
+  KVS_OK = 0,
+  KVS_EINVAL = -1,   /* bad geometry or argument, or a forbidden combination  */
+  KVS_EDTYPE = -2,   /* unsupported dtype or dtype/head-dim combination        */
+  KVS_EALIGN = -3,   /* a pointer is not 16-byte aligned                       */
+  KVS_EWS = -4,      /* workspace smaller than kvs_decode_workspace_bytes      */
+  KVS_EHIP = -5,     /* the HIP runtime refused a launch                       */
+  KVS_ENOTIMPL = -6  /* a combination this build does not provide              */
+} kvs_status;
+
+typedef enum {
+  KVS_F32 = 0,
+  KVS_BF16 = 1,
+  KVS_FP8_E4M3 = 2   /* OCP E4M3: 1 sign, 4 exponent (bias 7), 3 mantissa bits */
+} kvs_dtype;
+
+/*
+ * Cache geometry. It is fixed when the cache is allocated and must be passed
+ * unchanged to every call on that cache: element size, layout and scale
+ * arrays all follow from it (Context Optimization, "FP8 KV Cache / Flag
+ * Ordering": the FP8 and window choices have to be made before the buffers
+ * exist, or float-sized buffers end up holding FP8 data).
+ *
+ *   batch          B >= 1
+ *   n_q_heads      Hq >= 1, a multiple of n_kv_heads, Hq / Hkv <= 16
+ *   n_kv_heads     Hkv >= 1
+ *   head_dim       d: 16, 64 or 128 for KVS_F32; 64 or 128 for BF16 and FP8
+ *   capacity       C slots per sequence, a positive multiple of 16
+ *   window         0 = unlimited; w >= 1 lets position i read only positions
+ *                  i-w+1 .. i (LLM mechanics III, "1. Define the window")
+ *   ring           0: slot = position (requires position < C);
+ *                  1: circular cache, slot = position mod C, and the absolute
+ *                  position held by each slot is kept in pos_of_slot
+ *                  (Context Optimization, "Sliding Window Attention / Design";
+ *                  LLM mechanics III, "5. Keep three indices separate")
+ *   n_blocks_max   NBmax: entries per sequence of mass/score/side-car arrays.
+ *                  Linear caches need NBmax >= C / 16; ring caches need
+ *                  NBmax > (largest position ever written) / 16.
+ *   kv_dtype       element type of the cache
+ *   q_dtype        KVS_F32 with a KVS_F32 cache, KVS_BF16 otherwise; the
+ *                  attention output has the same type
+ *   softmax_scale  logit multiplier, finite and > 0 (usually 1/sqrt(d))
+ */
+typedef struct {
+  int32_t batch;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t capacity;
+  int32_t window;
+  int32_t ring;
+  int32_t n_blocks_max;
+  int32_t kv_dtype;  /* kvs_dtype */
+  int32_t q_dtype;   /* kvs_dtype */
+  float softmax_scale;
+} kvs_geom;
+
+/*
+ * Cache layout (one layer; K and V are separate buffers):
+ *   K   [B][Hkv][C][d]                 slot-major rows of d elements
+ *   V   [B][Hkv][C/16][4][d][4]        inside each 16-slot tile, slot 4a+e
+ *                                      and dimension j live at [a][j][e]
+ *   k_scale, v_scale  [B][C] float     FP8 caches only: one scale per
+ *                                      (sequence, slot) covering all Hkv*d
+ *                                      values of that position
+ *   pos_of_slot [B][C] int32           ring caches only; -1 marks an empty slot
+ * kvs_cache_bytes() gives the byte sizes.
+ */
+KVS_API int kvs_cache_bytes(const kvs_geom* geom, size_t* kv_bytes, size_t* scale_bytes,
+                    size_t* pos_bytes);
+
+/*
+ * kvs_encode_fp8 -- per-row FP8 E4M3 encoding (Context Optimization,
+ * "FP8 KV Cache / How It Works": per position, scale = absmax / 240, values
+ * clipped to +-448 and quantised to 8 bits, scale stored separately).
+ *
+ * For each row r of ``src`` ([n_rows][row_len], KVS_F32 or KVS_BF16, bf16
+ * widened exactly): a = max |x|; s = a / 240 rounded once to float32;
+ * code = E4M3(x / s), the quotient rounded once to float32, then rounded to
+ * the nearest E4M3 value with ties to even after clipping to +-448; the sign
+ * is kept (-0 encodes as 0x80). A row with a == 0 gets s = 0 and all codes 0.
+ * Outputs: codes [n_rows][row_len] uint8, scales [n_rows] float. Non-finite
+ * inputs are outside the contract (the result is unspecified, no fault).
+ * n_rows >= 0 (0 launches nothing), 1 <= row_len <= 65536.
+ */
+KVS_API int kvs_encode_fp8(const void* src, int32_t src_dtype, int64_t n_rows, int32_t row_len,
+                   uint8_t* codes, float* scales, void* stream);
+
+/*
+ * kvs_append_kv -- write n_rows new positions into one layer's cache.
+ * Row r holds the K (and V) values of every KV head for position
+ * row_pos[r] of sequence row_seq[r]: k_rows, v_rows are [n_rows][Hkv*d] of
+ * src_dtype (KVS_F32 or KVS_BF16). The slot is the position (linear) or
+ * position mod C (ring). For an FP8 cache each row is encoded exactly as
+ * kvs_encode_fp8 does and its scales go to k_scale / v_scale at that slot;
+ * for a BF16 or F32 cache src_dtype must equal the cache type and the values
+ * are copied. For a ring cache pos_of_slot[seq][slot] receives the position.
+ * Two rows may not target the same (sequence, slot). Row indices outside
+ * [0, B) or positions outside the cache (negative, or >= C when linear) are
+ * skipped by the kernel. k_scale, v_scale: non-NULL iff the cache is FP8;
+ * pos_of_slot: non-NULL iff ring.
+ */
+KVS_API int kvs_append_kv(const kvs_geom* geom, const void* k_rows, const void* v_rows, int32_t src_dtype,
+                  int32_t n_rows, const int32_t* row_seq, const int32_t* row_pos,
+                  void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                  int32_t* pos_of_slot, void* stream);
+
+/* Workspace bytes kvs_decode_attn_scored needs; depends on geometry only. */
+KVS_API int kvs_decode_workspace_bytes(const kvs_geom* geom, size_t* bytes);
+
+/*
+ * kvs_decode_attn_scored -- one layer of the scored decode step.
+ *
+ * For every sequence b the current token's K/V are already in the cache
+ * (write, then attend: the window includes the current token) and
+ * i = cur_pos[b] is its absolute position. Key slot t is read when its
+ * absolute position p (t if linear, pos_of_slot[b][t] if ring) satisfies
+ * p >= 0, p <= i, p >= i - w + 1 when window w > 0, and, when keep_mask is
+ * given, bit (p / 16) of keep_mask[b] is set. For every query head h:
+ *   logits  s_j = softmax_scale * (q_h . k_j)    (FP8: k_j = code_j * k_scale)
+ *   weights p_j = exp(s_j - max) / sum exp(s - max)
+ *   out_h   = sum_j p_j v_j                      (FP8: v_j = code_j * v_scale)
+ * (Context views at marginal cost, section 0 and Tier 0: the post-softmax
+ * weights the pass computes anyway.) When mass_accum is not NULL the weights
+ * are also reduced per (sequence, block) and summed over all query heads
+ * (Context Optimization, "H2O / How It Works": scores accumulated across all
+ * query heads; Per-Head Attention as a Scoring Signal: score per head, place
+ * per 16-token block):
+ *   mass_accum[b][p/16] += sum_h sum_{read j in block} p_j
+ * Heads are added in ascending order, with no atomics, so results are
+ * deterministic; calling the layers in order sums them in that order.
+ * With mass_accum == NULL no mass work runs and ``out`` is bit-identical to
+ * the scored call (the tap never changes the math; Context views at marginal
+ * cost, Tier 0 invariant).
+ *
+ *   q           [B][Hq][d] q_dtype
+ *   k_cache, v_cache, k_scale, v_scale, pos_of_slot: as in kvs_append_kv
+ *   cur_pos     [B] int32
+ *   keep_mask   [B][W] uint32 or NULL (all blocks kept); only with window 0
+ *               (Context Optimization, "H2O vs Sliding Window": eviction
+ *               replaces the window, so the two are never combined)
+ *   out         [B][Hq][d] q_dtype
+ *   mass_accum  [B][NBmax] float or NULL
+ *   workspace   device scratch of at least kvs_decode_workspace_bytes()
+ *
+ * Preconditions the library cannot check (unspecified results, never a
+ * fault): the current token is readable (so no row is all-masked); a ring
+ * cache only holds position p in slot p mod C; inputs are finite.
+ */
+KVS_API int kvs_decode_attn_scored(const kvs_geom* geom, const void* q, const void* k_cache,
+                           const void* v_cache, const float* k_scale, const float* v_scale,
+                           const int32_t* pos_of_slot, const int32_t* cur_pos,
+                           const uint32_t* keep_mask, void* out, float* mass_accum,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kvs_update_sidecar -- close one turn (Context views at marginal cost,
+ * section 2 Tier 1 and section 3: {Attended, EMA, Cumulative, traj}, O(1) per
+ * block per turn). With A = mass_accum (this step's mass):
+ *   attended = A;  ema = alpha*A + (1-alpha)*ema;  cum += A;
+ *   traj[b][step mod traj_cap][:] = A;  mass_accum = 0.
+ * mass_accum, attended, ema, cum: [B][NBmax] float; traj: [B][traj_cap][NBmax]
+ * float or NULL. step >= 0 counts turns from 0; 1 <= traj_cap; 0 <= alpha <= 1.
+ */
+KVS_API int kvs_update_sidecar(float* mass_accum, float* attended, float* ema, float* cum, float* traj,
+                       int32_t batch, int32_t n_blocks_max, int32_t traj_cap, int64_t step,
+                       float alpha, void* stream);
+
+/*
+ * kvs_select_blocks -- heavy-hitter block selection (Context Optimization,
+ * "H2O KV Cache Eviction": sinks and recent tokens are always kept; among the
+ * rest the top scorers survive), at 16-token block granularity.
+ * For sequence b with i = cur_pos[b], the existing blocks are 0 .. i/16.
+ * Protected: every block meeting positions [max(0, i-recent+1), i], and, when
+ * sink_tokens > 0, every block meeting positions [0, sink_tokens-1].
+ * Candidates: existing, alive (bit set in alive[b], or all when alive is
+ * NULL), not protected. Kept: protected blocks plus the budget_blocks
+ * candidates with the largest (score, -block index): equal scores go to the
+ * lower block index.
+ *   score     [B][NBmax] float (e.g. the Cumulative array), finite
+ *   alive     [B][W] uint32 or NULL
+ *   keep_mask [B][W] uint32 out: bit b set for kept blocks and for every
+ *             block b > i/16 (not yet written, so never evicted)
+ *   sel_ids   [B][NBmax] int32 out: kept blocks (b <= i/16) in ascending order
+ *   n_sel     [B] int32 out: number of entries of sel_ids
+ * budget_blocks >= 0, recent_tokens >= 1, sink_tokens >= 0. Sequences with
+ * i / 16 >= NBmax have their blocks clipped to NBmax.
+ */
+KVS_API int kvs_select_blocks(const float* score, const uint32_t* alive, const int32_t* cur_pos,
+                      int32_t batch, int32_t n_blocks_max, int32_t budget_blocks,
+                      int32_t recent_tokens, int32_t sink_tokens, uint32_t* keep_mask,
+                      int32_t* sel_ids, int32_t* n_sel, void* stream);
+
+/* Static text for a status code. */
+KVS_API const char* kvs_status_str(int status);
+
+/* Library version string. */
+KVS_API const char* kvs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVS_H */

@@ -1,0 +1,97 @@
+"""Helpers shared by the GPU parity tests: build caches through the C ABI from
+seeded rows, compute the same quantities with the float64 oracle, compare."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import kvs_oracle as orc
+
+
+def dequant_rows(rows_f32: np.ndarray, kv_dtype: str) -> np.ndarray:
+    """The values a cache of ``kv_dtype`` holds for float32 source rows, in
+    float64: FP8 rows are encoded and decoded by the oracle itself; bf16 rows
+    are the round-to-nearest-even cast done when the inputs were made."""
+    if kv_dtype == "fp8":
+        codes, scales = orc.fp8_encode_rows(rows_f32.astype(np.float32))
+        return orc.fp8_decode_rows(codes, scales)
+    if kv_dtype == "bf16":
+        return torch.from_numpy(rows_f32).to(torch.bfloat16).double().numpy()
+    return rows_f32.astype(np.float64)
+
+
+def heads(rows: np.ndarray, n_heads: int, d: int) -> np.ndarray:
+    """[n, H*d] -> [H, n, d]"""
+    return rows.reshape(rows.shape[0], n_heads, d).transpose(1, 0, 2)
+
+
+def oracle_layer(q, Kd, Vd, positions, i, window, alive, scale, n_blocks):
+    """Oracle output, block mass and the PV rounding scale ``sum_j p_j |v_j|``
+    for one (sequence, layer): ``Kd``, ``Vd`` are [Hkv, n, d] float64 values
+    held at absolute ``positions``."""
+    positions = np.asarray(positions)
+    sel = np.array([orc.key_visible(int(p), i, window) and orc.block_alive(alive, orc.block_of(int(p)))
+                    for p in positions], dtype=bool)
+    o, p = orc.attend(q, Kd[:, sel], Vd[:, sel], scale)
+    mass = orc.block_mass(p, positions[sel], n_blocks)
+    G = q.shape[0] // Kd.shape[0]
+    absv = np.abs(Vd[:, sel])
+    pav = np.stack([p[h] @ absv[h // G] for h in range(q.shape[0])])
+    return o, mass, pav
+
+
+def close_o(got: np.ndarray, ref: np.ndarray, kv_dtype: str, pav: np.ndarray | None = None):
+    """Output tolerance derived from the arithmetic. Float32 caches: rtol 1e-5,
+    atol 1e-6. bf16 and FP8 caches: the output is rounded to bf16 (relative
+    2^-9) and the PV product takes the weights as bf16, which moves each
+    output by at most 2^-9 * sum_j p_j |v_j|; the bound used is
+    |d| <= 2e-2 |ref| + 2^-8 * sum_j p_j |v_j| (``pav``), a factor 2 above it."""
+    got = np.asarray(got, dtype=np.float64)
+    if kv_dtype == "f32":
+        bad = np.abs(got - ref) > 1e-5 * np.abs(ref) + 1e-6
+    else:
+        assert pav is not None
+        bad = np.abs(got - ref) > 2e-2 * np.abs(ref) + 2.0 ** -8 * pav
+    assert not bad.any(), f"O mismatch at {np.argwhere(bad)[:5].tolist()}: max err {np.abs(got - ref).max()}"
+
+
+def close_mass(got: np.ndarray, ref: np.ndarray, kv_dtype: str, what="mass"):
+    got = np.asarray(got, dtype=np.float64)
+    if kv_dtype == "f32":
+        bad = np.abs(got - ref) > 1e-5 * np.abs(ref) + 1e-6
+    else:
+        bad = np.abs(got - ref) > 1e-4 * np.maximum(1.0, np.abs(ref))
+    assert not bad.any(), f"{what} mismatch at {np.argwhere(bad)[:5].tolist()}: max err {np.abs(got - ref).max()}"
+
+
+def keep_ids_from_mask(mask_words: np.ndarray, n_exist: int) -> np.ndarray:
+    w = mask_words.astype(np.int64) & 0xFFFFFFFF
+    bits = [(int(w[b >> 5]) >> (b & 31)) & 1 for b in range(n_exist)]
+    return np.flatnonzero(np.array(bits, dtype=bool))
+
+
+def compare_selection(gpu_ids, ref_ids, score_ref, i, budget, recent, sinks, alive, rel_tol):
+    """Near-tie protocol: with v the oracle's budget-th candidate score, blocks
+    whose score is within tol of v are ambiguous; outside them the sets must be
+    equal and both must take the same number of ambiguous blocks. Returns the
+    number of ambiguous blocks."""
+    gpu, ref = set(int(x) for x in gpu_ids), set(int(x) for x in ref_ids)
+    if gpu == ref:
+        return 0
+    prot = orc.protected_blocks(i, recent, sinks)
+    cand = [b for b in range(i // 16 + 1) if (alive is None or alive[b]) and b not in prot]
+    cand.sort(key=lambda b: (-float(score_ref[b]), b))
+    if budget == 0 or not cand:
+        raise AssertionError(f"selection differs: gpu-only {gpu - ref}, oracle-only {ref - gpu}")
+    v = float(score_ref[cand[min(budget, len(cand)) - 1]])
+    tol = rel_tol * max(1.0, abs(v))
+    amb = {b for b in cand if abs(float(score_ref[b]) - v) <= tol}
+    assert (gpu - amb) == (ref - amb), f"selection differs outside near-ties: {gpu ^ ref}"
+    assert len(gpu & amb) == len(ref & amb)
+    return len(amb)
+
+
+def to_dev(x, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    return t if dtype is None else t.to(dtype)

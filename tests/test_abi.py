@@ -1,0 +1,146 @@
+"""The C ABI: the library loads, exports every entry point the header declares,
+and its host-side checks reject bad arguments before anything is launched
+(these calls never reach the GPU, so they run on any machine)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvs.h")
+
+
+def _lib():
+    from heavy_hitter_eviction_amd import build as B
+    if not os.path.exists(B.OUT):
+        B.build()
+    from heavy_hitter_eviction_amd import api
+    return api
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"KVS_API\s+[\w\s\*]+?\b(kvs_\w+)\s*\(", text)
+
+
+def test_header_declares_the_entry_points():
+    names = set(declared_functions())
+    for n in ("kvs_encode_fp8", "kvs_decode_attn_scored", "kvs_update_sidecar", "kvs_select_blocks",
+              "kvs_append_kv", "kvs_decode_workspace_bytes", "kvs_cache_bytes", "kvs_status_str",
+              "kvs_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    api = _lib()
+    for name in declared_functions():
+        assert hasattr(api.LIB, name), name
+    assert set(api.EXPORTED) == set(declared_functions())
+    assert api.version().startswith("libkvs")
+    assert api.status_str(api.KVS_EWS) == "workspace too small"
+
+
+def _geom(api, **kw):
+    base = dict(batch=2, n_q_heads=16, n_kv_heads=4, head_dim=128, capacity=256, window=0, ring=0,
+                n_blocks_max=16, kv_dtype=api.KVS_BF16, q_dtype=api.KVS_BF16, softmax_scale=0.088388)
+    base.update(kw)
+    return api.Geom(*[base[f] for f, _ in api.Geom._fields_])
+
+
+def _decode(api, g, ws_bytes=1 << 20, **ptrs):
+    P = lambda v: ctypes.c_void_p(v) if v is not None else None  # noqa: E731
+    d = dict(q=0x1000, k=0x2000, v=0x3000, ks=None, vs=None, pos=None, cur=0x4000, keep=None,
+             out=0x5000, mass=0x6000, ws=0x7000)
+    d.update(ptrs)
+    return api.LIB.kvs_decode_attn_scored(ctypes.byref(g), P(d["q"]), P(d["k"]), P(d["v"]), P(d["ks"]),
+                                          P(d["vs"]), P(d["pos"]), P(d["cur"]), P(d["keep"]),
+                                          P(d["out"]), P(d["mass"]), P(d["ws"]), ws_bytes, None)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("n_q_heads", 15, "KVS_EINVAL"),
+    ("n_q_heads", 80, "KVS_ENOTIMPL"),      # group of 20 query heads per KV head
+    ("capacity", 100, "KVS_EINVAL"),
+    ("capacity", 0, "KVS_EINVAL"),
+    ("window", -1, "KVS_EINVAL"),
+    ("ring", 2, "KVS_EINVAL"),
+    ("n_blocks_max", 8, "KVS_EINVAL"),      # linear cache needs NBmax >= C/16
+    ("head_dim", 96, "KVS_EDTYPE"),
+    ("q_dtype", 0, "KVS_EDTYPE"),           # bf16 cache with an f32 query
+    ("kv_dtype", 7, "KVS_EDTYPE"),
+    ("softmax_scale", 0.0, "KVS_EINVAL"),
+    ("softmax_scale", float("inf"), "KVS_EINVAL"),
+])
+def test_bad_geometry_is_rejected(field, value, code):
+    api = _lib()
+    g = _geom(api, **{field: value})
+    assert _decode(api, g) == getattr(api, code)
+    n = ctypes.c_size_t()
+    assert api.LIB.kvs_decode_workspace_bytes(ctypes.byref(g), ctypes.byref(n)) == getattr(api, code)
+
+
+def test_dtype_flag_must_match_the_buffers():
+    """Context Optimization, Flag Ordering: an FP8 cache without scale buffers,
+    or a float cache handed scale buffers, is refused."""
+    api = _lib()
+    g = _geom(api, kv_dtype=api.KVS_FP8_E4M3)
+    assert _decode(api, g) == api.KVS_EINVAL
+    g = _geom(api)
+    assert _decode(api, g, ks=0x8000, vs=0x9000) == api.KVS_EINVAL
+
+
+def test_window_with_keep_mask_is_rejected_and_ring_needs_positions():
+    api = _lib()
+    assert _decode(api, _geom(api, window=64), keep=0xA000) == api.KVS_EINVAL
+    assert _decode(api, _geom(api, ring=1)) == api.KVS_EINVAL
+    assert _decode(api, _geom(api), pos=0xB000) == api.KVS_EINVAL
+
+
+def test_alignment_and_workspace_checks():
+    api = _lib()
+    g = _geom(api)
+    assert _decode(api, g, q=0x1004) == api.KVS_EALIGN
+    assert _decode(api, g, mass=0x6008) == api.KVS_EALIGN
+    need = ctypes.c_size_t()
+    assert api.LIB.kvs_decode_workspace_bytes(ctypes.byref(g), ctypes.byref(need)) == 0
+    assert need.value > 0
+    assert _decode(api, g, ws_bytes=need.value - 1) == api.KVS_EWS
+    assert _decode(api, g, cur=None) == api.KVS_EINVAL
+
+
+def test_cache_bytes_closed_form():
+    api = _lib()
+    g = _geom(api, kv_dtype=api.KVS_FP8_E4M3, ring=1, n_blocks_max=64)
+    kv, sc, pos = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    assert api.LIB.kvs_cache_bytes(ctypes.byref(g), ctypes.byref(kv), ctypes.byref(sc), ctypes.byref(pos)) == 0
+    assert kv.value == 2 * 4 * 256 * 128 and sc.value == 2 * 256 * 4 and pos.value == 2 * 256 * 4
+
+
+def test_other_entry_points_reject_bad_arguments():
+    api = _lib()
+    L = api.LIB
+    vp = ctypes.c_void_p
+    assert L.kvs_encode_fp8(vp(0x1000), 5, 4, 16, vp(0x2000), vp(0x3000), None) == api.KVS_EDTYPE
+    assert L.kvs_encode_fp8(vp(0x1000), 0, -1, 16, vp(0x2000), vp(0x3000), None) == api.KVS_EINVAL
+    assert L.kvs_encode_fp8(vp(0x1000), 0, 0, 16, vp(0x2000), vp(0x3000), None) == api.KVS_OK
+    assert L.kvs_encode_fp8(vp(0x1001), 0, 4, 16, vp(0x2000), vp(0x3000), None) == api.KVS_EALIGN
+    ok = [vp(0x1000)] * 5
+    assert L.kvs_update_sidecar(*ok, 2, 16, 64, 0, 1.5, None) == api.KVS_EINVAL
+    assert L.kvs_update_sidecar(*ok, 2, 16, 0, 0, 0.5, None) == api.KVS_EINVAL
+    assert L.kvs_update_sidecar(*ok, 2, 16, 64, -1, 0.5, None) == api.KVS_EINVAL
+    sel = lambda **kw: L.kvs_select_blocks(vp(0x1000), None, vp(0x2000), kw.get("B", 2), 16,  # noqa: E731
+                                           kw.get("budget", 4), kw.get("recent", 16), kw.get("sinks", 0),
+                                           vp(0x3000), vp(0x4000), vp(0x5000), None)
+    assert sel(recent=0) == api.KVS_EINVAL
+    assert sel(budget=-1) == api.KVS_EINVAL
+    assert sel(sinks=-4) == api.KVS_EINVAL
+    assert sel(B=0) == api.KVS_EINVAL
+    g = _geom(api, kv_dtype=api.KVS_FP8_E4M3)
+    app = lambda g, **kw: L.kvs_append_kv(ctypes.byref(g), vp(0x1000), vp(0x2000), kw.get("src", 0), 4,  # noqa: E731
+                                          vp(0x3000), vp(0x4000), vp(0x5000), vp(0x6000),
+                                          kw.get("ks"), kw.get("vs"), kw.get("pos"), None)
+    assert app(g) == api.KVS_EINVAL                     # FP8 cache without scale buffers
+    assert app(_geom(api), src=0) == api.KVS_EDTYPE     # f32 rows into a bf16 cache
+    assert app(g, src=3, ks=vp(0x7000), vs=vp(0x8000)) == api.KVS_EDTYPE

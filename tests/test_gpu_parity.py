@@ -1,0 +1,299 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on
+the same seeded inputs, at sizes that span several tiles, several partitions
+and ragged tails."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from heavy_hitter_eviction_amd import synth
+from oracle import kvs_oracle as orc
+from tests import gpu_support as gs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def api():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from heavy_hitter_eviction_amd import api as _api
+    return _api
+
+
+def _rows(shape, key):
+    return synth.normal(shape, key, "cpu").numpy()
+
+
+# ---------------------------------------------------------------- FP8 encode
+
+def test_encode_fp8_bit_exact(api):
+    rng = np.random.default_rng(7)
+    rows = (rng.standard_normal((300, 1024)) * rng.uniform(1e-3, 1e3, (300, 1))).astype(np.float32)
+    rows[0] = 0.0
+    rows[1, :10] = -0.0
+    rows[1, 10:] = 0.0
+    rows[2] = np.where(np.arange(1024) % 2 == 0, 240.0, -3.5)       # scale exactly 1.0
+    t = orc.e4m3_table()
+    mids = ((t[:0x7E] + t[1:0x7F]) / 2).astype(np.float32)          # exact E4M3 midpoints
+    rows[3, :126] = mids
+    rows[3, 126:] = 0.0
+    rows[3, 200] = 240.0
+    rows[4, :] = rng.standard_normal(1024).astype(np.float32) * 1e-3
+    rows[4, 0] = 448.0 * 240.0 / 240.0
+    codes, scales = api.encode_fp8(gs.to_dev(rows))
+    ref_codes, ref_scales = orc.fp8_encode_rows(rows)
+    assert np.array_equal(scales.cpu().numpy(), ref_scales)
+    got = codes.cpu().numpy()
+    assert np.array_equal(got, ref_codes), f"{(got != ref_codes).sum()} codes differ"
+    # bf16 source rows are widened exactly first
+    rb = torch.from_numpy(rows[5:40]).to(torch.bfloat16)
+    codes, scales = api.encode_fp8(rb.cuda())
+    ref_codes, ref_scales = orc.fp8_encode_rows(rb.float().numpy())
+    assert np.array_equal(codes.cpu().numpy(), ref_codes)
+    assert np.array_equal(scales.cpu().numpy(), ref_scales)
+
+
+def test_encode_fp8_odd_row_length(api):
+    rng = np.random.default_rng(19)
+    rows = rng.standard_normal((7, 333)).astype(np.float32)
+    codes, scales = api.encode_fp8(gs.to_dev(rows))
+    rc, rs = orc.fp8_encode_rows(rows)
+    assert np.array_equal(codes.cpu().numpy(), rc) and np.array_equal(scales.cpu().numpy(), rs)
+
+
+# ---------------------------------------------------------------- decode parity
+
+CASES = [
+    # kv,   d,  Hq, Hkv, C,    B, window, ring
+    ("f32", 16, 4, 2, 80, 1, 0, False),
+    ("f32", 64, 8, 8, 160, 2, 0, False),
+    ("f32", 128, 4, 2, 96, 1, 0, False),
+    ("bf16", 128, 16, 4, 1040, 3, 0, False),
+    ("bf16", 64, 32, 2, 512, 2, 0, False),
+    ("bf16", 128, 16, 4, 528, 2, 100, False),
+    ("fp8", 128, 32, 8, 2064, 2, 0, False),
+    ("fp8", 64, 4, 4, 96, 3, 0, False),
+    ("fp8", 128, 16, 4, 400, 2, 37, False),
+]
+
+
+def _build_linear(api, kv, d, Hq, Hkv, C, B, window, seed):
+    geom = api.CacheGeom(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, capacity=C, window=window,
+                         kv_dtype=kv, q_dtype="f32" if kv == "f32" else "bf16")
+    cache = api.KVCache(geom)
+    w = Hkv * d
+    K = _rows((B, C, w), (seed, 1))
+    V = _rows((B, C, w), (seed, 2))
+    src_dt = torch.float32 if kv in ("f32", "fp8") else torch.bfloat16
+    for b in range(B):
+        # in two chunks: a bulk prefill and a few single-row appends
+        n0 = C - 5
+        for lo, hi in ((0, n0), (n0, n0 + 2), (n0 + 2, C)):
+            seqs = torch.full((hi - lo,), b, dtype=torch.int32, device="cuda")
+            pos = torch.arange(lo, hi, dtype=torch.int32, device="cuda")
+            cache.append(gs.to_dev(K[b, lo:hi]).to(src_dt), gs.to_dev(V[b, lo:hi]).to(src_dt), seqs, pos)
+    return geom, cache, K, V
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_decode_matches_oracle(api, case):
+    kv, d, Hq, Hkv, C, B, window, _ = case
+    seed = 41
+    geom, cache, K, V = _build_linear(api, kv, d, Hq, Hkv, C, B, window, seed)
+    rng = np.random.default_rng(seed)
+    qdt = torch.float32 if kv == "f32" else torch.bfloat16
+    ws = torch.empty(api.decode_workspace_bytes(geom), dtype=torch.uint8, device="cuda")
+    scale = orc.softmax_scale(d)
+    for trial in range(3):
+        cur = np.array([C - 1 if trial == 0 else int(rng.integers(0, C)) for _ in range(B)], dtype=np.int32)
+        if trial == 2:
+            cur[0] = 0  # a single key
+        q = torch.from_numpy(_rows((B, Hq, d), (seed, 3, trial))).to(qdt)
+        out = torch.empty_like(q).cuda()
+        mass = torch.zeros((B, geom.nb), dtype=torch.float32, device="cuda")
+        api.decode_attn_scored(cache, q.cuda(), gs.to_dev(cur), out, ws, mass_accum=mass)
+        torch.cuda.synchronize()
+        o_gpu, m_gpu = out.float().cpu().numpy(), mass.cpu().numpy()
+        for b in range(B):
+            i = int(cur[b])
+            Kd = gs.heads(gs.dequant_rows(K[b, :i + 1], kv), Hkv, d)
+            Vd = gs.heads(gs.dequant_rows(V[b, :i + 1], kv), Hkv, d)
+            o_ref, m_ref, pav = gs.oracle_layer(q[b].double().numpy(), Kd, Vd, np.arange(i + 1), i, window,
+                                                None, scale, geom.nb)
+            gs.close_o(o_gpu[b], o_ref, kv, pav)
+            gs.close_mass(m_gpu[b], m_ref, kv)
+            assert abs(m_gpu[b].sum() - Hq) <= 1e-3
+
+
+def test_unscored_output_is_bit_identical_and_runs_are_deterministic(api):
+    for kv, d, Hq, Hkv, C in (("bf16", 128, 16, 4, 1040), ("fp8", 128, 32, 8, 2064), ("f32", 16, 4, 2, 80)):
+        geom, cache, _, _ = _build_linear(api, kv, d, Hq, Hkv, C, 2, 0, 7)
+        qdt = torch.float32 if kv == "f32" else torch.bfloat16
+        q = torch.from_numpy(_rows((2, Hq, d), (7, 9))).to(qdt).cuda()
+        cur = torch.tensor([C - 1, C // 2], dtype=torch.int32, device="cuda")
+        ws = torch.empty(api.decode_workspace_bytes(geom), dtype=torch.uint8, device="cuda")
+        outs, masses = [], []
+        for scored in (True, True, False):
+            out = torch.empty_like(q)
+            mass = torch.zeros((2, geom.nb), dtype=torch.float32, device="cuda") if scored else None
+            api.decode_attn_scored(cache, q, cur, out, ws, mass_accum=mass)
+            outs.append(out.clone())
+            masses.append(mass.clone() if scored else None)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0].view(torch.int16 if kv != "f32" else torch.int32),
+                           outs[2].view(torch.int16 if kv != "f32" else torch.int32))
+        assert torch.equal(outs[0], outs[1]) and torch.equal(masses[0], masses[1])
+
+
+def test_keep_mask_skips_dropped_blocks(api):
+    """Evict-mode masking equals attention over the kept blocks only."""
+    for kv in ("bf16", "fp8"):
+        d, Hq, Hkv, C, B = 128, 16, 4, 640, 2
+        geom, cache, K, V = _build_linear(api, kv, d, Hq, Hkv, C, B, 0, 19)
+        rng = np.random.default_rng(3)
+        alive = rng.random((B, geom.nb)) < 0.5
+        cur = np.array([C - 1, 333], dtype=np.int32)
+        for b in range(B):
+            alive[b, cur[b] // 16] = True
+        words = np.zeros((B, geom.words), dtype=np.int64)
+        for b in range(B):
+            for blk in np.flatnonzero(alive[b]):
+                words[b, blk >> 5] |= 1 << (blk & 31)
+        keep = gs.to_dev(words.astype(np.uint32).view(np.int32))
+        q = torch.from_numpy(_rows((B, Hq, d), (19, 5))).to(torch.bfloat16)
+        out = torch.empty_like(q).cuda()
+        mass = torch.zeros((B, geom.nb), dtype=torch.float32, device="cuda")
+        ws = torch.empty(api.decode_workspace_bytes(geom), dtype=torch.uint8, device="cuda")
+        api.decode_attn_scored(cache, q.cuda(), gs.to_dev(cur), out, ws, mass_accum=mass, keep_mask=keep)
+        torch.cuda.synchronize()
+        for b in range(B):
+            i = int(cur[b])
+            Kd = gs.heads(gs.dequant_rows(K[b, :i + 1], kv), Hkv, d)
+            Vd = gs.heads(gs.dequant_rows(V[b, :i + 1], kv), Hkv, d)
+            o_ref, m_ref, pav = gs.oracle_layer(q[b].double().numpy(), Kd, Vd, np.arange(i + 1), i, 0,
+                                                alive[b], orc.softmax_scale(d), geom.nb)
+            gs.close_o(out[b].float().cpu().numpy(), o_ref, kv, pav)
+            gs.close_mass(mass[b].cpu().numpy(), m_ref, kv)
+
+
+RING_CASES = [
+    # kv,   d,  Hq, Hkv, C,  window, steps
+    ("fp8", 128, 16, 4, 64, 64, 300),
+    ("bf16", 128, 8, 2, 80, 50, 260),
+    ("f32", 16, 4, 2, 32, 0, 100),
+]
+
+
+@pytest.mark.parametrize("case", RING_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_ring_cache_matches_full_masked_reference(api, case):
+    """LLM mechanics III: the slot-reusing cache, masked by absolute position,
+    equals the full masked reference; checked every few steps across wraps."""
+    kv, d, Hq, Hkv, C, window, steps = case
+    B = 2
+    nb = (steps + 15) // 16
+    geom = api.CacheGeom(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, capacity=C, window=window,
+                         ring=True, n_blocks_max=nb, kv_dtype=kv, q_dtype="f32" if kv == "f32" else "bf16")
+    cache = api.KVCache(geom)
+    w = Hkv * d
+    K = _rows((steps, B, w), (5, 1))
+    V = _rows((steps, B, w), (5, 2))
+    Q = _rows((steps, B, Hq, d), (5, 3))
+    src_dt = torch.float32 if kv in ("f32", "fp8") else torch.bfloat16
+    qdt = torch.float32 if kv == "f32" else torch.bfloat16
+    ws = torch.empty(api.decode_workspace_bytes(geom), dtype=torch.uint8, device="cuda")
+    seqs = torch.arange(B, dtype=torch.int32, device="cuda")
+    Kd = np.stack([gs.dequant_rows(K[:, b], kv) for b in range(B)])   # [B, steps, w]
+    Vd = np.stack([gs.dequant_rows(V[:, b], kv) for b in range(B)])
+    scale = orc.softmax_scale(d)
+    checked = 0
+    for i in range(steps):
+        pos = torch.full((B,), i, dtype=torch.int32, device="cuda")
+        cache.append(gs.to_dev(K[i]).to(src_dt), gs.to_dev(V[i]).to(src_dt), seqs, pos)
+        if not (i < 20 or i % 7 == 0 or i >= steps - 3 or i % C in (0, C - 1)):
+            continue
+        q = torch.from_numpy(Q[i]).to(qdt)
+        out = torch.empty_like(q).cuda()
+        mass = torch.zeros((B, nb), dtype=torch.float32, device="cuda")
+        api.decode_attn_scored(cache, q.cuda(), pos, out, ws, mass_accum=mass)
+        torch.cuda.synchronize()
+        eff_w = window if window else C
+        for b in range(B):
+            lo = max(0, i - min(eff_w, C) + 1)
+            o_ref, m_ref, pav = gs.oracle_layer(q[b].double().numpy(), gs.heads(Kd[b, lo:i + 1], Hkv, d),
+                                                gs.heads(Vd[b, lo:i + 1], Hkv, d), np.arange(lo, i + 1), i,
+                                                window, None, scale, nb)
+            gs.close_o(out[b].float().cpu().numpy(), o_ref, kv, pav)
+            gs.close_mass(mass[b].cpu().numpy(), m_ref, kv)
+        checked += 1
+    assert checked > 20
+    ps = cache.pos_of_slot.view(B, C).cpu().numpy()
+    for t in range(C):
+        want = max(p for p in range(steps) if p % C == t) if t < steps else -1
+        assert (ps[:, t] == want).all()
+
+
+# ---------------------------------------------------------------- side-car and selection
+
+def test_sidecar_update_matches_oracle(api):
+    B, nb, T = 3, 100, 64
+    rng = np.random.default_rng(11)
+    dev = dict(device="cuda", dtype=torch.float32)
+    mass = torch.zeros((B, nb), **dev)
+    att, ema, cum = (torch.zeros((B, nb), **dev) for _ in range(3))
+    traj = torch.zeros((B, T, nb), **dev)
+    ref = [orc.SideCar(nb, T) for _ in range(B)]
+    for step in range(70):
+        A = rng.random((B, nb)).astype(np.float32) * 4
+        mass.copy_(torch.from_numpy(A))
+        api.update_sidecar(mass, att, ema, cum, traj, step, 0.5)
+        for b in range(B):
+            ref[b].update(A[b].astype(np.float64), 0.5)
+    torch.cuda.synchronize()
+    assert float(mass.abs().max()) == 0.0
+    for b in range(B):
+        assert np.array_equal(att[b].cpu().numpy(), ref[b].attended.astype(np.float32))
+        assert np.allclose(ema[b].cpu().numpy(), ref[b].ema, rtol=1e-6, atol=1e-6)
+        assert np.allclose(cum[b].cpu().numpy(), ref[b].cum, rtol=1e-6, atol=1e-5)
+        assert np.array_equal(traj[b].cpu().numpy(), ref[b].traj.astype(np.float32))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_select_matches_oracle_exactly(api, seed):
+    rng = np.random.default_rng(seed)
+    B = 4
+    nb = int(rng.integers(40, 3000))
+    score = (np.round(rng.random((B, nb)) * 50) / 50).astype(np.float32)   # many exact ties
+    cur = rng.integers(0, nb * 16, B).astype(np.int32)
+    budget, recent, sinks = int(rng.integers(0, 200)), int(rng.integers(1, 900)), int(rng.integers(0, 40))
+    alive = rng.random((B, nb)) < 0.7 if seed % 2 else None
+    alive_t = None
+    if alive is not None:
+        for b in range(B):
+            alive[b, cur[b] // 16:] = True
+        words = np.zeros((B, (nb + 31) // 32), dtype=np.int64)
+        for b in range(B):
+            for blk in np.flatnonzero(alive[b]):
+                words[b, blk >> 5] |= 1 << (blk & 31)
+        alive_t = gs.to_dev(words.astype(np.uint32).view(np.int32))
+    keep, ids, n = api.select_blocks(gs.to_dev(score), gs.to_dev(cur), budget, recent, sinks, alive=alive_t)
+    torch.cuda.synchronize()
+    keep, ids, n = keep.cpu().numpy(), ids.cpu().numpy(), n.cpu().numpy()
+    for b in range(B):
+        i = int(cur[b])
+        ref = orc.select_blocks(score[b], None if alive is None else alive[b], i, budget, recent, sinks)
+        assert n[b] == len(ref)
+        assert np.array_equal(ids[b, :n[b]], ref)
+        mask = orc.keep_mask_after(ref, i, nb)
+        bits = np.array([(int(keep[b, x >> 5]) >> (x & 31)) & 1 for x in range(nb)], dtype=bool)
+        assert np.array_equal(bits, mask)
+
+
+def test_select_ties_lowest_index(api):
+    score = np.zeros((1, 64), dtype=np.float32)
+    score[0, [3, 9, 20, 33]] = 2.0
+    keep, ids, n = api.select_blocks(gs.to_dev(score), gs.to_dev(np.array([63 * 16], dtype=np.int32)), 3, 1)
+    torch.cuda.synchronize()
+    assert ids[0, :int(n[0])].cpu().tolist() == [3, 9, 20, 63]
