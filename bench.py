@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Scored decode-step benchmark on one MI355X.
+
+Metric: KV GB/s scanned per scored decode step (and % of HBM peak), plus
+blocks scored per second. One step is the whole hot path for every sequence:
+for each scored layer, append the new position's K/V (FP8 encode), run the
+scored attention (partial + combine, block masses added over heads and
+layers); then the side-car update and the heavy-hitter block selection.
+
+The default workload is the 397B-like shape: batch 16, 32 query / 8 KV heads,
+head dim 128, 15 layers, FP8 E4M3 KV with per-position scales, 32768 cached
+tokens, budget 512 blocks + 1024 recent tokens (score-only mode: every valid
+key is read each step). Inputs are seeded synthetic N(0, 1) draws resident in
+HBM before timing starts.
+
+Printed: one JSON line with the step throughput, a roofline entry for the
+dominant kernel (the scored partial kernel, timed with HIP events on the
+stream it runs on) and the float64 oracle timed on the host cores over a
+bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "KV GB/s scanned per scored decode step (% HBM peak) + blocks scored/s"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="397b_fp8")
+    ap.add_argument("--evict", action="store_true", help="feed the keep mask back (evict mode)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def prefill(dec, w, seed):
+    import torch
+
+    from heavy_hitter_eviction_amd import synth
+    src = torch.float32 if w.kv_dtype in ("f32", "fp8") else torch.bfloat16
+    for layer in range(dec.n_layers):
+        for seq in range(w.batch):
+            k = synth.prefill_rows(w, seed, layer, seq, synth.T_K, "cuda").to(src)
+            v = synth.prefill_rows(w, seed, layer, seq, synth.T_V, "cuda").to(src)
+            dec.prefill(layer, seq, k, v)
+            del k, v
+        torch.cuda.synchronize()
+        log(f"prefilled layer {layer + 1}/{dec.n_layers}")
+
+
+def step_inputs(w, seed, n_steps, layers):
+    import torch
+
+    from heavy_hitter_eviction_amd import synth
+    qdt = torch.float32 if w.q_dtype == "f32" else torch.bfloat16
+    src = torch.float32 if w.kv_dtype in ("f32", "fp8") else torch.bfloat16
+    Q, K, V = [], [], []
+    for layer in range(layers):
+        q = synth.step_block(w, seed, layer, 0, synth.T_Q, "cuda")[:n_steps]
+        Q.append(q.reshape(n_steps, w.batch, w.n_q_heads, w.head_dim).to(qdt).contiguous())
+        K.append(synth.step_block(w, seed, layer, 0, synth.T_K, "cuda")[:n_steps].to(src).contiguous())
+        V.append(synth.step_block(w, seed, layer, 0, synth.T_V, "cuda")[:n_steps].to(src).contiguous())
+    return Q, K, V
+
+
+def run_gpu(args, w):
+    import torch
+
+    from heavy_hitter_eviction_amd import api
+    from heavy_hitter_eviction_amd.session import ScoredDecoder
+
+    n_steps = args.warmup + args.steps
+    if n_steps > w.steps:
+        raise SystemExit(f"warmup + steps must be <= {w.steps} for this workload")
+    t0 = time.time()
+    dec = ScoredDecoder(w, evict=args.evict)
+    prefill(dec, w, args.seed)
+    Q, K, V = step_inputs(w, args.seed, n_steps, dec.n_layers)
+    cur = [torch.full((w.batch,), w.context + t, dtype=torch.int32, device="cuda") for t in range(n_steps)]
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t0:.1f}s, workspace {dec.workspace.numel() / 2**20:.1f} MiB")
+
+    L = dec.n_layers
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
+          for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    keep = None
+    for t in range(n_steps):
+        if t == args.warmup:
+            torch.cuda.synchronize()
+            start.record()
+        timed = t >= args.warmup
+        keep = dec.keep if (args.evict and not w.window) else None
+        for layer in range(L):
+            dec.caches[layer].append(K[layer][t], V[layer][t], dec.row_seq, cur[t])
+            if timed:
+                ev[t - args.warmup][layer][0].record()
+            api.decode_attn_scored(dec.caches[layer], Q[layer][t], cur[t], dec.out[layer], dec.workspace,
+                                   mass_accum=dec.mass, keep_mask=keep, phase="partial")
+            if timed:
+                ev[t - args.warmup][layer][1].record()
+            api.decode_attn_scored(dec.caches[layer], Q[layer][t], cur[t], dec.out[layer], dec.workspace,
+                                   mass_accum=dec.mass, keep_mask=keep, phase="combine")
+        dec.close_turn(cur[t])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    part_ms = [a.elapsed_time(b) for row in ev for (a, b) in row]
+    return dec, total_ms, part_ms
+
+
+def oracle_baseline(w, seed, seconds):
+    """Time the float64 oracle (as it stands) on (sequence, layer) units of the
+    same workload at the first timed step: FP8 decode (or bf16 widening) of the
+    held keys and values, explicit-softmax attention and block masses."""
+    import numpy as np
+    import torch
+
+    from heavy_hitter_eviction_amd import synth
+    from oracle import kvs_oracle as orc
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    i = w.context  # first decode position
+    n = i + 1
+    done, elapsed, units = 0, 0.0, []
+    seq = 0
+    while elapsed < seconds and seq < w.batch:
+        layer = 0
+        kr = synth.prefill_rows(w, seed, layer, seq, synth.T_K, "cuda")
+        vr = synth.prefill_rows(w, seed, layer, seq, synth.T_V, "cuda")
+        kn = torch.cat([kr, synth.step_rows(w, seed, layer, 0, synth.T_K, "cuda")[seq:seq + 1]]).cpu().numpy()
+        vn = torch.cat([vr, synth.step_rows(w, seed, layer, 0, synth.T_V, "cuda")[seq:seq + 1]]).cpu().numpy()
+        q = synth.step_rows(w, seed, layer, 0, synth.T_Q, "cuda")[seq].reshape(w.n_q_heads, w.head_dim)
+        q = q.to(torch.bfloat16 if w.q_dtype == "bf16" else torch.float32).double().cpu().numpy()
+        if w.kv_dtype == "fp8":
+            kc, ks = orc.fp8_encode_rows(kn)
+            vc, vs = orc.fp8_encode_rows(vn)
+        t0 = time.perf_counter()
+        if w.kv_dtype == "fp8":
+            Kd, Vd = orc.fp8_decode_rows(kc, ks), orc.fp8_decode_rows(vc, vs)
+        else:
+            Kd = torch.from_numpy(kn).to(torch.bfloat16).double().numpy() if w.kv_dtype == "bf16" else kn.astype(np.float64)
+            Vd = torch.from_numpy(vn).to(torch.bfloat16).double().numpy() if w.kv_dtype == "bf16" else vn.astype(np.float64)
+        Kh = Kd.reshape(n, w.n_kv_heads, w.head_dim).transpose(1, 0, 2)
+        Vh = Vd.reshape(n, w.n_kv_heads, w.head_dim).transpose(1, 0, 2)
+        orc.attend_scored(q, Kh, Vh, np.arange(n), i, w.window, None, orc.softmax_scale(w.head_dim),
+                          w.n_blocks_max)
+        dt = time.perf_counter() - t0
+        elapsed += dt
+        units.append(dt)
+        done += 1
+        seq += 1
+    unit_bytes = n * w.kv_bytes_per_key()
+    gbs = done * unit_bytes / elapsed / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} (sequence, layer) units at position {i} ({n} keys each, "
+                      f"{unit_bytes / 1e6:.1f} MB of KV per unit): dequantise + float64 attention + "
+                      f"block mass, {elapsed:.1f} s; full step would be "
+                      f"{w.batch * w.n_layers} units",
+            "seconds_per_unit": round(elapsed / done, 4)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    root = os.path.dirname(os.path.abspath(__file__))
+    if root not in sys.path:
+        sys.path.insert(0, root)
+    from heavy_hitter_eviction_amd import build as B
+    if not os.path.exists(B.OUT):
+        B.build()
+    from heavy_hitter_eviction_amd import workloads
+    w = workloads.ALL[args.workload]
+
+    dec, total_ms, part_ms = run_gpu(args, w)
+    ms_step = total_ms / args.steps
+    steps_t = range(args.warmup, args.warmup + args.steps)
+    bytes_step = sum(w.kv_bytes_at_step(t) for t in steps_t) / args.steps
+    blocks_step = sum(w.blocks_at_step(t) for t in steps_t) / args.steps
+    value = bytes_step / (ms_step / 1e3) / 1e9
+    # per launch of the partial kernel: one layer, every sequence
+    bytes_launch = bytes_step / w.n_layers
+    part_avg_ms = sum(part_ms) / len(part_ms)
+    achieved = bytes_launch / (part_avg_ms / 1e3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.kv_dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "batch": w.batch, "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+            "layers": w.n_layers, "context": w.context, "kv_dtype": w.kv_dtype, "block_tokens": 16,
+            "window": w.window, "ring": w.ring, "budget_blocks": w.budget_blocks,
+            "recent_tokens": w.recent_tokens, "mode": "evict" if args.evict else "score-only",
+        },
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "blocks_scored_per_s": round(blocks_step / (ms_step / 1e3), 1),
+        "roofline": {
+            "kernel": "kvs_partial",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_launch_us": round(part_avg_ms * 1e3, 2),
+            "bytes_per_launch": int(bytes_launch),
+        },
+    }
+    del dec
+    if not args.no_cpu_baseline:
+        log("timing the float64 oracle on the host")
+        res["cpu_baseline"] = oracle_baseline(w, args.seed, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

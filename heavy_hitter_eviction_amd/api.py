@@ -26,7 +26,7 @@ TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8
 
 EXPORTED = (
     "kvs_cache_bytes", "kvs_encode_fp8", "kvs_append_kv", "kvs_decode_workspace_bytes",
-    "kvs_decode_attn_scored", "kvs_update_sidecar", "kvs_select_blocks", "kvs_status_str",
+    "kvs_decode_attn_scored", "kvs_decode_partial", "kvs_decode_combine", "kvs_update_sidecar", "kvs_select_blocks", "kvs_status_str",
     "kvs_version",
 )
 
@@ -59,6 +59,8 @@ def _load():
         "kvs_append_kv": [G, P, P, I32, I32, P, P, P, P, P, P, P, P],
         "kvs_decode_workspace_bytes": [G, SZP],
         "kvs_decode_attn_scored": [G, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "kvs_decode_partial": [G, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "kvs_decode_combine": [G, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "kvs_update_sidecar": [P, P, P, P, P, I32, I32, I32, I64, F, P],
         "kvs_select_blocks": [P, P, P, I32, I32, I32, I32, I32, P, P, P, P],
     }
@@ -212,8 +214,10 @@ class KVCache:
 
 def decode_attn_scored(cache: KVCache, q: torch.Tensor, cur_pos: torch.Tensor, out: torch.Tensor,
                        workspace: torch.Tensor, mass_accum: torch.Tensor | None = None,
-                       keep_mask: torch.Tensor | None = None, stream=None):
-    """One layer of the scored decode step (kvs_decode_attn_scored)."""
+                       keep_mask: torch.Tensor | None = None, stream=None, phase: str = "both"):
+    """One layer of the scored decode step (kvs_decode_attn_scored). ``phase``
+    "partial" or "combine" runs one of its two phases (kvs_decode_partial,
+    kvs_decode_combine)."""
     g = cache.geom
     _device_check(q, cur_pos, out, workspace, mass_accum, keep_mask)
     qdt = TORCH_DTYPES[g.q_dtype]
@@ -229,11 +233,12 @@ def decode_attn_scored(cache: KVCache, q: torch.Tensor, cur_pos: torch.Tensor, o
         raise ValueError("keep_mask must be int32 (bit words) [B, W]")
     ws_bytes = workspace.numel() * workspace.element_size()
     gc = g.c()
-    _check(LIB.kvs_decode_attn_scored(ctypes.byref(gc), _ptr(q), _ptr(cache.k), _ptr(cache.v),
-                                      _ptr(cache.k_scale), _ptr(cache.v_scale), _ptr(cache.pos_of_slot),
-                                      _ptr(cur_pos), _ptr(keep_mask), _ptr(out), _ptr(mass_accum),
-                                      _ptr(workspace), ws_bytes, _stream(stream)),
-           "kvs_decode_attn_scored")
+    fn = {"both": LIB.kvs_decode_attn_scored, "partial": LIB.kvs_decode_partial,
+          "combine": LIB.kvs_decode_combine}[phase]
+    _check(fn(ctypes.byref(gc), _ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(cache.k_scale),
+              _ptr(cache.v_scale), _ptr(cache.pos_of_slot), _ptr(cur_pos), _ptr(keep_mask), _ptr(out),
+              _ptr(mass_accum), _ptr(workspace), ws_bytes, _stream(stream)),
+           f"kvs_decode ({phase})")
     return out
 
 

@@ -153,11 +153,16 @@ int kvs_decode_workspace_bytes(const kvs_geom* g, size_t* bytes) {
   return KVS_OK;
 }
 
-int kvs_decode_attn_scored(const kvs_geom* g, const void* q, const void* k_cache,
-                           const void* v_cache, const float* k_scale, const float* v_scale,
-                           const int32_t* pos_of_slot, const int32_t* cur_pos,
-                           const uint32_t* keep_mask, void* out, float* mass_accum,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared argument checks and setup of the two decode phases.
+int decode_setup(const kvs_geom* g, const void* q, const void* k_cache, const void* v_cache,
+                 const float* k_scale, const float* v_scale, const int32_t* pos_of_slot,
+                 const int32_t* cur_pos, const uint32_t* keep_mask, void* out, float* mass_accum,
+                 void* workspace, size_t workspace_bytes, Plan* plan, kvs::PartialArgs* a,
+                 kvs::CombineArgs* c, int* kv) {
   int st = check_geom(g);
   if (st) return st;
   const bool fp8 = g->kv_dtype == KVS_FP8_E4M3;
@@ -170,28 +175,64 @@ int kvs_decode_attn_scored(const kvs_geom* g, const void* q, const void* k_cache
     if (p && !aligned16(p)) return KVS_EALIGN;
   const Plan p = make_plan(g);
   if (workspace_bytes < p.total) return KVS_EWS;
+  *plan = p;
   char* ws = (char*)workspace;
-  kvs::PartialArgs a{};
-  a.q = q; a.k = k_cache; a.v = v_cache; a.ks = k_scale; a.vs = v_scale;
-  a.pos_of_slot = pos_of_slot; a.cur_pos = cur_pos; a.keep = keep_mask;
-  a.ws_m = (float*)(ws + p.off_m); a.ws_l = (float*)(ws + p.off_l);
-  a.ws_o = (float*)(ws + p.off_o); a.ws_e = (float*)(ws + p.off_e);
-  a.B = g->batch; a.Hq = g->n_q_heads; a.Hkv = g->n_kv_heads; a.G = p.G; a.C = g->capacity;
-  a.NT = p.NT; a.window = g->window; a.nbmax = g->n_blocks_max;
-  a.kwords = (g->n_blocks_max + 31) / 32; a.tpp = p.tpp; a.nparts = p.nparts;
-  a.scale_log2 = g->softmax_scale * 1.4426950408889634f;
-  const int kv = fp8 ? kvs::KV_FP8 : g->kv_dtype == KVS_BF16 ? kvs::KV_BF16 : kvs::KV_F32;
+  *a = kvs::PartialArgs{};
+  a->q = q; a->k = k_cache; a->v = v_cache; a->ks = k_scale; a->vs = v_scale;
+  a->pos_of_slot = pos_of_slot; a->cur_pos = cur_pos; a->keep = keep_mask;
+  a->ws_m = (float*)(ws + p.off_m); a->ws_l = (float*)(ws + p.off_l);
+  a->ws_o = (float*)(ws + p.off_o); a->ws_e = (float*)(ws + p.off_e);
+  a->B = g->batch; a->Hq = g->n_q_heads; a->Hkv = g->n_kv_heads; a->G = p.G; a->C = g->capacity;
+  a->NT = p.NT; a->window = g->window; a->nbmax = g->n_blocks_max;
+  a->kwords = (g->n_blocks_max + 31) / 32; a->tpp = p.tpp; a->nparts = p.nparts;
+  a->scale_log2 = g->softmax_scale * 1.4426950408889634f;
+  *c = kvs::CombineArgs{};
+  c->ws_m = a->ws_m; c->ws_l = a->ws_l; c->ws_o = a->ws_o; c->ws_e = a->ws_e; c->cur_pos = cur_pos;
+  c->out = out; c->mass = mass_accum;
+  c->B = g->batch; c->Hq = g->n_q_heads; c->D = g->head_dim; c->C = g->capacity; c->NT = p.NT;
+  c->nbmax = g->n_blocks_max; c->tpp = p.tpp; c->nparts = p.nparts;
+  c->n_o_chunks = (g->n_q_heads * g->head_dim + 255) / 256;
+  c->n_mass_chunks = (p.NT + 255) / 256;
+  *kv = fp8 ? kvs::KV_FP8 : g->kv_dtype == KVS_BF16 ? kvs::KV_BF16 : kvs::KV_F32;
+  return KVS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+#define KVS_DECODE_ARGS                                                                          \
+  const kvs_geom *g, const void *q, const void *k_cache, const void *v_cache,                     \
+      const float *k_scale, const float *v_scale, const int32_t *pos_of_slot,                     \
+      const int32_t *cur_pos, const uint32_t *keep_mask, void *out, float *mass_accum,            \
+      void *workspace, size_t workspace_bytes, void *stream
+#define KVS_DECODE_SETUP                                                                         \
+  Plan p;                                                                                        \
+  kvs::PartialArgs a;                                                                            \
+  kvs::CombineArgs c;                                                                            \
+  int kv;                                                                                        \
+  int st = decode_setup(g, q, k_cache, v_cache, k_scale, v_scale, pos_of_slot, cur_pos,           \
+                        keep_mask, out, mass_accum, workspace, workspace_bytes, &p, &a, &c, &kv); \
+  if (st) return st;                                                                             \
   hipStream_t s = (hipStream_t)stream;
+
+int kvs_decode_partial(KVS_DECODE_ARGS) {
+  KVS_DECODE_SETUP
+  return hip_status(kvs::launch_partial(kv, g->head_dim, a, mass_accum != nullptr, g->ring != 0,
+                                        p.lds_partial, s));
+}
+
+int kvs_decode_combine(KVS_DECODE_ARGS) {
+  KVS_DECODE_SETUP
+  (void)kv;
+  return hip_status(kvs::launch_combine(c, g->ring != 0, g->q_dtype == KVS_BF16, s));
+}
+
+int kvs_decode_attn_scored(KVS_DECODE_ARGS) {
+  KVS_DECODE_SETUP
   hipError_t e = kvs::launch_partial(kv, g->head_dim, a, mass_accum != nullptr, g->ring != 0,
                                      p.lds_partial, s);
   if (e != hipSuccess) return KVS_EHIP;
-  kvs::CombineArgs c{};
-  c.ws_m = a.ws_m; c.ws_l = a.ws_l; c.ws_o = a.ws_o; c.ws_e = a.ws_e; c.cur_pos = cur_pos;
-  c.out = out; c.mass = mass_accum;
-  c.B = g->batch; c.Hq = g->n_q_heads; c.D = g->head_dim; c.C = g->capacity; c.NT = p.NT;
-  c.nbmax = g->n_blocks_max; c.tpp = p.tpp; c.nparts = p.nparts;
-  c.n_o_chunks = (g->n_q_heads * g->head_dim + 255) / 256;
-  c.n_mass_chunks = (p.NT + 255) / 256;
   return hip_status(kvs::launch_combine(c, g->ring != 0, g->q_dtype == KVS_BF16, s));
 }
 

@@ -59,12 +59,12 @@ hipError_t launch_encode_fp8(const void* src, int src_bf16, int64_t n_rows, int 
   return hipSuccess;
 }
 
-// One workgroup per appended row: K and V of every KV head of one position.
-// K goes to [seq][g][slot][:]; V to the tile layout [seq][g][slot/16][a][dim][e]
-// with slot % 16 = 4a + e.
+// One workgroup per appended row: K and V of every KV head of one position,
+// written into the fragment-major tile layout (k_tile_offset / v_tile_offset).
 template <int KV>
 __global__ __launch_bounds__(256) void kvs_append_rows(AppendArgs a) {
   __shared__ float red[4];
+  constexpr int eb = KV == KV_F32 ? 4 : KV == KV_BF16 ? 2 : 1;
   const int r = blockIdx.x;
   const int seq = a.row_seq[r];
   const int pos = a.row_pos[r];
@@ -87,21 +87,22 @@ __global__ __launch_bounds__(256) void kvs_append_rows(AppendArgs a) {
     }
   }
   if (a.ring && threadIdx.x == 0) a.pos_of_slot[(size_t)seq * a.C + slot] = pos;
-  const int tile = slot >> 4, aa = (slot & 15) >> 2, e = slot & 3;
+  const int tile = slot >> 4, t = slot & 15;
+  const size_t tile_bytes = (size_t)kTile * a.D * eb;
   for (int i = threadIdx.x; i < n; i += 256) {
     const int g = i / a.D, dim = i - g * a.D;
-    const size_t bg = (size_t)seq * a.Hkv + g;
-    const size_t ko = (bg * a.C + slot) * a.D + dim;
-    const size_t vo = (((bg * (a.C >> 4) + tile) * 4 + aa) * a.D + dim) * 4 + e;
+    const size_t base = (((size_t)seq * a.Hkv + g) * (a.C >> 4) + tile) * tile_bytes;
+    char* kp = (char*)a.k_cache + base + k_tile_offset(t, dim, eb);
+    char* vp = (char*)a.v_cache + base + v_tile_offset(t, dim, a.D, eb);
     if constexpr (KV == KV_FP8) {
-      ((uint8_t*)a.k_cache)[ko] = (uint8_t)encode_with_scale(load_src(a.k_rows, rb + i, a.src_bf16), sk);
-      ((uint8_t*)a.v_cache)[vo] = (uint8_t)encode_with_scale(load_src(a.v_rows, rb + i, a.src_bf16), sv);
+      *(uint8_t*)kp = (uint8_t)encode_with_scale(load_src(a.k_rows, rb + i, a.src_bf16), sk);
+      *(uint8_t*)vp = (uint8_t)encode_with_scale(load_src(a.v_rows, rb + i, a.src_bf16), sv);
     } else if constexpr (KV == KV_BF16) {
-      ((uint16_t*)a.k_cache)[ko] = ((const uint16_t*)a.k_rows)[rb + i];
-      ((uint16_t*)a.v_cache)[vo] = ((const uint16_t*)a.v_rows)[rb + i];
+      *(uint16_t*)kp = ((const uint16_t*)a.k_rows)[rb + i];
+      *(uint16_t*)vp = ((const uint16_t*)a.v_rows)[rb + i];
     } else {
-      ((float*)a.k_cache)[ko] = ((const float*)a.k_rows)[rb + i];
-      ((float*)a.v_cache)[vo] = ((const float*)a.v_rows)[rb + i];
+      *(float*)kp = ((const float*)a.k_rows)[rb + i];
+      *(float*)vp = ((const float*)a.v_rows)[rb + i];
     }
   }
 }

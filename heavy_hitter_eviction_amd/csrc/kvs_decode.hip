@@ -51,35 +51,52 @@ struct TileRegs {
   static constexpr int NCH = D * KvT<KV>::eb / 64;  // 16-byte chunks per lane, K and V each
   u32x4 k[NCH];
   u32x4 v[NCH];
-  f32x4 ks, vs;    // FP8 scales of the lane's 4 tokens
-  int32_t pos[4];  // ring: absolute positions of the lane's 4 tokens
+  f32x4 ks, vs;  // FP8 scales of the lane's 4 tokens
+  int4 pos;      // ring: absolute positions of the lane's 4 tokens
 };
 
+// Buffer resources (base in scalar registers, bounds-checked: reads past
+// num_records return 0) over one (sequence, KV head)'s K and V regions and one
+// sequence's scale and position arrays, plus the lane's constant byte offsets.
+// A tile then costs one scalar offset per load.
+struct TileAddr {
+  __amdgpu_buffer_rsrc_t k, v, ks, vs, pos;
+  uint32_t koff, voff, soff;
+};
+
+constexpr int kRsrcWord3 = 0x00020000;  // raw untyped 32-bit dword access
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// AUX = 2 sets the non-temporal (streaming) cache policy, for bytes read once.
+template <int AUX>
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, AUX));
+}
+
 template <int KV, int D, bool RING>
-__device__ __forceinline__ void load_tile(TileRegs<KV, D>& t, const PartialArgs& a, int b, int g,
-                                          int tile, int lane) {
+__device__ __forceinline__ void load_tile(TileRegs<KV, D>& t, const TileAddr& ad, int tile) {
   constexpr int eb = KvT<KV>::eb;
   constexpr int NCH = TileRegs<KV, D>::NCH;
-  const int j = lane & 15, kg = lane >> 4;
-  const size_t bg = (size_t)b * a.Hkv + g;
-  // K: this lane's token is row j of the tile; chunk i covers row bytes [64 i + 16 kg, +16).
-  const char* krow = (const char*)a.k + ((bg * a.C + (size_t)tile * kTile + j) * D) * eb;
+  constexpr uint32_t tile_bytes = (uint32_t)kTile * D * eb;
+  const uint32_t so = (uint32_t)tile * tile_bytes;
+  // K and V tiles are stored fragment-major: chunk i of every lane is one
+  // contiguous 1 KiB run (lane-major), so each load instruction reads whole
+  // cache lines, streamed past the caches (non-temporal).
 #pragma unroll
-  for (int i = 0; i < NCH; ++i)
-    t.k[i] = __builtin_nontemporal_load((const u32x4*)(krow + 64 * i + 16 * kg));
-  // V: tile layout [4][D][4]; this lane reads [kg][(D/16) j .. +D/16][0..3], contiguous.
-  const char* vt = (const char*)a.v + ((bg * (a.C / kTile) + tile) * (size_t)(kTile * D)) * eb;
-  const char* vl = vt + ((size_t)kg * D + (D / 16) * j) * 4 * eb;
+  for (int i = 0; i < NCH; ++i) t.k[i] = bload16<2>(ad.k, ad.koff + 1024 * i, so);
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) t.v[i] = __builtin_nontemporal_load((const u32x4*)(vl + 16 * i));
-  const size_t slot0 = (size_t)b * a.C + (size_t)tile * kTile + 4 * kg;
+  for (int i = 0; i < NCH; ++i) t.v[i] = bload16<2>(ad.v, ad.voff + 1024 * i, so);
+  const uint32_t ss = (uint32_t)tile * (kTile * 4);
   if constexpr (KV == KV_FP8) {
-    t.ks = *(const f32x4*)(a.ks + slot0);
-    t.vs = *(const f32x4*)(a.vs + slot0);
+    t.ks = __builtin_bit_cast(f32x4, bload16<0>(ad.ks, ad.soff, ss));
+    t.vs = __builtin_bit_cast(f32x4, bload16<0>(ad.vs, ad.soff, ss));
   }
   if constexpr (RING) {
-    const int4 p = *(const int4*)(a.pos_of_slot + slot0);
-    t.pos[0] = p.x; t.pos[1] = p.y; t.pos[2] = p.z; t.pos[3] = p.w;
+    const u32x4 p = bload16<0>(ad.pos, ad.soff, ss);
+    t.pos = make_int4((int)p[0], (int)p[1], (int)p[2], (int)p[3]);
   }
 }
 
@@ -92,14 +109,21 @@ __device__ __forceinline__ int qk_dim(int t, int kg) {
   return (t / EPC) * 4 * EPC + kg * EPC + t % EPC;
 }
 
+template <int KV>
+struct Pipe {
+  static constexpr int depth = KV == KV_FP8 ? 3 : 2;  // tiles in flight per wave
+};
+
 template <int KV, int D, bool SCORED, bool RING>
 __global__ __launch_bounds__(256, 2) void kvs_partial(PartialArgs a) {
-  constexpr int NCH = TileRegs<KV, D>::NCH;
   constexpr int NSUB = RING ? 2 : 1;
   constexpr int NC = D / 16;  // PV output chunks of 16 dims
+  constexpr int NBUF = Pipe<KV>::depth;
+  constexpr int eb = KvT<KV>::eb;
   extern __shared__ float lds[];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 15, kg = lane >> 4;
   const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = a.G;
@@ -131,21 +155,34 @@ __global__ __launch_bounds__(256, 2) void kvs_partial(PartialArgs a) {
     if (a.window > 0) tb = max(tb, max(lo, 0) / kTile);
   }
 
-  // Query operand (B of the QK MFMA): lane holds Q[h][dim(t, kg)], zeros for padding heads.
-  const int hq = g * G + h;
+  // Query operand (B of the QK MFMA): lane holds Q[h][dim(t, kg)], zeros for
+  // padding heads. Runs of EPC consecutive dims are read with 16-byte loads.
+  const int hq = g * G + min(h, G - 1);
   constexpr int QN = D / 4;
   float qf[QN];
+  {
+    constexpr int EPC = 16 / eb;                  // dims per run
+    constexpr int QE = KV == KV_F32 ? 4 : 2;      // query element bytes
+    const char* qrow = (const char*)a.q + ((size_t)b * a.Hq + hq) * D * QE;
 #pragma unroll
-  for (int t = 0; t < QN; ++t) {
-    float x = 0.0f;
-    if (hreal) {
-      const size_t qi = ((size_t)b * a.Hq + hq) * D + qk_dim<KV>(t, kg);
-      if constexpr (KV == KV_F32)
-        x = ((const float*)a.q)[qi];
-      else
-        x = bits_to_f32((uint32_t)((const uint16_t*)a.q)[qi] << 16);
+    for (int r0 = 0; r0 < QN; r0 += EPC) {
+      const int d0 = qk_dim<KV>(r0, kg);
+#pragma unroll
+      for (int c = 0; c < EPC * QE / 16; ++c) {
+        const u32x4 w = *(const u32x4*)(qrow + (size_t)d0 * QE + 16 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (QE == 4) {
+            qf[r0 + 4 * c + e] = bits_to_f32(w[e]);
+          } else {
+            qf[r0 + 8 * c + 2 * e] = bf16_lo(w[e]);
+            qf[r0 + 8 * c + 2 * e + 1] = bf16_hi(w[e]);
+          }
+        }
+      }
     }
-    qf[t] = x;
+#pragma unroll
+    for (int t = 0; t < QN; ++t) qf[t] = hreal ? qf[t] : 0.0f;
   }
   bf16x8 qb[D / 32 > 0 ? D / 32 : 1];
   if constexpr (KV != KV_F32) {
@@ -166,161 +203,228 @@ __global__ __launch_bounds__(256, 2) void kvs_partial(PartialArgs a) {
   const int lap_i = RING ? i_cur / a.C : 0;
   const int lap_base = lap_i * a.C;
 
-  auto tile_kept = [&](int tile) -> bool {
-    if constexpr (RING) {
-      return true;
-    } else {
-      if (a.keep == nullptr) return true;
-      if (tile >= a.nbmax) return true;
-      return (a.keep[(size_t)b * a.kwords + (tile >> 5)] >> (tile & 31)) & 1u;
+  const uint32_t* keep_b = a.keep ? a.keep + (size_t)b * a.kwords : nullptr;
+  // Next tile of this wave (stride 4) whose block is kept, or te.
+  auto next_kept = [&](int t) -> int {
+    if constexpr (!RING) {
+      if (keep_b != nullptr) {
+        while (t < te && t < a.nbmax && !((keep_b[t >> 5] >> (t & 31)) & 1u)) t += 4;
+      }
     }
+    return t;
   };
 
-  TileRegs<KV, D> cur, nxt;
-  int tile = tb + wave;
-  while (tile < te && !tile_kept(tile)) tile += 4;
-  if (tile < te) load_tile<KV, D, RING>(cur, a, b, g, tile, lane);
+  TileAddr ad;
+  {
+    const size_t bg = (size_t)b * a.Hkv + g;
+    const uint32_t region = (uint32_t)((size_t)a.C * D * eb);
+    ad.k = make_rsrc((const char*)a.k + bg * region, region);
+    ad.v = make_rsrc((const char*)a.v + bg * region, region);
+    const uint32_t sbytes = (uint32_t)a.C * 4;
+    ad.ks = make_rsrc(a.ks ? a.ks + (size_t)b * a.C : nullptr, a.ks ? sbytes : 0);
+    ad.vs = make_rsrc(a.vs ? a.vs + (size_t)b * a.C : nullptr, a.vs ? sbytes : 0);
+    ad.pos = make_rsrc(a.pos_of_slot ? a.pos_of_slot + (size_t)b * a.C : nullptr, a.pos_of_slot ? sbytes : 0);
+    ad.koff = (uint32_t)(16 * lane);
+    ad.voff = (uint32_t)(16 * lane);
+    ad.soff = (uint32_t)(16 * kg);
+  }
 
-  while (tile < te) {
-    int ntile = tile + 4;
-    while (ntile < te && !tile_kept(ntile)) ntile += 4;
-    if (ntile < te) load_tile<KV, D, RING>(nxt, a, b, g, ntile, lane);
-
-    // ---- validity of the lane's 4 tokens (rows 4 kg + r of the tile) ----
+  // ---- one tile: online softmax, block sums, PV ----
+  auto process = [&](TileRegs<KV, D>& cur, const int tile) {
     bool valid[4];
     int sub[4];
+    bool all_valid, any_valid;
+    if constexpr (RING) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if constexpr (RING) {
+      for (int r = 0; r < 4; ++r) {
         const int p = cur.pos[r];
         bool v = p >= 0 && p <= i_cur && p >= lo;
-        if (v && a.keep != nullptr) {
+        if (v && keep_b != nullptr) {
           const int blk = p >> 4;
-          v = blk >= a.nbmax || ((a.keep[(size_t)b * a.kwords + (blk >> 5)] >> (blk & 31)) & 1u);
+          v = blk >= a.nbmax || ((keep_b[blk >> 5] >> (blk & 31)) & 1u);
         }
         valid[r] = v;
         sub[r] = ((p >= lap_base) ? lap_i : lap_i - 1) & 1;
-      } else {
-        const int p = tile * kTile + 4 * kg + r;
+      }
+      all_valid = wave_all(valid[0] && valid[1] && valid[2] && valid[3]);
+      any_valid = wave_any(valid[0] || valid[1] || valid[2] || valid[3]);
+    } else {
+      const int p0 = tile * kTile;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int p = p0 + 4 * kg + r;
         valid[r] = p <= i_cur && p >= lo;
         sub[r] = 0;
       }
+      all_valid = p0 >= lo && p0 + kTile - 1 <= i_cur;  // uniform
+      any_valid = true;                                  // tb..te only holds readable tiles
     }
-    const bool lane_all = valid[0] && valid[1] && valid[2] && valid[3];
-    const bool lane_any = valid[0] || valid[1] || valid[2] || valid[3];
-    if (wave_any(lane_any)) {
-      const bool all_valid = wave_all(lane_all);
+    if (!any_valid) return;
 
-      // ---- S^T = K Q^T ----
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (KV == KV_F32) {
+    // Codes of keys that are not read are zeroed before use: the cache may hold
+    // anything there, and 0 * NaN would poison the PV product.
+    if (!all_valid) {
+      if constexpr (KV == KV_FP8) {
+        // lane's V bytes: dim-group n, token e at byte 4 n + e
+        const uint32_t m = (valid[0] ? 0x000000FFu : 0u) | (valid[1] ? 0x0000FF00u : 0u) |
+                           (valid[2] ? 0x00FF0000u : 0u) | (valid[3] ? 0xFF000000u : 0u);
 #pragma unroll
-        for (int t = 0; t < QN; ++t)
-          s = __builtin_amdgcn_mfma_f32_16x16x4f32(bits_to_f32(cur.k[t / 4][t % 4]), qf[t], s, 0, 0, 0);
+        for (int i = 0; i < TileRegs<KV, D>::NCH; ++i) cur.v[i] &= m;
       } else if constexpr (KV == KV_BF16) {
+        const uint32_t m0 = (valid[0] ? 0x0000FFFFu : 0u) | (valid[1] ? 0xFFFF0000u : 0u);
+        const uint32_t m1 = (valid[2] ? 0x0000FFFFu : 0u) | (valid[3] ? 0xFFFF0000u : 0u);
+        const u32x4 m = {m0, m1, m0, m1};
 #pragma unroll
-        for (int c = 0; c < D / 32; ++c)
-          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[c]), qb[c], s, 0, 0, 0);
+        for (int i = 0; i < TileRegs<KV, D>::NCH; ++i) cur.v[i] &= m;
       } else {
+        const u32x4 m = {valid[0] ? ~0u : 0u, valid[1] ? ~0u : 0u, valid[2] ? ~0u : 0u, valid[3] ? ~0u : 0u};
 #pragma unroll
-        for (int c = 0; c < D / 32; ++c) {
-          const u32x4 w = cur.k[c >> 1];
-          const u32x2 lo2 = fp8x4_to_bf16x4(w[2 * (c & 1)]);
-          const u32x2 hi2 = fp8x4_to_bf16x4(w[2 * (c & 1) + 1]);
-          const u32x4 kk = {lo2[0], lo2[1], hi2[0], hi2[1]};
-          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kk), qb[c], s, 0, 0, 0);
-        }
+        for (int i = 0; i < TileRegs<KV, D>::NCH; ++i) cur.v[i] &= m;
       }
+    }
 
-      // ---- logits in log2 units, masked ----
-      float tl[4];
+    // ---- S^T = K Q^T ----
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (KV == KV_F32) {
+#pragma unroll
+      for (int t = 0; t < QN; ++t)
+        s = __builtin_amdgcn_mfma_f32_16x16x4f32(bits_to_f32(cur.k[t / 4][t % 4]), qf[t], s, 0, 0, 0);
+    } else if constexpr (KV == KV_BF16) {
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[c]), qb[c], s, 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) {
+        const u32x4 w = cur.k[c >> 1];
+        const u32x2 lo2 = fp8x4_to_bf16x4(w[2 * (c & 1)]);
+        const u32x2 hi2 = fp8x4_to_bf16x4(w[2 * (c & 1) + 1]);
+        const u32x4 kk = {lo2[0], lo2[1], hi2[0], hi2[1]};
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kk), qb[c], s, 0, 0, 0);
+      }
+    }
+
+    // ---- logits in log2 units, masked ----
+    float tl[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float x;
+      if constexpr (KV == KV_FP8) x = s[r] * (cur.ks[r] * a.scale_log2);
+      else x = s[r] * a.scale_log2;
+      tl[r] = (all_valid || valid[r]) ? x : -__builtin_inff();
+    }
+    float mx = fmaxf(fmaxf(tl[0], tl[1]), fmaxf(tl[2], tl[3]));
+    mx = rows_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = fast_exp2(m_run - m_new);
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(tl[r] - m_new);
+
+    float esub0 = 0.f, esub1 = 0.f;
+    if constexpr (NSUB == 2) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float x = s[r] * a.scale_log2;
-        if constexpr (KV == KV_FP8) x = s[r] * (cur.ks[r] * a.scale_log2);
-        tl[r] = valid[r] ? x : -__builtin_inff();
-      }
-      float mx = fmaxf(fmaxf(tl[0], tl[1]), fmaxf(tl[2], tl[3]));
-      mx = rows_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - m_new);
-      float p[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(tl[r] - m_new);
-
-      float esub0 = 0.f, esub1 = 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (NSUB == 2 && sub[r]) esub1 += p[r];
-        else esub0 += p[r];
+        esub0 += sub[r] ? 0.0f : p[r];
+        esub1 += sub[r] ? p[r] : 0.0f;
       }
       esub0 = rows_sum(esub0);
-      if constexpr (NSUB == 2) esub1 = rows_sum(esub1);
-      l_run = l_run * alpha + (esub0 + esub1);
+      esub1 = rows_sum(esub1);
+    } else {
+      esub0 = rows_sum((p[0] + p[1]) + (p[2] + p[3]));
+    }
+    l_run = l_run * alpha + (esub0 + esub1);
 
-      if constexpr (SCORED) {
-        if (kg == 0 && hreal) {
-          const int tlc = tile - t0;
-          e_rec[(tlc * NSUB) * G + h] = esub0;
-          if constexpr (NSUB == 2) e_rec[(tlc * NSUB + 1) * G + h] = esub1;
-          m_rec[tlc * G + h] = m_new;
-        }
+    if constexpr (SCORED) {
+      if (kg == 0 && hreal) {
+        const int tlc = tile - t0;
+        e_rec[(tlc * NSUB) * G + h] = esub0;
+        if constexpr (NSUB == 2) e_rec[(tlc * NSUB + 1) * G + h] = esub1;
+        m_rec[tlc * G + h] = m_new;
       }
+    }
 
-      if (wave_any(alpha != 1.0f)) {
+    if (wave_any(alpha != 1.0f)) {
 #pragma unroll
-        for (int n = 0; n < NC; ++n) oacc[n] *= alpha;
-      }
-      m_run = m_new;
+      for (int n = 0; n < NC; ++n) oacc[n] *= alpha;
+    }
+    m_run = m_new;
 
-      // ---- O^T += V^T P^T ----
-      if constexpr (KV == KV_F32) {
-        float pv[4];
+    // ---- O^T += V^T P^T ----
+    if constexpr (KV == KV_F32) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pv[r] = p[r];
-#pragma unroll
-        for (int n = 0; n < NC; ++n) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int u = 4 * n + r;  // lane's V element: dim (D/16) j + n, token 4 kg + r
-            float vv = bits_to_f32(cur.v[u / 4][u % 4]);
-            if (!all_valid) vv = valid[r] ? vv : 0.0f;
-            oacc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv, pv[r], oacc[n], 0, 0, 0);
-          }
-        }
-      } else {
-        float pw[4];
+      for (int n = 0; n < NC; ++n) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          pw[r] = p[r];
-          if constexpr (KV == KV_FP8) pw[r] = p[r] * cur.vs[r];
+          const int u = 4 * n + r;  // lane's V element: dim (D/16) j + n, token 4 kg + r
+          oacc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(bits_to_f32(cur.v[u / 4][u % 4]), p[r], oacc[n], 0, 0, 0);
         }
-        const u32x2 pb = {pack_bf16x2(pw[0], pw[1]), pack_bf16x2(pw[2], pw[3])};
-        u32x2 vmask = {0xFFFFFFFFu, 0xFFFFFFFFu};
-        if (!all_valid) {
-          vmask[0] = (valid[0] ? 0x0000FFFFu : 0u) | (valid[1] ? 0xFFFF0000u : 0u);
-          vmask[1] = (valid[2] ? 0x0000FFFFu : 0u) | (valid[3] ? 0xFFFF0000u : 0u);
-        }
+      }
+    } else {
+      float pw[4];
 #pragma unroll
-        for (int n = 0; n < NC; ++n) {
-          u32x2 vv;
-          if constexpr (KV == KV_BF16) {
-            // 4 bf16 per n: chunk n/2, dwords 2 (n%2), 2 (n%2) + 1
-            vv[0] = cur.v[n >> 1][2 * (n & 1)];
-            vv[1] = cur.v[n >> 1][2 * (n & 1) + 1];
-          } else {
-            // 4 codes per n: chunk n/4, dword n%4
-            vv = fp8x4_to_bf16x4(cur.v[n >> 2][n & 3]);
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (KV == KV_FP8) pw[r] = p[r] * cur.vs[r];
+        else pw[r] = p[r];
+      }
+      bf16x4 pb;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pb[r] = (__bf16)pw[r];
+#pragma unroll
+      for (int n = 0; n < NC; ++n) {
+        u32x2 vv;
+        if constexpr (KV == KV_BF16) {
+          // 4 bf16 per n: chunk n/2, dwords 2 (n%2), 2 (n%2) + 1
+          vv[0] = cur.v[n >> 1][2 * (n & 1)];
+          vv[1] = cur.v[n >> 1][2 * (n & 1) + 1];
+        } else {
+          // 4 codes per n: chunk n/4, dword n%4
+          vv = fp8x4_to_bf16x4(cur.v[n >> 2][n & 3]);
+        }
+        oacc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vv),
+                                                            __builtin_bit_cast(s16x4, pb), oacc[n], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- software pipeline: NBUF tiles of this wave in flight ----
+  // Loads are issued unconditionally (an exhausted slot re-reads the wave's
+  // last tile, which is still in cache) so the load count between a tile's
+  // issue and its use is the same on every path.
+  int nexti = next_kept(tb + wave);
+  if (nexti < te) {
+    TileRegs<KV, D> buf[NBUF];
+    int tq[NBUF];
+    int last = nexti;
+#pragma unroll
+    for (int s = 0; s < NBUF - 1; ++s) {
+      const bool ok = nexti < te;
+      tq[s] = ok ? nexti : -1;
+      load_tile<KV, D, RING>(buf[s], ad, ok ? nexti : last);
+      if (ok) {
+        last = nexti;
+        nexti = next_kept(nexti + 4);
+      }
+    }
+    tq[NBUF - 1] = -1;
+    bool more = true;
+    while (more) {
+#pragma unroll
+      for (int s = 0; s < NBUF; ++s) {
+        if (more) {
+          const int ls = (s + NBUF - 1) % NBUF;
+          const bool ok = nexti < te;
+          tq[ls] = ok ? nexti : -1;
+          load_tile<KV, D, RING>(buf[ls], ad, ok ? nexti : last);
+          if (ok) {
+            last = nexti;
+            nexti = next_kept(nexti + 4);
           }
-          vv[0] &= vmask[0];
-          vv[1] &= vmask[1];
-          oacc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vv),
-                                                              __builtin_bit_cast(s16x4, pb), oacc[n], 0, 0, 0);
+          if (tq[s] < 0) more = false;
+          else process(buf[s], tq[s]);
         }
       }
     }
-    cur = nxt;
-    tile = ntile;
   }
 
   // ---- merge the four waves of the partition ----

@@ -94,6 +94,26 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
   return r;
 }
 
+// ---------------------------------------------------------------------------
+// Cache tile layout. A tile is 16 consecutive slots of one (sequence, KV head),
+// 16*D elements of K and as many of V. Both are stored fragment-major: the
+// 16-byte chunk i that MFMA lane l (l = 16*kg + j) of the decode kernel reads
+// sits at byte 1024*i + 16*l of the tile, so one load instruction covers one
+// contiguous KiB.
+//   K: lane (j, kg) chunk i holds slot j, row bytes [64 i + 16 kg, +16).
+//   V: lane (j, kg) chunk i holds bytes [16 i, +16) of the run
+//      {slot 4 kg + e, dim (D/16) j + n : n < D/16, e < 4}, element 4 n + e.
+// Byte offsets inside the tile of element (slot t, dim x), element size eb:
+__host__ __device__ __forceinline__ uint32_t k_tile_offset(int t, int x, int eb) {
+  const int xb = x * eb;
+  return (uint32_t)(((xb / 64 * 4 + (xb % 64) / 16) * 16 + t) * 16 + xb % 16);
+}
+__host__ __device__ __forceinline__ uint32_t v_tile_offset(int t, int x, int D, int eb) {
+  const int kg = t / 4, e = t % 4, j = x / (D / 16), n = x % (D / 16);
+  const int ub = (4 * n + e) * eb;
+  return (uint32_t)(((ub / 16 * 4 + kg) * 16 + j) * 16 + ub % 16);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
 }

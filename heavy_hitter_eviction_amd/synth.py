@@ -78,18 +78,23 @@ def prefill_rows(w: Workload, seed: int, layer: int, seq: int, tensor: int, devi
     return rows.contiguous()
 
 
-def step_rows(w: Workload, seed: int, layer: int, step: int, tensor: int, device="cpu") -> torch.Tensor:
-    """Per-step rows for every sequence: queries ``[B, Hq*d]`` for ``T_Q``, the
-    new position's K or V ``[B, Hkv*d]`` for ``T_K`` / ``T_V``."""
+def step_block(w: Workload, seed: int, layer: int, chunk: int, tensor: int, device="cpu") -> torch.Tensor:
+    """Per-step rows for the decode steps ``chunk*256 .. chunk*256+255`` (fewer
+    in the last chunk): ``[n, B, Hq*d]`` queries for ``T_Q``, or the new
+    positions' K or V ``[n, B, Hkv*d]`` for ``T_K`` / ``T_V``."""
     width = (w.n_q_heads if tensor == T_Q else w.n_kv_heads) * w.head_dim
-    chunk = step // STEP_CHUNK
     n = min(STEP_CHUNK, w.steps - chunk * STEP_CHUNK)
     block = normal((n, w.batch, width), (seed, _tag(w), tensor, layer, 1 << 20 | chunk), device)
-    rows = block[step - chunk * STEP_CHUNK]
     if w.planted and tensor == T_Q:
         u = _directions(w, seed, device) * plant_gain(w.head_dim)
-        rows = rows + u.repeat_interleave(w.group, dim=1).reshape(w.batch, -1)
-    return rows.contiguous()
+        block = block + u.repeat_interleave(w.group, dim=1).reshape(1, w.batch, -1)
+    return block.contiguous()
+
+
+def step_rows(w: Workload, seed: int, layer: int, step: int, tensor: int, device="cpu") -> torch.Tensor:
+    """The rows of one decode step (see ``step_block``)."""
+    chunk = step // STEP_CHUNK
+    return step_block(w, seed, layer, chunk, tensor, device)[step - chunk * STEP_CHUNK].contiguous()
 
 
 def as_dtype(x: torch.Tensor, dtype: str) -> torch.Tensor:

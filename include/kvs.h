@@ -90,10 +90,15 @@ typedef struct {
 } kvs_geom;
 
 /*
- * Cache layout (one layer; K and V are separate buffers):
- *   K   [B][Hkv][C][d]                 slot-major rows of d elements
- *   V   [B][Hkv][C/16][4][d][4]        inside each 16-slot tile, slot 4a+e
- *                                      and dimension j live at [a][j][e]
+ * Cache layout (one layer; K and V are separate buffers of the same size):
+ *   K, V   [B][Hkv][C/16] tiles of 16 slots x d elements, each tile stored
+ *          fragment-major so the decode kernel reads it in whole KiB runs.
+ *          With element size s (4, 2 or 1 bytes), slot t (0..15) and head
+ *          dimension x inside a tile live at byte
+ *            K: 16*(16*(4*(x*s/64) + (x*s%64)/16) + t) + x*s%16
+ *            V: with a = t/4, e = t%4, j = x/(d/16), n = x%(d/16), u = (4n+e)*s:
+ *               16*(16*(4*(u/16) + a) + j) + u%16
+ *          Caches are meant to be written through kvs_append_kv.
  *   k_scale, v_scale  [B][C] float     FP8 caches only: one scale per
  *                                      (sequence, slot) covering all Hkv*d
  *                                      values of that position
@@ -186,6 +191,29 @@ KVS_API int kvs_decode_attn_scored(const kvs_geom* geom, const void* q, const vo
                            const int32_t* pos_of_slot, const int32_t* cur_pos,
                            const uint32_t* keep_mask, void* out, float* mass_accum,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kvs_decode_partial, kvs_decode_combine -- the two phases of
+ * kvs_decode_attn_scored, with the same arguments and checks. The partial
+ * phase reads the cache and leaves, per (sequence, query head, partition of
+ * slots), the partition's running max, sum of exponentials and unnormalised
+ * output, plus per-block sums of the post-softmax weights, in ``workspace``;
+ * the combine phase turns them into ``out`` and adds the normalised block
+ * masses into ``mass_accum``. Calling partial then combine on one stream, with
+ * the same arguments and workspace, is exactly kvs_decode_attn_scored; the
+ * split lets a caller time or overlap the phases. The combine phase does not
+ * read the cache buffers but validates them like the partial phase.
+ */
+KVS_API int kvs_decode_partial(const kvs_geom* geom, const void* q, const void* k_cache,
+                               const void* v_cache, const float* k_scale, const float* v_scale,
+                               const int32_t* pos_of_slot, const int32_t* cur_pos,
+                               const uint32_t* keep_mask, void* out, float* mass_accum,
+                               void* workspace, size_t workspace_bytes, void* stream);
+KVS_API int kvs_decode_combine(const kvs_geom* geom, const void* q, const void* k_cache,
+                               const void* v_cache, const float* k_scale, const float* v_scale,
+                               const int32_t* pos_of_slot, const int32_t* cur_pos,
+                               const uint32_t* keep_mask, void* out, float* mass_accum,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * kvs_update_sidecar -- close one turn (Context views at marginal cost,
