@@ -10,8 +10,11 @@
 namespace {
 
 constexpr int kTileSlots = 16;
-constexpr int kTargetWorkgroups = 2048;  // ~8 per CU on 256 CUs
-constexpr int kMaxTilesPerPart = 256;
+// One round of resident decode workgroups on MI355X: 256 CUs x 3 (the bf16
+// and FP8 kernels hold 3 waves per SIMD). Fewer, longer partitions measured
+// faster than several rounds: no tail of partly filled rounds.
+constexpr int kTargetWorkgroups = 768;
+constexpr int kLdsBudgetFloats = 12288;  // 48 KiB per decode workgroup
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -60,10 +63,14 @@ Plan make_plan(const kvs_geom* g) {
   if (ptarget < 1) ptarget = 1;
   int tpp = (p.NT + ptarget - 1) / ptarget;
   if (tpp < 4) tpp = 4;
-  // combine keeps [Hq][P] weights in LDS: bound P so that stays <= 48 KiB
-  const int pmax = 12288 / g->n_q_heads;
+  // the partial kernel keeps per-tile block sums of its partition in LDS:
+  // bound the partition so its LDS stays <= 48 KiB (3 workgroups per CU)
+  const int lds_fixed = 8 * p.G + 4 * p.G * g->head_dim;
+  const int tpp_lds = (kLdsBudgetFloats - lds_fixed) / (p.G * (p.nsub + 1));
+  if (tpp > tpp_lds) tpp = tpp_lds < 4 ? 4 : tpp_lds;
+  // combine keeps two [Hq][P] float tables in LDS: bound P so they stay <= 48 KiB
+  const int pmax = 6144 / g->n_q_heads;
   while ((p.NT + tpp - 1) / tpp > pmax) tpp *= 2;
-  if (tpp > kMaxTilesPerPart) tpp = kMaxTilesPerPart;
   p.tpp = tpp;
   p.nparts = (p.NT + tpp - 1) / tpp;
   const size_t bh = (size_t)g->batch * g->n_q_heads;
@@ -174,6 +181,7 @@ int decode_setup(const kvs_geom* g, const void* q, const void* k_cache, const vo
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return KVS_EALIGN;
   const Plan p = make_plan(g);
+  if (p.lds_partial > 65536) return KVS_ENOTIMPL;  // partition bookkeeping beyond LDS
   if (workspace_bytes < p.total) return KVS_EWS;
   *plan = p;
   char* ws = (char*)workspace;

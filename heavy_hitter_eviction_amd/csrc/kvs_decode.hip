@@ -134,9 +134,10 @@ __global__ __launch_bounds__(256, 2) void kvs_partial(PartialArgs a) {
 
   const int t0 = part * a.tpp;
   const int t1 = min(t0 + a.tpp, a.NT);
-  const int ntl = t1 - t0;
 
-  // LDS carve-up: per-tile block sums and running maxima, then the wave merge area.
+  // LDS carve-up: per-tile block sums and the running maxima they are relative
+  // to, then the wave merge area.
+  const int ntl = t1 - t0;
   float* e_rec = lds;                                   // [ntl][NSUB][G]
   float* m_rec = e_rec + a.tpp * NSUB * G;              // [ntl][G]
   float* mw = m_rec + a.tpp * G;                        // [4][G]
@@ -151,8 +152,8 @@ __global__ __launch_bounds__(256, 2) void kvs_partial(PartialArgs a) {
   // Tiles that can hold a readable key.
   int tb = t0, te = t1;
   if constexpr (!RING) {
-    te = min(te, i_cur / kTile + 1);
-    if (a.window > 0) tb = max(tb, max(lo, 0) / kTile);
+    te = max(t0, min(te, i_cur / kTile + 1));
+    if (a.window > 0) tb = min(te, max(tb, max(lo, 0) / kTile));
   }
 
   // Query operand (B of the QK MFMA): lane holds Q[h][dim(t, kg)], zeros for
@@ -462,7 +463,8 @@ __global__ __launch_bounds__(256, 2) void kvs_partial(PartialArgs a) {
     a.ws_l[(pbase + hh) * a.nparts + part] = l;
   }
   if constexpr (SCORED) {
-    // Block sums rescaled from the running max at the time to the partition max.
+    // Block sums rescaled from the running max at the time to the partition
+    // max; tiles never read keep 0.
     for (int x = threadIdx.x; x < G * ntl * NSUB; x += 256) {
       const int hh = x / (ntl * NSUB);
       const int rem = x % (ntl * NSUB);
@@ -484,19 +486,32 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
   extern __shared__ float lds[];
   const int b = blockIdx.y;
   const int P = a.nparts;
-  float* wgt = lds;                    // [Hq][P]: 2^(m_p - M_h) / L_h
-  // per-head max and normaliser
+  const int HP = a.Hq * P;
+  float* wgt = lds;               // [Hq][P]: partition maxima, then 2^(m_p - M_h) / L_h
+  float* lsum = wgt + HP;         // [Hq][P]: partition sums
+  float* hM = lsum + HP;          // [Hq]
+  float* hInv = hM + a.Hq;        // [Hq]
+  const float* mb = a.ws_m + (size_t)b * HP;
+  const float* lb = a.ws_l + (size_t)b * HP;
+  for (int x = threadIdx.x; x < HP; x += 256) {
+    wgt[x] = mb[x];
+    lsum[x] = lb[x];
+  }
+  __syncthreads();
   for (int h = threadIdx.x; h < a.Hq; h += 256) {
-    const float* m = a.ws_m + ((size_t)b * a.Hq + h) * P;
-    const float* l = a.ws_l + ((size_t)b * a.Hq + h) * P;
     float M = -__builtin_inff();
-    for (int p = 0; p < P; ++p) M = fmaxf(M, m[p]);
+    for (int p = 0; p < P; ++p) M = fmaxf(M, wgt[h * P + p]);
     float L = 0.0f;
     if (M != -__builtin_inff())
-      for (int p = 0; p < P; ++p) L += l[p] * fast_exp2(m[p] - M);
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    for (int p = 0; p < P; ++p)
-      wgt[h * P + p] = (M == -__builtin_inff()) ? 0.0f : fast_exp2(m[p] - M) * inv;
+      for (int p = 0; p < P; ++p) L += lsum[h * P + p] * fast_exp2(wgt[h * P + p] - M);
+    hM[h] = M;
+    hInv[h] = L > 0.0f ? 1.0f / L : 0.0f;
+  }
+  __syncthreads();
+  for (int x = threadIdx.x; x < HP; x += 256) {
+    const int h = x / P;
+    const float M = hM[h];
+    wgt[x] = (M == -__builtin_inff()) ? 0.0f : fast_exp2(wgt[x] - M) * hInv[h];
   }
   __syncthreads();
 
@@ -505,8 +520,17 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
     for (int x = blockIdx.x * 256 + threadIdx.x; x < total; x += a.n_o_chunks * 256) {
       const int h = x / a.D, d = x % a.D;
       const float* o = a.ws_o + (((size_t)b * a.Hq + h) * P) * a.D + d;
-      float acc = 0.0f;
-      for (int p = 0; p < P; ++p) acc += o[(size_t)p * a.D] * wgt[h * P + p];
+      const float* w = wgt + h * P;
+      float acc0 = 0.0f, acc1 = 0.0f, acc2 = 0.0f, acc3 = 0.0f;
+      int p = 0;
+      for (; p + 4 <= P; p += 4) {
+        acc0 += o[(size_t)(p + 0) * a.D] * w[p + 0];
+        acc1 += o[(size_t)(p + 1) * a.D] * w[p + 1];
+        acc2 += o[(size_t)(p + 2) * a.D] * w[p + 2];
+        acc3 += o[(size_t)(p + 3) * a.D] * w[p + 3];
+      }
+      for (; p < P; ++p) acc0 += o[(size_t)p * a.D] * w[p];
+      const float acc = (acc0 + acc1) + (acc2 + acc3);
       const size_t oi = ((size_t)b * a.Hq + h) * a.D + d;
       if constexpr (Q_BF16)
         ((uint16_t*)a.out)[oi] = f32_to_bf16_rne(acc);
@@ -521,19 +545,26 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
   const int i_cur = a.cur_pos[b];
   const int lap_i = RING ? i_cur / a.C : 0;
   for (int t = chunk * 256 + threadIdx.x; t < a.NT; t += a.n_mass_chunks * 256) {
+    // heads summed in ascending order
     const int p = t / a.tpp;
+    const float* e = a.ws_e + ((size_t)b * a.Hq * a.NT + t) * NSUB;
+    float acc[NSUB];
+#pragma unroll
+    for (int sb = 0; sb < NSUB; ++sb) acc[sb] = 0.0f;
+    for (int h = 0; h < a.Hq; ++h) {
+      const float w = wgt[h * P + p];
+#pragma unroll
+      for (int sb = 0; sb < NSUB; ++sb) acc[sb] += e[(size_t)h * a.NT * NSUB + sb] * w;
+    }
 #pragma unroll
     for (int sb = 0; sb < NSUB; ++sb) {
-      float acc = 0.0f;
-      for (int h = 0; h < a.Hq; ++h)
-        acc += a.ws_e[(((size_t)b * a.Hq + h) * a.NT + t) * NSUB + sb] * wgt[h * P + p];
       int blk = t;
       if constexpr (RING) {
         const int lap = ((lap_i & 1) == sb) ? lap_i : lap_i - 1;
         if (lap < 0) continue;
         blk = lap * (a.C / kTile) + t;
       }
-      if (blk < a.nbmax) a.mass[(size_t)b * a.nbmax + blk] += acc;
+      if (blk < a.nbmax) a.mass[(size_t)b * a.nbmax + blk] += acc[sb];
     }
   }
 }
@@ -573,7 +604,7 @@ hipError_t launch_partial(int kv, int d, const PartialArgs& a, bool scored, bool
 
 hipError_t launch_combine(const CombineArgs& a, bool ring, bool q_bf16, hipStream_t st) {
   dim3 grid(a.n_o_chunks + (a.mass ? a.n_mass_chunks : 0), a.B), block(256);
-  const size_t lds = (size_t)a.Hq * a.nparts * sizeof(float);
+  const size_t lds = (2 * (size_t)a.Hq * a.nparts + 2 * (size_t)a.Hq) * sizeof(float);
   if (ring) {
     if (q_bf16) hipLaunchKernelGGL((kvs_combine<true, true>), grid, block, lds, st, a);
     else hipLaunchKernelGGL((kvs_combine<true, false>), grid, block, lds, st, a);

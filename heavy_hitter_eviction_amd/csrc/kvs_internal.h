@@ -21,7 +21,7 @@ struct PartialArgs {
   float* ws_m;     // [B][Hq][P]
   float* ws_l;     // [B][Hq][P]
   float* ws_o;     // [B][Hq][P][D]
-  float* ws_e;     // [B][Hq][NT][NSUB]
+  float* ws_e;     // [B][Hq][NT][NSUB] per-tile block sums, relative to the partition max
   int B, Hq, Hkv, G, C, NT, window, nbmax, kwords, tpp, nparts;
   float scale_log2;
 };

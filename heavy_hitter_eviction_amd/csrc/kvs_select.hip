@@ -63,8 +63,8 @@ __global__ __launch_bounds__(kSelThreads) void kvs_select(SelectArgs a) {
   extern __shared__ uint32_t alive_lds[];  // [kwords]: alive bits, staged so keep may alias alive
   __shared__ uint32_t hist[256];
   __shared__ uint32_t wsum[kSelThreads / 64];
-  __shared__ uint64_t s_prefix, s_mask;
-  __shared__ int s_remaining, s_ncand, s_base;
+  __shared__ uint64_t s_prefix;
+  __shared__ int s_remaining, s_ncand, s_base, s_done;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -85,47 +85,68 @@ __global__ __launch_bounds__(kSelThreads) void kvs_select(SelectArgs a) {
   };
 
   // candidate count
-  if (tid == 0) s_ncand = 0;
+  if (tid == 0) {
+    s_ncand = 0;
+    s_prefix = 0;
+    s_done = 0;
+  }
   __syncthreads();
   int cnt = 0;
   for (int blk = tid; blk < nexist; blk += kSelThreads) cnt += is_cand(blk) ? 1 : 0;
   for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
   if (lane == 0) atomicAdd(&s_ncand, cnt);
-  if (tid == 0) {
-    s_prefix = 0;
-    s_mask = 0;
-  }
   __syncthreads();
   const int ncand = s_ncand;
   const int k = min(a.budget, ncand);
   if (tid == 0) s_remaining = k;
   __syncthreads();
 
-  // Radix select of the k-th largest key, 8 bits at a time from the top.
+  // Radix select of the k-th largest key, 8 bits at a time from the top. When
+  // every key of the chosen digit bin is taken, the lower bits do not matter
+  // and the search stops (threshold = prefix with zero low bits).
   const bool take_all = (k == ncand);
   if (k > 0 && !take_all) {
+    uint64_t mask = 0;
     for (int shift = 56; shift >= 0; shift -= 8) {
       for (int x = tid; x < 256; x += kSelThreads) hist[x] = 0;
       __syncthreads();
-      const uint64_t prefix = s_prefix, mask = s_mask;
+      const uint64_t prefix = s_prefix;
       for (int blk = tid; blk < nexist; blk += kSelThreads) {
         if (!is_cand(blk)) continue;
         const uint64_t key = select_key(score[blk], blk);
         if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xFF], 1u);
       }
       __syncthreads();
-      if (tid == 0) {
-        int rem = s_remaining;
-        int d = 255;
-        for (; d > 0; --d) {
-          if ((int)hist[d] >= rem) break;
-          rem -= (int)hist[d];
+      if (wave == 0) {
+        // suffix sums over bins (lane L owns bins 4L..4L+3), then locate the bin
+        // holding the remaining-th largest key
+        const int rem = s_remaining;
+        const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+        uint32_t suf = h0 + h1 + h2 + h3;  // inclusive suffix over lanes >= L after the scan
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t o = __shfl_down(suf, off, 64);
+          if (lane + off < 64) suf += o;
         }
-        s_remaining = rem;
-        s_prefix = prefix | ((uint64_t)d << shift);
-        s_mask = mask | ((uint64_t)0xFF << shift);
+        const uint32_t above = suf - (h0 + h1 + h2 + h3);  // keys in bins of higher lanes
+        const bool here = above < (uint32_t)rem && suf >= (uint32_t)rem;
+        if (here) {
+          uint32_t acc = above;
+          int d = 4 * lane + 3;
+          const uint32_t hv[4] = {h0, h1, h2, h3};
+          for (int q = 3; q >= 0; --q) {
+            d = 4 * lane + q;
+            if (acc + hv[q] >= (uint32_t)rem) break;
+            acc += hv[q];
+          }
+          const int new_rem = rem - (int)acc;
+          s_remaining = new_rem;
+          s_prefix = prefix | ((uint64_t)d << shift);
+          s_done = (hist[d] == (uint32_t)new_rem) ? 1 : 0;
+        }
       }
       __syncthreads();
+      mask |= (uint64_t)0xFF << shift;
+      if (s_done) break;
     }
   }
   const uint64_t thresh = s_prefix;
@@ -138,34 +159,29 @@ __global__ __launch_bounds__(kSelThreads) void kvs_select(SelectArgs a) {
     return select_key(score[blk], blk) >= thresh;
   };
 
-  // keep mask words
-  for (int w = tid; w < a.kwords; w += kSelThreads) {
-    uint32_t word = 0;
-    for (int bit = 0; bit < 32; ++bit) {
-      const int blk = w * 32 + bit;
-      if (blk < a.nbmax && kept(blk)) word |= 1u << bit;
-    }
-    a.keep[(size_t)b * a.kwords + w] = word;
-  }
-
-  // ascending ids of kept existing blocks (stream compaction)
+  // keep mask words and ascending ids of kept existing blocks, 1024 blocks at a time
   if (tid == 0) s_base = 0;
   __syncthreads();
   int32_t* ids = a.sel_ids + (size_t)b * a.nbmax;
-  for (int c0 = 0; c0 < nexist; c0 += kSelThreads) {
+  uint32_t* keep = a.keep + (size_t)b * a.kwords;
+  for (int c0 = 0; c0 < a.kwords * 32; c0 += kSelThreads) {
     const int blk = c0 + tid;
-    const bool f = blk < nexist && kept(blk);
+    const bool f = blk < a.nbmax && kept(blk);
     const uint64_t bal = __builtin_amdgcn_ballot_w64(f);
-    const int before = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) wsum[wave] = (uint32_t)__builtin_popcountll(bal);
+    const int w = blk >> 5;
+    if ((lane & 31) == 0 && w < a.kwords) keep[w] = (uint32_t)(bal >> (lane & 32));
+    const bool fe = f && blk < nexist;
+    const uint64_t bale = __builtin_amdgcn_ballot_w64(fe);
+    const int before = __builtin_popcountll(bale & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[wave] = (uint32_t)__builtin_popcountll(bale);
     __syncthreads();
     int off = s_base;
-    for (int w = 0; w < wave; ++w) off += (int)wsum[w];
-    if (f) ids[off + before] = blk;
+    for (int ww = 0; ww < wave; ++ww) off += (int)wsum[ww];
+    if (fe) ids[off + before] = blk;
     __syncthreads();
     if (tid == 0) {
       int t = 0;
-      for (int w = 0; w < kSelThreads / 64; ++w) t += (int)wsum[w];
+      for (int ww = 0; ww < kSelThreads / 64; ++ww) t += (int)wsum[ww];
       s_base += t;
     }
     __syncthreads();
