@@ -95,3 +95,32 @@ def compare_selection(gpu_ids, ref_ids, score_ref, i, budget, recent, sinks, ali
 def to_dev(x, dtype=None):
     t = torch.from_numpy(np.ascontiguousarray(x)).cuda()
     return t if dtype is None else t.to(dtype)
+
+
+def k_tile_offset(t, x, eb):
+    """Byte offset of K element (slot t in its 16-slot tile, dim x): the layout
+    documented in include/kvs.h."""
+    xb = x * eb
+    return ((xb // 64 * 4 + (xb % 64) // 16) * 16 + t) * 16 + xb % 16
+
+
+def v_tile_offset(t, x, D, eb):
+    kg, e, j, n = t // 4, t % 4, x // (D // 16), x % (D // 16)
+    ub = (4 * n + e) * eb
+    return ((ub // 16 * 4 + kg) * 16 + j) * 16 + ub % 16
+
+
+def logical_rows(buf: np.ndarray, B, Hkv, C, D, eb, seq, slots, which="k") -> np.ndarray:
+    """Read cache bytes back as [len(slots), Hkv*D] element rows (raw bytes of
+    width eb per element) for one sequence."""
+    raw = buf.view(np.uint8).reshape(B, Hkv, C // 16, 16 * D * eb)
+    slots = np.asarray(slots)
+    t = (slots % 16)[:, None]
+    x = np.arange(D)[None, :]
+    off = k_tile_offset(t, x, eb) if which == "k" else v_tile_offset(t, x, D, eb)
+    out = np.zeros((len(slots), Hkv, D, eb), dtype=np.uint8)
+    for g in range(Hkv):
+        tiles = raw[seq, g, slots // 16]                       # [n, tile bytes]
+        for k in range(eb):
+            out[:, g, :, k] = np.take_along_axis(tiles, off + k, axis=1)
+    return out.reshape(len(slots), Hkv * D * eb)
