@@ -41,7 +41,34 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB "
+                         "(a reference for hardware byte counters)")
     return ap.parse_args()
+
+
+TRAFFIC_NOTE = "profiles/kvs_partial_397b_fp8_32k_traffic.md"
+
+
+def measured_traffic(root, workload_key):
+    """HBM bytes per partial launch from the committed FETCH_SIZE/WRITE_SIZE
+    summary, or None when it does not describe the kernel as built now (its
+    source hash differs) or another workload is being measured."""
+    import hashlib
+    import re
+    path = os.path.join(root, TRAFFIC_NOTE)
+    if workload_key != "397b_fp8" or not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_val = re.search(r"^traffic_bytes_per_launch: (\d+)$", text, re.M)
+    m_hash = re.search(r"^kernel_source_sha256: ([0-9a-f]{64})$", text, re.M)
+    m_src = re.search(r"^\(sources hashed, in order: (.+)\)$", text, re.M)
+    if not (m_val and m_hash and m_src):
+        return None
+    h = hashlib.sha256()
+    for src in m_src.group(1).split(", "):
+        h.update(open(os.path.join(root, src), "rb").read())
+    return int(m_val.group(1)) if h.hexdigest() == m_hash.group(1) else None
 
 
 def log(msg):
@@ -232,12 +259,22 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(root, args.workload),
             "avg_launch_us": round(part_avg_ms * 1e3, 2),
             "bytes_per_launch": int(bytes_launch),
         },
     }
     del dec
+    if args.calibration_copy_mib:
+        import torch
+        n = args.calibration_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["calibration_copy_bytes"] = n
+        del src, dst
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on the host")
         res["cpu_baseline"] = oracle_baseline(w, args.seed, args.cpu_seconds)
