@@ -40,8 +40,10 @@ int check_geom(const kvs_geom* g) {
     if (q != KVS_BF16) return KVS_EDTYPE;
     if (d != 64 && d != 128) return KVS_EDTYPE;
   }
-  // sizes that must fit the kernels' 32-bit indexing of per-sequence slots
+  // sizes that must fit the kernels' 32-bit indexing of per-sequence slots;
+  // one (sequence, KV head) region is addressed with 32-bit buffer offsets
   if ((int64_t)g->capacity * g->n_kv_heads * d > (int64_t)1 << 40) return KVS_EINVAL;
+  if ((int64_t)g->capacity * d * elem_bytes(kv) > (int64_t)0xFFFF0000) return KVS_EINVAL;
   return KVS_OK;
 }
 
@@ -63,10 +65,13 @@ Plan make_plan(const kvs_geom* g) {
   if (ptarget < 1) ptarget = 1;
   int tpp = (p.NT + ptarget - 1) / ptarget;
   if (tpp < 4) tpp = 4;
-  // the partial kernel keeps per-tile block sums of its partition in LDS:
-  // bound the partition so its LDS stays <= 48 KiB (3 workgroups per CU)
-  const int lds_fixed = 8 * p.G + 4 * p.G * g->head_dim;
-  const int tpp_lds = (kLdsBudgetFloats - lds_fixed) / (p.G * (p.nsub + 1));
+  // the partial kernel keeps per-tile block sums, running maxima and the kept
+  // tile list of its partition in LDS: bound the partition so its LDS stays
+  // <= 48 KiB (3 workgroups per CU)
+  const int side = (g->kv_dtype == KVS_FP8_E4M3 ? 256 : 0) + (g->ring ? 128 : 0);  // per wave
+  const int lds_fixed = 4 * side + 4 * p.G * g->head_dim + 8 * p.G + 4;
+  const int per_tile = p.G * (p.nsub + 1) + 1;
+  const int tpp_lds = (kLdsBudgetFloats - lds_fixed) / per_tile;
   if (tpp > tpp_lds) tpp = tpp_lds < 4 ? 4 : tpp_lds;
   // combine keeps two [Hq][P] float tables in LDS: bound P so they stay <= 48 KiB
   const int pmax = 6144 / g->n_q_heads;
@@ -79,7 +84,7 @@ Plan make_plan(const kvs_geom* g) {
   p.off_o = round256(p.off_l + bh * p.nparts * 4);
   p.off_e = round256(p.off_o + bh * p.nparts * g->head_dim * 4);
   p.total = round256(p.off_e + bh * (size_t)p.NT * p.nsub * 4);
-  p.lds_partial = 4 * ((size_t)tpp * p.G * (p.nsub + 1) + 8 * p.G + 4 * (size_t)p.G * g->head_dim);
+  p.lds_partial = 4 * ((size_t)tpp * per_tile + (size_t)lds_fixed);
   return p;
 }
 

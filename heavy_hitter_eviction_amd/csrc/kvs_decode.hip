@@ -51,8 +51,6 @@ struct TileRegs {
   static constexpr int NCH = D * KvT<KV>::eb / 64;  // 16-byte chunks per lane, K and V each
   u32x4 k[NCH];
   u32x4 v[NCH];
-  f32x4 ks, vs;  // FP8 scales of the lane's 4 tokens
-  int4 pos;      // ring: absolute positions of the lane's 4 tokens
 };
 
 // Buffer resources (base in scalar registers, bounds-checked: reads past
@@ -60,8 +58,8 @@ struct TileRegs {
 // sequence's scale and position arrays, plus the lane's constant byte offsets.
 // A tile then costs one scalar offset per load.
 struct TileAddr {
-  __amdgpu_buffer_rsrc_t k, v, ks, vs, pos;
-  uint32_t koff, voff, soff;
+  __amdgpu_buffer_rsrc_t k, v;
+  uint32_t koff, voff;
 };
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw untyped 32-bit dword access
@@ -77,27 +75,16 @@ __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff
 }
 
 template <int KV, int D, bool RING>
-__device__ __forceinline__ void load_tile(TileRegs<KV, D>& t, const TileAddr& ad, int tile) {
-  constexpr int eb = KvT<KV>::eb;
+__device__ __forceinline__ void load_tile(TileRegs<KV, D>& t, const TileAddr& ad, uint32_t so) {
   constexpr int NCH = TileRegs<KV, D>::NCH;
-  constexpr uint32_t tile_bytes = (uint32_t)kTile * D * eb;
-  const uint32_t so = (uint32_t)tile * tile_bytes;
   // K and V tiles are stored fragment-major: chunk i of every lane is one
   // contiguous 1 KiB run (lane-major), so each load instruction reads whole
-  // cache lines, streamed past the caches (non-temporal).
+  // cache lines, streamed past the caches (non-temporal). so is the tile's
+  // byte offset in the (sequence, KV head) region.
 #pragma unroll
   for (int i = 0; i < NCH; ++i) t.k[i] = bload16<2>(ad.k, ad.koff + 1024 * i, so);
 #pragma unroll
   for (int i = 0; i < NCH; ++i) t.v[i] = bload16<2>(ad.v, ad.voff + 1024 * i, so);
-  const uint32_t ss = (uint32_t)tile * (kTile * 4);
-  if constexpr (KV == KV_FP8) {
-    t.ks = __builtin_bit_cast(f32x4, bload16<0>(ad.ks, ad.soff, ss));
-    t.vs = __builtin_bit_cast(f32x4, bload16<0>(ad.vs, ad.soff, ss));
-  }
-  if constexpr (RING) {
-    const u32x4 p = bload16<0>(ad.pos, ad.soff, ss);
-    t.pos = make_int4((int)p[0], (int)p[1], (int)p[2], (int)p[3]);
-  }
 }
 
 // Lane's t-th contraction element of the QK product lives at head dimension
@@ -111,7 +98,7 @@ __device__ __forceinline__ int qk_dim(int t, int kg) {
 
 template <int KV>
 struct Pipe {
-  static constexpr int depth = KV == KV_FP8 ? 3 : 2;  // tiles in flight per wave
+  static constexpr int depth = KV == KV_FP8 ? 4 : 2;  // tile buffers per wave (depth-1 in flight)
 };
 
 template <int KV, int D, bool SCORED, bool RING>
@@ -135,19 +122,28 @@ __global__ __launch_bounds__(256, 2) void kvs_partial(PartialArgs a) {
   const int t0 = part * a.tpp;
   const int t1 = min(t0 + a.tpp, a.NT);
 
-  // LDS carve-up: per-tile block sums and the running maxima they are relative
-  // to, then the wave merge area.
+  // Per-slot side data (FP8 scales, ring positions) of 8 of a wave's tiles at
+  // a time, staged in LDS (see gather below).
+  constexpr bool SIDE = KV == KV_FP8 || RING;
+  constexpr int SIDE_S = KV == KV_FP8 ? 8 * 8 * 4 : 0;  // floats per wave: [8 tiles][8 quads][4]
+  constexpr int SIDE_P = RING ? 8 * 4 * 4 : 0;          // ints per wave: [8 tiles][4 quads][4]
+
+  // LDS carve-up (16-byte aligned parts first): side data, the wave merge
+  // area, then per-tile block sums of the partition, the running maxima they
+  // are relative to, and the list of kept tiles.
   const int ntl = t1 - t0;
-  float* e_rec = lds;                                   // [ntl][NSUB][G]
-  float* m_rec = e_rec + a.tpp * NSUB * G;              // [ntl][G]
-  float* mw = m_rec + a.tpp * G;                        // [4][G]
+  float* side_area = lds;                               // [4 waves][SIDE_S + SIDE_P]
+  float* ow = side_area + 4 * (SIDE_S + SIDE_P);        // [4][G][D]
+  float* mw = ow + 4 * G * D;                           // [4][G]
   float* lw = mw + 4 * G;                               // [4][G]
-  float* ow = lw + 4 * G;                               // [4][G][D]
+  int* n_list_s = (int*)(lw + 4 * G);                   // [4]: kept-tile count
+  float* e_rec = (float*)(n_list_s + 4);                // [tpp][NSUB][G]
+  float* m_rec = e_rec + a.tpp * NSUB * G;              // [tpp][G]
+  int* tlist = (int*)(m_rec + a.tpp * G);               // [tpp]
   if constexpr (SCORED) {
     for (int x = threadIdx.x; x < ntl * NSUB * G; x += 256) e_rec[x] = 0.0f;
     for (int x = threadIdx.x; x < ntl * G; x += 256) m_rec[x] = -__builtin_inff();
   }
-  __syncthreads();
 
   // Tiles that can hold a readable key.
   int tb = t0, te = t1;
@@ -156,42 +152,78 @@ __global__ __launch_bounds__(256, 2) void kvs_partial(PartialArgs a) {
     if (a.window > 0) tb = min(te, max(tb, max(lo, 0) / kTile));
   }
 
+  // With a keep mask on a linear cache (tile = block), wave 0 compacts the
+  // partition's kept tiles into tlist; the four waves then take list entries
+  // wave, wave + 4, ... so evicted tiles are never read and the kept ones are
+  // shared evenly. Without one, the list is implicit: entry i is tile tb + i.
+  const uint32_t* keep_b = a.keep ? a.keep + (size_t)b * a.kwords : nullptr;
+  const bool use_list = !RING && keep_b != nullptr;
+  if (use_list && wave == 0) {
+    int n = 0;
+    for (int c = tb; c < te; c += 64) {
+      const int t = c + lane;
+      bool kept = false;
+      if (t < te) kept = t >= a.nbmax || ((keep_b[t >> 5] >> (t & 31)) & 1u);
+      const uint64_t m = __ballot(kept);
+      if (kept) tlist[n + __popcll(m & ((1ull << lane) - 1ull))] = t;
+      n += __popcll(m);
+    }
+    if (lane == 0) n_list_s[0] = n;
+  }
+  __syncthreads();
+  const int n_items = use_list ? n_list_s[0] : te - tb;
+  const int n_w = n_items > wave ? (n_items - wave + 3) >> 2 : 0;  // this wave's tiles
+  // k-th tile of this wave, k < n_w
+  auto tile_of = [&](int k) -> int {
+    if (use_list) return __builtin_amdgcn_readfirstlane(tlist[wave + 4 * k]);
+    return tb + wave + 4 * k;
+  };
+
   // Query operand (B of the QK MFMA): lane holds Q[h][dim(t, kg)], zeros for
-  // padding heads. Runs of EPC consecutive dims are read with 16-byte loads.
+  // padding heads. Runs of EPC consecutive dims are read with 16-byte loads
+  // here and converted once the first tile loads are in flight.
   const int hq = g * G + min(h, G - 1);
   constexpr int QN = D / 4;
-  float qf[QN];
+  constexpr int EPC = 16 / eb;                  // dims per run
+  constexpr int QE = KV == KV_F32 ? 4 : 2;      // query element bytes
+  constexpr int QRUN = EPC * QE / 16;           // 16-byte words per run
+  u32x4 qraw[QN / EPC][QRUN];
   {
-    constexpr int EPC = 16 / eb;                  // dims per run
-    constexpr int QE = KV == KV_F32 ? 4 : 2;      // query element bytes
     const char* qrow = (const char*)a.q + ((size_t)b * a.Hq + hq) * D * QE;
 #pragma unroll
-    for (int r0 = 0; r0 < QN; r0 += EPC) {
-      const int d0 = qk_dim<KV>(r0, kg);
+    for (int r = 0; r < QN / EPC; ++r)
 #pragma unroll
-      for (int c = 0; c < EPC * QE / 16; ++c) {
-        const u32x4 w = *(const u32x4*)(qrow + (size_t)d0 * QE + 16 * c);
+      for (int c = 0; c < QRUN; ++c)
+        qraw[r][c] = *(const u32x4*)(qrow + (size_t)qk_dim<KV>(r * EPC, kg) * QE + 16 * c);
+  }
+  float qf[QN];
+  bf16x8 qb[D / 32 > 0 ? D / 32 : 1];
+  auto convert_q = [&]() {
+#pragma unroll
+    for (int r = 0; r < QN / EPC; ++r) {
+#pragma unroll
+      for (int c = 0; c < QRUN; ++c) {
+        const u32x4 w = qraw[r][c];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if constexpr (QE == 4) {
-            qf[r0 + 4 * c + e] = bits_to_f32(w[e]);
+            qf[r * EPC + 4 * c + e] = bits_to_f32(w[e]);
           } else {
-            qf[r0 + 8 * c + 2 * e] = bf16_lo(w[e]);
-            qf[r0 + 8 * c + 2 * e + 1] = bf16_hi(w[e]);
+            qf[r * EPC + 8 * c + 2 * e] = bf16_lo(w[e]);
+            qf[r * EPC + 8 * c + 2 * e + 1] = bf16_hi(w[e]);
           }
         }
       }
     }
 #pragma unroll
     for (int t = 0; t < QN; ++t) qf[t] = hreal ? qf[t] : 0.0f;
-  }
-  bf16x8 qb[D / 32 > 0 ? D / 32 : 1];
-  if constexpr (KV != KV_F32) {
+    if constexpr (KV != KV_F32) {
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c)
+      for (int c = 0; c < D / 32; ++c)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qb[c][e] = (__bf16)qf[8 * c + e];  // exact: Q is bf16
-  }
+        for (int e = 0; e < 8; ++e) qb[c][e] = (__bf16)qf[8 * c + e];  // exact: Q is bf16
+    }
+  };
 
   f32x4 oacc[NC];
 #pragma unroll
@@ -204,41 +236,70 @@ __global__ __launch_bounds__(256, 2) void kvs_partial(PartialArgs a) {
   const int lap_i = RING ? i_cur / a.C : 0;
   const int lap_base = lap_i * a.C;
 
-  const uint32_t* keep_b = a.keep ? a.keep + (size_t)b * a.kwords : nullptr;
-  // Next tile of this wave (stride 4) whose block is kept, or te.
-  auto next_kept = [&](int t) -> int {
-    if constexpr (!RING) {
-      if (keep_b != nullptr) {
-        while (t < te && t < a.nbmax && !((keep_b[t >> 5] >> (t & 31)) & 1u)) t += 4;
-      }
-    }
-    return t;
-  };
-
   TileAddr ad;
   {
     const size_t bg = (size_t)b * a.Hkv + g;
     const uint32_t region = (uint32_t)((size_t)a.C * D * eb);
     ad.k = make_rsrc((const char*)a.k + bg * region, region);
     ad.v = make_rsrc((const char*)a.v + bg * region, region);
-    const uint32_t sbytes = (uint32_t)a.C * 4;
-    ad.ks = make_rsrc(a.ks ? a.ks + (size_t)b * a.C : nullptr, a.ks ? sbytes : 0);
-    ad.vs = make_rsrc(a.vs ? a.vs + (size_t)b * a.C : nullptr, a.vs ? sbytes : 0);
-    ad.pos = make_rsrc(a.pos_of_slot ? a.pos_of_slot + (size_t)b * a.C : nullptr, a.pos_of_slot ? sbytes : 0);
     ad.koff = (uint32_t)(16 * lane);
     ad.voff = (uint32_t)(16 * lane);
-    ad.soff = (uint32_t)(16 * kg);
   }
 
+  // ---- per-slot side data (FP8 scales, ring positions), 8 of this wave's
+  // tiles at a time ----
+  // One gathered 16-byte-per-lane load brings the K and V scales of 8 tiles
+  // (lane l: tile l/8, quad l%8: K scales 4q..4q+3 for q < 4, V scales after),
+  // another the ring positions (lane l: tile (l/4)%8, quad l%4). They are
+  // staged in this wave's LDS area and read back per tile, so a tile costs
+  // its KiB-wide K/V loads and nothing else on the vector memory path. Group
+  // g + 1 is fetched while group g is in use.
+  const float* ks_b = a.ks ? a.ks + (size_t)b * a.C : nullptr;
+  const float* vs_b = a.vs ? a.vs + (size_t)b * a.C : nullptr;
+  const int32_t* pos_b = a.pos_of_slot ? a.pos_of_slot + (size_t)b * a.C : nullptr;
+  u32x4 pf_s = {0u, 0u, 0u, 0u}, pf_p = {0u, 0u, 0u, 0u};
+  auto lane_tile = [&](int k) -> int {  // per-lane tile of entry k, clamped to the wave's last
+    k = min(k, n_w - 1);
+    return use_list ? tlist[wave + 4 * k] : tb + wave + 4 * k;
+  };
+  auto gather = [&](int grp) {
+    if constexpr (KV == KV_FP8) {
+      const int t = lane_tile(8 * grp + (lane >> 3));
+      const int q = lane & 7;
+      pf_s = *(const u32x4*)((q < 4 ? ks_b : vs_b) + (size_t)t * kTile + 4 * (q & 3));
+    }
+    if constexpr (RING) {
+      const int t = lane_tile(8 * grp + ((lane >> 2) & 7));
+      pf_p = *(const u32x4*)(pos_b + (size_t)t * kTile + 4 * (lane & 3));
+    }
+  };
+  float* side_s = side_area + wave * (SIDE_S + SIDE_P);
+  int* side_p = (int*)(side_s + SIDE_S);
+  auto commit = [&]() {
+    if constexpr (KV == KV_FP8) *(u32x4*)(side_s + 4 * lane) = pf_s;
+    if constexpr (RING) if (lane < 32) *(u32x4*)(side_p + 4 * lane) = pf_p;
+  };
+
   // ---- one tile: online softmax, block sums, PV ----
-  auto process = [&](TileRegs<KV, D>& cur, const int tile) {
+  auto process = [&](TileRegs<KV, D>& cur, const int tile, const int k) {
+    f32x4 ks = {0.f, 0.f, 0.f, 0.f}, vs = {0.f, 0.f, 0.f, 0.f};
+    int4 cpos = make_int4(0, 0, 0, 0);
+    if constexpr (SIDE) {
+      const int tau = k & 7;
+      if constexpr (KV == KV_FP8) {
+        ks = *(const f32x4*)(side_s + (tau * 8 + kg) * 4);
+        vs = *(const f32x4*)(side_s + (tau * 8 + 4 + kg) * 4);
+      }
+      if constexpr (RING) cpos = *(const int4*)(side_p + (tau * 4 + kg) * 4);
+    }
     bool valid[4];
     int sub[4];
     bool all_valid, any_valid;
     if constexpr (RING) {
+      const int pr[4] = {cpos.x, cpos.y, cpos.z, cpos.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int p = cur.pos[r];
+        const int p = pr[r];
         bool v = p >= 0 && p <= i_cur && p >= lo;
         if (v && keep_b != nullptr) {
           const int blk = p >> 4;
@@ -310,7 +371,7 @@ __global__ __launch_bounds__(256, 2) void kvs_partial(PartialArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float x;
-      if constexpr (KV == KV_FP8) x = s[r] * (cur.ks[r] * a.scale_log2);
+      if constexpr (KV == KV_FP8) x = s[r] * (ks[r] * a.scale_log2);
       else x = s[r] * a.scale_log2;
       tl[r] = (all_valid || valid[r]) ? x : -__builtin_inff();
     }
@@ -365,7 +426,7 @@ __global__ __launch_bounds__(256, 2) void kvs_partial(PartialArgs a) {
       float pw[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if constexpr (KV == KV_FP8) pw[r] = p[r] * cur.vs[r];
+        if constexpr (KV == KV_FP8) pw[r] = p[r] * vs[r];
         else pw[r] = p[r];
       }
       bf16x4 pb;
@@ -388,42 +449,32 @@ __global__ __launch_bounds__(256, 2) void kvs_partial(PartialArgs a) {
     }
   };
 
-  // ---- software pipeline: NBUF tiles of this wave in flight ----
-  // Loads are issued unconditionally (an exhausted slot re-reads the wave's
-  // last tile, which is still in cache) so the load count between a tile's
-  // issue and its use is the same on every path.
-  int nexti = next_kept(tb + wave);
-  if (nexti < te) {
+  // ---- software pipeline: NBUF - 1 tiles of this wave in flight ----
+  // Every vector-memory load in the loop is unconditional, so the compiler's
+  // wait counts can keep all of them in flight; loads past the wave's last
+  // tile use an offset beyond the buffer's range, which returns zeros without
+  // a memory access. The loop body covers U tiles (one side-data group).
+  constexpr int U = SIDE ? 8 : NBUF;
+  static_assert(U % NBUF == 0, "loop body must hold whole buffer rotations");
+  const uint32_t oob = (uint32_t)((size_t)a.C * D * eb);  // first offset past the region
+  constexpr uint32_t tile_bytes = (uint32_t)kTile * D * eb;
+  auto soff_of = [&](int k) -> uint32_t { return k < n_w ? (uint32_t)tile_of(k) * tile_bytes : oob; };
+  if (n_w > 0) {
     TileRegs<KV, D> buf[NBUF];
-    int tq[NBUF];
-    int last = nexti;
+    if constexpr (SIDE) gather(0);
 #pragma unroll
-    for (int s = 0; s < NBUF - 1; ++s) {
-      const bool ok = nexti < te;
-      tq[s] = ok ? nexti : -1;
-      load_tile<KV, D, RING>(buf[s], ad, ok ? nexti : last);
-      if (ok) {
-        last = nexti;
-        nexti = next_kept(nexti + 4);
+    for (int s = 0; s < NBUF - 1; ++s) load_tile<KV, D, RING>(buf[s], ad, soff_of(s));
+    convert_q();
+    for (int k0 = 0; k0 < n_w; k0 += U) {
+      if constexpr (SIDE) {
+        commit();
+        gather(k0 / U + 1);
       }
-    }
-    tq[NBUF - 1] = -1;
-    bool more = true;
-    while (more) {
 #pragma unroll
-      for (int s = 0; s < NBUF; ++s) {
-        if (more) {
-          const int ls = (s + NBUF - 1) % NBUF;
-          const bool ok = nexti < te;
-          tq[ls] = ok ? nexti : -1;
-          load_tile<KV, D, RING>(buf[ls], ad, ok ? nexti : last);
-          if (ok) {
-            last = nexti;
-            nexti = next_kept(nexti + 4);
-          }
-          if (tq[s] < 0) more = false;
-          else process(buf[s], tq[s]);
-        }
+      for (int s = 0; s < U; ++s) {
+        const int k = k0 + s;
+        load_tile<KV, D, RING>(buf[(s + NBUF - 1) % NBUF], ad, soff_of(k + NBUF - 1));
+        if (k < n_w) process(buf[s % NBUF], tile_of(k), k);
       }
     }
   }
