@@ -42,7 +42,7 @@ class Geom(ctypes.Structure):
         ("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
         ("head_dim", ctypes.c_int32), ("capacity", ctypes.c_int32), ("window", ctypes.c_int32),
         ("ring", ctypes.c_int32), ("n_blocks_max", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
-        ("q_dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("q_dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("deterministic", ctypes.c_int32),
     ]
 
 
@@ -129,13 +129,14 @@ class CacheGeom:
     kv_dtype: str = "bf16"
     q_dtype: str = "bf16"
     softmax_scale: float = 0.0
+    deterministic: bool = False
 
     def c(self) -> Geom:
         nb = self.n_blocks_max or self.capacity // 16
         scale = self.softmax_scale or float(torch.tensor(self.head_dim, dtype=torch.float64).rsqrt())
         return Geom(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim, self.capacity,
                     self.window, int(self.ring), nb, DTYPE_CODES[self.kv_dtype],
-                    DTYPE_CODES[self.q_dtype], scale)
+                    DTYPE_CODES[self.q_dtype], scale, int(self.deterministic))
 
     @property
     def nb(self) -> int:

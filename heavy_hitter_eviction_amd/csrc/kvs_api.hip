@@ -10,11 +10,12 @@
 namespace {
 
 constexpr int kTileSlots = 16;
-// One round of resident decode workgroups on MI355X: 256 CUs x 3 (the bf16
-// and FP8 kernels hold 3 waves per SIMD). Fewer, longer partitions measured
-// faster than several rounds: no tail of partly filled rounds.
-constexpr int kTargetWorkgroups = 768;
-constexpr int kLdsBudgetFloats = 12288;  // 48 KiB per decode workgroup
+// One decode workgroup (kPartialWaves waves) per compute unit of MI355X (256
+// CUs). With several workgroups per CU the younger ones were served last by
+// the memory pipeline and finished up to a third later; inside one workgroup
+// the waves share the partition's tiles dynamically instead.
+constexpr int kTargetWorkgroups = 256;
+constexpr int kLdsBudgetFloats = 16384;  // 64 KiB per decode workgroup
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -31,6 +32,7 @@ int check_geom(const kvs_geom* g) {
   if (g->n_blocks_max < 1) return KVS_EINVAL;
   if (!g->ring && g->n_blocks_max < g->capacity / kTileSlots) return KVS_EINVAL;
   if (!(g->softmax_scale > 0.0f) || !isfinite(g->softmax_scale)) return KVS_EINVAL;
+  if (g->deterministic != 0 && g->deterministic != 1) return KVS_EINVAL;
   const int kv = g->kv_dtype, q = g->q_dtype, d = g->head_dim;
   if (kv != KVS_F32 && kv != KVS_BF16 && kv != KVS_FP8_E4M3) return KVS_EDTYPE;
   if (kv == KVS_F32) {
@@ -48,7 +50,7 @@ int check_geom(const kvs_geom* g) {
 }
 
 struct Plan {
-  int NT, tpp, nparts, nsub, G;
+  int NT, tpp, nparts, nsub, G, oslots;
   size_t off_m, off_l, off_o, off_e, total;
   size_t lds_partial;
 };
@@ -65,11 +67,14 @@ Plan make_plan(const kvs_geom* g) {
   if (ptarget < 1) ptarget = 1;
   int tpp = (p.NT + ptarget - 1) / ptarget;
   if (tpp < 4) tpp = 4;
-  // the partial kernel keeps per-tile block sums, running maxima and the kept
-  // tile list of its partition in LDS: bound the partition so its LDS stays
-  // <= 48 KiB (3 workgroups per CU)
-  const int side = (g->kv_dtype == KVS_FP8_E4M3 ? 256 : 0) + (g->ring ? 128 : 0);  // per wave
-  const int lds_fixed = 4 * side + 4 * p.G * g->head_dim + 8 * p.G + 4;
+  // the partial kernel keeps per-wave side data, the wave merge area, and
+  // per-tile block sums, running maxima and the kept tile list of its
+  // partition in LDS: bound the partition so its LDS stays <= 64 KiB
+  const int nw = kvs::kPartialWaves;
+  // the wave merge gives every wave its own output slot when that is small,
+  // else pairs of waves share one
+  p.oslots = p.G * g->head_dim <= 512 ? nw : nw / 2;
+  const int lds_fixed = nw * 256 + p.oslots * p.G * g->head_dim + 2 * nw * p.G + 4;
   const int per_tile = p.G * (p.nsub + 1) + 1;
   const int tpp_lds = (kLdsBudgetFloats - lds_fixed) / per_tile;
   if (tpp > tpp_lds) tpp = tpp_lds < 4 ? 4 : tpp_lds;
@@ -198,6 +203,7 @@ int decode_setup(const kvs_geom* g, const void* q, const void* k_cache, const vo
   a->B = g->batch; a->Hq = g->n_q_heads; a->Hkv = g->n_kv_heads; a->G = p.G; a->C = g->capacity;
   a->NT = p.NT; a->window = g->window; a->nbmax = g->n_blocks_max;
   a->kwords = (g->n_blocks_max + 31) / 32; a->tpp = p.tpp; a->nparts = p.nparts;
+  a->dyn = g->deterministic ? 0 : 1; a->oslots = p.oslots;
   a->scale_log2 = g->softmax_scale * 1.4426950408889634f;
   *c = kvs::CombineArgs{};
   c->ws_m = a->ws_m; c->ws_l = a->ws_l; c->ws_o = a->ws_o; c->ws_e = a->ws_e; c->cur_pos = cur_pos;

@@ -98,14 +98,20 @@ __device__ __forceinline__ int qk_dim(int t, int kg) {
 
 template <int KV>
 struct Pipe {
-  static constexpr int depth = KV == KV_FP8 ? 4 : 2;  // tile buffers per wave (depth-1 in flight)
+  // tile buffers per wave (depth - 1 tiles in flight); also the tiles a wave
+  // claims at a time
+  static constexpr int depth = KV == KV_F32 ? 2 : 4;
 };
 
 template <int KV, int D, bool SCORED, bool RING>
-__global__ __launch_bounds__(256, 2) void kvs_partial(PartialArgs a) {
+__global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs a) {
+  constexpr int NW = kPartialWaves;      // waves per workgroup
+  constexpr int NTH = 64 * NW;           // threads per workgroup
   constexpr int NSUB = RING ? 2 : 1;
   constexpr int NC = D / 16;  // PV output chunks of 16 dims
   constexpr int NBUF = Pipe<KV>::depth;
+  constexpr int BATCH = NBUF;            // tiles per claim
+  constexpr int QPT = 64 / BATCH;        // side-data quads (16 bytes) per tile
   constexpr int eb = KvT<KV>::eb;
   extern __shared__ float lds[];
 
@@ -122,28 +128,25 @@ __global__ __launch_bounds__(256, 2) void kvs_partial(PartialArgs a) {
   const int t0 = part * a.tpp;
   const int t1 = min(t0 + a.tpp, a.NT);
 
-  // Per-slot side data (FP8 scales, ring positions) of 8 of a wave's tiles at
-  // a time, staged in LDS (see gather below).
-  constexpr bool SIDE = KV == KV_FP8 || RING;
-  constexpr int SIDE_S = KV == KV_FP8 ? 8 * 8 * 4 : 0;  // floats per wave: [8 tiles][8 quads][4]
-  constexpr int SIDE_P = RING ? 8 * 4 * 4 : 0;          // ints per wave: [8 tiles][4 quads][4]
-
-  // LDS carve-up (16-byte aligned parts first): side data, the wave merge
-  // area, then per-tile block sums of the partition, the running maxima they
-  // are relative to, and the list of kept tiles.
+  // LDS carve-up (16-byte aligned parts first): per-wave side data (FP8
+  // scales, ring positions of the claimed tiles), the wave merge area, the
+  // kept-tile count and the claim counter, then per-tile block sums of the
+  // partition, the running maxima they are relative to, and the list of kept
+  // tiles.
   const int ntl = t1 - t0;
-  float* side_area = lds;                               // [4 waves][SIDE_S + SIDE_P]
-  float* ow = side_area + 4 * (SIDE_S + SIDE_P);        // [4][G][D]
-  float* mw = ow + 4 * G * D;                           // [4][G]
-  float* lw = mw + 4 * G;                               // [4][G]
-  int* n_list_s = (int*)(lw + 4 * G);                   // [4]: kept-tile count
-  float* e_rec = (float*)(n_list_s + 4);                // [tpp][NSUB][G]
-  float* m_rec = e_rec + a.tpp * NSUB * G;              // [tpp][G]
+  float* side_area = lds;                               // [NW][64 quads][4]
+  float* ow = side_area + NW * 256;                     // [oslots][G][D]
+  float* mw = ow + a.oslots * G * D;                    // [NW][G]
+  float* lw = mw + NW * G;                              // [NW][G]
+  int* misc = (int*)(lw + NW * G);                      // [4]: kept-tile count, claim counter
+  float* e_rec = (float*)(misc + 4);                    // [G][tpp][NSUB]
+  float* m_rec = e_rec + a.tpp * NSUB * G;              // [G][tpp]
   int* tlist = (int*)(m_rec + a.tpp * G);               // [tpp]
   if constexpr (SCORED) {
-    for (int x = threadIdx.x; x < ntl * NSUB * G; x += 256) e_rec[x] = 0.0f;
-    for (int x = threadIdx.x; x < ntl * G; x += 256) m_rec[x] = -__builtin_inff();
+    for (int x = threadIdx.x; x < a.tpp * NSUB * G; x += NTH) e_rec[x] = 0.0f;
+    for (int x = threadIdx.x; x < a.tpp * G; x += NTH) m_rec[x] = -__builtin_inff();
   }
+  if (threadIdx.x == 0) misc[1] = 0;
 
   // Tiles that can hold a readable key.
   int tb = t0, te = t1;
@@ -153,9 +156,8 @@ __global__ __launch_bounds__(256, 2) void kvs_partial(PartialArgs a) {
   }
 
   // With a keep mask on a linear cache (tile = block), wave 0 compacts the
-  // partition's kept tiles into tlist; the four waves then take list entries
-  // wave, wave + 4, ... so evicted tiles are never read and the kept ones are
-  // shared evenly. Without one, the list is implicit: entry i is tile tb + i.
+  // partition's kept tiles into tlist, so evicted tiles are never read.
+  // Without one, the list is implicit: entry i is tile tb + i.
   const uint32_t* keep_b = a.keep ? a.keep + (size_t)b * a.kwords : nullptr;
   const bool use_list = !RING && keep_b != nullptr;
   if (use_list && wave == 0) {
@@ -168,15 +170,30 @@ __global__ __launch_bounds__(256, 2) void kvs_partial(PartialArgs a) {
       if (kept) tlist[n + __popcll(m & ((1ull << lane) - 1ull))] = t;
       n += __popcll(m);
     }
-    if (lane == 0) n_list_s[0] = n;
+    if (lane == 0) misc[0] = n;
   }
   __syncthreads();
-  const int n_items = use_list ? n_list_s[0] : te - tb;
-  const int n_w = n_items > wave ? (n_items - wave + 3) >> 2 : 0;  // this wave's tiles
-  // k-th tile of this wave, k < n_w
-  auto tile_of = [&](int k) -> int {
-    if (use_list) return __builtin_amdgcn_readfirstlane(tlist[wave + 4 * k]);
-    return tb + wave + 4 * k;
+  const int n_items = use_list ? misc[0] : te - tb;
+  const int n_batches = (n_items + BATCH - 1) / BATCH;
+  auto tile_of = [&](int e) -> int {  // tile of list entry e < n_items (wave-uniform e)
+    if (use_list) return __builtin_amdgcn_readfirstlane(tlist[e]);
+    return tb + e;
+  };
+  // The waves take batches of BATCH consecutive list entries from a shared
+  // counter, so a wave that is served faster by the memory system reads more
+  // tiles and all waves of the workgroup finish within about one batch. In
+  // deterministic mode wave w takes batches w, w + NW, ... instead.
+  int n_claimed = 0;
+  auto claim = [&]() -> int {
+    int v = 0;
+    if (a.dyn) {
+      if (lane == 0) v = __hip_atomic_fetch_add(&misc[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      v = __builtin_amdgcn_readfirstlane(v);
+    } else {
+      v = wave + NW * n_claimed;
+    }
+    ++n_claimed;
+    return v;
   };
 
   // Query operand (B of the QK MFMA): lane holds Q[h][dim(t, kg)], zeros for
@@ -246,52 +263,52 @@ __global__ __launch_bounds__(256, 2) void kvs_partial(PartialArgs a) {
     ad.voff = (uint32_t)(16 * lane);
   }
 
-  // ---- per-slot side data (FP8 scales, ring positions), 8 of this wave's
-  // tiles at a time ----
-  // One gathered 16-byte-per-lane load brings the K and V scales of 8 tiles
-  // (lane l: tile l/8, quad l%8: K scales 4q..4q+3 for q < 4, V scales after),
-  // another the ring positions (lane l: tile (l/4)%8, quad l%4). They are
-  // staged in this wave's LDS area and read back per tile, so a tile costs
-  // its KiB-wide K/V loads and nothing else on the vector memory path. Group
-  // g + 1 is fetched while group g is in use.
+  // ---- per-slot side data (FP8 scales, ring positions) of a claimed batch ----
+  // One gathered 16-byte-per-lane load brings all of it: lane l serves tile
+  // l / QPT of the batch and quad q = l % QPT of that tile: K scales 4q..4q+3
+  // for q < 4, V scales 4(q-4).. for q < 8, ring positions 4(q-8).. for
+  // q < 12. The quads are staged in the wave's LDS area and read back per
+  // tile, so a tile costs its KiB-wide K/V loads and nothing else on the
+  // vector memory path. The next batch's quads are fetched while the current
+  // batch is in use.
   const float* ks_b = a.ks ? a.ks + (size_t)b * a.C : nullptr;
   const float* vs_b = a.vs ? a.vs + (size_t)b * a.C : nullptr;
   const int32_t* pos_b = a.pos_of_slot ? a.pos_of_slot + (size_t)b * a.C : nullptr;
-  u32x4 pf_s = {0u, 0u, 0u, 0u}, pf_p = {0u, 0u, 0u, 0u};
-  auto lane_tile = [&](int k) -> int {  // per-lane tile of entry k, clamped to the wave's last
-    k = min(k, n_w - 1);
-    return use_list ? tlist[wave + 4 * k] : tb + wave + 4 * k;
-  };
-  auto gather = [&](int grp) {
-    if constexpr (KV == KV_FP8) {
-      const int t = lane_tile(8 * grp + (lane >> 3));
-      const int q = lane & 7;
-      pf_s = *(const u32x4*)((q < 4 ? ks_b : vs_b) + (size_t)t * kTile + 4 * (q & 3));
+  constexpr bool SIDE = KV == KV_FP8 || RING;
+  u32x4 pf = {0u, 0u, 0u, 0u};
+  auto gather = [&](int bi) {
+    if constexpr (SIDE) {
+      const int e = min(BATCH * bi + lane / QPT, n_items - 1);  // clamped: always a real slot
+      const int t = use_list ? tlist[e] : tb + e;
+      const int q = lane % QPT;
+      const size_t base = (size_t)t * kTile;
+      const void* src;
+      if constexpr (KV == KV_FP8 && RING) {
+        src = q < 4 ? (const void*)(ks_b + base + 4 * q)
+            : q < 8 ? (const void*)(vs_b + base + 4 * (q - 4))
+                    : (const void*)(pos_b + base + 4 * ((q - 8) & 3));
+      } else if constexpr (KV == KV_FP8) {
+        src = q < 4 ? (const void*)(ks_b + base + 4 * q) : (const void*)(vs_b + base + 4 * ((q - 4) & 3));
+      } else {
+        src = (const void*)(pos_b + base + 4 * ((q - 8) & 3));
+      }
+      pf = *(const u32x4*)src;
     }
-    if constexpr (RING) {
-      const int t = lane_tile(8 * grp + ((lane >> 2) & 7));
-      pf_p = *(const u32x4*)(pos_b + (size_t)t * kTile + 4 * (lane & 3));
-    }
   };
-  float* side_s = side_area + wave * (SIDE_S + SIDE_P);
-  int* side_p = (int*)(side_s + SIDE_S);
+  float* side_w = side_area + wave * 256;
   auto commit = [&]() {
-    if constexpr (KV == KV_FP8) *(u32x4*)(side_s + 4 * lane) = pf_s;
-    if constexpr (RING) if (lane < 32) *(u32x4*)(side_p + 4 * lane) = pf_p;
+    if constexpr (SIDE) *(u32x4*)(side_w + 4 * lane) = pf;
   };
 
   // ---- one tile: online softmax, block sums, PV ----
-  auto process = [&](TileRegs<KV, D>& cur, const int tile, const int k) {
+  auto process = [&](TileRegs<KV, D>& cur, const int tile, const int tau) {
     f32x4 ks = {0.f, 0.f, 0.f, 0.f}, vs = {0.f, 0.f, 0.f, 0.f};
     int4 cpos = make_int4(0, 0, 0, 0);
-    if constexpr (SIDE) {
-      const int tau = k & 7;
-      if constexpr (KV == KV_FP8) {
-        ks = *(const f32x4*)(side_s + (tau * 8 + kg) * 4);
-        vs = *(const f32x4*)(side_s + (tau * 8 + 4 + kg) * 4);
-      }
-      if constexpr (RING) cpos = *(const int4*)(side_p + (tau * 4 + kg) * 4);
+    if constexpr (KV == KV_FP8) {
+      ks = *(const f32x4*)(side_w + (tau * QPT + kg) * 4);
+      vs = *(const f32x4*)(side_w + (tau * QPT + 4 + kg) * 4);
     }
+    if constexpr (RING) cpos = *(const int4*)(side_w + (tau * QPT + 8 + kg) * 4);
     bool valid[4];
     int sub[4];
     bool all_valid, any_valid;
@@ -400,9 +417,9 @@ __global__ __launch_bounds__(256, 2) void kvs_partial(PartialArgs a) {
     if constexpr (SCORED) {
       if (kg == 0 && hreal) {
         const int tlc = tile - t0;
-        e_rec[(tlc * NSUB) * G + h] = esub0;
-        if constexpr (NSUB == 2) e_rec[(tlc * NSUB + 1) * G + h] = esub1;
-        m_rec[tlc * G + h] = m_new;
+        e_rec[(h * a.tpp + tlc) * NSUB] = esub0;
+        if constexpr (NSUB == 2) e_rec[(h * a.tpp + tlc) * NSUB + 1] = esub1;
+        m_rec[h * a.tpp + tlc] = m_new;
       }
     }
 
@@ -451,80 +468,125 @@ __global__ __launch_bounds__(256, 2) void kvs_partial(PartialArgs a) {
 
   // ---- software pipeline: NBUF - 1 tiles of this wave in flight ----
   // Every vector-memory load in the loop is unconditional, so the compiler's
-  // wait counts can keep all of them in flight; loads past the wave's last
-  // tile use an offset beyond the buffer's range, which returns zeros without
-  // a memory access. The loop body covers U tiles (one side-data group).
-  constexpr int U = SIDE ? 8 : NBUF;
-  static_assert(U % NBUF == 0, "loop body must hold whole buffer rotations");
+  // wait counts keep all of them in flight; loads past the last list entry
+  // use an offset beyond the buffer's range, which returns zeros without a
+  // memory access. Tile i of the current batch sits in buf[i]; step s loads
+  // the tile NBUF - 1 entries ahead (the last of this batch, then the first
+  // ones of the next claimed batch) and processes tile s.
   const uint32_t oob = (uint32_t)((size_t)a.C * D * eb);  // first offset past the region
   constexpr uint32_t tile_bytes = (uint32_t)kTile * D * eb;
-  auto soff_of = [&](int k) -> uint32_t { return k < n_w ? (uint32_t)tile_of(k) * tile_bytes : oob; };
-  if (n_w > 0) {
+  auto soff_of = [&](int bi, int i) -> uint32_t {
+    const int e = BATCH * bi + i;
+    return e < n_items ? (uint32_t)tile_of(e) * tile_bytes : oob;
+  };
+  int cur = claim();
+  if (cur < n_batches) {
     TileRegs<KV, D> buf[NBUF];
-    if constexpr (SIDE) gather(0);
+    gather(cur);
 #pragma unroll
-    for (int s = 0; s < NBUF - 1; ++s) load_tile<KV, D, RING>(buf[s], ad, soff_of(s));
+    for (int i = 0; i < NBUF - 1; ++i) load_tile<KV, D, RING>(buf[i], ad, soff_of(cur, i));
     convert_q();
-    for (int k0 = 0; k0 < n_w; k0 += U) {
-      if constexpr (SIDE) {
-        commit();
-        gather(k0 / U + 1);
-      }
+    while (true) {
+      commit();
+      const int nxt = claim();
+      gather(nxt);
 #pragma unroll
-      for (int s = 0; s < U; ++s) {
-        const int k = k0 + s;
-        load_tile<KV, D, RING>(buf[(s + NBUF - 1) % NBUF], ad, soff_of(k + NBUF - 1));
-        if (k < n_w) process(buf[s % NBUF], tile_of(k), k);
+      for (int s = 0; s < NBUF; ++s) {
+        load_tile<KV, D, RING>(buf[(s + NBUF - 1) % NBUF], ad,
+                               s == 0 ? soff_of(cur, NBUF - 1) : soff_of(nxt, s - 1));
+        const int e = BATCH * cur + s;
+        if (e < n_items) process(buf[s], tile_of(e), s);
       }
+      if (nxt >= n_batches) break;
+      cur = nxt;
     }
   }
 
-  // ---- merge the four waves of the partition ----
-  if (hreal) {
-    if (kg == 0) {
-      mw[wave * G + h] = m_run;
-      lw[wave * G + h] = l_run;
-    }
-#pragma unroll
-    for (int n = 0; n < NC; ++n)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ow[(wave * G + h) * D + (D / 16) * (4 * kg + r) + n] = oacc[n][r];
+  // ---- merge the waves of the workgroup ----
+  // Every wave leaves its (max, sum, O) in LDS; each output then combines the
+  // waves in a fixed order, rescaled to the workgroup max per head. When the
+  // slots do not fit, waves w and w + NW/2 share one: they rescale to the
+  // workgroup max first and the upper half adds into the lower half's slot.
+  if (hreal && kg == 0) {
+    mw[wave * G + h] = m_run;
+    lw[wave * G + h] = l_run;
   }
-  __syncthreads();
+  auto put_o = [&](int slot, float sc, bool add) {
+    float* dst = ow + (slot * G + h) * D;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int d0 = NC * (4 * kg + r);  // lane's dims d0 .. d0 + NC - 1
+      if constexpr (NC % 4 == 0) {
+#pragma unroll
+        for (int n0 = 0; n0 < NC; n0 += 4) {
+          f32x4 v = {oacc[n0][r] * sc, oacc[n0 + 1][r] * sc, oacc[n0 + 2][r] * sc, oacc[n0 + 3][r] * sc};
+          if (add) v += *(const f32x4*)(dst + d0 + n0);
+          *(f32x4*)(dst + d0 + n0) = v;
+        }
+      } else {
+#pragma unroll
+        for (int n = 0; n < NC; ++n) dst[d0 + n] = oacc[n][r] * sc + (add ? dst[d0 + n] : 0.0f);
+      }
+    }
+  };
+  const bool own_slots = a.oslots == NW;
+  if (own_slots) {
+    if (hreal) put_o(wave, 1.0f, false);
+    __syncthreads();
+  } else {
+    __syncthreads();
+    float M = -__builtin_inff();
+    if (hreal)
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, mw[w * G + h]);
+    const float sc = (M == -__builtin_inff()) ? 0.0f : fast_exp2(m_run - M);
+    if (hreal && wave < NW / 2) put_o(wave, sc, false);
+    __syncthreads();
+    if (hreal && wave >= NW / 2) put_o(wave - NW / 2, sc, true);
+    __syncthreads();
+  }
 
+  auto wg_max = [&](int hh) -> float {
+    float M = -__builtin_inff();
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, mw[w * G + hh]);
+    return M;
+  };
   const size_t pbase = ((size_t)b * a.Hq + (size_t)g * G);  // first head of the group
-  for (int x = threadIdx.x; x < G * D; x += 256) {
+  for (int x = threadIdx.x; x < G * D; x += NTH) {
     const int hh = x / D, dd = x % D;
-    float M = fmaxf(fmaxf(mw[hh], mw[G + hh]), fmaxf(mw[2 * G + hh], mw[3 * G + hh]));
     float o = 0.0f;
-    if (M != -__builtin_inff()) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) o += ow[(w * G + hh) * D + dd] * fast_exp2(mw[w * G + hh] - M);
+    if (own_slots) {
+      const float M = wg_max(hh);
+      if (M != -__builtin_inff()) {
+        for (int w = 0; w < NW; ++w) o += ow[(w * G + hh) * D + dd] * fast_exp2(mw[w * G + hh] - M);
+      }
+    } else {
+      for (int sl = 0; sl < NW / 2; ++sl) o += ow[(sl * G + hh) * D + dd];
     }
     a.ws_o[((pbase + hh) * a.nparts + part) * D + dd] = o;
   }
-  for (int hh = threadIdx.x; hh < G; hh += 256) {
-    float M = fmaxf(fmaxf(mw[hh], mw[G + hh]), fmaxf(mw[2 * G + hh], mw[3 * G + hh]));
+  for (int hh = threadIdx.x; hh < G; hh += NTH) {
+    const float M = wg_max(hh);
     float l = 0.0f;
     if (M != -__builtin_inff()) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) l += lw[w * G + hh] * fast_exp2(mw[w * G + hh] - M);
+      for (int w = 0; w < NW; ++w) l += lw[w * G + hh] * fast_exp2(mw[w * G + hh] - M);
     }
     a.ws_m[(pbase + hh) * a.nparts + part] = M;
     a.ws_l[(pbase + hh) * a.nparts + part] = l;
   }
   if constexpr (SCORED) {
-    // Block sums rescaled from the running max at the time to the partition
-    // max; tiles never read keep 0.
-    for (int x = threadIdx.x; x < G * ntl * NSUB; x += 256) {
-      const int hh = x / (ntl * NSUB);
-      const int rem = x % (ntl * NSUB);
-      const int tlc = rem / NSUB, sb = rem % NSUB;
-      const float M = fmaxf(fmaxf(mw[hh], mw[G + hh]), fmaxf(mw[2 * G + hh], mw[3 * G + hh]));
-      float e = e_rec[(tlc * NSUB + sb) * G + hh];
-      const float mr = m_rec[tlc * G + hh];
+    // Block sums rescaled from the running max at the time to the workgroup
+    // max; tiles never read keep 0. Consecutive threads take consecutive
+    // tiles of one head.
+    const int per_head = ntl * NSUB;
+    for (int x = threadIdx.x; x < G * per_head; x += NTH) {
+      const int hh = x / per_head;
+      const int rem = x - hh * per_head;
+      const int tlc = rem / NSUB;
+      const float M = wg_max(hh);
+      float e = e_rec[hh * a.tpp * NSUB + rem];
+      const float mr = m_rec[hh * a.tpp + tlc];
       e = (M == -__builtin_inff() || mr == -__builtin_inff()) ? 0.0f : e * fast_exp2(mr - M);
-      a.ws_e[((pbase + hh) * a.NT + t0 + tlc) * NSUB + sb] = e;
+      a.ws_e[(pbase + hh) * a.NT * NSUB + (size_t)t0 * NSUB + rem] = e;
     }
   }
 }
@@ -626,7 +688,7 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
 template <int KV, int D>
 static hipError_t launch_partial_t(const PartialArgs& a, bool scored, bool ring, size_t lds_bytes,
                                    hipStream_t st) {
-  dim3 grid(a.nparts, a.Hkv, a.B), block(256);
+  dim3 grid(a.nparts, a.Hkv, a.B), block(64 * kPartialWaves);
   if (scored) {
     if (ring) hipLaunchKernelGGL((kvs_partial<KV, D, true, true>), grid, block, lds_bytes, st, a);
     else hipLaunchKernelGGL((kvs_partial<KV, D, true, false>), grid, block, lds_bytes, st, a);

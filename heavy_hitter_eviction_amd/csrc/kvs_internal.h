@@ -9,6 +9,9 @@ namespace kvs {
 
 enum : int { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
 
+// Waves per decode (partial) workgroup; one such workgroup per compute unit.
+constexpr int kPartialWaves = 8;
+
 struct PartialArgs {
   const void* q;
   const void* k;
@@ -23,6 +26,8 @@ struct PartialArgs {
   float* ws_o;     // [B][Hq][P][D]
   float* ws_e;     // [B][Hq][NT][NSUB] per-tile block sums, relative to the partition max
   int B, Hq, Hkv, G, C, NT, window, nbmax, kwords, tpp, nparts;
+  int dyn;     // 1: waves claim tiles dynamically; 0: fixed round-robin order
+  int oslots;  // LDS output slots of the wave merge: kPartialWaves or kPartialWaves / 2
   float scale_log2;
 };
 

@@ -74,6 +74,11 @@ typedef enum {
  *   q_dtype        KVS_F32 with a KVS_F32 cache, KVS_BF16 otherwise; the
  *                  attention output has the same type
  *   softmax_scale  logit multiplier, finite and > 0 (usually 1/sqrt(d))
+ *   deterministic  0: the decode kernel's waves share each partition's
+ *                  tiles dynamically (fastest; the rounding of out and of
+ *                  the block masses can differ in the last bits between
+ *                  runs); 1: fixed tile order, results bit-identical between
+ *                  runs and between scored and unscored calls
  */
 typedef struct {
   int32_t batch;
@@ -87,6 +92,7 @@ typedef struct {
   int32_t kv_dtype;  /* kvs_dtype */
   int32_t q_dtype;   /* kvs_dtype */
   float softmax_scale;
+  int32_t deterministic;  /* 0 or 1 */
 } kvs_geom;
 
 /*
@@ -166,11 +172,12 @@ KVS_API int kvs_decode_workspace_bytes(const kvs_geom* geom, size_t* bytes);
  * query heads; Per-Head Attention as a Scoring Signal: score per head, place
  * per 16-token block):
  *   mass_accum[b][p/16] += sum_h sum_{read j in block} p_j
- * Heads are added in ascending order, with no atomics, so results are
- * deterministic; calling the layers in order sums them in that order.
- * With mass_accum == NULL no mass work runs and ``out`` is bit-identical to
+ * Heads are added in ascending order and layers in call order. With
+ * geom.deterministic = 1 results are bit-reproducible, and with
+ * mass_accum == NULL no mass work runs while ``out`` stays bit-identical to
  * the scored call (the tap never changes the math; Context views at marginal
- * cost, Tier 0 invariant).
+ * cost, Tier 0 invariant). With geom.deterministic = 0 both hold up to
+ * floating-point rounding.
  *
  *   q           [B][Hq][d] q_dtype
  *   k_cache, v_cache, k_scale, v_scale, pos_of_slot: as in kvs_append_kv

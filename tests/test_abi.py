@@ -44,7 +44,8 @@ def test_library_exports_every_declared_symbol():
 
 def _geom(api, **kw):
     base = dict(batch=2, n_q_heads=16, n_kv_heads=4, head_dim=128, capacity=256, window=0, ring=0,
-                n_blocks_max=16, kv_dtype=api.KVS_BF16, q_dtype=api.KVS_BF16, softmax_scale=0.088388)
+                n_blocks_max=16, kv_dtype=api.KVS_BF16, q_dtype=api.KVS_BF16, softmax_scale=0.088388,
+                deterministic=0)
     base.update(kw)
     return api.Geom(*[base[f] for f, _ in api.Geom._fields_])
 
@@ -72,6 +73,7 @@ def _decode(api, g, ws_bytes=1 << 20, **ptrs):
     ("kv_dtype", 7, "KVS_EDTYPE"),
     ("softmax_scale", 0.0, "KVS_EINVAL"),
     ("softmax_scale", float("inf"), "KVS_EINVAL"),
+    ("deterministic", 2, "KVS_EINVAL"),
 ])
 def test_bad_geometry_is_rejected(field, value, code):
     api = _lib()

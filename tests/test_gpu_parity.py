@@ -80,9 +80,9 @@ CASES = [
 ]
 
 
-def _build_linear(api, kv, d, Hq, Hkv, C, B, window, seed):
+def _build_linear(api, kv, d, Hq, Hkv, C, B, window, seed, deterministic=False):
     geom = api.CacheGeom(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, capacity=C, window=window,
-                         kv_dtype=kv, q_dtype="f32" if kv == "f32" else "bf16")
+                         kv_dtype=kv, q_dtype="f32" if kv == "f32" else "bf16", deterministic=deterministic)
     cache = api.KVCache(geom)
     w = Hkv * d
     K = _rows((B, C, w), (seed, 1))
@@ -128,24 +128,58 @@ def test_decode_matches_oracle(api, case):
             assert abs(m_gpu[b].sum() - Hq) <= 1e-3
 
 
-def test_unscored_output_is_bit_identical_and_runs_are_deterministic(api):
-    for kv, d, Hq, Hkv, C in (("bf16", 128, 16, 4, 1040), ("fp8", 128, 32, 8, 2064), ("f32", 16, 4, 2, 80)):
-        geom, cache, _, _ = _build_linear(api, kv, d, Hq, Hkv, C, 2, 0, 7)
-        qdt = torch.float32 if kv == "f32" else torch.bfloat16
-        q = torch.from_numpy(_rows((2, Hq, d), (7, 9))).to(qdt).cuda()
-        cur = torch.tensor([C - 1, C // 2], dtype=torch.int32, device="cuda")
-        ws = torch.empty(api.decode_workspace_bytes(geom), dtype=torch.uint8, device="cuda")
-        outs, masses = [], []
-        for scored in (True, True, False):
-            out = torch.empty_like(q)
-            mass = torch.zeros((2, geom.nb), dtype=torch.float32, device="cuda") if scored else None
-            api.decode_attn_scored(cache, q, cur, out, ws, mass_accum=mass)
-            outs.append(out.clone())
-            masses.append(mass.clone() if scored else None)
-        torch.cuda.synchronize()
+def _three_runs(api, kv, d, Hq, Hkv, C, deterministic):
+    geom, cache, K, V = _build_linear(api, kv, d, Hq, Hkv, C, 2, 0, 7, deterministic)
+    qdt = torch.float32 if kv == "f32" else torch.bfloat16
+    q = torch.from_numpy(_rows((2, Hq, d), (7, 9))).to(qdt).cuda()
+    cur = torch.tensor([C - 1, C // 2], dtype=torch.int32, device="cuda")
+    ws = torch.empty(api.decode_workspace_bytes(geom), dtype=torch.uint8, device="cuda")
+    outs, masses = [], []
+    for scored in (True, True, False):
+        out = torch.empty_like(q)
+        mass = torch.zeros((2, geom.nb), dtype=torch.float32, device="cuda") if scored else None
+        api.decode_attn_scored(cache, q, cur, out, ws, mass_accum=mass)
+        outs.append(out.clone())
+        masses.append(mass.clone() if scored else None)
+    torch.cuda.synchronize()
+    return outs, masses, (geom, K, V, q, cur)
+
+
+_DET_CASES = (("bf16", 128, 16, 4, 1040), ("fp8", 128, 32, 8, 2064), ("f32", 16, 4, 2, 80))
+
+
+def test_deterministic_mode_is_bit_reproducible_and_unscored_output_is_identical(api):
+    for kv, d, Hq, Hkv, C in _DET_CASES:
+        outs, masses, _ = _three_runs(api, kv, d, Hq, Hkv, C, True)
         assert torch.equal(outs[0].view(torch.int16 if kv != "f32" else torch.int32),
                            outs[2].view(torch.int16 if kv != "f32" else torch.int32))
         assert torch.equal(outs[0], outs[1]) and torch.equal(masses[0], masses[1])
+
+
+def test_dynamic_mode_matches_deterministic_mode_up_to_rounding(api):
+    # Dynamic tile sharing changes which running max each tile's weights are
+    # taken relative to. Masses and f32-cache outputs then differ by f32
+    # rounding only; bf16/FP8-cache outputs by the bf16 rounding of P in the PV
+    # product, at most 2^-9 sum_j p_j |v_j| per run (plus the bf16 output).
+    for kv, d, Hq, Hkv, C in _DET_CASES:
+        det_o, det_m, _ = _three_runs(api, kv, d, Hq, Hkv, C, True)
+        dyn_o, dyn_m, (geom, K, V, q, cur) = _three_runs(api, kv, d, Hq, Hkv, C, False)
+        ref = det_o[0].float().cpu().numpy().astype(np.float64)
+        if kv == "f32":
+            tol = 1e-5 * np.abs(ref) + 1e-6
+        else:
+            tol = np.zeros_like(ref)
+            for b in range(2):
+                i = int(cur[b])
+                Kd = gs.heads(gs.dequant_rows(K[b, :i + 1], kv), Hkv, d)
+                Vd = gs.heads(gs.dequant_rows(V[b, :i + 1], kv), Hkv, d)
+                _, _, pav = gs.oracle_layer(q[b].double().cpu().numpy(), Kd, Vd, np.arange(i + 1), i, 0, None,
+                                            orc.softmax_scale(d), geom.nb)
+                tol[b] = 2.0 ** -8 * pav + 2.0 ** -7 * np.abs(ref[b])
+        for o in dyn_o:
+            assert (np.abs(o.float().cpu().numpy() - ref) <= tol).all()
+        for m in (dyn_m[0], dyn_m[1]):
+            assert ((m - det_m[0]).abs() <= 1e-5 * det_m[0].abs() + 1e-7).all()
 
 
 def test_keep_mask_skips_dropped_blocks(api):

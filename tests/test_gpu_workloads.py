@@ -212,7 +212,9 @@ def test_397b_fp8_workload_sampled(session_mod):
                                dec.workspace, mass_accum=mass)
         torch.cuda.synchronize()
         gs.close_mass(_np(mass[seq]), m_ref, "fp8", f"layer {layer} mass")
-        assert torch.equal(out, dec.out[layer])
+        # the session runs in dynamic mode: a repeat call may round P
+        # differently, so it is held to the same oracle bound
+        gs.close_o(_np(out[seq].float()), o_ref, "fp8", pav)
 
 
 # ---------------------------------------------------------------- 128K planted
