@@ -71,6 +71,17 @@ def measured_traffic(root, workload_key):
     return int(m_val.group(1)) if h.hexdigest() == m_hash.group(1) else None
 
 
+def _percentiles(xs, ps):
+    xs = sorted(xs)
+    out = []
+    for p in ps:
+        k = (len(xs) - 1) * p / 100.0
+        lo = int(k)
+        hi = min(lo + 1, len(xs) - 1)
+        out.append(xs[lo] + (xs[hi] - xs[lo]) * (k - lo))
+    return out
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -125,6 +136,7 @@ def run_gpu(args, w):
     L = dec.n_layers
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
           for _ in range(args.steps)]
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     keep = None
     for t in range(n_steps):
@@ -132,6 +144,8 @@ def run_gpu(args, w):
             torch.cuda.synchronize()
             start.record()
         timed = t >= args.warmup
+        if timed:
+            sev[t - args.warmup].record()
         keep = dec.keep if (args.evict and not w.window) else None
         for layer in range(L):
             dec.caches[layer].append(K[layer][t], V[layer][t], dec.row_seq, cur[t])
@@ -144,11 +158,13 @@ def run_gpu(args, w):
             api.decode_attn_scored(dec.caches[layer], Q[layer][t], cur[t], dec.out[layer], dec.workspace,
                                    mass_accum=dec.mass, keep_mask=keep, phase="combine")
         dec.close_turn(cur[t])
+    sev[args.steps].record()
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     part_ms = [a.elapsed_time(b) for row in ev for (a, b) in row]
-    return dec, total_ms, part_ms
+    step_ms = [a.elapsed_time(b) for a, b in zip(sev, sev[1:])]
+    return dec, total_ms, part_ms, step_ms
 
 
 def oracle_baseline(w, seed, seconds):
@@ -220,7 +236,7 @@ def main():
     from heavy_hitter_eviction_amd import workloads
     w = workloads.ALL[args.workload]
 
-    dec, total_ms, part_ms = run_gpu(args, w)
+    dec, total_ms, part_ms, step_ms = run_gpu(args, w)
     ms_step = total_ms / args.steps
     steps_t = range(args.warmup, args.warmup + args.steps)
     bytes_step = sum(w.kv_bytes_at_step(t) for t in steps_t) / args.steps
@@ -251,6 +267,7 @@ def main():
             "recent_tokens": w.recent_tokens, "mode": "evict" if args.evict else "score-only",
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "step_ms_p10_p50_p90": [round(float(x), 4) for x in _percentiles(step_ms, (10, 50, 90))],
         "blocks_scored_per_s": round(blocks_step / (ms_step / 1e3), 1),
         "roofline": {
             "kernel": "kvs_partial",

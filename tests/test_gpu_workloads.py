@@ -129,6 +129,9 @@ def _check_selection_on_gpu_scores(dec, w, cur, alive=None):
 # ---------------------------------------------------------------- 35B-like bf16
 
 def test_35b_bf16_workload(session_mod):
+    """All 64 steps: side-car rule, mass totals and the selection on the GPU's
+    scores. Every sequence and layer against the oracle at steps 0, 1, 15, 31,
+    47 and 63 (output per layer, Attended summed over the 10 layers)."""
     api, session = session_mod
     w = workloads.QWEN35B_BF16
     seed = 7
@@ -136,7 +139,8 @@ def test_35b_bf16_workload(session_mod):
     _prefill_gpu(dec, w, seed)
     Q, K, V = _step_inputs(w, seed, w.n_layers, w.steps)
     scale = orc.softmax_scale(w.head_dim)
-    check = {0, 1, 31, w.steps - 1}
+    check = (0, 1, 15, 31, 47, w.steps - 1)
+    got = {}
     for t in range(w.steps):
         i = w.context + t
         cur = torch.full((w.batch,), i, dtype=torch.int32, device="cuda")
@@ -148,106 +152,133 @@ def test_35b_bf16_workload(session_mod):
         _sidecar_rule(prev_ema, prev_cum, att, _np(dec.ema), _np(dec.cum), w.alpha)
         assert np.abs(att.sum(axis=1) - w.n_layers * w.n_q_heads).max() <= 1e-2
         _check_selection_on_gpu_scores(dec, w, _np(cur))
-        if t not in check:
-            continue
-        for seq in (0, w.batch - 1):
-            mass = np.zeros(dec.geom.nb)
-            for layer in range(w.n_layers):
-                Kd = gs.dequant_rows(_held_rows(w, seed, layer, seq, synth.T_K, i), "bf16")
-                Vd = gs.dequant_rows(_held_rows(w, seed, layer, seq, synth.T_V, i), "bf16")
+        if t in check:
+            got[t] = ([_np(dec.out[layer].float()) for layer in range(w.n_layers)], att.copy())
+    i_end = w.context + w.steps - 1
+    for seq in range(w.batch):
+        mass = {t: np.zeros(dec.geom.nb) for t in check}
+        for layer in range(w.n_layers):
+            Kd = gs.heads(gs.dequant_rows(_held_rows(w, seed, layer, seq, synth.T_K, i_end), "bf16"),
+                          w.n_kv_heads, w.head_dim)
+            Vd = gs.heads(gs.dequant_rows(_held_rows(w, seed, layer, seq, synth.T_V, i_end), "bf16"),
+                          w.n_kv_heads, w.head_dim)
+            for t in check:
+                i = w.context + t
                 q = _np(Q[layer][t][seq].float()).astype(np.float64)
-                o_ref, m_ref, pav = gs.oracle_layer(q, gs.heads(Kd, w.n_kv_heads, w.head_dim),
-                                                    gs.heads(Vd, w.n_kv_heads, w.head_dim), np.arange(i + 1), i,
-                                                    0, None, scale, dec.geom.nb)
-                gs.close_o(_np(dec.out[layer][seq].float()), o_ref, "bf16", pav)
-                mass += m_ref
-            gs.close_mass(att[seq], mass, "bf16", "attended (10 layers)")
+                o_ref, m_ref, pav = gs.oracle_layer(q, Kd[:, :i + 1], Vd[:, :i + 1], np.arange(i + 1), i, 0, None,
+                                                    scale, dec.geom.nb)
+                gs.close_o(got[t][0][layer][seq], o_ref, "bf16", pav)
+                mass[t] += m_ref
+        for t in check:
+            gs.close_mass(got[t][1][seq], mass[t], "bf16", f"attended (10 layers), sequence {seq}, step {t}")
 
 
 # ---------------------------------------------------------------- 397B-like FP8, 32K
 
 def test_397b_fp8_workload_sampled(session_mod):
+    """72 decode steps, across the 64-step trajectory wrap. Every step: the
+    side-car rule, the trajectory slot, mass totals and the selection on the
+    GPU's scores. Sequence 0, all 15 layers: FP8 codes and scales of every
+    held slot bit-exact, and each layer's output and Attended (summed over
+    the layers) against the oracle at steps 0, 1, 63, 64 and 71."""
     api, session = session_mod
     w = workloads.QWEN397B_FP8
     seed = 19
-    n_steps = 3
+    n_steps = 72
+    check_steps = (0, 1, 63, 64, 71)
     dec = session.ScoredDecoder(w)
     _prefill_gpu(dec, w, seed)
     Q, K, V = _step_inputs(w, seed, w.n_layers, n_steps)
+    geom = dec.geom
+    got = {}
     for t in range(n_steps):
-        cur = torch.full((w.batch,), w.context + t, dtype=torch.int32, device="cuda")
+        i = w.context + t
+        cur = torch.full((w.batch,), i, dtype=torch.int32, device="cuda")
         prev_ema, prev_cum = _np(dec.ema), _np(dec.cum)
         dec.step([Q[l][t] for l in range(w.n_layers)], [K[l][t] for l in range(w.n_layers)],
                  [V[l][t] for l in range(w.n_layers)], cur)
         torch.cuda.synchronize()
         att = _np(dec.attended)
         _sidecar_rule(prev_ema, prev_cum, att, _np(dec.ema), _np(dec.cum), w.alpha)
+        assert np.array_equal(_np(dec.traj[:, t % w.traj_cap]), att)
         assert np.abs(att.sum(axis=1) - w.n_layers * w.n_q_heads).max() <= 2e-2
         _check_selection_on_gpu_scores(dec, w, _np(cur))
-    i = w.context + n_steps - 1
-    geom = dec.geom
+        if t in check_steps:
+            got[t] = ([_np(dec.out[layer][0].float()) for layer in range(w.n_layers)], att[0].copy())
     scale = orc.softmax_scale(w.head_dim)
-    for seq, layer in ((0, 0), (w.batch - 1, w.n_layers - 1)):
-        kr = _held_rows(w, seed, layer, seq, synth.T_K, i)
-        vr = _held_rows(w, seed, layer, seq, synth.T_V, i)
-        kc, ks = orc.fp8_encode_rows(kr)
-        vc, vs = orc.fp8_encode_rows(vr)
+    i_end = w.context + n_steps - 1
+    mass = {t: np.zeros(geom.nb) for t in check_steps}
+    for layer in range(w.n_layers):
         cache = dec.caches[layer]
-        slots = np.unique(np.concatenate([np.arange(0, 40), np.arange(16000, 16040), np.arange(i - 40, i + 1)]))
-        got_k = gs.logical_rows(_np(cache.k), w.batch, w.n_kv_heads, w.capacity, w.head_dim, 1, seq, slots, "k")
-        got_v = gs.logical_rows(_np(cache.v), w.batch, w.n_kv_heads, w.capacity, w.head_dim, 1, seq, slots, "v")
-        assert np.array_equal(got_k, kc[slots]) and np.array_equal(got_v, vc[slots])
-        sk = _np(cache.k_scale).reshape(w.batch, w.capacity)[seq, :i + 1]
-        sv = _np(cache.v_scale).reshape(w.batch, w.capacity)[seq, :i + 1]
-        assert np.array_equal(sk, ks) and np.array_equal(sv, vs)
-        Kd, Vd = orc.fp8_decode_rows(kc, ks), orc.fp8_decode_rows(vc, vs)
-        q = Q[layer][n_steps - 1]
-        o_ref, m_ref, pav = gs.oracle_layer(_np(q[seq].float()).astype(np.float64), gs.heads(Kd, 8, 128),
-                                            gs.heads(Vd, 8, 128), np.arange(i + 1), i, 0, None, scale, geom.nb)
-        gs.close_o(_np(dec.out[layer][seq].float()), o_ref, "fp8", pav)
-        # this layer's own block masses, from a separate scored call
-        mass = torch.zeros((w.batch, geom.nb), dtype=torch.float32, device="cuda")
-        out = torch.empty_like(q)
-        api.decode_attn_scored(cache, q, torch.full((w.batch,), i, dtype=torch.int32, device="cuda"), out,
-                               dec.workspace, mass_accum=mass)
-        torch.cuda.synchronize()
-        gs.close_mass(_np(mass[seq]), m_ref, "fp8", f"layer {layer} mass")
-        # the session runs in dynamic mode: a repeat call may round P
-        # differently, so it is held to the same oracle bound
-        gs.close_o(_np(out[seq].float()), o_ref, "fp8", pav)
+        kc, ks = orc.fp8_encode_rows(_held_rows(w, seed, layer, 0, synth.T_K, i_end))
+        vc, vs = orc.fp8_encode_rows(_held_rows(w, seed, layer, 0, synth.T_V, i_end))
+        slots = np.arange(i_end + 1)
+        got_k = gs.logical_rows(_np(cache.k), w.batch, w.n_kv_heads, w.capacity, w.head_dim, 1, 0, slots, "k")
+        got_v = gs.logical_rows(_np(cache.v), w.batch, w.n_kv_heads, w.capacity, w.head_dim, 1, 0, slots, "v")
+        assert np.array_equal(got_k, kc) and np.array_equal(got_v, vc)
+        assert np.array_equal(_np(cache.k_scale).reshape(w.batch, w.capacity)[0, :i_end + 1], ks)
+        assert np.array_equal(_np(cache.v_scale).reshape(w.batch, w.capacity)[0, :i_end + 1], vs)
+        Kd = gs.heads(orc.fp8_decode_rows(kc, ks), w.n_kv_heads, w.head_dim)
+        Vd = gs.heads(orc.fp8_decode_rows(vc, vs), w.n_kv_heads, w.head_dim)
+        for t in check_steps:
+            i = w.context + t
+            q = _np(Q[layer][t][0].float()).astype(np.float64)
+            o_ref, m_ref, pav = gs.oracle_layer(q, Kd[:, :i + 1], Vd[:, :i + 1], np.arange(i + 1), i, 0, None,
+                                                scale, geom.nb)
+            gs.close_o(got[t][0][layer], o_ref, "fp8", pav)
+            mass[t] += m_ref
+        del Kd, Vd
+    for t in check_steps:
+        gs.close_mass(got[t][1], mass[t], "fp8", f"attended (15 layers), step {t}")
 
 
 # ---------------------------------------------------------------- 128K planted
 
 def test_128k_planted_workload(session_mod):
+    """64 decode steps at 128K context. Every step: side-car rule, mass totals
+    and the selection on the GPU's scores. All four sequences against the
+    oracle at every eighth step (and steps 1 and 63), with the planted anchor
+    and needle kept."""
     api, session = session_mod
     w = workloads.DOCQA_128K
     seed = 41
-    n_steps = 2
+    n_steps = 64
+    check_steps = (0, 1, 8, 16, 24, 32, 40, 48, 56, 63)
     dec = session.ScoredDecoder(w)
     _prefill_gpu(dec, w, seed)
     Q, K, V = _step_inputs(w, seed, 1, n_steps)
+    got = {}
     for t in range(n_steps):
         cur = torch.full((w.batch,), w.context + t, dtype=torch.int32, device="cuda")
+        prev_ema, prev_cum = _np(dec.ema), _np(dec.cum)
         dec.step([Q[0][t]], [K[0][t]], [V[0][t]], cur)
-    torch.cuda.synchronize()
-    _check_selection_on_gpu_scores(dec, w, _np(cur))
-    i = w.context + n_steps - 1
+        torch.cuda.synchronize()
+        att = _np(dec.attended)
+        _sidecar_rule(prev_ema, prev_cum, att, _np(dec.ema), _np(dec.cum), w.alpha)
+        assert np.abs(att.sum(axis=1) - w.n_q_heads).max() <= 2e-3
+        _check_selection_on_gpu_scores(dec, w, _np(cur))
+        if t in check_steps:
+            n = _np(dec.n_sel)
+            for seq in range(w.batch):
+                # Per-Head Attention as a Scoring Signal, 128K example: the
+                # anchor blocks (positions 0-100) and the needle block near 64K
+                # are kept
+                kept = set(_np(dec.sel_ids[seq, :n[seq]]).tolist())
+                assert set(range(0, 7)) <= kept and (workloads.PLANT_NEEDLE.start // 16) in kept
+            got[t] = (_np(dec.out[0].float()), att.copy())
     scale = orc.softmax_scale(w.head_dim)
-    att = _np(dec.attended)
-    n = _np(dec.n_sel)
-    for seq in (0, 3):
-        Kd = gs.dequant_rows(_held_rows(w, seed, 0, seq, synth.T_K, i), "bf16")
-        Vd = gs.dequant_rows(_held_rows(w, seed, 0, seq, synth.T_V, i), "bf16")
-        o_ref, m_ref, pav = gs.oracle_layer(_np(Q[0][n_steps - 1][seq].float()).astype(np.float64),
-                                            gs.heads(Kd, 8, 128), gs.heads(Vd, 8, 128), np.arange(i + 1), i, 0,
-                                            None, scale, dec.geom.nb)
-        gs.close_o(_np(dec.out[0][seq].float()), o_ref, "bf16", pav)
-        gs.close_mass(att[seq], m_ref, "bf16", "attended")
-        # Per-Head Attention as a Scoring Signal, 128K example: the anchor
-        # blocks (positions 0-100) and the needle block near 64K are kept
-        kept = set(_np(dec.sel_ids[seq, :n[seq]]).tolist())
-        assert set(range(0, 7)) <= kept and (workloads.PLANT_NEEDLE.start // 16) in kept
+    i_end = w.context + n_steps - 1
+    for seq in range(w.batch):
+        Kd = gs.heads(gs.dequant_rows(_held_rows(w, seed, 0, seq, synth.T_K, i_end), "bf16"), 8, 128)
+        Vd = gs.heads(gs.dequant_rows(_held_rows(w, seed, 0, seq, synth.T_V, i_end), "bf16"), 8, 128)
+        for t in check_steps:
+            i = w.context + t
+            o_ref, m_ref, pav = gs.oracle_layer(_np(Q[0][t][seq].float()).astype(np.float64), Kd[:, :i + 1],
+                                                Vd[:, :i + 1], np.arange(i + 1), i, 0, None, scale, dec.geom.nb)
+            o_gpu, att = got[t]
+            gs.close_o(o_gpu[seq], o_ref, "bf16", pav)
+            gs.close_mass(att[seq], m_ref, "bf16", f"attended, step {t}")
+        del Kd, Vd
 
 
 # ---------------------------------------------------------------- 35B FP8 ring window
