@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=("decode", "reattend"), default="decode",
+                    help="decode: the scored decode step (headline); reattend: Tier 2, a new query "
+                         "over the blocks the selection kept")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
                          "(a reference for hardware byte counters)")
@@ -167,6 +170,88 @@ def run_gpu(args, w):
     return dec, total_ms, part_ms, step_ms
 
 
+def run_reattend(args, w):
+    """Tier 2 re-attend (Context views at marginal cost): after ``warmup``
+    scored decode steps have built Cumulative and the selection, time a new
+    query per layer over only the selected blocks (kvs_reattend_blocks), and a
+    full-context decode of the same query for comparison."""
+    import torch
+
+    from heavy_hitter_eviction_amd import api, synth
+    from heavy_hitter_eviction_amd.session import ScoredDecoder
+
+    if not w.select or w.ring:
+        raise SystemExit("re-attend needs a workload with block selection on a linear cache")
+    dec = ScoredDecoder(w)
+    prefill(dec, w, args.seed)
+    n_warm = max(1, args.warmup)
+    Q, K, V = step_inputs(w, args.seed, n_warm, dec.n_layers)
+    L = dec.n_layers
+    for t in range(n_warm):
+        cur = torch.full((w.batch,), w.context + t, dtype=torch.int32, device="cuda")
+        dec.step([Q[l][t] for l in range(L)], [K[l][t] for l in range(L)], [V[l][t] for l in range(L)], cur)
+    torch.cuda.synchronize()
+    qdt = torch.bfloat16 if w.q_dtype == "bf16" else torch.float32
+    # the new question: seeded queries from a chunk no decode step draws
+    qn = [synth.new_query(w, args.seed, l, "cuda").reshape(w.batch, w.n_q_heads, w.head_dim).to(qdt).contiguous()
+          for l in range(L)]
+    sel, nsel = dec.sel_ids, dec.n_sel
+    out = torch.empty_like(qn[0])
+    mass = torch.zeros_like(dec.mass)
+    i = int(cur[0])
+    per_key = 2 * w.n_kv_heads * w.head_dim * (1 if w.kv_dtype == "fp8" else 2 if w.kv_dtype == "bf16" else 4) \
+        + (8 if w.kv_dtype == "fp8" else 0)
+    ids_h, n_h = sel.cpu().numpy(), nsel.cpu().numpy()
+    keys = sum(min(16, i + 1 - 16 * int(blk)) for b in range(w.batch) for blk in ids_h[b, :n_h[b]] if 16 * blk <= i)
+    bytes_call = keys * per_key
+    full_bytes = w.batch * (i + 1) * per_key
+
+    def timed(fn, reps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps * L)]
+        for r in range(reps):
+            for l in range(L):
+                a, b = evs[r * L + l]
+                a.record()
+                fn(l)
+                b.record()
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+
+    re = lambda l: api.reattend_blocks(dec.caches[l], qn[l], cur, sel, nsel, out, dec.workspace,  # noqa: E731
+                                       mass_accum=mass)
+    full = lambda l: api.decode_attn_scored(dec.caches[l], qn[l], cur, out, dec.workspace,  # noqa: E731
+                                            mass_accum=mass)
+    timed(re, 1)
+    re_ms = timed(re, args.steps)
+    timed(full, 1)
+    full_ms = timed(full, args.steps)
+    gbs = bytes_call / (re_ms / 1e3) / 1e9
+    return {
+        "metric": "Tier 2 re-attend: KV GB/s over the selected blocks, per layer call",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": n_warm,
+        "ms_per_step": round(re_ms * L, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.kv_dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "mode": "reattend", "selected_fraction":
+                   round(bytes_call / full_bytes, 4), "budget_blocks": w.budget_blocks,
+                   "recent_tokens": w.recent_tokens, "layers": L, "context_at_query": i + 1},
+        "us_per_layer": round(re_ms * 1e3, 2),
+        "full_context_us_per_layer": round(full_ms * 1e3, 2),
+        "speedup_vs_full_context": round(full_ms / re_ms, 3),
+        "roofline": {"kernel": "kvs_partial + kvs_combine (re-attend call)", "bound": "hbm",
+                     "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(re_ms * 1e3, 2), "bytes_per_launch": int(bytes_call)},
+    }
+
+
 def oracle_baseline(w, seed, seconds):
     """Time the float64 oracle (as it stands) on (sequence, layer) units of the
     same workload at the first timed step: FP8 decode (or bf16 widening) of the
@@ -235,6 +320,9 @@ def main():
         B.build()
     from heavy_hitter_eviction_amd import workloads
     w = workloads.ALL[args.workload]
+    if args.mode == "reattend":
+        print(json.dumps(run_reattend(args, w)), flush=True)
+        return
 
     dec, total_ms, part_ms, step_ms = run_gpu(args, w)
     ms_step = total_ms / args.steps

@@ -26,7 +26,8 @@ TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8
 
 EXPORTED = (
     "kvs_cache_bytes", "kvs_encode_fp8", "kvs_append_kv", "kvs_decode_workspace_bytes",
-    "kvs_decode_attn_scored", "kvs_decode_partial", "kvs_decode_combine", "kvs_update_sidecar", "kvs_select_blocks", "kvs_status_str",
+    "kvs_decode_attn_scored", "kvs_decode_partial", "kvs_decode_combine", "kvs_reattend_blocks",
+    "kvs_update_sidecar", "kvs_select_blocks", "kvs_status_str",
     "kvs_version",
 )
 
@@ -61,6 +62,7 @@ def _load():
         "kvs_decode_attn_scored": [G, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "kvs_decode_partial": [G, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "kvs_decode_combine": [G, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "kvs_reattend_blocks": [G, P, P, P, P, P, P, P, P, I32, P, P, P, SZ, P],
         "kvs_update_sidecar": [P, P, P, P, P, I32, I32, I32, I64, F, P],
         "kvs_select_blocks": [P, P, P, I32, I32, I32, I32, I32, P, P, P, P],
     }
@@ -240,6 +242,37 @@ def decode_attn_scored(cache: KVCache, q: torch.Tensor, cur_pos: torch.Tensor, o
               _ptr(cache.v_scale), _ptr(cache.pos_of_slot), _ptr(cur_pos), _ptr(keep_mask), _ptr(out),
               _ptr(mass_accum), _ptr(workspace), ws_bytes, _stream(stream)),
            f"kvs_decode ({phase})")
+    return out
+
+
+def reattend_blocks(cache: KVCache, q: torch.Tensor, cur_pos: torch.Tensor, block_ids: torch.Tensor,
+                    n_ids: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
+                    mass_accum: torch.Tensor | None = None, stream=None):
+    """Attention of a new query over the listed blocks only (kvs_reattend_blocks):
+    ``block_ids`` int32 [B, S] (any order, repeats allowed), ``n_ids`` int32 [B]."""
+    g = cache.geom
+    _device_check(q, cur_pos, block_ids, n_ids, out, workspace, mass_accum)
+    qdt = TORCH_DTYPES[g.q_dtype]
+    if q.dtype != qdt or out.dtype != qdt:
+        raise TypeError("q and out must have the geometry's q dtype")
+    if q.shape != (g.batch, g.n_q_heads, g.head_dim) or out.shape != q.shape:
+        raise ValueError("q/out must be [B, Hq, d]")
+    if cur_pos.dtype != torch.int32 or cur_pos.numel() != g.batch:
+        raise ValueError("cur_pos must be int32 [B]")
+    if block_ids.dtype != torch.int32 or block_ids.dim() != 2 or block_ids.shape[0] != g.batch \
+            or not block_ids.is_contiguous():
+        raise ValueError("block_ids must be contiguous int32 [B, S]")
+    if n_ids.dtype != torch.int32 or n_ids.numel() != g.batch:
+        raise ValueError("n_ids must be int32 [B]")
+    if mass_accum is not None and (mass_accum.dtype != torch.float32 or mass_accum.numel() != g.batch * g.nb):
+        raise ValueError("mass_accum must be float32 [B, NBmax]")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    gc = g.c()
+    _check(LIB.kvs_reattend_blocks(ctypes.byref(gc), _ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(cache.k_scale),
+                                   _ptr(cache.v_scale), _ptr(cur_pos), _ptr(block_ids), _ptr(n_ids),
+                                   block_ids.shape[1], _ptr(out), _ptr(mass_accum), _ptr(workspace), ws_bytes,
+                                   _stream(stream)),
+           "kvs_reattend_blocks")
     return out
 
 

@@ -255,6 +255,30 @@ int kvs_decode_attn_scored(KVS_DECODE_ARGS) {
   return hip_status(kvs::launch_combine(c, g->ring != 0, g->q_dtype == KVS_BF16, s));
 }
 
+int kvs_reattend_blocks(const kvs_geom* g, const void* q, const void* k_cache, const void* v_cache,
+                        const float* k_scale, const float* v_scale, const int32_t* cur_pos,
+                        const int32_t* block_ids, const int32_t* n_ids, int32_t ids_stride, void* out,
+                        float* mass_accum, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!g) return KVS_EINVAL;
+  if (g->ring != 0 || g->window != 0) return KVS_EINVAL;  // the list replaces masks and windows
+  if (!block_ids || !n_ids || ids_stride < 1) return KVS_EINVAL;
+  if (!aligned16(block_ids) || !aligned16(n_ids)) return KVS_EALIGN;
+  Plan p;
+  kvs::PartialArgs a;
+  kvs::CombineArgs c;
+  int kv;
+  int st = decode_setup(g, q, k_cache, v_cache, k_scale, v_scale, nullptr, cur_pos, nullptr, out,
+                        mass_accum, workspace, workspace_bytes, &p, &a, &c, &kv);
+  if (st) return st;
+  a.ids = block_ids;
+  a.n_ids = n_ids;
+  a.ids_stride = ids_stride;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = kvs::launch_partial(kv, g->head_dim, a, mass_accum != nullptr, false, p.lds_partial, s);
+  if (e != hipSuccess) return KVS_EHIP;
+  return hip_status(kvs::launch_combine(c, false, g->q_dtype == KVS_BF16, s));
+}
+
 int kvs_update_sidecar(float* mass_accum, float* attended, float* ema, float* cum, float* traj,
                        int32_t batch, int32_t n_blocks_max, int32_t traj_cap, int64_t step,
                        float alpha, void* stream) {

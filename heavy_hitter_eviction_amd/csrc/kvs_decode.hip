@@ -155,17 +155,34 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
     if (a.window > 0) tb = min(te, max(tb, max(lo, 0) / kTile));
   }
 
-  // With a keep mask on a linear cache (tile = block), wave 0 compacts the
-  // partition's kept tiles into tlist, so evicted tiles are never read.
-  // Without one, the list is implicit: entry i is tile tb + i.
+  // With a keep mask, or a list of block ids to re-attend, on a linear cache
+  // (tile = block), wave 0 compacts the partition's readable tiles into tlist,
+  // so other tiles are never read. Without either, the list is implicit:
+  // entry i is tile tb + i.
   const uint32_t* keep_b = a.keep ? a.keep + (size_t)b * a.kwords : nullptr;
-  const bool use_list = !RING && keep_b != nullptr;
+  const bool use_ids = !RING && a.ids != nullptr;
+  const bool use_list = !RING && (keep_b != nullptr || use_ids);
   if (use_list && wave == 0) {
+    // a block-id list becomes a bitmap over [tb, te) first (in the side-data
+    // area, unused until the loop); ids may repeat and come in any order
+    uint32_t* bm = (uint32_t*)side_area;
+    if (use_ids) {
+      for (int wd = lane; wd < ((te - tb + 31) >> 5); wd += 64) bm[wd] = 0u;
+      const int nid = min(max(a.n_ids[b], 0), a.ids_stride);
+      const int32_t* idb = a.ids + (size_t)b * a.ids_stride;
+      for (int k = lane; k < nid; k += 64) {
+        const int id = idb[k];
+        if (id >= tb && id < te) atomicOr(&bm[(id - tb) >> 5], 1u << ((id - tb) & 31));
+      }
+    }
     int n = 0;
     for (int c = tb; c < te; c += 64) {
       const int t = c + lane;
       bool kept = false;
-      if (t < te) kept = t >= a.nbmax || ((keep_b[t >> 5] >> (t & 31)) & 1u);
+      if (t < te) {
+        if (use_ids) kept = (bm[(t - tb) >> 5] >> ((t - tb) & 31)) & 1u;
+        else kept = t >= a.nbmax || ((keep_b[t >> 5] >> (t & 31)) & 1u);
+      }
       const uint64_t m = __ballot(kept);
       if (kept) tlist[n + __popcll(m & ((1ull << lane) - 1ull))] = t;
       n += __popcll(m);

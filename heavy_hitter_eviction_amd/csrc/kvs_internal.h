@@ -21,11 +21,14 @@ struct PartialArgs {
   const int32_t* pos_of_slot;
   const int32_t* cur_pos;
   const uint32_t* keep;
+  const int32_t* ids;    // [B][ids_stride] block ids to read (re-attend), or NULL
+  const int32_t* n_ids;  // [B] entries of ids used per sequence
   float* ws_m;     // [B][Hq][P]
   float* ws_l;     // [B][Hq][P]
   float* ws_o;     // [B][Hq][P][D]
   float* ws_e;     // [B][Hq][NT][NSUB] per-tile block sums, relative to the partition max
   int B, Hq, Hkv, G, C, NT, window, nbmax, kwords, tpp, nparts;
+  int ids_stride;
   int dyn;     // 1: waves claim tiles dynamically; 0: fixed round-robin order
   int oslots;  // LDS output slots of the wave merge: kPartialWaves or kPartialWaves / 2
   float scale_log2;

@@ -91,6 +91,16 @@ def step_block(w: Workload, seed: int, layer: int, chunk: int, tensor: int, devi
     return block.contiguous()
 
 
+def new_query(w: Workload, seed: int, layer: int, device="cpu") -> torch.Tensor:
+    """A query ``[B, Hq*d]`` from a stream no decode step draws: the "new
+    question" of a re-attend over stored spans."""
+    q = normal((w.batch, w.n_q_heads * w.head_dim), (seed, _tag(w), T_Q, layer, 2 << 20), device)
+    if w.planted:
+        u = _directions(w, seed, device) * plant_gain(w.head_dim)
+        q = q + u.repeat_interleave(w.group, dim=1).reshape(w.batch, -1)
+    return q.contiguous()
+
+
 def step_rows(w: Workload, seed: int, layer: int, step: int, tensor: int, device="cpu") -> torch.Tensor:
     """The rows of one decode step (see ``step_block``)."""
     chunk = step // STEP_CHUNK

@@ -223,6 +223,38 @@ KVS_API int kvs_decode_combine(const kvs_geom* geom, const void* q, const void* 
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kvs_reattend_blocks -- one layer of attention for a new query over a chosen
+ * set of cached blocks only (Context views at marginal cost, "Tier 2 —
+ * RE-ATTEND" and "Fact 3": a relevance question about stored spans is asked by
+ * running the new query against the cached keys of the candidate spans and
+ * reading the resulting distribution; the keys and values are reused, and the
+ * read costs O(selected tokens)).
+ *
+ * Exactly kvs_decode_attn_scored on a linear cache (ring == 0, window == 0,
+ * else KVS_EINVAL) with the keep mask replaced by a list: key slot t is read
+ * when t <= cur_pos[b] and block t / 16 appears among the first n_ids[b]
+ * entries of block_ids[b]. Entries may repeat and come in any order; entries
+ * outside 0 .. C/16-1 are ignored (the selection's sel_ids / n_sel can be
+ * passed as they are). ``out`` is the attention over those keys; when
+ * mass_accum is not NULL the per-block masses of the new query (its
+ * distribution over the chosen spans, summed over query heads) are added to
+ * mass_accum[b][block]. A sequence with no readable key gets a zero output
+ * and no mass.
+ *
+ *   block_ids   [B][ids_stride] int32, device, 16-byte aligned
+ *   n_ids       [B] int32, device, 16-byte aligned; values are clamped to
+ *               0 .. ids_stride
+ *   ids_stride  >= 1
+ *   other arguments as in kvs_decode_attn_scored (pos_of_slot and keep_mask
+ *   do not apply)
+ */
+KVS_API int kvs_reattend_blocks(const kvs_geom* geom, const void* q, const void* k_cache,
+                                const void* v_cache, const float* k_scale, const float* v_scale,
+                                const int32_t* cur_pos, const int32_t* block_ids, const int32_t* n_ids,
+                                int32_t ids_stride, void* out, float* mass_accum, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
  * kvs_update_sidecar -- close one turn (Context views at marginal cost,
  * section 2 Tier 1 and section 3: {Attended, EMA, Cumulative, traj}, O(1) per
  * block per turn). With A = mass_accum (this step's mass):

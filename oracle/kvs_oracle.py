@@ -26,6 +26,10 @@ in the order the source pages state them:
 * Per-Head Attention as a Scoring Signal, "Scoring granularity, not eviction
   granularity": the unit that is scored and kept is a (sequence, 16-token
   block); heads are only a scoring input.
+* Context views at marginal cost, "Tier 2 — RE-ATTEND" and "Fact 3": a new
+  query is run against the cached keys of a chosen subset of spans, and the
+  resulting distribution is read; cached keys and values are reused as they
+  are.
 * Context Optimization, "H2O KV Cache Eviction": post-softmax scores are summed
   over all query heads (GQA-aware) and over steps; sinks and recent tokens are
   kept unconditionally and the top scorers among the rest survive.
@@ -237,6 +241,22 @@ def attend_scored(q, K_all, V_all, positions, i, window, alive, scale, n_blocks)
     positions = np.asarray(positions, dtype=np.int64)
     sel = np.array([key_visible(int(p), i, window) and block_alive(alive, block_of(int(p)))
                     for p in positions], dtype=bool)
+    o, p = attend(q, np.asarray(K_all)[:, sel], np.asarray(V_all)[:, sel], scale)
+    return o, block_mass(p, positions[sel], n_blocks)
+
+
+def reattend_blocks(q, K_all, V_all, positions, i, block_ids, scale, n_blocks):
+    """Tier 2 re-attend (Context views at marginal cost, "Tier 2 — RE-ATTEND",
+    "Fact 3"): attention of the query ``q`` over only the cached keys whose
+    block is among ``block_ids`` (a set: order and repeats do not matter) and
+    whose position is at most ``i``. Returns ``(o, mass)`` as attend_scored;
+    the mass is the new query's distribution over the chosen spans, summed
+    over query heads. With no such key the output and the mass are zero."""
+    chosen = {int(b) for b in np.asarray(block_ids).ravel()}
+    positions = np.asarray(positions, dtype=np.int64)
+    sel = np.array([int(p) <= i and block_of(int(p)) in chosen for p in positions], dtype=bool)
+    if not sel.any():
+        return np.zeros(np.asarray(q).shape), np.zeros(n_blocks)
     o, p = attend(q, np.asarray(K_all)[:, sel], np.asarray(V_all)[:, sel], scale)
     return o, block_mass(p, positions[sel], n_blocks)
 

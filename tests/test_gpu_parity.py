@@ -213,6 +213,65 @@ def test_keep_mask_skips_dropped_blocks(api):
             gs.close_mass(mass[b].cpu().numpy(), m_ref, kv)
 
 
+REATTEND_CASES = [
+    # kv,   d,  Hq, Hkv, C,    B
+    ("bf16", 128, 16, 4, 1040, 3),
+    ("fp8", 128, 32, 8, 2064, 2),
+    ("fp8", 64, 8, 2, 400, 2),
+    ("f32", 64, 8, 4, 272, 2),
+]
+
+
+@pytest.mark.parametrize("case", REATTEND_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_reattend_blocks_matches_oracle(api, case):
+    """Tier 2 re-attend (Context views at marginal cost): a new query over a
+    list of blocks only. Lists are unsorted with repeats and out-of-range
+    entries, one sequence's list is empty (zero output, no mass)."""
+    kv, d, Hq, Hkv, C, B = case
+    geom, cache, K, V = _build_linear(api, kv, d, Hq, Hkv, C, B, 0, 23)
+    rng = np.random.default_rng(11)
+    nbk = C // 16
+    S = 48
+    ids = np.full((B, S), -7, dtype=np.int32)
+    n_ids = np.zeros(B, dtype=np.int32)
+    for b in range(B - 1):
+        k = int(rng.integers(1, S - 4))
+        pick = rng.integers(0, nbk, size=k)
+        pick[: k // 4] = pick[k // 4: 2 * (k // 4)]          # repeats
+        ids[b, :k] = pick
+        ids[b, k] = nbk + 3                                   # ignored: past the cache
+        n_ids[b] = k + 1
+    n_ids[B - 1] = 0                                          # nothing chosen
+    ids[B - 1, :5] = [0, 1, 2, 3, 4]                          # present but beyond n_ids
+    cur = np.array([C - 1] + [int(rng.integers(100, C)) for _ in range(B - 1)], dtype=np.int32)
+    qdt = torch.float32 if kv == "f32" else torch.bfloat16
+    q = torch.from_numpy(_rows((B, Hq, d), (23, 8))).to(qdt)
+    out = torch.empty_like(q).cuda()
+    mass = torch.zeros((B, geom.nb), dtype=torch.float32, device="cuda")
+    ws = torch.empty(api.decode_workspace_bytes(geom), dtype=torch.uint8, device="cuda")
+    api.reattend_blocks(cache, q.cuda(), gs.to_dev(cur), gs.to_dev(ids), gs.to_dev(n_ids), out, ws,
+                        mass_accum=mass)
+    torch.cuda.synchronize()
+    for b in range(B):
+        i = int(cur[b])
+        chosen = ids[b, :n_ids[b]]
+        Kd = gs.heads(gs.dequant_rows(K[b, :i + 1], kv), Hkv, d)
+        Vd = gs.heads(gs.dequant_rows(V[b, :i + 1], kv), Hkv, d)
+        o_gpu, m_gpu = out[b].float().cpu().numpy(), mass[b].cpu().numpy()
+        o_ref, m_ref = orc.reattend_blocks(q[b].double().numpy(), Kd, Vd, np.arange(i + 1), i, chosen,
+                                           orc.softmax_scale(d), geom.nb)
+        if not m_ref.any():
+            assert not o_gpu.any() and not m_gpu.any()
+            continue
+        alive = np.zeros(geom.nb, dtype=bool)
+        alive[[c for c in chosen if 0 <= c < geom.nb]] = True
+        _, _, pav = gs.oracle_layer(q[b].double().numpy(), Kd, Vd, np.arange(i + 1), i, 0, alive,
+                                    orc.softmax_scale(d), geom.nb)
+        gs.close_o(o_gpu, o_ref, kv, pav)
+        gs.close_mass(m_gpu, m_ref, kv)
+        assert not m_gpu[~alive].any()
+
+
 RING_CASES = [
     # kv,   d,  Hq, Hkv, C,  window, steps
     ("fp8", 128, 16, 4, 64, 64, 300),

@@ -194,3 +194,52 @@ def test_alive_mask_equals_attending_kept_blocks_only():
     assert np.abs(o - o2).max() <= 1e-12
     assert np.abs(m - orc.block_mass(p2, perm, 6)).max() <= 1e-12
     assert m[1] == 0 and m[3] == 0
+
+
+# ---------------------------------------------------------------- Tier 2 re-attend
+
+def _sdpa_over(q, K, V, cols, scale):
+    """torch float64 attention over the key columns ``cols`` (GQA by repeat)."""
+    G = q.shape[0] // K.shape[0]
+    Kt = torch.from_numpy(K[:, cols]).repeat_interleave(G, 0)[None]
+    Vt = torch.from_numpy(V[:, cols]).repeat_interleave(G, 0)[None]
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None, :, None, :], Kt, Vt, scale=scale)[0, :, 0].numpy()
+
+
+def test_reattend_matches_sdpa_over_gathered_blocks():
+    """Context views at marginal cost, Tier 2: the new query against the cached
+    keys of the chosen spans only. Pinned against torch attention over the
+    gathered columns and an explicit per-block loop for the distribution."""
+    rng = np.random.default_rng(23)
+    Hq, Hkv, d, n, nb = 8, 2, 32, 150, 12
+    K, V, q = _rand(rng, Hkv, n, d), _rand(rng, Hkv, n, d), _rand(rng, Hq, d)
+    i = 140                      # keys after i exist in the cache but are not read
+    ids = [9, 2, 2, 7, 0, 11]    # any order, repeats; block 9 holds keys 144..149 > i only partly
+    o, m = orc.reattend_blocks(q, K, V, np.arange(n), i, ids, 0.17, nb)
+    cols = [j for j in range(n) if j <= i and j // 16 in set(ids)]
+    assert np.abs(o - _sdpa_over(q, K, V, cols, 0.17)).max() <= 1e-12
+    G = Hq // Hkv
+    want = np.zeros(nb)
+    for h in range(Hq):
+        s = np.array([K[h // G, j] @ q[h] * 0.17 for j in cols])
+        w = np.exp(s - s.max())
+        w /= w.sum()
+        for j, wj in zip(cols, w):
+            want[j // 16] += wj
+    assert np.abs(m - want).max() <= 1e-12
+    assert abs(m.sum() - Hq) <= 1e-12
+    assert all(m[b] == 0 for b in range(nb) if b not in set(ids))
+
+
+def test_reattend_over_every_block_is_full_attention_and_empty_set_is_zero():
+    rng = np.random.default_rng(29)
+    Hq, Hkv, d, n = 4, 4, 16, 40
+    K, V, q = _rand(rng, Hkv, n, d), _rand(rng, Hkv, n, d), _rand(rng, Hq, d)
+    o, m = orc.reattend_blocks(q, K, V, np.arange(n), n - 1, [2, 1, 0], 0.25, 3)
+    assert np.abs(o - _sdpa_over(q, K, V, list(range(n)), 0.25)).max() <= 1e-12
+    o0, m0 = orc.reattend_blocks(q, K, V, np.arange(n), n - 1, [], 0.25, 3)
+    assert not o0.any() and not m0.any()
+    # a block past the query position contributes nothing
+    o1, m1 = orc.reattend_blocks(q, K, V, np.arange(n), 15, [1, 2], 0.25, 3)
+    assert not o1.any() and not m1.any()
