@@ -41,9 +41,10 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=("decode", "reattend"), default="decode",
-                    help="decode: the scored decode step (headline); reattend: Tier 2, a new query "
-                         "over the blocks the selection kept")
+    ap.add_argument("--mode", choices=("decode", "profiled", "reattend"), default="decode",
+                    help="decode: the scored decode step (headline); profiled: the same step also "
+                         "keeping per-head block masses and their max over heads and layers; "
+                         "reattend: Tier 2, a new query over the blocks the selection kept")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
                          "(a reference for hardware byte counters)")
@@ -137,6 +138,10 @@ def run_gpu(args, w):
     log(f"setup {time.time() - t0:.1f}s, workspace {dec.workspace.numel() / 2**20:.1f} MiB")
 
     L = dec.n_layers
+    profiled = args.mode == "profiled"
+    if profiled:
+        head_mass = torch.zeros((w.batch, w.n_q_heads, dec.geom.nb), dtype=torch.float32, device="cuda")
+        mass_max = torch.zeros((w.batch, dec.geom.nb), dtype=torch.float32, device="cuda")
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
           for _ in range(args.steps)]
     sev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
@@ -154,6 +159,14 @@ def run_gpu(args, w):
             dec.caches[layer].append(K[layer][t], V[layer][t], dec.row_seq, cur[t])
             if timed:
                 ev[t - args.warmup][layer][0].record()
+            if profiled:
+                # one call, both phases: the events cover partial + combine
+                api.decode_attn_profiled(dec.caches[layer], Q[layer][t], cur[t], dec.out[layer], dec.workspace,
+                                         mass_accum=dec.mass, head_mass=head_mass, mass_max=mass_max,
+                                         keep_mask=keep)
+                if timed:
+                    ev[t - args.warmup][layer][1].record()
+                continue
             api.decode_attn_scored(dec.caches[layer], Q[layer][t], cur[t], dec.out[layer], dec.workspace,
                                    mass_accum=dec.mass, keep_mask=keep, phase="partial")
             if timed:
@@ -353,18 +366,20 @@ def main():
             "layers": w.n_layers, "context": w.context, "kv_dtype": w.kv_dtype, "block_tokens": 16,
             "window": w.window, "ring": w.ring, "budget_blocks": w.budget_blocks,
             "recent_tokens": w.recent_tokens, "mode": "evict" if args.evict else "score-only",
+            **({"outputs": "per-head block masses [B][Hq][NBmax] and max over heads and layers"}
+               if args.mode == "profiled" else {}),
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "step_ms_p10_p50_p90": [round(float(x), 4) for x in _percentiles(step_ms, (10, 50, 90))],
         "blocks_scored_per_s": round(blocks_step / (ms_step / 1e3), 1),
         "roofline": {
-            "kernel": "kvs_partial",
+            "kernel": "kvs_partial + kvs_combine (profiled call)" if args.mode == "profiled" else "kvs_partial",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(root, args.workload),
+            "traffic": measured_traffic(root, args.workload) if args.mode == "decode" else None,
             "avg_launch_us": round(part_avg_ms * 1e3, 2),
             "bytes_per_launch": int(bytes_launch),
         },

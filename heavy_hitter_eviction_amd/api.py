@@ -26,7 +26,8 @@ TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8
 
 EXPORTED = (
     "kvs_cache_bytes", "kvs_encode_fp8", "kvs_append_kv", "kvs_decode_workspace_bytes",
-    "kvs_decode_attn_scored", "kvs_decode_partial", "kvs_decode_combine", "kvs_reattend_blocks",
+    "kvs_decode_attn_scored", "kvs_decode_partial", "kvs_decode_combine", "kvs_decode_attn_profiled",
+    "kvs_reattend_blocks",
     "kvs_update_sidecar", "kvs_select_blocks", "kvs_status_str",
     "kvs_version",
 )
@@ -63,6 +64,7 @@ def _load():
         "kvs_decode_partial": [G, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "kvs_decode_combine": [G, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "kvs_reattend_blocks": [G, P, P, P, P, P, P, P, P, I32, P, P, P, SZ, P],
+        "kvs_decode_attn_profiled": [G, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "kvs_update_sidecar": [P, P, P, P, P, I32, I32, I32, I64, F, P],
         "kvs_select_blocks": [P, P, P, I32, I32, I32, I32, I32, P, P, P, P],
     }
@@ -242,6 +244,39 @@ def decode_attn_scored(cache: KVCache, q: torch.Tensor, cur_pos: torch.Tensor, o
               _ptr(cache.v_scale), _ptr(cache.pos_of_slot), _ptr(cur_pos), _ptr(keep_mask), _ptr(out),
               _ptr(mass_accum), _ptr(workspace), ws_bytes, _stream(stream)),
            f"kvs_decode ({phase})")
+    return out
+
+
+def decode_attn_profiled(cache: KVCache, q: torch.Tensor, cur_pos: torch.Tensor, out: torch.Tensor,
+                         workspace: torch.Tensor, mass_accum: torch.Tensor | None = None,
+                         head_mass: torch.Tensor | None = None, mass_max: torch.Tensor | None = None,
+                         keep_mask: torch.Tensor | None = None, stream=None):
+    """kvs_decode_attn_profiled: the scored decode step with per-head block
+    masses (``head_mass`` [B, Hq, NBmax], +=) and their running max over heads
+    (``mass_max`` [B, NBmax])."""
+    g = cache.geom
+    _device_check(q, cur_pos, out, workspace, mass_accum, head_mass, mass_max, keep_mask)
+    qdt = TORCH_DTYPES[g.q_dtype]
+    if q.dtype != qdt or out.dtype != qdt:
+        raise TypeError("q and out must have the geometry's q dtype")
+    if q.shape != (g.batch, g.n_q_heads, g.head_dim) or out.shape != q.shape:
+        raise ValueError("q/out must be [B, Hq, d]")
+    if cur_pos.dtype != torch.int32 or cur_pos.numel() != g.batch:
+        raise ValueError("cur_pos must be int32 [B]")
+    for name, t, n in (("mass_accum", mass_accum, g.batch * g.nb), ("mass_max", mass_max, g.batch * g.nb),
+                       ("head_mass", head_mass, g.batch * g.n_q_heads * g.nb)):
+        if t is not None and (t.dtype != torch.float32 or t.numel() != n or not t.is_contiguous()):
+            raise ValueError(f"{name} must be contiguous float32 with {n} elements")
+    if keep_mask is not None and (keep_mask.dtype != torch.int32 or keep_mask.numel() != g.batch * g.words):
+        raise ValueError("keep_mask must be int32 (bit words) [B, W]")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    gc = g.c()
+    _check(LIB.kvs_decode_attn_profiled(ctypes.byref(gc), _ptr(q), _ptr(cache.k), _ptr(cache.v),
+                                        _ptr(cache.k_scale), _ptr(cache.v_scale), _ptr(cache.pos_of_slot),
+                                        _ptr(cur_pos), _ptr(keep_mask), _ptr(out), _ptr(mass_accum),
+                                        _ptr(head_mass), _ptr(mass_max), _ptr(workspace), ws_bytes,
+                                        _stream(stream)),
+           "kvs_decode_attn_profiled")
     return out
 
 

@@ -255,6 +255,28 @@ int kvs_decode_attn_scored(KVS_DECODE_ARGS) {
   return hip_status(kvs::launch_combine(c, g->ring != 0, g->q_dtype == KVS_BF16, s));
 }
 
+int kvs_decode_attn_profiled(const kvs_geom* g, const void* q, const void* k_cache, const void* v_cache,
+                             const float* k_scale, const float* v_scale, const int32_t* pos_of_slot,
+                             const int32_t* cur_pos, const uint32_t* keep_mask, void* out,
+                             float* mass_accum, float* head_mass, float* mass_max, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if ((head_mass && !aligned16(head_mass)) || (mass_max && !aligned16(mass_max))) return KVS_EALIGN;
+  Plan p;
+  kvs::PartialArgs a;
+  kvs::CombineArgs c;
+  int kv;
+  int st = decode_setup(g, q, k_cache, v_cache, k_scale, v_scale, pos_of_slot, cur_pos, keep_mask, out,
+                        mass_accum, workspace, workspace_bytes, &p, &a, &c, &kv);
+  if (st) return st;
+  c.head_mass = head_mass;
+  c.mass_max = mass_max;
+  const bool scored = mass_accum || head_mass || mass_max;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = kvs::launch_partial(kv, g->head_dim, a, scored, g->ring != 0, p.lds_partial, s);
+  if (e != hipSuccess) return KVS_EHIP;
+  return hip_status(kvs::launch_combine(c, g->ring != 0, g->q_dtype == KVS_BF16, s));
+}
+
 int kvs_reattend_blocks(const kvs_geom* g, const void* q, const void* k_cache, const void* v_cache,
                         const float* k_scale, const float* v_scale, const int32_t* cur_pos,
                         const int32_t* block_ids, const int32_t* n_ids, int32_t ids_stride, void* out,

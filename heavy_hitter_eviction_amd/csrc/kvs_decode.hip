@@ -669,32 +669,74 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
     }
     return;
   }
-  if (a.mass == nullptr) return;
+  if (a.mass == nullptr && a.head_mass == nullptr && a.mass_max == nullptr) return;
   constexpr int NSUB = RING ? 2 : 1;
   const int chunk = blockIdx.x - a.n_o_chunks;
   const int i_cur = a.cur_pos[b];
   const int lap_i = RING ? i_cur / a.C : 0;
   for (int t = chunk * 256 + threadIdx.x; t < a.NT; t += a.n_mass_chunks * 256) {
-    // heads summed in ascending order
     const int p = t / a.tpp;
+    // logical block of each sub-block of tile t (-1: none)
+    int blk[NSUB];
+#pragma unroll
+    for (int sb = 0; sb < NSUB; ++sb) {
+      blk[sb] = t;
+      if constexpr (RING) {
+        const int lap = ((lap_i & 1) == sb) ? lap_i : lap_i - 1;
+        blk[sb] = lap < 0 ? -1 : lap * (a.C / kTile) + t;
+      }
+      if (blk[sb] >= a.nbmax) blk[sb] = -1;
+    }
+    // heads summed in ascending order; per-head masses and their max on the side
     const float* e = a.ws_e + ((size_t)b * a.Hq * a.NT + t) * NSUB;
-    float acc[NSUB];
+    float acc[NSUB], mx[NSUB];
 #pragma unroll
-    for (int sb = 0; sb < NSUB; ++sb) acc[sb] = 0.0f;
-    for (int h = 0; h < a.Hq; ++h) {
-      const float w = wgt[h * P + p];
+    for (int sb = 0; sb < NSUB; ++sb) {
+      acc[sb] = 0.0f;
+      mx[sb] = 0.0f;
+    }
+    if (a.head_mass == nullptr) {
+      for (int h = 0; h < a.Hq; ++h) {
+        const float w = wgt[h * P + p];
 #pragma unroll
-      for (int sb = 0; sb < NSUB; ++sb) acc[sb] += e[(size_t)h * a.NT * NSUB + sb] * w;
+        for (int sb = 0; sb < NSUB; ++sb) {
+          const float v = e[(size_t)h * a.NT * NSUB + sb] * w;
+          acc[sb] += v;
+          mx[sb] = fmaxf(mx[sb], v);
+        }
+      }
+    } else {
+      // per-head masses read-modify-written eight heads at a time, so the
+      // loads of a group are in flight together
+      constexpr int HB = 8;
+      for (int h0 = 0; h0 < a.Hq; h0 += HB) {
+        const int nh = min(HB, a.Hq - h0);
+#pragma unroll
+        for (int sb = 0; sb < NSUB; ++sb) {
+          float ev[HB], hv[HB];
+          float* hp = a.head_mass + ((size_t)b * a.Hq + h0) * a.nbmax + (blk[sb] < 0 ? 0 : blk[sb]);
+#pragma unroll
+          for (int k = 0; k < HB; ++k) {
+            ev[k] = k < nh ? e[(size_t)(h0 + k) * a.NT * NSUB + sb] : 0.0f;
+            hv[k] = (k < nh && blk[sb] >= 0) ? hp[(size_t)k * a.nbmax] : 0.0f;
+          }
+#pragma unroll
+          for (int k = 0; k < HB; ++k) {
+            if (k >= nh) break;
+            const float v = ev[k] * wgt[(h0 + k) * P + p];
+            acc[sb] += v;
+            mx[sb] = fmaxf(mx[sb], v);
+            if (blk[sb] >= 0) hp[(size_t)k * a.nbmax] = hv[k] + v;
+          }
+        }
+      }
     }
 #pragma unroll
     for (int sb = 0; sb < NSUB; ++sb) {
-      int blk = t;
-      if constexpr (RING) {
-        const int lap = ((lap_i & 1) == sb) ? lap_i : lap_i - 1;
-        if (lap < 0) continue;
-        blk = lap * (a.C / kTile) + t;
-      }
-      if (blk < a.nbmax) a.mass[(size_t)b * a.nbmax + blk] += acc[sb];
+      if (blk[sb] < 0) continue;
+      const size_t mi = (size_t)b * a.nbmax + blk[sb];
+      if (a.mass != nullptr) a.mass[mi] += acc[sb];
+      if (a.mass_max != nullptr) a.mass_max[mi] = fmaxf(a.mass_max[mi], mx[sb]);
     }
   }
 }
@@ -733,7 +775,8 @@ hipError_t launch_partial(int kv, int d, const PartialArgs& a, bool scored, bool
 }
 
 hipError_t launch_combine(const CombineArgs& a, bool ring, bool q_bf16, hipStream_t st) {
-  dim3 grid(a.n_o_chunks + (a.mass ? a.n_mass_chunks : 0), a.B), block(256);
+  const bool mass_work = a.mass || a.head_mass || a.mass_max;
+  dim3 grid(a.n_o_chunks + (mass_work ? a.n_mass_chunks : 0), a.B), block(256);
   const size_t lds = (2 * (size_t)a.Hq * a.nparts + 2 * (size_t)a.Hq) * sizeof(float);
   if (ring) {
     if (q_bf16) hipLaunchKernelGGL((kvs_combine<true, true>), grid, block, lds, st, a);

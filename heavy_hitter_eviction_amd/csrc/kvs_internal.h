@@ -42,6 +42,8 @@ struct CombineArgs {
   const int32_t* cur_pos;
   void* out;
   float* mass;
+  float* head_mass;  // [B][Hq][nbmax] per-head block masses (+=), or NULL
+  float* mass_max;   // [B][nbmax] running max over heads (and calls), or NULL
   int B, Hq, D, C, NT, nbmax, tpp, nparts, n_o_chunks, n_mass_chunks;
 };
 

@@ -223,6 +223,31 @@ KVS_API int kvs_decode_combine(const kvs_geom* geom, const void* q, const void* 
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kvs_decode_attn_profiled -- kvs_decode_attn_scored with the per-axis views
+ * of the block masses (Context views at marginal cost, section 4: the
+ * observer's layer and head axes kept as a reduced per-span profile, not the
+ * matrix; section 5, "within layer L" / "within head H"; Per-Head Attention as
+ * a Scoring Signal, "Fix: score per head, place per block": a block stays
+ * resident if any head still weights it).
+ *
+ * Same arguments and checks as kvs_decode_attn_scored, plus two optional
+ * outputs (NULL skips each; all three mass outputs may be NULL):
+ *   head_mass  [B][Hq][NBmax] float: head_mass[b][h][blk] += the block mass of
+ *              query head h alone (sum over its read keys of p_j)
+ *   mass_max   [B][NBmax] float: mass_max[b][blk] = max(mass_max[b][blk],
+ *              max over heads h of head h's block mass)
+ * mass_accum, if given, gets the same head-summed masses as the scored call.
+ * Passing one mass_accum per layer gives the per-layer profile; passing the
+ * same mass_max to every layer gives the max over layers and heads.
+ */
+KVS_API int kvs_decode_attn_profiled(const kvs_geom* geom, const void* q, const void* k_cache,
+                                     const void* v_cache, const float* k_scale, const float* v_scale,
+                                     const int32_t* pos_of_slot, const int32_t* cur_pos,
+                                     const uint32_t* keep_mask, void* out, float* mass_accum,
+                                     float* head_mass, float* mass_max, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/*
  * kvs_reattend_blocks -- one layer of attention for a new query over a chosen
  * set of cached blocks only (Context views at marginal cost, "Tier 2 —
  * RE-ATTEND" and "Fact 3": a relevance question about stored spans is asked by

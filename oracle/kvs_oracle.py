@@ -25,7 +25,11 @@ in the order the source pages state them:
   ring, O(1) per span per turn.
 * Per-Head Attention as a Scoring Signal, "Scoring granularity, not eviction
   granularity": the unit that is scored and kept is a (sequence, 16-token
-  block); heads are only a scoring input.
+  block); heads are only a scoring input. "Fix: score per head, place per
+  block": a block stays resident if any head still weights it (the max over
+  heads of the per-head masses).
+* Context views at marginal cost, section 4: the observer's layer and head
+  axes may be kept as a reduced per-span profile instead of being summed.
 * Context views at marginal cost, "Tier 2 — RE-ATTEND" and "Fact 3": a new
   query is run against the cached keys of a chosen subset of spans, and the
   resulting distribution is read; cached keys and values are reused as they
@@ -229,6 +233,35 @@ def block_mass(p: np.ndarray, positions: np.ndarray, n_blocks: int) -> np.ndarra
     for h in range(p.shape[0]):
         mass += np.bincount(blocks, weights=p[h], minlength=n_blocks)
     return mass
+
+
+def block_mass_per_head(p: np.ndarray, positions: np.ndarray, n_blocks: int) -> np.ndarray:
+    """The per-head profile (Context views at marginal cost, section 4, "within
+    head H"): ``[Hq, n_blocks]``, row ``h`` is head h's post-softmax weight
+    summed over each block's visible keys, before any sum over heads."""
+    p = np.asarray(p, dtype=np.float64)
+    blocks = np.asarray(positions, dtype=np.int64) // BLOCK_TOKENS
+    if blocks.size and (blocks.min() < 0 or blocks.max() >= n_blocks):
+        raise ValueError("block index out of range")
+    return np.stack([np.bincount(blocks, weights=p[h], minlength=n_blocks) for h in range(p.shape[0])])
+
+
+def max_over_heads(head_mass: np.ndarray) -> np.ndarray:
+    """Per-Head Attention as a Scoring Signal, "score per head, place per
+    block": a block stays resident if any head still weights it, so the
+    block's score is the largest of its per-head masses."""
+    return np.max(np.asarray(head_mass, dtype=np.float64), axis=0)
+
+
+def attend_profiled(q, K_all, V_all, positions, i, window, alive, scale, n_blocks):
+    """attend_scored plus the per-head profile and its max over heads:
+    ``(o, mass, head_mass [Hq, n_blocks], mass_max [n_blocks])``."""
+    positions = np.asarray(positions, dtype=np.int64)
+    sel = np.array([key_visible(int(p), i, window) and block_alive(alive, block_of(int(p)))
+                    for p in positions], dtype=bool)
+    o, p = attend(q, np.asarray(K_all)[:, sel], np.asarray(V_all)[:, sel], scale)
+    hm = block_mass_per_head(p, positions[sel], n_blocks)
+    return o, block_mass(p, positions[sel], n_blocks), hm, max_over_heads(hm)
 
 
 def attend_scored(q, K_all, V_all, positions, i, window, alive, scale, n_blocks):

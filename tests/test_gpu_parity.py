@@ -328,6 +328,100 @@ def test_ring_cache_matches_full_masked_reference(api, case):
         assert (ps[:, t] == want).all()
 
 
+def _oracle_profiled(q, Kd, Vd, positions, i, window, alive, scale, nb):
+    o, m, hm, mx = orc.attend_profiled(q, Kd, Vd, positions, i, window, alive, scale, nb)
+    _, _, pav = gs.oracle_layer(q, Kd, Vd, positions, i, window, alive, scale, nb)
+    return o, m, hm, mx, pav
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "f32"])
+def test_profiled_decode_per_head_and_max_over_heads(api, kv):
+    """Per-head block masses (+=) and their running max over heads (Context
+    views at marginal cost, section 4; Per-Head Attention as a Scoring
+    Signal), accumulated over two calls that stand for two layers, on top of
+    non-zero starting values; with a keep mask in the second call."""
+    d, Hq, Hkv, C, B = (16, 4, 2, 160, 2) if kv == "f32" else (128, 16, 4, 1040, 2)
+    geom, cache, K, V = _build_linear(api, kv, d, Hq, Hkv, C, B, 0, 13)
+    nb = geom.nb
+    rng = np.random.default_rng(13)
+    cur = np.array([C - 1, C // 3], dtype=np.int32)
+    qdt = torch.float32 if kv == "f32" else torch.bfloat16
+    alive = rng.random((B, nb)) < 0.6
+    for b in range(B):
+        alive[b, cur[b] // 16] = True
+    words = np.zeros((B, geom.words), dtype=np.int64)
+    for b in range(B):
+        for blk in np.flatnonzero(alive[b]):
+            words[b, blk >> 5] |= 1 << (blk & 31)
+    keep = gs.to_dev(words.astype(np.uint32).view(np.int32))
+    base_hm = rng.random((B, Hq, nb)).astype(np.float32) * 0.01
+    base_mx = rng.random((B, nb)).astype(np.float32) * 0.01
+    hm_dev, mx_dev = gs.to_dev(base_hm.copy()), gs.to_dev(base_mx.copy())
+    mass = torch.zeros((B, nb), dtype=torch.float32, device="cuda")
+    ws = torch.empty(api.decode_workspace_bytes(geom), dtype=torch.uint8, device="cuda")
+    want_hm, want_mx, want_m = base_hm.astype(np.float64), base_mx.astype(np.float64), np.zeros((B, nb))
+    for call in range(2):
+        q = torch.from_numpy(_rows((B, Hq, d), (13, 40 + call))).to(qdt)
+        out = torch.empty_like(q).cuda()
+        km = keep if call == 1 else None
+        api.decode_attn_profiled(cache, q.cuda(), gs.to_dev(cur), out, ws, mass_accum=mass, head_mass=hm_dev,
+                                 mass_max=mx_dev, keep_mask=km)
+        torch.cuda.synchronize()
+        for b in range(B):
+            i = int(cur[b])
+            Kd = gs.heads(gs.dequant_rows(K[b, :i + 1], kv), Hkv, d)
+            Vd = gs.heads(gs.dequant_rows(V[b, :i + 1], kv), Hkv, d)
+            o, m, hm, mx, pav = _oracle_profiled(q[b].double().numpy(), Kd, Vd, np.arange(i + 1), i, 0,
+                                                 alive[b] if call == 1 else None, orc.softmax_scale(d), nb)
+            gs.close_o(out[b].float().cpu().numpy(), o, kv, pav)
+            want_hm[b] += hm
+            want_mx[b] = np.maximum(want_mx[b], mx)
+            want_m[b] += m
+    got_hm, got_mx, got_m = hm_dev.cpu().numpy(), mx_dev.cpu().numpy(), mass.cpu().numpy()
+    for b in range(B):
+        for h in range(Hq):
+            gs.close_mass(got_hm[b, h], want_hm[b, h], kv, f"head {h} mass")
+        gs.close_mass(got_mx[b], want_mx[b], kv, "max over heads")
+        gs.close_mass(got_m[b], want_m[b], kv, "summed mass")
+        # the head-summed output is the scored call's, and the max never exceeds it
+        assert (got_mx[b] <= np.maximum(got_m[b], base_mx[b]) + 1e-6).all()
+
+
+def test_profiled_ring_decode_per_head(api):
+    """Per-head masses on a ring cache across a wrap: each tile's two laps land
+    on their own logical blocks."""
+    kv, d, Hq, Hkv, C, window, steps = "fp8", 128, 8, 2, 64, 48, 150
+    B = 2
+    nb = (steps + 15) // 16
+    geom = api.CacheGeom(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, capacity=C, window=window,
+                         ring=True, n_blocks_max=nb, kv_dtype=kv, q_dtype="bf16")
+    cache = api.KVCache(geom)
+    K = _rows((steps, B, Hkv * d), (6, 1))
+    V = _rows((steps, B, Hkv * d), (6, 2))
+    seqs = torch.arange(B, dtype=torch.int32, device="cuda")
+    for i in range(steps):
+        cache.append(gs.to_dev(K[i]), gs.to_dev(V[i]), seqs, torch.full((B,), i, dtype=torch.int32, device="cuda"))
+    i = steps - 1
+    q = torch.from_numpy(_rows((B, Hq, d), (6, 3))).to(torch.bfloat16)
+    out = torch.empty_like(q).cuda()
+    hm_dev = torch.zeros((B, Hq, nb), dtype=torch.float32, device="cuda")
+    mx_dev = torch.zeros((B, nb), dtype=torch.float32, device="cuda")
+    ws = torch.empty(api.decode_workspace_bytes(geom), dtype=torch.uint8, device="cuda")
+    api.decode_attn_profiled(cache, q.cuda(), torch.full((B,), i, dtype=torch.int32, device="cuda"), out, ws,
+                             head_mass=hm_dev, mass_max=mx_dev)
+    torch.cuda.synchronize()
+    lo = i - window + 1
+    for b in range(B):
+        Kd = gs.heads(gs.dequant_rows(K[lo:i + 1, b], kv), Hkv, d)
+        Vd = gs.heads(gs.dequant_rows(V[lo:i + 1, b], kv), Hkv, d)
+        o, m, hm, mx, pav = _oracle_profiled(q[b].double().numpy(), Kd, Vd, np.arange(lo, i + 1), i, window, None,
+                                             orc.softmax_scale(d), nb)
+        gs.close_o(out[b].float().cpu().numpy(), o, kv, pav)
+        for h in range(Hq):
+            gs.close_mass(hm_dev[b, h].cpu().numpy(), hm[h], kv, f"head {h} mass")
+        gs.close_mass(mx_dev[b].cpu().numpy(), mx, kv, "max over heads")
+
+
 # ---------------------------------------------------------------- side-car and selection
 
 def test_sidecar_update_matches_oracle(api):

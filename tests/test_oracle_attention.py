@@ -243,3 +243,51 @@ def test_reattend_over_every_block_is_full_attention_and_empty_set_is_zero():
     # a block past the query position contributes nothing
     o1, m1 = orc.reattend_blocks(q, K, V, np.arange(n), 15, [1, 2], 0.25, 3)
     assert not o1.any() and not m1.any()
+
+
+# ---------------------------------------------------------------- per-head profile, max over heads
+
+def test_per_head_profile_brute_force_and_invariants():
+    """Context views at marginal cost, section 4 (per-head profile) and
+    Per-Head Attention as a Scoring Signal (max over heads): per-head block
+    masses from an explicit loop over keys, each head's row sums to one, the
+    rows sum to the head-summed mass, and the max lies between mean and sum."""
+    rng = np.random.default_rng(31)
+    Hq, Hkv, d, n, nb = 8, 2, 16, 77, 6
+    K, V, q = _rand(rng, Hkv, n, d), _rand(rng, Hkv, n, d), _rand(rng, Hq, d)
+    alive = np.array([True, True, False, True, True, True])
+    o, mass, hm, mx = orc.attend_profiled(q, K, V, np.arange(n), n - 1, 0, alive, 0.3, nb)
+    G = Hq // Hkv
+    cols = [j for j in range(n) if alive[j // 16]]
+    want = np.zeros((Hq, nb))
+    for h in range(Hq):
+        s = np.array([K[h // G, j] @ q[h] * 0.3 for j in cols])
+        w = np.exp(s - s.max())
+        w /= w.sum()
+        for j, wj in zip(cols, w):
+            want[h, j // 16] += wj
+    assert np.abs(hm - want).max() <= 1e-12
+    assert np.abs(hm.sum(axis=1) - 1).max() <= 1e-12
+    assert np.abs(hm.sum(axis=0) - mass).max() <= 1e-12
+    assert np.abs(mx - want.max(axis=0)).max() <= 1e-12
+    assert (mx <= mass + 1e-15).all() and (mx >= mass / Hq - 1e-15).all()
+    assert mx[2] == 0
+
+
+def test_max_over_heads_keeps_a_block_one_head_weights():
+    """Per-Head Attention as a Scoring Signal: an anchor head that looks only at
+    block 0 keeps it on top of the max-over-heads score even when every other
+    head has moved on to the recent blocks, while the head sum ranks it last."""
+    d, n = 16, 64
+    Hq, Hkv = 8, 8
+    K = np.zeros((Hkv, n, d))
+    V = np.ones((Hkv, n, d))
+    q = np.zeros((Hq, d))
+    K[0, :16, 0] = 400.0         # head 0 (its own KV head) locks onto block 0
+    for h in range(1, Hq):
+        K[h, 48:, 1] = 400.0      # the others onto block 3
+        q[h, 1] = 1.0
+    q[0, 0] = 1.0
+    _, mass, hm, mx = orc.attend_profiled(q, K, V, np.arange(n), n - 1, 0, None, 0.25, 4)
+    assert abs(mx[0] - 1.0) <= 1e-9 and abs(mx[3] - 1.0) <= 1e-9
+    assert mass[0] < mass[3] / 5
