@@ -28,7 +28,7 @@ EXPORTED = (
     "kvs_cache_bytes", "kvs_encode_fp8", "kvs_append_kv", "kvs_decode_workspace_bytes",
     "kvs_decode_attn_scored", "kvs_decode_partial", "kvs_decode_combine", "kvs_decode_attn_profiled",
     "kvs_reattend_blocks",
-    "kvs_update_sidecar", "kvs_select_blocks", "kvs_status_str",
+    "kvs_update_sidecar", "kvs_update_counters", "kvs_filter_blocks", "kvs_select_blocks", "kvs_status_str",
     "kvs_version",
 )
 
@@ -66,6 +66,8 @@ def _load():
         "kvs_reattend_blocks": [G, P, P, P, P, P, P, P, P, I32, P, P, P, SZ, P],
         "kvs_decode_attn_profiled": [G, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "kvs_update_sidecar": [P, P, P, P, P, I32, I32, I32, I64, F, P],
+        "kvs_update_counters": [P, P, P, P, P, I32, I32, I32, F, F, I32, P],
+        "kvs_filter_blocks": [P, P, P, I32, I32, F, P, P, I32, P],
         "kvs_select_blocks": [P, P, P, I32, I32, I32, I32, I32, P, P, P, P],
     }
     for name, args in sig.items():
@@ -309,6 +311,31 @@ def reattend_blocks(cache: KVCache, q: torch.Tensor, cur_pos: torch.Tensor, bloc
                                    _stream(stream)),
            "kvs_reattend_blocks")
     return out
+
+
+def update_counters(attended, ema, hot_count=None, cold_turns=None, traj=None, hot_theta: float = 0.0,
+                    cold_theta: float = 0.0, cold_limit: int = 0, stream=None):
+    """kvs_update_counters: Scissorhands hot counts and cold-turn trajectory GC."""
+    _device_check(attended, ema, hot_count, cold_turns, traj)
+    B, nb = attended.shape
+    for name, t in (("hot_count", hot_count), ("cold_turns", cold_turns)):
+        if t is not None and (t.dtype != torch.int32 or t.shape != (B, nb) or not t.is_contiguous()):
+            raise ValueError(f"{name} must be contiguous int32 [B, NBmax]")
+    cap = traj.shape[1] if traj is not None else 0
+    _check(LIB.kvs_update_counters(_ptr(attended), _ptr(ema), _ptr(hot_count), _ptr(cold_turns), _ptr(traj), B, nb,
+                                   cap, hot_theta, cold_theta, cold_limit, _stream(stream)),
+           "kvs_update_counters")
+
+
+def filter_blocks(score, cur_pos, theta: float, ids, n_ids, alive=None, stream=None):
+    """kvs_filter_blocks: ascending ids of existing, alive blocks with score > theta."""
+    _device_check(score, cur_pos, ids, n_ids, alive)
+    B, nb = score.shape
+    if ids.dtype != torch.int32 or ids.dim() != 2 or ids.shape[0] != B or not ids.is_contiguous():
+        raise ValueError("ids must be contiguous int32 [B, S]")
+    _check(LIB.kvs_filter_blocks(_ptr(score), _ptr(alive), _ptr(cur_pos), B, nb, theta, _ptr(ids), _ptr(n_ids),
+                                 ids.shape[1], _stream(stream)),
+           "kvs_filter_blocks")
 
 
 def update_sidecar(mass_accum, attended, ema, cum, traj, step: int, alpha: float, stream=None):

@@ -314,6 +314,40 @@ int kvs_update_sidecar(float* mass_accum, float* attended, float* ema, float* cu
                                         traj_cap, step, alpha, (hipStream_t)stream));
 }
 
+int kvs_update_counters(const float* attended, const float* ema, int32_t* hot_count, int32_t* cold_turns,
+                        float* traj, int32_t batch, int32_t n_blocks_max, int32_t traj_cap, float hot_theta,
+                        float cold_theta, int32_t cold_limit, void* stream) {
+  if (batch < 1 || n_blocks_max < 1 || cold_limit < 0) return KVS_EINVAL;
+  if (!isfinite(hot_theta) || !isfinite(cold_theta)) return KVS_EINVAL;
+  if (hot_count && !attended) return KVS_EINVAL;
+  if (cold_turns && !ema) return KVS_EINVAL;
+  if (traj && (!cold_turns || traj_cap < 1)) return KVS_EINVAL;
+  const void* ptrs[] = {attended, ema, hot_count, cold_turns, traj};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KVS_EALIGN;
+  if (!hot_count && !cold_turns) return KVS_OK;
+  kvs::CounterArgs a{};
+  a.attended = attended; a.ema = ema; a.hot_count = hot_count; a.cold_turns = cold_turns; a.traj = traj;
+  a.B = batch; a.nbmax = n_blocks_max; a.traj_cap = traj_cap; a.cold_limit = cold_limit;
+  a.hot_theta = hot_theta; a.cold_theta = cold_theta;
+  return hip_status(kvs::launch_counters(a, (hipStream_t)stream));
+}
+
+int kvs_filter_blocks(const float* score, const uint32_t* alive, const int32_t* cur_pos, int32_t batch,
+                      int32_t n_blocks_max, float theta, int32_t* ids, int32_t* n_ids, int32_t ids_stride,
+                      void* stream) {
+  if (batch < 1 || n_blocks_max < 1 || ids_stride < 1 || isnan(theta)) return KVS_EINVAL;
+  if (!score || !cur_pos || !ids || !n_ids) return KVS_EINVAL;
+  const void* ptrs[] = {score, alive, cur_pos, ids, n_ids};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KVS_EALIGN;
+  kvs::FilterArgs a{};
+  a.score = score; a.alive = alive; a.cur_pos = cur_pos; a.ids = ids; a.n_ids = n_ids;
+  a.B = batch; a.nbmax = n_blocks_max; a.kwords = (n_blocks_max + 31) / 32; a.ids_stride = ids_stride;
+  a.theta = theta;
+  return hip_status(kvs::launch_filter(a, (hipStream_t)stream));
+}
+
 int kvs_select_blocks(const float* score, const uint32_t* alive, const int32_t* cur_pos,
                       int32_t batch, int32_t n_blocks_max, int32_t budget_blocks,
                       int32_t recent_tokens, int32_t sink_tokens, uint32_t* keep_mask,

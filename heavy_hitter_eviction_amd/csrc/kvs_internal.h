@@ -82,4 +82,26 @@ struct SelectArgs {
 };
 hipError_t launch_select(const SelectArgs& a, hipStream_t st);
 
+struct CounterArgs {
+  const float* attended;
+  const float* ema;
+  int32_t* hot_count;   // [B][nbmax] or NULL
+  int32_t* cold_turns;  // [B][nbmax] or NULL
+  float* traj;          // [B][traj_cap][nbmax] or NULL (no trajectory GC)
+  int B, nbmax, traj_cap, cold_limit;
+  float hot_theta, cold_theta;
+};
+hipError_t launch_counters(const CounterArgs& a, hipStream_t st);
+
+struct FilterArgs {
+  const float* score;
+  const uint32_t* alive;
+  const int32_t* cur_pos;
+  int32_t* ids;
+  int32_t* n_ids;
+  int B, nbmax, kwords, ids_stride;
+  float theta;
+};
+hipError_t launch_filter(const FilterArgs& a, hipStream_t st);
+
 }  // namespace kvs

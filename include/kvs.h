@@ -293,6 +293,49 @@ KVS_API int kvs_update_sidecar(float* mass_accum, float* attended, float* ema, f
                        float alpha, void* stream);
 
 /*
+ * kvs_update_counters -- side-car counters for threshold views, once per turn
+ * after kvs_update_sidecar (Context views at marginal cost, section 3: views
+ * are filters of the score table and the threshold doubles as a storage GC
+ * policy; a span whose EMA stays below the threshold for K turns drops its
+ * fine-grained trajectory and keeps its cumulative scalar. Section 3, Fact 1:
+ * Scissorhands keeps how often a token exceeds a threshold). Per block x of
+ * every sequence (all n_blocks_max entries):
+ *   hot_count[x]  += (attended[x] > hot_theta)                (NULL: skipped)
+ *   cold_turns[x]  = ema[x] < cold_theta ? cold_turns[x] + 1 : 0  (NULL: skipped)
+ *   if traj != NULL, cold_limit > 0 and cold_turns[x] >= cold_limit:
+ *       traj[b][s][blk] = 0 for every slot s of the ring
+ *
+ *   attended, ema  [B][NBmax] float (as kept by kvs_update_sidecar)
+ *   hot_count, cold_turns  [B][NBmax] int32, start at zero
+ *   traj   [B][traj_cap][NBmax] float; needs cold_turns
+ * Errors: KVS_EINVAL for sizes < 1, cold_limit < 0, non-finite thresholds, a
+ * counter without its input, traj without cold_turns; KVS_EALIGN.
+ */
+KVS_API int kvs_update_counters(const float* attended, const float* ema, int32_t* hot_count,
+                                int32_t* cold_turns, float* traj, int32_t batch, int32_t n_blocks_max,
+                                int32_t traj_cap, float hot_theta, float cold_theta, int32_t cold_limit,
+                                void* stream);
+
+/*
+ * kvs_filter_blocks -- a threshold view (Context views at marginal cost,
+ * section 3: "filter(a_s > θ)", computed lazily at query time; the result is a
+ * set of span refs). For each sequence b with i = cur_pos[b], the ascending
+ * ids of the existing blocks (0 .. i/16, below NBmax) that are alive (bit set
+ * in alive[b], or every block when alive is NULL) and whose score exceeds
+ * theta. n_ids[b] is the number of such blocks; ids[b] holds the first
+ * min(n_ids[b], ids_stride) of them. The result can be passed to
+ * kvs_reattend_blocks (the Tier 1 to Tier 2 handoff).
+ *
+ *   score  [B][NBmax] float (Attended, EMA, Cumulative, or any per-block scalar)
+ *   alive  [B][ceil(NBmax/32)] uint32 or NULL
+ *   ids    [B][ids_stride] int32; n_ids [B] int32
+ * Errors: KVS_EINVAL (sizes, NaN theta, NULL required pointers), KVS_EALIGN.
+ */
+KVS_API int kvs_filter_blocks(const float* score, const uint32_t* alive, const int32_t* cur_pos,
+                              int32_t batch, int32_t n_blocks_max, float theta, int32_t* ids,
+                              int32_t* n_ids, int32_t ids_stride, void* stream);
+
+/*
  * kvs_select_blocks -- heavy-hitter block selection (Context Optimization,
  * "H2O KV Cache Eviction": sinks and recent tokens are always kept; among the
  * rest the top scorers survive), at 16-token block granularity.

@@ -372,6 +372,39 @@ class SideCar:
 
 
 # ---------------------------------------------------------------------------
+# Threshold views and counters (Context views at marginal cost, section 3)
+# ---------------------------------------------------------------------------
+
+def hot_count_update(count: np.ndarray, attended: np.ndarray, theta: float) -> np.ndarray:
+    """Scissorhands (section 3, Fact 1): per span, the number of turns whose
+    attention exceeded the threshold; one increment per turn above it."""
+    return np.asarray(count) + (np.asarray(attended) > theta).astype(np.asarray(count).dtype)
+
+
+def cold_gc_update(cold_turns: np.ndarray, ema: np.ndarray, traj: np.ndarray, theta: float, limit: int):
+    """The threshold as a storage GC policy (section 3, "Pure side-car vs.
+    materialized"): count the consecutive turns a span's EMA has stayed below
+    theta; once that reaches ``limit`` (> 0) the span drops its fine-grained
+    trajectory (its ring column is cleared) and keeps only the cumulative
+    scalar. Returns the new counts and trajectory."""
+    ema = np.asarray(ema)
+    cold = np.where(ema < theta, np.asarray(cold_turns) + 1, 0)
+    traj = np.array(traj, copy=True)
+    if limit > 0:
+        traj[:, cold >= limit] = 0.0
+    return cold, traj
+
+
+def filter_blocks(score: np.ndarray, alive, i: int, theta: float) -> np.ndarray:
+    """A threshold view (section 3: filter(a_s > theta), computed at query
+    time): the ascending ids of the blocks that exist at position ``i``, are
+    alive, and score strictly above theta."""
+    n_exist = i // BLOCK_TOKENS + 1
+    return np.array([b for b in range(min(n_exist, len(score)))
+                     if block_alive(alive, b) and score[b] > theta], dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
 # Heavy-hitter block selection (Context Optimization, "H2O KV Cache Eviction")
 # ---------------------------------------------------------------------------
 

@@ -132,6 +132,37 @@ def test_other_entry_points_reject_bad_arguments():
     assert L.kvs_update_sidecar(*ok, 2, 16, 64, 0, 1.5, None) == api.KVS_EINVAL
     assert L.kvs_update_sidecar(*ok, 2, 16, 0, 0, 0.5, None) == api.KVS_EINVAL
     assert L.kvs_update_sidecar(*ok, 2, 16, 64, -1, 0.5, None) == api.KVS_EINVAL
+    cnt = lambda *a: L.kvs_update_counters(*a)  # noqa: E731
+    f, i1 = vp(0x1000), vp(0x2000)
+    assert cnt(f, f, i1, i1, None, 2, 16, 64, 0.5, 0.1, -1, None) == api.KVS_EINVAL      # cold_limit < 0
+    assert cnt(None, f, i1, None, None, 2, 16, 64, 0.5, 0.1, 3, None) == api.KVS_EINVAL  # hot without input
+    assert cnt(f, f, None, None, f, 2, 16, 64, 0.5, 0.1, 3, None) == api.KVS_EINVAL      # traj without cold
+    assert cnt(f, f, i1, i1, None, 2, 16, 64, float("nan"), 0.1, 3, None) == api.KVS_EINVAL
+    assert cnt(f, f, vp(0x2004), None, None, 2, 16, 64, 0.5, 0.1, 3, None) == api.KVS_EALIGN
+    flt = lambda *a: L.kvs_filter_blocks(*a)  # noqa: E731
+    assert flt(f, None, i1, 2, 16, float("nan"), i1, i1, 8, None) == api.KVS_EINVAL
+    assert flt(f, None, i1, 2, 16, 0.5, i1, i1, 0, None) == api.KVS_EINVAL
+    assert flt(f, None, None, 2, 16, 0.5, i1, i1, 8, None) == api.KVS_EINVAL
+    assert flt(f, None, i1, 2, 16, 0.5, vp(0x3008), i1, 8, None) == api.KVS_EALIGN
+
+
+def test_reattend_and_profiled_reject_bad_arguments():
+    api = _lib()
+    L = api.LIB
+    vp = ctypes.c_void_p
+    re = lambda g, ids=0x8000, n=0x9000, stride=8: L.kvs_reattend_blocks(  # noqa: E731
+        ctypes.byref(g), vp(0x1000), vp(0x2000), vp(0x3000), None, None, vp(0x4000),
+        vp(ids) if ids else None, vp(n) if n else None, stride, vp(0x5000), vp(0x6000), vp(0x7000), 1 << 20, None)
+    g = _geom(api)
+    assert re(_geom(api, ring=1)) == api.KVS_EINVAL          # the list replaces ring masking
+    assert re(_geom(api, window=8)) == api.KVS_EINVAL        # and windows
+    assert re(g, ids=0) == api.KVS_EINVAL
+    assert re(g, stride=0) == api.KVS_EINVAL
+    assert re(g, ids=0x8004) == api.KVS_EALIGN
+    pr = lambda hm: L.kvs_decode_attn_profiled(  # noqa: E731
+        ctypes.byref(g), vp(0x1000), vp(0x2000), vp(0x3000), None, None, None, vp(0x4000), None, vp(0x5000),
+        vp(0x6000), vp(hm), None, vp(0x7000), 1 << 20, None)
+    assert pr(0x8008) == api.KVS_EALIGN
     sel = lambda **kw: L.kvs_select_blocks(vp(0x1000), None, vp(0x2000), kw.get("B", 2), 16,  # noqa: E731
                                            kw.get("budget", 4), kw.get("recent", 16), kw.get("sinks", 0),
                                            vp(0x3000), vp(0x4000), vp(0x5000), None)

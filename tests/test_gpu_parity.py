@@ -447,6 +447,64 @@ def test_sidecar_update_matches_oracle(api):
         assert np.array_equal(traj[b].cpu().numpy(), ref[b].traj.astype(np.float32))
 
 
+def test_counters_match_oracle_exactly(api):
+    """Scissorhands counts and cold-turn trajectory GC (Context views at
+    marginal cost, section 3) on the same float32 inputs as the oracle: every
+    decision is a float32 comparison, so counts and cleared columns are exact."""
+    B, nb, T, limit = 2, 300, 64, 4
+    hot_t, cold_t = np.float32(0.3), np.float32(0.05)
+    rng = np.random.default_rng(21)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()  # noqa: E731
+    hot = torch.zeros((B, nb), dtype=torch.int32, device="cuda")
+    cold = torch.zeros((B, nb), dtype=torch.int32, device="cuda")
+    traj_h = (rng.random((B, T, nb)) + 0.5).astype(np.float32)
+    traj = dev(traj_h.copy())
+    r_hot, r_cold, r_traj = np.zeros((B, nb), np.int64), np.zeros((B, nb), np.int64), traj_h.astype(np.float64)
+    for turn in range(12):
+        att = (rng.random((B, nb)) * 0.6).astype(np.float32)
+        att[:, :5] = hot_t                       # exactly at the threshold
+        ema = (rng.random((B, nb)) * (1.0 if turn < 6 else 0.1)).astype(np.float32)
+        ema[:, 5:9] = cold_t
+        api.update_counters(dev(att), dev(ema), hot, cold, traj, float(hot_t), float(cold_t), limit)
+        for b in range(B):
+            r_hot[b] = orc.hot_count_update(r_hot[b], att[b], float(hot_t))
+            r_cold[b], r_traj[b] = orc.cold_gc_update(r_cold[b], ema[b], r_traj[b], float(cold_t), limit)
+    torch.cuda.synchronize()
+    assert np.array_equal(hot.cpu().numpy(), r_hot)
+    assert np.array_equal(cold.cpu().numpy(), r_cold)
+    assert np.array_equal(traj.cpu().numpy(), r_traj.astype(np.float32))
+    assert (r_cold >= limit).any() and (r_hot > 0).any()
+
+
+def test_filter_blocks_matches_oracle_exactly(api):
+    """A threshold view (section 3, filter(a_s > theta)) over more than one
+    1024-block chunk, with an alive mask, ragged positions and one sequence
+    whose result exceeds the id buffer (truncated, full count reported)."""
+    B, nb, S = 3, 2500, 500
+    theta = np.float32(0.7)
+    rng = np.random.default_rng(4)
+    score = rng.random((B, nb)).astype(np.float32)
+    score[:, 10:20] = theta
+    alive = rng.random((B, nb)) < 0.9
+    words = np.zeros((B, (nb + 31) // 32), dtype=np.int64)
+    for b in range(B):
+        for blk in np.flatnonzero(alive[b]):
+            words[b, blk >> 5] |= 1 << (blk & 31)
+    cur = np.array([16 * nb - 1, 16 * 1500 + 7, 16 * 3], dtype=np.int32)
+    ids = torch.full((B, S), -1, dtype=torch.int32, device="cuda")
+    n = torch.zeros(B, dtype=torch.int32, device="cuda")
+    api.filter_blocks(gs.to_dev(score), gs.to_dev(cur), float(theta), ids, n,
+                      alive=gs.to_dev(words.astype(np.uint32).view(np.int32)))
+    torch.cuda.synchronize()
+    got_ids, got_n = ids.cpu().numpy(), n.cpu().numpy()
+    for b in range(B):
+        want = orc.filter_blocks(score[b], alive[b], int(cur[b]), float(theta))
+        assert got_n[b] == len(want)
+        k = min(len(want), S)
+        assert np.array_equal(got_ids[b, :k], want[:k])
+    assert got_n[0] > S
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_select_matches_oracle_exactly(api, seed):
     rng = np.random.default_rng(seed)

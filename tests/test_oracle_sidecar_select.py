@@ -143,3 +143,79 @@ def test_fp8_scale_overhead_reading():
     per_pos = orc.kv_cache_bytes(10, 4, 128, 1, 1, scale_bytes_per_position_per_cache=4)
     assert per_pos == 10320
     assert 10 * 1024 < per_pos < 11 * 1024      # the page's "~10.5 KB/position"
+
+
+# ---------------------------------------------------------------- threshold views and counters
+
+def test_hot_count_is_the_number_of_turns_above_threshold():
+    """Scissorhands (Context views at marginal cost, section 3, Fact 1): the
+    count of turns whose attention exceeded the threshold; strict inequality."""
+    rng = np.random.default_rng(2)
+    nb, turns, theta = 9, 40, 0.35
+    A = rng.random((turns, nb))
+    A[5, 3] = theta                       # exactly at the threshold: not above it
+    count = np.zeros(nb, dtype=np.int32)
+    for t in range(turns):
+        count = orc.hot_count_update(count, A[t], theta)
+    assert np.array_equal(count, np.array([sum(1 for t in range(turns) if A[t, b] > theta) for b in range(nb)]))
+    const = np.zeros(nb, dtype=np.int32)
+    for _ in range(17):
+        const = orc.hot_count_update(const, np.full(nb, 0.5), 0.4)
+    assert (const == 17).all()
+
+
+@pytest.mark.parametrize("alpha", [0.5, 0.25])
+def test_cold_gc_turn_has_a_closed_form(alpha):
+    """The threshold as a storage GC policy (section 3): after one burst of
+    attention a at turn 0 the EMA is alpha*a*(1-alpha)^t, so it first drops
+    below theta at t* = floor(log(theta/(alpha*a)) / log(1-alpha)) + 1, and
+    the trajectory column is cleared exactly limit-1 turns later."""
+    a, theta, limit, nb = 3.0, 0.01, 5, 4
+    t_star = int(np.floor(np.log(theta / (alpha * a)) / np.log(1 - alpha))) + 1
+    sc = orc.SideCar(nb)
+    cold = np.zeros(nb, dtype=np.int64)
+    traj = sc.traj
+    cleared_at = None
+    for t in range(t_star + limit + 3):
+        A = np.zeros(nb)
+        if t == 0:
+            A[1] = a
+        sc.update(A, alpha)
+        cold, traj = orc.cold_gc_update(cold, sc.ema, sc.traj, theta, limit)
+        sc.traj = traj
+        if t == 0:
+            assert traj[0, 1] == a           # the burst is in the ring until GC
+        if cleared_at is None and cold[1] >= limit:
+            cleared_at = t
+    assert cleared_at == t_star + limit - 1
+    assert not traj[:, 1].any() and sc.cum[1] == a   # the cumulative scalar is kept
+    assert (cold[[0, 2, 3]] == t_star + limit + 3).all()  # never-attended blocks are cold from turn 0
+
+
+def test_filter_blocks_brute_force_and_boundaries():
+    """A threshold view (section 3, filter(a_s > theta)): existing, alive
+    blocks strictly above theta, ascending."""
+    rng = np.random.default_rng(8)
+    nb, i, theta = 50, 16 * 37 + 3, 0.6
+    score = rng.random(nb)
+    score[4] = theta                      # not strictly above
+    score[45] = 0.99                      # does not exist yet at position i
+    alive = rng.random(nb) < 0.8
+    ids = orc.filter_blocks(score, alive, i, theta)
+    want = [b for b in range(nb) if b <= i // 16 and alive[b] and score[b] > theta]
+    assert ids.tolist() == want and 4 not in ids and 45 not in ids
+    assert orc.filter_blocks(score, None, i, 2.0).size == 0
+
+
+def test_selection_on_attended_is_tova():
+    """TOVA (section 3, Fact 1): the latest query's head-summed weight, evict
+    the minimum. Selecting on Attended with one block less than the candidates
+    drops exactly the least-attended candidate."""
+    rng = np.random.default_rng(12)
+    nb, i, R = 40, 16 * 39 + 5, 16
+    att = rng.random(nb)
+    prot = set(orc.protected_blocks(i, R, 0))
+    cand = [b for b in range(nb) if b not in prot]
+    keep = orc.select_blocks(att, None, i, len(cand) - 1, R, 0)
+    dropped = set(range(nb)) - set(keep.tolist())
+    assert dropped == {min(cand, key=lambda b: att[b])}
