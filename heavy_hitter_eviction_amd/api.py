@@ -28,7 +28,8 @@ EXPORTED = (
     "kvs_cache_bytes", "kvs_encode_fp8", "kvs_append_kv", "kvs_decode_workspace_bytes",
     "kvs_decode_attn_scored", "kvs_decode_partial", "kvs_decode_combine", "kvs_decode_attn_profiled",
     "kvs_reattend_blocks",
-    "kvs_update_sidecar", "kvs_update_counters", "kvs_filter_blocks", "kvs_select_blocks", "kvs_status_str",
+    "kvs_update_sidecar", "kvs_update_counters", "kvs_filter_blocks", "kvs_select_blocks",
+    "kvs_compact_blocks", "kvs_status_str",
     "kvs_version",
 )
 
@@ -37,6 +38,10 @@ class KvsError(RuntimeError):
     def __init__(self, status: int, call: str):
         super().__init__(f"{call} failed: {status} ({status_str(status)})")
         self.status = status
+
+
+class BlockTable(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("rows", ctypes.c_int32)]
 
 
 class Geom(ctypes.Structure):
@@ -68,6 +73,7 @@ def _load():
         "kvs_update_sidecar": [P, P, P, P, P, I32, I32, I32, I64, F, P],
         "kvs_update_counters": [P, P, P, P, P, I32, I32, I32, F, F, I32, P],
         "kvs_filter_blocks": [P, P, P, I32, I32, F, P, P, I32, P],
+        "kvs_compact_blocks": [G, P, P, P, P, P, P, I32, P, I32, P],
         "kvs_select_blocks": [P, P, P, I32, I32, I32, I32, I32, P, P, P, P],
     }
     for name, args in sig.items():
@@ -336,6 +342,28 @@ def filter_blocks(score, cur_pos, theta: float, ids, n_ids, alive=None, stream=N
     _check(LIB.kvs_filter_blocks(_ptr(score), _ptr(alive), _ptr(cur_pos), B, nb, theta, _ptr(ids), _ptr(n_ids),
                                  ids.shape[1], _stream(stream)),
            "kvs_filter_blocks")
+
+
+def compact_blocks(cache: KVCache, keep_ids: torch.Tensor, n_keep: torch.Tensor, tables=(), stream=None):
+    """kvs_compact_blocks: kept blocks (ascending ids [B, S], counts [B]) move
+    to the front of the cache; ``tables`` are per-block arrays of 4-byte
+    entries shaped [B, NBmax] or [B, rows, NBmax], compacted alike."""
+    g = cache.geom
+    if g.ring:
+        raise ValueError("compaction applies to linear caches")
+    _device_check(keep_ids, n_keep, *tables)
+    if keep_ids.dtype != torch.int32 or keep_ids.dim() != 2 or keep_ids.shape[0] != g.batch \
+            or not keep_ids.is_contiguous():
+        raise ValueError("keep_ids must be contiguous int32 [B, S]")
+    arr = (BlockTable * max(1, len(tables)))()
+    for j, t in enumerate(tables):
+        if t.element_size() != 4 or not t.is_contiguous() or t.shape[0] != g.batch or t.shape[-1] != g.nb:
+            raise ValueError("tables must be contiguous 4-byte [B, (rows,) NBmax]")
+        arr[j] = BlockTable(t.data_ptr(), 1 if t.dim() == 2 else int(t.shape[1]))
+    _check(LIB.kvs_compact_blocks(ctypes.byref(g.c()), _ptr(cache.k), _ptr(cache.v), _ptr(cache.k_scale),
+                                  _ptr(cache.v_scale), _ptr(keep_ids), _ptr(n_keep), keep_ids.shape[1],
+                                  arr if tables else None, len(tables), _stream(stream)),
+           "kvs_compact_blocks")
 
 
 def update_sidecar(mass_accum, attended, ema, cum, traj, step: int, alpha: float, stream=None):

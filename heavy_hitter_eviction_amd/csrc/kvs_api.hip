@@ -314,6 +314,34 @@ int kvs_update_sidecar(float* mass_accum, float* attended, float* ema, float* cu
                                         traj_cap, step, alpha, (hipStream_t)stream));
 }
 
+int kvs_compact_blocks(const kvs_geom* g, void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                       const int32_t* keep_ids, const int32_t* n_keep, int32_t ids_stride,
+                       const kvs_block_table* tables, int32_t n_tables, void* stream) {
+  int st = check_geom(g);
+  if (st) return st;
+  if (g->ring != 0) return KVS_EINVAL;
+  const bool fp8 = g->kv_dtype == KVS_FP8_E4M3;
+  if (!k_cache || !v_cache || !keep_ids || !n_keep || ids_stride < 1) return KVS_EINVAL;
+  if (fp8 != (k_scale != nullptr) || fp8 != (v_scale != nullptr)) return KVS_EINVAL;
+  if (n_tables < 0 || n_tables > kvs::kMaxCompactTables || (n_tables > 0 && !tables)) return KVS_EINVAL;
+  const void* ptrs[] = {k_cache, v_cache, k_scale, v_scale, keep_ids, n_keep};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KVS_EALIGN;
+  kvs::CompactArgs a{};
+  for (int t = 0; t < n_tables; ++t) {
+    if (!tables[t].data || tables[t].rows < 1) return KVS_EINVAL;
+    if (!aligned16(tables[t].data)) return KVS_EALIGN;
+    a.tables[t] = tables[t].data;
+    a.table_rows[t] = tables[t].rows;
+  }
+  a.n_tables = n_tables;
+  a.k = k_cache; a.v = v_cache; a.ks = k_scale; a.vs = v_scale; a.ids = keep_ids; a.n_keep = n_keep;
+  a.B = g->batch; a.Hkv = g->n_kv_heads; a.C = g->capacity; a.NT = g->capacity / kTileSlots;
+  a.nbmax = g->n_blocks_max; a.ids_stride = ids_stride;
+  a.tile_bytes = kTileSlots * g->head_dim * elem_bytes(g->kv_dtype);
+  return hip_status(kvs::launch_compact(a, (hipStream_t)stream));
+}
+
 int kvs_update_counters(const float* attended, const float* ema, int32_t* hot_count, int32_t* cold_turns,
                         float* traj, int32_t batch, int32_t n_blocks_max, int32_t traj_cap, float hot_theta,
                         float cold_theta, int32_t cold_limit, void* stream) {

@@ -104,4 +104,19 @@ struct FilterArgs {
 };
 hipError_t launch_filter(const FilterArgs& a, hipStream_t st);
 
+constexpr int kMaxCompactTables = 8;
+struct CompactArgs {
+  void* k;
+  void* v;
+  float* ks;
+  float* vs;
+  const int32_t* ids;     // [B][ids_stride] kept block ids, ascending
+  const int32_t* n_keep;  // [B]
+  void* tables[kMaxCompactTables];  // per-block tables of 4-byte entries [B][rows][nbmax]
+  int table_rows[kMaxCompactTables];
+  int n_tables;
+  int B, Hkv, C, NT, nbmax, ids_stride, tile_bytes;
+};
+hipError_t launch_compact(const CompactArgs& a, hipStream_t st);
+
 }  // namespace kvs

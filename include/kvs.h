@@ -292,6 +292,44 @@ KVS_API int kvs_update_sidecar(float* mass_accum, float* attended, float* ema, f
                        int32_t batch, int32_t n_blocks_max, int32_t traj_cap, int64_t step,
                        float alpha, void* stream);
 
+/* One per-block table to compact alongside the cache: 4-byte entries (float
+ * or int32) laid out [B][rows][NBmax] (rows = 1 for Attended, EMA,
+ * Cumulative or a counter; rows = traj_cap for the trajectory ring). */
+typedef struct {
+  void* data;
+  int32_t rows;
+} kvs_block_table;
+
+/*
+ * kvs_compact_blocks -- move the kept blocks of a linear cache to the front,
+ * in order (Context Optimization, "H2O KV Cache Eviction / How It Works in
+ * Flash-MoE", step 4: survivors are moved to contiguous positions so later
+ * kernels see a shorter, contiguous sequence), at 16-slot block granularity
+ * (Per-Head Attention as a Scoring Signal: the block is the unit kept).
+ *
+ * For each sequence b and k < n_keep[b] (clamped to ids_stride and C/16),
+ * block keep_ids[b][k] becomes block k: its K and V codes of every KV head,
+ * its K/V scales (FP8), and its entry in every row of every table. Table
+ * entries from n_keep[b] on are set to zero; cache slots from block n_keep[b]
+ * on are left as they were (never read: decode reads slots <= cur_pos). Ids
+ * outside 0 .. C/16-1 move nothing. In place, on the stream; a ring cache
+ * gives KVS_EINVAL.
+ *
+ * After compaction the sequence continues at position (n_keep[b]-1)*16 +
+ * (i mod 16) + 1 when the current block (that of position i) is the last one
+ * kept, as kvs_select_blocks always keeps it; positions are then positions in
+ * the compacted sequence.
+ *
+ *   keep_ids  [B][ids_stride] int32, ascending and distinct (kvs_select_blocks'
+ *             sel_ids); other orders give unspecified contents, never a fault
+ *   n_keep    [B] int32
+ *   tables    n_tables (0..8) entries, each 16-byte aligned
+ */
+KVS_API int kvs_compact_blocks(const kvs_geom* geom, void* k_cache, void* v_cache, float* k_scale,
+                               float* v_scale, const int32_t* keep_ids, const int32_t* n_keep,
+                               int32_t ids_stride, const kvs_block_table* tables, int32_t n_tables,
+                               void* stream);
+
 /*
  * kvs_update_counters -- side-car counters for threshold views, once per turn
  * after kvs_update_sidecar (Context views at marginal cost, section 3: views

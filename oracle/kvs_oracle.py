@@ -470,6 +470,45 @@ def keep_mask_after(keep_ids, i, n_blocks):
 # KV memory sizes (Context Optimization, "Memory Budget Calculator")
 # ---------------------------------------------------------------------------
 
+# ---------------------------------------------------------------------------
+# Block compaction (Context Optimization, "H2O KV Cache Eviction / How It
+# Works in Flash-MoE", step 4)
+# ---------------------------------------------------------------------------
+
+def compact_rows(rows: np.ndarray, keep_ids, n_slots_after: int) -> np.ndarray:
+    """Survivors moved to contiguous positions: the per-position rows
+    ``[positions, ...]`` of one sequence, with kept block ``keep_ids[k]``
+    becoming block ``k`` (16 rows each), in order. Returns the first
+    ``n_slots_after`` rows of the compacted sequence."""
+    rows = np.asarray(rows)
+    out = np.zeros((n_slots_after,) + rows.shape[1:], dtype=rows.dtype)
+    for k, b in enumerate(keep_ids):
+        lo = k * BLOCK_TOKENS
+        if lo >= n_slots_after:
+            break
+        n = min(BLOCK_TOKENS, n_slots_after - lo, rows.shape[0] - b * BLOCK_TOKENS)
+        out[lo:lo + n] = rows[b * BLOCK_TOKENS: b * BLOCK_TOKENS + n]
+    return out
+
+
+def compact_table(table: np.ndarray, keep_ids) -> np.ndarray:
+    """A per-block table ``[rows, n_blocks]`` compacted alike: column
+    ``keep_ids[k]`` becomes column ``k``; the columns after the kept ones are
+    zero (their blocks are free)."""
+    table = np.asarray(table)
+    out = np.zeros_like(table)
+    ids = list(keep_ids)
+    if ids:
+        out[:, :len(ids)] = table[:, ids]
+    return out
+
+
+def compacted_position(i: int, n_keep: int) -> int:
+    """The current position after compaction when the current block (that of
+    position i) is the last one kept: the same offset inside the block."""
+    return (n_keep - 1) * BLOCK_TOKENS + i % BLOCK_TOKENS
+
+
 def kv_cache_bytes(n_layers, n_kv_heads, head_dim, bytes_per_elem, positions,
                    scale_bytes_per_position_per_cache=0):
     """``layers x 2 (K+V) x kv_heads x head_dim x bytes x positions``, plus the

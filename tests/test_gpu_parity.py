@@ -422,6 +422,72 @@ def test_profiled_ring_decode_per_head(api):
         gs.close_mass(mx_dev[b].cpu().numpy(), mx, kv, "max over heads")
 
 
+@pytest.mark.parametrize("kv", ["fp8", "bf16", "f32"])
+def test_compact_blocks_matches_oracle_and_preserves_attention(api, kv):
+    """Context Optimization, H2O step 4: kept blocks move to contiguous
+    positions. Codes, scales and side tables are compared bit-exactly with the
+    oracle's gather; decoding the compacted cache at the compacted position
+    equals the oracle's masked decode over the original cache."""
+    d, Hq, Hkv, C, B = (64, 8, 4, 1600, 2) if kv == "f32" else (128, 16, 4, 2064, 2)
+    geom, cache, K, V = _build_linear(api, kv, d, Hq, Hkv, C, B, 0, 17)
+    nb, T = geom.nb, 64
+    rng = np.random.default_rng(17)
+    cur = np.array([C - 1, C - 300], dtype=np.int32)
+    eb = {"fp8": 1, "bf16": 2, "f32": 4}[kv]
+    raw = lambda t: t.contiguous().view(-1).view(torch.uint8).cpu().numpy()  # noqa: E731
+    before_k = raw(cache.k)
+    before_v = raw(cache.v)
+    before_ks = cache.k_scale.cpu().numpy().reshape(B, C) if kv == "fp8" else None
+    before_vs = cache.v_scale.cpu().numpy().reshape(B, C) if kv == "fp8" else None
+    score = rng.random((B, nb))
+    keeps = [orc.select_blocks(score[b], None, int(cur[b]), 80, 64, 32) for b in range(B)]
+    S = max(len(k) for k in keeps) + 3
+    ids = np.full((B, S), -1, dtype=np.int32)
+    n_keep = np.array([len(k) for k in keeps], dtype=np.int32)
+    for b in range(B):
+        ids[b, :n_keep[b]] = keeps[b]
+    att = rng.random((B, nb)).astype(np.float32)
+    traj = rng.random((B, T, nb)).astype(np.float32)
+    cnt = rng.integers(0, 50, size=(B, nb)).astype(np.int32)
+    t_att, t_traj, t_cnt = gs.to_dev(att.copy()), gs.to_dev(traj.copy()), gs.to_dev(cnt.copy())
+    api.compact_blocks(cache, gs.to_dev(ids), gs.to_dev(n_keep), tables=(t_att, t_traj, t_cnt))
+    torch.cuda.synchronize()
+    got_k, got_v = raw(cache.k), raw(cache.v)
+    ws = torch.empty(api.decode_workspace_bytes(geom), dtype=torch.uint8, device="cuda")
+    qdt = torch.float32 if kv == "f32" else torch.bfloat16
+    q = torch.from_numpy(_rows((B, Hq, d), (17, 9))).to(qdt)
+    cur2 = np.array([orc.compacted_position(int(cur[b]), int(n_keep[b])) for b in range(B)], dtype=np.int32)
+    out = torch.empty_like(q).cuda()
+    mass = torch.zeros((B, nb), dtype=torch.float32, device="cuda")
+    api.decode_attn_scored(cache, q.cuda(), gs.to_dev(cur2), out, ws, mass_accum=mass)
+    torch.cuda.synchronize()
+    for b in range(B):
+        i, i2, keep = int(cur[b]), int(cur2[b]), keeps[b]
+        slots_new = np.arange(i2 + 1)
+        for which, before, got in (("k", before_k, got_k), ("v", before_v, got_v)):
+            old_rows = gs.logical_rows(before, B, Hkv, C, d, eb, b, np.arange(i + 1), which)
+            new_rows = gs.logical_rows(got, B, Hkv, C, d, eb, b, slots_new, which)
+            assert np.array_equal(new_rows, orc.compact_rows(old_rows, keep, i2 + 1)), which
+        if kv == "fp8":
+            assert np.array_equal(cache.k_scale.cpu().numpy().reshape(B, C)[b, :i2 + 1],
+                                  orc.compact_rows(before_ks[b, :i + 1], keep, i2 + 1))
+            assert np.array_equal(cache.v_scale.cpu().numpy().reshape(B, C)[b, :i2 + 1],
+                                  orc.compact_rows(before_vs[b, :i + 1], keep, i2 + 1))
+        assert np.array_equal(t_att[b].cpu().numpy(), orc.compact_table(att[b][None], keep)[0])
+        assert np.array_equal(t_traj[b].cpu().numpy(), orc.compact_table(traj[b], keep))
+        assert np.array_equal(t_cnt[b].cpu().numpy(), orc.compact_table(cnt[b][None], keep)[0])
+        alive = np.zeros(nb, dtype=bool)
+        alive[keep] = True
+        Kd = gs.heads(gs.dequant_rows(K[b, :i + 1], kv), Hkv, d)
+        Vd = gs.heads(gs.dequant_rows(V[b, :i + 1], kv), Hkv, d)
+        o_ref, m_ref, pav = gs.oracle_layer(q[b].double().numpy(), Kd, Vd, np.arange(i + 1), i, 0, alive,
+                                            orc.softmax_scale(d), nb)
+        gs.close_o(out[b].float().cpu().numpy(), o_ref, kv, pav)
+        m_new = np.zeros(nb)
+        m_new[:len(keep)] = m_ref[keep]
+        gs.close_mass(mass[b].cpu().numpy(), m_new, kv, "compacted masses")
+
+
 # ---------------------------------------------------------------- side-car and selection
 
 def test_sidecar_update_matches_oracle(api):

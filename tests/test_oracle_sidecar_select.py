@@ -219,3 +219,46 @@ def test_selection_on_attended_is_tova():
     keep = orc.select_blocks(att, None, i, len(cand) - 1, R, 0)
     dropped = set(range(nb)) - set(keep.tolist())
     assert dropped == {min(cand, key=lambda b: att[b])}
+
+
+# ---------------------------------------------------------------- block compaction
+
+def test_compaction_preserves_attention_over_the_kept_blocks():
+    """Context Optimization, H2O step 4: after moving the survivors to
+    contiguous positions the kernels see a shorter sequence with the same
+    keys, so attention at the compacted position equals attention over the
+    original with the evicted blocks masked, and each kept block's mass moves
+    with it."""
+    rng = np.random.default_rng(14)
+    Hq, Hkv, d, i, nb = 8, 2, 16, 16 * 20 + 6, 24
+    K = rng.standard_normal((Hkv, i + 1, d))
+    V = rng.standard_normal((Hkv, i + 1, d))
+    q = rng.standard_normal((Hq, d))
+    score = rng.random(nb)
+    keep = orc.select_blocks(score, None, i, 6, 20, 4)
+    assert keep[-1] == i // 16
+    alive = np.zeros(nb, dtype=bool)
+    alive[keep] = True
+    o_mask, m_mask = orc.attend_scored(q, K, V, np.arange(i + 1), i, 0, alive, 0.25, nb)
+    i2 = orc.compacted_position(i, len(keep))
+    Kc = orc.compact_rows(K.transpose(1, 0, 2), keep, i2 + 1).transpose(1, 0, 2)
+    Vc = orc.compact_rows(V.transpose(1, 0, 2), keep, i2 + 1).transpose(1, 0, 2)
+    o_c, m_c = orc.attend_scored(q, Kc, Vc, np.arange(i2 + 1), i2, 0, None, 0.25, nb)
+    assert np.abs(o_c - o_mask).max() <= 1e-12
+    assert np.abs(m_c[:len(keep)] - m_mask[keep]).max() <= 1e-12 and not m_c[len(keep):].any()
+
+
+def test_compaction_gather_brute_force():
+    rng = np.random.default_rng(15)
+    rows = rng.standard_normal((16 * 9 + 5, 3))
+    keep = [0, 2, 3, 7, 9]
+    n_after = 16 * 4 + 5
+    out = orc.compact_rows(rows, keep, n_after)
+    for s_new in range(n_after):
+        k, t = divmod(s_new, 16)
+        assert np.array_equal(out[s_new], rows[16 * keep[k] + t])
+    table = rng.random((3, 12))
+    ct = orc.compact_table(table, keep)
+    for k in range(12):
+        assert np.array_equal(ct[:, k], table[:, keep[k]] if k < len(keep) else np.zeros(3))
+    assert orc.compacted_position(16 * 9 + 4, 5) == 16 * 4 + 4
