@@ -41,10 +41,14 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=("decode", "profiled", "reattend"), default="decode",
+    ap.add_argument("--mode", choices=("decode", "profiled", "reattend", "compact"), default="decode",
                     help="decode: the scored decode step (headline); profiled: the same step also "
                          "keeping per-head block masses and their max over heads and layers; "
-                         "reattend: Tier 2, a new query over the blocks the selection kept")
+                         "reattend: Tier 2, a new query over the blocks the selection kept; "
+                         "compact: evict mode that moves the kept blocks to the front after each "
+                         "selection (H2O compaction) and decodes the shorter cache")
+    ap.add_argument("--compact-every", type=int, default=64,
+                    help="compact mode: steps between physical compactions (evicted blocks are masked between)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
                          "(a reference for hardware byte counters)")
@@ -265,6 +269,81 @@ def run_reattend(args, w):
     }
 
 
+def run_compact(args, w):
+    """Evict mode with block compaction (Context Optimization, H2O steps 3-4):
+    each step appends, decodes every layer over the kept blocks (masking the
+    dropped ones), closes the turn and selects; every ``compact_every`` steps
+    the kept blocks and side-car entries move to the front of every layer's
+    cache. The first step compacts the prefilled cache down to the kept set
+    (untimed, with the other warm-up steps); the timed steps are whole
+    compaction periods, compactions included."""
+    import torch
+
+    from heavy_hitter_eviction_amd.session import ScoredDecoder
+
+    N = args.compact_every
+    steps = max(N, (args.steps + N - 1) // N * N)
+    warm = max(1, args.warmup)
+    if warm + steps > w.steps:
+        steps = (w.steps - warm) // N * N
+    if steps < 1:
+        raise SystemExit("not enough decode steps for one compaction period")
+    n_steps = warm + steps
+    dec = ScoredDecoder(w, compact=True, compact_every=N)
+    prefill(dec, w, args.seed)
+    Q, K, V = step_inputs(w, args.seed, n_steps, dec.n_layers)
+    L = dec.n_layers
+    per_key = 2 * w.n_kv_heads * w.head_dim * (1 if w.kv_dtype == "fp8" else 2 if w.kv_dtype == "bf16" else 4) \
+        + (8 if w.kv_dtype == "fp8" else 0)
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    seen = []
+    for t in range(n_steps):
+        timed = t >= warm
+        if timed:
+            seen.append((dec.keep.clone(), dec.pos.clone()))
+            sev[t - warm][0].record()
+        compact_now = True if t == 0 else (None if t >= warm else False)
+        dec.step_compact([Q[l][t] for l in range(L)], [K[l][t] for l in range(L)], [V[l][t] for l in range(L)],
+                         compact_now=compact_now)
+        if timed:
+            sev[t - warm][1].record()
+        if t == warm - 1:
+            dec.step_index = 0            # the schedule counts from the first timed step
+    torch.cuda.synchronize()
+    step_ms = [a.elapsed_time(b) for a, b in sev]
+    ms = sum(step_ms) / len(step_ms)
+    # keys each step read: the kept blocks up to the current one (always kept)
+    keys = 0
+    for keep, pos in seen:
+        bits = keep.cpu().numpy().view("uint32")
+        for b in range(w.batch):
+            p = int(pos[b])
+            nblk = p // 16 + 1
+            kept = sum((int(bits[b, k >> 5]) >> (k & 31)) & 1 for k in range(nblk))
+            keys += 16 * kept - (15 - p % 16)
+    kb = keys / len(seen) * per_key * L
+    gbs = kb / (ms / 1e3) / 1e9
+    return {
+        "metric": "evict-mode step with H2O block compaction: KV GB/s read per step",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.kv_dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "mode": "evict + compact", "compact_every": N,
+                   "budget_blocks": w.budget_blocks, "recent_tokens": w.recent_tokens, "layers": L,
+                   "keys_per_sequence_read": round(kb / per_key / L / w.batch, 1)},
+        "step_ms_p10_p50_p90": [round(float(x), 4) for x in _percentiles(step_ms, (10, 50, 90))],
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+    }
+
+
 def oracle_baseline(w, seed, seconds):
     """Time the float64 oracle (as it stands) on (sequence, layer) units of the
     same workload at the first timed step: FP8 decode (or bf16 widening) of the
@@ -335,6 +414,9 @@ def main():
     w = workloads.ALL[args.workload]
     if args.mode == "reattend":
         print(json.dumps(run_reattend(args, w)), flush=True)
+        return
+    if args.mode == "compact":
+        print(json.dumps(run_compact(args, w)), flush=True)
         return
 
     dec, total_ms, part_ms, step_ms = run_gpu(args, w)

@@ -209,7 +209,7 @@ int decode_setup(const kvs_geom* g, const void* q, const void* k_cache, const vo
   c->ws_m = a->ws_m; c->ws_l = a->ws_l; c->ws_o = a->ws_o; c->ws_e = a->ws_e; c->cur_pos = cur_pos;
   c->out = out; c->mass = mass_accum;
   c->B = g->batch; c->Hq = g->n_q_heads; c->D = g->head_dim; c->C = g->capacity; c->NT = p.NT;
-  c->nbmax = g->n_blocks_max; c->tpp = p.tpp; c->nparts = p.nparts;
+  c->nbmax = g->n_blocks_max; c->tpp = p.tpp; c->nparts = p.nparts; c->window = g->window;
   c->n_o_chunks = (g->n_q_heads * g->head_dim + 255) / 256;
   c->n_mass_chunks = (p.NT + 255) / 256;
   *kv = fp8 ? kvs::KV_FP8 : g->kv_dtype == KVS_BF16 ? kvs::KV_BF16 : kvs::KV_F32;

@@ -15,10 +15,30 @@
 namespace kvs {
 
 constexpr int kCompactThreads = 512;
-constexpr int kPiecesPerThread = 8;  // 16-byte pieces held per thread per chunk
+constexpr int kPiecesPerThread = 8;  // 16-byte pieces held per thread per chunk (two chunks in flight)
+
+// With ids ascending and distinct, ids[k] == k holds exactly on a prefix (once
+// ids[k] > k it stays so). Returns its length: moves start there. One pass,
+// each thread checking a strided share, reduced with an LDS minimum.
+__device__ int in_place_prefix(const int32_t* ids, int n, int* s_first) {
+  if (threadIdx.x == 0) *s_first = n;
+  __syncthreads();
+  int first = n;
+  for (int k = threadIdx.x; k < n; k += kCompactThreads)
+    if (ids[k] != k) {
+      first = k;
+      break;
+    }
+  if (first < n) atomicMin(s_first, first);
+  __syncthreads();
+  return *s_first;
+}
 
 // K/V tiles of one (KV head, sequence), plus the sequence's K/V scales (KV
-// head 0's workgroup). grid (Hkv, B).
+// head 0's workgroup). grid (Hkv, B). Chunks are software-pipelined: the
+// next chunk's sources (never a destination of this or an earlier chunk) are
+// loaded while this chunk is stored; a barrier separates each chunk's loads
+// from its own stores.
 __global__ __launch_bounds__(kCompactThreads) void kvs_compact_kv(CompactArgs a) {
   const int g = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x;
@@ -35,37 +55,50 @@ __global__ __launch_bounds__(kCompactThreads) void kvs_compact_kv(CompactArgs a)
   const int code_pieces = (int)(tb / 16);
   const int pieces_per_tile = 2 * code_pieces + (scales ? 8 : 0);
   const int chunk = max(1, kCompactThreads * kPiecesPerThread / pieces_per_tile);  // tiles per round
-  for (int k0 = 0; k0 < n; k0 += chunk) {
-    const int nk = min(chunk, n - k0);
-    const int total = nk * pieces_per_tile;
-    u32x4 buf[kPiecesPerThread];
+  __shared__ int s_first;
+  const int m = in_place_prefix(ids, n, &s_first);
+  // address of piece pc of block blk
+  auto addr = [&](int blk, int pc) -> char* {
+    if (pc < code_pieces) return kreg + (size_t)blk * tb + 16 * pc;
+    if (pc < 2 * code_pieces) return vreg + (size_t)blk * tb + 16 * (pc - code_pieces);
+    if (pc < 2 * code_pieces + 4) return (char*)(ksb + (size_t)blk * kTile + 4 * (pc - 2 * code_pieces));
+    return (char*)(vsb + (size_t)blk * kTile + 4 * (pc - 2 * code_pieces - 4));
+  };
+  auto load = [&](u32x4* buf, int k0) {
+    const int total = min(chunk, n - k0) * pieces_per_tile;
 #pragma unroll
     for (int r = 0; r < kPiecesPerThread; ++r) {
       const int x = tid + r * kCompactThreads;
       if (x < total) {
-        const int k = k0 + x / pieces_per_tile, pc = x % pieces_per_tile;
+        const int k = k0 + x / pieces_per_tile;
         const int src = ids[k];
-        if (src < 0 || src >= a.NT) continue;  // not a block of this cache: no move
-        if (pc < code_pieces) buf[r] = *(const u32x4*)(kreg + (size_t)src * tb + 16 * pc);
-        else if (pc < 2 * code_pieces) buf[r] = *(const u32x4*)(vreg + (size_t)src * tb + 16 * (pc - code_pieces));
-        else if (pc < 2 * code_pieces + 4) buf[r] = *(const u32x4*)(ksb + (size_t)src * kTile + 4 * (pc - 2 * code_pieces));
-        else buf[r] = *(const u32x4*)(vsb + (size_t)src * kTile + 4 * (pc - 2 * code_pieces - 4));
+        if (src >= 0 && src < a.NT && src != k) buf[r] = *(const u32x4*)addr(src, x % pieces_per_tile);
       }
     }
-    __syncthreads();  // every source of this chunk is read before any store
+  };
+  auto store = [&](const u32x4* buf, int k0) {
+    const int total = min(chunk, n - k0) * pieces_per_tile;
 #pragma unroll
     for (int r = 0; r < kPiecesPerThread; ++r) {
       const int x = tid + r * kCompactThreads;
       if (x < total) {
-        const int k = k0 + x / pieces_per_tile, pc = x % pieces_per_tile;
-        if (ids[k] < 0 || ids[k] >= a.NT) continue;
-        if (pc < code_pieces) *(u32x4*)(kreg + (size_t)k * tb + 16 * pc) = buf[r];
-        else if (pc < 2 * code_pieces) *(u32x4*)(vreg + (size_t)k * tb + 16 * (pc - code_pieces)) = buf[r];
-        else if (pc < 2 * code_pieces + 4) *(u32x4*)(ksb + (size_t)k * kTile + 4 * (pc - 2 * code_pieces)) = buf[r];
-        else *(u32x4*)(vsb + (size_t)k * kTile + 4 * (pc - 2 * code_pieces - 4)) = buf[r];
+        const int k = k0 + x / pieces_per_tile;
+        const int src = ids[k];
+        if (src >= 0 && src < a.NT && src != k) *(u32x4*)addr(k, x % pieces_per_tile) = buf[r];
       }
     }
+  };
+  if (m >= n) return;
+  u32x4 bufa[kPiecesPerThread], bufb[kPiecesPerThread];
+  load(bufa, m);
+  for (int k0 = m; k0 < n; k0 += 2 * chunk) {
+    __syncthreads();  // chunk k0 read everywhere before any of its stores
+    if (k0 + chunk < n) load(bufb, k0 + chunk);
+    store(bufa, k0);
+    if (k0 + chunk >= n) break;
     __syncthreads();
+    if (k0 + 2 * chunk < n) load(bufa, k0 + 2 * chunk);
+    store(bufb, k0 + chunk);
   }
 }
 
@@ -80,18 +113,20 @@ __global__ __launch_bounds__(kCompactThreads) void kvs_compact_rows(CompactArgs 
   const int n = min(max(a.n_keep[b], 0), min(a.ids_stride, a.nbmax));
   const int32_t* ids = a.ids + (size_t)b * a.ids_stride;
   const int tid = threadIdx.x;
-  for (int k0 = 0; k0 < n; k0 += kCompactThreads * kPiecesPerThread) {
+  __shared__ int s_first;
+  const int m = in_place_prefix(ids, n, &s_first);
+  for (int k0 = m; k0 < n; k0 += kCompactThreads * kPiecesPerThread) {
     uint32_t v[kPiecesPerThread];
 #pragma unroll
     for (int r = 0; r < kPiecesPerThread; ++r) {
       const int k = k0 + tid + r * kCompactThreads;
-      if (k < n && ids[k] >= 0 && ids[k] < a.nbmax) v[r] = base[ids[k]];
+      if (k < n && ids[k] >= 0 && ids[k] < a.nbmax && ids[k] != k) v[r] = base[ids[k]];
     }
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < kPiecesPerThread; ++r) {
       const int k = k0 + tid + r * kCompactThreads;
-      if (k < n && ids[k] >= 0 && ids[k] < a.nbmax) base[k] = v[r];
+      if (k < n && ids[k] >= 0 && ids[k] < a.nbmax && ids[k] != k) base[k] = v[r];
     }
     __syncthreads();
   }

@@ -125,8 +125,21 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   const int i_cur = a.cur_pos[b];
   const int lo = a.window > 0 ? i_cur - a.window + 1 : (int)0x80000000;
 
-  const int t0 = part * a.tpp;
-  const int t1 = min(t0 + a.tpp, a.NT);
+  // This workgroup's tiles [t0, t1). A ring reads every tile; a linear cache
+  // splits its readable range (window start .. current position) evenly over
+  // the partitions, so a partly filled or compacted cache keeps every
+  // workgroup busy. kvs_combine derives the same split from cur_pos.
+  int t0, t1;
+  if constexpr (RING) {
+    t0 = part * a.tpp;
+    t1 = min(t0 + a.tpp, a.NT);
+  } else {
+    const int gte = max(0, min(a.NT, i_cur / kTile + 1));
+    const int gtb = a.window > 0 ? min(gte, max(lo, 0) / kTile) : 0;
+    const int tpe = max(1, (gte - gtb + a.nparts - 1) / a.nparts);
+    t0 = min(gte, gtb + part * tpe);
+    t1 = min(gte, t0 + tpe);
+  }
 
   // LDS carve-up (16-byte aligned parts first): per-wave side data (FP8
   // scales, ring positions of the claimed tiles), the wave merge area, the
@@ -149,11 +162,7 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   if (threadIdx.x == 0) misc[1] = 0;
 
   // Tiles that can hold a readable key.
-  int tb = t0, te = t1;
-  if constexpr (!RING) {
-    te = max(t0, min(te, i_cur / kTile + 1));
-    if (a.window > 0) tb = min(te, max(tb, max(lo, 0) / kTile));
-  }
+  const int tb = t0, te = t1;
 
   // With a keep mask, or a list of block ids to re-attend, on a linear cache
   // (tile = block), wave 0 compacts the partition's readable tiles into tlist,
@@ -674,8 +683,17 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
   const int chunk = blockIdx.x - a.n_o_chunks;
   const int i_cur = a.cur_pos[b];
   const int lap_i = RING ? i_cur / a.C : 0;
-  for (int t = chunk * 256 + threadIdx.x; t < a.NT; t += a.n_mass_chunks * 256) {
-    const int p = t / a.tpp;
+  // tiles with block sums: every tile of a ring; a linear cache's readable
+  // range, split over the partitions as the partial kernel split it
+  int tlo = 0, thi = a.NT, tpe = a.tpp;
+  if constexpr (!RING) {
+    const int lo = a.window > 0 ? i_cur - a.window + 1 : 0;
+    thi = max(0, min(a.NT, i_cur / kTile + 1));
+    tlo = a.window > 0 ? min(thi, max(lo, 0) / kTile) : 0;
+    tpe = max(1, (thi - tlo + P - 1) / P);
+  }
+  for (int t = tlo + chunk * 256 + threadIdx.x; t < thi; t += a.n_mass_chunks * 256) {
+    const int p = (t - tlo) / tpe;
     // logical block of each sub-block of tile t (-1: none)
     int blk[NSUB];
 #pragma unroll

@@ -44,7 +44,7 @@ struct CombineArgs {
   float* mass;
   float* head_mass;  // [B][Hq][nbmax] per-head block masses (+=), or NULL
   float* mass_max;   // [B][nbmax] running max over heads (and calls), or NULL
-  int B, Hq, D, C, NT, nbmax, tpp, nparts, n_o_chunks, n_mass_chunks;
+  int B, Hq, D, C, NT, nbmax, tpp, nparts, n_o_chunks, n_mass_chunks, window;
 };
 
 hipError_t launch_partial(int kv, int d, const PartialArgs& a, bool scored, bool ring,

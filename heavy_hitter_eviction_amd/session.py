@@ -6,7 +6,10 @@ block masses into ``mass``. After the last layer the side-car closes the turn,
 and the heavy-hitter selection produces the keep mask. In evict mode that
 mask feeds the next step's attention, so dropped blocks are never read again
 (Context Optimization, "H2O KV Cache Eviction"); in score-only mode the full
-context is read and the mask is only reported.
+context is read and the mask is only reported. Compact mode (linear caches) is
+evict mode plus, every ``compact_every`` steps, moving the kept blocks to the
+front of every layer's cache with the side-car arrays (H2O step 4); the
+sequence then continues at its compacted position.
 
 Host code here only sequences library calls and owns torch buffers.
 """
@@ -26,9 +29,16 @@ def geom_of(w: Workload) -> api.CacheGeom:
 
 
 class ScoredDecoder:
-    def __init__(self, w: Workload, evict: bool = False, device="cuda", layers: int | None = None):
+    def __init__(self, w: Workload, evict: bool = False, device="cuda", layers: int | None = None,
+                 compact: bool = False, compact_every: int = 1):
+        if compact and (w.ring or w.window or not w.select):
+            raise ValueError("compaction needs a linear cache with selection and no window")
+        if compact_every < 1:
+            raise ValueError("compact_every must be at least 1")
         self.w = w
         self.evict = evict
+        self.compact = compact
+        self.compact_every = compact_every
         self.device = torch.device(device)
         self.geom = geom_of(w)
         self.n_layers = w.n_layers if layers is None else layers
@@ -50,6 +60,8 @@ class ScoredDecoder:
                     for _ in range(self.n_layers)]
         self.row_seq = torch.arange(B, dtype=torch.int32, device=device)
         self.step_index = 0
+        # compact mode: each sequence's next position in its compacted cache
+        self.pos = torch.full((B,), w.context, dtype=torch.int32, device=device)
 
     def prefill(self, layer: int, seq: int, k_rows: torch.Tensor, v_rows: torch.Tensor, pos0: int = 0):
         n = k_rows.shape[0]
@@ -70,6 +82,36 @@ class ScoredDecoder:
             self.caches[l].append(k_layers[l], v_layers[l], self.row_seq, cur_pos)
             self.attend_layer(l, q_layers[l], cur_pos)
         self.close_turn(cur_pos)
+
+    def step_compact(self, q_layers, k_layers, v_layers, compact_now: bool | None = None):
+        """One decode step in compact mode: evict mode at each sequence's
+        compacted position (dropped blocks are masked out of the reads), and
+        every ``compact_every`` steps the kept blocks and their side-car
+        entries move to the front of every layer's cache, which frees the
+        dropped blocks' slots (H2O step 4)."""
+        cur = self.pos
+        for l in range(self.n_layers):
+            self.caches[l].append(k_layers[l], v_layers[l], self.row_seq, cur)
+            api.decode_attn_scored(self.caches[l], q_layers[l], cur, self.out[l], self.workspace,
+                                   mass_accum=self.mass, keep_mask=self.keep)
+        api.update_sidecar(self.mass, self.attended, self.ema, self.cum, self.traj,
+                           self.step_index, self.w.alpha)
+        api.select_blocks(self.cum, cur, self.w.budget_blocks, self.w.recent_tokens, self.w.sink_tokens,
+                          alive=self.keep, keep_mask=self.keep, sel_ids=self.sel_ids, n_sel=self.n_sel)
+        self.step_index += 1
+        if compact_now is None:
+            compact_now = self.step_index % self.compact_every == 0
+        if not compact_now:
+            self.pos = cur + 1
+            return
+        side = (self.attended, self.ema, self.cum, self.traj)
+        for l in range(self.n_layers):
+            # the side-car arrays move once, with the last layer's cache
+            api.compact_blocks(self.caches[l], self.sel_ids, self.n_sel,
+                               tables=side if l == self.n_layers - 1 else ())
+        self.keep.fill_(-1)                      # every block of the compacted cache is alive
+        # the current block is always kept last: same offset inside it
+        self.pos = ((self.n_sel - 1) * 16 + cur % 16 + 1).to(torch.int32)
 
     def close_turn(self, cur_pos: torch.Tensor):
         api.update_sidecar(self.mass, self.attended, self.ema, self.cum, self.traj,

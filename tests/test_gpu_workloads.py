@@ -347,3 +347,63 @@ def test_35b_fp8_ring_window_workload(session_mod):
                 gs.close_o(_np(dec.out[layer][seq].float()), o_ref, "fp8", pav)
                 mass += m_ref
             gs.close_mass(att[seq], mass, "fp8", f"attended at step {t}")
+
+
+# ---------------------------------------------------------------- evict with compaction
+
+@pytest.mark.parametrize("wname,every", [("tiny", 1), ("tiny", 3), ("35b_bf16", 1), ("35b_bf16", 5)])
+def test_compact_mode_equals_evict_mode(session_mod, wname, every):
+    """Context Optimization, H2O steps 3-4: evicting by moving the kept blocks
+    to contiguous positions gives, at every step, the same attention output,
+    the same block masses and the same kept set (mapped back to original block
+    ids) as evicting by masking the dropped blocks in place."""
+    api, session = session_mod
+    w = workloads.ALL[wname]
+    seed = 3
+    ev = session.ScoredDecoder(w, evict=True)
+    cp = session.ScoredDecoder(w, compact=True, compact_every=every)
+    for dec in (ev, cp):
+        if wname == "tiny":
+            dec.prefill(0, 0, synth.prefill_rows(w, seed, 0, 0, synth.T_K, "cuda"),
+                        synth.prefill_rows(w, seed, 0, 0, synth.T_V, "cuda"))
+        else:
+            _prefill_gpu(dec, w, seed)
+    n_steps = w.steps if wname == "tiny" else 24
+    Q, K, V = _step_inputs(w, seed, w.n_layers, n_steps)
+    origin = np.tile(np.arange(cp.geom.nb), (w.batch, 1))   # compacted block -> original block
+    f32 = w.kv_dtype == "f32"
+    for t in range(n_steps):
+        cur = torch.full((w.batch,), w.context + t, dtype=torch.int32, device="cuda")
+        qs, ks, vs = [Q[l][t] for l in range(w.n_layers)], [K[l][t] for l in range(w.n_layers)], \
+            [V[l][t] for l in range(w.n_layers)]
+        pos_c = _np(cp.pos)
+        for b in range(w.batch):
+            # the block being written is a new original block once it starts
+            origin[b, pos_c[b] // 16] = (w.context + t) // 16
+        ev.step(qs, ks, vs, cur)
+        cp.step_compact(qs, ks, vs)
+        torch.cuda.synchronize()
+        for l in range(w.n_layers):
+            a, b = _np(ev.out[l].float()), _np(cp.out[l].float())
+            tol = (1e-5 * np.abs(a) + 1e-6) if f32 else (2.0 ** -6 * np.abs(a) + 2e-3)
+            assert (np.abs(a - b) <= tol).all(), f"step {t} layer {l}"
+        ev_att = _np(ev.attended)
+        n_sel = _np(cp.n_sel)
+        sel_c = _np(cp.sel_ids)
+        att_c = _np(cp.attended)
+        compacted = cp.step_index % every == 0
+        for b in range(w.batch):
+            kept_orig = origin[b, sel_c[b, :n_sel[b]]]
+            ev_ids = _np(ev.sel_ids[b, :int(ev.n_sel[b])])
+            assert np.array_equal(kept_orig, ev_ids), f"step {t} sequence {b}: kept sets differ"
+            mtol = (1e-5 if f32 else 1e-4) * max(1.0, ev_att[b].max())
+            if compacted:
+                # Attended moved with the blocks: entry k belongs to kept_orig[k]
+                assert np.abs(att_c[b, :n_sel[b]] - ev_att[b, kept_orig]).max() <= mtol
+                new_origin = np.zeros_like(origin[b])
+                new_origin[:n_sel[b]] = kept_orig
+                origin[b] = new_origin
+            else:
+                # not compacted yet: compacted-space blocks 0 .. pos/16 keep their origins
+                live = np.arange(int(pos_c[b]) // 16 + 1)
+                assert np.abs(att_c[b, live] - ev_att[b, origin[b, live]]).max() <= mtol
