@@ -41,12 +41,13 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=("decode", "profiled", "reattend", "compact"), default="decode",
+    ap.add_argument("--mode", choices=("decode", "profiled", "reattend", "compact", "snapkv"), default="decode",
                     help="decode: the scored decode step (headline); profiled: the same step also "
                          "keeping per-head block masses and their max over heads and layers; "
                          "reattend: Tier 2, a new query over the blocks the selection kept; "
                          "compact: evict mode that moves the kept blocks to the front after each "
-                         "selection (H2O compaction) and decodes the shorter cache")
+                         "selection (H2O compaction) and decodes the shorter cache; snapkv: prefill "
+                         "scoring from the last 32 prompt queries, max-pooled per block")
     ap.add_argument("--compact-every", type=int, default=64,
                     help="compact mode: steps between physical compactions (evicted blocks are masked between)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -344,6 +345,56 @@ def run_compact(args, w):
     }
 
 
+def run_snapkv(args, w):
+    """SnapKV-style prefill scoring (Context views at marginal cost, section 3,
+    Fact 1) after the prefill: per layer, the last 32 prompt positions' queries
+    score every prompt token per head, max-pooled with kernel 7 into block
+    scores. Two passes over K."""
+    import torch
+
+    from heavy_hitter_eviction_amd import api, synth
+    from heavy_hitter_eviction_amd.session import ScoredDecoder
+
+    W = 32
+    dec = ScoredDecoder(w)
+    prefill(dec, w, args.seed)
+    L = dec.n_layers
+    g = dec.geom
+    qw = [synth.normal((w.batch, W, w.n_q_heads * w.head_dim), (args.seed, 97, l), "cuda")
+          .reshape(w.batch, W, w.n_q_heads, w.head_dim).to(torch.bfloat16).contiguous() for l in range(L)]
+    n = torch.full((w.batch,), w.context, dtype=torch.int32, device="cuda")
+    ts = torch.zeros((w.batch, w.n_q_heads, w.capacity), dtype=torch.float32, device="cuda")
+    bs = torch.zeros((w.batch, g.nb), dtype=torch.float32, device="cuda")
+    ws = torch.empty(api.snapkv_workspace_bytes(g, W), dtype=torch.uint8, device="cuda")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps * L)]
+    for l in range(L):
+        api.snapkv_scores(dec.caches[l], qw[l], n, ts, ws, block_score=bs)
+    for r in range(args.steps):
+        for l in range(L):
+            a, b = evs[r * L + l]
+            a.record()
+            api.snapkv_scores(dec.caches[l], qw[l], n, ts, ws, block_score=bs)
+            b.record()
+    torch.cuda.synchronize()
+    us = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e3
+    kbytes = w.batch * w.context * w.n_kv_heads * w.head_dim * (1 if w.kv_dtype == "fp8" else 2) \
+        + (w.batch * w.context * 4 if w.kv_dtype == "fp8" else 0)
+    gbs = 2 * kbytes / (us / 1e6) / 1e9
+    return {
+        "metric": "SnapKV prefill scoring: K GB/s over its two passes, per layer call",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": 1,
+        "ms_per_step": round(us * L / 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.kv_dtype, "data": "synthetic",
+        "config": {"workload": w.name, "mode": "snapkv", "window": W, "pool_kernel": 7, "layers": L,
+                   "prompt_tokens": w.context},
+        "us_per_layer": round(us, 2),
+        "roofline": {"kernel": "kvs_snap_pass x2 + merge + pool (one call)", "bound": "hbm",
+                     "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "avg_launch_us": round(us, 2),
+                     "bytes_per_launch": int(2 * kbytes)},
+    }
+
+
 def oracle_baseline(w, seed, seconds):
     """Time the float64 oracle (as it stands) on (sequence, layer) units of the
     same workload at the first timed step: FP8 decode (or bf16 widening) of the
@@ -417,6 +468,9 @@ def main():
         return
     if args.mode == "compact":
         print(json.dumps(run_compact(args, w)), flush=True)
+        return
+    if args.mode == "snapkv":
+        print(json.dumps(run_snapkv(args, w)), flush=True)
         return
 
     dec, total_ms, part_ms, step_ms = run_gpu(args, w)

@@ -29,7 +29,7 @@ EXPORTED = (
     "kvs_decode_attn_scored", "kvs_decode_partial", "kvs_decode_combine", "kvs_decode_attn_profiled",
     "kvs_reattend_blocks",
     "kvs_update_sidecar", "kvs_update_counters", "kvs_filter_blocks", "kvs_select_blocks",
-    "kvs_compact_blocks", "kvs_status_str",
+    "kvs_compact_blocks", "kvs_snapkv_workspace_bytes", "kvs_snapkv_scores", "kvs_status_str",
     "kvs_version",
 )
 
@@ -74,6 +74,8 @@ def _load():
         "kvs_update_counters": [P, P, P, P, P, I32, I32, I32, F, F, I32, P],
         "kvs_filter_blocks": [P, P, P, I32, I32, F, P, P, I32, P],
         "kvs_compact_blocks": [G, P, P, P, P, P, P, I32, P, I32, P],
+        "kvs_snapkv_workspace_bytes": [G, I32, SZP],
+        "kvs_snapkv_scores": [G, P, I32, P, P, P, P, P, I32, P, SZ, P],
         "kvs_select_blocks": [P, P, P, I32, I32, I32, I32, I32, P, P, P, P],
     }
     for name, args in sig.items():
@@ -364,6 +366,34 @@ def compact_blocks(cache: KVCache, keep_ids: torch.Tensor, n_keep: torch.Tensor,
                                   _ptr(cache.v_scale), _ptr(keep_ids), _ptr(n_keep), keep_ids.shape[1],
                                   arr if tables else None, len(tables), _stream(stream)),
            "kvs_compact_blocks")
+
+
+def snapkv_workspace_bytes(geom: CacheGeom, window: int) -> int:
+    n = ctypes.c_size_t()
+    _check(LIB.kvs_snapkv_workspace_bytes(ctypes.byref(geom.c()), window, ctypes.byref(n)),
+           "kvs_snapkv_workspace_bytes")
+    return n.value
+
+
+def snapkv_scores(cache: KVCache, q_window: torch.Tensor, n_prompt: torch.Tensor, token_score: torch.Tensor,
+                  workspace: torch.Tensor, block_score: torch.Tensor | None = None, pool_kernel: int = 7,
+                  stream=None):
+    """kvs_snapkv_scores: observation-window scores per (token, head) and
+    max-pooled block scores (+=). ``q_window`` bf16 [B, W, Hq, d]."""
+    g = cache.geom
+    _device_check(q_window, n_prompt, token_score, workspace, block_score)
+    if q_window.dtype != torch.bfloat16 or q_window.dim() != 4 or q_window.shape[0] != g.batch \
+            or q_window.shape[2:] != (g.n_q_heads, g.head_dim) or not q_window.is_contiguous():
+        raise ValueError("q_window must be contiguous bf16 [B, W, Hq, d]")
+    if token_score.dtype != torch.float32 or token_score.numel() != g.batch * g.n_q_heads * g.capacity:
+        raise ValueError("token_score must be float32 [B, Hq, C]")
+    if block_score is not None and (block_score.dtype != torch.float32 or block_score.numel() != g.batch * g.nb):
+        raise ValueError("block_score must be float32 [B, NBmax]")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(LIB.kvs_snapkv_scores(ctypes.byref(g.c()), _ptr(q_window), q_window.shape[1], _ptr(cache.k),
+                                 _ptr(cache.k_scale), _ptr(n_prompt), _ptr(token_score), _ptr(block_score),
+                                 pool_kernel, _ptr(workspace), ws_bytes, _stream(stream)),
+           "kvs_snapkv_scores")
 
 
 def update_sidecar(mass_accum, attended, ema, cum, traj, step: int, alpha: float, stream=None):

@@ -314,6 +314,68 @@ int kvs_update_sidecar(float* mass_accum, float* attended, float* ema, float* cu
                                         traj_cap, step, alpha, (hipStream_t)stream));
 }
 
+namespace {
+struct SnapPlan {
+  int tpp, nparts;
+  size_t off_part, off_m, off_l, total;
+};
+// Partitions of the prefill scoring passes: about 768 workgroups of 4 waves.
+SnapPlan snap_plan(const kvs_geom* g, int window) {
+  SnapPlan p{};
+  const int NT = g->capacity / kTileSlots;
+  const int pairs = g->batch * g->n_kv_heads;
+  int pt = (768 + pairs - 1) / pairs;
+  if (pt < 1) pt = 1;
+  p.tpp = (NT + pt - 1) / pt;
+  if (p.tpp < 1) p.tpp = 1;
+  p.nparts = (NT + p.tpp - 1) / p.tpp;
+  const size_t cols = (size_t)g->batch * g->n_kv_heads * window * (g->n_q_heads / g->n_kv_heads);
+  p.off_part = 0;
+  p.off_m = round256(cols * p.nparts * 2 * 4);
+  p.off_l = round256(p.off_m + cols * 4);
+  p.total = round256(p.off_l + cols * 4);
+  return p;
+}
+}  // namespace
+
+int kvs_snapkv_workspace_bytes(const kvs_geom* g, int32_t window, size_t* bytes) {
+  int st = check_geom(g);
+  if (st) return st;
+  if (!bytes || window < 1) return KVS_EINVAL;
+  *bytes = snap_plan(g, window).total;
+  return KVS_OK;
+}
+
+int kvs_snapkv_scores(const kvs_geom* g, const void* q_window, int32_t window, const void* k_cache,
+                      const float* k_scale, const int32_t* n_prompt, float* token_score, float* block_score,
+                      int32_t pool_kernel, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_geom(g);
+  if (st) return st;
+  if (g->ring != 0) return KVS_EINVAL;
+  if (g->kv_dtype == KVS_F32) return KVS_ENOTIMPL;
+  const int G = g->n_q_heads / g->n_kv_heads;
+  if (window < 1 || pool_kernel < 1 || pool_kernel % 2 == 0 || pool_kernel > 33) return KVS_EINVAL;
+  if (window * G > 128) return KVS_ENOTIMPL;
+  const bool fp8 = g->kv_dtype == KVS_FP8_E4M3;
+  if (!q_window || !k_cache || !n_prompt || !token_score || !workspace) return KVS_EINVAL;
+  if (fp8 != (k_scale != nullptr)) return KVS_EINVAL;
+  const void* ptrs[] = {q_window, k_cache, k_scale, n_prompt, token_score, block_score, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KVS_EALIGN;
+  const SnapPlan p = snap_plan(g, window);
+  if (workspace_bytes < p.total) return KVS_EWS;
+  char* ws = (char*)workspace;
+  kvs::SnapArgs a{};
+  a.q = q_window; a.k = k_cache; a.ks = k_scale; a.n_prompt = n_prompt;
+  a.part_ml = (float*)(ws + p.off_part); a.col_m = (float*)(ws + p.off_m); a.col_l = (float*)(ws + p.off_l);
+  a.token_score = token_score; a.block_score = block_score;
+  a.B = g->batch; a.Hq = g->n_q_heads; a.Hkv = g->n_kv_heads; a.G = G; a.C = g->capacity;
+  a.NT = g->capacity / kTileSlots; a.nbmax = g->n_blocks_max; a.W = window; a.tpp = p.tpp;
+  a.nparts = p.nparts; a.pool = pool_kernel;
+  a.scale_log2 = g->softmax_scale * 1.4426950408889634f;
+  return hip_status(kvs::launch_snap(fp8 ? kvs::KV_FP8 : kvs::KV_BF16, g->head_dim, a, (hipStream_t)stream));
+}
+
 int kvs_compact_blocks(const kvs_geom* g, void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                        const int32_t* keep_ids, const int32_t* n_keep, int32_t ids_stride,
                        const kvs_block_table* tables, int32_t n_tables, void* stream) {

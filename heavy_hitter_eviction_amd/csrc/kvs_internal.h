@@ -119,4 +119,19 @@ struct CompactArgs {
 };
 hipError_t launch_compact(const CompactArgs& a, hipStream_t st);
 
+struct SnapArgs {
+  const void* q;             // [B][W][Hq][D] bf16 window queries
+  const void* k;
+  const float* ks;
+  const int32_t* n_prompt;   // [B]
+  float* part_ml;            // [B][Hkv][W*G][nparts][2] workspace
+  float* col_m;              // [B][Hkv][W*G] workspace
+  float* col_l;              // [B][Hkv][W*G] workspace
+  float* token_score;        // [B][Hq][C]
+  float* block_score;        // [B][nbmax] (+=) or NULL
+  int B, Hq, Hkv, G, C, NT, nbmax, W, tpp, nparts, pool;
+  float scale_log2;
+};
+hipError_t launch_snap(int kv, int d, const SnapArgs& a, hipStream_t st);
+
 }  // namespace kvs

@@ -292,6 +292,40 @@ KVS_API int kvs_update_sidecar(float* mass_accum, float* attended, float* ema, f
                        int32_t batch, int32_t n_blocks_max, int32_t traj_cap, int64_t step,
                        float alpha, void* stream);
 
+/*
+ * kvs_snapkv_scores -- prefill scoring from an observation window (Context
+ * views at marginal cost, section 3, Fact 1, SnapKV: one-shot at the end of
+ * prefill, the attention of the last W prompt queries is pooled into one
+ * score per prompt token per head, then max-pooled with an odd kernel --
+ * 7 on the page -- so a kept key drags its neighbours), placed per 16-token
+ * block (Per-Head Attention as a Scoring Signal: score per head, place per
+ * block).
+ *
+ * For sequence b with n = n_prompt[b] prompt tokens in a linear cache and
+ * window query w (0 <= w < W) of head h at position n - W + w, reading keys
+ * j <= its position with softmax weights p_{w,h,j} (logits as in
+ * kvs_decode_attn_scored):
+ *   token_score[b][h][j] = sum_w p_{w,h,j}                       (j < n)
+ *   block_score[b][k]   += sum_h sum_{j in block k, j < n} max_{|i-j| <= R, 0 <= i < n} token_score[b][h][i]
+ * with R = (pool_kernel - 1) / 2, summed in a fixed order. Queries at
+ * negative positions (n < W) read nothing. token_score entries j >= n are not
+ * written; block_score may be NULL.
+ *
+ *   q_window     [B][W][Hq][d] bf16
+ *   k_cache, k_scale  as in kvs_append_kv (bf16 or FP8 caches; F32 gives
+ *                KVS_ENOTIMPL; a ring cache gives KVS_EINVAL)
+ *   n_prompt     [B] int32, 0 <= n <= C
+ *   token_score  [B][Hq][C] float
+ *   block_score  [B][NBmax] float or NULL
+ *   workspace    at least kvs_snapkv_workspace_bytes(geom, W)
+ * W * (Hq / Hkv) <= 128, else KVS_ENOTIMPL; pool_kernel must be odd, at most 33.
+ */
+KVS_API int kvs_snapkv_workspace_bytes(const kvs_geom* geom, int32_t window, size_t* bytes);
+KVS_API int kvs_snapkv_scores(const kvs_geom* geom, const void* q_window, int32_t window,
+                              const void* k_cache, const float* k_scale, const int32_t* n_prompt,
+                              float* token_score, float* block_score, int32_t pool_kernel,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* One per-block table to compact alongside the cache: 4-byte entries (float
  * or int32) laid out [B][rows][NBmax] (rows = 1 for Attended, EMA,
  * Cumulative or a counter; rows = traj_cap for the trajectory ring). */

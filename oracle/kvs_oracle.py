@@ -34,6 +34,9 @@ in the order the source pages state them:
   query is run against the cached keys of a chosen subset of spans, and the
   resulting distribution is read; cached keys and values are reused as they
   are.
+* Context views at marginal cost, section 3, Fact 1: SnapKV pools the
+  attention of the last N prompt queries into one score per prompt token per
+  head, then max-pools it with kernel 7.
 * Context Optimization, "H2O KV Cache Eviction": post-softmax scores are summed
   over all query heads (GQA-aware) and over steps; sinks and recent tokens are
   kept unconditionally and the top scorers among the rest survive.
@@ -469,6 +472,51 @@ def keep_mask_after(keep_ids, i, n_blocks):
 # ---------------------------------------------------------------------------
 # KV memory sizes (Context Optimization, "Memory Budget Calculator")
 # ---------------------------------------------------------------------------
+
+# ---------------------------------------------------------------------------
+# SnapKV-style prefill scoring (Context views at marginal cost, section 3,
+# Fact 1)
+# ---------------------------------------------------------------------------
+
+def snapkv_token_scores(q_window: np.ndarray, K: np.ndarray, n_prompt: int, scale: float) -> np.ndarray:
+    """One-shot at the end of prefill: the attention of the last W prompt
+    queries (the observation window) pooled into one score per prompt token
+    per head, ``score[h][j] = sum_w p_{w,h,j}``. ``q_window`` is
+    ``[W, Hq, d]``, query w at position ``n_prompt - W + w`` reading keys at or
+    before it; ``K`` is ``[Hkv, >= n_prompt, d]``. Returns ``[Hq, n_prompt]``."""
+    q_window = np.asarray(q_window, dtype=np.float64)
+    W, Hq, _ = q_window.shape
+    score = np.zeros((Hq, n_prompt))
+    for w in range(W):
+        pos = n_prompt - W + w
+        if pos < 0:
+            continue
+        Kw = np.asarray(K)[:, :pos + 1]
+        _, p = attend(q_window[w], Kw, Kw, scale)
+        score[:, :pos + 1] += p
+    return score
+
+
+def max_pool_tokens(score: np.ndarray, kernel: int) -> np.ndarray:
+    """SnapKV's max-pooling along tokens (kernel 7 on the page) so that a kept
+    key drags its neighbours: ``out[h][j] = max score[h][j-R .. j+R]`` inside
+    the prompt, R = (kernel - 1) / 2."""
+    if kernel < 1 or kernel % 2 == 0:
+        raise ValueError("the pooling kernel must be odd")
+    score = np.asarray(score, dtype=np.float64)
+    R = kernel // 2
+    n = score.shape[1]
+    return np.stack([[score[h, max(0, j - R):min(n, j + R + 1)].max() for j in range(n)]
+                     for h in range(score.shape[0])]) if n else score.copy()
+
+
+def snapkv_block_scores(pooled: np.ndarray, n_blocks: int) -> np.ndarray:
+    """Placed per block (Per-Head Attention as a Scoring Signal): the pooled
+    per-head token scores summed over heads and over each block's tokens."""
+    pooled = np.asarray(pooled, dtype=np.float64)
+    blocks = np.arange(pooled.shape[1]) // BLOCK_TOKENS
+    return np.bincount(blocks, weights=pooled.sum(axis=0), minlength=n_blocks)
+
 
 # ---------------------------------------------------------------------------
 # Block compaction (Context Optimization, "H2O KV Cache Eviction / How It

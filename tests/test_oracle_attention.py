@@ -291,3 +291,46 @@ def test_max_over_heads_keeps_a_block_one_head_weights():
     _, mass, hm, mx = orc.attend_profiled(q, K, V, np.arange(n), n - 1, 0, None, 0.25, 4)
     assert abs(mx[0] - 1.0) <= 1e-9 and abs(mx[3] - 1.0) <= 1e-9
     assert mass[0] < mass[3] / 5
+
+
+# ---------------------------------------------------------------- SnapKV prefill scoring
+
+def test_snapkv_token_scores_independent_softmax_and_invariants():
+    """Context views at marginal cost, section 3 (SnapKV): window queries'
+    weights summed per (token, head). Pinned by explicit torch softmaxes per
+    query, the per-head total equal to the number of window queries, and the
+    one-query window equal to that query's attention weights."""
+    rng = np.random.default_rng(33)
+    Hq, Hkv, d, n, W = 8, 2, 16, 70, 5
+    K = rng.standard_normal((Hkv, n + 4, d))      # slots past the prompt are never read
+    qw = rng.standard_normal((W, Hq, d))
+    s = orc.snapkv_token_scores(qw, K, n, 0.3)
+    G = Hq // Hkv
+    want = np.zeros((Hq, n))
+    for w in range(W):
+        pos = n - W + w
+        for h in range(Hq):
+            logits = torch.from_numpy(K[h // G, :pos + 1] @ qw[w, h] * 0.3)
+            want[h, :pos + 1] += torch.softmax(logits, 0).numpy()
+    assert np.abs(s - want).max() <= 1e-12
+    assert np.abs(s.sum(axis=1) - W).max() <= 1e-12
+    one = orc.snapkv_token_scores(qw[-1:], K, n, 0.3)
+    _, p = orc.attend(qw[-1], K[:, :n], K[:, :n], 0.3)
+    assert np.abs(one - p).max() <= 1e-12
+    short = orc.snapkv_token_scores(qw, K, 3, 0.3)   # queries at negative positions read nothing
+    assert abs(short.sum(axis=1)[0] - 3) <= 1e-12
+
+
+def test_max_pool_matches_torch_and_drags_neighbours():
+    """SnapKV's max-pool (kernel 7): against torch's max_pool1d with -inf
+    padding; kernel 1 is the identity; one spike spreads to +-3 tokens."""
+    rng = np.random.default_rng(34)
+    sc = rng.random((3, 45))
+    for k in (1, 3, 7):
+        ref = torch.nn.functional.max_pool1d(torch.from_numpy(sc)[None], k, stride=1, padding=k // 2)[0].numpy()
+        assert np.array_equal(orc.max_pool_tokens(sc, k), ref)
+    spike = np.zeros((1, 20))
+    spike[0, 10] = 1.0
+    assert orc.max_pool_tokens(spike, 7)[0].tolist() == [0.0] * 7 + [1.0] * 7 + [0.0] * 6
+    b = orc.snapkv_block_scores(np.ones((2, 40)), 4)
+    assert b.tolist() == [32.0, 32.0, 16.0, 0.0]
