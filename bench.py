@@ -3,9 +3,10 @@
 
 Metric: KV GB/s scanned per scored decode step (and % of HBM peak), plus
 blocks scored per second. One step is the whole hot path for every sequence:
-for each scored layer, append the new position's K/V (FP8 encode), run the
+for each scored layer, append the new position's K/V (FP8 encode) and run the
 scored attention (partial + combine, block masses added over heads and
-layers); then the side-car update and the heavy-hitter block selection.
+layers), the append inside the partial kernel unless --separate-append; then
+the side-car update and the heavy-hitter block selection.
 
 The default workload is the 397B-like shape: batch 16, 32 query / 8 KV heads,
 head dim 128, 15 layers, FP8 E4M3 KV with per-position scales, 32768 cached
@@ -48,6 +49,9 @@ def parse():
                          "compact: evict mode that moves the kept blocks to the front after each "
                          "selection (H2O compaction) and decodes the shorter cache; snapkv: prefill "
                          "scoring from the last 32 prompt queries, max-pooled per block")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="decode/profiled modes: append with its own launch (kvs_append_kv) instead "
+                         "of inside the partial kernel (kvs_append_decode_attn)")
     ap.add_argument("--compact-every", type=int, default=64,
                     help="compact mode: steps between physical compactions (evicted blocks are masked between)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -135,7 +139,8 @@ def run_gpu(args, w):
     if n_steps > w.steps:
         raise SystemExit(f"warmup + steps must be <= {w.steps} for this workload")
     t0 = time.time()
-    dec = ScoredDecoder(w, evict=args.evict)
+    fused = not args.separate_append and args.mode == "decode"
+    dec = ScoredDecoder(w, evict=args.evict, fused=fused)
     prefill(dec, w, args.seed)
     Q, K, V = step_inputs(w, args.seed, n_steps, dec.n_layers)
     cur = [torch.full((w.batch,), w.context + t, dtype=torch.int32, device="cuda") for t in range(n_steps)]
@@ -161,9 +166,20 @@ def run_gpu(args, w):
             sev[t - args.warmup].record()
         keep = dec.keep if (args.evict and not w.window) else None
         for layer in range(L):
-            dec.caches[layer].append(K[layer][t], V[layer][t], dec.row_seq, cur[t])
+            if not fused:
+                dec.caches[layer].append(K[layer][t], V[layer][t], dec.row_seq, cur[t])
             if timed:
                 ev[t - args.warmup][layer][0].record()
+            if fused:
+                # the append runs inside the partial kernel the events bracket
+                api.append_decode_attn(dec.caches[layer], K[layer][t], V[layer][t], Q[layer][t], cur[t],
+                                       dec.out[layer], dec.workspace, mass_accum=dec.mass, keep_mask=keep,
+                                       phase="partial")
+                if timed:
+                    ev[t - args.warmup][layer][1].record()
+                api.decode_attn_scored(dec.caches[layer], Q[layer][t], cur[t], dec.out[layer], dec.workspace,
+                                       mass_accum=dec.mass, keep_mask=keep, phase="combine")
+                continue
             if profiled:
                 # one call, both phases: the events cover partial + combine
                 api.decode_attn_profiled(dec.caches[layer], Q[layer][t], cur[t], dec.out[layer], dec.workspace,
@@ -502,6 +518,7 @@ def main():
             "layers": w.n_layers, "context": w.context, "kv_dtype": w.kv_dtype, "block_tokens": 16,
             "window": w.window, "ring": w.ring, "budget_blocks": w.budget_blocks,
             "recent_tokens": w.recent_tokens, "mode": "evict" if args.evict else "score-only",
+            "append": "separate launch" if (args.separate_append or args.mode != "decode") else "in the partial kernel",
             **({"outputs": "per-head block masses [B][Hq][NBmax] and max over heads and layers"}
                if args.mode == "profiled" else {}),
         },

@@ -26,7 +26,8 @@ TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8
 
 EXPORTED = (
     "kvs_cache_bytes", "kvs_encode_fp8", "kvs_append_kv", "kvs_decode_workspace_bytes",
-    "kvs_decode_attn_scored", "kvs_decode_partial", "kvs_decode_combine", "kvs_decode_attn_profiled",
+    "kvs_decode_attn_scored", "kvs_decode_partial", "kvs_decode_combine", "kvs_append_decode_attn",
+    "kvs_append_decode_partial", "kvs_decode_attn_profiled",
     "kvs_reattend_blocks",
     "kvs_update_sidecar", "kvs_update_counters", "kvs_filter_blocks", "kvs_select_blocks",
     "kvs_compact_blocks", "kvs_snapkv_workspace_bytes", "kvs_snapkv_scores", "kvs_status_str",
@@ -68,6 +69,8 @@ def _load():
         "kvs_decode_attn_scored": [G, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "kvs_decode_partial": [G, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "kvs_decode_combine": [G, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "kvs_append_decode_attn": [G, P, P, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "kvs_append_decode_partial": [G, P, P, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "kvs_reattend_blocks": [G, P, P, P, P, P, P, P, P, I32, P, P, P, SZ, P],
         "kvs_decode_attn_profiled": [G, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "kvs_update_sidecar": [P, P, P, P, P, I32, I32, I32, I64, F, P],
@@ -254,6 +257,44 @@ def decode_attn_scored(cache: KVCache, q: torch.Tensor, cur_pos: torch.Tensor, o
               _ptr(cache.v_scale), _ptr(cache.pos_of_slot), _ptr(cur_pos), _ptr(keep_mask), _ptr(out),
               _ptr(mass_accum), _ptr(workspace), ws_bytes, _stream(stream)),
            f"kvs_decode ({phase})")
+    return out
+
+
+def append_decode_attn(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                       cur_pos: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
+                       mass_accum: torch.Tensor | None = None, keep_mask: torch.Tensor | None = None,
+                       stream=None, phase: str = "both"):
+    """kvs_append_decode_attn: write row b of ``k_new`` / ``v_new`` ([B, Hkv*d],
+    float32 or bfloat16) at position ``cur_pos[b]`` and run the scored decode
+    step over the cache that now holds it, in one pass. ``phase`` "partial"
+    runs kvs_append_decode_partial only (append + partial phase); follow it
+    with ``decode_attn_scored(..., phase="combine")``."""
+    g = cache.geom
+    _device_check(k_new, v_new, q, cur_pos, out, workspace, mass_accum, keep_mask)
+    dt = {torch.float32: KVS_F32, torch.bfloat16: KVS_BF16}.get(k_new.dtype)
+    if dt is None or v_new.dtype != k_new.dtype:
+        raise TypeError("new rows must be float32 or bfloat16, K and V alike")
+    w = g.n_kv_heads * g.head_dim
+    if k_new.shape != (g.batch, w) or v_new.shape != (g.batch, w):
+        raise ValueError("new rows must be [B, Hkv*d]")
+    qdt = TORCH_DTYPES[g.q_dtype]
+    if q.dtype != qdt or out.dtype != qdt:
+        raise TypeError("q and out must have the geometry's q dtype")
+    if q.shape != (g.batch, g.n_q_heads, g.head_dim) or out.shape != q.shape:
+        raise ValueError("q/out must be [B, Hq, d]")
+    if cur_pos.dtype != torch.int32 or cur_pos.numel() != g.batch:
+        raise ValueError("cur_pos must be int32 [B]")
+    if mass_accum is not None and (mass_accum.dtype != torch.float32 or mass_accum.numel() != g.batch * g.nb):
+        raise ValueError("mass_accum must be float32 [B, NBmax]")
+    if keep_mask is not None and (keep_mask.dtype != torch.int32 or keep_mask.numel() != g.batch * g.words):
+        raise ValueError("keep_mask must be int32 (bit words) [B, W]")
+    fn = {"both": LIB.kvs_append_decode_attn, "partial": LIB.kvs_append_decode_partial}[phase]
+    ws_bytes = workspace.numel() * workspace.element_size()
+    gc = g.c()
+    _check(fn(ctypes.byref(gc), _ptr(k_new), _ptr(v_new), dt, _ptr(q), _ptr(cache.k), _ptr(cache.v),
+              _ptr(cache.k_scale), _ptr(cache.v_scale), _ptr(cache.pos_of_slot), _ptr(cur_pos),
+              _ptr(keep_mask), _ptr(out), _ptr(mass_accum), _ptr(workspace), ws_bytes, _stream(stream)),
+           f"kvs_append_decode ({phase})")
     return out
 
 

@@ -277,6 +277,51 @@ int kvs_decode_attn_profiled(const kvs_geom* g, const void* q, const void* k_cac
   return hip_status(kvs::launch_combine(c, g->ring != 0, g->q_dtype == KVS_BF16, s));
 }
 
+}  // extern "C"
+
+namespace {
+
+// The fused-append arguments (after decode_setup has checked the rest).
+int append_args(const kvs_geom* g, const void* k_new, const void* v_new, int32_t src_dtype,
+                kvs::PartialArgs* a) {
+  if (src_dtype != KVS_F32 && src_dtype != KVS_BF16) return KVS_EDTYPE;
+  if (g->kv_dtype != KVS_FP8_E4M3 && src_dtype != g->kv_dtype) return KVS_EDTYPE;
+  if (!k_new || !v_new) return KVS_EINVAL;
+  if (!aligned16(k_new) || !aligned16(v_new)) return KVS_EALIGN;
+  a->app_k = k_new;
+  a->app_v = v_new;
+  a->app_bf16 = src_dtype == KVS_BF16;
+  return KVS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+#define KVS_APPEND_DECODE_ARGS                                                                   \
+  const kvs_geom *g, const void *k_new, const void *v_new, int32_t src_dtype, const void *q,     \
+      void *k_cache, void *v_cache, float *k_scale, float *v_scale, int32_t *pos_of_slot,         \
+      const int32_t *cur_pos, const uint32_t *keep_mask, void *out, float *mass_accum,            \
+      void *workspace, size_t workspace_bytes, void *stream
+#define KVS_APPEND_DECODE_SETUP                                                                  \
+  KVS_DECODE_SETUP                                                                               \
+  st = append_args(g, k_new, v_new, src_dtype, &a);                                              \
+  if (st) return st;
+
+int kvs_append_decode_partial(KVS_APPEND_DECODE_ARGS) {
+  KVS_APPEND_DECODE_SETUP
+  return hip_status(kvs::launch_partial(kv, g->head_dim, a, mass_accum != nullptr, g->ring != 0,
+                                        p.lds_partial, s));
+}
+
+int kvs_append_decode_attn(KVS_APPEND_DECODE_ARGS) {
+  KVS_APPEND_DECODE_SETUP
+  hipError_t e = kvs::launch_partial(kv, g->head_dim, a, mass_accum != nullptr, g->ring != 0,
+                                     p.lds_partial, s);
+  if (e != hipSuccess) return KVS_EHIP;
+  return hip_status(kvs::launch_combine(c, g->ring != 0, g->q_dtype == KVS_BF16, s));
+}
+
 int kvs_reattend_blocks(const kvs_geom* g, const void* q, const void* k_cache, const void* v_cache,
                         const float* k_scale, const float* v_scale, const int32_t* cur_pos,
                         const int32_t* block_ids, const int32_t* n_ids, int32_t ids_stride, void* out,

@@ -10,11 +10,6 @@
 
 namespace kvs {
 
-__device__ __forceinline__ float load_src(const void* p, size_t i, int src_bf16) {
-  if (src_bf16) return bf16_lo((uint32_t)((const uint16_t*)p)[i]);
-  return ((const float*)p)[i];
-}
-
 // Workgroup max of non-negative values (256 threads).
 __device__ __forceinline__ float block_max256(float v, float* red) {
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
@@ -23,10 +18,6 @@ __device__ __forceinline__ float block_max256(float v, float* red) {
   const float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   __syncthreads();
   return r;
-}
-
-__device__ __forceinline__ uint32_t encode_with_scale(float x, float s) {
-  return s > 0.0f ? e4m3_encode(__fdiv_rn(x, s)) : 0u;
 }
 
 // One workgroup per row.

@@ -141,6 +141,15 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
     t1 = min(gte, t0 + tpe);
   }
 
+  // Fused append: the workgroup whose tiles hold the new position's slot
+  // writes this KV head's part of the row there before anyone reads that tile.
+  int app_slot = -1;
+  if (a.app_k != nullptr && i_cur >= 0 && (RING || i_cur < a.C)) {
+    const int sl = RING ? i_cur % a.C : i_cur;
+    if (sl / kTile >= t0 && sl / kTile < t1) app_slot = sl;
+  }
+  const int app_tile = app_slot >= 0 ? app_slot / kTile : -1;
+
   // LDS carve-up (16-byte aligned parts first): per-wave side data (FP8
   // scales, ring positions of the claimed tiles), the wave merge area, the
   // kept-tile count and the claim counter, then per-tile block sums of the
@@ -151,7 +160,8 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   float* ow = side_area + NW * 256;                     // [oslots][G][D]
   float* mw = ow + a.oslots * G * D;                    // [NW][G]
   float* lw = mw + NW * G;                              // [NW][G]
-  int* misc = (int*)(lw + NW * G);                      // [4]: kept-tile count, claim counter
+  int* misc = (int*)(lw + NW * G);                      // [4]: kept-tile count, claim counter,
+                                                        // append-done flag, list entry of the appended tile
   float* e_rec = (float*)(misc + 4);                    // [G][tpp][NSUB]
   float* m_rec = e_rec + a.tpp * NSUB * G;              // [G][tpp]
   int* tlist = (int*)(m_rec + a.tpp * G);               // [tpp]
@@ -159,7 +169,11 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
     for (int x = threadIdx.x; x < a.tpp * NSUB * G; x += NTH) e_rec[x] = 0.0f;
     for (int x = threadIdx.x; x < a.tpp * G; x += NTH) m_rec[x] = -__builtin_inff();
   }
-  if (threadIdx.x == 0) misc[1] = 0;
+  if (threadIdx.x == 0) {
+    misc[1] = 0;
+    misc[2] = 0;
+    misc[3] = -1;
+  }
 
   // Tiles that can hold a readable key.
   const int tb = t0, te = t1;
@@ -193,7 +207,11 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
         else kept = t >= a.nbmax || ((keep_b[t >> 5] >> (t & 31)) & 1u);
       }
       const uint64_t m = __ballot(kept);
-      if (kept) tlist[n + __popcll(m & ((1ull << lane) - 1ull))] = t;
+      if (kept) {
+        const int e = n + __popcll(m & ((1ull << lane) - 1ull));
+        tlist[e] = t;
+        if (t == app_tile) misc[3] = e;
+      }
       n += __popcll(m);
     }
     if (lane == 0) misc[0] = n;
@@ -201,6 +219,9 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   __syncthreads();
   const int n_items = use_list ? misc[0] : te - tb;
   const int n_batches = (n_items + BATCH - 1) / BATCH;
+  // batch holding the appended tile (-1: none here, or not read)
+  const int app_entry = app_tile < 0 ? -1 : use_list ? misc[3] : app_tile - tb;
+  const int app_batch = __builtin_amdgcn_readfirstlane(app_entry < 0 ? -1 : app_entry / BATCH);
   auto tile_of = [&](int e) -> int {  // tile of list entry e < n_items (wave-uniform e)
     if (use_list) return __builtin_amdgcn_readfirstlane(tlist[e]);
     return tb + e;
@@ -219,6 +240,11 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
       v = wave + NW * n_claimed;
     }
     ++n_claimed;
+    // the batch with the appended tile is read only once the row is written
+    if (v == app_batch) {
+      while (__hip_atomic_load(&misc[2], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
+        __builtin_amdgcn_s_sleep(1);
+    }
     return v;
   };
 
@@ -505,6 +531,90 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
     const int e = BATCH * bi + i;
     return e < n_items ? (uint32_t)tile_of(e) * tile_bytes : oob;
   };
+  // ---- fused append (last wave, before its first claim) ----
+  // Same encoding as kvs_append_rows: the FP8 scale covers every KV head of
+  // the position, so each workgroup of the sequence derives it from the whole
+  // row (identical values); this workgroup writes its own head's codes.
+  auto append_row = [&]() {
+    const int n = a.Hkv * D;
+    const size_t rb = (size_t)b * n;
+    const int sbf = a.app_bf16;
+    float sk = 0.0f, sv = 0.0f;
+    if constexpr (KV == KV_FP8) {
+      float mk = 0.0f, mv = 0.0f;
+      for (int i = 8 * lane; i < n; i += 8 * 64) {  // 8 values per lane and load (n % 8 == 0)
+        float xk[8], xv[8];
+        if (sbf) {
+          const u32x4 wk = *(const u32x4*)((const uint16_t*)a.app_k + rb + i);
+          const u32x4 wv = *(const u32x4*)((const uint16_t*)a.app_v + rb + i);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            xk[2 * e] = bf16_lo(wk[e]);
+            xk[2 * e + 1] = bf16_hi(wk[e]);
+            xv[2 * e] = bf16_lo(wv[e]);
+            xv[2 * e + 1] = bf16_hi(wv[e]);
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const f32x4 fk = *(const f32x4*)((const float*)a.app_k + rb + i + 4 * c);
+            const f32x4 fv = *(const f32x4*)((const float*)a.app_v + rb + i + 4 * c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              xk[4 * c + e] = fk[e];
+              xv[4 * c + e] = fv[e];
+            }
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          mk = fmaxf(mk, fabsf(xk[e]));
+          mv = fmaxf(mv, fabsf(xv[e]));
+        }
+      }
+      for (int off = 32; off > 0; off >>= 1) {
+        mk = fmaxf(mk, __shfl_xor(mk, off, 64));
+        mv = fmaxf(mv, __shfl_xor(mv, off, 64));
+      }
+      sk = fp8_scale_of(mk);
+      sv = fp8_scale_of(mv);
+    }
+    const int t = app_slot & (kTile - 1);
+    const size_t base = (((size_t)b * a.Hkv + g) * (size_t)(a.C / kTile) + app_tile) * tile_bytes;
+    char* kc = (char*)const_cast<void*>(a.k) + base;
+    char* vc = (char*)const_cast<void*>(a.v) + base;
+    for (int x = lane; x < D; x += 64) {
+      const size_t i = rb + (size_t)g * D + x;
+      char* kp = kc + k_tile_offset(t, x, eb);
+      char* vp = vc + v_tile_offset(t, x, D, eb);
+      if constexpr (KV == KV_FP8) {
+        *(uint8_t*)kp = (uint8_t)encode_with_scale(load_src(a.app_k, i, sbf), sk);
+        *(uint8_t*)vp = (uint8_t)encode_with_scale(load_src(a.app_v, i, sbf), sv);
+      } else if constexpr (KV == KV_BF16) {
+        *(uint16_t*)kp = ((const uint16_t*)a.app_k)[i];
+        *(uint16_t*)vp = ((const uint16_t*)a.app_v)[i];
+      } else {
+        *(float*)kp = ((const float*)a.app_k)[i];
+        *(float*)vp = ((const float*)a.app_v)[i];
+      }
+    }
+    if (lane == 0) {
+      if constexpr (KV == KV_FP8) {
+        const_cast<float*>(a.ks)[(size_t)b * a.C + app_slot] = sk;
+        const_cast<float*>(a.vs)[(size_t)b * a.C + app_slot] = sv;
+      }
+      if constexpr (RING) const_cast<int32_t*>(a.pos_of_slot)[(size_t)b * a.C + app_slot] = i_cur;
+    }
+  };
+  if (app_slot >= 0 && wave == NW - 1) {
+    append_row();
+    // release: the wave's stores complete (vmcnt 0) before the flag is seen;
+    // the workgroup-scope release alone relies on the CU's in-order memory
+    // pipeline, the explicit wait does not
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (lane == 0) __hip_atomic_store(&misc[2], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+
   int cur = claim();
   if (cur < n_batches) {
     TileRegs<KV, D> buf[NBUF];

@@ -84,6 +84,18 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
 // absmax / 240, correctly rounded (the pages' per-position scale).
 __device__ __forceinline__ float fp8_scale_of(float absmax) { return __fdiv_rn(absmax, 240.0f); }
 
+// Element i of a row of float32 or (src_bf16) bf16 values, widened exactly.
+__device__ __forceinline__ float load_src(const void* p, size_t i, int src_bf16) {
+  if (src_bf16) return bf16_lo((uint32_t)((const uint16_t*)p)[i]);
+  return ((const float*)p)[i];
+}
+
+// E4M3 code of x / s (the quotient rounded once); a zero scale (all-zero row)
+// gives code 0.
+__device__ __forceinline__ uint32_t encode_with_scale(float x, float s) {
+  return s > 0.0f ? e4m3_encode(__fdiv_rn(x, s)) : 0u;
+}
+
 // Four FP8 codes (one dword) to four bf16 values, exact (E4M3 is a subset of bf16).
 __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
   bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);

@@ -32,6 +32,13 @@ struct PartialArgs {
   int dyn;     // 1: waves claim tiles dynamically; 0: fixed round-robin order
   int oslots;  // LDS output slots of the wave merge: kPartialWaves or kPartialWaves / 2
   float scale_log2;
+  // Fused append: row b of app_k / app_v ([B][Hkv*D], bf16 if app_bf16, else
+  // f32) is written at position cur_pos[b] of the cache (k, v, ks, vs and
+  // pos_of_slot are then written too) before the tile holding it is read.
+  // NULL app_k: no append.
+  const void* app_k;
+  const void* app_v;
+  int app_bf16;
 };
 
 struct CombineArgs {

@@ -2,7 +2,9 @@
 
 For every layer: append the new position's K/V (FP8-encoding when the cache
 is FP8), then the scored attention (partial + combine) that adds this layer's
-block masses into ``mass``. After the last layer the side-car closes the turn,
+block masses into ``mass``; by default the append runs inside the attention's
+partial kernel (kvs_append_decode_attn), ``fused=False`` makes it a launch of
+its own. After the last layer the side-car closes the turn,
 and the heavy-hitter selection produces the keep mask. In evict mode that
 mask feeds the next step's attention, so dropped blocks are never read again
 (Context Optimization, "H2O KV Cache Eviction"); in score-only mode the full
@@ -30,7 +32,7 @@ def geom_of(w: Workload) -> api.CacheGeom:
 
 class ScoredDecoder:
     def __init__(self, w: Workload, evict: bool = False, device="cuda", layers: int | None = None,
-                 compact: bool = False, compact_every: int = 1):
+                 compact: bool = False, compact_every: int = 1, fused: bool = True):
         if compact and (w.ring or w.window or not w.select):
             raise ValueError("compaction needs a linear cache with selection and no window")
         if compact_every < 1:
@@ -39,6 +41,7 @@ class ScoredDecoder:
         self.evict = evict
         self.compact = compact
         self.compact_every = compact_every
+        self.fused = fused
         self.device = torch.device(device)
         self.geom = geom_of(w)
         self.n_layers = w.n_layers if layers is None else layers
@@ -79,9 +82,22 @@ class ScoredDecoder:
         ``v_layers[l]`` are the new position's rows [B, Hkv*d]; ``cur_pos`` is
         the int32 [B] absolute position being written and read."""
         for l in range(self.n_layers):
-            self.caches[l].append(k_layers[l], v_layers[l], self.row_seq, cur_pos)
-            self.attend_layer(l, q_layers[l], cur_pos)
+            self.append_attend_layer(l, q_layers[l], k_layers[l], v_layers[l], cur_pos)
         self.close_turn(cur_pos)
+
+    def append_attend_layer(self, layer: int, q, k_rows, v_rows, cur_pos: torch.Tensor,
+                            keep: torch.Tensor | None = None, use_own_keep: bool = True):
+        """Append row b of ``k_rows`` / ``v_rows`` at ``cur_pos[b]``, then the
+        scored attention of ``layer`` (one launch pair when fused)."""
+        if use_own_keep:
+            keep = self.keep if (self.evict and not self.w.window) else None
+        if self.fused:
+            api.append_decode_attn(self.caches[layer], k_rows, v_rows, q, cur_pos, self.out[layer],
+                                   self.workspace, mass_accum=self.mass, keep_mask=keep)
+        else:
+            self.caches[layer].append(k_rows, v_rows, self.row_seq, cur_pos)
+            api.decode_attn_scored(self.caches[layer], q, cur_pos, self.out[layer], self.workspace,
+                                   mass_accum=self.mass, keep_mask=keep)
 
     def step_compact(self, q_layers, k_layers, v_layers, compact_now: bool | None = None):
         """One decode step in compact mode: evict mode at each sequence's
@@ -91,9 +107,8 @@ class ScoredDecoder:
         dropped blocks' slots (H2O step 4)."""
         cur = self.pos
         for l in range(self.n_layers):
-            self.caches[l].append(k_layers[l], v_layers[l], self.row_seq, cur)
-            api.decode_attn_scored(self.caches[l], q_layers[l], cur, self.out[l], self.workspace,
-                                   mass_accum=self.mass, keep_mask=self.keep)
+            self.append_attend_layer(l, q_layers[l], k_layers[l], v_layers[l], cur, keep=self.keep,
+                                     use_own_keep=False)
         api.update_sidecar(self.mass, self.attended, self.ema, self.cum, self.traj,
                            self.step_index, self.w.alpha)
         api.select_blocks(self.cum, cur, self.w.budget_blocks, self.w.recent_tokens, self.w.sink_tokens,

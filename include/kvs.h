@@ -223,6 +223,41 @@ KVS_API int kvs_decode_combine(const kvs_geom* geom, const void* q, const void* 
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kvs_append_decode_attn -- kvs_append_kv of the step's new rows followed by
+ * kvs_decode_attn_scored, in one pass over the cache (the write-then-attend
+ * order of a decode step: Context Optimization, "FP8 KV Cache / How It Works"
+ * for the encoding, "Context views at marginal cost" for the scored read).
+ *
+ * Row b of k_new / v_new ([B][Hkv*d] of src_dtype, KVS_F32 or KVS_BF16; for a
+ * BF16 or F32 cache src_dtype must equal the cache type) goes to position
+ * cur_pos[b] of sequence b exactly as kvs_append_kv with row_seq[b] = b and
+ * row_pos[b] = cur_pos[b] writes it (same codes, scales and pos_of_slot
+ * entry; skipped when cur_pos[b] < 0, or >= C for a linear cache), and the
+ * attention then reads it: the results equal those two calls on one stream
+ * (bit for bit in deterministic mode). The workgroup holding the new slot
+ * writes it before reading that tile, so the separate append launch and its
+ * pass over the row go away. The cache buffers are written, hence not const.
+ * Other arguments, checks and errors as kvs_decode_attn_scored; null or
+ * misaligned k_new / v_new give KVS_EINVAL / KVS_EALIGN, a bad src_dtype
+ * KVS_EDTYPE.
+ *
+ * kvs_append_decode_partial is its partial phase (append + partial); follow it
+ * with kvs_decode_combine, with the same arguments, on the same stream.
+ */
+KVS_API int kvs_append_decode_attn(const kvs_geom* geom, const void* k_new, const void* v_new,
+                                   int32_t src_dtype, const void* q, void* k_cache, void* v_cache,
+                                   float* k_scale, float* v_scale, int32_t* pos_of_slot,
+                                   const int32_t* cur_pos, const uint32_t* keep_mask, void* out,
+                                   float* mass_accum, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+KVS_API int kvs_append_decode_partial(const kvs_geom* geom, const void* k_new, const void* v_new,
+                                      int32_t src_dtype, const void* q, void* k_cache, void* v_cache,
+                                      float* k_scale, float* v_scale, int32_t* pos_of_slot,
+                                      const int32_t* cur_pos, const uint32_t* keep_mask, void* out,
+                                      float* mass_accum, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+/*
  * kvs_decode_attn_profiled -- kvs_decode_attn_scored with the per-axis views
  * of the block masses (Context views at marginal cost, section 4: the
  * observer's layer and head axes kept as a reduced per-span profile, not the

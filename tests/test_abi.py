@@ -177,3 +177,27 @@ def test_reattend_and_profiled_reject_bad_arguments():
     assert app(g) == api.KVS_EINVAL                     # FP8 cache without scale buffers
     assert app(_geom(api), src=0) == api.KVS_EDTYPE     # f32 rows into a bf16 cache
     assert app(g, src=3, ks=vp(0x7000), vs=vp(0x8000)) == api.KVS_EDTYPE
+
+
+def test_fused_append_decode_rejects_bad_arguments():
+    """kvs_append_decode_attn / _partial: the decode checks, then the new
+    rows' pointers, alignment and dtype; every call below fails a check."""
+    api = _lib()
+    L = api.LIB
+    vp = ctypes.c_void_p
+
+    def fz(g, kn=0x8000, vn=0x9000, src=None, ws=1 << 20, fn=L.kvs_append_decode_attn):
+        return fn(ctypes.byref(g), vp(kn) if kn else None, vp(vn) if vn else None,
+                  api.KVS_BF16 if src is None else src, vp(0x1000), vp(0x2000), vp(0x3000), None, None, None,
+                  vp(0x4000), None, vp(0x5000), vp(0x6000), vp(0x7000), ws, None)
+
+    g = _geom(api)                                        # bf16 cache
+    assert fz(_geom(api, n_q_heads=15)) == api.KVS_EINVAL  # geometry first
+    assert fz(g, ws=16) == api.KVS_EWS
+    assert fz(g, kn=0) == api.KVS_EINVAL
+    assert fz(g, vn=0) == api.KVS_EINVAL
+    assert fz(g, vn=0x9004) == api.KVS_EALIGN
+    assert fz(g, src=3) == api.KVS_EDTYPE
+    assert fz(g, src=api.KVS_F32) == api.KVS_EDTYPE        # f32 rows into a bf16 cache
+    assert fz(g, kn=0, fn=L.kvs_append_decode_partial) == api.KVS_EINVAL
+    assert fz(_geom(api, kv_dtype=api.KVS_FP8_E4M3)) == api.KVS_EINVAL  # FP8 cache without scales

@@ -1,0 +1,168 @@
+"""The fused append + scored decode (kvs_append_decode_attn) against the two
+calls it replaces, kvs_append_kv then kvs_decode_attn_scored, in deterministic
+mode: outputs, accumulated block masses and every cache buffer must agree bit
+for bit after each step, across tile boundaries, ring wraps, windows, keep
+masks, both source dtypes and the split (partial, combine) form. The two-call
+path is checked against the float64 oracle by the other parity tests; one
+case here also checks the fused path against the oracle directly."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from heavy_hitter_eviction_amd import synth
+from oracle import kvs_oracle as orc
+from tests import gpu_support as gs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def api():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from heavy_hitter_eviction_amd import api as _api
+    return _api
+
+
+def _rows(shape, key):
+    return synth.normal(shape, key, "cpu").numpy()
+
+
+FUSED_CASES = [
+    # kv,   d,  Hq, Hkv, C,   B, window, ring,  src,   keep
+    ("fp8", 128, 32, 8, 2064, 2, 0, False, "f32", False),
+    ("fp8", 128, 16, 4, 400, 2, 37, False, "bf16", False),
+    ("fp8", 128, 16, 4, 640, 2, 0, False, "bf16", True),
+    ("bf16", 128, 16, 4, 1040, 3, 0, False, "bf16", False),
+    ("bf16", 64, 32, 2, 512, 2, 0, False, "bf16", True),
+    ("f32", 16, 4, 2, 80, 1, 0, False, "f32", False),
+    ("fp8", 128, 16, 4, 64, 2, 64, True, "f32", False),
+    ("bf16", 64, 8, 2, 80, 2, 50, True, "bf16", False),
+    ("f32", 16, 4, 2, 32, 2, 0, True, "f32", False),
+]
+STEPS = 24
+
+
+def _setup(api, case, deterministic, seed=23):
+    kv, d, Hq, Hkv, C, B, window, ring, src, use_keep = case
+    n_total = C + 40 if ring else C
+    nb = (n_total + 15) // 16 if ring else 0
+    geom = api.CacheGeom(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, capacity=C, window=window,
+                         ring=ring, n_blocks_max=nb, kv_dtype=kv, q_dtype="f32" if kv == "f32" else "bf16",
+                         deterministic=deterministic)
+    w = Hkv * d
+    K = _rows((B, n_total, w), (seed, 1))
+    V = _rows((B, n_total, w), (seed, 2))
+    src_dt = torch.float32 if src == "f32" else torch.bfloat16
+    # per-sequence first decode position: linear caches end inside the
+    # capacity, rings wrap during the steps
+    start = [(C - 12 - 3 * b) if ring else (C - STEPS - 6 - 7 * b) for b in range(B)]
+    keep = None
+    alive = None
+    if use_keep:
+        rng = np.random.default_rng(seed)
+        alive = rng.random((B, geom.nb)) < 0.5
+        for b in range(B):
+            alive[b, start[b] // 16:(start[b] + STEPS) // 16 + 1] = True
+        words = np.zeros((B, geom.words), dtype=np.int64)
+        for b in range(B):
+            for blk in np.flatnonzero(alive[b]):
+                words[b, blk >> 5] |= 1 << (blk & 31)
+        keep = gs.to_dev(words.astype(np.uint32).view(np.int32))
+    return geom, K, V, src_dt, start, keep, alive
+
+
+def _prefill(api, geom, K, V, src_dt, start):
+    cache = api.KVCache(geom)
+    cache.k.zero_()          # slots never written compare equal too
+    cache.v.zero_()
+    for b, n in enumerate(start):
+        seqs = torch.full((n,), b, dtype=torch.int32, device="cuda")
+        pos = torch.arange(n, dtype=torch.int32, device="cuda")
+        cache.append(gs.to_dev(K[b, :n]).to(src_dt), gs.to_dev(V[b, :n]).to(src_dt), seqs, pos)
+    return cache
+
+
+def _cache_buffers(cache):
+    return [t for t in (cache.k, cache.v, cache.k_scale, cache.v_scale, cache.pos_of_slot) if t is not None]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_fused_append_decode_equals_append_then_decode(api, case):
+    kv, d, Hq, Hkv, C, B, window, ring, src, use_keep = case
+    geom, K, V, src_dt, start, keep, _ = _setup(api, case, deterministic=True)
+    ref_cache = _prefill(api, geom, K, V, src_dt, start)
+    fz_cache = _prefill(api, geom, K, V, src_dt, start)
+    qdt = torch.float32 if kv == "f32" else torch.bfloat16
+    ws_bytes = api.decode_workspace_bytes(geom)
+    ws_r = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    ws_f = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    mass_r = torch.zeros((B, geom.nb), dtype=torch.float32, device="cuda")
+    mass_f = torch.zeros((B, geom.nb), dtype=torch.float32, device="cuda")
+    seqs = torch.arange(B, dtype=torch.int32, device="cuda")
+    for t in range(STEPS):
+        pos = np.array([s + t for s in start], dtype=np.int32)
+        cur = gs.to_dev(pos)
+        krow = torch.from_numpy(np.stack([K[b, pos[b]] for b in range(B)])).to(src_dt).cuda()
+        vrow = torch.from_numpy(np.stack([V[b, pos[b]] for b in range(B)])).to(src_dt).cuda()
+        q = torch.from_numpy(_rows((B, Hq, d), (23, 3, t))).to(qdt).cuda()
+        scored = t % 5 != 3                  # some unscored steps too
+        out_r = torch.empty_like(q)
+        out_f = torch.empty_like(q)
+        ref_cache.append(krow, vrow, seqs, cur)
+        api.decode_attn_scored(ref_cache, q, cur, out_r, ws_r, mass_accum=mass_r if scored else None,
+                               keep_mask=keep)
+        if t % 2 == 0:
+            api.append_decode_attn(fz_cache, krow, vrow, q, cur, out_f, ws_f,
+                                   mass_accum=mass_f if scored else None, keep_mask=keep)
+        else:
+            api.append_decode_attn(fz_cache, krow, vrow, q, cur, out_f, ws_f,
+                                   mass_accum=mass_f if scored else None, keep_mask=keep, phase="partial")
+            api.decode_attn_scored(fz_cache, q, cur, out_f, ws_f, mass_accum=mass_f if scored else None,
+                                   keep_mask=keep, phase="combine")
+        torch.cuda.synchronize()
+        assert torch.equal(out_r.view(torch.int16 if kv != "f32" else torch.int32),
+                           out_f.view(torch.int16 if kv != "f32" else torch.int32)), f"step {t}: out"
+        assert torch.equal(mass_r, mass_f), f"step {t}: mass"
+        for a, b in zip(_cache_buffers(ref_cache), _cache_buffers(fz_cache)):
+            assert torch.equal(a, b), f"step {t}: cache buffer"
+
+
+@pytest.mark.parametrize("case", [FUSED_CASES[0], FUSED_CASES[2], FUSED_CASES[6]],
+                         ids=lambda c: "-".join(map(str, c)))
+def test_fused_append_decode_dynamic_mode_matches_oracle(api, case):
+    """Dynamic tile sharing, fused append, checked against the float64
+    oracle on the last step (keys dequantised by the oracle's own encoder)."""
+    kv, d, Hq, Hkv, C, B, window, ring, src, use_keep = case
+    geom, K, V, src_dt, start, keep, alive = _setup(api, case, deterministic=False, seed=31)
+    cache = _prefill(api, geom, K, V, src_dt, start)
+    qdt = torch.float32 if kv == "f32" else torch.bfloat16
+    ws = torch.empty(api.decode_workspace_bytes(geom), dtype=torch.uint8, device="cuda")
+    scale = orc.softmax_scale(d)
+    n_steps = 6
+    for t in range(n_steps):
+        pos = np.array([s + t for s in start], dtype=np.int32)
+        krow = torch.from_numpy(np.stack([K[b, pos[b]] for b in range(B)])).to(src_dt).cuda()
+        vrow = torch.from_numpy(np.stack([V[b, pos[b]] for b in range(B)])).to(src_dt).cuda()
+        q = torch.from_numpy(_rows((B, Hq, d), (31, 3, t))).to(qdt)
+        out = torch.empty_like(q).cuda()
+        mass = torch.zeros((B, geom.nb), dtype=torch.float32, device="cuda")
+        api.append_decode_attn(cache, krow, vrow, q.cuda(), gs.to_dev(pos), out, ws, mass_accum=mass,
+                               keep_mask=keep)
+    torch.cuda.synchronize()
+    # rows as the cache holds them: the source dtype's values, then the cache's encoding
+    Ksrc = torch.from_numpy(K).to(src_dt).float().numpy()
+    Vsrc = torch.from_numpy(V).to(src_dt).float().numpy()
+    eff_w = window if window else C
+    for b in range(B):
+        i = int(pos[b])
+        lo = max(0, i - min(eff_w, C) + 1) if ring else 0
+        Kd = gs.heads(gs.dequant_rows(Ksrc[b, lo:i + 1], kv), Hkv, d)
+        Vd = gs.heads(gs.dequant_rows(Vsrc[b, lo:i + 1], kv), Hkv, d)
+        o_ref, m_ref, pav = gs.oracle_layer(q[b].double().numpy(), Kd, Vd, np.arange(lo, i + 1), i, window,
+                                            None if alive is None else alive[b], scale, geom.nb)
+        gs.close_o(out[b].float().cpu().numpy(), o_ref, kv, pav)
+        gs.close_mass(mass[b].cpu().numpy(), m_ref, kv)
