@@ -50,8 +50,8 @@ int check_geom(const kvs_geom* g) {
 }
 
 struct Plan {
-  int NT, tpp, nparts, nsub, G, oslots;
-  size_t off_m, off_l, off_o, off_e, total;
+  int NT, tpp, nparts, nsub, G, S, tl_cap, n_wg, oslots;
+  size_t off_m, off_l, off_o, off_e, off_bnd, off_time, off_rates, total;
   size_t lds_partial;
 };
 
@@ -67,29 +67,48 @@ Plan make_plan(const kvs_geom* g) {
   if (ptarget < 1) ptarget = 1;
   int tpp = (p.NT + ptarget - 1) / ptarget;
   if (tpp < 4) tpp = 4;
-  // the partial kernel keeps per-wave side data, the wave merge area, and
-  // per-tile block sums, running maxima and the kept tile list of its
-  // partition in LDS: bound the partition so its LDS stays <= 64 KiB
+  // the partial kernel keeps per-wave side data and, per tile of its
+  // partition, the block-sum records and the kept-tile list in LDS: bound the
+  // partition so its LDS stays <= 64 KiB
   const int nw = kvs::kPartialWaves;
-  // the wave merge gives every wave its own output slot when that is small,
-  // else pairs of waves share one
-  p.oslots = p.G * g->head_dim <= 512 ? nw : nw / 2;
-  const int lds_fixed = nw * 256 + p.oslots * p.G * g->head_dim + 2 * nw * p.G + 4;
+  const int lds_fixed = nw * 256 + 4 + 2 * nw * 16;
   const int per_tile = p.G * (p.nsub + 1) + 1;
   const int tpp_lds = (kLdsBudgetFloats - lds_fixed) / per_tile;
+  // the waves' outputs are merged in LDS over the same area, rows padded by 4
+  // floats: a slot per wave when that fits, else one per pair of waves
+  const int orow = p.G * (g->head_dim + 4);
+  p.oslots = nw * orow <= kLdsBudgetFloats - lds_fixed ? nw : nw / 2;
   if (tpp > tpp_lds) tpp = tpp_lds < 4 ? 4 : tpp_lds;
-  // combine keeps two [Hq][P] float tables in LDS: bound P so they stay <= 48 KiB
-  const int pmax = 6144 / g->n_q_heads;
-  while ((p.NT + tpp - 1) / tpp > pmax) tpp *= 2;
+  // the combine keeps per-head tables and the O weights of 256 / d heads
+  // over the nparts * nw partials in LDS: bound them to 48 KiB
+  while (true) {
+    const int np = (p.NT + tpp - 1) / tpp;
+    if (kvs::combine_lds_bytes(g->n_q_heads, g->n_kv_heads, g->head_dim, np, np) <= 49152) break;
+    tpp *= 2;
+  }
   p.tpp = tpp;
   p.nparts = (p.NT + tpp - 1) / tpp;
+  p.S = p.nparts;
+  p.n_wg = p.nparts * pairs;
+  // two partitions split their range by measured rates (35..65 %): the list
+  // must hold the larger share
+  p.tl_cap = tpp;
+  if (p.nparts == 2 && !g->ring) {
+    const int cap = (int)((0.65 * p.NT) + 2);
+    if (cap <= tpp_lds && cap > p.tl_cap) p.tl_cap = cap;
+  }
   const size_t bh = (size_t)g->batch * g->n_q_heads;
   p.off_m = 0;
-  p.off_l = round256(p.off_m + bh * p.nparts * 4);
-  p.off_o = round256(p.off_l + bh * p.nparts * 4);
-  p.off_e = round256(p.off_o + bh * p.nparts * g->head_dim * 4);
-  p.total = round256(p.off_e + bh * (size_t)p.NT * p.nsub * 4);
-  p.lds_partial = 4 * ((size_t)tpp * per_tile + (size_t)lds_fixed);
+  p.off_l = round256(p.off_m + bh * p.S * 4);
+  p.off_o = round256(p.off_l + bh * p.S * 4);
+  p.off_e = round256(p.off_o + bh * p.S * g->head_dim * 4);
+  p.off_bnd = round256(p.off_e + (size_t)g->batch * p.NT * p.nsub * g->n_q_heads * 4);
+  p.off_time = round256(p.off_bnd + (size_t)pairs * 4);
+  p.off_rates = round256(p.off_time + (size_t)p.n_wg * nw * 2 * 4);
+  p.total = round256(p.off_rates + 8 * 4);
+  size_t area = (size_t)p.tl_cap * per_tile;
+  if (area < (size_t)p.oslots * orow) area = (size_t)p.oslots * orow;
+  p.lds_partial = 4 * ((size_t)lds_fixed + area);
   return p;
 }
 
@@ -200,15 +219,20 @@ int decode_setup(const kvs_geom* g, const void* q, const void* k_cache, const vo
   a->pos_of_slot = pos_of_slot; a->cur_pos = cur_pos; a->keep = keep_mask;
   a->ws_m = (float*)(ws + p.off_m); a->ws_l = (float*)(ws + p.off_l);
   a->ws_o = (float*)(ws + p.off_o); a->ws_e = (float*)(ws + p.off_e);
+  a->ws_bnd = (int*)(ws + p.off_bnd); a->ws_time = (float*)(ws + p.off_time);
+  a->rates = (const float*)(ws + p.off_rates);
   a->B = g->batch; a->Hq = g->n_q_heads; a->Hkv = g->n_kv_heads; a->G = p.G; a->C = g->capacity;
   a->NT = p.NT; a->window = g->window; a->nbmax = g->n_blocks_max;
   a->kwords = (g->n_blocks_max + 31) / 32; a->tpp = p.tpp; a->nparts = p.nparts;
-  a->dyn = g->deterministic ? 0 : 1; a->oslots = p.oslots;
+  a->dyn = g->deterministic ? 0 : 1; a->tl_cap = p.tl_cap; a->oslots = p.oslots;
   a->scale_log2 = g->softmax_scale * 1.4426950408889634f;
   *c = kvs::CombineArgs{};
   c->ws_m = a->ws_m; c->ws_l = a->ws_l; c->ws_o = a->ws_o; c->ws_e = a->ws_e; c->cur_pos = cur_pos;
+  c->ws_bnd = a->ws_bnd; c->ws_time = a->ws_time; c->rates = (float*)(ws + p.off_rates);
+  c->n_wg = p.n_wg; c->S = p.S;
+  c->adaptive = !g->ring && p.nparts == 2 && !g->deterministic;
   c->out = out; c->mass = mass_accum;
-  c->B = g->batch; c->Hq = g->n_q_heads; c->D = g->head_dim; c->C = g->capacity; c->NT = p.NT;
+  c->B = g->batch; c->Hq = g->n_q_heads; c->Hkv = g->n_kv_heads; c->D = g->head_dim; c->C = g->capacity; c->NT = p.NT;
   c->nbmax = g->n_blocks_max; c->tpp = p.tpp; c->nparts = p.nparts; c->window = g->window;
   c->n_o_chunks = (g->n_q_heads * g->head_dim + 255) / 256;
   c->n_mass_chunks = (p.NT + 255) / 256;

@@ -1,8 +1,9 @@
 // Scored split-K decode attention for gfx950.
 //
-// kvs_partial: one workgroup (4 waves) per (partition of slots, KV head,
-// sequence). Each wave walks 16-slot tiles of its partition (tiles w, w+4, ...)
-// with an online softmax, for all G query heads of the KV head at once:
+// kvs_partial: one workgroup of 8 waves per (partition of slots, KV head,
+// sequence), one workgroup per compute unit. The waves take batches of
+// 16-slot tiles of the partition from a shared LDS counter and run an online
+// softmax over them for all G query heads of the KV head at once:
 //
 //   QK:  S^T[token][head] = K[token][:] . Q[head][:]   MFMA, A = K tile, B = Q^T
 //   PV:  O^T[dim][head]  += V^T[dim][token] . P^T[token][head]   MFMA
@@ -16,10 +17,10 @@
 // scale is folded into P); F32 caches use the f32 MFMA.
 //
 // The tap (Context views at marginal cost, Tier 0): for every tile the wave
-// also sums its post-softmax weights per head relative to its running max; at
-// the end of the partition those block sums are rescaled to the partition max
-// and stored with the partition's (max, sum, unnormalised O). kvs_combine then
-// turns them into exact normalised masses.
+// also sums its post-softmax weights per head relative to its running max and
+// keeps that record in LDS; at the end of the partition the records are
+// rescaled to the workgroup max and stored with the partition's (max, sum,
+// unnormalised O). kvs_combine then turns them into exact normalised masses.
 //
 // kvs_combine: per sequence, M_h = max_p m_p, L_h = sum_p l_p 2^(m_p - M_h);
 // O_h = sum_p o_p 2^(m_p - M_h) / L_h; block mass = sum_h E_h,b 2^(m_p(b) - M_h)
@@ -122,13 +123,26 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   const int G = a.G;
   const int h = j;                       // query head within the group (this lane's column)
   const bool hreal = h < G;
+  const uint64_t clk0 = __builtin_amdgcn_s_memrealtime();
+  const int wg_id = part + a.nparts * (g + a.Hkv * b);  // dispatch order
   const int i_cur = a.cur_pos[b];
   const int lo = a.window > 0 ? i_cur - a.window + 1 : (int)0x80000000;
+  // speeds of the two workgroups of an adaptive pair (see below), fetched with cur_pos
+  const bool adaptive = !RING && a.nparts == 2 && a.dyn && a.rates != nullptr;
+  float r0 = 1.0f, r1 = 1.0f;
+  if (adaptive) {
+    r0 = a.rates[(wg_id - part) & 7];
+    r1 = a.rates[(wg_id - part + 1) & 7];
+  }
 
   // This workgroup's tiles [t0, t1). A ring reads every tile; a linear cache
-  // splits its readable range (window start .. current position) evenly over
-  // the partitions, so a partly filled or compacted cache keeps every
-  // workgroup busy. kvs_combine derives the same split from cur_pos.
+  // splits its readable range (window start .. current position) over the
+  // partitions, so a partly filled or compacted cache keeps every workgroup
+  // busy. Workgroups are placed on the chip's XCDs in dispatch order (id mod
+  // 8), and XCDs stream at measurably different rates; with two partitions
+  // and dynamic claiming the split point follows the rates the previous
+  // launches measured for the two workgroups' dispatch classes (clamped to
+  // 35..65 %), so both finish together. Otherwise the split is even.
   int t0, t1;
   if constexpr (RING) {
     t0 = part * a.tpp;
@@ -136,9 +150,19 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   } else {
     const int gte = max(0, min(a.NT, i_cur / kTile + 1));
     const int gtb = a.window > 0 ? min(gte, max(lo, 0) / kTile) : 0;
-    const int tpe = max(1, (gte - gtb + a.nparts - 1) / a.nparts);
-    t0 = min(gte, gtb + part * tpe);
-    t1 = min(gte, t0 + tpe);
+    if (adaptive) {
+      const bool ok = r0 >= 0.5f && r0 <= 2.0f && r1 >= 0.5f && r1 <= 2.0f;  // NaN fails too
+      const float f = ok ? fminf(fmaxf(r0 / (r0 + r1), 0.35f), 0.65f) : 0.5f;
+      const int n = gte - gtb;
+      int bnd = gtb + (int)(f * (float)n + 0.5f);
+      bnd = min(max(bnd, max(gtb, gte - a.tl_cap)), min(gte, gtb + a.tl_cap));
+      t0 = part == 0 ? gtb : bnd;
+      t1 = part == 0 ? bnd : gte;
+    } else {
+      const int tpe = max(1, (gte - gtb + a.nparts - 1) / a.nparts);
+      t0 = min(gte, gtb + part * tpe);
+      t1 = min(gte, t0 + tpe);
+    }
   }
 
   // Fused append: the workgroup whose tiles hold the new position's slot
@@ -151,24 +175,19 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   const int app_tile = app_slot >= 0 ? app_slot / kTile : -1;
 
   // LDS carve-up (16-byte aligned parts first): per-wave side data (FP8
-  // scales, ring positions of the claimed tiles), the wave merge area, the
-  // kept-tile count and the claim counter, then per-tile block sums of the
-  // partition, the running maxima they are relative to, and the list of kept
-  // tiles.
-  const int ntl = t1 - t0;
+  // scales, ring positions of the claimed tiles), then the kept-tile count,
+  // the claim counter, the append flag and the list entry of the appended
+  // tile, each wave's final max and sum per head, the block-sum records of
+  // every list entry (sums per sub-block and head, and the running max they
+  // are relative to) and the list of kept tiles. The waves' outputs are
+  // staged over the records at the end.
   float* side_area = lds;                               // [NW][64 quads][4]
-  float* ow = side_area + NW * 256;                     // [oslots][G][D]
-  float* mw = ow + a.oslots * G * D;                    // [NW][G]
-  float* lw = mw + NW * G;                              // [NW][G]
-  int* misc = (int*)(lw + NW * G);                      // [4]: kept-tile count, claim counter,
-                                                        // append-done flag, list entry of the appended tile
-  float* e_rec = (float*)(misc + 4);                    // [G][tpp][NSUB]
-  float* m_rec = e_rec + a.tpp * NSUB * G;              // [G][tpp]
-  int* tlist = (int*)(m_rec + a.tpp * G);               // [tpp]
-  if constexpr (SCORED) {
-    for (int x = threadIdx.x; x < a.tpp * NSUB * G; x += NTH) e_rec[x] = 0.0f;
-    for (int x = threadIdx.x; x < a.tpp * G; x += NTH) m_rec[x] = -__builtin_inff();
-  }
+  int* misc = (int*)(side_area + NW * 256);             // [4]
+  float* mw = (float*)(misc + 4);                       // [NW][16]
+  float* lw = mw + NW * 16;                             // [NW][16]
+  float* e_rec = lw + NW * 16;                          // [tl_cap][NSUB][G]
+  float* m_rec = e_rec + (size_t)a.tl_cap * NSUB * G;   // [tl_cap][G]
+  int* tlist = (int*)(m_rec + (size_t)a.tl_cap * G);    // [tl_cap]
   if (threadIdx.x == 0) {
     misc[1] = 0;
     misc[2] = 0;
@@ -185,6 +204,15 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   const uint32_t* keep_b = a.keep ? a.keep + (size_t)b * a.kwords : nullptr;
   const bool use_ids = !RING && a.ids != nullptr;
   const bool use_list = !RING && (keep_b != nullptr || use_ids);
+
+  // Block-sum records of this (sequence, KV head): tile t, sub-block sb,
+  // query head hh of the group, laid out [NT][NSUB][G], so one workgroup's
+  // records are one contiguous run; stored relative to the workgroup's max
+  // per head. Every tile of the readable range gets them each launch
+  // (skipped tiles zeros).
+  const size_t rec_row = ((size_t)b * a.Hkv + g) * a.NT;
+  const size_t hq0 = (size_t)g * G;
+  auto e_index = [&](int t, int sb, int hh) -> size_t { return ((rec_row + t) * NSUB + sb) * G + hh; };
   if (use_list && wave == 0) {
     // a block-id list becomes a bitmap over [tb, te) first (in the side-data
     // area, unused until the loop); ids may repeat and come in any order
@@ -211,6 +239,11 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
         const int e = n + __popcll(m & ((1ull << lane) - 1ull));
         tlist[e] = t;
         if (t == app_tile) misc[3] = e;
+      }
+      if constexpr (SCORED) {
+        if (t < te && !kept) {
+          for (int hh = 0; hh < G; ++hh) a.ws_e[e_index(t, 0, hh)] = 0.0f;
+        }
       }
       n += __popcll(m);
     }
@@ -353,7 +386,7 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   };
 
   // ---- one tile: online softmax, block sums, PV ----
-  auto process = [&](TileRegs<KV, D>& cur, const int tile, const int tau) {
+  auto process = [&](TileRegs<KV, D>& cur, const int tile, const int tau, const int ent) {
     f32x4 ks = {0.f, 0.f, 0.f, 0.f}, vs = {0.f, 0.f, 0.f, 0.f};
     int4 cpos = make_int4(0, 0, 0, 0);
     if constexpr (KV == KV_FP8) {
@@ -390,7 +423,16 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
       all_valid = p0 >= lo && p0 + kTile - 1 <= i_cur;  // uniform
       any_valid = true;                                  // tb..te only holds readable tiles
     }
-    if (!any_valid) return;
+    if (!any_valid) {
+      if constexpr (SCORED) {
+        if (kg == 0 && hreal) {
+#pragma unroll
+          for (int sb = 0; sb < NSUB; ++sb) e_rec[(ent * NSUB + sb) * G + h] = 0.0f;
+          m_rec[ent * G + h] = -__builtin_inff();
+        }
+      }
+      return;
+    }
 
     // Codes of keys that are not read are zeroed before use: the cache may hold
     // anything there, and 0 * NaN would poison the PV product.
@@ -467,11 +509,11 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
     l_run = l_run * alpha + (esub0 + esub1);
 
     if constexpr (SCORED) {
+      // the tile's block sums and the running max they are relative to
       if (kg == 0 && hreal) {
-        const int tlc = tile - t0;
-        e_rec[(h * a.tpp + tlc) * NSUB] = esub0;
-        if constexpr (NSUB == 2) e_rec[(h * a.tpp + tlc) * NSUB + 1] = esub1;
-        m_rec[h * a.tpp + tlc] = m_new;
+        e_rec[(ent * NSUB) * G + h] = esub0;
+        if constexpr (NSUB == 2) e_rec[(ent * NSUB + 1) * G + h] = esub1;
+        m_rec[ent * G + h] = m_new;
       }
     }
 
@@ -615,6 +657,7 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
     if (lane == 0) __hip_atomic_store(&misc[2], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
 
+  int n_done = 0;  // tiles this wave processed
   int cur = claim();
   if (cur < n_batches) {
     TileRegs<KV, D> buf[NBUF];
@@ -631,24 +674,64 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
         load_tile<KV, D, RING>(buf[(s + NBUF - 1) % NBUF], ad,
                                s == 0 ? soff_of(cur, NBUF - 1) : soff_of(nxt, s - 1));
         const int e = BATCH * cur + s;
-        if (e < n_items) process(buf[s], tile_of(e), s);
+        if (e < n_items) process(buf[s], tile_of(e), s, e);
       }
+      n_done += min(BATCH, n_items - BATCH * cur);
       if (nxt >= n_batches) break;
       cur = nxt;
     }
   }
 
-  // ---- merge the waves of the workgroup ----
-  // Every wave leaves its (max, sum, O) in LDS; each output then combines the
-  // waves in a fixed order, rescaled to the workgroup max per head. When the
-  // slots do not fit, waves w and w + NW/2 share one: they rescale to the
-  // workgroup max first and the upper half adds into the lower half's slot.
+  // ---- end of the partition: records, then the workgroup's partial ----
   if (hreal && kg == 0) {
-    mw[wave * G + h] = m_run;
-    lw[wave * G + h] = l_run;
+    mw[wave * 16 + h] = m_run;
+    lw[wave * 16 + h] = l_run;
   }
+  // tiles and clock ticks (100 MHz) of this wave, for the split of later launches
+  if (a.ws_time != nullptr && lane == 0) {
+    float* tm = a.ws_time + ((size_t)wg_id * NW + wave) * 2;
+    tm[0] = (float)n_done;
+    tm[1] = (float)(__builtin_amdgcn_s_memrealtime() - clk0);
+  }
+  if constexpr (SCORED) {
+    if (adaptive && part == 0 && threadIdx.x == 0) a.ws_bnd[(size_t)b * a.Hkv + g] = t1;
+  }
+  __syncthreads();
+  auto wg_max = [&](int hh) -> float {
+    float M = -__builtin_inff();
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, mw[w * 16 + hh]);
+    return M;
+  };
+
+  // The block-sum records, rescaled from the running max at the time to the
+  // workgroup max per head, are stored by the whole workgroup as contiguous
+  // runs once every wave is done: global stores inside the streaming loop
+  // would hold up the in-order completion count the tile loads are waited on
+  // with. The split point of an adaptive pair goes with them, for
+  // kvs_combine's tile-to-partition map.
+  if constexpr (SCORED) {
+    const int per_e = NSUB * G;
+    for (int x = threadIdx.x; x < n_items * per_e; x += NTH) {
+      const int e = x / per_e;
+      const int hh = x % G;
+      const float M = wg_max(hh);
+      const float mr = m_rec[e * G + hh];
+      const float v = (M == -__builtin_inff() || mr == -__builtin_inff()) ? 0.0f : e_rec[x] * fast_exp2(mr - M);
+      const int t = use_list ? tlist[e] : tb + e;
+      a.ws_e[e_index(t, 0, 0) + (x - e * per_e)] = v;
+    }
+    __syncthreads();  // the record area is reused below
+  }
+
+  // The waves' outputs merge in LDS (staged over the records, rows padded by
+  // 4 floats against bank conflicts) into one partial per workgroup: each
+  // output sums the waves in a fixed order, rescaled to the workgroup max.
+  // When the slots do not fit, waves w and w + NW/2 share one: they rescale
+  // first and the upper half adds into the lower half's slot.
+  constexpr int DP = D + 4;
+  float* ow = e_rec;  // [oslots][G][DP]
   auto put_o = [&](int slot, float sc, bool add) {
-    float* dst = ow + (slot * G + h) * D;
+    float* dst = ow + (slot * G + h) * DP;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int d0 = NC * (4 * kg + r);  // lane's dims d0 .. d0 + NC - 1
@@ -670,122 +753,192 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
     if (hreal) put_o(wave, 1.0f, false);
     __syncthreads();
   } else {
-    __syncthreads();
-    float M = -__builtin_inff();
-    if (hreal)
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, mw[w * G + h]);
-    const float sc = (M == -__builtin_inff()) ? 0.0f : fast_exp2(m_run - M);
+    const float M = hreal ? wg_max(h) : 0.0f;
+    const float sc = (m_run == -__builtin_inff()) ? 0.0f : fast_exp2(m_run - M);
     if (hreal && wave < NW / 2) put_o(wave, sc, false);
     __syncthreads();
     if (hreal && wave >= NW / 2) put_o(wave - NW / 2, sc, true);
     __syncthreads();
   }
-
-  auto wg_max = [&](int hh) -> float {
-    float M = -__builtin_inff();
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, mw[w * G + hh]);
-    return M;
-  };
-  const size_t pbase = ((size_t)b * a.Hq + (size_t)g * G);  // first head of the group
+  const size_t pbase = (size_t)b * a.Hq + hq0;  // first head of the group
   for (int x = threadIdx.x; x < G * D; x += NTH) {
     const int hh = x / D, dd = x % D;
     float o = 0.0f;
     if (own_slots) {
       const float M = wg_max(hh);
-      if (M != -__builtin_inff()) {
-        for (int w = 0; w < NW; ++w) o += ow[(w * G + hh) * D + dd] * fast_exp2(mw[w * G + hh] - M);
+      for (int w = 0; w < NW; ++w) {
+        const float m = mw[w * 16 + hh];
+        if (m != -__builtin_inff()) o += ow[(w * G + hh) * DP + dd] * fast_exp2(m - M);
       }
     } else {
-      for (int sl = 0; sl < NW / 2; ++sl) o += ow[(sl * G + hh) * D + dd];
+      for (int sl = 0; sl < NW / 2; ++sl) o += ow[(sl * G + hh) * DP + dd];
     }
     a.ws_o[((pbase + hh) * a.nparts + part) * D + dd] = o;
   }
   for (int hh = threadIdx.x; hh < G; hh += NTH) {
     const float M = wg_max(hh);
     float l = 0.0f;
-    if (M != -__builtin_inff()) {
-      for (int w = 0; w < NW; ++w) l += lw[w * G + hh] * fast_exp2(mw[w * G + hh] - M);
+    for (int w = 0; w < NW; ++w) {
+      const float m = mw[w * 16 + hh];
+      if (m != -__builtin_inff()) l += lw[w * 16 + hh] * fast_exp2(m - M);
     }
     a.ws_m[(pbase + hh) * a.nparts + part] = M;
     a.ws_l[(pbase + hh) * a.nparts + part] = l;
   }
-  if constexpr (SCORED) {
-    // Block sums rescaled from the running max at the time to the workgroup
-    // max; tiles never read keep 0. Consecutive threads take consecutive
-    // tiles of one head.
-    const int per_head = ntl * NSUB;
-    for (int x = threadIdx.x; x < G * per_head; x += NTH) {
-      const int hh = x / per_head;
-      const int rem = x - hh * per_head;
-      const int tlc = rem / NSUB;
-      const float M = wg_max(hh);
-      float e = e_rec[hh * a.tpp * NSUB + rem];
-      const float mr = m_rec[hh * a.tpp + tlc];
-      e = (M == -__builtin_inff() || mr == -__builtin_inff()) ? 0.0f : e * fast_exp2(mr - M);
-      a.ws_e[(pbase + hh) * a.NT * NSUB + (size_t)t0 * NSUB + rem] = e;
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
-// Combine: grid (n_o_chunks + n_mass_chunks, B), 256 threads.
+// Combine: grid (n_o_chunks + n_mass_chunks + 1, B), 256 threads.
+// Every workgroup first reduces, per head h of its sequence, the partitions'
+// partials to M_h = max_p m_p and L_h = sum_p l_p 2^(m_p - M_h). O chunks then
+// form O_h = sum_p o_p 2^(m_p - M_h) / L_h for 256 / D heads each; mass chunks
+// add, per tile and sub-block, sum_h E 2^(m_p(tile) - M_h) / L_h over the heads
+// in ascending order into mass_accum, E being the tile's record relative to
+// its partition's max. The last column (sequence 0 only) refreshes the
+// per-class streaming rates from the partial kernel's clock records.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max64(float v) {
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum64(float v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
 template <bool RING, bool Q_BF16>
 __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
   extern __shared__ float lds[];
   const int b = blockIdx.y;
+  const int S = a.S;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n_work = a.n_o_chunks + a.n_mass_chunks;
+
+  if ((int)blockIdx.x >= n_work) {
+    // ---- rates: per dispatch class (workgroup id mod 8), tiles per tick of
+    // its workgroups (a workgroup's time is its slowest wave's), relative to
+    // the mean over classes, blended half-and-half into the stored value ----
+    if (b != 0 || a.rates == nullptr || a.ws_time == nullptr) return;
+    float* ct = lds;       // [8] tiles
+    float* cs = lds + 8;   // [8] ticks
+    if (tid < 16) lds[tid] = 0.0f;
+    __syncthreads();
+    for (int w = tid; w < a.n_wg; w += 256) {
+      float tiles = 0.0f, ticks = 0.0f;
+      for (int k = 0; k < kPartialWaves; ++k) {
+        const float* tm = a.ws_time + ((size_t)w * kPartialWaves + k) * 2;
+        tiles += tm[0];
+        ticks = fmaxf(ticks, tm[1]);
+      }
+      if (tiles > 0.0f && ticks > 0.0f && tiles < 1e9f && ticks < 1e9f) {
+        atomicAdd(&ct[w & 7], tiles);
+        atomicAdd(&cs[w & 7], ticks);
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float r[8], mean = 0.0f;
+      int nv = 0;
+      for (int c = 0; c < 8; ++c) {
+        r[c] = cs[c] > 0.0f ? ct[c] / cs[c] : 0.0f;
+        if (r[c] > 0.0f) {
+          mean += r[c];
+          ++nv;
+        }
+      }
+      if (nv > 0) {
+        mean /= (float)nv;
+        for (int c = 0; c < 8; ++c) {
+          if (!(r[c] > 0.0f)) continue;
+          const float rel = fminf(fmaxf(r[c] / mean, 0.5f), 2.0f);
+          const float old = a.rates[c];
+          const bool ok = old >= 0.5f && old <= 2.0f;
+          a.rates[c] = ok ? 0.5f * old + 0.5f * rel : rel;
+        }
+      }
+    }
+    return;
+  }
+
   const int P = a.nparts;
-  const int HP = a.Hq * P;
-  float* wgt = lds;               // [Hq][P]: partition maxima, then 2^(m_p - M_h) / L_h
-  float* lsum = wgt + HP;         // [Hq][P]: partition sums
-  float* hM = lsum + HP;          // [Hq]
-  float* hInv = hM + a.Hq;        // [Hq]
-  const float* mb = a.ws_m + (size_t)b * HP;
-  const float* lb = a.ws_l + (size_t)b * HP;
-  for (int x = threadIdx.x; x < HP; x += 256) {
-    wgt[x] = mb[x];
-    lsum[x] = lb[x];
+  const int NWP = S / P;        // partials (waves) per partition
+  float* hM = lds;              // [Hq]
+  float* hInv = hM + a.Hq;      // [Hq]
+  float* mS = hInv + a.Hq;      // [Hq][S] partial maxima
+  float* lS = mS + a.Hq * S;    // [Hq][S] partial sums
+  float* wp = lS + a.Hq * S;    // [Hq][P] record weights 2^(M_p - M_h) / L_h
+  int* bnd = (int*)(wp + a.Hq * P);  // [Hkv] split points
+  {
+    const float* mp = a.ws_m + (size_t)b * a.Hq * S;
+    const float* lp = a.ws_l + (size_t)b * a.Hq * S;
+    for (int x = tid; x < a.Hq * S; x += 256) {
+      mS[x] = mp[x];
+      lS[x] = lp[x];
+    }
+    if (a.adaptive)
+      for (int x = tid; x < a.Hkv; x += 256) bnd[x] = a.ws_bnd[(size_t)b * a.Hkv + x];
   }
   __syncthreads();
-  for (int h = threadIdx.x; h < a.Hq; h += 256) {
+  for (int hh = tid; hh < a.Hq; hh += 256) {
     float M = -__builtin_inff();
-    for (int p = 0; p < P; ++p) M = fmaxf(M, wgt[h * P + p]);
+    for (int x = 0; x < S; ++x) M = fmaxf(M, mS[hh * S + x]);
     float L = 0.0f;
-    if (M != -__builtin_inff())
-      for (int p = 0; p < P; ++p) L += lsum[h * P + p] * fast_exp2(wgt[h * P + p] - M);
-    hM[h] = M;
-    hInv[h] = L > 0.0f ? 1.0f / L : 0.0f;
-  }
-  __syncthreads();
-  for (int x = threadIdx.x; x < HP; x += 256) {
-    const int h = x / P;
-    const float M = hM[h];
-    wgt[x] = (M == -__builtin_inff()) ? 0.0f : fast_exp2(wgt[x] - M) * hInv[h];
+    if (M != -__builtin_inff()) {
+      for (int x = 0; x < S; ++x) {
+        const float m = mS[hh * S + x];
+        if (m != -__builtin_inff()) L += lS[hh * S + x] * fast_exp2(m - M);
+      }
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    hM[hh] = M;
+    hInv[hh] = inv;
+    // a partition's records are relative to the max over its waves
+    for (int p = 0; p < P; ++p) {
+      float Mp = -__builtin_inff();
+      for (int w = 0; w < NWP; ++w) Mp = fmaxf(Mp, mS[hh * S + p * NWP + w]);
+      wp[hh * P + p] = (Mp == -__builtin_inff() || inv == 0.0f) ? 0.0f : fast_exp2(Mp - M) * inv;
+    }
   }
   __syncthreads();
 
   if ((int)blockIdx.x < a.n_o_chunks) {
-    const int total = a.Hq * a.D;
-    for (int x = blockIdx.x * 256 + threadIdx.x; x < total; x += a.n_o_chunks * 256) {
-      const int h = x / a.D, d = x % a.D;
-      const float* o = a.ws_o + (((size_t)b * a.Hq + h) * P) * a.D + d;
-      const float* w = wgt + h * P;
-      float acc0 = 0.0f, acc1 = 0.0f, acc2 = 0.0f, acc3 = 0.0f;
-      int p = 0;
-      for (; p + 4 <= P; p += 4) {
-        acc0 += o[(size_t)(p + 0) * a.D] * w[p + 0];
-        acc1 += o[(size_t)(p + 1) * a.D] * w[p + 1];
-        acc2 += o[(size_t)(p + 2) * a.D] * w[p + 2];
-        acc3 += o[(size_t)(p + 3) * a.D] * w[p + 3];
+    const int HPC = 256 / a.D;           // heads per chunk (D divides 256)
+    const int h0 = blockIdx.x * HPC;
+    float* wts = (float*)(bnd + a.Hkv);  // [HPC][S]
+    for (int x = tid; x < HPC * S; x += 256) {
+      const int hl = x / S, sl = x - hl * S;
+      const int hh = h0 + hl;
+      float w = 0.0f;
+      if (hh < a.Hq) {
+        const float m = mS[hh * S + sl];
+        w = (m == -__builtin_inff() || hInv[hh] == 0.0f) ? 0.0f : fast_exp2(m - hM[hh]) * hInv[hh];
       }
-      for (; p < P; ++p) acc0 += o[(size_t)p * a.D] * w[p];
-      const float acc = (acc0 + acc1) + (acc2 + acc3);
-      const size_t oi = ((size_t)b * a.Hq + h) * a.D + d;
-      if constexpr (Q_BF16)
-        ((uint16_t*)a.out)[oi] = f32_to_bf16_rne(acc);
-      else
-        ((float*)a.out)[oi] = acc;
+      wts[x] = w;
     }
+    __syncthreads();
+    const int x = blockIdx.x * 256 + tid;
+    if (x >= a.Hq * a.D) return;
+    const int hh = x / a.D, d = x % a.D;
+    const float* o = a.ws_o + ((size_t)b * a.Hq + hh) * S * a.D + d;
+    const float* w = wts + (hh - h0) * S;
+    // every partition writes its partial each launch (zeros when it read
+    // nothing), so all are finite and summed unconditionally
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    int p = 0;
+    for (; p + 4 <= S; p += 4) {
+      float v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = o[(size_t)(p + k) * a.D];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] += v[k] * w[p + k];
+    }
+    for (; p < S; ++p) acc[0] += o[(size_t)p * a.D] * w[p];
+    const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    const size_t oi = ((size_t)b * a.Hq + hh) * a.D + d;
+    if constexpr (Q_BF16)
+      ((uint16_t*)a.out)[oi] = f32_to_bf16_rne(sum);
+    else
+      ((float*)a.out)[oi] = sum;
     return;
   }
   if (a.mass == nullptr && a.head_mass == nullptr && a.mass_max == nullptr) return;
@@ -793,7 +946,7 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
   const int chunk = blockIdx.x - a.n_o_chunks;
   const int i_cur = a.cur_pos[b];
   const int lap_i = RING ? i_cur / a.C : 0;
-  // tiles with block sums: every tile of a ring; a linear cache's readable
+  // tiles with records: every tile of a ring; a linear cache's readable
   // range, split over the partitions as the partial kernel split it
   int tlo = 0, thi = a.NT, tpe = a.tpp;
   if constexpr (!RING) {
@@ -802,8 +955,7 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
     tlo = a.window > 0 ? min(thi, max(lo, 0) / kTile) : 0;
     tpe = max(1, (thi - tlo + P - 1) / P);
   }
-  for (int t = tlo + chunk * 256 + threadIdx.x; t < thi; t += a.n_mass_chunks * 256) {
-    const int p = (t - tlo) / tpe;
+  for (int t = tlo + chunk * 256 + tid; t < thi; t += a.n_mass_chunks * 256) {
     // logical block of each sub-block of tile t (-1: none)
     int blk[NSUB];
 #pragma unroll
@@ -815,46 +967,87 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
       }
       if (blk[sb] >= a.nbmax) blk[sb] = -1;
     }
-    // heads summed in ascending order; per-head masses and their max on the side
-    const float* e = a.ws_e + ((size_t)b * a.Hq * a.NT + t) * NSUB;
     float acc[NSUB], mx[NSUB];
 #pragma unroll
     for (int sb = 0; sb < NSUB; ++sb) {
       acc[sb] = 0.0f;
       mx[sb] = 0.0f;
     }
-    if (a.head_mass == nullptr) {
-      for (int h = 0; h < a.Hq; ++h) {
-        const float w = wgt[h * P + p];
+    // heads in ascending order, up to 32 (16 for rings) at a time with all
+    // their record loads in flight (head h sits at row (b, h / G) of the
+    // records, entry h % G); per-head masses read-modify-written alongside
+    // when asked for. Every tile of the range has records from this launch.
+    const int G = a.Hq / a.Hkv;
+    const int p_even = (t - tlo) / tpe;  // partition of t under an even split
+    auto part_of = [&](int gg) -> int { return a.adaptive ? (t < bnd[gg] ? 0 : 1) : p_even; };
+    constexpr int HC = RING ? 16 : 32;
+    for (int hc = 0; hc < a.Hq; hc += HC) {
+      float ev[NSUB][HC], sc[HC];
+      if (G % 4 == 0) {
+        // four heads of one group per 16-byte load; consecutive threads
+        // (tiles) read consecutive 16-byte pieces
 #pragma unroll
-        for (int sb = 0; sb < NSUB; ++sb) {
-          const float v = e[(size_t)h * a.NT * NSUB + sb] * w;
+        for (int q = 0; q < HC / 4; ++q) {
+          const int hh = hc + 4 * q;
+          f32x4 e4[NSUB];
+#pragma unroll
+          for (int sb = 0; sb < NSUB; ++sb) e4[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          int pp = 0;
+          if (hh < a.Hq) {
+            const int gg = hh / G;
+            const size_t row = ((size_t)b * a.Hkv + gg) * a.NT + t;
+            const int kk = hh - gg * G;
+            pp = part_of(gg);
+#pragma unroll
+            for (int sb = 0; sb < NSUB; ++sb) e4[sb] = *(const f32x4*)(a.ws_e + (row * NSUB + sb) * G + kk);
+          }
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            sc[4 * q + k] = hh + k < a.Hq ? wp[(hh + k) * P + pp] : 0.0f;
+#pragma unroll
+            for (int sb = 0; sb < NSUB; ++sb) ev[sb][4 * q + k] = e4[sb][k];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < HC; ++k) {
+          const int hh = hc + k;
+          float w = 0.0f;
+#pragma unroll
+          for (int sb = 0; sb < NSUB; ++sb) ev[sb][k] = 0.0f;
+          if (hh < a.Hq) {
+            const int gg = hh / G;
+            const size_t row = ((size_t)b * a.Hkv + gg) * a.NT + t;
+            const int kk = hh - gg * G;
+            w = wp[hh * P + part_of(gg)];
+#pragma unroll
+            for (int sb = 0; sb < NSUB; ++sb) ev[sb][k] = a.ws_e[(row * NSUB + sb) * G + kk];
+          }
+          sc[k] = w;
+        }
+      }
+#pragma unroll
+      for (int sb = 0; sb < NSUB; ++sb) {
+        float* hp = a.head_mass ? a.head_mass + ((size_t)b * a.Hq + hc) * a.nbmax + (blk[sb] < 0 ? 0 : blk[sb])
+                                : nullptr;
+#pragma unroll
+        for (int k = 0; k < HC; ++k) {
+          if (hc + k >= a.Hq) break;
+          const float v = ev[sb][k] * sc[k];
           acc[sb] += v;
           mx[sb] = fmaxf(mx[sb], v);
         }
-      }
-    } else {
-      // per-head masses read-modify-written eight heads at a time, so the
-      // loads of a group are in flight together
-      constexpr int HB = 8;
-      for (int h0 = 0; h0 < a.Hq; h0 += HB) {
-        const int nh = min(HB, a.Hq - h0);
+        if (hp != nullptr && blk[sb] >= 0) {
+          // per-head masses, eight read-modify-writes in flight at a time
 #pragma unroll
-        for (int sb = 0; sb < NSUB; ++sb) {
-          float ev[HB], hv[HB];
-          float* hp = a.head_mass + ((size_t)b * a.Hq + h0) * a.nbmax + (blk[sb] < 0 ? 0 : blk[sb]);
+          for (int k0 = 0; k0 < HC; k0 += 8) {
+            if (hc + k0 >= a.Hq) break;
+            float hv[8];
 #pragma unroll
-          for (int k = 0; k < HB; ++k) {
-            ev[k] = k < nh ? e[(size_t)(h0 + k) * a.NT * NSUB + sb] : 0.0f;
-            hv[k] = (k < nh && blk[sb] >= 0) ? hp[(size_t)k * a.nbmax] : 0.0f;
-          }
+            for (int k = 0; k < 8; ++k) hv[k] = hc + k0 + k < a.Hq ? hp[(size_t)(k0 + k) * a.nbmax] : 0.0f;
 #pragma unroll
-          for (int k = 0; k < HB; ++k) {
-            if (k >= nh) break;
-            const float v = ev[k] * wgt[(h0 + k) * P + p];
-            acc[sb] += v;
-            mx[sb] = fmaxf(mx[sb], v);
-            if (blk[sb] >= 0) hp[(size_t)k * a.nbmax] = hv[k] + v;
+            for (int k = 0; k < 8; ++k)
+              if (hc + k0 + k < a.Hq) hp[(size_t)(k0 + k) * a.nbmax] = hv[k] + ev[sb][k0 + k] * sc[k0 + k];
           }
         }
       }
@@ -904,14 +1097,16 @@ hipError_t launch_partial(int kv, int d, const PartialArgs& a, bool scored, bool
 
 hipError_t launch_combine(const CombineArgs& a, bool ring, bool q_bf16, hipStream_t st) {
   const bool mass_work = a.mass || a.head_mass || a.mass_max;
-  dim3 grid(a.n_o_chunks + (mass_work ? a.n_mass_chunks : 0), a.B), block(256);
-  const size_t lds = (2 * (size_t)a.Hq * a.nparts + 2 * (size_t)a.Hq) * sizeof(float);
+  CombineArgs c = a;
+  if (!mass_work) c.n_mass_chunks = 0;
+  dim3 grid(c.n_o_chunks + c.n_mass_chunks + 1, c.B), block(256);
+  const size_t lds = combine_lds_bytes(c.Hq, c.Hkv, c.D, c.S, c.nparts);
   if (ring) {
-    if (q_bf16) hipLaunchKernelGGL((kvs_combine<true, true>), grid, block, lds, st, a);
-    else hipLaunchKernelGGL((kvs_combine<true, false>), grid, block, lds, st, a);
+    if (q_bf16) hipLaunchKernelGGL((kvs_combine<true, true>), grid, block, lds, st, c);
+    else hipLaunchKernelGGL((kvs_combine<true, false>), grid, block, lds, st, c);
   } else {
-    if (q_bf16) hipLaunchKernelGGL((kvs_combine<false, true>), grid, block, lds, st, a);
-    else hipLaunchKernelGGL((kvs_combine<false, false>), grid, block, lds, st, a);
+    if (q_bf16) hipLaunchKernelGGL((kvs_combine<false, true>), grid, block, lds, st, c);
+    else hipLaunchKernelGGL((kvs_combine<false, false>), grid, block, lds, st, c);
   }
   return hipGetLastError();
 }

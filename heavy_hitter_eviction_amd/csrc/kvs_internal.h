@@ -23,13 +23,19 @@ struct PartialArgs {
   const uint32_t* keep;
   const int32_t* ids;    // [B][ids_stride] block ids to read (re-attend), or NULL
   const int32_t* n_ids;  // [B] entries of ids used per sequence
-  float* ws_m;     // [B][Hq][P]
-  float* ws_l;     // [B][Hq][P]
-  float* ws_o;     // [B][Hq][P][D]
-  float* ws_e;     // [B][Hq][NT][NSUB] per-tile block sums, relative to the partition max
+  // one partial per partition (workgroup)
+  float* ws_m;     // [B][Hq][P] max (log2 units)
+  float* ws_l;     // [B][Hq][P] sum of 2^(logit - max)
+  float* ws_o;     // [B][Hq][P][D] unnormalised output
+  float* ws_e;     // [B][Hkv][NT][NSUB][G] per-tile block sums, relative to the
+                   // max of the partition's workgroup (its waves' ws_m)
+  int* ws_bnd;     // [B][Hkv] split point of an adaptive two-partition range
+  float* ws_time;  // [workgroups][kPartialWaves][2] tiles processed, clock ticks
+  const float* rates;  // [8] relative streaming rate per dispatch class, or NULL
   int B, Hq, Hkv, G, C, NT, window, nbmax, kwords, tpp, nparts;
   int ids_stride;
   int dyn;     // 1: waves claim tiles dynamically; 0: fixed round-robin order
+  int tl_cap;  // LDS capacity of the kept-tile list (>= any partition's tiles)
   int oslots;  // LDS output slots of the wave merge: kPartialWaves or kPartialWaves / 2
   float scale_log2;
   // Fused append: row b of app_k / app_v ([B][Hkv*D], bf16 if app_bf16, else
@@ -46,13 +52,27 @@ struct CombineArgs {
   const float* ws_l;
   const float* ws_o;
   const float* ws_e;
+  const int* ws_bnd;
+  const float* ws_time;
+  float* rates;   // updated from ws_time by one workgroup, or NULL
+  int n_wg;       // partial workgroups that wrote ws_time
+  int S;          // partial slots per (sequence, head)
+  int adaptive;   // two partitions split at ws_bnd (else evenly)
   const int32_t* cur_pos;
   void* out;
   float* mass;
   float* head_mass;  // [B][Hq][nbmax] per-head block masses (+=), or NULL
   float* mass_max;   // [B][nbmax] running max over heads (and calls), or NULL
-  int B, Hq, D, C, NT, nbmax, tpp, nparts, n_o_chunks, n_mass_chunks, window;
+  int B, Hq, Hkv, D, C, NT, nbmax, tpp, nparts, n_o_chunks, n_mass_chunks, window;
 };
+
+// LDS of one combine workgroup: per-head max and 1/sum, every partial's max
+// and sum, per (head, partition) record weights, the split points, the
+// O-merge weights of its heads, or the rate accumulators (16 floats).
+inline size_t combine_lds_bytes(int Hq, int Hkv, int D, int S, int P) {
+  const size_t f = 2 * (size_t)Hq + 2 * (size_t)Hq * S + (size_t)Hq * P + Hkv + (size_t)(256 / D) * S;
+  return (f < 16 ? 16 : f) * sizeof(float);
+}
 
 hipError_t launch_partial(int kv, int d, const PartialArgs& a, bool scored, bool ring,
                           size_t lds_bytes, hipStream_t st);
