@@ -836,229 +836,281 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
       }
     }
     __syncthreads();
-    if (tid == 0) {
-      float r[8], mean = 0.0f;
+    if (tid < 8) {
+      // every thread derives the mean itself, then blends its own class
+      float mean = 0.0f;
       int nv = 0;
       for (int c = 0; c < 8; ++c) {
-        r[c] = cs[c] > 0.0f ? ct[c] / cs[c] : 0.0f;
-        if (r[c] > 0.0f) {
-          mean += r[c];
+        const float r = cs[c] > 0.0f ? ct[c] / cs[c] : 0.0f;
+        if (r > 0.0f) {
+          mean += r;
           ++nv;
         }
       }
-      if (nv > 0) {
-        mean /= (float)nv;
-        for (int c = 0; c < 8; ++c) {
-          if (!(r[c] > 0.0f)) continue;
-          const float rel = fminf(fmaxf(r[c] / mean, 0.5f), 2.0f);
-          const float old = a.rates[c];
-          const bool ok = old >= 0.5f && old <= 2.0f;
-          a.rates[c] = ok ? 0.5f * old + 0.5f * rel : rel;
-        }
+      const float r = cs[tid] > 0.0f ? ct[tid] / cs[tid] : 0.0f;
+      const float old = a.rates[tid];
+      if (nv > 0 && r > 0.0f) {
+        const float rel = fminf(fmaxf(r / (mean / (float)nv), 0.5f), 2.0f);
+        const bool ok = old >= 0.5f && old <= 2.0f;  // NaN fails too
+        a.rates[tid] = ok ? 0.5f * old + 0.5f * rel : rel;
       }
     }
     return;
   }
 
-  const int P = a.nparts;
-  const int NWP = S / P;        // partials (waves) per partition
+  // One partial per partition (S == nparts). Each workgroup first issues the
+  // global loads that need nothing from the shared prologue (its O partials,
+  // or its tile's records and current masses), then builds the per-head
+  // tables, then finishes: one round of load latency instead of three.
+  const int P = S;
+  constexpr int NSUB = RING ? 2 : 1;
+  constexpr int HC = RING ? 16 : 32;   // heads per record chunk
+  constexpr int OPF = 8;               // O partials prefetched per output
+  const bool is_o = (int)blockIdx.x < a.n_o_chunks;
+  const bool any_mass = a.mass != nullptr || a.head_mass != nullptr || a.mass_max != nullptr;
+  if (!is_o && !any_mass) return;
+  const int G = a.Hq / a.Hkv;
+
+  // ---- independent loads ----
+  // the partitions' maxima and sums of the sequence (staged in LDS below)
+  const float* mp = a.ws_m + (size_t)b * a.Hq * S;
+  const float* lp = a.ws_l + (size_t)b * a.Hq * S;
+  const int n_ml = a.Hq * S;
+  const float m_pre0 = mp[min(tid, n_ml - 1)], l_pre0 = lp[min(tid, n_ml - 1)];
+  const float m_pre1 = mp[min(tid + 256, n_ml - 1)], l_pre1 = lp[min(tid + 256, n_ml - 1)];
+  const int bnd_pre = a.ws_bnd[(size_t)b * a.Hkv + min(tid, a.Hkv - 1)];  // used only if adaptive
+  // O chunk: output (hh, d) of this thread
+  const int xo = blockIdx.x * 256 + tid;
+  const bool o_live = is_o && xo < a.Hq * a.D;
+  const int oh = o_live ? xo / a.D : 0, od = o_live ? xo % a.D : 0;
+  const float* o_src = a.ws_o + ((size_t)b * a.Hq + oh) * S * a.D + od;
+  // loads are unconditional (indices clamped into range, unused values
+  // masked later): conditional loads make the compiler wait for each one
+  float ov[OPF];
+#pragma unroll
+  for (int k = 0; k < OPF; ++k) ov[k] = o_src[(size_t)min(k, S - 1) * a.D];
+  // mass chunk: tile t of this thread (tiles with records: every tile of a
+  // ring; a linear cache's readable range), its logical blocks, the records
+  // of its first HC heads and the current masses of its blocks
+  // (without a window the range starts at tile 0, so the record loads need
+  // not wait for cur_pos; the range end and the blocks come after them)
+  int tlo = 0;
+  if constexpr (!RING) {
+    if (a.window > 0) {
+      const int ic = a.cur_pos[b];
+      const int thi0 = max(0, min(a.NT, ic / kTile + 1));
+      tlo = min(thi0, max(ic - a.window + 1, 0) / kTile);
+    }
+  }
+  const int t = tlo + ((int)blockIdx.x - a.n_o_chunks) * 256 + tid;
+  // records of heads past Hq (clamped duplicates) get weight 0; a dead
+  // thread's values are never used
+  const int tc = min(max(t, 0), a.NT - 1);
+  float ev[NSUB][HC];
+  auto load_records = [&](int hc) {
+    if (G % 4 == 0) {
+      // four heads of one group per 16-byte load; consecutive threads
+      // (tiles) read consecutive 16-byte pieces
+#pragma unroll
+      for (int q = 0; q < HC / 4; ++q) {
+        const int hh = min(hc + 4 * q, a.Hq - 4);
+        const int gg = hh / G;
+        const size_t row = ((size_t)b * a.Hkv + gg) * a.NT + tc;
+#pragma unroll
+        for (int sb = 0; sb < NSUB; ++sb) {
+          const f32x4 e4 = *(const f32x4*)(a.ws_e + (row * NSUB + sb) * G + (hh - gg * G));
+#pragma unroll
+          for (int k = 0; k < 4; ++k) ev[sb][4 * q + k] = e4[k];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < HC; ++k) {
+        const int hh = min(hc + k, a.Hq - 1);
+        const int gg = hh / G;
+        const size_t row = ((size_t)b * a.Hkv + gg) * a.NT + tc;
+#pragma unroll
+        for (int sb = 0; sb < NSUB; ++sb) ev[sb][k] = a.ws_e[(row * NSUB + sb) * G + (hh - gg * G)];
+      }
+    }
+  };
+  load_records(0);
+  float mass_old[NSUB], max_old[NSUB];
+  if constexpr (!RING) {
+    // a linear cache's block is the tile: its index needs no cur_pos
+    const size_t mi = (size_t)b * a.nbmax + min(tc, a.nbmax - 1);
+    mass_old[0] = a.mass != nullptr ? a.mass[mi] : 0.0f;
+    max_old[0] = a.mass_max != nullptr ? a.mass_max[mi] : 0.0f;
+  }
+  const int i_cur = a.cur_pos[b];
+  int thi = a.NT, tpe = a.tpp;
+  if constexpr (!RING) {
+    thi = max(0, min(a.NT, i_cur / kTile + 1));
+    tpe = max(1, (thi - tlo + P - 1) / P);
+  }
+  const bool m_live = !is_o && t < thi;
+  const int lap_i = RING ? i_cur / a.C : 0;
+  int blk[NSUB];
+#pragma unroll
+  for (int sb = 0; sb < NSUB; ++sb) {
+    blk[sb] = t;
+    if constexpr (RING) {
+      const int lap = ((lap_i & 1) == sb) ? lap_i : lap_i - 1;
+      blk[sb] = lap < 0 ? -1 : lap * (a.C / kTile) + t;
+    }
+    if (!m_live || blk[sb] >= a.nbmax) blk[sb] = -1;
+  }
+  if constexpr (RING) {
+#pragma unroll
+    for (int sb = 0; sb < NSUB; ++sb) {
+      const size_t mi = (size_t)b * a.nbmax + max(blk[sb], 0);
+      mass_old[sb] = a.mass != nullptr ? a.mass[mi] : 0.0f;
+      max_old[sb] = a.mass_max != nullptr ? a.mass_max[mi] : 0.0f;
+    }
+  }
+
+  // ---- per-head tables: M_h, 1 / L_h and the partition weights ----
   float* hM = lds;              // [Hq]
   float* hInv = hM + a.Hq;      // [Hq]
-  float* mS = hInv + a.Hq;      // [Hq][S] partial maxima
-  float* lS = mS + a.Hq * S;    // [Hq][S] partial sums
-  float* wp = lS + a.Hq * S;    // [Hq][P] record weights 2^(M_p - M_h) / L_h
+  float* mS = hInv + a.Hq;      // [Hq][P] partition maxima
+  float* lS = mS + a.Hq * S;    // [Hq][P] partition sums
+  float* wp = lS + a.Hq * S;    // [P][Hq] weights 2^(m_p - M_h) / L_h
   int* bnd = (int*)(wp + a.Hq * P);  // [Hkv] split points
   {
-    const float* mp = a.ws_m + (size_t)b * a.Hq * S;
-    const float* lp = a.ws_l + (size_t)b * a.Hq * S;
-    for (int x = tid; x < a.Hq * S; x += 256) {
+    if (tid < n_ml) {
+      mS[tid] = m_pre0;
+      lS[tid] = l_pre0;
+    }
+    if (tid + 256 < n_ml) {
+      mS[tid + 256] = m_pre1;
+      lS[tid + 256] = l_pre1;
+    }
+    for (int x = tid + 512; x < n_ml; x += 256) {
       mS[x] = mp[x];
       lS[x] = lp[x];
     }
-    if (a.adaptive)
-      for (int x = tid; x < a.Hkv; x += 256) bnd[x] = a.ws_bnd[(size_t)b * a.Hkv + x];
+    if (a.adaptive) {
+      if (tid < a.Hkv) bnd[tid] = bnd_pre;
+      for (int x = tid + 256; x < a.Hkv; x += 256) bnd[x] = a.ws_bnd[(size_t)b * a.Hkv + x];
+    }
   }
   __syncthreads();
+  // branch-free: guarded LDS reads would each be waited for on their own
   for (int hh = tid; hh < a.Hq; hh += 256) {
     float M = -__builtin_inff();
     for (int x = 0; x < S; ++x) M = fmaxf(M, mS[hh * S + x]);
+    const bool none = M == -__builtin_inff();
     float L = 0.0f;
-    if (M != -__builtin_inff()) {
-      for (int x = 0; x < S; ++x) {
-        const float m = mS[hh * S + x];
-        if (m != -__builtin_inff()) L += lS[hh * S + x] * fast_exp2(m - M);
-      }
+    for (int x = 0; x < S; ++x) {
+      const float m = mS[hh * S + x];
+      const float l = lS[hh * S + x];
+      L += (none || m == -__builtin_inff()) ? 0.0f : l * fast_exp2(m - M);
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     hM[hh] = M;
     hInv[hh] = inv;
-    // a partition's records are relative to the max over its waves
     for (int p = 0; p < P; ++p) {
-      float Mp = -__builtin_inff();
-      for (int w = 0; w < NWP; ++w) Mp = fmaxf(Mp, mS[hh * S + p * NWP + w]);
-      wp[hh * P + p] = (Mp == -__builtin_inff() || inv == 0.0f) ? 0.0f : fast_exp2(Mp - M) * inv;
+      const float m = mS[hh * S + p];
+      wp[p * a.Hq + hh] = (m == -__builtin_inff() || inv == 0.0f) ? 0.0f : fast_exp2(m - M) * inv;
     }
   }
   __syncthreads();
 
-  if ((int)blockIdx.x < a.n_o_chunks) {
-    const int HPC = 256 / a.D;           // heads per chunk (D divides 256)
-    const int h0 = blockIdx.x * HPC;
-    float* wts = (float*)(bnd + a.Hkv);  // [HPC][S]
-    for (int x = tid; x < HPC * S; x += 256) {
-      const int hl = x / S, sl = x - hl * S;
-      const int hh = h0 + hl;
-      float w = 0.0f;
-      if (hh < a.Hq) {
-        const float m = mS[hh * S + sl];
-        w = (m == -__builtin_inff() || hInv[hh] == 0.0f) ? 0.0f : fast_exp2(m - hM[hh]) * hInv[hh];
-      }
-      wts[x] = w;
-    }
-    __syncthreads();
-    const int x = blockIdx.x * 256 + tid;
-    if (x >= a.Hq * a.D) return;
-    const int hh = x / a.D, d = x % a.D;
-    const float* o = a.ws_o + ((size_t)b * a.Hq + hh) * S * a.D + d;
-    const float* w = wts + (hh - h0) * S;
+  if (is_o) {
+    if (!o_live) return;
     // every partition writes its partial each launch (zeros when it read
     // nothing), so all are finite and summed unconditionally
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    int p = 0;
-    for (; p + 4 <= S; p += 4) {
-      float v[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) v[k] = o[(size_t)(p + k) * a.D];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) acc[k] += v[k] * w[p + k];
+    for (int k = 0; k < OPF; ++k) {
+      const float w = wp[min(k, S - 1) * a.Hq + oh];
+      acc[k & 3] += k < S ? ov[k] * w : 0.0f;
     }
-    for (; p < S; ++p) acc[0] += o[(size_t)p * a.D] * w[p];
+    for (int p = OPF; p < S; ++p) acc[p & 3] += o_src[(size_t)p * a.D] * wp[p * a.Hq + oh];
     const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    const size_t oi = ((size_t)b * a.Hq + hh) * a.D + d;
+    const size_t oi = ((size_t)b * a.Hq + oh) * a.D + od;
     if constexpr (Q_BF16)
       ((uint16_t*)a.out)[oi] = f32_to_bf16_rne(sum);
     else
       ((float*)a.out)[oi] = sum;
     return;
   }
-  if (a.mass == nullptr && a.head_mass == nullptr && a.mass_max == nullptr) return;
-  constexpr int NSUB = RING ? 2 : 1;
-  const int chunk = blockIdx.x - a.n_o_chunks;
-  const int i_cur = a.cur_pos[b];
-  const int lap_i = RING ? i_cur / a.C : 0;
-  // tiles with records: every tile of a ring; a linear cache's readable
-  // range, split over the partitions as the partial kernel split it
-  int tlo = 0, thi = a.NT, tpe = a.tpp;
-  if constexpr (!RING) {
-    const int lo = a.window > 0 ? i_cur - a.window + 1 : 0;
-    thi = max(0, min(a.NT, i_cur / kTile + 1));
-    tlo = a.window > 0 ? min(thi, max(lo, 0) / kTile) : 0;
-    tpe = max(1, (thi - tlo + P - 1) / P);
+  if (!m_live) return;
+
+  // ---- masses: heads in ascending order, HC at a time (head h sits at row
+  // (b, h / G) of the records, entry h % G); per-head masses
+  // read-modify-written alongside when asked for. Every tile of the range
+  // has records from this launch, relative to its partition's max. ----
+  const int p_even = min(max(tc - tlo, 0) / tpe, P - 1);  // partition of t under an even split
+  float acc[NSUB], mx[NSUB];
+#pragma unroll
+  for (int sb = 0; sb < NSUB; ++sb) {
+    acc[sb] = 0.0f;
+    mx[sb] = 0.0f;
   }
-  for (int t = tlo + chunk * 256 + tid; t < thi; t += a.n_mass_chunks * 256) {
-    // logical block of each sub-block of tile t (-1: none)
-    int blk[NSUB];
+  for (int hc = 0; hc < a.Hq; hc += HC) {
+    if (hc > 0) load_records(hc);
+    // weights of the chunk's heads: unconditional (clamped) LDS reads, a
+    // group's four heads at once when G % 4 == 0
+    float sc[HC];
+    if (G % 4 == 0) {
+      int bq[HC / 4];
 #pragma unroll
-    for (int sb = 0; sb < NSUB; ++sb) {
-      blk[sb] = t;
-      if constexpr (RING) {
-        const int lap = ((lap_i & 1) == sb) ? lap_i : lap_i - 1;
-        blk[sb] = lap < 0 ? -1 : lap * (a.C / kTile) + t;
-      }
-      if (blk[sb] >= a.nbmax) blk[sb] = -1;
-    }
-    float acc[NSUB], mx[NSUB];
+      for (int q = 0; q < HC / 4; ++q) bq[q] = bnd[min(hc + 4 * q, a.Hq - 4) / G];  // unused unless adaptive
+      f32x4 w4[HC / 4];
 #pragma unroll
-    for (int sb = 0; sb < NSUB; ++sb) {
-      acc[sb] = 0.0f;
-      mx[sb] = 0.0f;
-    }
-    // heads in ascending order, up to 32 (16 for rings) at a time with all
-    // their record loads in flight (head h sits at row (b, h / G) of the
-    // records, entry h % G); per-head masses read-modify-written alongside
-    // when asked for. Every tile of the range has records from this launch.
-    const int G = a.Hq / a.Hkv;
-    const int p_even = (t - tlo) / tpe;  // partition of t under an even split
-    auto part_of = [&](int gg) -> int { return a.adaptive ? (t < bnd[gg] ? 0 : 1) : p_even; };
-    constexpr int HC = RING ? 16 : 32;
-    for (int hc = 0; hc < a.Hq; hc += HC) {
-      float ev[NSUB][HC], sc[HC];
-      if (G % 4 == 0) {
-        // four heads of one group per 16-byte load; consecutive threads
-        // (tiles) read consecutive 16-byte pieces
-#pragma unroll
-        for (int q = 0; q < HC / 4; ++q) {
-          const int hh = hc + 4 * q;
-          f32x4 e4[NSUB];
-#pragma unroll
-          for (int sb = 0; sb < NSUB; ++sb) e4[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          int pp = 0;
-          if (hh < a.Hq) {
-            const int gg = hh / G;
-            const size_t row = ((size_t)b * a.Hkv + gg) * a.NT + t;
-            const int kk = hh - gg * G;
-            pp = part_of(gg);
-#pragma unroll
-            for (int sb = 0; sb < NSUB; ++sb) e4[sb] = *(const f32x4*)(a.ws_e + (row * NSUB + sb) * G + kk);
-          }
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            sc[4 * q + k] = hh + k < a.Hq ? wp[(hh + k) * P + pp] : 0.0f;
-#pragma unroll
-            for (int sb = 0; sb < NSUB; ++sb) ev[sb][4 * q + k] = e4[sb][k];
-          }
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < HC; ++k) {
-          const int hh = hc + k;
-          float w = 0.0f;
-#pragma unroll
-          for (int sb = 0; sb < NSUB; ++sb) ev[sb][k] = 0.0f;
-          if (hh < a.Hq) {
-            const int gg = hh / G;
-            const size_t row = ((size_t)b * a.Hkv + gg) * a.NT + t;
-            const int kk = hh - gg * G;
-            w = wp[hh * P + part_of(gg)];
-#pragma unroll
-            for (int sb = 0; sb < NSUB; ++sb) ev[sb][k] = a.ws_e[(row * NSUB + sb) * G + kk];
-          }
-          sc[k] = w;
-        }
+      for (int q = 0; q < HC / 4; ++q) {
+        const int hh = min(hc + 4 * q, a.Hq - 4);
+        const int pq = a.adaptive ? (tc < bq[q] ? 0 : 1) : p_even;
+        w4[q] = *(const f32x4*)(wp + pq * a.Hq + hh);
       }
 #pragma unroll
-      for (int sb = 0; sb < NSUB; ++sb) {
-        float* hp = a.head_mass ? a.head_mass + ((size_t)b * a.Hq + hc) * a.nbmax + (blk[sb] < 0 ? 0 : blk[sb])
-                                : nullptr;
+      for (int q = 0; q < HC / 4; ++q)
 #pragma unroll
-        for (int k = 0; k < HC; ++k) {
-          if (hc + k >= a.Hq) break;
-          const float v = ev[sb][k] * sc[k];
-          acc[sb] += v;
-          mx[sb] = fmaxf(mx[sb], v);
-        }
-        if (hp != nullptr && blk[sb] >= 0) {
-          // per-head masses, eight read-modify-writes in flight at a time
+        for (int k = 0; k < 4; ++k) sc[4 * q + k] = hc + 4 * q + k < a.Hq ? w4[q][k] : 0.0f;
+    } else {
+      int bk[HC];
 #pragma unroll
-          for (int k0 = 0; k0 < HC; k0 += 8) {
-            if (hc + k0 >= a.Hq) break;
-            float hv[8];
+      for (int k = 0; k < HC; ++k) bk[k] = bnd[min(hc + k, a.Hq - 1) / G];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) hv[k] = hc + k0 + k < a.Hq ? hp[(size_t)(k0 + k) * a.nbmax] : 0.0f;
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-              if (hc + k0 + k < a.Hq) hp[(size_t)(k0 + k) * a.nbmax] = hv[k] + ev[sb][k0 + k] * sc[k0 + k];
-          }
-        }
+      for (int k = 0; k < HC; ++k) {
+        const int hh = min(hc + k, a.Hq - 1);
+        const int pk = a.adaptive ? (tc < bk[k] ? 0 : 1) : p_even;
+        const float w = wp[pk * a.Hq + hh];
+        sc[k] = hc + k < a.Hq ? w : 0.0f;
       }
     }
 #pragma unroll
     for (int sb = 0; sb < NSUB; ++sb) {
-      if (blk[sb] < 0) continue;
-      const size_t mi = (size_t)b * a.nbmax + blk[sb];
-      if (a.mass != nullptr) a.mass[mi] += acc[sb];
-      if (a.mass_max != nullptr) a.mass_max[mi] = fmaxf(a.mass_max[mi], mx[sb]);
+#pragma unroll
+      for (int k = 0; k < HC; ++k) {
+        if (hc + k >= a.Hq) break;
+        const float v = ev[sb][k] * sc[k];
+        acc[sb] += v;
+        mx[sb] = fmaxf(mx[sb], v);
+      }
+      if (a.head_mass != nullptr && blk[sb] >= 0) {
+        float* hp = a.head_mass + ((size_t)b * a.Hq + hc) * a.nbmax + blk[sb];
+        // per-head masses, eight read-modify-writes in flight at a time
+#pragma unroll
+        for (int k0 = 0; k0 < HC; k0 += 8) {
+          if (hc + k0 >= a.Hq) break;
+          float hv[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) hv[k] = hp[(size_t)min(k0 + k, a.Hq - 1 - hc) * a.nbmax];
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if (hc + k0 + k < a.Hq) hp[(size_t)(k0 + k) * a.nbmax] = hv[k] + ev[sb][k0 + k] * sc[k0 + k];
+        }
+      }
     }
+  }
+#pragma unroll
+  for (int sb = 0; sb < NSUB; ++sb) {
+    if (blk[sb] < 0) continue;
+    const size_t mi = (size_t)b * a.nbmax + blk[sb];
+    if (a.mass != nullptr) a.mass[mi] = mass_old[sb] + acc[sb];
+    if (a.mass_max != nullptr) a.mass_max[mi] = fmaxf(max_old[sb], mx[sb]);
   }
 }
 
