@@ -71,7 +71,7 @@ Plan make_plan(const kvs_geom* g) {
   // partition, the block-sum records and the kept-tile list in LDS: bound the
   // partition so its LDS stays <= 64 KiB
   const int nw = kvs::kPartialWaves;
-  const int lds_fixed = nw * 256 + 4 + 2 * nw * 16;
+  const int lds_fixed = nw * 256 + 8 + 2 * nw * 16 + p.NT / 32 + 1;  // + the keep bitmap
   const int per_tile = p.G * (p.nsub + 1) + 1;
   const int tpp_lds = (kLdsBudgetFloats - lds_fixed) / per_tile;
   // the waves' outputs are merged in LDS over the same area, rows padded by 4
@@ -230,7 +230,7 @@ int decode_setup(const kvs_geom* g, const void* q, const void* k_cache, const vo
   c->ws_m = a->ws_m; c->ws_l = a->ws_l; c->ws_o = a->ws_o; c->ws_e = a->ws_e; c->cur_pos = cur_pos;
   c->ws_bnd = a->ws_bnd; c->ws_time = a->ws_time; c->rates = (float*)(ws + p.off_rates);
   c->n_wg = p.n_wg; c->S = p.S;
-  c->adaptive = !g->ring && p.nparts == 2 && !g->deterministic;
+  c->split_at_bnd = !g->ring && p.nparts == 2;
   c->out = out; c->mass = mass_accum;
   c->B = g->batch; c->Hq = g->n_q_heads; c->Hkv = g->n_kv_heads; c->D = g->head_dim; c->C = g->capacity; c->NT = p.NT;
   c->nbmax = g->n_blocks_max; c->tpp = p.tpp; c->nparts = p.nparts; c->window = g->window;

@@ -127,34 +127,38 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   const int wg_id = part + a.nparts * (g + a.Hkv * b);  // dispatch order
   const int i_cur = a.cur_pos[b];
   const int lo = a.window > 0 ? i_cur - a.window + 1 : (int)0x80000000;
-  // speeds of the two workgroups of an adaptive pair (see below), fetched with cur_pos
-  const bool adaptive = !RING && a.nparts == 2 && a.dyn && a.rates != nullptr;
+  // speeds of the two workgroups of a pair (see below), fetched with cur_pos
+  const bool split2 = !RING && a.nparts == 2;
+  const bool use_rates = split2 && a.dyn && a.rates != nullptr;
   float r0 = 1.0f, r1 = 1.0f;
-  if (adaptive) {
+  if (use_rates) {
     r0 = a.rates[(wg_id - part) & 7];
     r1 = a.rates[(wg_id - part + 1) & 7];
   }
+  const bool rates_ok = use_rates && r0 >= 0.5f && r0 <= 2.0f && r1 >= 0.5f && r1 <= 2.0f;  // NaN fails too
+  const float fsplit = rates_ok ? fminf(fmaxf(r0 / (r0 + r1), 0.35f), 0.65f) : 0.5f;
 
   // This workgroup's tiles [t0, t1). A ring reads every tile; a linear cache
-  // splits its readable range (window start .. current position) over the
-  // partitions, so a partly filled or compacted cache keeps every workgroup
-  // busy. Workgroups are placed on the chip's XCDs in dispatch order (id mod
-  // 8), and XCDs stream at measurably different rates; with two partitions
-  // and dynamic claiming the split point follows the rates the previous
-  // launches measured for the two workgroups' dispatch classes (clamped to
-  // 35..65 %), so both finish together. Otherwise the split is even.
+  // splits its readable range [gtb, gte) (window start .. current position)
+  // over the partitions, so a partly filled or compacted cache keeps every
+  // workgroup busy. Workgroups are placed on the chip's XCDs in dispatch
+  // order (id mod 8), and XCDs stream at measurably different rates; with two
+  // partitions and dynamic claiming the split follows the rates the previous
+  // launches measured for the two workgroups' dispatch classes (fraction
+  // fsplit, clamped to 35..65 %), so both finish together, else it is even.
+  // With a keep list and two partitions the split divides the kept tiles
+  // (worked out below), otherwise the tile range.
+  int gtb = 0, gte = a.NT;
   int t0, t1;
   if constexpr (RING) {
     t0 = part * a.tpp;
     t1 = min(t0 + a.tpp, a.NT);
   } else {
-    const int gte = max(0, min(a.NT, i_cur / kTile + 1));
-    const int gtb = a.window > 0 ? min(gte, max(lo, 0) / kTile) : 0;
-    if (adaptive) {
-      const bool ok = r0 >= 0.5f && r0 <= 2.0f && r1 >= 0.5f && r1 <= 2.0f;  // NaN fails too
-      const float f = ok ? fminf(fmaxf(r0 / (r0 + r1), 0.35f), 0.65f) : 0.5f;
+    gte = max(0, min(a.NT, i_cur / kTile + 1));
+    gtb = a.window > 0 ? min(gte, max(lo, 0) / kTile) : 0;
+    if (split2) {
       const int n = gte - gtb;
-      int bnd = gtb + (int)(f * (float)n + 0.5f);
+      int bnd = gtb + (int)(fsplit * (float)n + 0.5f);
       bnd = min(max(bnd, max(gtb, gte - a.tl_cap)), min(gte, gtb + a.tl_cap));
       t0 = part == 0 ? gtb : bnd;
       t1 = part == 0 ? bnd : gte;
@@ -167,43 +171,73 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
 
   // Fused append: the workgroup whose tiles hold the new position's slot
   // writes this KV head's part of the row there before anyone reads that tile.
-  int app_slot = -1;
-  if (a.app_k != nullptr && i_cur >= 0 && (RING || i_cur < a.C)) {
-    const int sl = RING ? i_cur % a.C : i_cur;
-    if (sl / kTile >= t0 && sl / kTile < t1) app_slot = sl;
-  }
-  const int app_tile = app_slot >= 0 ? app_slot / kTile : -1;
+  const int app_cand = (a.app_k != nullptr && i_cur >= 0 && (RING || i_cur < a.C)) ? (RING ? i_cur % a.C : i_cur) : -1;
+  const int app_cand_tile = app_cand >= 0 ? app_cand / kTile : -1;
 
   // LDS carve-up (16-byte aligned parts first): per-wave side data (FP8
   // scales, ring positions of the claimed tiles), then the kept-tile count,
-  // the claim counter, the append flag and the list entry of the appended
-  // tile, each wave's final max and sum per head, the block-sum records of
-  // every list entry (sums per sub-block and head, and the running max they
-  // are relative to) and the list of kept tiles. The waves' outputs are
-  // staged over the records at the end.
+  // the claim counter, the append flag, the list entry of the appended tile
+  // and the list split point, each wave's final max and sum per head, the
+  // block-sum records of every list entry (sums per sub-block and head, and
+  // the running max they are relative to), the list of kept tiles and the
+  // keep bitmap. The waves' outputs are staged over the records at the end.
   float* side_area = lds;                               // [NW][64 quads][4]
-  int* misc = (int*)(side_area + NW * 256);             // [4]
-  float* mw = (float*)(misc + 4);                       // [NW][16]
+  int* misc = (int*)(side_area + NW * 256);             // [8]
+  float* mw = (float*)(misc + 8);                       // [NW][16]
   float* lw = mw + NW * 16;                             // [NW][16]
   float* e_rec = lw + NW * 16;                          // [tl_cap][NSUB][G]
   float* m_rec = e_rec + (size_t)a.tl_cap * NSUB * G;   // [tl_cap][G]
   int* tlist = (int*)(m_rec + (size_t)a.tl_cap * G);    // [tl_cap]
+  uint32_t* kb = (uint32_t*)(tlist + a.tl_cap);         // [NT / 32 + 1]
   if (threadIdx.x == 0) {
     misc[1] = 0;
     misc[2] = 0;
     misc[3] = -1;
   }
 
-  // Tiles that can hold a readable key.
-  const int tb = t0, te = t1;
-
   // With a keep mask, or a list of block ids to re-attend, on a linear cache
-  // (tile = block), wave 0 compacts the partition's readable tiles into tlist,
-  // so other tiles are never read. Without either, the list is implicit:
-  // entry i is tile tb + i.
+  // (tile = block), the kept tiles of the range [r_lo, r_hi) (the pair's
+  // range with two partitions, else this workgroup's) become a bitmap, and
+  // wave 0 compacts this workgroup's kept tiles into tlist, so other tiles
+  // are never read. Without either, the list is implicit: entry i is tile
+  // t0 + i.
   const uint32_t* keep_b = a.keep ? a.keep + (size_t)b * a.kwords : nullptr;
   const bool use_ids = !RING && a.ids != nullptr;
   const bool use_list = !RING && (keep_b != nullptr || use_ids);
+  const int r_lo = split2 ? gtb : t0, r_hi = split2 ? gte : t1;
+  const int nwords = (r_hi - r_lo + 31) >> 5;
+  if (use_list) {
+    if (use_ids) {
+      // ids may repeat and come in any order
+      for (int w = threadIdx.x; w < nwords; w += NTH) kb[w] = 0u;
+      __syncthreads();
+      const int nid = min(max(a.n_ids[b], 0), a.ids_stride);
+      const int32_t* idb = a.ids + (size_t)b * a.ids_stride;
+      for (int k = threadIdx.x; k < nid; k += NTH) {
+        const int id = idb[k];
+        if (id >= r_lo && id < r_hi) atomicOr(&kb[(id - r_lo) >> 5], 1u << ((id - r_lo) & 31));
+      }
+    } else {
+      // the keep words, shifted to start at tile r_lo (tiles >= NBmax are kept)
+      for (int w = threadIdx.x; w < nwords; w += NTH) {
+        const int t = r_lo + 32 * w;
+        const int wa = t >> 5, sh = t & 31;
+        auto word = [&](int x) -> uint32_t {
+          if (x >= a.kwords) return ~0u;
+          uint32_t v = keep_b[x];
+          const int past = 32 * x + 32 - a.nbmax;   // bits at or past NBmax
+          if (past > 0) v |= past >= 32 ? ~0u : ~0u << (32 - past);
+          return v;
+        };
+        uint32_t v = word(wa) >> sh;
+        if (sh) v |= word(wa + 1) << (32 - sh);
+        const int nvalid = r_hi - t;
+        if (nvalid < 32) v &= (1u << nvalid) - 1u;
+        kb[w] = v;
+      }
+    }
+    __syncthreads();
+  }
 
   // Block-sum records of this (sequence, KV head): tile t, sub-block sb,
   // query head hh of the group, laid out [NT][NSUB][G], so one workgroup's
@@ -214,42 +248,66 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   const size_t hq0 = (size_t)g * G;
   auto e_index = [&](int t, int sb, int hh) -> size_t { return ((rec_row + t) * NSUB + sb) * G + hh; };
   if (use_list && wave == 0) {
-    // a block-id list becomes a bitmap over [tb, te) first (in the side-data
-    // area, unused until the loop); ids may repeat and come in any order
-    uint32_t* bm = (uint32_t*)side_area;
-    if (use_ids) {
-      for (int wd = lane; wd < ((te - tb + 31) >> 5); wd += 64) bm[wd] = 0u;
-      const int nid = min(max(a.n_ids[b], 0), a.ids_stride);
-      const int32_t* idb = a.ids + (size_t)b * a.ids_stride;
-      for (int k = lane; k < nid; k += 64) {
-        const int id = idb[k];
-        if (id >= tb && id < te) atomicOr(&bm[(id - tb) >> 5], 1u << ((id - tb) & 31));
+    if (split2) {
+      // two partitions divide the kept tiles: entry e_split (fsplit of them)
+      // starts partition 1; its tile is the split point
+      int n_kept = 0;
+      for (int c = 0; c < nwords; c += 64) {
+        int cnt = c + lane < nwords ? __popc(kb[c + lane]) : 0;
+        for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+        n_kept += cnt;
       }
+      int e_split = (int)(fsplit * (float)n_kept + 0.5f);
+      e_split = min(max(e_split, max(0, n_kept - a.tl_cap)), min(n_kept, a.tl_cap));
+      int bnd = r_hi, run = 0;
+      for (int c = 0; c < nwords && bnd == r_hi && e_split < n_kept; c += 64) {
+        const uint32_t wv = c + lane < nwords ? kb[c + lane] : 0u;
+        const int cnt = __popc(wv);
+        int incl = cnt;  // inclusive prefix over the lanes
+        for (int off = 1; off < 64; off <<= 1) {
+          const int y = __shfl_up(incl, off, 64);
+          if (lane >= off) incl += y;
+        }
+        const uint64_t hit = __ballot(run + incl > e_split && cnt > 0);
+        if (hit) {
+          const int ln = __builtin_ctzll(hit);
+          const uint32_t wsel = __shfl(wv, ln, 64);
+          int rank = e_split - (run + __shfl(incl, ln, 64) - __popc(wsel));  // set bits to skip
+          uint32_t x = wsel;
+          for (int it = 0; it < 32 && rank > 0; ++it, --rank) x &= x - 1u;  // drop the skipped bits
+          bnd = r_lo + 32 * (c + ln) + (x ? __builtin_ctz(x) : 31);
+        }
+        run += __shfl(incl, 63, 64);
+      }
+      t0 = part == 0 ? gtb : bnd;
+      t1 = part == 0 ? bnd : gte;
+      if (lane == 0) misc[4] = bnd;
     }
     int n = 0;
-    for (int c = tb; c < te; c += 64) {
+    for (int c = t0; c < t1; c += 64) {
       const int t = c + lane;
-      bool kept = false;
-      if (t < te) {
-        if (use_ids) kept = (bm[(t - tb) >> 5] >> ((t - tb) & 31)) & 1u;
-        else kept = t >= a.nbmax || ((keep_b[t >> 5] >> (t & 31)) & 1u);
-      }
+      const int rb = t - r_lo;
+      const bool kept = t < t1 && ((kb[rb >> 5] >> (rb & 31)) & 1u);
       const uint64_t m = __ballot(kept);
       if (kept) {
         const int e = n + __popcll(m & ((1ull << lane) - 1ull));
         tlist[e] = t;
-        if (t == app_tile) misc[3] = e;
-      }
-      if constexpr (SCORED) {
-        if (t < te && !kept) {
-          for (int hh = 0; hh < G; ++hh) a.ws_e[e_index(t, 0, hh)] = 0.0f;
-        }
+        if (t == app_cand_tile) misc[3] = e;
       }
       n += __popcll(m);
     }
     if (lane == 0) misc[0] = n;
   }
   __syncthreads();
+  if (use_list && split2) {
+    const int bnd = misc[4];
+    t0 = part == 0 ? gtb : bnd;
+    t1 = part == 0 ? bnd : gte;
+  }
+  // Tiles that can hold a readable key.
+  const int tb = t0, te = t1;
+  const int app_slot = (app_cand_tile >= tb && app_cand_tile < te) ? app_cand : -1;
+  const int app_tile = app_slot >= 0 ? app_cand_tile : -1;
   const int n_items = use_list ? misc[0] : te - tb;
   const int n_batches = (n_items + BATCH - 1) / BATCH;
   // batch holding the appended tile (-1: none here, or not read)
@@ -694,7 +752,7 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
     tm[1] = (float)(__builtin_amdgcn_s_memrealtime() - clk0);
   }
   if constexpr (SCORED) {
-    if (adaptive && part == 0 && threadIdx.x == 0) a.ws_bnd[(size_t)b * a.Hkv + g] = t1;
+    if (split2 && part == 0 && threadIdx.x == 0) a.ws_bnd[(size_t)b * a.Hkv + g] = t1;
   }
   __syncthreads();
   auto wg_max = [&](int hh) -> float {
@@ -707,7 +765,7 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   // workgroup max per head, are stored by the whole workgroup as contiguous
   // runs once every wave is done: global stores inside the streaming loop
   // would hold up the in-order completion count the tile loads are waited on
-  // with. The split point of an adaptive pair goes with them, for
+  // with. The split point of a two-partition range goes with them, for
   // kvs_combine's tile-to-partition map.
   if constexpr (SCORED) {
     const int per_e = NSUB * G;
@@ -719,6 +777,14 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
       const float v = (M == -__builtin_inff() || mr == -__builtin_inff()) ? 0.0f : e_rec[x] * fast_exp2(mr - M);
       const int t = use_list ? tlist[e] : tb + e;
       a.ws_e[e_index(t, 0, 0) + (x - e * per_e)] = v;
+    }
+    if (use_list) {
+      // tiles of the range that were not kept: zero records
+      for (int x = threadIdx.x; x < (te - tb) * per_e; x += NTH) {
+        const int tl = x / per_e;
+        const int rb = tb + tl - r_lo;
+        if (!((kb[rb >> 5] >> (rb & 31)) & 1u)) a.ws_e[e_index(tb + tl, 0, 0) + (x - tl * per_e)] = 0.0f;
+      }
     }
     __syncthreads();  // the record area is reused below
   }
@@ -878,7 +944,7 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
   const int n_ml = a.Hq * S;
   const float m_pre0 = mp[min(tid, n_ml - 1)], l_pre0 = lp[min(tid, n_ml - 1)];
   const float m_pre1 = mp[min(tid + 256, n_ml - 1)], l_pre1 = lp[min(tid + 256, n_ml - 1)];
-  const int bnd_pre = a.ws_bnd[(size_t)b * a.Hkv + min(tid, a.Hkv - 1)];  // used only if adaptive
+  const int bnd_pre = a.ws_bnd[(size_t)b * a.Hkv + min(tid, a.Hkv - 1)];  // used only when split at ws_bnd
   // O chunk: output (hh, d) of this thread
   const int xo = blockIdx.x * 256 + tid;
   const bool o_live = is_o && xo < a.Hq * a.D;
@@ -989,7 +1055,7 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
       mS[x] = mp[x];
       lS[x] = lp[x];
     }
-    if (a.adaptive) {
+    if (a.split_at_bnd) {
       if (tid < a.Hkv) bnd[tid] = bnd_pre;
       for (int x = tid + 256; x < a.Hkv; x += 256) bnd[x] = a.ws_bnd[(size_t)b * a.Hkv + x];
     }
@@ -1056,12 +1122,12 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
     if (G % 4 == 0) {
       int bq[HC / 4];
 #pragma unroll
-      for (int q = 0; q < HC / 4; ++q) bq[q] = bnd[min(hc + 4 * q, a.Hq - 4) / G];  // unused unless adaptive
+      for (int q = 0; q < HC / 4; ++q) bq[q] = bnd[min(hc + 4 * q, a.Hq - 4) / G];  // unused unless split at ws_bnd
       f32x4 w4[HC / 4];
 #pragma unroll
       for (int q = 0; q < HC / 4; ++q) {
         const int hh = min(hc + 4 * q, a.Hq - 4);
-        const int pq = a.adaptive ? (tc < bq[q] ? 0 : 1) : p_even;
+        const int pq = a.split_at_bnd ? (tc < bq[q] ? 0 : 1) : p_even;
         w4[q] = *(const f32x4*)(wp + pq * a.Hq + hh);
       }
 #pragma unroll
@@ -1075,7 +1141,7 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
 #pragma unroll
       for (int k = 0; k < HC; ++k) {
         const int hh = min(hc + k, a.Hq - 1);
-        const int pk = a.adaptive ? (tc < bk[k] ? 0 : 1) : p_even;
+        const int pk = a.split_at_bnd ? (tc < bk[k] ? 0 : 1) : p_even;
         const float w = wp[pk * a.Hq + hh];
         sc[k] = hc + k < a.Hq ? w : 0.0f;
       }

@@ -29,7 +29,7 @@ struct PartialArgs {
   float* ws_o;     // [B][Hq][P][D] unnormalised output
   float* ws_e;     // [B][Hkv][NT][NSUB][G] per-tile block sums, relative to the
                    // max of the partition's workgroup (its waves' ws_m)
-  int* ws_bnd;     // [B][Hkv] split point of an adaptive two-partition range
+  int* ws_bnd;     // [B][Hkv] split point of a two-partition range
   float* ws_time;  // [workgroups][kPartialWaves][2] tiles processed, clock ticks
   const float* rates;  // [8] relative streaming rate per dispatch class, or NULL
   int B, Hq, Hkv, G, C, NT, window, nbmax, kwords, tpp, nparts;
@@ -57,7 +57,7 @@ struct CombineArgs {
   float* rates;   // updated from ws_time by one workgroup, or NULL
   int n_wg;       // partial workgroups that wrote ws_time
   int S;          // partial slots per (sequence, head)
-  int adaptive;   // two partitions split at ws_bnd (else evenly)
+  int split_at_bnd;  // two partitions split at ws_bnd (else evenly by tiles)
   const int32_t* cur_pos;
   void* out;
   float* mass;
