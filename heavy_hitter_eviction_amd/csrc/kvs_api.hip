@@ -50,7 +50,7 @@ int check_geom(const kvs_geom* g) {
 }
 
 struct Plan {
-  int NT, tpp, nparts, nsub, G, S, tl_cap, n_wg, oslots;
+  int NT, tpp, nparts, nsub, G, S, tl_cap, n_wg, oslots, adapt;
   size_t off_m, off_l, off_o, off_e, off_bnd, off_time, off_rates, total;
   size_t lds_partial;
 };
@@ -90,12 +90,18 @@ Plan make_plan(const kvs_geom* g) {
   p.nparts = (p.NT + tpp - 1) / tpp;
   p.S = p.nparts;
   p.n_wg = p.nparts * pairs;
-  // two partitions split their range by measured rates (35..65 %): the list
-  // must hold the larger share
+  // a linear range's partitions may be weighted by the measured rates, each
+  // weight within 1/1.2 .. 1.2 of the others' mean: the list must then hold a
+  // share of up to 1.44 / (1.44 + nparts - 1) of the tiles; without the LDS
+  // for that the split stays even
   p.tl_cap = tpp;
-  if (p.nparts == 2 && !g->ring) {
-    const int cap = (int)((0.65 * p.NT) + 2);
-    if (cap <= tpp_lds && cap > p.tl_cap) p.tl_cap = cap;
+  p.adapt = 0;
+  if (!g->ring) {
+    const int need = (int)(1.44 * p.NT / (1.44 + p.nparts - 1)) + 2;
+    if (need <= tpp_lds) {
+      p.adapt = 1;
+      if (need > p.tl_cap) p.tl_cap = need;
+    }
   }
   const size_t bh = (size_t)g->batch * g->n_q_heads;
   p.off_m = 0;
@@ -103,7 +109,7 @@ Plan make_plan(const kvs_geom* g) {
   p.off_o = round256(p.off_l + bh * p.S * 4);
   p.off_e = round256(p.off_o + bh * p.S * g->head_dim * 4);
   p.off_bnd = round256(p.off_e + (size_t)g->batch * p.NT * p.nsub * g->n_q_heads * 4);
-  p.off_time = round256(p.off_bnd + (size_t)pairs * 4);
+  p.off_time = round256(p.off_bnd + (size_t)pairs * (p.nparts + 1) * 4);
   p.off_rates = round256(p.off_time + (size_t)p.n_wg * nw * 2 * 4);
   p.total = round256(p.off_rates + 8 * 4);
   size_t area = (size_t)p.tl_cap * per_tile;
@@ -224,13 +230,12 @@ int decode_setup(const kvs_geom* g, const void* q, const void* k_cache, const vo
   a->B = g->batch; a->Hq = g->n_q_heads; a->Hkv = g->n_kv_heads; a->G = p.G; a->C = g->capacity;
   a->NT = p.NT; a->window = g->window; a->nbmax = g->n_blocks_max;
   a->kwords = (g->n_blocks_max + 31) / 32; a->tpp = p.tpp; a->nparts = p.nparts;
-  a->dyn = g->deterministic ? 0 : 1; a->tl_cap = p.tl_cap; a->oslots = p.oslots;
+  a->dyn = g->deterministic ? 0 : 1; a->tl_cap = p.tl_cap; a->oslots = p.oslots; a->adapt = p.adapt;
   a->scale_log2 = g->softmax_scale * 1.4426950408889634f;
   *c = kvs::CombineArgs{};
   c->ws_m = a->ws_m; c->ws_l = a->ws_l; c->ws_o = a->ws_o; c->ws_e = a->ws_e; c->cur_pos = cur_pos;
   c->ws_bnd = a->ws_bnd; c->ws_time = a->ws_time; c->rates = (float*)(ws + p.off_rates);
   c->n_wg = p.n_wg; c->S = p.S;
-  c->split_at_bnd = !g->ring && p.nparts == 2;
   c->out = out; c->mass = mass_accum;
   c->B = g->batch; c->Hq = g->n_q_heads; c->Hkv = g->n_kv_heads; c->D = g->head_dim; c->C = g->capacity; c->NT = p.NT;
   c->nbmax = g->n_blocks_max; c->tpp = p.tpp; c->nparts = p.nparts; c->window = g->window;

@@ -125,29 +125,68 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   const bool hreal = h < G;
   const uint64_t clk0 = __builtin_amdgcn_s_memrealtime();
   const int wg_id = part + a.nparts * (g + a.Hkv * b);  // dispatch order
+  // fused append: the appending wave fetches the first 512 values of the new
+  // K and V rows right away (their address needs no cur_pos); it is decided
+  // further down whether this workgroup appends at all
+  const int app_n = a.Hkv * D;
+  const size_t app_rb = (size_t)b * app_n;
+  u32x4 app_k0[2], app_v0[2];  // 8 values per lane: bf16 in [0], f32 in [0..1]
+  if (KV == KV_FP8 && a.app_k != nullptr && wave == NW - 1 && 8 * lane < app_n) {
+    if (a.app_bf16) {
+      app_k0[0] = *(const u32x4*)((const uint16_t*)a.app_k + app_rb + 8 * lane);
+      app_v0[0] = *(const u32x4*)((const uint16_t*)a.app_v + app_rb + 8 * lane);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        app_k0[c] = *(const u32x4*)((const float*)a.app_k + app_rb + 8 * lane + 4 * c);
+        app_v0[c] = *(const u32x4*)((const float*)a.app_v + app_rb + 8 * lane + 4 * c);
+      }
+    }
+  }
   const int i_cur = a.cur_pos[b];
   const int lo = a.window > 0 ? i_cur - a.window + 1 : (int)0x80000000;
-  // speeds of the two workgroups of a pair (see below), fetched with cur_pos
-  const bool split2 = !RING && a.nparts == 2;
-  const bool use_rates = split2 && a.dyn && a.rates != nullptr;
-  float r0 = 1.0f, r1 = 1.0f;
-  if (use_rates) {
-    r0 = a.rates[(wg_id - part) & 7];
-    r1 = a.rates[(wg_id - part + 1) & 7];
+  // Partition weights (see below): the measured rate of each partition's
+  // dispatch class, fetched with cur_pos
+  const bool use_rates = !RING && a.dyn && a.adapt && a.rates != nullptr;
+  const int cls0 = (a.nparts * (g + a.Hkv * b)) & 7;  // class of partition 0
+  float wcls[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    float r = 1.0f;
+    if (use_rates) {
+      r = a.rates[c];
+      r = (r >= 0.5f && r <= 2.0f) ? fminf(fmaxf(r, 1.0f / 1.2f), 1.2f) : 1.0f;  // NaN -> 1
+    }
+    wcls[c] = r;
   }
-  const bool rates_ok = use_rates && r0 >= 0.5f && r0 <= 2.0f && r1 >= 0.5f && r1 <= 2.0f;  // NaN fails too
-  const float fsplit = rates_ok ? fminf(fmaxf(r0 / (r0 + r1), 0.35f), 0.65f) : 0.5f;
+  // weight of partitions [0, k): partition q belongs to class (cls0 + q) mod 8
+  auto wprefix = [&](int k) -> float {
+    float acc = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int d = (c - cls0) & 7;  // first partition of class c
+      const int cnt = k > d ? (k - 1 - d) / 8 + 1 : 0;
+      acc += wcls[c] * (float)cnt;
+    }
+    return acc;
+  };
+  const float wtot = wprefix(a.nparts);
+  // boundary q of n items split by weight (boundary 0 is 0, boundary nparts is n)
+  auto split_at = [&](int q, int n) -> int {
+    if (q >= a.nparts) return n;
+    return min(n, (int)((float)n * (wprefix(q) / wtot) + 0.5f));
+  };
 
   // This workgroup's tiles [t0, t1). A ring reads every tile; a linear cache
   // splits its readable range [gtb, gte) (window start .. current position)
   // over the partitions, so a partly filled or compacted cache keeps every
   // workgroup busy. Workgroups are placed on the chip's XCDs in dispatch
-  // order (id mod 8), and XCDs stream at measurably different rates; with two
-  // partitions and dynamic claiming the split follows the rates the previous
-  // launches measured for the two workgroups' dispatch classes (fraction
-  // fsplit, clamped to 35..65 %), so both finish together, else it is even.
-  // With a keep list and two partitions the split divides the kept tiles
-  // (worked out below), otherwise the tile range.
+  // order (id mod 8), and XCDs stream at measurably different rates; with
+  // dynamic claiming the split follows the rates the previous launches
+  // measured per dispatch class (clamped to +-20 % of the mean), so the
+  // partitions of a range finish together; otherwise it is even. With a keep
+  // list the split divides the kept tiles (worked out below), otherwise the
+  // tile range.
   int gtb = 0, gte = a.NT;
   int t0, t1;
   if constexpr (RING) {
@@ -156,17 +195,8 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   } else {
     gte = max(0, min(a.NT, i_cur / kTile + 1));
     gtb = a.window > 0 ? min(gte, max(lo, 0) / kTile) : 0;
-    if (split2) {
-      const int n = gte - gtb;
-      int bnd = gtb + (int)(fsplit * (float)n + 0.5f);
-      bnd = min(max(bnd, max(gtb, gte - a.tl_cap)), min(gte, gtb + a.tl_cap));
-      t0 = part == 0 ? gtb : bnd;
-      t1 = part == 0 ? bnd : gte;
-    } else {
-      const int tpe = max(1, (gte - gtb + a.nparts - 1) / a.nparts);
-      t0 = min(gte, gtb + part * tpe);
-      t1 = min(gte, t0 + tpe);
-    }
+    t0 = gtb + split_at(part, gte - gtb);
+    t1 = gtb + split_at(part + 1, gte - gtb);
   }
 
   // Fused append: the workgroup whose tiles hold the new position's slot
@@ -204,7 +234,7 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   const uint32_t* keep_b = a.keep ? a.keep + (size_t)b * a.kwords : nullptr;
   const bool use_ids = !RING && a.ids != nullptr;
   const bool use_list = !RING && (keep_b != nullptr || use_ids);
-  const int r_lo = split2 ? gtb : t0, r_hi = split2 ? gte : t1;
+  const int r_lo = gtb, r_hi = gte;
   const int nwords = (r_hi - r_lo + 31) >> 5;
   if (use_list) {
     if (use_ids) {
@@ -248,19 +278,20 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   const size_t hq0 = (size_t)g * G;
   auto e_index = [&](int t, int sb, int hh) -> size_t { return ((rec_row + t) * NSUB + sb) * G + hh; };
   if (use_list && wave == 0) {
-    if (split2) {
-      // two partitions divide the kept tiles: entry e_split (fsplit of them)
-      // starts partition 1; its tile is the split point
-      int n_kept = 0;
-      for (int c = 0; c < nwords; c += 64) {
-        int cnt = c + lane < nwords ? __popc(kb[c + lane]) : 0;
-        for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
-        n_kept += cnt;
-      }
-      int e_split = (int)(fsplit * (float)n_kept + 0.5f);
-      e_split = min(max(e_split, max(0, n_kept - a.tl_cap)), min(n_kept, a.tl_cap));
-      int bnd = r_hi, run = 0;
-      for (int c = 0; c < nwords && bnd == r_hi && e_split < n_kept; c += 64) {
+    // the partitions divide the kept tiles by weight: this one takes entries
+    // [e0, e1); its tiles run from the tile of entry e0 (the range start for
+    // entry 0) to the tile of entry e1 (the range end past the last entry)
+    int n_kept = 0;
+    for (int c = 0; c < nwords; c += 64) {
+      int cnt = c + lane < nwords ? __popc(kb[c + lane]) : 0;
+      for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+      n_kept += cnt;
+    }
+    auto tile_of_entry = [&](int e) -> int {
+      if (e <= 0) return r_lo;
+      if (e >= n_kept) return r_hi;
+      int found = r_hi, run = 0;
+      for (int c = 0; c < nwords && found == r_hi; c += 64) {
         const uint32_t wv = c + lane < nwords ? kb[c + lane] : 0u;
         const int cnt = __popc(wv);
         int incl = cnt;  // inclusive prefix over the lanes
@@ -268,20 +299,24 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
           const int y = __shfl_up(incl, off, 64);
           if (lane >= off) incl += y;
         }
-        const uint64_t hit = __ballot(run + incl > e_split && cnt > 0);
+        const uint64_t hit = __ballot(run + incl > e && cnt > 0);
         if (hit) {
           const int ln = __builtin_ctzll(hit);
           const uint32_t wsel = __shfl(wv, ln, 64);
-          int rank = e_split - (run + __shfl(incl, ln, 64) - __popc(wsel));  // set bits to skip
+          int rank = e - (run + __shfl(incl, ln, 64) - __popc(wsel));  // set bits to skip
           uint32_t x = wsel;
           for (int it = 0; it < 32 && rank > 0; ++it, --rank) x &= x - 1u;  // drop the skipped bits
-          bnd = r_lo + 32 * (c + ln) + (x ? __builtin_ctz(x) : 31);
+          found = r_lo + 32 * (c + ln) + (x ? __builtin_ctz(x) : 31);
         }
         run += __shfl(incl, 63, 64);
       }
-      t0 = part == 0 ? gtb : bnd;
-      t1 = part == 0 ? bnd : gte;
-      if (lane == 0) misc[4] = bnd;
+      return found;
+    };
+    t0 = part == 0 ? r_lo : tile_of_entry(split_at(part, n_kept));
+    t1 = part == a.nparts - 1 ? r_hi : tile_of_entry(split_at(part + 1, n_kept));
+    if (lane == 0) {
+      misc[4] = t0;
+      misc[5] = t1;
     }
     int n = 0;
     for (int c = t0; c < t1; c += 64) {
@@ -299,10 +334,9 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
     if (lane == 0) misc[0] = n;
   }
   __syncthreads();
-  if (use_list && split2) {
-    const int bnd = misc[4];
-    t0 = part == 0 ? gtb : bnd;
-    t1 = part == 0 ? bnd : gte;
+  if (use_list) {
+    t0 = misc[4];
+    t1 = misc[5];
   }
   // Tiles that can hold a readable key.
   const int tb = t0, te = t1;
@@ -636,17 +670,18 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   // the position, so each workgroup of the sequence derives it from the whole
   // row (identical values); this workgroup writes its own head's codes.
   auto append_row = [&]() {
-    const int n = a.Hkv * D;
-    const size_t rb = (size_t)b * n;
+    const int n = app_n;
+    const size_t rb = app_rb;
     const int sbf = a.app_bf16;
     float sk = 0.0f, sv = 0.0f;
     if constexpr (KV == KV_FP8) {
       float mk = 0.0f, mv = 0.0f;
       for (int i = 8 * lane; i < n; i += 8 * 64) {  // 8 values per lane and load (n % 8 == 0)
         float xk[8], xv[8];
+        const bool pre = i < 512;  // fetched at kernel entry
         if (sbf) {
-          const u32x4 wk = *(const u32x4*)((const uint16_t*)a.app_k + rb + i);
-          const u32x4 wv = *(const u32x4*)((const uint16_t*)a.app_v + rb + i);
+          const u32x4 wk = pre ? app_k0[0] : *(const u32x4*)((const uint16_t*)a.app_k + rb + i);
+          const u32x4 wv = pre ? app_v0[0] : *(const u32x4*)((const uint16_t*)a.app_v + rb + i);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             xk[2 * e] = bf16_lo(wk[e]);
@@ -657,8 +692,8 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
         } else {
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
-            const f32x4 fk = *(const f32x4*)((const float*)a.app_k + rb + i + 4 * c);
-            const f32x4 fv = *(const f32x4*)((const float*)a.app_v + rb + i + 4 * c);
+            const f32x4 fk = pre ? __builtin_bit_cast(f32x4, app_k0[c]) : *(const f32x4*)((const float*)a.app_k + rb + i + 4 * c);
+            const f32x4 fv = pre ? __builtin_bit_cast(f32x4, app_v0[c]) : *(const f32x4*)((const float*)a.app_v + rb + i + 4 * c);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               xk[4 * c + e] = fk[e];
@@ -752,7 +787,13 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
     tm[1] = (float)(__builtin_amdgcn_s_memrealtime() - clk0);
   }
   if constexpr (SCORED) {
-    if (split2 && part == 0 && threadIdx.x == 0) a.ws_bnd[(size_t)b * a.Hkv + g] = t1;
+    // boundaries of a linear range: partition q writes its start, the last
+    // one the end too
+    if (!RING && threadIdx.x == 0) {
+      int* bd = a.ws_bnd + ((size_t)b * a.Hkv + g) * (a.nparts + 1);
+      bd[part] = t0;
+      if (part == a.nparts - 1) bd[a.nparts] = t1;
+    }
   }
   __syncthreads();
   auto wg_max = [&](int hh) -> float {
@@ -944,7 +985,8 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
   const int n_ml = a.Hq * S;
   const float m_pre0 = mp[min(tid, n_ml - 1)], l_pre0 = lp[min(tid, n_ml - 1)];
   const float m_pre1 = mp[min(tid + 256, n_ml - 1)], l_pre1 = lp[min(tid + 256, n_ml - 1)];
-  const int bnd_pre = a.ws_bnd[(size_t)b * a.Hkv + min(tid, a.Hkv - 1)];  // used only when split at ws_bnd
+  const int n_bnd = a.Hkv * (P + 1);
+  const int bnd_pre = RING ? 0 : a.ws_bnd[(size_t)b * n_bnd + min(tid, n_bnd - 1)];
   // O chunk: output (hh, d) of this thread
   const int xo = blockIdx.x * 256 + tid;
   const bool o_live = is_o && xo < a.Hq * a.D;
@@ -1041,7 +1083,7 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
   float* mS = hInv + a.Hq;      // [Hq][P] partition maxima
   float* lS = mS + a.Hq * S;    // [Hq][P] partition sums
   float* wp = lS + a.Hq * S;    // [P][Hq] weights 2^(m_p - M_h) / L_h
-  int* bnd = (int*)(wp + a.Hq * P);  // [Hkv] split points
+  int* bnd = (int*)(wp + a.Hq * P);  // [Hkv][P + 1] partition boundaries (linear)
   {
     if (tid < n_ml) {
       mS[tid] = m_pre0;
@@ -1055,9 +1097,9 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
       mS[x] = mp[x];
       lS[x] = lp[x];
     }
-    if (a.split_at_bnd) {
-      if (tid < a.Hkv) bnd[tid] = bnd_pre;
-      for (int x = tid + 256; x < a.Hkv; x += 256) bnd[x] = a.ws_bnd[(size_t)b * a.Hkv + x];
+    if (!RING) {
+      if (tid < n_bnd) bnd[tid] = bnd_pre;
+      for (int x = tid + 256; x < n_bnd; x += 256) bnd[x] = a.ws_bnd[(size_t)b * n_bnd + x];
     }
   }
   __syncthreads();
@@ -1107,7 +1149,23 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
   // (b, h / G) of the records, entry h % G); per-head masses
   // read-modify-written alongside when asked for. Every tile of the range
   // has records from this launch, relative to its partition's max. ----
-  const int p_even = min(max(tc - tlo, 0) / tpe, P - 1);  // partition of t under an even split
+  // partition that produced tile tc's records for KV head gg: a ring splits
+  // evenly; a linear range at the stored boundaries (the last one at or
+  // below tc; boundary 0 is the range start)
+  auto part_of = [&](int gg) -> int {
+    if constexpr (RING) {
+      return min(tc / a.tpp, P - 1);
+    } else {
+      const int* bg = bnd + gg * (P + 1);
+      int base = 0;
+      for (int n = P; n > 1;) {
+        const int half = n >> 1;
+        base = bg[base + half] <= tc ? base + half : base;
+        n -= half;
+      }
+      return base;
+    }
+  };
   float acc[NSUB], mx[NSUB];
 #pragma unroll
   for (int sb = 0; sb < NSUB; ++sb) {
@@ -1120,29 +1178,27 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
     // group's four heads at once when G % 4 == 0
     float sc[HC];
     if (G % 4 == 0) {
-      int bq[HC / 4];
+      int pq[HC / 4];
 #pragma unroll
-      for (int q = 0; q < HC / 4; ++q) bq[q] = bnd[min(hc + 4 * q, a.Hq - 4) / G];  // unused unless split at ws_bnd
+      for (int q = 0; q < HC / 4; ++q) pq[q] = part_of(min(hc + 4 * q, a.Hq - 4) / G);
       f32x4 w4[HC / 4];
 #pragma unroll
       for (int q = 0; q < HC / 4; ++q) {
         const int hh = min(hc + 4 * q, a.Hq - 4);
-        const int pq = a.split_at_bnd ? (tc < bq[q] ? 0 : 1) : p_even;
-        w4[q] = *(const f32x4*)(wp + pq * a.Hq + hh);
+        w4[q] = *(const f32x4*)(wp + pq[q] * a.Hq + hh);
       }
 #pragma unroll
       for (int q = 0; q < HC / 4; ++q)
 #pragma unroll
         for (int k = 0; k < 4; ++k) sc[4 * q + k] = hc + 4 * q + k < a.Hq ? w4[q][k] : 0.0f;
     } else {
-      int bk[HC];
+      int pk[HC];
 #pragma unroll
-      for (int k = 0; k < HC; ++k) bk[k] = bnd[min(hc + k, a.Hq - 1) / G];
+      for (int k = 0; k < HC; ++k) pk[k] = part_of(min(hc + k, a.Hq - 1) / G);
 #pragma unroll
       for (int k = 0; k < HC; ++k) {
         const int hh = min(hc + k, a.Hq - 1);
-        const int pk = a.split_at_bnd ? (tc < bk[k] ? 0 : 1) : p_even;
-        const float w = wp[pk * a.Hq + hh];
+        const float w = wp[pk[k] * a.Hq + hh];
         sc[k] = hc + k < a.Hq ? w : 0.0f;
       }
     }

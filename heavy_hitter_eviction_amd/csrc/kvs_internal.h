@@ -29,13 +29,14 @@ struct PartialArgs {
   float* ws_o;     // [B][Hq][P][D] unnormalised output
   float* ws_e;     // [B][Hkv][NT][NSUB][G] per-tile block sums, relative to the
                    // max of the partition's workgroup (its waves' ws_m)
-  int* ws_bnd;     // [B][Hkv] split point of a two-partition range
+  int* ws_bnd;     // [B][Hkv][P + 1] partition boundaries of a linear range
   float* ws_time;  // [workgroups][kPartialWaves][2] tiles processed, clock ticks
   const float* rates;  // [8] relative streaming rate per dispatch class, or NULL
   int B, Hq, Hkv, G, C, NT, window, nbmax, kwords, tpp, nparts;
   int ids_stride;
   int dyn;     // 1: waves claim tiles dynamically; 0: fixed round-robin order
   int tl_cap;  // LDS capacity of the kept-tile list (>= any partition's tiles)
+  int adapt;   // 1: partitions may be weighted by the measured rates (tl_cap allows it)
   int oslots;  // LDS output slots of the wave merge: kPartialWaves or kPartialWaves / 2
   float scale_log2;
   // Fused append: row b of app_k / app_v ([B][Hkv*D], bf16 if app_bf16, else
@@ -57,7 +58,6 @@ struct CombineArgs {
   float* rates;   // updated from ws_time by one workgroup, or NULL
   int n_wg;       // partial workgroups that wrote ws_time
   int S;          // partial slots per (sequence, head)
-  int split_at_bnd;  // two partitions split at ws_bnd (else evenly by tiles)
   const int32_t* cur_pos;
   void* out;
   float* mass;
@@ -70,7 +70,7 @@ struct CombineArgs {
 // and sum, per (head, partition) record weights, the split points, the
 // O-merge weights of its heads, or the rate accumulators (16 floats).
 inline size_t combine_lds_bytes(int Hq, int Hkv, int D, int S, int P) {
-  const size_t f = 2 * (size_t)Hq + 2 * (size_t)Hq * S + (size_t)Hq * P + Hkv + (size_t)(256 / D) * S;
+  const size_t f = 2 * (size_t)Hq + 2 * (size_t)Hq * S + (size_t)Hq * P + (size_t)Hkv * (P + 1) + (size_t)(256 / D) * S;
   return (f < 16 ? 16 : f) * sizeof(float);
 }
 
