@@ -187,7 +187,14 @@ KVS_API int kvs_decode_workspace_bytes(const kvs_geom* geom, size_t* bytes);
  *               replaces the window, so the two are never combined)
  *   out         [B][Hq][d] q_dtype
  *   mass_accum  [B][NBmax] float or NULL
- *   workspace   device scratch of at least kvs_decode_workspace_bytes()
+ *   workspace   device scratch of at least kvs_decode_workspace_bytes(),
+ *               owned by the caller; calls that share one must not overlap.
+ *               Besides per-call partials it keeps, from call to call, the
+ *               streaming rate measured for each of the GPU's dispatch
+ *               classes (workgroup id mod 8); in dynamic mode the next call
+ *               splits each sequence's tiles over its workgroups by those
+ *               rates. Any initial content is valid (unreadable rates count
+ *               as equal); the rates never change a result beyond rounding.
  *
  * Preconditions the library cannot check (unspecified results, never a
  * fault): the current token is readable (so no row is all-masked); a ring
