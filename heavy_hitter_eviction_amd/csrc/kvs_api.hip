@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/kvs.h"
 #include "kvs_internal.h"
 
@@ -51,7 +53,7 @@ int check_geom(const kvs_geom* g) {
 
 struct Plan {
   int NT, tpp, nparts, nsub, G, S, tl_cap, n_wg, oslots, adapt;
-  size_t off_m, off_l, off_o, off_e, off_bnd, off_time, off_rates, total;
+  size_t off_m, off_l, off_o, off_e, off_bnd, off_time, off_rates, off_cnt, total;
   size_t lds_partial;
 };
 
@@ -83,7 +85,7 @@ Plan make_plan(const kvs_geom* g) {
   // over the nparts * nw partials in LDS: bound them to 48 KiB
   while (true) {
     const int np = (p.NT + tpp - 1) / tpp;
-    if (kvs::combine_lds_bytes(g->n_q_heads, g->n_kv_heads, g->head_dim, np, np) <= 49152) break;
+    if (kvs::combine_lds_bytes(g->n_q_heads, g->n_kv_heads, np, np) <= 49152) break;
     tpp *= 2;
   }
   p.tpp = tpp;
@@ -111,14 +113,30 @@ Plan make_plan(const kvs_geom* g) {
   p.off_bnd = round256(p.off_e + (size_t)g->batch * p.NT * p.nsub * g->n_q_heads * 4);
   p.off_time = round256(p.off_bnd + (size_t)pairs * (p.nparts + 1) * 4);
   p.off_rates = round256(p.off_time + (size_t)p.n_wg * nw * 2 * 4);
-  p.total = round256(p.off_rates + 8 * 4);
+  p.off_cnt = round256(p.off_rates + 8 * 4);
+  p.total = round256(p.off_cnt + (size_t)pairs * 8);
   size_t area = (size_t)p.tl_cap * per_tile;
   if (area < (size_t)p.oslots * orow) area = (size_t)p.oslots * orow;
+  // the output merge of a (sequence, KV head) stages 3 G nparts + 2 G floats
+  // over the same area
+  const size_t merge_f = 3 * (size_t)p.G * p.nparts + 2 * (size_t)p.G;
+  if (area < merge_f) area = merge_f;
   p.lds_partial = 4 * ((size_t)lds_fixed + area);
   return p;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? KVS_OK : KVS_EHIP; }
+
+// Per-call token for the partial kernel's completion counters (never 0, so a
+// zero-filled counter is never mistaken for a live count).
+uint32_t next_token() {
+  static std::atomic<uint32_t> counter{0};
+  uint32_t t;
+  do {
+    t = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+  } while (t == 0);
+  return t;
+}
 
 }  // namespace
 
@@ -226,6 +244,9 @@ int decode_setup(const kvs_geom* g, const void* q, const void* k_cache, const vo
   a->ws_m = (float*)(ws + p.off_m); a->ws_l = (float*)(ws + p.off_l);
   a->ws_o = (float*)(ws + p.off_o); a->ws_e = (float*)(ws + p.off_e);
   a->ws_bnd = (int*)(ws + p.off_bnd); a->ws_time = (float*)(ws + p.off_time);
+  a->pair_cnt = (unsigned long long*)(ws + p.off_cnt);
+  a->token = next_token();
+  a->out = out;
   a->rates = (const float*)(ws + p.off_rates);
   a->B = g->batch; a->Hq = g->n_q_heads; a->Hkv = g->n_kv_heads; a->G = p.G; a->C = g->capacity;
   a->NT = p.NT; a->window = g->window; a->nbmax = g->n_blocks_max;
@@ -236,10 +257,9 @@ int decode_setup(const kvs_geom* g, const void* q, const void* k_cache, const vo
   c->ws_m = a->ws_m; c->ws_l = a->ws_l; c->ws_o = a->ws_o; c->ws_e = a->ws_e; c->cur_pos = cur_pos;
   c->ws_bnd = a->ws_bnd; c->ws_time = a->ws_time; c->rates = (float*)(ws + p.off_rates);
   c->n_wg = p.n_wg; c->S = p.S;
-  c->out = out; c->mass = mass_accum;
-  c->B = g->batch; c->Hq = g->n_q_heads; c->Hkv = g->n_kv_heads; c->D = g->head_dim; c->C = g->capacity; c->NT = p.NT;
+  c->mass = mass_accum;
+  c->B = g->batch; c->Hq = g->n_q_heads; c->Hkv = g->n_kv_heads; c->C = g->capacity; c->NT = p.NT;
   c->nbmax = g->n_blocks_max; c->tpp = p.tpp; c->nparts = p.nparts; c->window = g->window;
-  c->n_o_chunks = (g->n_q_heads * g->head_dim + 255) / 256;
   c->n_mass_chunks = (p.NT + 255) / 256;
   *kv = fp8 ? kvs::KV_FP8 : g->kv_dtype == KVS_BF16 ? kvs::KV_BF16 : kvs::KV_F32;
   return KVS_OK;
@@ -273,7 +293,7 @@ int kvs_decode_partial(KVS_DECODE_ARGS) {
 int kvs_decode_combine(KVS_DECODE_ARGS) {
   KVS_DECODE_SETUP
   (void)kv;
-  return hip_status(kvs::launch_combine(c, g->ring != 0, g->q_dtype == KVS_BF16, s));
+  return hip_status(kvs::launch_combine(c, g->ring != 0, s));
 }
 
 int kvs_decode_attn_scored(KVS_DECODE_ARGS) {
@@ -281,7 +301,7 @@ int kvs_decode_attn_scored(KVS_DECODE_ARGS) {
   hipError_t e = kvs::launch_partial(kv, g->head_dim, a, mass_accum != nullptr, g->ring != 0,
                                      p.lds_partial, s);
   if (e != hipSuccess) return KVS_EHIP;
-  return hip_status(kvs::launch_combine(c, g->ring != 0, g->q_dtype == KVS_BF16, s));
+  return hip_status(kvs::launch_combine(c, g->ring != 0, s));
 }
 
 int kvs_decode_attn_profiled(const kvs_geom* g, const void* q, const void* k_cache, const void* v_cache,
@@ -303,7 +323,7 @@ int kvs_decode_attn_profiled(const kvs_geom* g, const void* q, const void* k_cac
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = kvs::launch_partial(kv, g->head_dim, a, scored, g->ring != 0, p.lds_partial, s);
   if (e != hipSuccess) return KVS_EHIP;
-  return hip_status(kvs::launch_combine(c, g->ring != 0, g->q_dtype == KVS_BF16, s));
+  return hip_status(kvs::launch_combine(c, g->ring != 0, s));
 }
 
 }  // extern "C"
@@ -348,7 +368,7 @@ int kvs_append_decode_attn(KVS_APPEND_DECODE_ARGS) {
   hipError_t e = kvs::launch_partial(kv, g->head_dim, a, mass_accum != nullptr, g->ring != 0,
                                      p.lds_partial, s);
   if (e != hipSuccess) return KVS_EHIP;
-  return hip_status(kvs::launch_combine(c, g->ring != 0, g->q_dtype == KVS_BF16, s));
+  return hip_status(kvs::launch_combine(c, g->ring != 0, s));
 }
 
 int kvs_reattend_blocks(const kvs_geom* g, const void* q, const void* k_cache, const void* v_cache,
@@ -372,7 +392,7 @@ int kvs_reattend_blocks(const kvs_geom* g, const void* q, const void* k_cache, c
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = kvs::launch_partial(kv, g->head_dim, a, mass_accum != nullptr, false, p.lds_partial, s);
   if (e != hipSuccess) return KVS_EHIP;
-  return hip_status(kvs::launch_combine(c, false, g->q_dtype == KVS_BF16, s));
+  return hip_status(kvs::launch_combine(c, false, s));
 }
 
 int kvs_update_sidecar(float* mass_accum, float* attended, float* ema, float* cum, float* traj,

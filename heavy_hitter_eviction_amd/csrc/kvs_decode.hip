@@ -97,6 +97,47 @@ __device__ __forceinline__ int qk_dim(int t, int kg) {
   return (t / EPC) * 4 * EPC + kg * EPC + t % EPC;
 }
 
+// ---- merging partitions (shared by kvs_combine and the partial kernel's
+// own merge of a (sequence, KV head)'s outputs) ----
+// One head's merge weights from its partitions' maxima m[p] and sums l[p]:
+// M = max_p m_p, L = sum_p l_p 2^(m_p - M) in ascending p, w_p = 2^(m_p - M) / L
+// (stored at w[p * wst]; 0 for an empty partition). Branch-free: guarded LDS
+// reads would each be waited for on their own.
+__device__ __forceinline__ void merge_weights(const float* m, const float* l, int P, float* w, int wst,
+                                              float* M_out, float* inv_out) {
+  float M = -__builtin_inff();
+  for (int x = 0; x < P; ++x) M = fmaxf(M, m[x]);
+  const bool none = M == -__builtin_inff();
+  float L = 0.0f;
+  for (int x = 0; x < P; ++x) {
+    const float mx = m[x];
+    L += (none || mx == -__builtin_inff()) ? 0.0f : l[x] * fast_exp2(mx - M);
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  *M_out = M;
+  *inv_out = inv;
+  for (int x = 0; x < P; ++x) {
+    const float mx = m[x];
+    w[x * wst] = (mx == -__builtin_inff() || inv == 0.0f) ? 0.0f : fast_exp2(mx - M) * inv;
+  }
+}
+
+// sum_p o_p w_p over P partitions with four accumulators (p mod 4) in
+// ascending p; the first OPF values are given (loaded with clamped indices,
+// terms past P are +0), the rest come from ldo(p). Every partition writes its
+// partial each launch (zeros when it read nothing), so all are finite.
+template <int OPF, class LdO>
+__device__ __forceinline__ float merge_o(const float (&ov)[OPF], LdO ldo, const float* w, int wst, int P) {
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < OPF; ++k) {
+    const float wk = w[min(k, P - 1) * wst];
+    acc[k & 3] += k < P ? ov[k] * wk : 0.0f;
+  }
+  for (int p = OPF; p < P; ++p) acc[p & 3] += ldo(p) * w[p * wst];
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
 template <int KV>
 struct Pipe {
   // tile buffers per wave (depth - 1 tiles in flight); also the tiles a wave
@@ -880,7 +921,10 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
     } else {
       for (int sl = 0; sl < NW / 2; ++sl) o += ow[(sl * G + hh) * DP + dd];
     }
-    a.ws_o[((pbase + hh) * a.nparts + part) * D + dd] = o;
+    // the partials go to memory past the (per-XCD, non-coherent) L2, for
+    // the merge below: relaxed system-scope stores are written through
+    __hip_atomic_store(&a.ws_o[((pbase + hh) * a.nparts + part) * D + dd], o, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_SYSTEM);
   }
   for (int hh = threadIdx.x; hh < G; hh += NTH) {
     const float M = wg_max(hh);
@@ -889,37 +933,91 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
       const float m = mw[w * 16 + hh];
       if (m != -__builtin_inff()) l += lw[w * 16 + hh] * fast_exp2(m - M);
     }
-    a.ws_m[(pbase + hh) * a.nparts + part] = M;
-    a.ws_l[(pbase + hh) * a.nparts + part] = l;
+    __hip_atomic_store(&a.ws_m[(pbase + hh) * a.nparts + part], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(&a.ws_l[(pbase + hh) * a.nparts + part], l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+
+  // ---- the last partition of this (sequence, KV head) to finish merges the
+  // group's outputs, so the output needs no further launch. The count is
+  // tagged with the call's token in its upper half: a word left by another
+  // call (or never written) restarts at 1, and the merging workgroup leaves
+  // it at (token, 0) for a replay of the same call. ----
+  // The partials are write-through stores; once every wave has them
+  // acknowledged (vmcnt 0) they are in memory, so the count needs no cache
+  // writeback, and the merging workgroup reads them past its caches.
+  // (Device-scope fences here write back the whole L2 per workgroup and
+  // cost tens of microseconds per launch.)
+  if (a.pair_cnt != nullptr) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores acknowledged
+    __syncthreads();
+    unsigned long long* cp = a.pair_cnt + (size_t)b * a.Hkv + g;
+    const unsigned long long tok = (unsigned long long)a.token << 32;
+    if (threadIdx.x == 0) {
+      // system scope: performed at memory, past every XCD's L2
+      unsigned long long cur = __hip_atomic_load(cp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      int count = 0;
+      // each failed exchange is another partition's success: at most nparts - 1
+      for (int it = 0; it <= a.nparts; ++it) {
+        const unsigned long long next = (cur & 0xFFFFFFFF00000000ull) == tok ? cur + 1ull : (tok | 1ull);
+        if (__hip_atomic_compare_exchange_strong(cp, &cur, next, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_SYSTEM)) {
+          count = (int)(next & 0xFFFFFFFFull);
+          break;
+        }
+      }
+      misc[6] = count;
+    }
+    __syncthreads();
+    if (misc[6] == a.nparts) {
+      const int P = a.nparts;
+      auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM); };
+      float* mT = e_rec;          // [G][P] partition maxima   (record area, free now)
+      float* lT = mT + G * P;     // [G][P] partition sums
+      float* wT = lT + G * P;     // [P][G] weights
+      float* hMt = wT + G * P;    // [G]
+      float* hIt = hMt + G;       // [G]
+      for (int x = threadIdx.x; x < G * P; x += NTH) {
+        mT[x] = ld(a.ws_m + pbase * P + x);
+        lT[x] = ld(a.ws_l + pbase * P + x);
+      }
+      __syncthreads();
+      for (int hh = threadIdx.x; hh < G; hh += NTH) merge_weights(mT + hh * P, lT + hh * P, P, wT + hh, G, &hMt[hh], &hIt[hh]);
+      __syncthreads();
+      for (int x = threadIdx.x; x < G * D; x += NTH) {
+        const int hh = x / D, dd = x % D;
+        const float* o_src = a.ws_o + (pbase + hh) * P * D + dd;
+        float ov[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) ov[k] = ld(o_src + (size_t)min(k, P - 1) * D);
+        const float sum = merge_o(ov, [&](int p) { return ld(o_src + (size_t)p * D); }, wT + hh, G, P);
+        const size_t oi = (pbase + hh) * D + dd;
+        if constexpr (KV != KV_F32)
+          ((uint16_t*)a.out)[oi] = f32_to_bf16_rne(sum);
+        else
+          ((float*)a.out)[oi] = sum;
+      }
+      if (threadIdx.x == 0) __hip_atomic_store(cp, tok, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Combine: grid (n_o_chunks + n_mass_chunks + 1, B), 256 threads.
+// Combine: grid (n_mass_chunks + 1, B), 256 threads: the block masses.
 // Every workgroup first reduces, per head h of its sequence, the partitions'
-// partials to M_h = max_p m_p and L_h = sum_p l_p 2^(m_p - M_h). O chunks then
-// form O_h = sum_p o_p 2^(m_p - M_h) / L_h for 256 / D heads each; mass chunks
-// add, per tile and sub-block, sum_h E 2^(m_p(tile) - M_h) / L_h over the heads
-// in ascending order into mass_accum, E being the tile's record relative to
-// its partition's max. The last column (sequence 0 only) refreshes the
-// per-class streaming rates from the partial kernel's clock records.
+// partials to M_h = max_p m_p and L_h = sum_p l_p 2^(m_p - M_h); then each
+// thread adds, for its tile and sub-block, sum_h E 2^(m_p(tile) - M_h) / L_h
+// over the heads in ascending order into mass_accum, E being the tile's
+// record relative to its partition's max. (The outputs were merged by the
+// partial kernel.) The last column (sequence 0 only) refreshes the per-class
+// streaming rates from the partial kernel's clock records.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float wave_max64(float v) {
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
-}
-__device__ __forceinline__ float wave_sum64(float v) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
-template <bool RING, bool Q_BF16>
+template <bool RING>
 __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
   extern __shared__ float lds[];
   const int b = blockIdx.y;
   const int S = a.S;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int n_work = a.n_o_chunks + a.n_mass_chunks;
+  const int n_work = a.n_mass_chunks;
 
   if ((int)blockIdx.x >= n_work) {
     // ---- rates: per dispatch class (workgroup id mod 8), tiles per tick of
@@ -966,16 +1064,12 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
   }
 
   // One partial per partition (S == nparts). Each workgroup first issues the
-  // global loads that need nothing from the shared prologue (its O partials,
-  // or its tile's records and current masses), then builds the per-head
-  // tables, then finishes: one round of load latency instead of three.
+  // global loads that need nothing from the shared prologue (its tile's
+  // records and current masses), then builds the per-head tables, then
+  // finishes: one round of load latency instead of three.
   const int P = S;
   constexpr int NSUB = RING ? 2 : 1;
   constexpr int HC = RING ? 16 : 32;   // heads per record chunk
-  constexpr int OPF = 8;               // O partials prefetched per output
-  const bool is_o = (int)blockIdx.x < a.n_o_chunks;
-  const bool any_mass = a.mass != nullptr || a.head_mass != nullptr || a.mass_max != nullptr;
-  if (!is_o && !any_mass) return;
   const int G = a.Hq / a.Hkv;
 
   // ---- independent loads ----
@@ -987,16 +1081,6 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
   const float m_pre1 = mp[min(tid + 256, n_ml - 1)], l_pre1 = lp[min(tid + 256, n_ml - 1)];
   const int n_bnd = a.Hkv * (P + 1);
   const int bnd_pre = RING ? 0 : a.ws_bnd[(size_t)b * n_bnd + min(tid, n_bnd - 1)];
-  // O chunk: output (hh, d) of this thread
-  const int xo = blockIdx.x * 256 + tid;
-  const bool o_live = is_o && xo < a.Hq * a.D;
-  const int oh = o_live ? xo / a.D : 0, od = o_live ? xo % a.D : 0;
-  const float* o_src = a.ws_o + ((size_t)b * a.Hq + oh) * S * a.D + od;
-  // loads are unconditional (indices clamped into range, unused values
-  // masked later): conditional loads make the compiler wait for each one
-  float ov[OPF];
-#pragma unroll
-  for (int k = 0; k < OPF; ++k) ov[k] = o_src[(size_t)min(k, S - 1) * a.D];
   // mass chunk: tile t of this thread (tiles with records: every tile of a
   // ring; a linear cache's readable range), its logical blocks, the records
   // of its first HC heads and the current masses of its blocks
@@ -1010,7 +1094,7 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
       tlo = min(thi0, max(ic - a.window + 1, 0) / kTile);
     }
   }
-  const int t = tlo + ((int)blockIdx.x - a.n_o_chunks) * 256 + tid;
+  const int t = tlo + (int)blockIdx.x * 256 + tid;
   // records of heads past Hq (clamped duplicates) get weight 0; a dead
   // thread's values are never used
   const int tc = min(max(t, 0), a.NT - 1);
@@ -1056,7 +1140,7 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
     thi = max(0, min(a.NT, i_cur / kTile + 1));
     tpe = max(1, (thi - tlo + P - 1) / P);
   }
-  const bool m_live = !is_o && t < thi;
+  const bool m_live = t < thi;
   const int lap_i = RING ? i_cur / a.C : 0;
   int blk[NSUB];
 #pragma unroll
@@ -1103,46 +1187,10 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
     }
   }
   __syncthreads();
-  // branch-free: guarded LDS reads would each be waited for on their own
-  for (int hh = tid; hh < a.Hq; hh += 256) {
-    float M = -__builtin_inff();
-    for (int x = 0; x < S; ++x) M = fmaxf(M, mS[hh * S + x]);
-    const bool none = M == -__builtin_inff();
-    float L = 0.0f;
-    for (int x = 0; x < S; ++x) {
-      const float m = mS[hh * S + x];
-      const float l = lS[hh * S + x];
-      L += (none || m == -__builtin_inff()) ? 0.0f : l * fast_exp2(m - M);
-    }
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    hM[hh] = M;
-    hInv[hh] = inv;
-    for (int p = 0; p < P; ++p) {
-      const float m = mS[hh * S + p];
-      wp[p * a.Hq + hh] = (m == -__builtin_inff() || inv == 0.0f) ? 0.0f : fast_exp2(m - M) * inv;
-    }
-  }
+  for (int hh = tid; hh < a.Hq; hh += 256)
+    merge_weights(mS + hh * S, lS + hh * S, P, wp + hh, a.Hq, &hM[hh], &hInv[hh]);
   __syncthreads();
 
-  if (is_o) {
-    if (!o_live) return;
-    // every partition writes its partial each launch (zeros when it read
-    // nothing), so all are finite and summed unconditionally
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < OPF; ++k) {
-      const float w = wp[min(k, S - 1) * a.Hq + oh];
-      acc[k & 3] += k < S ? ov[k] * w : 0.0f;
-    }
-    for (int p = OPF; p < S; ++p) acc[p & 3] += o_src[(size_t)p * a.D] * wp[p * a.Hq + oh];
-    const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    const size_t oi = ((size_t)b * a.Hq + oh) * a.D + od;
-    if constexpr (Q_BF16)
-      ((uint16_t*)a.out)[oi] = f32_to_bf16_rne(sum);
-    else
-      ((float*)a.out)[oi] = sum;
-    return;
-  }
   if (!m_live) return;
 
   // ---- masses: heads in ascending order, HC at a time (head h sits at row
@@ -1269,19 +1317,14 @@ hipError_t launch_partial(int kv, int d, const PartialArgs& a, bool scored, bool
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_combine(const CombineArgs& a, bool ring, bool q_bf16, hipStream_t st) {
-  const bool mass_work = a.mass || a.head_mass || a.mass_max;
-  CombineArgs c = a;
-  if (!mass_work) c.n_mass_chunks = 0;
-  dim3 grid(c.n_o_chunks + c.n_mass_chunks + 1, c.B), block(256);
-  const size_t lds = combine_lds_bytes(c.Hq, c.Hkv, c.D, c.S, c.nparts);
-  if (ring) {
-    if (q_bf16) hipLaunchKernelGGL((kvs_combine<true, true>), grid, block, lds, st, c);
-    else hipLaunchKernelGGL((kvs_combine<true, false>), grid, block, lds, st, c);
-  } else {
-    if (q_bf16) hipLaunchKernelGGL((kvs_combine<false, true>), grid, block, lds, st, c);
-    else hipLaunchKernelGGL((kvs_combine<false, false>), grid, block, lds, st, c);
-  }
+hipError_t launch_combine(const CombineArgs& a, bool ring, hipStream_t st) {
+  // outputs are merged by the partial kernel: without mass work there is
+  // nothing to do (the partition rates then keep their last values)
+  if (!(a.mass || a.head_mass || a.mass_max)) return hipSuccess;
+  dim3 grid(a.n_mass_chunks + 1, a.B), block(256);
+  const size_t lds = combine_lds_bytes(a.Hq, a.Hkv, a.S, a.nparts);
+  if (ring) hipLaunchKernelGGL((kvs_combine<true>), grid, block, lds, st, a);
+  else hipLaunchKernelGGL((kvs_combine<false>), grid, block, lds, st, a);
   return hipGetLastError();
 }
 

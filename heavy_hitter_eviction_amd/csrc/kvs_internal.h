@@ -46,6 +46,12 @@ struct PartialArgs {
   const void* app_k;
   const void* app_v;
   int app_bf16;
+  // Output merge in the kernel: the last partition of a (sequence, KV head)
+  // to finish (counted in pair_cnt[B][Hkv], tagged with this call's token)
+  // merges the group's partials into out. NULL pair_cnt: kvs_combine does it.
+  unsigned long long* pair_cnt;
+  uint32_t token;
+  void* out;
 };
 
 struct CombineArgs {
@@ -59,24 +65,23 @@ struct CombineArgs {
   int n_wg;       // partial workgroups that wrote ws_time
   int S;          // partial slots per (sequence, head)
   const int32_t* cur_pos;
-  void* out;
   float* mass;
   float* head_mass;  // [B][Hq][nbmax] per-head block masses (+=), or NULL
   float* mass_max;   // [B][nbmax] running max over heads (and calls), or NULL
-  int B, Hq, Hkv, D, C, NT, nbmax, tpp, nparts, n_o_chunks, n_mass_chunks, window;
+  int B, Hq, Hkv, C, NT, nbmax, tpp, nparts, n_mass_chunks, window;
 };
 
 // LDS of one combine workgroup: per-head max and 1/sum, every partial's max
-// and sum, per (head, partition) record weights, the split points, the
-// O-merge weights of its heads, or the rate accumulators (16 floats).
-inline size_t combine_lds_bytes(int Hq, int Hkv, int D, int S, int P) {
-  const size_t f = 2 * (size_t)Hq + 2 * (size_t)Hq * S + (size_t)Hq * P + (size_t)Hkv * (P + 1) + (size_t)(256 / D) * S;
+// and sum, per (head, partition) record weights and the partition
+// boundaries, or the rate accumulators (16 floats).
+inline size_t combine_lds_bytes(int Hq, int Hkv, int S, int P) {
+  const size_t f = 2 * (size_t)Hq + 2 * (size_t)Hq * S + (size_t)Hq * P + (size_t)Hkv * (P + 1);
   return (f < 16 ? 16 : f) * sizeof(float);
 }
 
 hipError_t launch_partial(int kv, int d, const PartialArgs& a, bool scored, bool ring,
                           size_t lds_bytes, hipStream_t st);
-hipError_t launch_combine(const CombineArgs& a, bool ring, bool q_bf16, hipStream_t st);
+hipError_t launch_combine(const CombineArgs& a, bool ring, hipStream_t st);
 
 hipError_t launch_encode_fp8(const void* src, int src_bf16, int64_t n_rows, int row_len,
                              uint8_t* codes, float* scales, hipStream_t st);
