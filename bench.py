@@ -4,9 +4,12 @@
 Metric: KV GB/s scanned per scored decode step (and % of HBM peak), plus
 blocks scored per second. One step is the whole hot path for every sequence:
 for each scored layer, append the new position's K/V (FP8 encode) and run the
-scored attention (partial + combine, block masses added over heads and
-layers), the append inside the partial kernel unless --separate-append; then
-the side-car update and the heavy-hitter block selection.
+scored attention; then add every layer's block masses (summed over heads and
+layers), update the side-car and run the heavy-hitter block selection. By
+default each layer is one kernel (append, attention, output merge) and the
+masses of all layers are added by one call after the last layer
+(kvs_append_decode_attn_tap, kvs_tap_masses); --separate-append runs the
+append, the partial and the per-layer combine as launches of their own.
 
 The default workload is the 397B-like shape: batch 16, 32 query / 8 KV heads,
 head dim 128, 15 layers, FP8 E4M3 KV with per-position scales, 32768 cached
@@ -141,7 +144,7 @@ def run_gpu(args, w):
         raise SystemExit(f"warmup + steps must be <= {w.steps} for this workload")
     t0 = time.time()
     fused = not args.separate_append and args.mode == "decode"
-    dec = ScoredDecoder(w, evict=args.evict, fused=fused)
+    dec = ScoredDecoder(w, evict=args.evict, fused=fused, tap=fused)
     prefill(dec, w, args.seed)
     Q, K, V = step_inputs(w, args.seed, n_steps, dec.n_layers)
     cur = [torch.full((w.batch,), w.context + t, dtype=torch.int32, device="cuda") for t in range(n_steps)]
@@ -175,14 +178,13 @@ def run_gpu(args, w):
             if ev_here:
                 ev[t - args.warmup][0].record()
             if fused:
-                # the append runs inside the partial kernel the events bracket
-                api.append_decode_attn(dec.caches[layer], K[layer][t], V[layer][t], Q[layer][t], cur[t],
-                                       dec.out[layer], dec.workspace, mass_accum=dec.mass, keep_mask=keep,
-                                       phase="partial")
+                # one kernel per layer: the append, the attention and its output
+                # merge; the layer's block sums stay in its workspace for the
+                # step's one tap_masses call
+                api.decode_attn_tap(dec.caches[layer], Q[layer][t], cur[t], dec.out[layer], dec.workspaces[layer],
+                                    keep_mask=keep, k_new=K[layer][t], v_new=V[layer][t])
                 if ev_here:
                     ev[t - args.warmup][1].record()
-                api.decode_attn_scored(dec.caches[layer], Q[layer][t], cur[t], dec.out[layer], dec.workspace,
-                                       mass_accum=dec.mass, keep_mask=keep, phase="combine")
                 continue
             if profiled:
                 # one call, both phases: the events cover partial + combine
@@ -198,6 +200,8 @@ def run_gpu(args, w):
                 ev[t - args.warmup][1].record()
             api.decode_attn_scored(dec.caches[layer], Q[layer][t], cur[t], dec.out[layer], dec.workspace,
                                    mass_accum=dec.mass, keep_mask=keep, phase="combine")
+        if fused:
+            api.tap_masses(dec.geom, dec.workspaces, cur[t], mass_accum=dec.mass)
         dec.close_turn(cur[t])
     sev[args.steps].record()
     end.record()
@@ -523,6 +527,7 @@ def main():
             "window": w.window, "ring": w.ring, "budget_blocks": w.budget_blocks,
             "recent_tokens": w.recent_tokens, "mode": "evict" if args.evict else "score-only",
             "append": "separate launch" if (args.separate_append or args.mode != "decode") else "in the partial kernel",
+            "masses": "per layer" if (args.separate_append or args.mode != "decode") else "once per step, all layers",
             **({"outputs": "per-head block masses [B][Hq][NBmax] and max over heads and layers"}
                if args.mode == "profiled" else {}),
         },

@@ -11,6 +11,7 @@ kernels. Tensors are torch device tensors; each call passes their
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from dataclasses import dataclass
 
@@ -27,7 +28,8 @@ TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8
 EXPORTED = (
     "kvs_cache_bytes", "kvs_encode_fp8", "kvs_append_kv", "kvs_decode_workspace_bytes",
     "kvs_decode_attn_scored", "kvs_decode_partial", "kvs_decode_combine", "kvs_append_decode_attn",
-    "kvs_append_decode_partial", "kvs_decode_attn_profiled",
+    "kvs_append_decode_partial", "kvs_decode_attn_tap", "kvs_append_decode_attn_tap", "kvs_tap_masses",
+    "kvs_decode_attn_profiled",
     "kvs_reattend_blocks",
     "kvs_update_sidecar", "kvs_update_counters", "kvs_filter_blocks", "kvs_select_blocks",
     "kvs_compact_blocks", "kvs_snapkv_workspace_bytes", "kvs_snapkv_scores", "kvs_status_str",
@@ -71,6 +73,9 @@ def _load():
         "kvs_decode_combine": [G, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "kvs_append_decode_attn": [G, P, P, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "kvs_append_decode_partial": [G, P, P, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "kvs_decode_attn_tap": [G, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "kvs_append_decode_attn_tap": [G, P, P, I32, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "kvs_tap_masses": [G, P, I32, SZ, P, P, P, P, P],
         "kvs_reattend_blocks": [G, P, P, P, P, P, P, P, P, I32, P, P, P, SZ, P],
         "kvs_decode_attn_profiled": [G, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "kvs_update_sidecar": [P, P, P, P, P, I32, I32, I32, I64, F, P],
@@ -296,6 +301,65 @@ def append_decode_attn(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor,
               _ptr(keep_mask), _ptr(out), _ptr(mass_accum), _ptr(workspace), ws_bytes, _stream(stream)),
            f"kvs_append_decode ({phase})")
     return out
+
+
+def decode_attn_tap(cache: KVCache, q: torch.Tensor, cur_pos: torch.Tensor, out: torch.Tensor,
+                    workspace: torch.Tensor, keep_mask: torch.Tensor | None = None, stream=None,
+                    k_new: torch.Tensor | None = None, v_new: torch.Tensor | None = None):
+    """kvs_decode_attn_tap (or, with ``k_new`` / ``v_new``, kvs_append_decode_attn_tap):
+    the layer's output, and its per-block sums left in ``workspace`` for
+    :func:`tap_masses`. ``workspace`` is this layer's own."""
+    g = cache.geom
+    _device_check(q, cur_pos, out, workspace, keep_mask, k_new, v_new)
+    qdt = TORCH_DTYPES[g.q_dtype]
+    if q.dtype != qdt or out.dtype != qdt:
+        raise TypeError("q and out must have the geometry's q dtype")
+    if q.shape != (g.batch, g.n_q_heads, g.head_dim) or out.shape != q.shape:
+        raise ValueError("q/out must be [B, Hq, d]")
+    if cur_pos.dtype != torch.int32 or cur_pos.numel() != g.batch:
+        raise ValueError("cur_pos must be int32 [B]")
+    if keep_mask is not None and (keep_mask.dtype != torch.int32 or keep_mask.numel() != g.batch * g.words):
+        raise ValueError("keep_mask must be int32 (bit words) [B, W]")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    gc = g.c()
+    if k_new is None:
+        _check(LIB.kvs_decode_attn_tap(ctypes.byref(gc), _ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(cache.k_scale),
+                                       _ptr(cache.v_scale), _ptr(cache.pos_of_slot), _ptr(cur_pos),
+                                       _ptr(keep_mask), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)),
+               "kvs_decode_attn_tap")
+        return out
+    dt = {torch.float32: KVS_F32, torch.bfloat16: KVS_BF16}.get(k_new.dtype)
+    if dt is None or v_new is None or v_new.dtype != k_new.dtype:
+        raise TypeError("new rows must be float32 or bfloat16, K and V alike")
+    w = g.n_kv_heads * g.head_dim
+    if k_new.shape != (g.batch, w) or v_new.shape != (g.batch, w):
+        raise ValueError("new rows must be [B, Hkv*d]")
+    _check(LIB.kvs_append_decode_attn_tap(ctypes.byref(gc), _ptr(k_new), _ptr(v_new), dt, _ptr(q), _ptr(cache.k),
+                                          _ptr(cache.v), _ptr(cache.k_scale), _ptr(cache.v_scale),
+                                          _ptr(cache.pos_of_slot), _ptr(cur_pos), _ptr(keep_mask), _ptr(out),
+                                          _ptr(workspace), ws_bytes, _stream(stream)),
+           "kvs_append_decode_attn_tap")
+    return out
+
+
+def tap_masses(geom: CacheGeom, workspaces, cur_pos: torch.Tensor, mass_accum: torch.Tensor | None = None,
+               head_mass: torch.Tensor | None = None, mass_max: torch.Tensor | None = None, stream=None):
+    """kvs_tap_masses: add the block masses the per-layer tap calls left in
+    ``workspaces`` (one per layer, in call order)."""
+    _device_check(cur_pos, mass_accum, head_mass, mass_max, *workspaces)
+    if not workspaces:
+        raise ValueError("need at least one layer workspace")
+    if cur_pos.dtype != torch.int32 or cur_pos.numel() != geom.batch:
+        raise ValueError("cur_pos must be int32 [B]")
+    for t, shape in ((mass_accum, (geom.batch, geom.nb)), (mass_max, (geom.batch, geom.nb)),
+                     (head_mass, (geom.batch, geom.n_q_heads, geom.nb))):
+        if t is not None and (t.dtype != torch.float32 or t.numel() != math.prod(shape)):
+            raise ValueError(f"mass outputs must be float32 {shape}")
+    ws_bytes = min(w.numel() * w.element_size() for w in workspaces)
+    arr = (ctypes.c_void_p * len(workspaces))(*[w.data_ptr() for w in workspaces])
+    gc = geom.c()
+    _check(LIB.kvs_tap_masses(ctypes.byref(gc), arr, len(workspaces), ws_bytes, _ptr(cur_pos), _ptr(mass_accum),
+                              _ptr(head_mass), _ptr(mass_max), _stream(stream)), "kvs_tap_masses")
 
 
 def decode_attn_profiled(cache: KVCache, q: torch.Tensor, cur_pos: torch.Tensor, out: torch.Tensor,

@@ -85,7 +85,7 @@ Plan make_plan(const kvs_geom* g) {
   // over the nparts * nw partials in LDS: bound them to 48 KiB
   while (true) {
     const int np = (p.NT + tpp - 1) / tpp;
-    if (kvs::combine_lds_bytes(g->n_q_heads, g->n_kv_heads, np, np) <= 49152) break;
+    if (kvs::combine_layer_floats(g->n_q_heads, g->n_kv_heads, np) * 4 <= kvs::kCombineLdsBytes) break;
     tpp *= 2;
   }
   p.tpp = tpp;
@@ -254,9 +254,10 @@ int decode_setup(const kvs_geom* g, const void* q, const void* k_cache, const vo
   a->dyn = g->deterministic ? 0 : 1; a->tl_cap = p.tl_cap; a->oslots = p.oslots; a->adapt = p.adapt;
   a->scale_log2 = g->softmax_scale * 1.4426950408889634f;
   *c = kvs::CombineArgs{};
-  c->ws_m = a->ws_m; c->ws_l = a->ws_l; c->ws_o = a->ws_o; c->ws_e = a->ws_e; c->cur_pos = cur_pos;
-  c->ws_bnd = a->ws_bnd; c->ws_time = a->ws_time; c->rates = (float*)(ws + p.off_rates);
-  c->n_wg = p.n_wg; c->S = p.S;
+  c->lws[0] = ws; c->n_layers = 1; c->layers_per_chunk = 1;
+  c->off_m = p.off_m; c->off_l = p.off_l; c->off_e = p.off_e; c->off_bnd = p.off_bnd;
+  c->off_time = p.off_time; c->off_rates = p.off_rates;
+  c->cur_pos = cur_pos; c->n_wg = p.n_wg;
   c->mass = mass_accum;
   c->B = g->batch; c->Hq = g->n_q_heads; c->Hkv = g->n_kv_heads; c->C = g->capacity; c->NT = p.NT;
   c->nbmax = g->n_blocks_max; c->tpp = p.tpp; c->nparts = p.nparts; c->window = g->window;
@@ -369,6 +370,61 @@ int kvs_append_decode_attn(KVS_APPEND_DECODE_ARGS) {
                                      p.lds_partial, s);
   if (e != hipSuccess) return KVS_EHIP;
   return hip_status(kvs::launch_combine(c, g->ring != 0, s));
+}
+
+int kvs_decode_attn_tap(const kvs_geom* g, const void* q, const void* k_cache, const void* v_cache,
+                        const float* k_scale, const float* v_scale, const int32_t* pos_of_slot,
+                        const int32_t* cur_pos, const uint32_t* keep_mask, void* out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  float* mass_accum = nullptr;
+  KVS_DECODE_SETUP
+  (void)c;
+  return hip_status(kvs::launch_partial(kv, g->head_dim, a, true, g->ring != 0, p.lds_partial, s));
+}
+
+int kvs_append_decode_attn_tap(const kvs_geom* g, const void* k_new, const void* v_new, int32_t src_dtype,
+                               const void* q, void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                               int32_t* pos_of_slot, const int32_t* cur_pos, const uint32_t* keep_mask,
+                               void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  float* mass_accum = nullptr;
+  KVS_APPEND_DECODE_SETUP
+  (void)c;
+  return hip_status(kvs::launch_partial(kv, g->head_dim, a, true, g->ring != 0, p.lds_partial, s));
+}
+
+int kvs_tap_masses(const kvs_geom* g, void* const* workspaces, int32_t n_layers, size_t workspace_bytes,
+                   const int32_t* cur_pos, float* mass_accum, float* head_mass, float* mass_max, void* stream) {
+  int st = check_geom(g);
+  if (st) return st;
+  if (n_layers < 1 || n_layers > kvs::kMaxTapLayers || !workspaces || !cur_pos) return KVS_EINVAL;
+  const void* ptrs[] = {cur_pos, mass_accum, head_mass, mass_max};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return KVS_EALIGN;
+  const Plan p = make_plan(g);
+  if (workspace_bytes < p.total) return KVS_EWS;
+  kvs::CombineArgs c{};
+  for (int l = 0; l < n_layers; ++l) {
+    if (!workspaces[l]) return KVS_EINVAL;
+    if (!aligned16(workspaces[l])) return KVS_EALIGN;
+    c.lws[l] = (const char*)workspaces[l];
+  }
+  c.n_layers = n_layers;
+  const size_t per_layer = kvs::combine_layer_floats(g->n_q_heads, g->n_kv_heads, p.nparts) * 4;
+  const int fit = (int)(kvs::kCombineLdsBytes / per_layer);
+  c.layers_per_chunk = fit < 1 ? 1 : (fit < n_layers ? fit : n_layers);
+  c.off_m = p.off_m; c.off_l = p.off_l; c.off_e = p.off_e; c.off_bnd = p.off_bnd;
+  c.off_time = p.off_time; c.off_rates = p.off_rates;
+  c.n_wg = p.n_wg; c.cur_pos = cur_pos;
+  c.mass = mass_accum; c.head_mass = head_mass; c.mass_max = mass_max;
+  c.B = g->batch; c.Hq = g->n_q_heads; c.Hkv = g->n_kv_heads; c.C = g->capacity; c.NT = p.NT;
+  c.nbmax = g->n_blocks_max; c.tpp = p.tpp; c.nparts = p.nparts; c.window = g->window;
+  c.n_mass_chunks = (p.NT + 255) / 256;
+  // without per-head masses, and when every layer's tables fit the LDS at
+  // once, the layers are summed in parallel (same values, bit for bit)
+  if (!head_mass && kvs::combine_layers_lds_bytes(g->n_q_heads, g->n_kv_heads, p.nparts, n_layers, g->ring != 0) <=
+                        kvs::kCombineLdsBytes)
+    return hip_status(kvs::launch_combine_layers(c, g->ring != 0, (hipStream_t)stream));
+  return hip_status(kvs::launch_combine(c, g->ring != 0, (hipStream_t)stream));
 }
 
 int kvs_reattend_blocks(const kvs_geom* g, const void* q, const void* k_cache, const void* v_cache,

@@ -1002,28 +1002,34 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
 }
 
 // ---------------------------------------------------------------------------
-// Combine: grid (n_mass_chunks + 1, B), 256 threads: the block masses.
-// Every workgroup first reduces, per head h of its sequence, the partitions'
+// Combine: grid (n_mass_chunks + n_layers, B), 256 threads: the block masses
+// of n_layers calls (one for kvs_decode_combine, a whole step's layers for
+// kvs_tap_masses), added in call order.
+// Per layer and head h of its sequence a workgroup reduces the partitions'
 // partials to M_h = max_p m_p and L_h = sum_p l_p 2^(m_p - M_h); then each
 // thread adds, for its tile and sub-block, sum_h E 2^(m_p(tile) - M_h) / L_h
-// over the heads in ascending order into mass_accum, E being the tile's
-// record relative to its partition's max. (The outputs were merged by the
-// partial kernel.) The last column (sequence 0 only) refreshes the per-class
-// streaming rates from the partial kernel's clock records.
+// over the heads in ascending order, layer after layer, into mass_accum, E
+// being the tile's record relative to its partition's max. (The outputs were
+// merged by the partial kernel.) The extra columns (sequence 0 only) refresh
+// each layer's per-class streaming rates from its clock records.
 // ---------------------------------------------------------------------------
 template <bool RING>
 __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
   extern __shared__ float lds[];
   const int b = blockIdx.y;
-  const int S = a.S;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int n_work = a.n_mass_chunks;
+  const int tid = threadIdx.x;
+  const int P = a.nparts, L = a.n_layers;
+  auto ws_f = [&](int l, size_t off) { return (const float*)(a.lws[l] + off); };
 
-  if ((int)blockIdx.x >= n_work) {
-    // ---- rates: per dispatch class (workgroup id mod 8), tiles per tick of
-    // its workgroups (a workgroup's time is its slowest wave's), relative to
-    // the mean over classes, blended half-and-half into the stored value ----
-    if (b != 0 || a.rates == nullptr || a.ws_time == nullptr) return;
+  if ((int)blockIdx.x >= a.n_mass_chunks) {
+    // ---- rates of one layer: per dispatch class (workgroup id mod 8),
+    // tiles per tick of its workgroups (a workgroup's time is its slowest
+    // wave's), relative to the mean over classes, blended half-and-half into
+    // the stored value ----
+    const int l = blockIdx.x - a.n_mass_chunks;
+    if (b != 0 || l >= L) return;
+    const float* ws_time = ws_f(l, a.off_time);
+    float* rates = (float*)(a.lws[l] + a.off_rates);
     float* ct = lds;       // [8] tiles
     float* cs = lds + 8;   // [8] ticks
     if (tid < 16) lds[tid] = 0.0f;
@@ -1031,7 +1037,7 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
     for (int w = tid; w < a.n_wg; w += 256) {
       float tiles = 0.0f, ticks = 0.0f;
       for (int k = 0; k < kPartialWaves; ++k) {
-        const float* tm = a.ws_time + ((size_t)w * kPartialWaves + k) * 2;
+        const float* tm = ws_time + ((size_t)w * kPartialWaves + k) * 2;
         tiles += tm[0];
         ticks = fmaxf(ticks, tm[1]);
       }
@@ -1053,39 +1059,63 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
         }
       }
       const float r = cs[tid] > 0.0f ? ct[tid] / cs[tid] : 0.0f;
-      const float old = a.rates[tid];
+      const float old = rates[tid];
       if (nv > 0 && r > 0.0f) {
         const float rel = fminf(fmaxf(r / (mean / (float)nv), 0.5f), 2.0f);
         const bool ok = old >= 0.5f && old <= 2.0f;  // NaN fails too
-        a.rates[tid] = ok ? 0.5f * old + 0.5f * rel : rel;
+        rates[tid] = ok ? 0.5f * old + 0.5f * rel : rel;
       }
     }
     return;
   }
 
-  // One partial per partition (S == nparts). Each workgroup first issues the
-  // global loads that need nothing from the shared prologue (its tile's
-  // records and current masses), then builds the per-head tables, then
-  // finishes: one round of load latency instead of three.
-  const int P = S;
+  // Each workgroup first issues the global loads that need nothing from the
+  // shared tables (the first layer's records of its tile, the current
+  // masses, the first layers' partition maxima, sums and boundaries), then
+  // builds the tables and finishes, the next layer's records loading while
+  // one layer is summed. Loads are unconditional (indices clamped into
+  // range, unused values masked later): conditional loads make the compiler
+  // wait for each one.
   constexpr int NSUB = RING ? 2 : 1;
   constexpr int HC = RING ? 16 : 32;   // heads per record chunk
   const int G = a.Hq / a.Hkv;
+  const int n_ml = a.Hq * P;                 // partition maxima (and sums) per layer
+  const int n_bnd = a.Hkv * (P + 1);         // boundaries per layer
+  const int lc0 = min(L, a.layers_per_chunk);
+  // layer-table block of layer slot s in LDS
+  const int per_layer = (int)combine_layer_floats(a.Hq, a.Hkv, P);
+  auto t_hM = [&](int s_) { return lds + (size_t)s_ * per_layer; };           // [Hq]
+  auto t_hI = [&](int s_) { return t_hM(s_) + a.Hq; };                        // [Hq]
+  auto t_mS = [&](int s_) { return t_hI(s_) + a.Hq; };                        // [Hq][P]
+  auto t_lS = [&](int s_) { return t_mS(s_) + n_ml; };                        // [Hq][P]
+  auto t_wp = [&](int s_) { return t_lS(s_) + n_ml; };                        // [P][Hq]
+  auto t_bd = [&](int s_) { return (int*)(t_wp(s_) + n_ml); };               // [Hkv][P + 1]
+  // the first chunk's maxima/sums/boundaries: two per thread prefetched
+  const int n_stage = lc0 * (2 * n_ml + n_bnd);
+  auto stage_src = [&](int l0, int x) -> float {
+    // value x of the staged tables of layers [l0, l0 + lc): per layer
+    // n_ml maxima, n_ml sums, n_bnd boundaries (bit patterns)
+    const int per = 2 * n_ml + n_bnd;
+    const int l = l0 + x / per, r = x % per;
+    if (r < n_ml) return ws_f(l, a.off_m)[(size_t)b * n_ml + r];
+    if (r < 2 * n_ml) return ws_f(l, a.off_l)[(size_t)b * n_ml + r - n_ml];
+    if constexpr (RING) return 0.0f;
+    return __builtin_bit_cast(float, ((const int*)(a.lws[l] + a.off_bnd))[(size_t)b * n_bnd + r - 2 * n_ml]);
+  };
+  auto stage_dst = [&](int x) -> float* {
+    const int per = 2 * n_ml + n_bnd;
+    const int s_ = x / per, r = x % per;
+    if (r < n_ml) return t_mS(s_) + r;
+    if (r < 2 * n_ml) return t_lS(s_) + (r - n_ml);
+    return (float*)t_bd(s_) + (r - 2 * n_ml);
+  };
+  const float pre0 = stage_src(0, min(tid, n_stage - 1));
+  const float pre1 = stage_src(0, min(tid + 256, n_stage - 1));
 
-  // ---- independent loads ----
-  // the partitions' maxima and sums of the sequence (staged in LDS below)
-  const float* mp = a.ws_m + (size_t)b * a.Hq * S;
-  const float* lp = a.ws_l + (size_t)b * a.Hq * S;
-  const int n_ml = a.Hq * S;
-  const float m_pre0 = mp[min(tid, n_ml - 1)], l_pre0 = lp[min(tid, n_ml - 1)];
-  const float m_pre1 = mp[min(tid + 256, n_ml - 1)], l_pre1 = lp[min(tid + 256, n_ml - 1)];
-  const int n_bnd = a.Hkv * (P + 1);
-  const int bnd_pre = RING ? 0 : a.ws_bnd[(size_t)b * n_bnd + min(tid, n_bnd - 1)];
-  // mass chunk: tile t of this thread (tiles with records: every tile of a
-  // ring; a linear cache's readable range), its logical blocks, the records
-  // of its first HC heads and the current masses of its blocks
-  // (without a window the range starts at tile 0, so the record loads need
-  // not wait for cur_pos; the range end and the blocks come after them)
+  // tile t of this thread (tiles with records: every tile of a ring; a
+  // linear cache's readable range). Without a window the range starts at
+  // tile 0, so the record loads need not wait for cur_pos; the range end
+  // and the blocks come after them.
   int tlo = 0;
   if constexpr (!RING) {
     if (a.window > 0) {
@@ -1098,8 +1128,8 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
   // records of heads past Hq (clamped duplicates) get weight 0; a dead
   // thread's values are never used
   const int tc = min(max(t, 0), a.NT - 1);
-  float ev[NSUB][HC];
-  auto load_records = [&](int hc) {
+  auto load_records = [&](int l, int hc, float (&ev)[NSUB][HC]) {
+    const float* we = ws_f(l, a.off_e);
     if (G % 4 == 0) {
       // four heads of one group per 16-byte load; consecutive threads
       // (tiles) read consecutive 16-byte pieces
@@ -1110,7 +1140,7 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
         const size_t row = ((size_t)b * a.Hkv + gg) * a.NT + tc;
 #pragma unroll
         for (int sb = 0; sb < NSUB; ++sb) {
-          const f32x4 e4 = *(const f32x4*)(a.ws_e + (row * NSUB + sb) * G + (hh - gg * G));
+          const f32x4 e4 = *(const f32x4*)(we + (row * NSUB + sb) * G + (hh - gg * G));
 #pragma unroll
           for (int k = 0; k < 4; ++k) ev[sb][4 * q + k] = e4[k];
         }
@@ -1122,24 +1152,22 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
         const int gg = hh / G;
         const size_t row = ((size_t)b * a.Hkv + gg) * a.NT + tc;
 #pragma unroll
-        for (int sb = 0; sb < NSUB; ++sb) ev[sb][k] = a.ws_e[(row * NSUB + sb) * G + (hh - gg * G)];
+        for (int sb = 0; sb < NSUB; ++sb) ev[sb][k] = we[(row * NSUB + sb) * G + (hh - gg * G)];
       }
     }
   };
-  load_records(0);
-  float mass_old[NSUB], max_old[NSUB];
+  float ev[NSUB][HC], ev_next[NSUB][HC];
+  load_records(0, 0, ev);
+  float mass_run[NSUB], max_run[NSUB];
   if constexpr (!RING) {
     // a linear cache's block is the tile: its index needs no cur_pos
     const size_t mi = (size_t)b * a.nbmax + min(tc, a.nbmax - 1);
-    mass_old[0] = a.mass != nullptr ? a.mass[mi] : 0.0f;
-    max_old[0] = a.mass_max != nullptr ? a.mass_max[mi] : 0.0f;
+    mass_run[0] = a.mass != nullptr ? a.mass[mi] : 0.0f;
+    max_run[0] = a.mass_max != nullptr ? a.mass_max[mi] : 0.0f;
   }
   const int i_cur = a.cur_pos[b];
-  int thi = a.NT, tpe = a.tpp;
-  if constexpr (!RING) {
-    thi = max(0, min(a.NT, i_cur / kTile + 1));
-    tpe = max(1, (thi - tlo + P - 1) / P);
-  }
+  int thi = a.NT;
+  if constexpr (!RING) thi = max(0, min(a.NT, i_cur / kTile + 1));
   const bool m_live = t < thi;
   const int lap_i = RING ? i_cur / a.C : 0;
   int blk[NSUB];
@@ -1156,132 +1184,419 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
 #pragma unroll
     for (int sb = 0; sb < NSUB; ++sb) {
       const size_t mi = (size_t)b * a.nbmax + max(blk[sb], 0);
-      mass_old[sb] = a.mass != nullptr ? a.mass[mi] : 0.0f;
-      max_old[sb] = a.mass_max != nullptr ? a.mass_max[mi] : 0.0f;
+      mass_run[sb] = a.mass != nullptr ? a.mass[mi] : 0.0f;
+      max_run[sb] = a.mass_max != nullptr ? a.mass_max[mi] : 0.0f;
     }
   }
 
-  // ---- per-head tables: M_h, 1 / L_h and the partition weights ----
-  float* hM = lds;              // [Hq]
-  float* hInv = hM + a.Hq;      // [Hq]
-  float* mS = hInv + a.Hq;      // [Hq][P] partition maxima
-  float* lS = mS + a.Hq * S;    // [Hq][P] partition sums
-  float* wp = lS + a.Hq * S;    // [P][Hq] weights 2^(m_p - M_h) / L_h
-  int* bnd = (int*)(wp + a.Hq * P);  // [Hkv][P + 1] partition boundaries (linear)
-  {
-    if (tid < n_ml) {
-      mS[tid] = m_pre0;
-      lS[tid] = l_pre0;
-    }
-    if (tid + 256 < n_ml) {
-      mS[tid + 256] = m_pre1;
-      lS[tid + 256] = l_pre1;
-    }
-    for (int x = tid + 512; x < n_ml; x += 256) {
-      mS[x] = mp[x];
-      lS[x] = lp[x];
-    }
-    if (!RING) {
-      if (tid < n_bnd) bnd[tid] = bnd_pre;
-      for (int x = tid + 256; x < n_bnd; x += 256) bnd[x] = a.ws_bnd[(size_t)b * n_bnd + x];
-    }
-  }
-  __syncthreads();
-  for (int hh = tid; hh < a.Hq; hh += 256)
-    merge_weights(mS + hh * S, lS + hh * S, P, wp + hh, a.Hq, &hM[hh], &hInv[hh]);
-  __syncthreads();
-
-  if (!m_live) return;
-
-  // ---- masses: heads in ascending order, HC at a time (head h sits at row
-  // (b, h / G) of the records, entry h % G); per-head masses
-  // read-modify-written alongside when asked for. Every tile of the range
-  // has records from this launch, relative to its partition's max. ----
-  // partition that produced tile tc's records for KV head gg: a ring splits
-  // evenly; a linear range at the stored boundaries (the last one at or
-  // below tc; boundary 0 is the range start)
-  auto part_of = [&](int gg) -> int {
-    if constexpr (RING) {
-      return min(tc / a.tpp, P - 1);
+  for (int l0 = 0; l0 < L; l0 += lc0) {
+    const int lc = min(lc0, L - l0);
+    // ---- tables of layers [l0, l0 + lc) ----
+    if (l0 > 0) __syncthreads();  // the previous chunk's tables are done with
+    const int n_st = lc * (2 * n_ml + n_bnd);
+    if (l0 == 0) {
+      if (tid < n_st) *stage_dst(tid) = pre0;
+      if (tid + 256 < n_st) *stage_dst(tid + 256) = pre1;
+      for (int x = tid + 512; x < n_st; x += 256) *stage_dst(x) = stage_src(0, x);
     } else {
-      const int* bg = bnd + gg * (P + 1);
-      int base = 0;
-      for (int n = P; n > 1;) {
-        const int half = n >> 1;
-        base = bg[base + half] <= tc ? base + half : base;
-        n -= half;
-      }
-      return base;
+      for (int x = tid; x < n_st; x += 256) *stage_dst(x) = stage_src(l0, x);
     }
-  };
-  float acc[NSUB], mx[NSUB];
-#pragma unroll
-  for (int sb = 0; sb < NSUB; ++sb) {
-    acc[sb] = 0.0f;
-    mx[sb] = 0.0f;
-  }
-  for (int hc = 0; hc < a.Hq; hc += HC) {
-    if (hc > 0) load_records(hc);
-    // weights of the chunk's heads: unconditional (clamped) LDS reads, a
-    // group's four heads at once when G % 4 == 0
-    float sc[HC];
-    if (G % 4 == 0) {
-      int pq[HC / 4];
-#pragma unroll
-      for (int q = 0; q < HC / 4; ++q) pq[q] = part_of(min(hc + 4 * q, a.Hq - 4) / G);
-      f32x4 w4[HC / 4];
-#pragma unroll
-      for (int q = 0; q < HC / 4; ++q) {
-        const int hh = min(hc + 4 * q, a.Hq - 4);
-        w4[q] = *(const f32x4*)(wp + pq[q] * a.Hq + hh);
-      }
-#pragma unroll
-      for (int q = 0; q < HC / 4; ++q)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) sc[4 * q + k] = hc + 4 * q + k < a.Hq ? w4[q][k] : 0.0f;
-    } else {
-      int pk[HC];
-#pragma unroll
-      for (int k = 0; k < HC; ++k) pk[k] = part_of(min(hc + k, a.Hq - 1) / G);
-#pragma unroll
-      for (int k = 0; k < HC; ++k) {
-        const int hh = min(hc + k, a.Hq - 1);
-        const float w = wp[pk[k] * a.Hq + hh];
-        sc[k] = hc + k < a.Hq ? w : 0.0f;
-      }
+    __syncthreads();
+    for (int x = tid; x < lc * a.Hq; x += 256) {
+      const int s_ = x / a.Hq, hh = x % a.Hq;
+      merge_weights(t_mS(s_) + hh * P, t_lS(s_) + hh * P, P, t_wp(s_) + hh, a.Hq, &t_hM(s_)[hh], &t_hI(s_)[hh]);
     }
+    __syncthreads();
+    if (!m_live) continue;
+
+    for (int s_ = 0; s_ < lc; ++s_) {
+      const int l = l0 + s_;
+      const float* wp = t_wp(s_);
+      const int* bnd = t_bd(s_);
+      // partition that produced tile tc's records for KV head gg: a ring
+      // splits evenly; a linear range at the stored boundaries (the last one
+      // at or below tc; boundary 0 is the range start)
+      auto part_of = [&](int gg) -> int {
+        if constexpr (RING) {
+          return min(tc / a.tpp, P - 1);
+        } else {
+          const int* bg = bnd + gg * (P + 1);
+          int base = 0;
+          for (int n = P; n > 1;) {
+            const int half = n >> 1;
+            base = bg[base + half] <= tc ? base + half : base;
+            n -= half;
+          }
+          return base;
+        }
+      };
+      float acc[NSUB], mx[NSUB];
 #pragma unroll
-    for (int sb = 0; sb < NSUB; ++sb) {
-#pragma unroll
-      for (int k = 0; k < HC; ++k) {
-        if (hc + k >= a.Hq) break;
-        const float v = ev[sb][k] * sc[k];
-        acc[sb] += v;
-        mx[sb] = fmaxf(mx[sb], v);
+      for (int sb = 0; sb < NSUB; ++sb) {
+        acc[sb] = 0.0f;
+        mx[sb] = 0.0f;
       }
-      if (a.head_mass != nullptr && blk[sb] >= 0) {
-        float* hp = a.head_mass + ((size_t)b * a.Hq + hc) * a.nbmax + blk[sb];
-        // per-head masses, eight read-modify-writes in flight at a time
+      // heads in ascending order, HC at a time (head h sits at row (b, h / G)
+      // of the records, entry h % G); per-head masses read-modify-written
+      // alongside when asked for. Every tile of the range has records from
+      // this layer's call, relative to its partition's max.
+      for (int hc = 0; hc < a.Hq; hc += HC) {
+        if (hc > 0) load_records(l, hc, ev);
+        // the next layer's first records load while this chunk is summed
+        const bool prefetch = hc + HC >= a.Hq && l + 1 < L;
+        if (prefetch) load_records(l + 1, 0, ev_next);
+        // weights of the chunk's heads: unconditional (clamped) LDS reads, a
+        // group's four heads at once when G % 4 == 0
+        float sc[HC];
+        if (G % 4 == 0) {
+          int pq[HC / 4];
 #pragma unroll
-        for (int k0 = 0; k0 < HC; k0 += 8) {
-          if (hc + k0 >= a.Hq) break;
-          float hv[8];
+          for (int q = 0; q < HC / 4; ++q) pq[q] = part_of(min(hc + 4 * q, a.Hq - 4) / G);
+          f32x4 w4[HC / 4];
 #pragma unroll
-          for (int k = 0; k < 8; ++k) hv[k] = hp[(size_t)min(k0 + k, a.Hq - 1 - hc) * a.nbmax];
+          for (int q = 0; q < HC / 4; ++q) {
+            const int hh = min(hc + 4 * q, a.Hq - 4);
+            w4[q] = *(const f32x4*)(wp + pq[q] * a.Hq + hh);
+          }
 #pragma unroll
-          for (int k = 0; k < 8; ++k)
-            if (hc + k0 + k < a.Hq) hp[(size_t)(k0 + k) * a.nbmax] = hv[k] + ev[sb][k0 + k] * sc[k0 + k];
+          for (int q = 0; q < HC / 4; ++q)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) sc[4 * q + k] = hc + 4 * q + k < a.Hq ? w4[q][k] : 0.0f;
+        } else {
+          int pk[HC];
+#pragma unroll
+          for (int k = 0; k < HC; ++k) pk[k] = part_of(min(hc + k, a.Hq - 1) / G);
+#pragma unroll
+          for (int k = 0; k < HC; ++k) {
+            const int hh = min(hc + k, a.Hq - 1);
+            const float w = wp[pk[k] * a.Hq + hh];
+            sc[k] = hc + k < a.Hq ? w : 0.0f;
+          }
+        }
+#pragma unroll
+        for (int sb = 0; sb < NSUB; ++sb) {
+#pragma unroll
+          for (int k = 0; k < HC; ++k) {
+            if (hc + k >= a.Hq) break;
+            const float v = ev[sb][k] * sc[k];
+            acc[sb] += v;
+            mx[sb] = fmaxf(mx[sb], v);
+          }
+          if (a.head_mass != nullptr && blk[sb] >= 0) {
+            float* hp = a.head_mass + ((size_t)b * a.Hq + hc) * a.nbmax + blk[sb];
+            // per-head masses, eight read-modify-writes in flight at a time
+#pragma unroll
+            for (int k0 = 0; k0 < HC; k0 += 8) {
+              if (hc + k0 >= a.Hq) break;
+              float hv[8];
+#pragma unroll
+              for (int k = 0; k < 8; ++k) hv[k] = hp[(size_t)min(k0 + k, a.Hq - 1 - hc) * a.nbmax];
+#pragma unroll
+              for (int k = 0; k < 8; ++k)
+                if (hc + k0 + k < a.Hq) hp[(size_t)(k0 + k) * a.nbmax] = hv[k] + ev[sb][k0 + k] * sc[k0 + k];
+            }
+          }
+        }
+        if (prefetch) {
+#pragma unroll
+          for (int sb = 0; sb < NSUB; ++sb)
+#pragma unroll
+            for (int k = 0; k < HC; ++k) ev[sb][k] = ev_next[sb][k];
         }
       }
+#pragma unroll
+      for (int sb = 0; sb < NSUB; ++sb) {
+        mass_run[sb] = mass_run[sb] + acc[sb];
+        max_run[sb] = fmaxf(max_run[sb], mx[sb]);
+      }
     }
   }
+  if (!m_live) return;
 #pragma unroll
   for (int sb = 0; sb < NSUB; ++sb) {
     if (blk[sb] < 0) continue;
     const size_t mi = (size_t)b * a.nbmax + blk[sb];
-    if (a.mass != nullptr) a.mass[mi] = mass_old[sb] + acc[sb];
-    if (a.mass_max != nullptr) a.mass_max[mi] = fmaxf(max_old[sb], mx[sb]);
+    if (a.mass != nullptr) a.mass[mi] = mass_run[sb];
+    if (a.mass_max != nullptr) a.mass_max[mi] = max_run[sb];
   }
+}
+
+// ---------------------------------------------------------------------------
+// Layer-parallel combine (kvs_tap_masses without per-head masses): grid
+// (ceil(NT / 64), B) plus n_layers rate columns, 512 threads. Wave w of a
+// workgroup takes layers w, w + 8, ... for 64 consecutive tiles (one per
+// lane), keeping each (tile, layer)'s sum over heads, computed exactly as
+// kvs_combine does, in LDS; then one lane per tile adds them in layer order
+// to the current mass, so the result equals the layer-by-layer sum bit for
+// bit. The tables of all layers are in LDS at once.
+// ---------------------------------------------------------------------------
+constexpr int kCmbTiles = 64;
+constexpr int kCmbWaves = 8;
+
+template <bool RING>
+__global__ __launch_bounds__(64 * kCmbWaves) void kvs_combine_layers(CombineArgs a) {
+  constexpr int NTH = 64 * kCmbWaves;
+  extern __shared__ float lds[];
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int P = a.nparts, L = a.n_layers;
+  constexpr int NSUB = RING ? 2 : 1;
+  constexpr int HC = RING ? 16 : 32;
+  auto ws_f = [&](int l, size_t off) { return (const float*)(a.lws[l] + off); };
+  const int n_chunks = (a.NT + kCmbTiles - 1) / kCmbTiles;
+  if ((int)blockIdx.x >= n_chunks) {
+    // rates: the same per-layer refresh as in kvs_combine
+    const int l = blockIdx.x - n_chunks;
+    if (b != 0 || l >= L) return;
+    const float* ws_time = ws_f(l, a.off_time);
+    float* rates = (float*)(a.lws[l] + a.off_rates);
+    float* ct = lds;
+    float* cs = lds + 8;
+    if (tid < 16) lds[tid] = 0.0f;
+    __syncthreads();
+    for (int w = tid; w < a.n_wg; w += NTH) {
+      float tiles = 0.0f, ticks = 0.0f;
+      for (int k = 0; k < kPartialWaves; ++k) {
+        const float* tm = ws_time + ((size_t)w * kPartialWaves + k) * 2;
+        tiles += tm[0];
+        ticks = fmaxf(ticks, tm[1]);
+      }
+      if (tiles > 0.0f && ticks > 0.0f && tiles < 1e9f && ticks < 1e9f) {
+        atomicAdd(&ct[w & 7], tiles);
+        atomicAdd(&cs[w & 7], ticks);
+      }
+    }
+    __syncthreads();
+    if (tid < 8) {
+      float mean = 0.0f;
+      int nv = 0;
+      for (int c = 0; c < 8; ++c) {
+        const float r = cs[c] > 0.0f ? ct[c] / cs[c] : 0.0f;
+        if (r > 0.0f) {
+          mean += r;
+          ++nv;
+        }
+      }
+      const float r = cs[tid] > 0.0f ? ct[tid] / cs[tid] : 0.0f;
+      const float old = rates[tid];
+      if (nv > 0 && r > 0.0f) {
+        const float rel = fminf(fmaxf(r / (mean / (float)nv), 0.5f), 2.0f);
+        const bool ok = old >= 0.5f && old <= 2.0f;
+        rates[tid] = ok ? 0.5f * old + 0.5f * rel : rel;
+      }
+    }
+    return;
+  }
+
+  const int G = a.Hq / a.Hkv;
+  const int n_ml = a.Hq * P, n_bnd = a.Hkv * (P + 1);
+  const int per_layer = (int)combine_layer_floats(a.Hq, a.Hkv, P);
+  auto t_hM = [&](int l) { return lds + (size_t)l * per_layer; };
+  auto t_hI = [&](int l) { return t_hM(l) + a.Hq; };
+  auto t_mS = [&](int l) { return t_hI(l) + a.Hq; };
+  auto t_lS = [&](int l) { return t_mS(l) + n_ml; };
+  auto t_wp = [&](int l) { return t_lS(l) + n_ml; };
+  auto t_bd = [&](int l) { return (int*)(t_wp(l) + n_ml); };
+  float* cl = lds + (size_t)L * per_layer;  // [kCmbTiles][L][NSUB][2]: sum and max over heads
+
+  // tile of this lane; without a window the range starts at tile 0
+  int tlo = 0;
+  if constexpr (!RING) {
+    if (a.window > 0) {
+      const int ic = a.cur_pos[b];
+      const int thi0 = max(0, min(a.NT, ic / kTile + 1));
+      tlo = min(thi0, max(ic - a.window + 1, 0) / kTile);
+    }
+  }
+  const int t = tlo + (int)blockIdx.x * kCmbTiles + lane;
+  const int tc = min(max(t, 0), a.NT - 1);
+  auto load_records = [&](int l, int hc, float (&ev)[NSUB][HC]) {
+    const float* we = ws_f(min(l, L - 1), a.off_e);
+    if (G % 4 == 0) {
+#pragma unroll
+      for (int q = 0; q < HC / 4; ++q) {
+        const int hh = min(hc + 4 * q, a.Hq - 4);
+        const int gg = hh / G;
+        const size_t row = ((size_t)b * a.Hkv + gg) * a.NT + tc;
+#pragma unroll
+        for (int sb = 0; sb < NSUB; ++sb) {
+          const f32x4 e4 = *(const f32x4*)(we + (row * NSUB + sb) * G + (hh - gg * G));
+#pragma unroll
+          for (int k = 0; k < 4; ++k) ev[sb][4 * q + k] = e4[k];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < HC; ++k) {
+        const int hh = min(hc + k, a.Hq - 1);
+        const int gg = hh / G;
+        const size_t row = ((size_t)b * a.Hkv + gg) * a.NT + tc;
+#pragma unroll
+        for (int sb = 0; sb < NSUB; ++sb) ev[sb][k] = we[(row * NSUB + sb) * G + (hh - gg * G)];
+      }
+    }
+  };
+  // this wave's first two layers' records, both in flight from the start
+  float ev[NSUB][HC], ev_next[NSUB][HC];
+  load_records(wv, 0, ev);
+  load_records(wv + kCmbWaves, 0, ev_next);
+
+  // tables of every layer: eight layers' loads in flight at a time (the
+  // values of a layer are its maxima, sums and boundaries, read as floats)
+  const int per = 2 * n_ml + n_bnd;
+  for (int r0 = 0; r0 < per; r0 += NTH) {
+    const int r = r0 + tid;
+    const int rc = min(r, per - 1);
+    for (int l0 = 0; l0 < L; l0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int l = min(l0 + k, L - 1);
+        const char* base = a.lws[l];
+        const float* src = rc < n_ml       ? (const float*)(base + a.off_m) + (size_t)b * n_ml + rc
+                           : rc < 2 * n_ml ? (const float*)(base + a.off_l) + (size_t)b * n_ml + (rc - n_ml)
+                                           : (const float*)(base + a.off_bnd) + (size_t)b * n_bnd + (rc - 2 * n_ml);
+        v[k] = *src;  // a ring's boundary slots are never read
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int l = l0 + k;
+        if (l >= L || r >= per) continue;
+        float* dst = r < n_ml ? t_mS(l) + r : r < 2 * n_ml ? t_lS(l) + (r - n_ml) : (float*)t_bd(l) + (r - 2 * n_ml);
+        *dst = v[k];
+      }
+    }
+  }
+  const int i_cur = a.cur_pos[b];
+  int thi = a.NT;
+  if constexpr (!RING) thi = max(0, min(a.NT, i_cur / kTile + 1));
+  const bool m_live = t < thi;
+  const int lap_i = RING ? i_cur / a.C : 0;
+  __syncthreads();
+  for (int x = tid; x < L * a.Hq; x += NTH) {
+    const int l = x / a.Hq, hh = x % a.Hq;
+    merge_weights(t_mS(l) + hh * P, t_lS(l) + hh * P, P, t_wp(l) + hh, a.Hq, &t_hM(l)[hh], &t_hI(l)[hh]);
+  }
+  __syncthreads();
+
+  // ---- this wave's layers: per (tile, layer) sums over heads ----
+  for (int l = wv; l < L; l += kCmbWaves) {
+    const float* wp = t_wp(l);
+    const int* bnd = t_bd(l);
+    auto part_of = [&](int gg) -> int {
+      if constexpr (RING) {
+        return min(tc / a.tpp, P - 1);
+      } else {
+        const int* bg = bnd + gg * (P + 1);
+        int base = 0;
+        for (int n = P; n > 1;) {
+          const int half = n >> 1;
+          base = bg[base + half] <= tc ? base + half : base;
+          n -= half;
+        }
+        return base;
+      }
+    };
+    float acc[NSUB], mx[NSUB];
+#pragma unroll
+    for (int sb = 0; sb < NSUB; ++sb) {
+      acc[sb] = 0.0f;
+      mx[sb] = 0.0f;
+    }
+    for (int hc = 0; hc < a.Hq; hc += HC) {
+      if (hc > 0) load_records(l, hc, ev);
+      // the layer after next starts loading once this one's last chunk is in
+      // hand (ev_next already holds the next layer's first chunk, or is
+      // refilled from here when the head chunks were reloaded)
+      const bool last = hc + HC >= a.Hq;
+      if (last && a.Hq > HC && l + kCmbWaves < L) load_records(l + kCmbWaves, 0, ev_next);
+      float sc[HC];
+      if (G % 4 == 0) {
+        int pq[HC / 4];
+#pragma unroll
+        for (int q = 0; q < HC / 4; ++q) pq[q] = part_of(min(hc + 4 * q, a.Hq - 4) / G);
+        f32x4 w4[HC / 4];
+#pragma unroll
+        for (int q = 0; q < HC / 4; ++q) {
+          const int hh = min(hc + 4 * q, a.Hq - 4);
+          w4[q] = *(const f32x4*)(wp + pq[q] * a.Hq + hh);
+        }
+#pragma unroll
+        for (int q = 0; q < HC / 4; ++q)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) sc[4 * q + k] = hc + 4 * q + k < a.Hq ? w4[q][k] : 0.0f;
+      } else {
+        int pk[HC];
+#pragma unroll
+        for (int k = 0; k < HC; ++k) pk[k] = part_of(min(hc + k, a.Hq - 1) / G);
+#pragma unroll
+        for (int k = 0; k < HC; ++k) {
+          const int hh = min(hc + k, a.Hq - 1);
+          const float w = wp[pk[k] * a.Hq + hh];
+          sc[k] = hc + k < a.Hq ? w : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int sb = 0; sb < NSUB; ++sb) {
+#pragma unroll
+        for (int k = 0; k < HC; ++k) {
+          if (hc + k >= a.Hq) break;
+          const float v = ev[sb][k] * sc[k];
+          acc[sb] += v;
+          mx[sb] = fmaxf(mx[sb], v);
+        }
+      }
+      if (last) {
+#pragma unroll
+        for (int sb = 0; sb < NSUB; ++sb)
+#pragma unroll
+          for (int k = 0; k < HC; ++k) ev[sb][k] = ev_next[sb][k];
+        if (a.Hq <= HC && l + 2 * kCmbWaves < L) load_records(l + 2 * kCmbWaves, 0, ev_next);
+      }
+    }
+#pragma unroll
+    for (int sb = 0; sb < NSUB; ++sb) {
+      cl[((lane * L + l) * NSUB + sb) * 2] = acc[sb];
+      cl[((lane * L + l) * NSUB + sb) * 2 + 1] = mx[sb];
+    }
+  }
+  __syncthreads();
+
+  // ---- one lane per tile: the layers in call order ----
+  if (wv != 0 || !m_live) return;
+#pragma unroll
+  for (int sb = 0; sb < NSUB; ++sb) {
+    int blk = t;
+    if constexpr (RING) {
+      const int lap = ((lap_i & 1) == sb) ? lap_i : lap_i - 1;
+      blk = lap < 0 ? -1 : lap * (a.C / kTile) + t;
+    }
+    if (blk < 0 || blk >= a.nbmax) continue;
+    const size_t mi = (size_t)b * a.nbmax + blk;
+    float mass_run = a.mass != nullptr ? a.mass[mi] : 0.0f;
+    float max_run = a.mass_max != nullptr ? a.mass_max[mi] : 0.0f;
+    for (int l = 0; l < L; ++l) {
+      mass_run = mass_run + cl[((lane * L + l) * NSUB + sb) * 2];
+      max_run = fmaxf(max_run, cl[((lane * L + l) * NSUB + sb) * 2 + 1]);
+    }
+    if (a.mass != nullptr) a.mass[mi] = mass_run;
+    if (a.mass_max != nullptr) a.mass_max[mi] = max_run;
+  }
+}
+
+size_t combine_layers_lds_bytes(int Hq, int Hkv, int P, int L, bool ring) {
+  return ((size_t)L * combine_layer_floats(Hq, Hkv, P) + (size_t)kCmbTiles * L * (ring ? 2 : 1) * 2) * sizeof(float);
+}
+
+hipError_t launch_combine_layers(const CombineArgs& a, bool ring, hipStream_t st) {
+  if (!(a.mass || a.mass_max)) return hipSuccess;
+  const int n_chunks = (a.NT + kCmbTiles - 1) / kCmbTiles;
+  dim3 grid(n_chunks + a.n_layers, a.B), block(64 * kCmbWaves);
+  size_t lds = combine_layers_lds_bytes(a.Hq, a.Hkv, a.nparts, a.n_layers, ring);
+  if (lds < 16 * sizeof(float)) lds = 16 * sizeof(float);
+  if (ring) hipLaunchKernelGGL((kvs_combine_layers<true>), grid, block, lds, st, a);
+  else hipLaunchKernelGGL((kvs_combine_layers<false>), grid, block, lds, st, a);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -1321,8 +1636,9 @@ hipError_t launch_combine(const CombineArgs& a, bool ring, hipStream_t st) {
   // outputs are merged by the partial kernel: without mass work there is
   // nothing to do (the partition rates then keep their last values)
   if (!(a.mass || a.head_mass || a.mass_max)) return hipSuccess;
-  dim3 grid(a.n_mass_chunks + 1, a.B), block(256);
-  const size_t lds = combine_lds_bytes(a.Hq, a.Hkv, a.S, a.nparts);
+  dim3 grid(a.n_mass_chunks + a.n_layers, a.B), block(256);
+  size_t lds = (size_t)a.layers_per_chunk * combine_layer_floats(a.Hq, a.Hkv, a.nparts) * sizeof(float);
+  if (lds < 16 * sizeof(float)) lds = 16 * sizeof(float);
   if (ring) hipLaunchKernelGGL((kvs_combine<true>), grid, block, lds, st, a);
   else hipLaunchKernelGGL((kvs_combine<false>), grid, block, lds, st, a);
   return hipGetLastError();

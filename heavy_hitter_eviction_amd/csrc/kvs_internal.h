@@ -54,16 +54,17 @@ struct PartialArgs {
   void* out;
 };
 
+// Most layers one kvs_combine launch sums (kvs_tap_masses).
+constexpr int kMaxTapLayers = 128;
+
+// Block masses of n_layers calls' records, added in call order. Layer l's
+// workspace starts at lws[l]; every layer has the same plan (offsets).
 struct CombineArgs {
-  const float* ws_m;
-  const float* ws_l;
-  const float* ws_o;
-  const float* ws_e;
-  const int* ws_bnd;
-  const float* ws_time;
-  float* rates;   // updated from ws_time by one workgroup, or NULL
-  int n_wg;       // partial workgroups that wrote ws_time
-  int S;          // partial slots per (sequence, head)
+  const char* lws[kMaxTapLayers];
+  size_t off_m, off_l, off_e, off_bnd, off_time, off_rates;
+  int n_layers;
+  int layers_per_chunk;  // layers whose tables fit the LDS at once
+  int n_wg;       // partial workgroups per layer that wrote clock records
   const int32_t* cur_pos;
   float* mass;
   float* head_mass;  // [B][Hq][nbmax] per-head block masses (+=), or NULL
@@ -71,17 +72,20 @@ struct CombineArgs {
   int B, Hq, Hkv, C, NT, nbmax, tpp, nparts, n_mass_chunks, window;
 };
 
-// LDS of one combine workgroup: per-head max and 1/sum, every partial's max
-// and sum, per (head, partition) record weights and the partition
-// boundaries, or the rate accumulators (16 floats).
-inline size_t combine_lds_bytes(int Hq, int Hkv, int S, int P) {
-  const size_t f = 2 * (size_t)Hq + 2 * (size_t)Hq * S + (size_t)Hq * P + (size_t)Hkv * (P + 1);
-  return (f < 16 ? 16 : f) * sizeof(float);
+// LDS floats one layer's combine tables take: per-head max and 1/sum, the
+// partitions' maxima and sums, per (partition, head) record weights and the
+// partition boundaries. A combine workgroup also needs 16 floats for rates.
+__host__ __device__ inline size_t combine_layer_floats(int Hq, int Hkv, int P) {
+  return 2 * (size_t)Hq + 3 * (size_t)Hq * P + (size_t)Hkv * (P + 1);
 }
+constexpr size_t kCombineLdsBytes = 49152;
 
 hipError_t launch_partial(int kv, int d, const PartialArgs& a, bool scored, bool ring,
                           size_t lds_bytes, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, bool ring, hipStream_t st);
+// The layer-parallel form (no per-head masses); its LDS must fit kCombineLdsBytes.
+size_t combine_layers_lds_bytes(int Hq, int Hkv, int P, int L, bool ring);
+hipError_t launch_combine_layers(const CombineArgs& a, bool ring, hipStream_t st);
 
 hipError_t launch_encode_fp8(const void* src, int src_bf16, int64_t n_rows, int row_len,
                              uint8_t* codes, float* scales, hipStream_t st);

@@ -1,10 +1,12 @@
 """A whole scored decode step over L layers, driven through the C ABI.
 
 For every layer: append the new position's K/V (FP8-encoding when the cache
-is FP8), then the scored attention (partial + combine) that adds this layer's
-block masses into ``mass``; by default the append runs inside the attention's
-partial kernel (kvs_append_decode_attn), ``fused=False`` makes it a launch of
-its own. After the last layer the side-car closes the turn,
+is FP8), then the scored attention. By default the append runs inside the
+attention's partial kernel and each layer leaves its per-block sums in its own
+workspace (kvs_append_decode_attn_tap); after the last layer one call adds all
+layers' block masses into ``mass`` (kvs_tap_masses). ``tap=False`` adds them
+layer by layer instead (kvs_append_decode_attn / kvs_decode_attn_scored), and
+``fused=False`` makes the append a launch of its own. After the last layer the side-car closes the turn,
 and the heavy-hitter selection produces the keep mask. In evict mode that
 mask feeds the next step's attention, so dropped blocks are never read again
 (Context Optimization, "H2O KV Cache Eviction"); in score-only mode the full
@@ -32,7 +34,7 @@ def geom_of(w: Workload) -> api.CacheGeom:
 
 class ScoredDecoder:
     def __init__(self, w: Workload, evict: bool = False, device="cuda", layers: int | None = None,
-                 compact: bool = False, compact_every: int = 1, fused: bool = True):
+                 compact: bool = False, compact_every: int = 1, fused: bool = True, tap: bool = True):
         if compact and (w.ring or w.window or not w.select):
             raise ValueError("compaction needs a linear cache with selection and no window")
         if compact_every < 1:
@@ -42,12 +44,16 @@ class ScoredDecoder:
         self.compact = compact
         self.compact_every = compact_every
         self.fused = fused
+        self.tap = tap
         self.device = torch.device(device)
         self.geom = geom_of(w)
         self.n_layers = w.n_layers if layers is None else layers
         self.caches = [api.KVCache(self.geom, device) for _ in range(self.n_layers)]
         ws = api.decode_workspace_bytes(self.geom)
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
+        # tap mode: one workspace per layer, read once per step by tap_masses
+        self.workspaces = ([torch.empty(ws, dtype=torch.uint8, device=device) for _ in range(self.n_layers)]
+                           if tap else [])
         B, nb = w.batch, self.geom.nb
         f32 = dict(dtype=torch.float32, device=device)
         self.mass = torch.zeros((B, nb), **f32)
@@ -83,7 +89,13 @@ class ScoredDecoder:
         the int32 [B] absolute position being written and read."""
         for l in range(self.n_layers):
             self.append_attend_layer(l, q_layers[l], k_layers[l], v_layers[l], cur_pos)
+        self.finish_masses(cur_pos)
         self.close_turn(cur_pos)
+
+    def finish_masses(self, cur_pos: torch.Tensor):
+        """Tap mode: add every layer's block masses into ``mass`` (one call)."""
+        if self.tap:
+            api.tap_masses(self.geom, self.workspaces, cur_pos, mass_accum=self.mass)
 
     def append_attend_layer(self, layer: int, q, k_rows, v_rows, cur_pos: torch.Tensor,
                             keep: torch.Tensor | None = None, use_own_keep: bool = True):
@@ -91,6 +103,15 @@ class ScoredDecoder:
         scored attention of ``layer`` (one launch pair when fused)."""
         if use_own_keep:
             keep = self.keep if (self.evict and not self.w.window) else None
+        if self.tap:
+            if self.fused:
+                api.decode_attn_tap(self.caches[layer], q, cur_pos, self.out[layer], self.workspaces[layer],
+                                    keep_mask=keep, k_new=k_rows, v_new=v_rows)
+            else:
+                self.caches[layer].append(k_rows, v_rows, self.row_seq, cur_pos)
+                api.decode_attn_tap(self.caches[layer], q, cur_pos, self.out[layer], self.workspaces[layer],
+                                    keep_mask=keep)
+            return
         if self.fused:
             api.append_decode_attn(self.caches[layer], k_rows, v_rows, q, cur_pos, self.out[layer],
                                    self.workspace, mass_accum=self.mass, keep_mask=keep)
@@ -109,6 +130,7 @@ class ScoredDecoder:
         for l in range(self.n_layers):
             self.append_attend_layer(l, q_layers[l], k_layers[l], v_layers[l], cur, keep=self.keep,
                                      use_own_keep=False)
+        self.finish_masses(cur)
         api.update_sidecar(self.mass, self.attended, self.ema, self.cum, self.traj,
                            self.step_index, self.w.alpha)
         api.select_blocks(self.cum, cur, self.w.budget_blocks, self.w.recent_tokens, self.w.sink_tokens,

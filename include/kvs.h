@@ -207,6 +207,44 @@ KVS_API int kvs_decode_attn_scored(const kvs_geom* geom, const void* q, const vo
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kvs_decode_attn_tap, kvs_append_decode_attn_tap, kvs_tap_masses -- the
+ * scored decode step with the block masses added once per step instead of
+ * once per layer (Context views at marginal cost, Tier 0: the tap leaves
+ * per-block sums that are reduced later; section 2: the side-car consumes
+ * them once per turn).
+ *
+ * The two per-layer calls take the arguments of kvs_decode_attn_scored and
+ * kvs_append_decode_attn without mass_accum: they compute ``out`` in the same
+ * way and leave the layer's per-block sums in ``workspace``, which must then
+ * stay untouched until kvs_tap_masses has read it (one workspace per layer).
+ * kvs_tap_masses then adds the masses of all n_layers calls, in order, exactly
+ * as one scored call per layer would have: mass_accum (and head_mass /
+ * mass_max as in kvs_decode_attn_profiled) get the same values, bit for bit
+ * in deterministic mode.
+ *
+ *   workspaces  host array of n_layers device workspace pointers, the ones
+ *               the per-layer calls used, in call order (1 <= n_layers <= 128)
+ *   cur_pos     the [B] positions the per-layer calls used
+ *   mass_accum, head_mass, mass_max: as in kvs_decode_attn_profiled, each
+ *               may be NULL (all NULL: nothing to do)
+ * Errors: KVS_EINVAL for a bad geometry, layer count or NULL pointer,
+ * KVS_EALIGN, KVS_EWS if workspace_bytes is below kvs_decode_workspace_bytes().
+ */
+KVS_API int kvs_decode_attn_tap(const kvs_geom* geom, const void* q, const void* k_cache,
+                                const void* v_cache, const float* k_scale, const float* v_scale,
+                                const int32_t* pos_of_slot, const int32_t* cur_pos,
+                                const uint32_t* keep_mask, void* out, void* workspace,
+                                size_t workspace_bytes, void* stream);
+KVS_API int kvs_append_decode_attn_tap(const kvs_geom* geom, const void* k_new, const void* v_new,
+                                       int32_t src_dtype, const void* q, void* k_cache, void* v_cache,
+                                       float* k_scale, float* v_scale, int32_t* pos_of_slot,
+                                       const int32_t* cur_pos, const uint32_t* keep_mask, void* out,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+KVS_API int kvs_tap_masses(const kvs_geom* geom, void* const* workspaces, int32_t n_layers,
+                           size_t workspace_bytes, const int32_t* cur_pos, float* mass_accum,
+                           float* head_mass, float* mass_max, void* stream);
+
+/*
  * kvs_decode_partial, kvs_decode_combine -- the two phases of
  * kvs_decode_attn_scored, with the same arguments and checks. The partial
  * phase reads the cache and leaves, per (sequence, query head, partition of
