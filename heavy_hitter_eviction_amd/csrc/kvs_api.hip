@@ -53,7 +53,7 @@ int check_geom(const kvs_geom* g) {
 
 struct Plan {
   int NT, tpp, nparts, nsub, G, S, tl_cap, n_wg, oslots, adapt;
-  size_t off_m, off_l, off_o, off_e, off_bnd, off_time, off_rates, off_cnt, total;
+  size_t off_m, off_l, off_o, off_e, off_bnd, off_w, off_time, off_rates, off_cnt, total;
   size_t lds_partial;
 };
 
@@ -111,7 +111,8 @@ Plan make_plan(const kvs_geom* g) {
   p.off_o = round256(p.off_l + bh * p.S * 4);
   p.off_e = round256(p.off_o + bh * p.S * g->head_dim * 4);
   p.off_bnd = round256(p.off_e + (size_t)g->batch * p.NT * p.nsub * g->n_q_heads * 4);
-  p.off_time = round256(p.off_bnd + (size_t)pairs * (p.nparts + 1) * 4);
+  p.off_w = round256(p.off_bnd + (size_t)pairs * (p.nparts + 1) * 4);
+  p.off_time = round256(p.off_w + bh * p.nparts * 4);
   p.off_rates = round256(p.off_time + (size_t)p.n_wg * nw * 2 * 4);
   p.off_cnt = round256(p.off_rates + 8 * 4);
   p.total = round256(p.off_cnt + (size_t)pairs * 8);
@@ -244,6 +245,7 @@ int decode_setup(const kvs_geom* g, const void* q, const void* k_cache, const vo
   a->ws_m = (float*)(ws + p.off_m); a->ws_l = (float*)(ws + p.off_l);
   a->ws_o = (float*)(ws + p.off_o); a->ws_e = (float*)(ws + p.off_e);
   a->ws_bnd = (int*)(ws + p.off_bnd); a->ws_time = (float*)(ws + p.off_time);
+  a->ws_w = (float*)(ws + p.off_w);
   a->pair_cnt = (unsigned long long*)(ws + p.off_cnt);
   a->token = next_token();
   a->out = out;
@@ -255,7 +257,7 @@ int decode_setup(const kvs_geom* g, const void* q, const void* k_cache, const vo
   a->scale_log2 = g->softmax_scale * 1.4426950408889634f;
   *c = kvs::CombineArgs{};
   c->lws[0] = ws; c->n_layers = 1; c->layers_per_chunk = 1;
-  c->off_m = p.off_m; c->off_l = p.off_l; c->off_e = p.off_e; c->off_bnd = p.off_bnd;
+  c->off_w = p.off_w; c->off_e = p.off_e; c->off_bnd = p.off_bnd;
   c->off_time = p.off_time; c->off_rates = p.off_rates;
   c->cur_pos = cur_pos; c->n_wg = p.n_wg;
   c->mass = mass_accum;
@@ -412,7 +414,7 @@ int kvs_tap_masses(const kvs_geom* g, void* const* workspaces, int32_t n_layers,
   const size_t per_layer = kvs::combine_layer_floats(g->n_q_heads, g->n_kv_heads, p.nparts) * 4;
   const int fit = (int)(kvs::kCombineLdsBytes / per_layer);
   c.layers_per_chunk = fit < 1 ? 1 : (fit < n_layers ? fit : n_layers);
-  c.off_m = p.off_m; c.off_l = p.off_l; c.off_e = p.off_e; c.off_bnd = p.off_bnd;
+  c.off_w = p.off_w; c.off_e = p.off_e; c.off_bnd = p.off_bnd;
   c.off_time = p.off_time; c.off_rates = p.off_rates;
   c.n_wg = p.n_wg; c.cur_pos = cur_pos;
   c.mass = mass_accum; c.head_mass = head_mass; c.mass_max = mass_max;

@@ -983,6 +983,9 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
       __syncthreads();
       for (int hh = threadIdx.x; hh < G; hh += NTH) merge_weights(mT + hh * P, lT + hh * P, P, wT + hh, G, &hMt[hh], &hIt[hh]);
       __syncthreads();
+      // the same weights scale the block records in the mass combine
+      for (int x = threadIdx.x; x < G * P; x += NTH)
+        a.ws_w[((size_t)b * P + x / G) * a.Hq + hq0 + x % G] = wT[x];
       for (int x = threadIdx.x; x < G * D; x += NTH) {
         const int hh = x / D, dd = x % D;
         const float* o_src = a.ws_o + (pbase + hh) * P * D + dd;
@@ -1001,19 +1004,59 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   }
 }
 
+// ---- block records for the mass combines ----
+// Records of heads hc .. hc + HC - 1 (clamped to Hq - 1; the caller masks the
+// heads past Hq) of one tile, one layer and one sequence: rec covers the
+// sequence's [Hkv][NT][NSUB][G] records, vo is the tile's byte offset
+// (tc NSUB G 4). Head h sits at row h / G, entry h % G: the per-head part of
+// the address is the same for the whole wave (a scalar offset), so the loads
+// need one address register between them. With V4 (G % 4 == 0) four heads of
+// a group come in one 16-byte load, consecutive lanes (tiles) reading
+// consecutive 16-byte pieces.
+template <int NSUB, int HC, bool V4>
+__device__ __forceinline__ void load_rec(float (&ev)[NSUB][HC], __amdgpu_buffer_rsrc_t rec, uint32_t vo, int hc,
+                                         int Hq, int G, int NT) {
+  if constexpr (V4) {
+#pragma unroll
+    for (int q = 0; q < HC / 4; ++q) {
+      const int hh = min(hc + 4 * q, Hq - 4);
+      const int gg = hh / G;
+      const uint32_t so = ((uint32_t)gg * NT * NSUB * G + (hh - gg * G)) * 4;
+#pragma unroll
+      for (int sb = 0; sb < NSUB; ++sb) {
+        const f32x4 e4 =
+            __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rec, (int)vo, (int)(so + sb * G * 4), 0));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) ev[sb][4 * q + k] = e4[k];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < HC; ++k) {
+      const int hh = min(hc + k, Hq - 1);
+      const int gg = hh / G;
+      const uint32_t so = ((uint32_t)gg * NT * NSUB * G + (hh - gg * G)) * 4;
+#pragma unroll
+      for (int sb = 0; sb < NSUB; ++sb)
+        ev[sb][k] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rec, (int)vo, (int)(so + sb * G * 4), 0));
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Combine: grid (n_mass_chunks + n_layers, B), 256 threads: the block masses
 // of n_layers calls (one for kvs_decode_combine, a whole step's layers for
 // kvs_tap_masses), added in call order.
-// Per layer and head h of its sequence a workgroup reduces the partitions'
-// partials to M_h = max_p m_p and L_h = sum_p l_p 2^(m_p - M_h); then each
-// thread adds, for its tile and sub-block, sum_h E 2^(m_p(tile) - M_h) / L_h
-// over the heads in ascending order, layer after layer, into mass_accum, E
-// being the tile's record relative to its partition's max. (The outputs were
-// merged by the partial kernel.) The extra columns (sequence 0 only) refresh
-// each layer's per-class streaming rates from its clock records.
+// Each thread adds, for its tile and sub-block, sum_h E w_p(tile),h over the
+// heads in ascending order, layer after layer, into mass_accum: E is the
+// tile's record relative to its partition's max, and w_p,h = 2^(m_p - M_h) /
+// L_h (M_h = max_p m_p, L_h = sum_p l_p 2^(m_p - M_h)) the weight the partial
+// kernel's output merge computed and stored for partition p and head h. The
+// extra columns (sequence 0 only) refresh each layer's per-class streaming
+// rates from its clock records.
 // ---------------------------------------------------------------------------
-template <bool RING>
+template <bool RING, bool V4>
 __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
   extern __shared__ float lds[];
   const int b = blockIdx.y;
@@ -1071,7 +1114,7 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
 
   // Each workgroup first issues the global loads that need nothing from the
   // shared tables (the first layer's records of its tile, the current
-  // masses, the first layers' partition maxima, sums and boundaries), then
+  // masses, the first layers' record weights and boundaries), then
   // builds the tables and finishes, the next layer's records loading while
   // one layer is summed. Loads are unconditional (indices clamped into
   // range, unused values masked later): conditional loads make the compiler
@@ -1079,35 +1122,29 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
   constexpr int NSUB = RING ? 2 : 1;
   constexpr int HC = RING ? 16 : 32;   // heads per record chunk
   const int G = a.Hq / a.Hkv;
-  const int n_ml = a.Hq * P;                 // partition maxima (and sums) per layer
+  const int n_ml = a.Hq * P;                 // record weights per layer
   const int n_bnd = a.Hkv * (P + 1);         // boundaries per layer
   const int lc0 = min(L, a.layers_per_chunk);
   // layer-table block of layer slot s in LDS
   const int per_layer = (int)combine_layer_floats(a.Hq, a.Hkv, P);
-  auto t_hM = [&](int s_) { return lds + (size_t)s_ * per_layer; };           // [Hq]
-  auto t_hI = [&](int s_) { return t_hM(s_) + a.Hq; };                        // [Hq]
-  auto t_mS = [&](int s_) { return t_hI(s_) + a.Hq; };                        // [Hq][P]
-  auto t_lS = [&](int s_) { return t_mS(s_) + n_ml; };                        // [Hq][P]
-  auto t_wp = [&](int s_) { return t_lS(s_) + n_ml; };                        // [P][Hq]
+  auto t_wp = [&](int s_) { return lds + (size_t)s_ * per_layer; };          // [P][Hq]
   auto t_bd = [&](int s_) { return (int*)(t_wp(s_) + n_ml); };               // [Hkv][P + 1]
-  // the first chunk's maxima/sums/boundaries: two per thread prefetched
-  const int n_stage = lc0 * (2 * n_ml + n_bnd);
+  // the first chunk's weights/boundaries: two per thread prefetched
+  const int n_stage = lc0 * (n_ml + n_bnd);
   auto stage_src = [&](int l0, int x) -> float {
     // value x of the staged tables of layers [l0, l0 + lc): per layer
-    // n_ml maxima, n_ml sums, n_bnd boundaries (bit patterns)
-    const int per = 2 * n_ml + n_bnd;
+    // n_ml weights, then n_bnd boundaries (bit patterns)
+    const int per = n_ml + n_bnd;
     const int l = l0 + x / per, r = x % per;
-    if (r < n_ml) return ws_f(l, a.off_m)[(size_t)b * n_ml + r];
-    if (r < 2 * n_ml) return ws_f(l, a.off_l)[(size_t)b * n_ml + r - n_ml];
+    if (r < n_ml) return ws_f(l, a.off_w)[(size_t)b * n_ml + r];
     if constexpr (RING) return 0.0f;
-    return __builtin_bit_cast(float, ((const int*)(a.lws[l] + a.off_bnd))[(size_t)b * n_bnd + r - 2 * n_ml]);
+    return __builtin_bit_cast(float, ((const int*)(a.lws[l] + a.off_bnd))[(size_t)b * n_bnd + r - n_ml]);
   };
   auto stage_dst = [&](int x) -> float* {
-    const int per = 2 * n_ml + n_bnd;
+    const int per = n_ml + n_bnd;
     const int s_ = x / per, r = x % per;
-    if (r < n_ml) return t_mS(s_) + r;
-    if (r < 2 * n_ml) return t_lS(s_) + (r - n_ml);
-    return (float*)t_bd(s_) + (r - 2 * n_ml);
+    if (r < n_ml) return t_wp(s_) + r;
+    return (float*)t_bd(s_) + (r - n_ml);
   };
   const float pre0 = stage_src(0, min(tid, n_stage - 1));
   const float pre1 = stage_src(0, min(tid + 256, n_stage - 1));
@@ -1128,33 +1165,12 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
   // records of heads past Hq (clamped duplicates) get weight 0; a dead
   // thread's values are never used
   const int tc = min(max(t, 0), a.NT - 1);
+  // this sequence's records of layer l; the tile's byte offset
+  const uint32_t rec_bytes = (uint32_t)a.Hkv * a.NT * NSUB * G * 4;
+  const uint32_t rec_vo = (uint32_t)tc * NSUB * G * 4;
   auto load_records = [&](int l, int hc, float (&ev)[NSUB][HC]) {
-    const float* we = ws_f(l, a.off_e);
-    if (G % 4 == 0) {
-      // four heads of one group per 16-byte load; consecutive threads
-      // (tiles) read consecutive 16-byte pieces
-#pragma unroll
-      for (int q = 0; q < HC / 4; ++q) {
-        const int hh = min(hc + 4 * q, a.Hq - 4);
-        const int gg = hh / G;
-        const size_t row = ((size_t)b * a.Hkv + gg) * a.NT + tc;
-#pragma unroll
-        for (int sb = 0; sb < NSUB; ++sb) {
-          const f32x4 e4 = *(const f32x4*)(we + (row * NSUB + sb) * G + (hh - gg * G));
-#pragma unroll
-          for (int k = 0; k < 4; ++k) ev[sb][4 * q + k] = e4[k];
-        }
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < HC; ++k) {
-        const int hh = min(hc + k, a.Hq - 1);
-        const int gg = hh / G;
-        const size_t row = ((size_t)b * a.Hkv + gg) * a.NT + tc;
-#pragma unroll
-        for (int sb = 0; sb < NSUB; ++sb) ev[sb][k] = we[(row * NSUB + sb) * G + (hh - gg * G)];
-      }
-    }
+    const char* base = a.lws[l] + a.off_e + (size_t)b * rec_bytes;
+    load_rec<NSUB, HC, V4>(ev, make_rsrc(base, rec_bytes), rec_vo, hc, a.Hq, G, a.NT);
   };
   float ev[NSUB][HC], ev_next[NSUB][HC];
   load_records(0, 0, ev);
@@ -1193,18 +1209,13 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
     const int lc = min(lc0, L - l0);
     // ---- tables of layers [l0, l0 + lc) ----
     if (l0 > 0) __syncthreads();  // the previous chunk's tables are done with
-    const int n_st = lc * (2 * n_ml + n_bnd);
+    const int n_st = lc * (n_ml + n_bnd);
     if (l0 == 0) {
       if (tid < n_st) *stage_dst(tid) = pre0;
       if (tid + 256 < n_st) *stage_dst(tid + 256) = pre1;
       for (int x = tid + 512; x < n_st; x += 256) *stage_dst(x) = stage_src(0, x);
     } else {
       for (int x = tid; x < n_st; x += 256) *stage_dst(x) = stage_src(l0, x);
-    }
-    __syncthreads();
-    for (int x = tid; x < lc * a.Hq; x += 256) {
-      const int s_ = x / a.Hq, hh = x % a.Hq;
-      merge_weights(t_mS(s_) + hh * P, t_lS(s_) + hh * P, P, t_wp(s_) + hh, a.Hq, &t_hM(s_)[hh], &t_hI(s_)[hh]);
     }
     __syncthreads();
     if (!m_live) continue;
@@ -1245,55 +1256,62 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
         // the next layer's first records load while this chunk is summed
         const bool prefetch = hc + HC >= a.Hq && l + 1 < L;
         if (prefetch) load_records(l + 1, 0, ev_next);
-        // weights of the chunk's heads: unconditional (clamped) LDS reads, a
-        // group's four heads at once when G % 4 == 0
-        float sc[HC];
-        if (G % 4 == 0) {
-          int pq[HC / 4];
-#pragma unroll
-          for (int q = 0; q < HC / 4; ++q) pq[q] = part_of(min(hc + 4 * q, a.Hq - 4) / G);
-          f32x4 w4[HC / 4];
+        // the chunk's products E w, in place of its records: a group's four
+        // weights read from LDS (unconditional, clamped) as they are used,
+        // heads in ascending order per sub-block; heads past Hq add +0 (sums
+        // and maxima are >= 0: no change)
+        if constexpr (V4) {
 #pragma unroll
           for (int q = 0; q < HC / 4; ++q) {
             const int hh = min(hc + 4 * q, a.Hq - 4);
-            w4[q] = *(const f32x4*)(wp + pq[q] * a.Hq + hh);
+            const f32x4 w4 = *(const f32x4*)(wp + part_of(hh / G) * a.Hq + hh);
+#pragma unroll
+            for (int sb = 0; sb < NSUB; ++sb)
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                const float v = hc + 4 * q + k < a.Hq ? ev[sb][4 * q + k] * w4[k] : 0.0f;
+                ev[sb][4 * q + k] = v;
+                acc[sb] += v;
+                mx[sb] = fmaxf(mx[sb], v);
+              }
           }
-#pragma unroll
-          for (int q = 0; q < HC / 4; ++q)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) sc[4 * q + k] = hc + 4 * q + k < a.Hq ? w4[q][k] : 0.0f;
         } else {
-          int pk[HC];
-#pragma unroll
-          for (int k = 0; k < HC; ++k) pk[k] = part_of(min(hc + k, a.Hq - 1) / G);
 #pragma unroll
           for (int k = 0; k < HC; ++k) {
             const int hh = min(hc + k, a.Hq - 1);
-            const float w = wp[pk[k] * a.Hq + hh];
-            sc[k] = hc + k < a.Hq ? w : 0.0f;
+            const float w = wp[part_of(hh / G) * a.Hq + hh];
+#pragma unroll
+            for (int sb = 0; sb < NSUB; ++sb) {
+              const float v = hc + k < a.Hq ? ev[sb][k] * w : 0.0f;
+              ev[sb][k] = v;
+              acc[sb] += v;
+              mx[sb] = fmaxf(mx[sb], v);
+            }
           }
         }
 #pragma unroll
         for (int sb = 0; sb < NSUB; ++sb) {
-#pragma unroll
-          for (int k = 0; k < HC; ++k) {
-            if (hc + k >= a.Hq) break;
-            const float v = ev[sb][k] * sc[k];
-            acc[sb] += v;
-            mx[sb] = fmaxf(mx[sb], v);
-          }
           if (a.head_mass != nullptr && blk[sb] >= 0) {
-            float* hp = a.head_mass + ((size_t)b * a.Hq + hc) * a.nbmax + blk[sb];
-            // per-head masses, eight read-modify-writes in flight at a time
+            // per-head masses, eight read-modify-writes in flight at a time:
+            // the sequence's [Hq][nbmax] rows as one buffer, the block as the
+            // lane's offset and the head as a scalar one
+            const __amdgpu_buffer_rsrc_t hr =
+                make_rsrc(a.head_mass + (size_t)b * a.Hq * a.nbmax, (uint32_t)a.Hq * a.nbmax * 4);
+            const uint32_t hvo = (uint32_t)blk[sb] * 4;
 #pragma unroll
             for (int k0 = 0; k0 < HC; k0 += 8) {
               if (hc + k0 >= a.Hq) break;
               float hv[8];
 #pragma unroll
-              for (int k = 0; k < 8; ++k) hv[k] = hp[(size_t)min(k0 + k, a.Hq - 1 - hc) * a.nbmax];
+              for (int k = 0; k < 8; ++k) {
+                const uint32_t so = (uint32_t)min(hc + k0 + k, a.Hq - 1) * a.nbmax * 4;
+                hv[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(hr, (int)hvo, (int)so, 0));
+              }
 #pragma unroll
               for (int k = 0; k < 8; ++k)
-                if (hc + k0 + k < a.Hq) hp[(size_t)(k0 + k) * a.nbmax] = hv[k] + ev[sb][k0 + k] * sc[k0 + k];
+                if (hc + k0 + k < a.Hq)
+                  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, hv[k] + ev[sb][k0 + k]), hr, (int)hvo,
+                                                        (int)((uint32_t)(hc + k0 + k) * a.nbmax * 4), 0);
             }
           }
         }
@@ -1328,17 +1346,22 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
 // lane), keeping each (tile, layer)'s sum over heads, computed exactly as
 // kvs_combine does, in LDS; then one lane per tile adds them in layer order
 // to the current mass, so the result equals the layer-by-layer sum bit for
-// bit. The tables of all layers are in LDS at once.
+// bit. A wave stages only its own layers' weights and boundaries, loaded
+// together with its records, so the one barrier is before the final sums.
 // ---------------------------------------------------------------------------
 constexpr int kCmbTiles = 64;
 constexpr int kCmbWaves = 8;
 
-template <bool RING>
-__global__ __launch_bounds__(64 * kCmbWaves) void kvs_combine_layers(CombineArgs a) {
+// Two workgroups per compute unit (<= 128 VGPRs): the mass workgroups of the
+// 397B-like step (16 sequences x 32 chunks) are then all resident at once.
+template <bool RING, bool V4>
+__global__ __launch_bounds__(64 * kCmbWaves) __attribute__((amdgpu_waves_per_eu(4)))
+void kvs_combine_layers(CombineArgs a) {
   constexpr int NTH = 64 * kCmbWaves;
   extern __shared__ float lds[];
   const int b = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: per-layer pointers load as scalars
   const int P = a.nparts, L = a.n_layers;
   constexpr int NSUB = RING ? 2 : 1;
   constexpr int HC = RING ? 16 : 32;
@@ -1390,16 +1413,13 @@ __global__ __launch_bounds__(64 * kCmbWaves) void kvs_combine_layers(CombineArgs
 
   const int G = a.Hq / a.Hkv;
   const int n_ml = a.Hq * P, n_bnd = a.Hkv * (P + 1);
-  const int per_layer = (int)combine_layer_floats(a.Hq, a.Hkv, P);
-  auto t_hM = [&](int l) { return lds + (size_t)l * per_layer; };
-  auto t_hI = [&](int l) { return t_hM(l) + a.Hq; };
-  auto t_mS = [&](int l) { return t_hI(l) + a.Hq; };
-  auto t_lS = [&](int l) { return t_mS(l) + n_ml; };
-  auto t_wp = [&](int l) { return t_lS(l) + n_ml; };
+  const int per = n_ml + n_bnd;  // one layer's table: weights [P][Hq], boundaries [Hkv][P + 1]
+  auto t_wp = [&](int l) { return lds + (size_t)l * per; };
   auto t_bd = [&](int l) { return (int*)(t_wp(l) + n_ml); };
-  float* cl = lds + (size_t)L * per_layer;  // [kCmbTiles][L][NSUB][2]: sum and max over heads
+  float* cl = lds + (size_t)L * per;  // [kCmbTiles][L][NSUB][2]: sum and max over heads
 
-  // tile of this lane; without a window the range starts at tile 0
+  // tile of this lane; without a window the range starts at tile 0, so the
+  // loads below need not wait for cur_pos
   int tlo = 0;
   if constexpr (!RING) {
     if (a.window > 0) {
@@ -1410,79 +1430,65 @@ __global__ __launch_bounds__(64 * kCmbWaves) void kvs_combine_layers(CombineArgs
   }
   const int t = tlo + (int)blockIdx.x * kCmbTiles + lane;
   const int tc = min(max(t, 0), a.NT - 1);
+  const uint32_t rec_bytes = (uint32_t)a.Hkv * a.NT * NSUB * G * 4;
+  const uint32_t rec_vo = (uint32_t)tc * NSUB * G * 4;
   auto load_records = [&](int l, int hc, float (&ev)[NSUB][HC]) {
-    const float* we = ws_f(min(l, L - 1), a.off_e);
-    if (G % 4 == 0) {
-#pragma unroll
-      for (int q = 0; q < HC / 4; ++q) {
-        const int hh = min(hc + 4 * q, a.Hq - 4);
-        const int gg = hh / G;
-        const size_t row = ((size_t)b * a.Hkv + gg) * a.NT + tc;
-#pragma unroll
-        for (int sb = 0; sb < NSUB; ++sb) {
-          const f32x4 e4 = *(const f32x4*)(we + (row * NSUB + sb) * G + (hh - gg * G));
-#pragma unroll
-          for (int k = 0; k < 4; ++k) ev[sb][4 * q + k] = e4[k];
-        }
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < HC; ++k) {
-        const int hh = min(hc + k, a.Hq - 1);
-        const int gg = hh / G;
-        const size_t row = ((size_t)b * a.Hkv + gg) * a.NT + tc;
-#pragma unroll
-        for (int sb = 0; sb < NSUB; ++sb) ev[sb][k] = we[(row * NSUB + sb) * G + (hh - gg * G)];
-      }
-    }
+    const char* base = a.lws[min(l, L - 1)] + a.off_e + (size_t)b * rec_bytes;
+    load_rec<NSUB, HC, V4>(ev, make_rsrc(base, rec_bytes), rec_vo, hc, a.Hq, G, a.NT);
   };
-  // this wave's first two layers' records, both in flight from the start
+  // Each wave stages the tables of its own layers (wv, wv + 8, ...) and reads
+  // only those, so no workgroup barrier comes before the sums. The first two
+  // layers' tables (two values per lane each) are issued ahead of the
+  // records, so storing them waits for nothing else.
+  auto tab_val = [&](int l, int r) -> float {
+    const char* base = a.lws[min(l, L - 1)];
+    const int rc = min(r, per - 1);
+    return rc < n_ml ? ((const float*)(base + a.off_w))[(size_t)b * n_ml + rc]
+                     : ((const float*)(base + a.off_bnd))[(size_t)b * n_bnd + (rc - n_ml)];  // a ring's are unused
+  };
+  float tv[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) tv[j][k] = tab_val(wv + j * kCmbWaves, lane + 64 * k);
+  asm volatile("" ::: "memory");
   float ev[NSUB][HC], ev_next[NSUB][HC];
   load_records(wv, 0, ev);
   load_records(wv + kCmbWaves, 0, ev_next);
-
-  // tables of every layer: eight layers' loads in flight at a time (the
-  // values of a layer are its maxima, sums and boundaries, read as floats)
-  const int per = 2 * n_ml + n_bnd;
-  for (int r0 = 0; r0 < per; r0 += NTH) {
-    const int r = r0 + tid;
-    const int rc = min(r, per - 1);
-    for (int l0 = 0; l0 < L; l0 += 8) {
-      float v[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int l = min(l0 + k, L - 1);
-        const char* base = a.lws[l];
-        const float* src = rc < n_ml       ? (const float*)(base + a.off_m) + (size_t)b * n_ml + rc
-                           : rc < 2 * n_ml ? (const float*)(base + a.off_l) + (size_t)b * n_ml + (rc - n_ml)
-                                           : (const float*)(base + a.off_bnd) + (size_t)b * n_bnd + (rc - 2 * n_ml);
-        v[k] = *src;  // a ring's boundary slots are never read
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int l = l0 + k;
-        if (l >= L || r >= per) continue;
-        float* dst = r < n_ml ? t_mS(l) + r : r < 2 * n_ml ? t_lS(l) + (r - n_ml) : (float*)t_bd(l) + (r - 2 * n_ml);
-        *dst = v[k];
-      }
+  // a linear cache's block is the tile: wave 0 fetches the current masses
+  // it adds to now (a ring's blocks depend on cur_pos, read at the end)
+  float mass0 = 0.0f, max0 = 0.0f;
+  if constexpr (!RING) {
+    if (wv == 0) {
+      const size_t mi = (size_t)b * a.nbmax + min(tc, a.nbmax - 1);
+      mass0 = a.mass != nullptr ? a.mass[mi] : 0.0f;
+      max0 = a.mass_max != nullptr ? a.mass_max[mi] : 0.0f;
     }
   }
-  const int i_cur = a.cur_pos[b];
-  int thi = a.NT;
-  if constexpr (!RING) thi = max(0, min(a.NT, i_cur / kTile + 1));
-  const bool m_live = t < thi;
-  const int lap_i = RING ? i_cur / a.C : 0;
-  __syncthreads();
-  for (int x = tid; x < L * a.Hq; x += NTH) {
-    const int l = x / a.Hq, hh = x % a.Hq;
-    merge_weights(t_mS(l) + hh * P, t_lS(l) + hh * P, P, t_wp(l) + hh, a.Hq, &t_hM(l)[hh], &t_hI(l)[hh]);
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int l = wv + j * kCmbWaves;
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      if (l < L && lane + 64 * k < per) t_wp(l)[lane + 64 * k] = tv[j][k];
   }
-  __syncthreads();
-
-  // ---- this wave's layers: per (tile, layer) sums over heads ----
+  // the rest (layers past a wave's second, entries past 128 of a layer)
   for (int l = wv; l < L; l += kCmbWaves) {
+    const int r0 = l < wv + 2 * kCmbWaves ? 128 : 0;
+    for (int r = r0 + lane; r < per; r += 64) t_wp(l)[r] = tab_val(l, r);
+  }
+  // ---- this wave's layers: per (tile, layer) sums over heads ----
+  // Layer l's sum and max over heads for this lane's tile into cl, its first
+  // head chunk given in ev (further chunks, when Hq > HC, loaded into ev here).
+  // Heads in ascending order per sub-block; each group's four weights are read
+  // from LDS as they are used.
+  auto sum_layer = [&](int l, float (&ev)[NSUB][HC]) {
     const float* wp = t_wp(l);
     const int* bnd = t_bd(l);
+    // partition that produced tile tc's records for KV head gg: a ring splits
+    // evenly; a linear range at the stored boundaries (the last one at or
+    // below tc; boundary 0 is the range start)
     auto part_of = [&](int gg) -> int {
       if constexpr (RING) {
         return min(tc / a.tpp, P - 1);
@@ -1505,53 +1511,33 @@ __global__ __launch_bounds__(64 * kCmbWaves) void kvs_combine_layers(CombineArgs
     }
     for (int hc = 0; hc < a.Hq; hc += HC) {
       if (hc > 0) load_records(l, hc, ev);
-      // the layer after next starts loading once this one's last chunk is in
-      // hand (ev_next already holds the next layer's first chunk, or is
-      // refilled from here when the head chunks were reloaded)
-      const bool last = hc + HC >= a.Hq;
-      if (last && a.Hq > HC && l + kCmbWaves < L) load_records(l + kCmbWaves, 0, ev_next);
-      float sc[HC];
-      if (G % 4 == 0) {
-        int pq[HC / 4];
-#pragma unroll
-        for (int q = 0; q < HC / 4; ++q) pq[q] = part_of(min(hc + 4 * q, a.Hq - 4) / G);
-        f32x4 w4[HC / 4];
+      // heads past Hq add +0 (sums and maxima are >= 0: no change)
+      if constexpr (V4) {
 #pragma unroll
         for (int q = 0; q < HC / 4; ++q) {
           const int hh = min(hc + 4 * q, a.Hq - 4);
-          w4[q] = *(const f32x4*)(wp + pq[q] * a.Hq + hh);
+          const f32x4 w4 = *(const f32x4*)(wp + part_of(hh / G) * a.Hq + hh);
+#pragma unroll
+          for (int sb = 0; sb < NSUB; ++sb)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const float v = hc + 4 * q + k < a.Hq ? ev[sb][4 * q + k] * w4[k] : 0.0f;
+              acc[sb] += v;
+              mx[sb] = fmaxf(mx[sb], v);
+            }
         }
-#pragma unroll
-        for (int q = 0; q < HC / 4; ++q)
-#pragma unroll
-          for (int k = 0; k < 4; ++k) sc[4 * q + k] = hc + 4 * q + k < a.Hq ? w4[q][k] : 0.0f;
       } else {
-        int pk[HC];
-#pragma unroll
-        for (int k = 0; k < HC; ++k) pk[k] = part_of(min(hc + k, a.Hq - 1) / G);
 #pragma unroll
         for (int k = 0; k < HC; ++k) {
           const int hh = min(hc + k, a.Hq - 1);
-          const float w = wp[pk[k] * a.Hq + hh];
-          sc[k] = hc + k < a.Hq ? w : 0.0f;
+          const float w = wp[part_of(hh / G) * a.Hq + hh];
+#pragma unroll
+          for (int sb = 0; sb < NSUB; ++sb) {
+            const float v = hc + k < a.Hq ? ev[sb][k] * w : 0.0f;
+            acc[sb] += v;
+            mx[sb] = fmaxf(mx[sb], v);
+          }
         }
-      }
-#pragma unroll
-      for (int sb = 0; sb < NSUB; ++sb) {
-#pragma unroll
-        for (int k = 0; k < HC; ++k) {
-          if (hc + k >= a.Hq) break;
-          const float v = ev[sb][k] * sc[k];
-          acc[sb] += v;
-          mx[sb] = fmaxf(mx[sb], v);
-        }
-      }
-      if (last) {
-#pragma unroll
-        for (int sb = 0; sb < NSUB; ++sb)
-#pragma unroll
-          for (int k = 0; k < HC; ++k) ev[sb][k] = ev_next[sb][k];
-        if (a.Hq <= HC && l + 2 * kCmbWaves < L) load_records(l + 2 * kCmbWaves, 0, ev_next);
       }
     }
 #pragma unroll
@@ -1559,11 +1545,23 @@ __global__ __launch_bounds__(64 * kCmbWaves) void kvs_combine_layers(CombineArgs
       cl[((lane * L + l) * NSUB + sb) * 2] = acc[sb];
       cl[((lane * L + l) * NSUB + sb) * 2 + 1] = mx[sb];
     }
+  };
+  // the first two layers' first chunks are in flight since the start
+  if (wv < L) sum_layer(wv, ev);
+  if (wv + kCmbWaves < L) sum_layer(wv + kCmbWaves, ev_next);
+  for (int l = wv + 2 * kCmbWaves; l < L; l += kCmbWaves) {
+    load_records(l, 0, ev);
+    sum_layer(l, ev);
   }
   __syncthreads();
 
   // ---- one lane per tile: the layers in call order ----
-  if (wv != 0 || !m_live) return;
+  if (wv != 0) return;
+  const int i_cur = a.cur_pos[b];
+  int thi = a.NT;
+  if constexpr (!RING) thi = max(0, min(a.NT, i_cur / kTile + 1));
+  if (t >= thi) return;
+  const int lap_i = RING ? i_cur / a.C : 0;
 #pragma unroll
   for (int sb = 0; sb < NSUB; ++sb) {
     int blk = t;
@@ -1573,8 +1571,11 @@ __global__ __launch_bounds__(64 * kCmbWaves) void kvs_combine_layers(CombineArgs
     }
     if (blk < 0 || blk >= a.nbmax) continue;
     const size_t mi = (size_t)b * a.nbmax + blk;
-    float mass_run = a.mass != nullptr ? a.mass[mi] : 0.0f;
-    float max_run = a.mass_max != nullptr ? a.mass_max[mi] : 0.0f;
+    float mass_run = mass0, max_run = max0;
+    if constexpr (RING) {
+      mass_run = a.mass != nullptr ? a.mass[mi] : 0.0f;
+      max_run = a.mass_max != nullptr ? a.mass_max[mi] : 0.0f;
+    }
     for (int l = 0; l < L; ++l) {
       mass_run = mass_run + cl[((lane * L + l) * NSUB + sb) * 2];
       max_run = fmaxf(max_run, cl[((lane * L + l) * NSUB + sb) * 2 + 1]);
@@ -1594,8 +1595,15 @@ hipError_t launch_combine_layers(const CombineArgs& a, bool ring, hipStream_t st
   dim3 grid(n_chunks + a.n_layers, a.B), block(64 * kCmbWaves);
   size_t lds = combine_layers_lds_bytes(a.Hq, a.Hkv, a.nparts, a.n_layers, ring);
   if (lds < 16 * sizeof(float)) lds = 16 * sizeof(float);
-  if (ring) hipLaunchKernelGGL((kvs_combine_layers<true>), grid, block, lds, st, a);
-  else hipLaunchKernelGGL((kvs_combine_layers<false>), grid, block, lds, st, a);
+  // four heads of a group per 16-byte record load when the group size allows
+  const bool v4 = (a.Hq / a.Hkv) % 4 == 0;
+  if (ring) {
+    if (v4) hipLaunchKernelGGL((kvs_combine_layers<true, true>), grid, block, lds, st, a);
+    else hipLaunchKernelGGL((kvs_combine_layers<true, false>), grid, block, lds, st, a);
+  } else {
+    if (v4) hipLaunchKernelGGL((kvs_combine_layers<false, true>), grid, block, lds, st, a);
+    else hipLaunchKernelGGL((kvs_combine_layers<false, false>), grid, block, lds, st, a);
+  }
   return hipGetLastError();
 }
 
@@ -1639,8 +1647,14 @@ hipError_t launch_combine(const CombineArgs& a, bool ring, hipStream_t st) {
   dim3 grid(a.n_mass_chunks + a.n_layers, a.B), block(256);
   size_t lds = (size_t)a.layers_per_chunk * combine_layer_floats(a.Hq, a.Hkv, a.nparts) * sizeof(float);
   if (lds < 16 * sizeof(float)) lds = 16 * sizeof(float);
-  if (ring) hipLaunchKernelGGL((kvs_combine<true>), grid, block, lds, st, a);
-  else hipLaunchKernelGGL((kvs_combine<false>), grid, block, lds, st, a);
+  const bool v4 = (a.Hq / a.Hkv) % 4 == 0;
+  if (ring) {
+    if (v4) hipLaunchKernelGGL((kvs_combine<true, true>), grid, block, lds, st, a);
+    else hipLaunchKernelGGL((kvs_combine<true, false>), grid, block, lds, st, a);
+  } else {
+    if (v4) hipLaunchKernelGGL((kvs_combine<false, true>), grid, block, lds, st, a);
+    else hipLaunchKernelGGL((kvs_combine<false, false>), grid, block, lds, st, a);
+  }
   return hipGetLastError();
 }
 
