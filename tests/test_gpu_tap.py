@@ -29,7 +29,7 @@ def api():
 
 # kv, d, Hq, Hkv, C, B, window, ring, src, keep  (+ layers)
 TAP_CASES = [c + (3,) for c in FUSED_CASES] + [
-    ("bf16", 64, 16, 1, 16384, 1, 0, False, "bf16", False, 3),   # 128 partitions: one layer's tables per LDS chunk
+    ("bf16", 64, 16, 1, 16384, 1, 0, False, "bf16", False, 3),   # 256 partitions: two layers' tables per LDS chunk
     ("fp8", 128, 32, 8, 2064, 2, 0, False, "f32", True, 5),
 ]
 STEPS = 6
