@@ -32,7 +32,7 @@ EXPORTED = (
     "kvs_decode_attn_profiled",
     "kvs_reattend_blocks",
     "kvs_update_sidecar", "kvs_update_counters", "kvs_filter_blocks", "kvs_select_blocks",
-    "kvs_compact_blocks", "kvs_snapkv_workspace_bytes", "kvs_snapkv_scores", "kvs_status_str",
+    "kvs_update_sidecar_select", "kvs_compact_blocks", "kvs_snapkv_workspace_bytes", "kvs_snapkv_scores", "kvs_status_str",
     "kvs_version",
 )
 
@@ -85,6 +85,7 @@ def _load():
         "kvs_snapkv_workspace_bytes": [G, I32, SZP],
         "kvs_snapkv_scores": [G, P, I32, P, P, P, P, P, I32, P, SZ, P],
         "kvs_select_blocks": [P, P, P, I32, I32, I32, I32, I32, P, P, P, P],
+        "kvs_update_sidecar_select": [P, P, P, P, P, I32, I32, I32, I64, F, I32, P, P, I32, I32, I32, P, P, P, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -535,4 +536,43 @@ def select_blocks(score, cur_pos, budget_blocks: int, recent_tokens: int, sink_t
                                  int(recent_tokens), int(sink_tokens), _ptr(keep_mask), _ptr(sel_ids),
                                  _ptr(n_sel), _stream(stream)),
            "kvs_select_blocks")
+    return keep_mask, sel_ids, n_sel
+
+
+SCORE_SOURCES = {"cumulative": 0, "ema": 1, "attended": 2}
+
+
+def update_sidecar_select(mass_accum, attended, ema, cum, traj, step: int, alpha: float, cur_pos,
+                          budget_blocks: int, recent_tokens: int, sink_tokens: int = 0,
+                          score: str = "cumulative", alive=None, keep_mask=None, sel_ids=None, n_sel=None,
+                          stream=None):
+    """update_sidecar then select_blocks on the updated ``score`` array
+    ("cumulative", "ema" or "attended"), in one launch; returns (keep_mask,
+    sel_ids, n_sel)."""
+    _device_check(mass_accum, attended, ema, cum, traj, cur_pos, alive)
+    B, nb = attended.shape
+    traj_cap = traj.shape[1] if traj is not None else 1
+    for t in (mass_accum, ema, cum):
+        if t.numel() != B * nb or t.dtype != torch.float32:
+            raise ValueError("side-car arrays must be float32 [B, NBmax]")
+    if score not in SCORE_SOURCES:
+        raise ValueError(f"score must be one of {sorted(SCORE_SOURCES)}")
+    words = (nb + 31) // 32
+    dev = attended.device
+    if keep_mask is None:
+        keep_mask = torch.empty((B, words), dtype=torch.int32, device=dev)
+    if sel_ids is None:
+        sel_ids = torch.empty((B, nb), dtype=torch.int32, device=dev)
+    if n_sel is None:
+        n_sel = torch.empty((B,), dtype=torch.int32, device=dev)
+    if cur_pos.dtype != torch.int32:
+        raise TypeError("cur_pos int32")
+    if alive is not None and (alive.dtype != torch.int32 or alive.numel() != B * words):
+        raise ValueError("alive must be int32 bit words [B, W]")
+    _check(LIB.kvs_update_sidecar_select(_ptr(mass_accum), _ptr(attended), _ptr(ema), _ptr(cum), _ptr(traj),
+                                         B, nb, traj_cap, int(step), float(alpha), SCORE_SOURCES[score],
+                                         _ptr(alive), _ptr(cur_pos), int(budget_blocks), int(recent_tokens),
+                                         int(sink_tokens), _ptr(keep_mask), _ptr(sel_ids), _ptr(n_sel),
+                                         _stream(stream)),
+           "kvs_update_sidecar_select")
     return keep_mask, sel_ids, n_sel

@@ -607,4 +607,28 @@ int kvs_select_blocks(const float* score, const uint32_t* alive, const int32_t* 
   return hip_status(kvs::launch_select(a, (hipStream_t)stream));
 }
 
+int kvs_update_sidecar_select(float* mass_accum, float* attended, float* ema, float* cum, float* traj,
+                              int32_t batch, int32_t n_blocks_max, int32_t traj_cap, int64_t step,
+                              float alpha, int32_t score_source, const uint32_t* alive,
+                              const int32_t* cur_pos, int32_t budget_blocks, int32_t recent_tokens,
+                              int32_t sink_tokens, uint32_t* keep_mask, int32_t* sel_ids, int32_t* n_sel,
+                              void* stream) {
+  if (batch < 1 || n_blocks_max < 1 || traj_cap < 1 || step < 0) return KVS_EINVAL;
+  if (!(alpha >= 0.0f && alpha <= 1.0f)) return KVS_EINVAL;
+  if (score_source < KVS_SCORE_CUMULATIVE || score_source > KVS_SCORE_ATTENDED) return KVS_EINVAL;
+  if (budget_blocks < 0 || recent_tokens < 1 || sink_tokens < 0) return KVS_EINVAL;
+  if (!mass_accum || !attended || !ema || !cum || !cur_pos || !keep_mask || !sel_ids || !n_sel)
+    return KVS_EINVAL;
+  const void* ptrs[] = {mass_accum, attended, ema, cum, traj, alive, cur_pos, keep_mask, sel_ids, n_sel};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KVS_EALIGN;
+  kvs::SelectArgs a{};
+  a.alive = alive; a.cur_pos = cur_pos; a.keep = keep_mask; a.sel_ids = sel_ids; a.n_sel = n_sel;
+  a.B = batch; a.nbmax = n_blocks_max; a.kwords = (n_blocks_max + 31) / 32;
+  a.budget = budget_blocks; a.recent = recent_tokens; a.sinks = sink_tokens;
+  a.mass = mass_accum; a.att = attended; a.ema = ema; a.cum = cum; a.traj = traj;
+  a.traj_cap = traj_cap; a.slot = (int)(step % traj_cap); a.alpha = alpha; a.score_src = score_source;
+  return hip_status(kvs::launch_select(a, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -1341,16 +1341,25 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
 
 // ---------------------------------------------------------------------------
 // Layer-parallel combine (kvs_tap_masses without per-head masses): grid
-// (ceil(NT / 64), B) plus n_layers rate columns, 512 threads. Wave w of a
-// workgroup takes layers w, w + 8, ... for 64 consecutive tiles (one per
-// lane), keeping each (tile, layer)'s sum over heads, computed exactly as
-// kvs_combine does, in LDS; then one lane per tile adds them in layer order
-// to the current mass, so the result equals the layer-by-layer sum bit for
-// bit. A wave stages only its own layers' weights and boundaries, loaded
+// (ceil(NT / (64 TG)), B) plus n_layers rate columns, 512 threads. Wave w of
+// a workgroup takes tile group w % TG (64 consecutive tiles, one per lane)
+// and layers w / TG, w / TG + 8 / TG, ... (TG = 1 from 8 layers up), keeping
+// each (tile, layer)'s sum over heads, computed exactly as kvs_combine does,
+// in LDS; then one lane per tile adds them in layer order to the current
+// mass, so the result equals the layer-by-layer sum bit for bit. A wave stages only its own layers' weights and boundaries, loaded
 // together with its records, so the one barrier is before the final sums.
 // ---------------------------------------------------------------------------
 constexpr int kCmbTiles = 64;
 constexpr int kCmbWaves = 8;
+
+// Tile groups of a layer-parallel workgroup: with fewer than 8 layers the
+// waves split the tiles too (TG groups of 64 tiles, TG L <= 8, TG a power
+// of two), so no wave idles.
+__host__ __device__ inline int cmb_groups(int L) {
+  int g = 1;
+  while (g * 2 * L <= kCmbWaves) g *= 2;
+  return g;
+}
 
 // Two workgroups per compute unit (<= 128 VGPRs): the mass workgroups of the
 // 397B-like step (16 sequences x 32 chunks) are then all resident at once.
@@ -1366,7 +1375,9 @@ void kvs_combine_layers(CombineArgs a) {
   constexpr int NSUB = RING ? 2 : 1;
   constexpr int HC = RING ? 16 : 32;
   auto ws_f = [&](int l, size_t off) { return (const float*)(a.lws[l] + off); };
-  const int n_chunks = (a.NT + kCmbTiles - 1) / kCmbTiles;
+  const int TG = cmb_groups(L);
+  const int tpw = kCmbTiles * TG;  // tiles per workgroup
+  const int n_chunks = (a.NT + tpw - 1) / tpw;
   if ((int)blockIdx.x >= n_chunks) {
     // rates: the same per-layer refresh as in kvs_combine
     const int l = blockIdx.x - n_chunks;
@@ -1416,7 +1427,10 @@ void kvs_combine_layers(CombineArgs a) {
   const int per = n_ml + n_bnd;  // one layer's table: weights [P][Hq], boundaries [Hkv][P + 1]
   auto t_wp = [&](int l) { return lds + (size_t)l * per; };
   auto t_bd = [&](int l) { return (int*)(t_wp(l) + n_ml); };
-  float* cl = lds + (size_t)L * per;  // [kCmbTiles][L][NSUB][2]: sum and max over heads
+  float* cl = lds + (size_t)L * per;  // [tpw][L][NSUB][2]: sum and max over heads
+  // this wave: tile group tg, layers l0, l0 + ls, ...
+  const int tg = wv % TG, l0 = wv / TG, ls = kCmbWaves / TG;
+  const int tl = tg * 64 + lane;  // tile of this lane within the workgroup
 
   // tile of this lane; without a window the range starts at tile 0, so the
   // loads below need not wait for cur_pos
@@ -1428,7 +1442,7 @@ void kvs_combine_layers(CombineArgs a) {
       tlo = min(thi0, max(ic - a.window + 1, 0) / kTile);
     }
   }
-  const int t = tlo + (int)blockIdx.x * kCmbTiles + lane;
+  const int t = tlo + (int)blockIdx.x * tpw + tl;
   const int tc = min(max(t, 0), a.NT - 1);
   const uint32_t rec_bytes = (uint32_t)a.Hkv * a.NT * NSUB * G * 4;
   const uint32_t rec_vo = (uint32_t)tc * NSUB * G * 4;
@@ -1436,48 +1450,68 @@ void kvs_combine_layers(CombineArgs a) {
     const char* base = a.lws[min(l, L - 1)] + a.off_e + (size_t)b * rec_bytes;
     load_rec<NSUB, HC, V4>(ev, make_rsrc(base, rec_bytes), rec_vo, hc, a.Hq, G, a.NT);
   };
-  // Each wave stages the tables of its own layers (wv, wv + 8, ...) and reads
-  // only those, so no workgroup barrier comes before the sums. The first two
-  // layers' tables (two values per lane each) are issued ahead of the
-  // records, so storing them waits for nothing else.
+  // Tables of up to 128 values per layer (the usual case): each wave stages
+  // those of its own layers and reads only those (waves of a layer's tile
+  // groups write the same values), so no workgroup barrier comes before the
+  // sums. The first two layers' tables
+  // (two values per lane each) are issued ahead of the records, so storing
+  // them waits for nothing else. Larger tables (many partitions) are staged
+  // by the whole workgroup, four values per thread in flight, then a barrier.
   auto tab_val = [&](int l, int r) -> float {
     const char* base = a.lws[min(l, L - 1)];
     const int rc = min(r, per - 1);
     return rc < n_ml ? ((const float*)(base + a.off_w))[(size_t)b * n_ml + rc]
                      : ((const float*)(base + a.off_bnd))[(size_t)b * n_bnd + (rc - n_ml)];  // a ring's are unused
   };
+  const bool coop = per > 128;
   float tv[2][2];
+  if (!coop) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int k = 0; k < 2; ++k) tv[j][k] = tab_val(wv + j * kCmbWaves, lane + 64 * k);
+      for (int k = 0; k < 2; ++k) tv[j][k] = tab_val(l0 + j * ls, lane + 64 * k);
+  }
   asm volatile("" ::: "memory");
   float ev[NSUB][HC], ev_next[NSUB][HC];
-  load_records(wv, 0, ev);
-  load_records(wv + kCmbWaves, 0, ev_next);
-  // a linear cache's block is the tile: wave 0 fetches the current masses
-  // it adds to now (a ring's blocks depend on cur_pos, read at the end)
+  load_records(l0, 0, ev);
+  load_records(l0 + ls, 0, ev_next);
+  // a linear cache's block is the tile: the first wave of each tile group
+  // fetches the current masses it adds to now (a ring's blocks depend on
+  // cur_pos, read at the end)
   float mass0 = 0.0f, max0 = 0.0f;
   if constexpr (!RING) {
-    if (wv == 0) {
+    if (l0 == 0) {
       const size_t mi = (size_t)b * a.nbmax + min(tc, a.nbmax - 1);
       mass0 = a.mass != nullptr ? a.mass[mi] : 0.0f;
       max0 = a.mass_max != nullptr ? a.mass_max[mi] : 0.0f;
     }
   }
   asm volatile("" ::: "memory");
+  if (!coop) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int l = wv + j * kCmbWaves;
+    for (int j = 0; j < 2; ++j) {
+      const int l = l0 + j * ls;
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
-      if (l < L && lane + 64 * k < per) t_wp(l)[lane + 64 * k] = tv[j][k];
+      for (int k = 0; k < 2; ++k)
+        if (l < L && lane + 64 * k < per) t_wp(l)[lane + 64 * k] = tv[j][k];
+    }
+    // layers past a wave's second
+    for (int l = l0 + 2 * ls; l < L; l += ls)
+      for (int r = lane; r < per; r += 64) t_wp(l)[r] = tab_val(l, r);
+  } else {
+    for (int l = 0; l < L; ++l) {
+      for (int r0 = 0; r0 < per; r0 += 4 * NTH) {
+        float v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = tab_val(l, r0 + tid + k * NTH);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (r0 + tid + k * NTH < per) t_wp(l)[r0 + tid + k * NTH] = v[k];
+      }
+    }
+    __syncthreads();
   }
-  // the rest (layers past a wave's second, entries past 128 of a layer)
-  for (int l = wv; l < L; l += kCmbWaves) {
-    const int r0 = l < wv + 2 * kCmbWaves ? 128 : 0;
-    for (int r = r0 + lane; r < per; r += 64) t_wp(l)[r] = tab_val(l, r);
-  }
+
   // ---- this wave's layers: per (tile, layer) sums over heads ----
   // Layer l's sum and max over heads for this lane's tile into cl, its first
   // head chunk given in ev (further chunks, when Hq > HC, loaded into ev here).
@@ -1542,21 +1576,21 @@ void kvs_combine_layers(CombineArgs a) {
     }
 #pragma unroll
     for (int sb = 0; sb < NSUB; ++sb) {
-      cl[((lane * L + l) * NSUB + sb) * 2] = acc[sb];
-      cl[((lane * L + l) * NSUB + sb) * 2 + 1] = mx[sb];
+      cl[((tl * L + l) * NSUB + sb) * 2] = acc[sb];
+      cl[((tl * L + l) * NSUB + sb) * 2 + 1] = mx[sb];
     }
   };
   // the first two layers' first chunks are in flight since the start
-  if (wv < L) sum_layer(wv, ev);
-  if (wv + kCmbWaves < L) sum_layer(wv + kCmbWaves, ev_next);
-  for (int l = wv + 2 * kCmbWaves; l < L; l += kCmbWaves) {
+  if (l0 < L) sum_layer(l0, ev);
+  if (l0 + ls < L) sum_layer(l0 + ls, ev_next);
+  for (int l = l0 + 2 * ls; l < L; l += ls) {
     load_records(l, 0, ev);
     sum_layer(l, ev);
   }
   __syncthreads();
 
   // ---- one lane per tile: the layers in call order ----
-  if (wv != 0) return;
+  if (l0 != 0) return;  // the first wave of each tile group
   const int i_cur = a.cur_pos[b];
   int thi = a.NT;
   if constexpr (!RING) thi = max(0, min(a.NT, i_cur / kTile + 1));
@@ -1577,8 +1611,8 @@ void kvs_combine_layers(CombineArgs a) {
       max_run = a.mass_max != nullptr ? a.mass_max[mi] : 0.0f;
     }
     for (int l = 0; l < L; ++l) {
-      mass_run = mass_run + cl[((lane * L + l) * NSUB + sb) * 2];
-      max_run = fmaxf(max_run, cl[((lane * L + l) * NSUB + sb) * 2 + 1]);
+      mass_run = mass_run + cl[((tl * L + l) * NSUB + sb) * 2];
+      max_run = fmaxf(max_run, cl[((tl * L + l) * NSUB + sb) * 2 + 1]);
     }
     if (a.mass != nullptr) a.mass[mi] = mass_run;
     if (a.mass_max != nullptr) a.mass_max[mi] = max_run;
@@ -1586,12 +1620,14 @@ void kvs_combine_layers(CombineArgs a) {
 }
 
 size_t combine_layers_lds_bytes(int Hq, int Hkv, int P, int L, bool ring) {
-  return ((size_t)L * combine_layer_floats(Hq, Hkv, P) + (size_t)kCmbTiles * L * (ring ? 2 : 1) * 2) * sizeof(float);
+  return ((size_t)L * combine_layer_floats(Hq, Hkv, P) + (size_t)kCmbTiles * cmb_groups(L) * L * (ring ? 2 : 1) * 2) *
+         sizeof(float);
 }
 
 hipError_t launch_combine_layers(const CombineArgs& a, bool ring, hipStream_t st) {
   if (!(a.mass || a.mass_max)) return hipSuccess;
-  const int n_chunks = (a.NT + kCmbTiles - 1) / kCmbTiles;
+  const int tpw = kCmbTiles * cmb_groups(a.n_layers);
+  const int n_chunks = (a.NT + tpw - 1) / tpw;
   dim3 grid(n_chunks + a.n_layers, a.B), block(64 * kCmbWaves);
   size_t lds = combine_layers_lds_bytes(a.Hq, a.Hkv, a.nparts, a.n_layers, ring);
   if (lds < 16 * sizeof(float)) lds = 16 * sizeof(float);

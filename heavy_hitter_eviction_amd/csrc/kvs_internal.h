@@ -117,6 +117,16 @@ struct SelectArgs {
   int32_t* sel_ids;
   int32_t* n_sel;
   int B, nbmax, kwords, budget, recent, sinks;
+  // Side-car update in the same launch (kvs_update_sidecar_select), applied
+  // to every block before the selection, which then scores with the updated
+  // array score_src names (0 cumulative, 1 EMA, 2 attended). NULL mass: none.
+  float* mass;
+  float* att;
+  float* ema;
+  float* cum;
+  float* traj;
+  int traj_cap, slot, score_src;
+  float alpha;
 };
 hipError_t launch_select(const SelectArgs& a, hipStream_t st);
 

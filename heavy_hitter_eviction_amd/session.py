@@ -131,10 +131,10 @@ class ScoredDecoder:
             self.append_attend_layer(l, q_layers[l], k_layers[l], v_layers[l], cur, keep=self.keep,
                                      use_own_keep=False)
         self.finish_masses(cur)
-        api.update_sidecar(self.mass, self.attended, self.ema, self.cum, self.traj,
-                           self.step_index, self.w.alpha)
-        api.select_blocks(self.cum, cur, self.w.budget_blocks, self.w.recent_tokens, self.w.sink_tokens,
-                          alive=self.keep, keep_mask=self.keep, sel_ids=self.sel_ids, n_sel=self.n_sel)
+        api.update_sidecar_select(self.mass, self.attended, self.ema, self.cum, self.traj, self.step_index,
+                                  self.w.alpha, cur, self.w.budget_blocks, self.w.recent_tokens,
+                                  self.w.sink_tokens, alive=self.keep, keep_mask=self.keep,
+                                  sel_ids=self.sel_ids, n_sel=self.n_sel)
         self.step_index += 1
         if compact_now is None:
             compact_now = self.step_index % self.compact_every == 0
@@ -151,11 +151,14 @@ class ScoredDecoder:
         self.pos = ((self.n_sel - 1) * 16 + cur % 16 + 1).to(torch.int32)
 
     def close_turn(self, cur_pos: torch.Tensor):
-        api.update_sidecar(self.mass, self.attended, self.ema, self.cum, self.traj,
-                           self.step_index, self.w.alpha)
         if self.w.select:
+            # side-car update and selection on the updated Cumulative, one launch
             alive = self.keep if self.evict else None
-            api.select_blocks(self.cum, cur_pos, self.w.budget_blocks, self.w.recent_tokens,
-                              self.w.sink_tokens, alive=alive, keep_mask=self.keep,
-                              sel_ids=self.sel_ids, n_sel=self.n_sel)
+            api.update_sidecar_select(self.mass, self.attended, self.ema, self.cum, self.traj,
+                                      self.step_index, self.w.alpha, cur_pos, self.w.budget_blocks,
+                                      self.w.recent_tokens, self.w.sink_tokens, alive=alive,
+                                      keep_mask=self.keep, sel_ids=self.sel_ids, n_sel=self.n_sel)
+        else:
+            api.update_sidecar(self.mass, self.attended, self.ema, self.cum, self.traj,
+                               self.step_index, self.w.alpha)
         self.step_index += 1

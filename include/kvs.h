@@ -512,6 +512,27 @@ KVS_API int kvs_select_blocks(const float* score, const uint32_t* alive, const i
                       int32_t recent_tokens, int32_t sink_tokens, uint32_t* keep_mask,
                       int32_t* sel_ids, int32_t* n_sel, void* stream);
 
+/*
+ * kvs_update_sidecar_select -- kvs_update_sidecar followed by
+ * kvs_select_blocks in one launch (Context views at marginal cost, section 2
+ * Tier 1, closing the turn; Context Optimization, "H2O KV Cache Eviction",
+ * selecting on the score it just updated). The selection scores the updated
+ * array score_source names: KVS_SCORE_CUMULATIVE (H2O's accumulated
+ * attention), KVS_SCORE_EMA or KVS_SCORE_ATTENDED (TOVA: this turn's mass).
+ * Every output equals that of the two calls with the same arguments, bit for
+ * bit. Arguments, layouts and errors as in the two calls; alive may be the
+ * same buffer as keep_mask (the feedback of evict mode).
+ */
+#define KVS_SCORE_CUMULATIVE 0
+#define KVS_SCORE_EMA 1
+#define KVS_SCORE_ATTENDED 2
+KVS_API int kvs_update_sidecar_select(float* mass_accum, float* attended, float* ema, float* cum, float* traj,
+                                      int32_t batch, int32_t n_blocks_max, int32_t traj_cap, int64_t step,
+                                      float alpha, int32_t score_source, const uint32_t* alive,
+                                      const int32_t* cur_pos, int32_t budget_blocks, int32_t recent_tokens,
+                                      int32_t sink_tokens, uint32_t* keep_mask, int32_t* sel_ids,
+                                      int32_t* n_sel, void* stream);
+
 /* Static text for a status code. */
 KVS_API const char* kvs_status_str(int status);
 

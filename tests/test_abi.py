@@ -201,3 +201,33 @@ def test_fused_append_decode_rejects_bad_arguments():
     assert fz(g, src=api.KVS_F32) == api.KVS_EDTYPE        # f32 rows into a bf16 cache
     assert fz(g, kn=0, fn=L.kvs_append_decode_partial) == api.KVS_EINVAL
     assert fz(_geom(api, kv_dtype=api.KVS_FP8_E4M3)) == api.KVS_EINVAL  # FP8 cache without scales
+
+
+def test_sidecar_select_rejects_bad_arguments():
+    """kvs_update_sidecar_select: the checks of both calls it stands for,
+    plus the score source; every call below fails one."""
+    api = _lib()
+    L = api.LIB
+    vp = ctypes.c_void_p
+    f = vp(0x1000)
+
+    def ss(alpha=0.5, src=0, budget=8, recent=16, sinks=0, cap=64, step=0, alive=None, mass=f, traj=f,
+           keep=vp(0x2000), B=2, nb=16):
+        return L.kvs_update_sidecar_select(mass, f, f, f, traj, B, nb, cap, step, alpha, src, alive,
+                                           vp(0x3000), budget, recent, sinks, keep, vp(0x4000),
+                                           vp(0x5000), None)
+
+    assert ss(alpha=1.5) == api.KVS_EINVAL
+    assert ss(alpha=float("nan")) == api.KVS_EINVAL
+    assert ss(src=3) == api.KVS_EINVAL
+    assert ss(src=-1) == api.KVS_EINVAL
+    assert ss(budget=-1) == api.KVS_EINVAL
+    assert ss(recent=0) == api.KVS_EINVAL
+    assert ss(sinks=-1) == api.KVS_EINVAL
+    assert ss(cap=0) == api.KVS_EINVAL
+    assert ss(step=-1) == api.KVS_EINVAL
+    assert ss(B=0) == api.KVS_EINVAL
+    assert ss(mass=None) == api.KVS_EINVAL
+    assert ss(keep=None) == api.KVS_EINVAL
+    assert ss(alive=vp(0x6004)) == api.KVS_EALIGN
+    assert ss(traj=vp(0x6008)) == api.KVS_EALIGN

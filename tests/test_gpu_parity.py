@@ -608,11 +608,16 @@ def test_filter_blocks_matches_oracle_exactly(api):
     assert got_n[0] > S
 
 
-@pytest.mark.parametrize("seed", range(6))
-def test_select_matches_oracle_exactly(api, seed):
+# (seed, blocks per sequence or None for a random 40..2999): the wider ones
+# take 8 and 16 keys per thread, and past 16384 blocks the memory-reading kernel
+SELECT_CASES = [(s, None) for s in range(6)] + [(6, 8193), (7, 16384), (8, 16385), (9, 40000)]
+
+
+@pytest.mark.parametrize("seed,nb_fixed", SELECT_CASES)
+def test_select_matches_oracle_exactly(api, seed, nb_fixed):
     rng = np.random.default_rng(seed)
     B = 4
-    nb = int(rng.integers(40, 3000))
+    nb = int(rng.integers(40, 3000)) if nb_fixed is None else nb_fixed
     score = (np.round(rng.random((B, nb)) * 50) / 50).astype(np.float32)   # many exact ties
     cur = rng.integers(0, nb * 16, B).astype(np.int32)
     budget, recent, sinks = int(rng.integers(0, 200)), int(rng.integers(1, 900)), int(rng.integers(0, 40))
@@ -645,3 +650,56 @@ def test_select_ties_lowest_index(api):
     keep, ids, n = api.select_blocks(gs.to_dev(score), gs.to_dev(np.array([63 * 16], dtype=np.int32)), 3, 1)
     torch.cuda.synchronize()
     assert ids[0, :int(n[0])].cpu().tolist() == [3, 9, 20, 63]
+
+
+@pytest.mark.parametrize("nb,score,evict", [(300, "cumulative", False), (8193, "cumulative", True),
+                                            (2049, "ema", False), (700, "attended", True),
+                                            (20000, "cumulative", True)])
+def test_sidecar_select_equals_the_two_calls(api, nb, score, evict):
+    """kvs_update_sidecar_select against kvs_update_sidecar then
+    kvs_select_blocks on the updated array, over several steps with the keep
+    mask fed back in evict mode: every side-car array, the trajectory, the
+    keep mask, the ids and their count bit for bit (20000 blocks takes the
+    two-launch form inside the fused call)."""
+    rng = np.random.default_rng(nb)
+    B, cap = 3, 8
+    budget, recent, sinks = 40, 100, 16
+    cur = np.array([nb * 16 - 1, nb * 8, 300], dtype=np.int32)
+    arrays = [gs.to_dev(np.zeros((B, nb), dtype=np.float32)) for _ in range(4)]
+    fused = dict(zip(("att", "ema", "cum", "mass"), arrays))
+    fused["traj"] = gs.to_dev(np.zeros((B, cap, nb), dtype=np.float32))
+    sep = {k: v.clone() for k, v in fused.items()}
+    words = (nb + 31) // 32
+    keep_f = gs.to_dev(np.full((B, words), -1, dtype=np.int32))
+    keep_s = keep_f.clone()
+    ids_f = gs.to_dev(np.full((B, nb), -7, dtype=np.int32))
+    ids_s = ids_f.clone()
+    n_f = gs.to_dev(np.zeros(B, dtype=np.int32))
+    n_s = n_f.clone()
+    cur_t = gs.to_dev(cur)
+    for step in range(5):
+        A = (np.round(rng.random((B, nb)) * 20) / 20).astype(np.float32)   # ties
+        fused["mass"].copy_(torch.from_numpy(A))
+        sep["mass"].copy_(torch.from_numpy(A))
+        api.update_sidecar_select(fused["mass"], fused["att"], fused["ema"], fused["cum"], fused["traj"], step,
+                                  0.5, cur_t, budget, recent, sinks, score=score,
+                                  alive=keep_f if evict else None, keep_mask=keep_f, sel_ids=ids_f, n_sel=n_f)
+        api.update_sidecar(sep["mass"], sep["att"], sep["ema"], sep["cum"], sep["traj"], step, 0.5)
+        src = {"cumulative": sep["cum"], "ema": sep["ema"], "attended": sep["att"]}[score]
+        api.select_blocks(src, cur_t, budget, recent, sinks, alive=keep_s if evict else None,
+                          keep_mask=keep_s, sel_ids=ids_s, n_sel=n_s)
+        torch.cuda.synchronize()
+        for k in fused:
+            assert torch.equal(fused[k], sep[k]), (step, k)
+        assert torch.equal(keep_f, keep_s), step
+        assert torch.equal(n_f, n_s), step
+        for b in range(B):
+            n = int(n_s[b])
+            assert torch.equal(ids_f[b, :n], ids_s[b, :n]), (step, b)
+    # and the selection itself against the oracle at the last step (no feedback case)
+    if not evict:
+        sc = {"cumulative": sep["cum"], "ema": sep["ema"], "attended": sep["att"]}[score].cpu().numpy()
+        for b in range(B):
+            ref = orc.select_blocks(sc[b], None, int(cur[b]), budget, recent, sinks)
+            assert int(n_f[b]) == len(ref)
+            assert np.array_equal(ids_f[b, :len(ref)].cpu().numpy(), ref)

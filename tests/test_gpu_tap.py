@@ -31,6 +31,11 @@ def api():
 TAP_CASES = [c + (3,) for c in FUSED_CASES] + [
     ("bf16", 64, 16, 1, 16384, 1, 0, False, "bf16", False, 3),   # 256 partitions: two layers' tables per LDS chunk
     ("fp8", 128, 32, 8, 2064, 2, 0, False, "f32", True, 5),
+    # one and two layers: the layer combine's waves split the tiles (8 and 4 groups)
+    ("fp8", 128, 32, 8, 8208, 2, 0, False, "f32", False, 1),
+    ("bf16", 128, 16, 4, 4112, 3, 0, False, "bf16", True, 2),
+    ("fp8", 128, 16, 4, 1024, 2, 1000, True, "f32", False, 1),
+    ("bf16", 64, 8, 2, 2064, 2, 700, False, "bf16", False, 2),
 ]
 STEPS = 6
 
