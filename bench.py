@@ -19,9 +19,10 @@ HBM before timing starts.
 
 Printed: one JSON line with the step throughput, a roofline entry for the
 dominant kernel (the scored partial kernel, timed with a HIP event pair on
-the stream it runs on around one layer's launch in every timed step, the
-layer rotating) and the float64 oracle timed on the host cores over a
-bounded sample of the same workload.
+the stream it runs on around the step's back-to-back launches of all layers;
+with a separate append, around one layer's launch per step, the layer
+rotating) and the float64 oracle timed on the host cores over a bounded
+sample of the same workload.
 """
 
 from __future__ import annotations
@@ -156,9 +157,11 @@ def run_gpu(args, w):
     if profiled:
         head_mass = torch.zeros((w.batch, w.n_q_heads, dec.geom.nb), dtype=torch.float32, device="cuda")
         mass_max = torch.zeros((w.batch, dec.geom.nb), dtype=torch.float32, device="cuda")
-    # one event pair per timed step, around the partial kernel of layer
-    # (step mod L): every layer is timed in turn, and the events (about 1.2 us
-    # of queue time each pair) do not tax every launch of the step
+    # one event pair per timed step (about 1.2 us of queue time each pair, so
+    # not one per launch): fused, around the L partial launches, which run
+    # back to back (the average launch then includes the dispatch gaps
+    # between them); otherwise around the partial kernel of layer
+    # (step mod L), every layer timed in turn
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     sev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -175,17 +178,19 @@ def run_gpu(args, w):
             if not fused:
                 dec.caches[layer].append(K[layer][t], V[layer][t], dec.row_seq, cur[t])
             ev_here = timed and layer == (t - args.warmup) % L
-            if ev_here:
-                ev[t - args.warmup][0].record()
             if fused:
                 # one kernel per layer: the append, the attention and its output
                 # merge; the layer's block sums stay in its workspace for the
                 # step's one tap_masses call
+                if timed and layer == 0:
+                    ev[t - args.warmup][0].record()
                 api.decode_attn_tap(dec.caches[layer], Q[layer][t], cur[t], dec.out[layer], dec.workspaces[layer],
                                     keep_mask=keep, k_new=K[layer][t], v_new=V[layer][t])
-                if ev_here:
+                if timed and layer == L - 1:
                     ev[t - args.warmup][1].record()
                 continue
+            if ev_here:
+                ev[t - args.warmup][0].record()
             if profiled:
                 # one call, both phases: the events cover partial + combine
                 api.decode_attn_profiled(dec.caches[layer], Q[layer][t], cur[t], dec.out[layer], dec.workspace,
@@ -207,7 +212,8 @@ def run_gpu(args, w):
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
-    part_ms = [a.elapsed_time(b) for (a, b) in ev]
+    # per launch: a fused step's pair covers its L launches
+    part_ms = [a.elapsed_time(b) / (L if fused else 1) for (a, b) in ev]
     step_ms = [a.elapsed_time(b) for a, b in zip(sev, sev[1:])]
     return dec, total_ms, part_ms, step_ms
 

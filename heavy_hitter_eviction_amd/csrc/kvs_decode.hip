@@ -160,12 +160,12 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 15, kg = lane >> 4;
-  const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = a.G;
   const int h = j;                       // query head within the group (this lane's column)
   const bool hreal = h < G;
   const uint64_t clk0 = __builtin_amdgcn_s_memrealtime();
-  const int wg_id = part + a.nparts * (g + a.Hkv * b);  // dispatch order
+  const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int wg_id = part + a.nparts * (g + a.Hkv * b);  // dispatch order: XCD = id mod 8
   // fused append: the appending wave fetches the first 512 values of the new
   // K and V rows right away (their address needs no cur_pos); it is decided
   // further down whether this workgroup appends at all
@@ -184,22 +184,20 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
       }
     }
   }
-  const int i_cur = a.cur_pos[b];
-  const int lo = a.window > 0 ? i_cur - a.window + 1 : (int)0x80000000;
-  // Partition weights (see below): the measured rate of each partition's
-  // dispatch class, fetched with cur_pos
+  // Partition weights: the measured streaming rate of each dispatch class,
+  // one per lane in a single load issued with the position's (eight
+  // guarded scalar-indexed loads would each wait for the one before)
   const bool use_rates = !RING && a.dyn && a.adapt && a.rates != nullptr;
-  const int cls0 = (a.nparts * (g + a.Hkv * b)) & 7;  // class of partition 0
+  const float r_lane = use_rates && lane < 8 ? a.rates[lane] : 1.0f;
+  const int i_cur = a.cur_pos[b];
   float wcls[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    float r = 1.0f;
-    if (use_rates) {
-      r = a.rates[c];
-      r = (r >= 0.5f && r <= 2.0f) ? fminf(fmaxf(r, 1.0f / 1.2f), 1.2f) : 1.0f;  // NaN -> 1
-    }
-    wcls[c] = r;
+    const float r = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r_lane), c));
+    wcls[c] = (r >= 0.5f && r <= 2.0f) ? fminf(fmaxf(r, 1.0f / 1.2f), 1.2f) : 1.0f;  // NaN -> 1
   }
+  const int lo = a.window > 0 ? i_cur - a.window + 1 : (int)0x80000000;
+  const int cls0 = (a.nparts * (g + a.Hkv * b)) & 7;  // class of partition 0
   // weight of partitions [0, k): partition q belongs to class (cls0 + q) mod 8
   auto wprefix = [&](int k) -> float {
     float acc = 0.0f;
