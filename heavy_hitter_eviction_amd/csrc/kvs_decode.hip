@@ -184,9 +184,28 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
       }
     }
   }
+  // Query operand (B of the QK MFMA): lane holds Q[h][dim(t, kg)], zeros for
+  // padding heads. Runs of EPC consecutive dims are read with 16-byte loads
+  // at entry (they need no cur_pos) and converted once the first tile loads
+  // are in flight.
+  const int hq = g * G + min(h, G - 1);
+  constexpr int QN = D / 4;
+  constexpr int EPC = 16 / eb;                  // dims per run
+  constexpr int QE = KV == KV_F32 ? 4 : 2;      // query element bytes
+  constexpr int QRUN = EPC * QE / 16;           // 16-byte words per run
+  u32x4 qraw[QN / EPC][QRUN];
+  {
+    const char* qrow = (const char*)a.q + ((size_t)b * a.Hq + hq) * D * QE;
+#pragma unroll
+    for (int r = 0; r < QN / EPC; ++r)
+#pragma unroll
+      for (int c = 0; c < QRUN; ++c)
+        qraw[r][c] = *(const u32x4*)(qrow + (size_t)qk_dim<KV>(r * EPC, kg) * QE + 16 * c);
+  }
   // Partition weights: the measured streaming rate of each dispatch class,
-  // one per lane in a single load issued with the position's (eight
-  // guarded scalar-indexed loads would each wait for the one before)
+  // one per lane in a single load, with the position's, after the loads
+  // above (eight guarded scalar-indexed loads would each wait for the one
+  // before)
   const bool use_rates = !RING && a.dyn && a.adapt && a.rates != nullptr;
   const float r_lane = use_rates && lane < 8 ? a.rates[lane] : 1.0f;
   const int i_cur = a.cur_pos[b];
@@ -259,7 +278,7 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   int* tlist = (int*)(m_rec + (size_t)a.tl_cap * G);    // [tl_cap]
   uint32_t* kb = (uint32_t*)(tlist + a.tl_cap);         // [NT / 32 + 1]
   if (threadIdx.x == 0) {
-    misc[1] = 0;
+    misc[1] = NW;  // claim counter: batches 0 .. NW - 1 are the waves' first
     misc[2] = 0;
     misc[3] = -1;
   }
@@ -372,8 +391,10 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
     }
     if (lane == 0) misc[0] = n;
   }
-  __syncthreads();
+  // (without a list the workgroup's first barrier comes after the first
+  // tile loads are issued, below)
   if (use_list) {
+    __syncthreads();
     t0 = misc[4];
     t1 = misc[5];
   }
@@ -390,10 +411,12 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
     if (use_list) return __builtin_amdgcn_readfirstlane(tlist[e]);
     return tb + e;
   };
-  // The waves take batches of BATCH consecutive list entries from a shared
-  // counter, so a wave that is served faster by the memory system reads more
-  // tiles and all waves of the workgroup finish within about one batch. In
-  // deterministic mode wave w takes batches w, w + NW, ... instead.
+  // Wave w reads batch w first (its loads go out before the workgroup's
+  // first barrier); then the waves take batches of BATCH consecutive list
+  // entries from a shared counter, so a wave that is served faster by the
+  // memory system reads more tiles and all waves of the workgroup finish
+  // within about one batch. In deterministic mode wave w takes batches w,
+  // w + NW, ... instead.
   int n_claimed = 0;
   auto claim = [&]() -> int {
     int v = 0;
@@ -412,23 +435,6 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
     return v;
   };
 
-  // Query operand (B of the QK MFMA): lane holds Q[h][dim(t, kg)], zeros for
-  // padding heads. Runs of EPC consecutive dims are read with 16-byte loads
-  // here and converted once the first tile loads are in flight.
-  const int hq = g * G + min(h, G - 1);
-  constexpr int QN = D / 4;
-  constexpr int EPC = 16 / eb;                  // dims per run
-  constexpr int QE = KV == KV_F32 ? 4 : 2;      // query element bytes
-  constexpr int QRUN = EPC * QE / 16;           // 16-byte words per run
-  u32x4 qraw[QN / EPC][QRUN];
-  {
-    const char* qrow = (const char*)a.q + ((size_t)b * a.Hq + hq) * D * QE;
-#pragma unroll
-    for (int r = 0; r < QN / EPC; ++r)
-#pragma unroll
-      for (int c = 0; c < QRUN; ++c)
-        qraw[r][c] = *(const u32x4*)(qrow + (size_t)qk_dim<KV>(r * EPC, kg) * QE + 16 * c);
-  }
   float qf[QN];
   bf16x8 qb[D / 32 > 0 ? D / 32 : 1];
   auto convert_q = [&]() {
@@ -780,6 +786,21 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
       if constexpr (RING) const_cast<int32_t*>(a.pos_of_slot)[(size_t)b * a.C + app_slot] = i_cur;
     }
   };
+  // First batch of this wave: its own index, its side data and first tiles
+  // requested before the workgroup's first barrier (without a keep list).
+  // The batch holding the appended row is requested once the row is written.
+  TileRegs<KV, D> buf[NBUF];
+  int cur = wave;
+  ++n_claimed;
+  const bool early = cur < n_batches && cur != app_batch;
+  if (early) {
+    gather(cur);
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i) load_tile<KV, D, RING>(buf[i], ad, soff_of(cur, i));
+  }
+  // the claim counter and the append flag are initialised (with a keep list
+  // the list's barrier has seen to that)
+  if (!use_list) __syncthreads();
   if (app_slot >= 0 && wave == NW - 1) {
     append_row();
     // release: the wave's stores complete (vmcnt 0) before the flag is seen;
@@ -790,12 +811,14 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   }
 
   int n_done = 0;  // tiles this wave processed
-  int cur = claim();
-  if (cur < n_batches) {
-    TileRegs<KV, D> buf[NBUF];
+  if (!early && cur < n_batches) {
+    while (__hip_atomic_load(&misc[2], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
+      __builtin_amdgcn_s_sleep(1);
     gather(cur);
 #pragma unroll
     for (int i = 0; i < NBUF - 1; ++i) load_tile<KV, D, RING>(buf[i], ad, soff_of(cur, i));
+  }
+  if (cur < n_batches) {
     convert_q();
     while (true) {
       commit();
