@@ -208,7 +208,7 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   // before)
   const bool use_rates = !RING && a.dyn && a.adapt && a.rates != nullptr;
   const float r_lane = use_rates && lane < 8 ? a.rates[lane] : 1.0f;
-  const int i_cur = a.cur_pos[b];
+  const int i_cur = __builtin_amdgcn_readfirstlane(a.cur_pos[b]);  // uniform, as are the tile offsets from it
   float wcls[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
@@ -253,8 +253,8 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   } else {
     gte = max(0, min(a.NT, i_cur / kTile + 1));
     gtb = a.window > 0 ? min(gte, max(lo, 0) / kTile) : 0;
-    t0 = gtb + split_at(part, gte - gtb);
-    t1 = gtb + split_at(part + 1, gte - gtb);
+    t0 = __builtin_amdgcn_readfirstlane(gtb + split_at(part, gte - gtb));
+    t1 = __builtin_amdgcn_readfirstlane(gtb + split_at(part + 1, gte - gtb));
   }
 
   // Fused append: the workgroup whose tiles hold the new position's slot
@@ -395,14 +395,17 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   // tile loads are issued, below)
   if (use_list) {
     __syncthreads();
-    t0 = misc[4];
-    t1 = misc[5];
+    t0 = __builtin_amdgcn_readfirstlane(misc[4]);
+    t1 = __builtin_amdgcn_readfirstlane(misc[5]);
   }
   // Tiles that can hold a readable key.
   const int tb = t0, te = t1;
   const int app_slot = (app_cand_tile >= tb && app_cand_tile < te) ? app_cand : -1;
   const int app_tile = app_slot >= 0 ? app_cand_tile : -1;
-  const int n_items = use_list ? misc[0] : te - tb;
+  // uniform (readfirstlane): the tile offsets derived from these are scalar
+  // operands of the buffer loads, which the compiler would otherwise wrap in
+  // a per-lane loop
+  const int n_items = __builtin_amdgcn_readfirstlane(use_list ? misc[0] : te - tb);
   const int n_batches = (n_items + BATCH - 1) / BATCH;
   // batch holding the appended tile (-1: none here, or not read)
   const int app_entry = app_tile < 0 ? -1 : use_list ? misc[3] : app_tile - tb;
@@ -708,7 +711,8 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   constexpr uint32_t tile_bytes = (uint32_t)kTile * D * eb;
   auto soff_of = [&](int bi, int i) -> uint32_t {
     const int e = BATCH * bi + i;
-    return e < n_items ? (uint32_t)tile_of(e) * tile_bytes : oob;
+    // a scalar operand of the loads: uniform, and marked so
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)(e < n_items ? (uint32_t)tile_of(e) * tile_bytes : oob));
   };
   // ---- fused append (last wave, before its first claim) ----
   // Same encoding as kvs_append_rows: the FP8 scale covers every KV head of
@@ -872,14 +876,29 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   // kvs_combine's tile-to-partition map.
   if constexpr (SCORED) {
     const int per_e = NSUB * G;
-    for (int x = threadIdx.x; x < n_items * per_e; x += NTH) {
-      const int e = x / per_e;
-      const int hh = x % G;
+    if (NTH % per_e == 0) {
+      // the usual case: a thread keeps one (sub-block, head) r of every
+      // (NTH / per_e)-th entry, so its head's workgroup max is taken once
+      const int r = threadIdx.x % per_e, hh = r % G;
       const float M = wg_max(hh);
-      const float mr = m_rec[e * G + hh];
-      const float v = (M == -__builtin_inff() || mr == -__builtin_inff()) ? 0.0f : e_rec[x] * fast_exp2(mr - M);
-      const int t = use_list ? tlist[e] : tb + e;
-      a.ws_e[e_index(t, 0, 0) + (x - e * per_e)] = v;
+      const int estep = NTH / per_e;
+      for (int e = threadIdx.x / per_e; e < n_items; e += estep) {
+        const float mr = m_rec[e * G + hh];
+        const float v =
+            (M == -__builtin_inff() || mr == -__builtin_inff()) ? 0.0f : e_rec[e * per_e + r] * fast_exp2(mr - M);
+        const int t = use_list ? tlist[e] : tb + e;
+        a.ws_e[e_index(t, 0, 0) + r] = v;
+      }
+    } else {
+      for (int x = threadIdx.x; x < n_items * per_e; x += NTH) {
+        const int e = x / per_e;
+        const int hh = x % G;
+        const float M = wg_max(hh);
+        const float mr = m_rec[e * G + hh];
+        const float v = (M == -__builtin_inff() || mr == -__builtin_inff()) ? 0.0f : e_rec[x] * fast_exp2(mr - M);
+        const int t = use_list ? tlist[e] : tb + e;
+        a.ws_e[e_index(t, 0, 0) + (x - e * per_e)] = v;
+      }
     }
     if (use_list) {
       // tiles of the range that were not kept: zero records
