@@ -17,7 +17,10 @@ constexpr int kTileSlots = 16;
 // the memory pipeline and finished up to a third later; inside one workgroup
 // the waves share the partition's tiles dynamically instead.
 constexpr int kTargetWorkgroups = 256;
-constexpr int kLdsBudgetFloats = 16384;  // 64 KiB per decode workgroup
+constexpr int kLdsBudgetFloats = 16384;  // 64 KiB per decode workgroup for the partition's records
+// the whole workgroup, output slots included (the MI355X gives a workgroup
+// up to 160 KiB)
+constexpr size_t kLdsMaxBytes = 163840;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -52,7 +55,7 @@ int check_geom(const kvs_geom* g) {
 }
 
 struct Plan {
-  int NT, tpp, nparts, nsub, G, S, tl_cap, n_wg, oslots, adapt;
+  int NT, tpp, nparts, nsub, G, S, tl_cap, n_wg, adapt;
   size_t off_m, off_l, off_o, off_e, off_bnd, off_w, off_time, off_rates, off_cnt, total;
   size_t lds_partial;
 };
@@ -71,18 +74,14 @@ Plan make_plan(const kvs_geom* g) {
   if (tpp < 4) tpp = 4;
   // the partial kernel keeps per-wave side data and, per tile of its
   // partition, the block-sum records and the kept-tile list in LDS: bound the
-  // partition so its LDS stays <= 64 KiB
+  // partition so that part stays <= 64 KiB
   const int nw = kvs::kPartialWaves;
   const int lds_fixed = nw * 256 + 8 + 2 * nw * 16 + p.NT / 32 + 1;  // + the keep bitmap
   const int per_tile = p.G * (p.nsub + 1) + 1;
   const int tpp_lds = (kLdsBudgetFloats - lds_fixed) / per_tile;
-  // the waves' outputs are merged in LDS over the same area, rows padded by 4
-  // floats: a slot per wave when that fits, else one per pair of waves
-  const int orow = p.G * (g->head_dim + 4);
-  p.oslots = nw * orow <= kLdsBudgetFloats - lds_fixed ? nw : nw / 2;
   if (tpp > tpp_lds) tpp = tpp_lds < 4 ? 4 : tpp_lds;
-  // the combine keeps per-head tables and the O weights of 256 / d heads
-  // over the nparts * nw partials in LDS: bound them to 48 KiB
+  // the mass combine keeps a layer's record weights and partition boundaries
+  // in LDS: bound them to 48 KiB
   while (true) {
     const int np = (p.NT + tpp - 1) / tpp;
     if (kvs::combine_layer_floats(g->n_q_heads, g->n_kv_heads, np) * 4 <= kvs::kCombineLdsBytes) break;
@@ -116,13 +115,13 @@ Plan make_plan(const kvs_geom* g) {
   p.off_rates = round256(p.off_time + (size_t)p.n_wg * nw * 2 * 4);
   p.off_cnt = round256(p.off_rates + 8 * 4);
   p.total = round256(p.off_cnt + (size_t)pairs * 8);
-  size_t area = (size_t)p.tl_cap * per_tile;
-  if (area < (size_t)p.oslots * orow) area = (size_t)p.oslots * orow;
-  // the output merge of a (sequence, KV head) stages 3 G nparts + 2 G floats
-  // over the same area
-  const size_t merge_f = 3 * (size_t)p.G * p.nparts + 2 * (size_t)p.G;
-  if (area < merge_f) area = merge_f;
-  p.lds_partial = 4 * ((size_t)lds_fixed + area);
+  // LDS: the fixed part and the records, then (16-byte aligned) one output
+  // slot per wave, rows padded by 4 floats; at the end the output merge of a
+  // (sequence, KV head) stages 3 G nparts + 2 G floats from the records on
+  const size_t rec_end = (size_t)lds_fixed + (size_t)p.tl_cap * per_tile;
+  const size_t o_end = ((rec_end + 3) & ~(size_t)3) + (size_t)nw * p.G * (g->head_dim + 4);
+  const size_t merge_end = (size_t)lds_fixed + 3 * (size_t)p.G * p.nparts + 2 * (size_t)p.G;
+  p.lds_partial = 4 * (o_end > merge_end ? o_end : merge_end);
   return p;
 }
 
@@ -235,7 +234,7 @@ int decode_setup(const kvs_geom* g, const void* q, const void* k_cache, const vo
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return KVS_EALIGN;
   const Plan p = make_plan(g);
-  if (p.lds_partial > 65536) return KVS_ENOTIMPL;  // partition bookkeeping beyond LDS
+  if (p.lds_partial > kLdsMaxBytes) return KVS_ENOTIMPL;  // partition bookkeeping beyond LDS
   if (workspace_bytes < p.total) return KVS_EWS;
   *plan = p;
   char* ws = (char*)workspace;
@@ -253,7 +252,7 @@ int decode_setup(const kvs_geom* g, const void* q, const void* k_cache, const vo
   a->B = g->batch; a->Hq = g->n_q_heads; a->Hkv = g->n_kv_heads; a->G = p.G; a->C = g->capacity;
   a->NT = p.NT; a->window = g->window; a->nbmax = g->n_blocks_max;
   a->kwords = (g->n_blocks_max + 31) / 32; a->tpp = p.tpp; a->nparts = p.nparts;
-  a->dyn = g->deterministic ? 0 : 1; a->tl_cap = p.tl_cap; a->oslots = p.oslots; a->adapt = p.adapt;
+  a->dyn = g->deterministic ? 0 : 1; a->tl_cap = p.tl_cap; a->adapt = p.adapt;
   a->scale_log2 = g->softmax_scale * 1.4426950408889634f;
   *c = kvs::CombineArgs{};
   c->lws[0] = ws; c->n_layers = 1; c->layers_per_chunk = 1;

@@ -277,6 +277,9 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   float* m_rec = e_rec + (size_t)a.tl_cap * NSUB * G;   // [tl_cap][G]
   int* tlist = (int*)(m_rec + (size_t)a.tl_cap * G);    // [tl_cap]
   uint32_t* kb = (uint32_t*)(tlist + a.tl_cap);         // [NT / 32 + 1]
+  // the waves' outputs at the end: one slot per wave, 16-byte aligned after
+  // the bitmap
+  float* ow = lds + ((((float*)(kb + a.NT / 32 + 1) - lds) + 3) & ~(ptrdiff_t)3);
   if (threadIdx.x == 0) {
     misc[1] = NW;  // claim counter: batches 0 .. NW - 1 are the waves' first
     misc[2] = 0;
@@ -874,7 +877,7 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   // would hold up the in-order completion count the tile loads are waited on
   // with. The split point of a two-partition range goes with them, for
   // kvs_combine's tile-to-partition map.
-  if constexpr (SCORED) {
+  auto store_records = [&]() {
     const int per_e = NSUB * G;
     if (NTH % per_e == 0) {
       // the usual case: a thread keeps one (sub-block, head) r of every
@@ -908,74 +911,60 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
         if (!((kb[rb >> 5] >> (rb & 31)) & 1u)) a.ws_e[e_index(tb + tl, 0, 0) + (x - tl * per_e)] = 0.0f;
       }
     }
-    __syncthreads();  // the record area is reused below
-  }
+  };
 
-  // The waves' outputs merge in LDS (staged over the records, rows padded by
-  // 4 floats against bank conflicts) into one partial per workgroup: each
-  // output sums the waves in a fixed order, rescaled to the workgroup max.
-  // When the slots do not fit, waves w and w + NW/2 share one: they rescale
-  // first and the upper half adds into the lower half's slot.
-  constexpr int DP = D + 4;
-  float* ow = e_rec;  // [oslots][G][DP]
-  auto put_o = [&](int slot, float sc, bool add) {
-    float* dst = ow + (slot * G + h) * DP;
+  // The waves' outputs merge in LDS (a slot per wave in an area of its own,
+  // rows padded by 4 floats against bank conflicts) into one partial per
+  // workgroup: each output sums the waves in a fixed order, rescaled to the
+  // workgroup max.
+  const size_t pbase = (size_t)b * a.Hq + hq0;  // first head of the group
+  auto store_partial = [&]() {
+    constexpr int DP = D + 4;
+    // ow: [NW][G][DP]
+    if (hreal) {
+      float* dst = ow + (wave * G + h) * DP;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int d0 = NC * (4 * kg + r);  // lane's dims d0 .. d0 + NC - 1
-      if constexpr (NC % 4 == 0) {
+      for (int r = 0; r < 4; ++r) {
+        const int d0 = NC * (4 * kg + r);  // lane's dims d0 .. d0 + NC - 1
+        if constexpr (NC % 4 == 0) {
 #pragma unroll
-        for (int n0 = 0; n0 < NC; n0 += 4) {
-          f32x4 v = {oacc[n0][r] * sc, oacc[n0 + 1][r] * sc, oacc[n0 + 2][r] * sc, oacc[n0 + 3][r] * sc};
-          if (add) v += *(const f32x4*)(dst + d0 + n0);
-          *(f32x4*)(dst + d0 + n0) = v;
+          for (int n0 = 0; n0 < NC; n0 += 4)
+            *(f32x4*)(dst + d0 + n0) = f32x4{oacc[n0][r], oacc[n0 + 1][r], oacc[n0 + 2][r], oacc[n0 + 3][r]};
+        } else {
+#pragma unroll
+          for (int n = 0; n < NC; ++n) dst[d0 + n] = oacc[n][r];
         }
-      } else {
-#pragma unroll
-        for (int n = 0; n < NC; ++n) dst[d0 + n] = oacc[n][r] * sc + (add ? dst[d0 + n] : 0.0f);
       }
     }
-  };
-  const bool own_slots = a.oslots == NW;
-  if (own_slots) {
-    if (hreal) put_o(wave, 1.0f, false);
     __syncthreads();
-  } else {
-    const float M = hreal ? wg_max(h) : 0.0f;
-    const float sc = (m_run == -__builtin_inff()) ? 0.0f : fast_exp2(m_run - M);
-    if (hreal && wave < NW / 2) put_o(wave, sc, false);
-    __syncthreads();
-    if (hreal && wave >= NW / 2) put_o(wave - NW / 2, sc, true);
-    __syncthreads();
-  }
-  const size_t pbase = (size_t)b * a.Hq + hq0;  // first head of the group
-  for (int x = threadIdx.x; x < G * D; x += NTH) {
-    const int hh = x / D, dd = x % D;
-    float o = 0.0f;
-    if (own_slots) {
+    for (int x = threadIdx.x; x < G * D; x += NTH) {
+      const int hh = x / D, dd = x % D;
+      float o = 0.0f;
       const float M = wg_max(hh);
       for (int w = 0; w < NW; ++w) {
         const float m = mw[w * 16 + hh];
         if (m != -__builtin_inff()) o += ow[(w * G + hh) * DP + dd] * fast_exp2(m - M);
       }
-    } else {
-      for (int sl = 0; sl < NW / 2; ++sl) o += ow[(sl * G + hh) * DP + dd];
+      // the partials go to memory past the (per-XCD, non-coherent) L2, for
+      // the merge below: relaxed system-scope stores are written through
+      __hip_atomic_store(&a.ws_o[((pbase + hh) * a.nparts + part) * D + dd], o, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_SYSTEM);
     }
-    // the partials go to memory past the (per-XCD, non-coherent) L2, for
-    // the merge below: relaxed system-scope stores are written through
-    __hip_atomic_store(&a.ws_o[((pbase + hh) * a.nparts + part) * D + dd], o, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_SYSTEM);
-  }
-  for (int hh = threadIdx.x; hh < G; hh += NTH) {
-    const float M = wg_max(hh);
-    float l = 0.0f;
-    for (int w = 0; w < NW; ++w) {
-      const float m = mw[w * 16 + hh];
-      if (m != -__builtin_inff()) l += lw[w * 16 + hh] * fast_exp2(m - M);
+    for (int hh = threadIdx.x; hh < G; hh += NTH) {
+      const float M = wg_max(hh);
+      float l = 0.0f;
+      for (int w = 0; w < NW; ++w) {
+        const float m = mw[w * 16 + hh];
+        if (m != -__builtin_inff()) l += lw[w * 16 + hh] * fast_exp2(m - M);
+      }
+      __hip_atomic_store(&a.ws_m[(pbase + hh) * a.nparts + part], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      __hip_atomic_store(&a.ws_l[(pbase + hh) * a.nparts + part], l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
-    __hip_atomic_store(&a.ws_m[(pbase + hh) * a.nparts + part], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    __hip_atomic_store(&a.ws_l[(pbase + hh) * a.nparts + part], l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-  }
+  };
+  // the partial's write-through stores go out first; the records are stored
+  // while those complete
+  store_partial();
+  if constexpr (SCORED) store_records();
 
   // ---- the last partition of this (sequence, KV head) to finish merges the
   // group's outputs, so the output needs no further launch. The count is

@@ -39,7 +39,6 @@ struct PartialArgs {
   int dyn;     // 1: waves claim tiles dynamically; 0: fixed round-robin order
   int tl_cap;  // LDS capacity of the kept-tile list (>= any partition's tiles)
   int adapt;   // 1: partitions may be weighted by the measured rates (tl_cap allows it)
-  int oslots;  // LDS output slots of the wave merge: kPartialWaves or kPartialWaves / 2
   float scale_log2;
   // Fused append: row b of app_k / app_v ([B][Hkv*D], bf16 if app_bf16, else
   // f32) is written at position cur_pos[b] of the cache (k, v, ks, vs and
