@@ -114,7 +114,7 @@ Plan make_plan(const kvs_geom* g) {
   p.off_time = round256(p.off_w + bh * p.nparts * 4);
   p.off_rates = round256(p.off_time + (size_t)p.n_wg * nw * 2 * 4);
   p.off_cnt = round256(p.off_rates + 8 * 4);
-  p.total = round256(p.off_cnt + (size_t)pairs * 8);
+  p.total = round256(p.off_cnt + (size_t)pairs * p.nparts * 4);
   // LDS: the fixed part and the records, then (16-byte aligned) one output
   // slot per wave, rows padded by 4 floats; at the end the output merge of a
   // (sequence, KV head) stages 3 G nparts + 2 G floats from the records on
@@ -127,8 +127,8 @@ Plan make_plan(const kvs_geom* g) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? KVS_OK : KVS_EHIP; }
 
-// Per-call token for the partial kernel's completion counters (never 0, so a
-// zero-filled counter is never mistaken for a live count).
+// Per-call token for the partial kernel's completion flags (never 0, so a
+// cleared or zero-filled flag is never taken for a set one).
 uint32_t next_token() {
   static std::atomic<uint32_t> counter{0};
   uint32_t t;
@@ -245,7 +245,7 @@ int decode_setup(const kvs_geom* g, const void* q, const void* k_cache, const vo
   a->ws_o = (float*)(ws + p.off_o); a->ws_e = (float*)(ws + p.off_e);
   a->ws_bnd = (int*)(ws + p.off_bnd); a->ws_time = (float*)(ws + p.off_time);
   a->ws_w = (float*)(ws + p.off_w);
-  a->pair_cnt = (unsigned long long*)(ws + p.off_cnt);
+  a->pair_flag = (uint32_t*)(ws + p.off_cnt);
   a->token = next_token();
   a->out = out;
   a->rates = (const float*)(ws + p.off_rates);

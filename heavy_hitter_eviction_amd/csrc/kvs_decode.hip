@@ -967,37 +967,37 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   if constexpr (SCORED) store_records();
 
   // ---- the last partition of this (sequence, KV head) to finish merges the
-  // group's outputs, so the output needs no further launch. The count is
-  // tagged with the call's token in its upper half: a word left by another
-  // call (or never written) restarts at 1, and the merging workgroup leaves
-  // it at (token, 0) for a replay of the same call. ----
+  // group's outputs, so the output needs no further launch. Each partition,
+  // once its partial is in memory, sets its flag word to the call's token and
+  // then reads the pair's flags: the partition whose flag lands last sees
+  // them all set and merges (two whose flags land together may both merge:
+  // they read the same partials in the same order and write the same
+  // values). A flag left by another call, or never written, holds another
+  // value; a merging workgroup clears the flags afterwards, so a replay of
+  // the same call (same token) starts clean. One round trip to memory, where
+  // a shared counter took one per partition finishing at the same time. ----
   // The partials are write-through stores; once every wave has them
-  // acknowledged (vmcnt 0) they are in memory, so the count needs no cache
+  // acknowledged (vmcnt 0) they are in memory, so the flag needs no cache
   // writeback, and the merging workgroup reads them past its caches.
   // (Device-scope fences here write back the whole L2 per workgroup and
   // cost tens of microseconds per launch.)
-  if (a.pair_cnt != nullptr) {
+  if (a.pair_flag != nullptr) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores acknowledged
     __syncthreads();
-    unsigned long long* cp = a.pair_cnt + (size_t)b * a.Hkv + g;
-    const unsigned long long tok = (unsigned long long)a.token << 32;
-    if (threadIdx.x == 0) {
+    uint32_t* fl = a.pair_flag + ((size_t)b * a.Hkv + g) * a.nparts;
+    if (wave == 0) {
       // system scope: performed at memory, past every XCD's L2
-      unsigned long long cur = __hip_atomic_load(cp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      int count = 0;
-      // each failed exchange is another partition's success: at most nparts - 1
-      for (int it = 0; it <= a.nparts; ++it) {
-        const unsigned long long next = (cur & 0xFFFFFFFF00000000ull) == tok ? cur + 1ull : (tok | 1ull);
-        if (__hip_atomic_compare_exchange_strong(cp, &cur, next, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_SYSTEM)) {
-          count = (int)(next & 0xFFFFFFFFull);
-          break;
-        }
-      }
-      misc[6] = count;
+      if (lane == 0) __hip_atomic_store(fl + part, a.token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // the flag is in memory before the others are read
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      bool set = true;
+      for (int x = lane; x < a.nparts; x += 64)
+        set = set && __hip_atomic_load(fl + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == a.token;
+      const bool all = __builtin_amdgcn_ballot_w64(!set) == 0;
+      if (lane == 0) misc[6] = all ? 1 : 0;
     }
     __syncthreads();
-    if (misc[6] == a.nparts) {
+    if (misc[6] == 1) {
       const int P = a.nparts;
       auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM); };
       float* mT = e_rec;          // [G][P] partition maxima   (record area, free now)
@@ -1028,7 +1028,7 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
         else
           ((float*)a.out)[oi] = sum;
       }
-      if (threadIdx.x == 0) __hip_atomic_store(cp, tok, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      for (int x = threadIdx.x; x < P; x += NTH) __hip_atomic_store(fl + x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
   }
 }

@@ -47,10 +47,10 @@ struct PartialArgs {
   const void* app_k;
   const void* app_v;
   int app_bf16;
-  // Output merge in the kernel: the last partition of a (sequence, KV head)
-  // to finish (counted in pair_cnt[B][Hkv], tagged with this call's token)
-  // merges the group's partials into out. NULL pair_cnt: kvs_combine does it.
-  unsigned long long* pair_cnt;
+  // Output merge in the kernel: the partition of a (sequence, KV head) that
+  // finds every partition's flag (pair_flag[B][Hkv][P]) set to this call's
+  // token merges the group's partials into out.
+  uint32_t* pair_flag;
   uint32_t token;
   void* out;
 };
