@@ -144,7 +144,7 @@ def run_gpu(args, w):
     if n_steps > w.steps:
         raise SystemExit(f"warmup + steps must be <= {w.steps} for this workload")
     t0 = time.time()
-    fused = not args.separate_append and args.mode == "decode"
+    fused = not args.separate_append and args.mode in ("decode", "profiled")
     dec = ScoredDecoder(w, evict=args.evict, fused=fused, tap=fused)
     prefill(dec, w, args.seed)
     Q, K, V = step_inputs(w, args.seed, n_steps, dec.n_layers)
@@ -206,7 +206,11 @@ def run_gpu(args, w):
             api.decode_attn_scored(dec.caches[layer], Q[layer][t], cur[t], dec.out[layer], dec.workspace,
                                    mass_accum=dec.mass, keep_mask=keep, phase="combine")
         if fused:
-            api.tap_masses(dec.geom, dec.workspaces, cur[t], mass_accum=dec.mass)
+            if profiled:
+                api.tap_masses(dec.geom, dec.workspaces, cur[t], mass_accum=dec.mass, head_mass=head_mass,
+                               mass_max=mass_max)
+            else:
+                api.tap_masses(dec.geom, dec.workspaces, cur[t], mass_accum=dec.mass)
         dec.close_turn(cur[t])
     sev[args.steps].record()
     end.record()
@@ -532,8 +536,8 @@ def main():
             "layers": w.n_layers, "context": w.context, "kv_dtype": w.kv_dtype, "block_tokens": 16,
             "window": w.window, "ring": w.ring, "budget_blocks": w.budget_blocks,
             "recent_tokens": w.recent_tokens, "mode": "evict" if args.evict else "score-only",
-            "append": "separate launch" if (args.separate_append or args.mode != "decode") else "in the partial kernel",
-            "masses": "per layer" if (args.separate_append or args.mode != "decode") else "once per step, all layers",
+            "append": "separate launch" if args.separate_append else "in the partial kernel",
+            "masses": "per layer" if args.separate_append else "once per step, all layers",
             **({"outputs": "per-head block masses [B][Hq][NBmax] and max over heads and layers"}
                if args.mode == "profiled" else {}),
         },
@@ -541,7 +545,8 @@ def main():
         "step_ms_p10_p50_p90": [round(float(x), 4) for x in _percentiles(step_ms, (10, 50, 90))],
         "blocks_scored_per_s": round(blocks_step / (ms_step / 1e3), 1),
         "roofline": {
-            "kernel": "kvs_partial + kvs_combine (profiled call)" if args.mode == "profiled" else "kvs_partial",
+            "kernel": ("kvs_partial + kvs_combine (profiled call)" if args.mode == "profiled" and args.separate_append
+                       else "kvs_partial"),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,

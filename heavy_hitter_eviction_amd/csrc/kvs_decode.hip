@@ -1234,6 +1234,27 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
     }
   }
 
+  // Per-head masses: the sequence's [Hq][nbmax] rows as one buffer, the
+  // block as the lane's offset and the head as a scalar one. With every head
+  // in one chunk a thread keeps its heads' masses in registers over the
+  // layers: read once, each layer's values added in order, written once (the
+  // same additions as a read-modify-write per layer).
+  const bool hm_reg = a.head_mass != nullptr && a.Hq <= HC;
+  const __amdgpu_buffer_rsrc_t hr =
+      make_rsrc(a.head_mass != nullptr ? a.head_mass + (size_t)b * a.Hq * a.nbmax : nullptr,
+                a.head_mass != nullptr ? (uint32_t)a.Hq * a.nbmax * 4 : 0u);
+  float hacc[NSUB][HC];
+  if (hm_reg && m_live) {
+#pragma unroll
+    for (int sb = 0; sb < NSUB; ++sb) {
+      const uint32_t hvo = (uint32_t)max(blk[sb], 0) * 4;
+#pragma unroll
+      for (int k = 0; k < HC; ++k)
+        hacc[sb][k] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(hr, (int)hvo, (int)((uint32_t)min(k, a.Hq - 1) * a.nbmax * 4), 0));
+    }
+  }
+
   for (int l0 = 0; l0 < L; l0 += lc0) {
     const int lc = min(lc0, L - l0);
     // ---- tables of layers [l0, l0 + lc) ----
@@ -1320,12 +1341,12 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
         }
 #pragma unroll
         for (int sb = 0; sb < NSUB; ++sb) {
-          if (a.head_mass != nullptr && blk[sb] >= 0) {
-            // per-head masses, eight read-modify-writes in flight at a time:
-            // the sequence's [Hq][nbmax] rows as one buffer, the block as the
-            // lane's offset and the head as a scalar one
-            const __amdgpu_buffer_rsrc_t hr =
-                make_rsrc(a.head_mass + (size_t)b * a.Hq * a.nbmax, (uint32_t)a.Hq * a.nbmax * 4);
+          if (hm_reg) {
+            // heads past Hq add +0
+#pragma unroll
+            for (int k = 0; k < HC; ++k) hacc[sb][k] = hacc[sb][k] + ev[sb][k];
+          } else if (a.head_mass != nullptr && blk[sb] >= 0) {
+            // per-head masses, eight read-modify-writes in flight at a time
             const uint32_t hvo = (uint32_t)blk[sb] * 4;
 #pragma unroll
             for (int k0 = 0; k0 < HC; k0 += 8) {
@@ -1365,6 +1386,13 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
     const size_t mi = (size_t)b * a.nbmax + blk[sb];
     if (a.mass != nullptr) a.mass[mi] = mass_run[sb];
     if (a.mass_max != nullptr) a.mass_max[mi] = max_run[sb];
+    if (hm_reg) {
+#pragma unroll
+      for (int k = 0; k < HC; ++k)
+        if (k < a.Hq)
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, hacc[sb][k]), hr, (int)((uint32_t)blk[sb] * 4),
+                                                (int)((uint32_t)k * a.nbmax * 4), 0);
+    }
   }
 }
 
