@@ -470,12 +470,13 @@ struct SnapPlan {
   int tpp, nparts;
   size_t off_part, off_m, off_l, total;
 };
-// Partitions of the prefill scoring passes: about 768 workgroups of 4 waves.
+// Partitions of the prefill scoring passes: about 1024 workgroups of 4 waves
+// (four per CU at up to 128 VGPRs).
 SnapPlan snap_plan(const kvs_geom* g, int window) {
   SnapPlan p{};
   const int NT = g->capacity / kTileSlots;
   const int pairs = g->batch * g->n_kv_heads;
-  int pt = (768 + pairs - 1) / pairs;
+  int pt = (1024 + pairs - 1) / pairs;
   if (pt < 1) pt = 1;
   p.tpp = (NT + pt - 1) / pt;
   if (p.tpp < 1) p.tpp = 1;
@@ -506,7 +507,8 @@ int kvs_snapkv_scores(const kvs_geom* g, const void* q_window, int32_t window, c
   if (g->kv_dtype == KVS_F32) return KVS_ENOTIMPL;
   const int G = g->n_q_heads / g->n_kv_heads;
   if (window < 1 || pool_kernel < 1 || pool_kernel % 2 == 0 || pool_kernel > 33) return KVS_EINVAL;
-  if (window * G > 128) return KVS_ENOTIMPL;
+  // a lane's 16 columns hold whole heads only when G divides 16
+  if (window * G > 128 || 16 % G != 0) return KVS_ENOTIMPL;
   const bool fp8 = g->kv_dtype == KVS_FP8_E4M3;
   if (!q_window || !k_cache || !n_prompt || !token_score || !workspace) return KVS_EINVAL;
   if (fp8 != (k_scale != nullptr)) return KVS_EINVAL;

@@ -231,3 +231,29 @@ def test_sidecar_select_rejects_bad_arguments():
     assert ss(keep=None) == api.KVS_EINVAL
     assert ss(alive=vp(0x6004)) == api.KVS_EALIGN
     assert ss(traj=vp(0x6008)) == api.KVS_EALIGN
+
+
+def test_snapkv_rejects_bad_arguments():
+    """kvs_snapkv_scores: every call below fails one check, so no kernel runs."""
+    api = _lib()
+    vp = ctypes.c_void_p
+    f = vp(0x1000)
+
+    def sk(g, window=8, ks=None, pool=7, ws_bytes=1 << 20, ts=vp(0x2000), q=f):
+        return api.LIB.kvs_snapkv_scores(ctypes.byref(g), q, window, f, ks, f, ts, None, pool, vp(0x3000),
+                                         ws_bytes, None)
+
+    g = _geom(api)                                           # bf16, G = 4
+    assert sk(g, window=0) == api.KVS_EINVAL
+    assert sk(g, pool=0) == api.KVS_EINVAL
+    assert sk(g, pool=8) == api.KVS_EINVAL                   # even kernel
+    assert sk(g, pool=35) == api.KVS_EINVAL
+    assert sk(g, window=33) == api.KVS_ENOTIMPL              # 132 window columns
+    assert sk(_geom(api, n_q_heads=12)) == api.KVS_ENOTIMPL  # G = 3 does not divide 16
+    assert sk(_geom(api, ring=1)) == api.KVS_EINVAL
+    assert sk(_geom(api, kv_dtype=api.KVS_F32, q_dtype=api.KVS_F32)) == api.KVS_ENOTIMPL
+    assert sk(_geom(api, kv_dtype=api.KVS_FP8_E4M3)) == api.KVS_EINVAL  # FP8 cache without scales
+    assert sk(g, ks=f) == api.KVS_EINVAL                     # scales with a bf16 cache
+    assert sk(g, q=None) == api.KVS_EINVAL
+    assert sk(g, ts=vp(0x2004)) == api.KVS_EALIGN
+    assert sk(g, ws_bytes=0) == api.KVS_EWS

@@ -489,21 +489,23 @@ def test_compact_blocks_matches_oracle_and_preserves_attention(api, kv):
 
 
 SNAP_CASES = [
-    # kv,   d,  Hq, Hkv, C,    W,  n_prompt
-    ("fp8", 128, 32, 8, 2064, 32, (2050, 700)),
-    ("bf16", 128, 16, 4, 1040, 32, (1040, 20)),
-    ("bf16", 64, 8, 4, 400, 8, (399, 150)),
-    ("fp8", 64, 16, 2, 256, 16, (255, 40)),
+    # kv,   d,  Hq, Hkv, C,    W,  n_prompt,  pooling kernel
+    ("fp8", 128, 32, 8, 2064, 32, (2050, 700), 7),
+    ("bf16", 128, 16, 4, 1040, 32, (1040, 20), 1),
+    ("bf16", 64, 8, 4, 400, 8, (399, 150), 13),
+    ("fp8", 64, 16, 2, 256, 16, (255, 40), 33),
+    ("bf16", 128, 4, 4, 528, 5, (520, 3), 9),      # G = 1: 5 columns, 11 of padding
+    ("fp8", 128, 16, 1, 784, 8, (777, 300), 7),    # G = 16
 ]
 
 
-@pytest.mark.parametrize("case", SNAP_CASES, ids=lambda c: "-".join(map(str, c[:6])))
+@pytest.mark.parametrize("case", SNAP_CASES, ids=lambda c: "-".join(map(str, c[:6] + c[7:])))
 def test_snapkv_scores_match_oracle(api, case):
     """SnapKV-style prefill scoring (Context views at marginal cost, section
-    3, Fact 1): window scores per (token, head) and max-pooled (kernel 7)
-    block scores added onto a non-zero start; one prompt shorter than the
-    window."""
-    kv, d, Hq, Hkv, C, W, n_prompt = case
+    3, Fact 1): window scores per (token, head) and max-pooled block scores
+    added onto a non-zero start; prompts shorter than the window, pooling
+    kernels from 1 to 33, GQA groups 1 to 16."""
+    kv, d, Hq, Hkv, C, W, n_prompt, pool = case
     B = 2
     geom, cache, K, V = _build_linear(api, kv, d, Hq, Hkv, C, B, 0, 29)
     q = torch.from_numpy(_rows((B, W, Hq, d), (29, 4))).to(torch.bfloat16)
@@ -512,7 +514,7 @@ def test_snapkv_scores_match_oracle(api, case):
     base = np.random.default_rng(2).random((B, geom.nb)).astype(np.float32)
     bs = gs.to_dev(base.copy())
     ws = torch.empty(api.snapkv_workspace_bytes(geom, W), dtype=torch.uint8, device="cuda")
-    api.snapkv_scores(cache, q.cuda(), gs.to_dev(n), ts, ws, block_score=bs, pool_kernel=7)
+    api.snapkv_scores(cache, q.cuda(), gs.to_dev(n), ts, ws, block_score=bs, pool_kernel=pool)
     torch.cuda.synchronize()
     got_t, got_b = ts.cpu().numpy(), bs.cpu().numpy()
     for b in range(B):
@@ -520,7 +522,7 @@ def test_snapkv_scores_match_oracle(api, case):
         Kd = gs.heads(gs.dequant_rows(K[b, :nb_], kv), Hkv, d)
         ref = orc.snapkv_token_scores(q[b].double().numpy(), Kd, nb_, orc.softmax_scale(d))
         assert np.abs(got_t[b, :, :nb_] - ref).max() <= 1e-5 * max(1.0, ref.max()), f"sequence {b}"
-        pooled = orc.max_pool_tokens(ref, 7)
+        pooled = orc.max_pool_tokens(ref, pool)
         want = base[b].astype(np.float64) + orc.snapkv_block_scores(pooled, geom.nb)
         gs.close_mass(got_b[b], want, "bf16", "SnapKV block score")
 
