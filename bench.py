@@ -119,19 +119,56 @@ def prefill(dec, w, seed):
         log(f"prefilled layer {layer + 1}/{dec.n_layers}")
 
 
-def step_inputs(w, seed, n_steps, layers):
+def step_inputs(w, seed, n_steps, layers, first=0):
+    """Per-layer query, K and V rows of decode steps ``first .. first + n_steps - 1``."""
     import torch
 
     from heavy_hitter_eviction_amd import synth
     qdt = torch.float32 if w.q_dtype == "f32" else torch.bfloat16
     src = torch.float32 if w.kv_dtype in ("f32", "fp8") else torch.bfloat16
+    ch = synth.STEP_CHUNK
+    c0, c1 = first // ch, (first + n_steps - 1) // ch
+    lo = first - c0 * ch
+
+    def rows(layer, tensor):
+        blk = torch.cat([synth.step_block(w, seed, layer, c, tensor, "cuda") for c in range(c0, c1 + 1)])
+        return blk[lo:lo + n_steps]
+
     Q, K, V = [], [], []
     for layer in range(layers):
-        q = synth.step_block(w, seed, layer, 0, synth.T_Q, "cuda")[:n_steps]
-        Q.append(q.reshape(n_steps, w.batch, w.n_q_heads, w.head_dim).to(qdt).contiguous())
-        K.append(synth.step_block(w, seed, layer, 0, synth.T_K, "cuda")[:n_steps].to(src).contiguous())
-        V.append(synth.step_block(w, seed, layer, 0, synth.T_V, "cuda")[:n_steps].to(src).contiguous())
+        Q.append(rows(layer, synth.T_Q).reshape(n_steps, w.batch, w.n_q_heads, w.head_dim).to(qdt).contiguous())
+        K.append(rows(layer, synth.T_K).to(src).contiguous())
+        V.append(rows(layer, synth.T_V).to(src).contiguous())
     return Q, K, V
+
+
+def ring_start(w):
+    """First decode step of a ring workload's measured run: two ring lengths
+    in, so the ring has wrapped and every step reads a full window (the
+    steady state). Other workloads start at step 0."""
+    return 2 * w.capacity if w.ring else 0
+
+
+def preroll_ring(dec, w, seed, s0):
+    """Write decode positions ``s0 - C .. s0 - 1`` (their rows from the same
+    per-step stream the decode steps draw) into every layer's ring, so the
+    steps from ``s0`` on run on a full ring."""
+    import torch
+
+    from heavy_hitter_eviction_amd import synth
+    src = torch.float32 if w.kv_dtype in ("f32", "fp8") else torch.bfloat16
+    ch = synth.STEP_CHUNK
+    assert (s0 - w.capacity) % ch == 0 and s0 % ch == 0
+    seqs = torch.arange(w.batch, dtype=torch.int32, device="cuda")
+    for layer in range(dec.n_layers):
+        for c in range((s0 - w.capacity) // ch, s0 // ch):
+            k = synth.step_block(w, seed, layer, c, synth.T_K, "cuda").to(src)
+            v = synth.step_block(w, seed, layer, c, synth.T_V, "cuda").to(src)
+            n = k.shape[0]
+            pos = (w.context + c * ch + torch.arange(n, dtype=torch.int32, device="cuda")).repeat_interleave(w.batch)
+            dec.caches[layer].append(k.reshape(n * w.batch, -1), v.reshape(n * w.batch, -1), seqs.repeat(n), pos)
+        torch.cuda.synchronize()
+    log(f"ring filled with positions {w.context + s0 - w.capacity} .. {w.context + s0 - 1}")
 
 
 def run_gpu(args, w):
@@ -141,14 +178,17 @@ def run_gpu(args, w):
     from heavy_hitter_eviction_amd.session import ScoredDecoder
 
     n_steps = args.warmup + args.steps
-    if n_steps > w.steps:
-        raise SystemExit(f"warmup + steps must be <= {w.steps} for this workload")
+    s0 = ring_start(w)
+    if s0 + n_steps > w.steps:
+        raise SystemExit(f"warmup + steps must be <= {w.steps - s0} for this workload")
     t0 = time.time()
     fused = not args.separate_append and args.mode in ("decode", "profiled")
     dec = ScoredDecoder(w, evict=args.evict, fused=fused, tap=fused)
     prefill(dec, w, args.seed)
-    Q, K, V = step_inputs(w, args.seed, n_steps, dec.n_layers)
-    cur = [torch.full((w.batch,), w.context + t, dtype=torch.int32, device="cuda") for t in range(n_steps)]
+    if s0:
+        preroll_ring(dec, w, args.seed, s0)
+    Q, K, V = step_inputs(w, args.seed, n_steps, dec.n_layers, first=s0)
+    cur = [torch.full((w.batch,), w.context + s0 + t, dtype=torch.int32, device="cuda") for t in range(n_steps)]
     torch.cuda.synchronize()
     log(f"setup {time.time() - t0:.1f}s, workspace {dec.workspace.numel() / 2**20:.1f} MiB")
 
@@ -509,7 +549,8 @@ def main():
 
     dec, total_ms, part_ms, step_ms = run_gpu(args, w)
     ms_step = total_ms / args.steps
-    steps_t = range(args.warmup, args.warmup + args.steps)
+    s0 = ring_start(w)
+    steps_t = range(s0 + args.warmup, s0 + args.warmup + args.steps)
     bytes_step = sum(w.kv_bytes_at_step(t) for t in steps_t) / args.steps
     blocks_step = sum(w.blocks_at_step(t) for t in steps_t) / args.steps
     value = bytes_step / (ms_step / 1e3) / 1e9
@@ -536,6 +577,8 @@ def main():
             "layers": w.n_layers, "context": w.context, "kv_dtype": w.kv_dtype, "block_tokens": 16,
             "window": w.window, "ring": w.ring, "budget_blocks": w.budget_blocks,
             "recent_tokens": w.recent_tokens, "mode": "evict" if args.evict else "score-only",
+            **({"timed_positions": [w.context + s0 + args.warmup, w.context + s0 + args.warmup + args.steps - 1],
+                "ring_state": "full (steady state)"} if w.ring else {}),
             "append": "separate launch" if args.separate_append else "in the partial kernel",
             "masses": "per layer" if args.separate_append else "once per step, all layers",
             **({"outputs": "per-head block masses [B][Hq][NBmax] and max over heads and layers"}
