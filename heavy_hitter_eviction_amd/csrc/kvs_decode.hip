@@ -872,20 +872,21 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   };
 
   // The block-sum records, rescaled from the running max at the time to the
-  // workgroup max per head, are stored by the whole workgroup as contiguous
-  // runs once every wave is done: global stores inside the streaming loop
-  // would hold up the in-order completion count the tile loads are waited on
-  // with. The split point of a two-partition range goes with them, for
-  // kvs_combine's tile-to-partition map.
-  auto store_records = [&]() {
+  // workgroup max per head, are stored as contiguous runs once every wave is
+  // done: global stores inside the streaming loop would hold up the in-order
+  // completion count the tile loads are waited on with. Threads th0 .. th0 +
+  // nth - 1 of the workgroup store them (all of them, or the waves other than
+  // wave 0 while it runs the output-merge handshake below).
+  auto store_records = [&](int th0, int nth) {
     const int per_e = NSUB * G;
-    if (NTH % per_e == 0) {
+    const int tid = threadIdx.x - th0;
+    if (nth % per_e == 0) {
       // the usual case: a thread keeps one (sub-block, head) r of every
-      // (NTH / per_e)-th entry, so its head's workgroup max is taken once
-      const int r = threadIdx.x % per_e, hh = r % G;
+      // (nth / per_e)-th entry, so its head's workgroup max is taken once
+      const int r = tid % per_e, hh = r % G;
       const float M = wg_max(hh);
-      const int estep = NTH / per_e;
-      for (int e = threadIdx.x / per_e; e < n_items; e += estep) {
+      const int estep = nth / per_e;
+      for (int e = tid / per_e; e < n_items; e += estep) {
         const float mr = m_rec[e * G + hh];
         const float v =
             (M == -__builtin_inff() || mr == -__builtin_inff()) ? 0.0f : e_rec[e * per_e + r] * fast_exp2(mr - M);
@@ -893,7 +894,7 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
         a.ws_e[e_index(t, 0, 0) + r] = v;
       }
     } else {
-      for (int x = threadIdx.x; x < n_items * per_e; x += NTH) {
+      for (int x = tid; x < n_items * per_e; x += nth) {
         const int e = x / per_e;
         const int hh = x % G;
         const float M = wg_max(hh);
@@ -905,7 +906,7 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
     }
     if (use_list) {
       // tiles of the range that were not kept: zero records
-      for (int x = threadIdx.x; x < (te - tb) * per_e; x += NTH) {
+      for (int x = tid; x < (te - tb) * per_e; x += nth) {
         const int tl = x / per_e;
         const int rb = tb + tl - r_lo;
         if (!((kb[rb >> 5] >> (rb & 31)) & 1u)) a.ws_e[e_index(tb + tl, 0, 0) + (x - tl * per_e)] = 0.0f;
@@ -961,10 +962,7 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
       __hip_atomic_store(&a.ws_l[(pbase + hh) * a.nparts + part], l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
   };
-  // the partial's write-through stores go out first; the records are stored
-  // while those complete
   store_partial();
-  if constexpr (SCORED) store_records();
 
   // ---- the last partition of this (sequence, KV head) to finish merges the
   // group's outputs, so the output needs no further launch. Each partition,
@@ -981,11 +979,17 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   // writeback, and the merging workgroup reads them past its caches.
   // (Device-scope fences here write back the whole L2 per workgroup and
   // cost tens of microseconds per launch.)
-  if (a.pair_flag != nullptr) {
+  // The other waves store the block records meanwhile: the completion count
+  // is per wave, so wave 0's waits for its flag do not wait for them.
+  if (a.pair_flag == nullptr) {
+    if constexpr (SCORED) store_records(0, NTH);
+  } else {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores acknowledged
     __syncthreads();
     uint32_t* fl = a.pair_flag + ((size_t)b * a.Hkv + g) * a.nparts;
-    if (wave == 0) {
+    if (wave != 0) {
+      if constexpr (SCORED) store_records(64, NTH - 64);
+    } else {
       // system scope: performed at memory, past every XCD's L2
       if (lane == 0) __hip_atomic_store(fl + part, a.token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       __builtin_amdgcn_s_waitcnt(0x0F70);  // the flag is in memory before the others are read
@@ -1005,6 +1009,14 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
       float* wT = lT + G * P;     // [P][G] weights
       float* hMt = wT + G * P;    // [G]
       float* hIt = hMt + G;       // [G]
+      // a thread's first output: its partitions' values are requested with
+      // the maxima and sums, so both arrive in one round trip
+      float ov0[8];
+      if (threadIdx.x < G * D) {
+        const float* o_src = a.ws_o + (pbase + threadIdx.x / D) * P * D + threadIdx.x % D;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) ov0[k] = ld(o_src + (size_t)min(k, P - 1) * D);
+      }
       for (int x = threadIdx.x; x < G * P; x += NTH) {
         mT[x] = ld(a.ws_m + pbase * P + x);
         lT[x] = ld(a.ws_l + pbase * P + x);
@@ -1019,8 +1031,13 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
         const int hh = x / D, dd = x % D;
         const float* o_src = a.ws_o + (pbase + hh) * P * D + dd;
         float ov[8];
+        if (x == (int)threadIdx.x) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) ov[k] = ld(o_src + (size_t)min(k, P - 1) * D);
+          for (int k = 0; k < 8; ++k) ov[k] = ov0[k];
+        } else {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) ov[k] = ld(o_src + (size_t)min(k, P - 1) * D);
+        }
         const float sum = merge_o(ov, [&](int p) { return ld(o_src + (size_t)p * D); }, wT + hh, G, P);
         const size_t oi = (pbase + hh) * D + dd;
         if constexpr (KV != KV_F32)
