@@ -131,7 +131,8 @@ def step_inputs(w, seed, n_steps, layers, first=0):
     lo = first - c0 * ch
 
     def rows(layer, tensor):
-        blk = torch.cat([synth.step_block(w, seed, layer, c, tensor, "cuda") for c in range(c0, c1 + 1)])
+        blks = [synth.step_block(w, seed, layer, c, tensor, "cuda") for c in range(c0, c1 + 1)]
+        blk = blks[0] if len(blks) == 1 else torch.cat(blks)
         return blk[lo:lo + n_steps]
 
     Q, K, V = [], [], []
