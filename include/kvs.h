@@ -398,7 +398,8 @@ KVS_API int kvs_update_sidecar(float* mass_accum, float* attended, float* ema, f
  *   token_score  [B][Hq][C] float
  *   block_score  [B][NBmax] float or NULL
  *   workspace    at least kvs_snapkv_workspace_bytes(geom, W)
- * W * (Hq / Hkv) <= 128, else KVS_ENOTIMPL; pool_kernel must be odd, at most 33.
+ * W * (Hq / Hkv) <= 128 and Hq / Hkv dividing 16 (1, 2, 4, 8 or 16), else
+ * KVS_ENOTIMPL; pool_kernel must be odd, at most 33.
  */
 KVS_API int kvs_snapkv_workspace_bytes(const kvs_geom* geom, int32_t window, size_t* bytes);
 KVS_API int kvs_snapkv_scores(const kvs_geom* geom, const void* q_window, int32_t window,
