@@ -77,6 +77,10 @@ CASES = [
     ("fp8", 128, 32, 8, 2064, 2, 0, False),
     ("fp8", 64, 4, 4, 96, 3, 0, False),
     ("fp8", 128, 16, 4, 400, 2, 37, False),
+    # group sizes that are not powers of two
+    ("bf16", 128, 12, 4, 528, 2, 0, False),
+    ("fp8", 64, 24, 4, 400, 2, 0, False),
+    ("fp8", 128, 12, 1, 528, 2, 100, False),
 ]
 
 

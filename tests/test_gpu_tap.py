@@ -36,6 +36,9 @@ TAP_CASES = [c + (3,) for c in FUSED_CASES] + [
     ("bf16", 128, 16, 4, 4112, 3, 0, False, "bf16", True, 2),
     ("fp8", 128, 16, 4, 1024, 2, 1000, True, "f32", False, 1),
     ("bf16", 64, 8, 2, 2064, 2, 700, False, "bf16", False, 2),
+    # group sizes that are not powers of two (G = 3 and 6)
+    ("fp8", 128, 12, 4, 1040, 2, 0, False, "f32", True, 3),
+    ("bf16", 128, 24, 4, 528, 2, 500, True, "bf16", False, 2),
 ]
 STEPS = 6
 
