@@ -485,19 +485,31 @@ def oracle_baseline(w, seed, seconds):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
-    i = w.context  # first decode position
-    n = i + 1
+    s0 = ring_start(w)
+    i = w.context + s0  # first decode position (a ring's steady state: a full window)
+    lo = max(0, i - w.window + 1) if w.window else 0
+    n = i - lo + 1
     done, elapsed = 0, 0.0
     wall0 = time.time()
     units = [(seq, layer) for layer in range(w.n_layers) for seq in range(w.batch)]
     for seq, layer in units:
         if elapsed >= seconds or (done and time.time() - wall0 > 5 * seconds):
             break
-        kr = synth.prefill_rows(w, seed, layer, seq, synth.T_K, "cuda")
-        vr = synth.prefill_rows(w, seed, layer, seq, synth.T_V, "cuda")
-        kn = torch.cat([kr, synth.step_rows(w, seed, layer, 0, synth.T_K, "cuda")[seq:seq + 1]]).cpu().numpy()
-        vn = torch.cat([vr, synth.step_rows(w, seed, layer, 0, synth.T_V, "cuda")[seq:seq + 1]]).cpu().numpy()
-        q = synth.step_rows(w, seed, layer, 0, synth.T_Q, "cuda")[seq].reshape(w.n_q_heads, w.head_dim)
+        if w.ring:
+            # the window's rows come from the per-step stream (decode steps lo .. i)
+            f, ch = lo - w.context, synth.STEP_CHUNK
+
+            def window_rows(tensor):
+                blks = [synth.step_block(w, seed, layer, c, tensor, "cuda") for c in range(f // ch, (f + n - 1) // ch + 1)]
+                return torch.cat(blks)[f - (f // ch) * ch:][:n, seq].cpu().numpy()
+
+            kn, vn = window_rows(synth.T_K), window_rows(synth.T_V)
+        else:
+            kr = synth.prefill_rows(w, seed, layer, seq, synth.T_K, "cuda")
+            vr = synth.prefill_rows(w, seed, layer, seq, synth.T_V, "cuda")
+            kn = torch.cat([kr, synth.step_rows(w, seed, layer, 0, synth.T_K, "cuda")[seq:seq + 1]]).cpu().numpy()
+            vn = torch.cat([vr, synth.step_rows(w, seed, layer, 0, synth.T_V, "cuda")[seq:seq + 1]]).cpu().numpy()
+        q = synth.step_rows(w, seed, layer, s0, synth.T_Q, "cuda")[seq].reshape(w.n_q_heads, w.head_dim)
         q = q.to(torch.bfloat16 if w.q_dtype == "bf16" else torch.float32).double().cpu().numpy()
         if w.kv_dtype == "fp8":  # the cache fill, not timed: a decode step reads codes already written
             kc, ks = orc.fp8_encode_rows(kn)
@@ -510,7 +522,7 @@ def oracle_baseline(w, seed, seconds):
             Vd = torch.from_numpy(vn).to(torch.bfloat16).double().numpy() if w.kv_dtype == "bf16" else vn.astype(np.float64)
         Kh = Kd.reshape(n, w.n_kv_heads, w.head_dim).transpose(1, 0, 2)
         Vh = Vd.reshape(n, w.n_kv_heads, w.head_dim).transpose(1, 0, 2)
-        orc.attend_scored(q, Kh, Vh, np.arange(n), i, w.window, None, orc.softmax_scale(w.head_dim),
+        orc.attend_scored(q, Kh, Vh, np.arange(lo, i + 1), i, w.window, None, orc.softmax_scale(w.head_dim),
                           w.n_blocks_max)
         elapsed += time.perf_counter() - t0
         done += 1
