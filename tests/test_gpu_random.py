@@ -1,0 +1,83 @@
+"""Randomized decode parity: a fixed, seeded draw of geometries (cache dtype,
+head dim, GQA group 1..16, capacity, batch, window or keep mask, ragged
+positions, deterministic or dynamic mode), each through the C ABI against the
+float64 oracle (scored attention and block masses, LLM mechanics: the write-
+then-attend decode step; Per-Head Scoring: one mass per 16-token block)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import kvs_oracle as orc
+from tests import gpu_support as gs
+from tests.test_gpu_parity import _build_linear, _rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _draw_cases(n, seed=2024):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for k in range(n):
+        kv = ("f32", "bf16", "fp8")[k % 3]
+        d = int(rng.choice((16, 64, 128))) if kv == "f32" else int(rng.choice((64, 128)))
+        Hkv = int(rng.choice((1, 2, 4, 8)))
+        G = int(rng.integers(1, 17))
+        C = 16 * int(rng.integers(2, 81))
+        B = int(rng.integers(1, 5))
+        window = int(rng.integers(1, C + 1)) if rng.random() < 0.3 else 0
+        keep = window == 0 and rng.random() < 0.4
+        det = bool(rng.random() < 0.3)
+        cases.append((kv, d, G * Hkv, Hkv, C, B, window, keep, det, k))
+    return cases
+
+
+CASES = _draw_cases(48)
+
+
+@pytest.fixture(scope="module")
+def api():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from heavy_hitter_eviction_amd import api as _api
+    return _api
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_random_geometry_matches_oracle(api, case):
+    kv, d, Hq, Hkv, C, B, window, use_keep, det, k = case
+    seed = 100 + k
+    geom, cache, K, V = _build_linear(api, kv, d, Hq, Hkv, C, B, window, seed, det)
+    rng = np.random.default_rng(seed)
+    cur = rng.integers(0, C, size=B).astype(np.int32)
+    cur[0] = C - 1
+    alive = None
+    keep = None
+    if use_keep:
+        alive = rng.random((B, geom.nb)) < 0.5
+        for b in range(B):
+            alive[b, cur[b] // 16] = True  # the current position's block stays
+        words = np.zeros((B, geom.words), dtype=np.int64)
+        for b in range(B):
+            for blk in np.flatnonzero(alive[b]):
+                words[b, blk >> 5] |= 1 << (blk & 31)
+        keep = gs.to_dev(words.astype(np.uint32).view(np.int32))
+    qdt = torch.float32 if kv == "f32" else torch.bfloat16
+    q = torch.from_numpy(_rows((B, Hq, d), (seed, 3))).to(qdt)
+    out = torch.empty_like(q).cuda()
+    mass = torch.zeros((B, geom.nb), dtype=torch.float32, device="cuda")
+    ws = torch.empty(api.decode_workspace_bytes(geom), dtype=torch.uint8, device="cuda")
+    print(f"case {case}: cur {cur.tolist()}", flush=True)
+    api.decode_attn_scored(cache, q.cuda(), gs.to_dev(cur), out, ws, mass_accum=mass, keep_mask=keep)
+    torch.cuda.synchronize()
+    o_gpu, m_gpu = out.float().cpu().numpy(), mass.cpu().numpy()
+    for b in range(B):
+        i = int(cur[b])
+        Kd = gs.heads(gs.dequant_rows(K[b, :i + 1], kv), Hkv, d)
+        Vd = gs.heads(gs.dequant_rows(V[b, :i + 1], kv), Hkv, d)
+        o_ref, m_ref, pav = gs.oracle_layer(q[b].double().numpy(), Kd, Vd, np.arange(i + 1), i, window,
+                                            None if alive is None else alive[b], orc.softmax_scale(d), geom.nb)
+        gs.close_o(o_gpu[b], o_ref, kv, pav)
+        gs.close_mass(m_gpu[b], m_ref, kv)
+        assert abs(m_gpu[b].sum() - Hq) <= 1e-3 * max(1, Hq / 16)
