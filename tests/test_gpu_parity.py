@@ -281,6 +281,10 @@ RING_CASES = [
     ("fp8", 128, 16, 4, 64, 64, 300),
     ("bf16", 128, 8, 2, 80, 50, 260),
     ("f32", 16, 4, 2, 32, 0, 100),
+    # GQA groups 3, 6 and 5; small rings; windows narrower than the ring
+    ("fp8", 64, 12, 4, 48, 40, 200),
+    ("bf16", 128, 6, 1, 96, 0, 230),
+    ("f32", 64, 10, 2, 16, 16, 90),
 ]
 
 
