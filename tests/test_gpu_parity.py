@@ -620,7 +620,8 @@ def test_filter_blocks_matches_oracle_exactly(api):
 
 # (seed, blocks per sequence or None for a random 40..2999): the wider ones
 # take 8 and 16 keys per thread, and past 16384 blocks the memory-reading kernel
-SELECT_CASES = [(s, None) for s in range(6)] + [(6, 8193), (7, 16384), (8, 16385), (9, 40000)]
+SELECT_CASES = [(s, None) for s in range(6)] + [(6, 8193), (7, 16384), (8, 16385), (9, 40000)] + \
+    [(s, None) for s in range(10, 20)]
 
 
 @pytest.mark.parametrize("seed,nb_fixed", SELECT_CASES)
@@ -628,9 +629,17 @@ def test_select_matches_oracle_exactly(api, seed, nb_fixed):
     rng = np.random.default_rng(seed)
     B = 4
     nb = int(rng.integers(40, 3000)) if nb_fixed is None else nb_fixed
-    score = (np.round(rng.random((B, nb)) * 50) / 50).astype(np.float32)   # many exact ties
+    if seed % 3 == 2:
+        # any float32 score is accepted: signed values, -0.0 and exact zeros
+        score = rng.standard_normal((B, nb)).astype(np.float32)
+        score[:, ::7] = 0.0
+        score[:, 3::11] = -0.0
+    else:
+        score = (np.round(rng.random((B, nb)) * 50) / 50).astype(np.float32)   # many exact ties
     cur = rng.integers(0, nb * 16, B).astype(np.int32)
     budget, recent, sinks = int(rng.integers(0, 200)), int(rng.integers(1, 900)), int(rng.integers(0, 40))
+    if seed >= 16:
+        budget = nb + 5  # more than the candidates: every alive block is kept
     alive = rng.random((B, nb)) < 0.7 if seed % 2 else None
     alive_t = None
     if alive is not None:
