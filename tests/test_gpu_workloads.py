@@ -407,3 +407,49 @@ def test_compact_mode_equals_evict_mode(session_mod, wname, every):
                 # not compacted yet: compacted-space blocks 0 .. pos/16 keep their origins
                 live = np.arange(int(pos_c[b]) // 16 + 1)
                 assert np.abs(att_c[b, live] - ev_att[b, origin[b, live]]).max() <= mtol
+
+
+# ---------------------------------------------------------------- SnapKV at full size
+
+def test_snapkv_397b_full_size_sampled(session_mod):
+    """SnapKV-style prefill scoring (Context views at marginal cost, section 3,
+    Fact 1) at the benchmark's shape and launch configuration: 16 sequences,
+    32 query / 8 KV heads, FP8, a 32768-token prompt, window 32, pooling
+    kernel 7, one layer's cache. The oracle checks sampled outputs one by one:
+    every token score of every head of sequence 11 and the block scores built
+    from them, and every token score of KV head 5's query heads in sequence 0."""
+    api, session = session_mod
+    w = workloads.QWEN397B_FP8
+    seed, W = 23, 32
+    B, Hq, Hkv, d, n = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.context
+    G = Hq // Hkv
+    geom = api.CacheGeom(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, capacity=w.capacity,
+                         kv_dtype="fp8", q_dtype="bf16")
+    cache = api.KVCache(geom)
+    for seq in range(B):
+        k = synth.prefill_rows(w, seed, 0, seq, synth.T_K, "cuda")
+        v = synth.prefill_rows(w, seed, 0, seq, synth.T_V, "cuda")
+        cache.append(k, v, torch.full((n,), seq, dtype=torch.int32, device="cuda"),
+                     torch.arange(n, dtype=torch.int32, device="cuda"))
+    qw = synth.normal((B, W, Hq * d), (seed, 97, 0), "cuda").reshape(B, W, Hq, d).to(torch.bfloat16).contiguous()
+    npr = torch.full((B,), n, dtype=torch.int32, device="cuda")
+    ts = torch.zeros((B, Hq, w.capacity), dtype=torch.float32, device="cuda")
+    bs = torch.zeros((B, geom.nb), dtype=torch.float32, device="cuda")
+    ws = torch.empty(api.snapkv_workspace_bytes(geom, W), dtype=torch.uint8, device="cuda")
+    print("snapkv full size: scoring", flush=True)
+    api.snapkv_scores(cache, qw, npr, ts, ws, block_score=bs, pool_kernel=7)
+    torch.cuda.synchronize()
+    scale = orc.softmax_scale(d)
+    q64 = _np(qw.float()).astype(np.float64)
+    for seq, kv_heads in ((11, range(Hkv)), (0, (5,))):
+        Kd = gs.heads(gs.dequant_rows(_np(synth.prefill_rows(w, seed, 0, seq, synth.T_K, "cuda")), "fp8"), Hkv, d)
+        ref = np.zeros((Hq, n))
+        for g in kv_heads:
+            hs = slice(g * G, (g + 1) * G)
+            ref[hs] = orc.snapkv_token_scores(q64[seq][:, hs], Kd[g:g + 1], n, scale)
+            got = _np(ts[seq, hs, :n]).astype(np.float64)
+            err = np.abs(got - ref[hs]).max()
+            assert err <= 1e-5 * max(1.0, ref[hs].max()), f"sequence {seq}, KV head {g}: max err {err}"
+        if len(kv_heads) == Hkv:
+            want = orc.snapkv_block_scores(orc.max_pool_tokens(ref, 7), geom.nb)
+            gs.close_mass(_np(bs[seq]), want, "fp8", f"sequence {seq} block scores")
