@@ -453,3 +453,64 @@ def test_snapkv_397b_full_size_sampled(session_mod):
         if len(kv_heads) == Hkv:
             want = orc.snapkv_block_scores(orc.max_pool_tokens(ref, 7), geom.nb)
             gs.close_mass(_np(bs[seq]), want, "fp8", f"sequence {seq} block scores")
+
+
+# ---------------------------------------------------------------- NEXT rows at full size
+
+def test_profiled_and_reattend_397b_full_size_sampled(session_mod):
+    """At the benchmark's shape (16 sequences, 32 query / 8 KV heads, FP8,
+    32768 cached tokens, one layer): the profiled call's output, block masses,
+    per-head masses and their max over heads (Context views at marginal cost,
+    section 4), and a re-attend of a new query over 300 listed blocks (Tier 2,
+    Fact 3), each checked against the oracle for sampled sequences."""
+    api, session = session_mod
+    w = workloads.QWEN397B_FP8
+    seed = 31
+    B, Hq, Hkv, d, n = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.context
+    geom = api.CacheGeom(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, capacity=w.capacity,
+                         kv_dtype="fp8", q_dtype="bf16")
+    cache = api.KVCache(geom)
+    for seq in range(B):
+        cache.append(synth.prefill_rows(w, seed, 0, seq, synth.T_K, "cuda"),
+                     synth.prefill_rows(w, seed, 0, seq, synth.T_V, "cuda"),
+                     torch.full((n,), seq, dtype=torch.int32, device="cuda"),
+                     torch.arange(n, dtype=torch.int32, device="cuda"))
+    i = n - 1
+    cur = torch.full((B,), i, dtype=torch.int32, device="cuda")
+    ws = torch.empty(api.decode_workspace_bytes(geom), dtype=torch.uint8, device="cuda")
+    nb = geom.nb
+    f32 = dict(dtype=torch.float32, device="cuda")
+    q = synth.normal((B, Hq * d), (seed, 5), "cuda").reshape(B, Hq, d).to(torch.bfloat16).contiguous()
+    out, mass = torch.empty_like(q), torch.zeros((B, nb), **f32)
+    head_mass, mass_max = torch.zeros((B, Hq, nb), **f32), torch.zeros((B, nb), **f32)
+    print("full size: profiled call", flush=True)
+    api.decode_attn_profiled(cache, q, cur, out, ws, mass_accum=mass, head_mass=head_mass, mass_max=mass_max)
+    q2 = synth.normal((B, Hq * d), (seed, 6), "cuda").reshape(B, Hq, d).to(torch.bfloat16).contiguous()
+    rng = np.random.default_rng(seed)
+    S = 300
+    ids = np.stack([np.append(rng.choice(i // 16, S - 1, replace=False), i // 16) for _ in range(B)]).astype(np.int32)
+    n_ids = np.full(B, S, dtype=np.int32)
+    out2, mass2 = torch.empty_like(q2), torch.zeros((B, nb), **f32)
+    print("full size: re-attend", flush=True)
+    api.reattend_blocks(cache, q2, cur, gs.to_dev(ids), gs.to_dev(n_ids), out2, ws, mass_accum=mass2)
+    torch.cuda.synchronize()
+    scale = orc.softmax_scale(d)
+    pos = np.arange(n)
+    for seq in (4, 13):
+        Kd = gs.heads(gs.dequant_rows(_np(synth.prefill_rows(w, seed, 0, seq, synth.T_K, "cuda")), "fp8"), Hkv, d)
+        Vd = gs.heads(gs.dequant_rows(_np(synth.prefill_rows(w, seed, 0, seq, synth.T_V, "cuda")), "fp8"), Hkv, d)
+        qs = _np(q[seq].float()).astype(np.float64)
+        o, m, hm, mx = orc.attend_profiled(qs, Kd, Vd, pos, i, 0, None, scale, nb)
+        _, _, pav = gs.oracle_layer(qs, Kd, Vd, pos, i, 0, None, scale, nb)
+        gs.close_o(_np(out[seq].float()), o, "fp8", pav)
+        gs.close_mass(_np(mass[seq]), m, "fp8", f"sequence {seq} masses")
+        gs.close_mass(_np(head_mass[seq]), hm, "fp8", f"sequence {seq} per-head masses")
+        gs.close_mass(_np(mass_max[seq]), mx, "fp8", f"sequence {seq} max over heads")
+        q2s = _np(q2[seq].float()).astype(np.float64)
+        o2, m2 = orc.reattend_blocks(q2s, Kd, Vd, pos, i, ids[seq], scale, nb)
+        alive = np.zeros(nb, dtype=bool)
+        alive[ids[seq]] = True
+        _, _, pav2 = gs.oracle_layer(q2s, Kd, Vd, pos, i, 0, alive, scale, nb)
+        gs.close_o(_np(out2[seq].float()), o2, "fp8", pav2)
+        gs.close_mass(_np(mass2[seq]), m2, "fp8", f"sequence {seq} re-attend masses")
+        assert not _np(mass2[seq])[~alive].any()
