@@ -514,3 +514,75 @@ def test_profiled_and_reattend_397b_full_size_sampled(session_mod):
         gs.close_o(_np(out2[seq].float()), o2, "fp8", pav2)
         gs.close_mass(_np(mass2[seq]), m2, "fp8", f"sequence {seq} re-attend masses")
         assert not _np(mass2[seq])[~alive].any()
+
+
+def test_compact_blocks_397b_full_size_sampled(session_mod):
+    """Block compaction (Context Optimization, H2O step 4) of the 32K FP8
+    cache at the benchmark's shape, keeping each sequence's H2O selection
+    (512 heavy blocks plus the last 1024 tokens): for sampled sequences, the
+    moved codes, scales and a side table bit-exact against the oracle's
+    gather, and decoding the compacted cache equal to the oracle's masked
+    decode of the original."""
+    api, session = session_mod
+    w = workloads.QWEN397B_FP8
+    seed = 37
+    B, Hq, Hkv, d, n = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.context
+    C = w.capacity
+    geom = api.CacheGeom(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, capacity=C,
+                         kv_dtype="fp8", q_dtype="bf16")
+    cache = api.KVCache(geom)
+    for seq in range(B):
+        cache.append(synth.prefill_rows(w, seed, 0, seq, synth.T_K, "cuda"),
+                     synth.prefill_rows(w, seed, 0, seq, synth.T_V, "cuda"),
+                     torch.full((n,), seq, dtype=torch.int32, device="cuda"),
+                     torch.arange(n, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    nb, i = geom.nb, n - 1
+    rng = np.random.default_rng(seed)
+    raw = lambda t: t.contiguous().view(-1).view(torch.uint8).cpu().numpy()  # noqa: E731
+    check = (2, 9)
+    before = {s: (gs.logical_rows(raw(cache.k), B, Hkv, C, d, 1, s, np.arange(i + 1), "k"),
+                  gs.logical_rows(raw(cache.v), B, Hkv, C, d, 1, s, np.arange(i + 1), "v")) for s in check}
+    before_ks = cache.k_scale.cpu().numpy().reshape(B, C)[:, :i + 1].copy()
+    before_vs = cache.v_scale.cpu().numpy().reshape(B, C)[:, :i + 1].copy()
+    score = rng.random((B, nb))
+    keeps = [orc.select_blocks(score[b], None, i, w.budget_blocks, w.recent_tokens, 0) for b in range(B)]
+    S = max(len(k) for k in keeps)
+    ids = np.full((B, S), -1, dtype=np.int32)
+    n_keep = np.array([len(k) for k in keeps], dtype=np.int32)
+    for b in range(B):
+        ids[b, :n_keep[b]] = keeps[b]
+    att = rng.random((B, nb)).astype(np.float32)
+    t_att = gs.to_dev(att.copy())
+    print("full size: compaction", flush=True)
+    api.compact_blocks(cache, gs.to_dev(ids), gs.to_dev(n_keep), tables=(t_att,))
+    torch.cuda.synchronize()
+    cur2 = np.array([orc.compacted_position(i, int(n_keep[b])) for b in range(B)], dtype=np.int32)
+    q = synth.normal((B, Hq * d), (seed, 8), "cuda").reshape(B, Hq, d).to(torch.bfloat16).contiguous()
+    out = torch.empty_like(q)
+    mass = torch.zeros((B, nb), dtype=torch.float32, device="cuda")
+    ws = torch.empty(api.decode_workspace_bytes(geom), dtype=torch.uint8, device="cuda")
+    api.decode_attn_scored(cache, q, gs.to_dev(cur2), out, ws, mass_accum=mass)
+    torch.cuda.synchronize()
+    got_k, got_v = raw(cache.k), raw(cache.v)
+    scale = orc.softmax_scale(d)
+    for s in check:
+        keep, i2 = keeps[s], int(cur2[s])
+        for which, got, old in (("k", got_k, before[s][0]), ("v", got_v, before[s][1])):
+            new_rows = gs.logical_rows(got, B, Hkv, C, d, 1, s, np.arange(i2 + 1), which)
+            assert np.array_equal(new_rows, orc.compact_rows(old, keep, i2 + 1)), (s, which)
+        assert np.array_equal(cache.k_scale.cpu().numpy().reshape(B, C)[s, :i2 + 1],
+                              orc.compact_rows(before_ks[s], keep, i2 + 1))
+        assert np.array_equal(cache.v_scale.cpu().numpy().reshape(B, C)[s, :i2 + 1],
+                              orc.compact_rows(before_vs[s], keep, i2 + 1))
+        assert np.array_equal(_np(t_att[s]), orc.compact_table(att[s][None], keep)[0])
+        Kd = gs.heads(gs.dequant_rows(_np(synth.prefill_rows(w, seed, 0, s, synth.T_K, "cuda")), "fp8"), Hkv, d)
+        Vd = gs.heads(gs.dequant_rows(_np(synth.prefill_rows(w, seed, 0, s, synth.T_V, "cuda")), "fp8"), Hkv, d)
+        alive = np.zeros(nb, dtype=bool)
+        alive[keep] = True
+        o_ref, m_ref, pav = gs.oracle_layer(_np(q[s].float()).astype(np.float64), Kd, Vd, np.arange(n), i, 0,
+                                            alive, scale, nb)
+        gs.close_o(_np(out[s].float()), o_ref, "fp8", pav)
+        m_new = np.zeros(nb)
+        m_new[:len(keep)] = m_ref[keep]
+        gs.close_mass(_np(mass[s]), m_new, "fp8", f"sequence {s} compacted masses")
