@@ -129,3 +129,56 @@ def test_decode_is_exact_product():
     s = np.array([np.float32(0.0123)], dtype=np.float32)
     dec = orc.fp8_decode_rows(codes, s)
     assert np.array_equal(dec[0], orc.e4m3_table()[codes[0]] * float(s[0]))
+
+
+def _quotient_rows(seed, n_rows=400, row_len=256):
+    """Rows whose elements sit one float32 ulp around values ``m * s`` where m
+    is an E4M3 rounding midpoint and s the row's scale: there a quotient that
+    is off by one ulp (a reciprocal multiply instead of a division) changes
+    the code. Element 0 fixes the row's absmax (so s is known in advance)."""
+    rng = np.random.default_rng(seed)
+    t = orc.e4m3_table()[:0x77]
+    mids = (t[:-1] + t[1:]) / 2                      # midpoints below 240
+    rows = np.zeros((n_rows, row_len), dtype=np.float32)
+    for r in range(n_rows):
+        amax = np.float32(rng.uniform(0.5, 4.0) * 2.0 ** rng.integers(-20, 20))
+        s = np.float32(amax / np.float32(240.0))
+        m = rng.choice(mids, row_len - 1)
+        x = (m * np.float64(s)).astype(np.float32)
+        nudge = rng.integers(-2, 3, row_len - 1)
+        for k in range(1, 3):
+            up, dn = nudge >= k, nudge <= -k
+            x[up] = np.nextafter(x[up], np.float32(np.inf))
+            x[dn] = np.nextafter(x[dn], np.float32(0))
+        x *= np.where(rng.random(row_len - 1) < 0.5, np.float32(-1), np.float32(1))
+        rows[r, 0] = amax
+        rows[r, 1:] = x
+    return rows
+
+
+def test_row_quotient_is_a_correctly_rounded_division():
+    """Context Optimization, "FP8 KV Cache / How It Works": each value is
+    divided by its position's scale before quantisation. The oracle's codes
+    must equal torch's independent float8_e4m3fn cast of numpy's IEEE float32
+    quotient x / s (a correctly rounded division), on random rows and on rows
+    built so that a quotient one ulp off changes the code."""
+    rng = np.random.default_rng(3)
+    plain = (rng.standard_normal((300, 1024)) * rng.uniform(1e-4, 1e4, (300, 1))).astype(np.float32)
+    for x in (plain, _quotient_rows(11)):
+        codes, scales = orc.fp8_encode_rows(x)
+        y = x / scales[:, None]                       # float32 / float32: IEEE division
+        assert y.dtype == np.float32
+        ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(codes, ref)
+
+
+def test_reciprocal_multiply_quotient_fails_the_pin():
+    """Negative control for the pin above: a quotient taken as x * (1/s) in
+    float32 gives other codes on the constructed rows, so the pin can tell the
+    two apart."""
+    x = _quotient_rows(11)
+    codes, scales = orc.fp8_encode_rows(x)
+    recip = (np.float32(1.0) / scales).astype(np.float32)
+    y_bad = (x * recip[:, None]).astype(np.float32)
+    bad = torch.from_numpy(y_bad).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert not np.array_equal(codes, bad)
