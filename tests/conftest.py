@@ -16,3 +16,19 @@ def pytest_configure(config):
 def gpu_available():
     import torch
     return torch.cuda.is_available()
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Worst |got - ref| / bound of the output checks per test (GPU runs)."""
+    import json
+    mod = sys.modules.get("tests.gpu_support")
+    ratios = getattr(mod, "WORST_RATIO", None) if mod else None
+    if not ratios:
+        return
+    terminalreporter.write_sep("-", "worst output error / bound per test")
+    for name, r in sorted(ratios.items(), key=lambda kv: -kv[1]):
+        terminalreporter.write_line(f"{r:8.4f}  {name}")
+    path = os.environ.get("KVS_RATIO_FILE")
+    if path:
+        with open(path, "w") as f:
+            json.dump(ratios, f, indent=1, sort_keys=True)

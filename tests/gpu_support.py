@@ -26,34 +26,73 @@ def heads(rows: np.ndarray, n_heads: int, d: int) -> np.ndarray:
     return rows.reshape(rows.shape[0], n_heads, d).transpose(1, 0, 2)
 
 
+def out_spread(p: np.ndarray, Vsel: np.ndarray) -> np.ndarray:
+    """``[2, Hq, d]`` spread of the PV sum for weights ``p [Hq, n]`` over the
+    read values ``Vsel [Hkv, n, d]`` (query head h reads KV head h // G)."""
+    G = p.shape[0] // Vsel.shape[0]
+    pav = np.stack([p[h] @ np.abs(Vsel[h // G]) for h in range(p.shape[0])])
+    rms = np.sqrt(np.stack([(p[h] * p[h]) @ (Vsel[h // G] * Vsel[h // G]) for h in range(p.shape[0])]))
+    return np.stack([pav, rms])
+
+
 def oracle_layer(q, Kd, Vd, positions, i, window, alive, scale, n_blocks):
-    """Oracle output, block mass and the PV rounding scale ``sum_j p_j |v_j|``
-    for one (sequence, layer): ``Kd``, ``Vd`` are [Hkv, n, d] float64 values
-    held at absolute ``positions``."""
+    """Oracle output, block mass and the output's spread (``out_spread``) for
+    one (sequence, layer): ``Kd``, ``Vd`` are [Hkv, n, d] float64 values held
+    at absolute ``positions``."""
     positions = np.asarray(positions)
     sel = np.array([orc.key_visible(int(p), i, window) and orc.block_alive(alive, orc.block_of(int(p)))
                     for p in positions], dtype=bool)
     o, p = orc.attend(q, Kd[:, sel], Vd[:, sel], scale)
     mass = orc.block_mass(p, positions[sel], n_blocks)
-    G = q.shape[0] // Kd.shape[0]
-    absv = np.abs(Vd[:, sel])
-    pav = np.stack([p[h] @ absv[h // G] for h in range(q.shape[0])])
-    return o, mass, pav
+    return o, mass, out_spread(p, Vd[:, sel])
 
 
-def close_o(got: np.ndarray, ref: np.ndarray, kv_dtype: str, pav: np.ndarray | None = None):
-    """Output tolerance derived from the arithmetic. Float32 caches: rtol 1e-5,
-    atol 1e-6. bf16 and FP8 caches: the output is rounded to bf16 (relative
-    2^-9) and the PV product takes the weights as bf16, which moves each
-    output by at most 2^-9 * sum_j p_j |v_j|; the bound used is
-    |d| <= 2e-2 |ref| + 2^-8 * sum_j p_j |v_j| (``pav``), a factor 2 above it."""
+# Output tolerance for bf16 and FP8 caches (float32 caches: rtol 1e-5, atol
+# 1e-6). The kernel takes the post-softmax weights into the PV product as
+# bf16 (for FP8 the V scale folded in first): each term p_j v_j gets an
+# independent relative rounding error of at most 2^-8 (round to nearest even
+# with 8 significant bits), zero-mean and of standard deviation below 2^-9,
+# so the output moves by about 2^-9 sqrt(sum_j p_j^2 v_j^2) and, with the
+# largest of ~10^5 elements checked per call, stays far below 8 of those.
+# The output itself is rounded to bf16 (relative 2^-8) and lies inside the
+# north-star relative tolerance 2e-2. Float32 logits, exponentials and
+# accumulation add far less than 2^-20 sum_j p_j |v_j|.
+OUT_REL = 2e-2
+OUT_SIGMAS = 8.0
+OUT_F32_FLOOR = 2.0 ** -20
+
+
+def out_bound(ref: np.ndarray, spread: np.ndarray, runs: int = 1) -> np.ndarray:
+    """Largest allowed |got - ref| per element for a bf16/FP8-cache output;
+    ``runs = 2`` bounds the difference of two independently rounded GPU runs."""
+    return (OUT_REL * np.abs(ref) + runs * OUT_SIGMAS * 2.0 ** -9 * spread[1]
+            + runs * OUT_F32_FLOOR * spread[0])
+
+
+# worst |got - ref| / bound per test, reported at the end of a GPU session
+WORST_RATIO: dict = {}
+
+
+def _note_ratio(ratio: float):
+    import os
+    key = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    WORST_RATIO[key] = max(WORST_RATIO.get(key, 0.0), ratio)
+
+
+def close_o(got: np.ndarray, ref: np.ndarray, kv_dtype: str, spread: np.ndarray | None = None):
+    """Output check: float32 caches within rtol 1e-5, atol 1e-6; bf16 and FP8
+    caches within ``out_bound`` (see above)."""
     got = np.asarray(got, dtype=np.float64)
+    err = np.abs(got - ref)
     if kv_dtype == "f32":
-        bad = np.abs(got - ref) > 1e-5 * np.abs(ref) + 1e-6
+        bound = 1e-5 * np.abs(ref) + 1e-6
     else:
-        assert pav is not None
-        bad = np.abs(got - ref) > 2e-2 * np.abs(ref) + 2.0 ** -8 * pav
-    assert not bad.any(), f"O mismatch at {np.argwhere(bad)[:5].tolist()}: max err {np.abs(got - ref).max()}"
+        assert spread is not None
+        bound = out_bound(ref, spread)
+    _note_ratio(float((err / bound).max()) if err.size else 0.0)
+    bad = err > bound
+    assert not bad.any(), (f"O mismatch at {np.argwhere(bad)[:5].tolist()}: max err {err.max()}, "
+                           f"worst err/bound {(err / bound).max():.3g}")
 
 
 def close_mass(got: np.ndarray, ref: np.ndarray, kv_dtype: str, what="mass"):

@@ -97,9 +97,8 @@ def test_fused_append_decode_equals_append_then_decode(api, case):
     ref_cache = _prefill(api, geom, K, V, src_dt, start)
     fz_cache = _prefill(api, geom, K, V, src_dt, start)
     qdt = torch.float32 if kv == "f32" else torch.bfloat16
-    ws_bytes = api.decode_workspace_bytes(geom)
-    ws_r = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-    ws_f = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    ws_r = api.decode_workspace(geom)
+    ws_f = api.decode_workspace(geom)
     mass_r = torch.zeros((B, geom.nb), dtype=torch.float32, device="cuda")
     mass_f = torch.zeros((B, geom.nb), dtype=torch.float32, device="cuda")
     seqs = torch.arange(B, dtype=torch.int32, device="cuda")
@@ -140,7 +139,7 @@ def test_fused_append_decode_dynamic_mode_matches_oracle(api, case):
     geom, K, V, src_dt, start, keep, alive = _setup(api, case, deterministic=False, seed=31)
     cache = _prefill(api, geom, K, V, src_dt, start)
     qdt = torch.float32 if kv == "f32" else torch.bfloat16
-    ws = torch.empty(api.decode_workspace_bytes(geom), dtype=torch.uint8, device="cuda")
+    ws = api.decode_workspace(geom)
     scale = orc.softmax_scale(d)
     n_steps = 6
     for t in range(n_steps):
@@ -162,7 +161,7 @@ def test_fused_append_decode_dynamic_mode_matches_oracle(api, case):
         lo = max(0, i - min(eff_w, C) + 1) if ring else 0
         Kd = gs.heads(gs.dequant_rows(Ksrc[b, lo:i + 1], kv), Hkv, d)
         Vd = gs.heads(gs.dequant_rows(Vsrc[b, lo:i + 1], kv), Hkv, d)
-        o_ref, m_ref, pav = gs.oracle_layer(q[b].double().numpy(), Kd, Vd, np.arange(lo, i + 1), i, window,
+        o_ref, m_ref, spread = gs.oracle_layer(q[b].double().numpy(), Kd, Vd, np.arange(lo, i + 1), i, window,
                                             None if alive is None else alive[b], scale, geom.nb)
-        gs.close_o(out[b].float().cpu().numpy(), o_ref, kv, pav)
+        gs.close_o(out[b].float().cpu().numpy(), o_ref, kv, spread)
         gs.close_mass(mass[b].cpu().numpy(), m_ref, kv)

@@ -109,7 +109,7 @@ def test_decode_matches_oracle(api, case):
     geom, cache, K, V = _build_linear(api, kv, d, Hq, Hkv, C, B, window, seed)
     rng = np.random.default_rng(seed)
     qdt = torch.float32 if kv == "f32" else torch.bfloat16
-    ws = torch.empty(api.decode_workspace_bytes(geom), dtype=torch.uint8, device="cuda")
+    ws = api.decode_workspace(geom)
     scale = orc.softmax_scale(d)
     for trial in range(3):
         cur = np.array([C - 1 if trial == 0 else int(rng.integers(0, C)) for _ in range(B)], dtype=np.int32)
@@ -125,9 +125,9 @@ def test_decode_matches_oracle(api, case):
             i = int(cur[b])
             Kd = gs.heads(gs.dequant_rows(K[b, :i + 1], kv), Hkv, d)
             Vd = gs.heads(gs.dequant_rows(V[b, :i + 1], kv), Hkv, d)
-            o_ref, m_ref, pav = gs.oracle_layer(q[b].double().numpy(), Kd, Vd, np.arange(i + 1), i, window,
+            o_ref, m_ref, spread = gs.oracle_layer(q[b].double().numpy(), Kd, Vd, np.arange(i + 1), i, window,
                                                 None, scale, geom.nb)
-            gs.close_o(o_gpu[b], o_ref, kv, pav)
+            gs.close_o(o_gpu[b], o_ref, kv, spread)
             gs.close_mass(m_gpu[b], m_ref, kv)
             assert abs(m_gpu[b].sum() - Hq) <= 1e-3
 
@@ -137,7 +137,7 @@ def _three_runs(api, kv, d, Hq, Hkv, C, deterministic):
     qdt = torch.float32 if kv == "f32" else torch.bfloat16
     q = torch.from_numpy(_rows((2, Hq, d), (7, 9))).to(qdt).cuda()
     cur = torch.tensor([C - 1, C // 2], dtype=torch.int32, device="cuda")
-    ws = torch.empty(api.decode_workspace_bytes(geom), dtype=torch.uint8, device="cuda")
+    ws = api.decode_workspace(geom)
     outs, masses = [], []
     for scored in (True, True, False):
         out = torch.empty_like(q)
@@ -160,6 +160,35 @@ def test_deterministic_mode_is_bit_reproducible_and_unscored_output_is_identical
         assert torch.equal(outs[0], outs[1]) and torch.equal(masses[0], masses[1])
 
 
+def test_workspace_init_clears_stale_content(api):
+    """The decode calls need the workspace's completion flags zero at entry
+    and leave them zero. A workspace full of stale non-zero words (a ramp of
+    int32 values, as left by earlier positions, ids or another geometry's
+    records) gives bit-identical results to a fresh one once
+    kvs_decode_workspace_init has run, and keeps doing so over later calls
+    with no further initialisation; so does one reused for another geometry
+    after re-initialising it."""
+    big = api.decode_workspace_bytes(api.CacheGeom(batch=4, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                                                   capacity=4096, kv_dtype="fp8"))
+    stale = torch.arange(big // 4, dtype=torch.int32, device="cuda").view(torch.uint8)
+    for kv, d, Hq, Hkv, C in _DET_CASES[:2]:
+        geom, cache, K, V = _build_linear(api, kv, d, Hq, Hkv, C, 2, 0, 11, True)
+        assert api.decode_workspace_bytes(geom) <= big
+        q = torch.from_numpy(_rows((2, Hq, d), (11, 9))).to(torch.bfloat16).cuda()
+        cur = torch.tensor([C - 1, C // 3], dtype=torch.int32, device="cuda")
+        fresh = api.decode_workspace(geom)
+        # the first geometry finds the ramp, the second the first one's records
+        api.decode_workspace_init(geom, stale)
+        ref_out, ref_mass = torch.empty_like(q), torch.zeros((2, geom.nb), dtype=torch.float32, device="cuda")
+        api.decode_attn_scored(cache, q, cur, ref_out, fresh, mass_accum=ref_mass)
+        for call in range(3):
+            out, mass = torch.empty_like(q), torch.zeros_like(ref_mass)
+            api.decode_attn_scored(cache, q, cur, out, stale, mass_accum=mass)
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), (kv, call)
+            assert torch.equal(mass, ref_mass), (kv, call)
+
+
 def test_dynamic_mode_matches_deterministic_mode_up_to_rounding(api):
     # Dynamic tile sharing changes which running max each tile's weights are
     # taken relative to. Masses and f32-cache outputs then differ by f32
@@ -177,9 +206,9 @@ def test_dynamic_mode_matches_deterministic_mode_up_to_rounding(api):
                 i = int(cur[b])
                 Kd = gs.heads(gs.dequant_rows(K[b, :i + 1], kv), Hkv, d)
                 Vd = gs.heads(gs.dequant_rows(V[b, :i + 1], kv), Hkv, d)
-                _, _, pav = gs.oracle_layer(q[b].double().cpu().numpy(), Kd, Vd, np.arange(i + 1), i, 0, None,
+                _, _, spread = gs.oracle_layer(q[b].double().cpu().numpy(), Kd, Vd, np.arange(i + 1), i, 0, None,
                                             orc.softmax_scale(d), geom.nb)
-                tol[b] = 2.0 ** -8 * pav + 2.0 ** -7 * np.abs(ref[b])
+                tol[b] = gs.out_bound(ref[b], spread, runs=2)
         for o in dyn_o:
             assert (np.abs(o.float().cpu().numpy() - ref) <= tol).all()
         for m in (dyn_m[0], dyn_m[1]):
@@ -204,16 +233,16 @@ def test_keep_mask_skips_dropped_blocks(api):
         q = torch.from_numpy(_rows((B, Hq, d), (19, 5))).to(torch.bfloat16)
         out = torch.empty_like(q).cuda()
         mass = torch.zeros((B, geom.nb), dtype=torch.float32, device="cuda")
-        ws = torch.empty(api.decode_workspace_bytes(geom), dtype=torch.uint8, device="cuda")
+        ws = api.decode_workspace(geom)
         api.decode_attn_scored(cache, q.cuda(), gs.to_dev(cur), out, ws, mass_accum=mass, keep_mask=keep)
         torch.cuda.synchronize()
         for b in range(B):
             i = int(cur[b])
             Kd = gs.heads(gs.dequant_rows(K[b, :i + 1], kv), Hkv, d)
             Vd = gs.heads(gs.dequant_rows(V[b, :i + 1], kv), Hkv, d)
-            o_ref, m_ref, pav = gs.oracle_layer(q[b].double().numpy(), Kd, Vd, np.arange(i + 1), i, 0,
+            o_ref, m_ref, spread = gs.oracle_layer(q[b].double().numpy(), Kd, Vd, np.arange(i + 1), i, 0,
                                                 alive[b], orc.softmax_scale(d), geom.nb)
-            gs.close_o(out[b].float().cpu().numpy(), o_ref, kv, pav)
+            gs.close_o(out[b].float().cpu().numpy(), o_ref, kv, spread)
             gs.close_mass(mass[b].cpu().numpy(), m_ref, kv)
 
 
@@ -252,7 +281,7 @@ def test_reattend_blocks_matches_oracle(api, case):
     q = torch.from_numpy(_rows((B, Hq, d), (23, 8))).to(qdt)
     out = torch.empty_like(q).cuda()
     mass = torch.zeros((B, geom.nb), dtype=torch.float32, device="cuda")
-    ws = torch.empty(api.decode_workspace_bytes(geom), dtype=torch.uint8, device="cuda")
+    ws = api.decode_workspace(geom)
     api.reattend_blocks(cache, q.cuda(), gs.to_dev(cur), gs.to_dev(ids), gs.to_dev(n_ids), out, ws,
                         mass_accum=mass)
     torch.cuda.synchronize()
@@ -269,9 +298,9 @@ def test_reattend_blocks_matches_oracle(api, case):
             continue
         alive = np.zeros(geom.nb, dtype=bool)
         alive[[c for c in chosen if 0 <= c < geom.nb]] = True
-        _, _, pav = gs.oracle_layer(q[b].double().numpy(), Kd, Vd, np.arange(i + 1), i, 0, alive,
+        _, _, spread = gs.oracle_layer(q[b].double().numpy(), Kd, Vd, np.arange(i + 1), i, 0, alive,
                                     orc.softmax_scale(d), geom.nb)
-        gs.close_o(o_gpu, o_ref, kv, pav)
+        gs.close_o(o_gpu, o_ref, kv, spread)
         gs.close_mass(m_gpu, m_ref, kv)
         assert not m_gpu[~alive].any()
 
@@ -304,7 +333,7 @@ def test_ring_cache_matches_full_masked_reference(api, case):
     Q = _rows((steps, B, Hq, d), (5, 3))
     src_dt = torch.float32 if kv in ("f32", "fp8") else torch.bfloat16
     qdt = torch.float32 if kv == "f32" else torch.bfloat16
-    ws = torch.empty(api.decode_workspace_bytes(geom), dtype=torch.uint8, device="cuda")
+    ws = api.decode_workspace(geom)
     seqs = torch.arange(B, dtype=torch.int32, device="cuda")
     Kd = np.stack([gs.dequant_rows(K[:, b], kv) for b in range(B)])   # [B, steps, w]
     Vd = np.stack([gs.dequant_rows(V[:, b], kv) for b in range(B)])
@@ -323,10 +352,10 @@ def test_ring_cache_matches_full_masked_reference(api, case):
         eff_w = window if window else C
         for b in range(B):
             lo = max(0, i - min(eff_w, C) + 1)
-            o_ref, m_ref, pav = gs.oracle_layer(q[b].double().numpy(), gs.heads(Kd[b, lo:i + 1], Hkv, d),
+            o_ref, m_ref, spread = gs.oracle_layer(q[b].double().numpy(), gs.heads(Kd[b, lo:i + 1], Hkv, d),
                                                 gs.heads(Vd[b, lo:i + 1], Hkv, d), np.arange(lo, i + 1), i,
                                                 window, None, scale, nb)
-            gs.close_o(out[b].float().cpu().numpy(), o_ref, kv, pav)
+            gs.close_o(out[b].float().cpu().numpy(), o_ref, kv, spread)
             gs.close_mass(mass[b].cpu().numpy(), m_ref, kv)
         checked += 1
     assert checked > 20
@@ -338,8 +367,8 @@ def test_ring_cache_matches_full_masked_reference(api, case):
 
 def _oracle_profiled(q, Kd, Vd, positions, i, window, alive, scale, nb):
     o, m, hm, mx = orc.attend_profiled(q, Kd, Vd, positions, i, window, alive, scale, nb)
-    _, _, pav = gs.oracle_layer(q, Kd, Vd, positions, i, window, alive, scale, nb)
-    return o, m, hm, mx, pav
+    _, _, spread = gs.oracle_layer(q, Kd, Vd, positions, i, window, alive, scale, nb)
+    return o, m, hm, mx, spread
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8", "f32"])
@@ -366,7 +395,7 @@ def test_profiled_decode_per_head_and_max_over_heads(api, kv):
     base_mx = rng.random((B, nb)).astype(np.float32) * 0.01
     hm_dev, mx_dev = gs.to_dev(base_hm.copy()), gs.to_dev(base_mx.copy())
     mass = torch.zeros((B, nb), dtype=torch.float32, device="cuda")
-    ws = torch.empty(api.decode_workspace_bytes(geom), dtype=torch.uint8, device="cuda")
+    ws = api.decode_workspace(geom)
     want_hm, want_mx, want_m = base_hm.astype(np.float64), base_mx.astype(np.float64), np.zeros((B, nb))
     for call in range(2):
         q = torch.from_numpy(_rows((B, Hq, d), (13, 40 + call))).to(qdt)
@@ -379,9 +408,9 @@ def test_profiled_decode_per_head_and_max_over_heads(api, kv):
             i = int(cur[b])
             Kd = gs.heads(gs.dequant_rows(K[b, :i + 1], kv), Hkv, d)
             Vd = gs.heads(gs.dequant_rows(V[b, :i + 1], kv), Hkv, d)
-            o, m, hm, mx, pav = _oracle_profiled(q[b].double().numpy(), Kd, Vd, np.arange(i + 1), i, 0,
+            o, m, hm, mx, spread = _oracle_profiled(q[b].double().numpy(), Kd, Vd, np.arange(i + 1), i, 0,
                                                  alive[b] if call == 1 else None, orc.softmax_scale(d), nb)
-            gs.close_o(out[b].float().cpu().numpy(), o, kv, pav)
+            gs.close_o(out[b].float().cpu().numpy(), o, kv, spread)
             want_hm[b] += hm
             want_mx[b] = np.maximum(want_mx[b], mx)
             want_m[b] += m
@@ -414,7 +443,7 @@ def test_profiled_ring_decode_per_head(api):
     out = torch.empty_like(q).cuda()
     hm_dev = torch.zeros((B, Hq, nb), dtype=torch.float32, device="cuda")
     mx_dev = torch.zeros((B, nb), dtype=torch.float32, device="cuda")
-    ws = torch.empty(api.decode_workspace_bytes(geom), dtype=torch.uint8, device="cuda")
+    ws = api.decode_workspace(geom)
     api.decode_attn_profiled(cache, q.cuda(), torch.full((B,), i, dtype=torch.int32, device="cuda"), out, ws,
                              head_mass=hm_dev, mass_max=mx_dev)
     torch.cuda.synchronize()
@@ -422,9 +451,9 @@ def test_profiled_ring_decode_per_head(api):
     for b in range(B):
         Kd = gs.heads(gs.dequant_rows(K[lo:i + 1, b], kv), Hkv, d)
         Vd = gs.heads(gs.dequant_rows(V[lo:i + 1, b], kv), Hkv, d)
-        o, m, hm, mx, pav = _oracle_profiled(q[b].double().numpy(), Kd, Vd, np.arange(lo, i + 1), i, window, None,
+        o, m, hm, mx, spread = _oracle_profiled(q[b].double().numpy(), Kd, Vd, np.arange(lo, i + 1), i, window, None,
                                              orc.softmax_scale(d), nb)
-        gs.close_o(out[b].float().cpu().numpy(), o, kv, pav)
+        gs.close_o(out[b].float().cpu().numpy(), o, kv, spread)
         for h in range(Hq):
             gs.close_mass(hm_dev[b, h].cpu().numpy(), hm[h], kv, f"head {h} mass")
         gs.close_mass(mx_dev[b].cpu().numpy(), mx, kv, "max over heads")
@@ -461,7 +490,7 @@ def test_compact_blocks_matches_oracle_and_preserves_attention(api, kv):
     api.compact_blocks(cache, gs.to_dev(ids), gs.to_dev(n_keep), tables=(t_att, t_traj, t_cnt))
     torch.cuda.synchronize()
     got_k, got_v = raw(cache.k), raw(cache.v)
-    ws = torch.empty(api.decode_workspace_bytes(geom), dtype=torch.uint8, device="cuda")
+    ws = api.decode_workspace(geom)
     qdt = torch.float32 if kv == "f32" else torch.bfloat16
     q = torch.from_numpy(_rows((B, Hq, d), (17, 9))).to(qdt)
     cur2 = np.array([orc.compacted_position(int(cur[b]), int(n_keep[b])) for b in range(B)], dtype=np.int32)
@@ -488,9 +517,9 @@ def test_compact_blocks_matches_oracle_and_preserves_attention(api, kv):
         alive[keep] = True
         Kd = gs.heads(gs.dequant_rows(K[b, :i + 1], kv), Hkv, d)
         Vd = gs.heads(gs.dequant_rows(V[b, :i + 1], kv), Hkv, d)
-        o_ref, m_ref, pav = gs.oracle_layer(q[b].double().numpy(), Kd, Vd, np.arange(i + 1), i, 0, alive,
+        o_ref, m_ref, spread = gs.oracle_layer(q[b].double().numpy(), Kd, Vd, np.arange(i + 1), i, 0, alive,
                                             orc.softmax_scale(d), nb)
-        gs.close_o(out[b].float().cpu().numpy(), o_ref, kv, pav)
+        gs.close_o(out[b].float().cpu().numpy(), o_ref, kv, spread)
         m_new = np.zeros(nb)
         m_new[:len(keep)] = m_ref[keep]
         gs.close_mass(mass[b].cpu().numpy(), m_new, kv, "compacted masses")

@@ -67,7 +67,7 @@ def test_random_geometry_matches_oracle(api, case):
     q = torch.from_numpy(_rows((B, Hq, d), (seed, 3))).to(qdt)
     out = torch.empty_like(q).cuda()
     mass = torch.zeros((B, geom.nb), dtype=torch.float32, device="cuda")
-    ws = torch.empty(api.decode_workspace_bytes(geom), dtype=torch.uint8, device="cuda")
+    ws = api.decode_workspace(geom)
     print(f"case {case}: cur {cur.tolist()}", flush=True)
     api.decode_attn_scored(cache, q.cuda(), gs.to_dev(cur), out, ws, mass_accum=mass, keep_mask=keep)
     torch.cuda.synchronize()
@@ -76,8 +76,8 @@ def test_random_geometry_matches_oracle(api, case):
         i = int(cur[b])
         Kd = gs.heads(gs.dequant_rows(K[b, :i + 1], kv), Hkv, d)
         Vd = gs.heads(gs.dequant_rows(V[b, :i + 1], kv), Hkv, d)
-        o_ref, m_ref, pav = gs.oracle_layer(q[b].double().numpy(), Kd, Vd, np.arange(i + 1), i, window,
+        o_ref, m_ref, spread = gs.oracle_layer(q[b].double().numpy(), Kd, Vd, np.arange(i + 1), i, window,
                                             None if alive is None else alive[b], orc.softmax_scale(d), geom.nb)
-        gs.close_o(o_gpu[b], o_ref, kv, pav)
+        gs.close_o(o_gpu[b], o_ref, kv, spread)
         gs.close_mass(m_gpu[b], m_ref, kv)
         assert abs(m_gpu[b].sum() - Hq) <= 1e-3 * max(1, Hq / 16)

@@ -165,9 +165,9 @@ def test_35b_bf16_workload(session_mod):
             for t in check:
                 i = w.context + t
                 q = _np(Q[layer][t][seq].float()).astype(np.float64)
-                o_ref, m_ref, pav = gs.oracle_layer(q, Kd[:, :i + 1], Vd[:, :i + 1], np.arange(i + 1), i, 0, None,
+                o_ref, m_ref, spread = gs.oracle_layer(q, Kd[:, :i + 1], Vd[:, :i + 1], np.arange(i + 1), i, 0, None,
                                                     scale, dec.geom.nb)
-                gs.close_o(got[t][0][layer][seq], o_ref, "bf16", pav)
+                gs.close_o(got[t][0][layer][seq], o_ref, "bf16", spread)
                 mass[t] += m_ref
         for t in check:
             gs.close_mass(got[t][1][seq], mass[t], "bf16", f"attended (10 layers), sequence {seq}, step {t}")
@@ -223,9 +223,9 @@ def test_397b_fp8_workload_sampled(session_mod):
         for t in check_steps:
             i = w.context + t
             q = _np(Q[layer][t][0].float()).astype(np.float64)
-            o_ref, m_ref, pav = gs.oracle_layer(q, Kd[:, :i + 1], Vd[:, :i + 1], np.arange(i + 1), i, 0, None,
+            o_ref, m_ref, spread = gs.oracle_layer(q, Kd[:, :i + 1], Vd[:, :i + 1], np.arange(i + 1), i, 0, None,
                                                 scale, geom.nb)
-            gs.close_o(got[t][0][layer], o_ref, "fp8", pav)
+            gs.close_o(got[t][0][layer], o_ref, "fp8", spread)
             mass[t] += m_ref
         del Kd, Vd
     for t in check_steps:
@@ -273,10 +273,10 @@ def test_128k_planted_workload(session_mod):
         Vd = gs.heads(gs.dequant_rows(_held_rows(w, seed, 0, seq, synth.T_V, i_end), "bf16"), 8, 128)
         for t in check_steps:
             i = w.context + t
-            o_ref, m_ref, pav = gs.oracle_layer(_np(Q[0][t][seq].float()).astype(np.float64), Kd[:, :i + 1],
+            o_ref, m_ref, spread = gs.oracle_layer(_np(Q[0][t][seq].float()).astype(np.float64), Kd[:, :i + 1],
                                                 Vd[:, :i + 1], np.arange(i + 1), i, 0, None, scale, dec.geom.nb)
             o_gpu, att = got[t]
-            gs.close_o(o_gpu[seq], o_ref, "bf16", pav)
+            gs.close_o(o_gpu[seq], o_ref, "bf16", spread)
             gs.close_mass(att[seq], m_ref, "bf16", f"attended, step {t}")
         del Kd, Vd
 
@@ -341,10 +341,10 @@ def test_35b_fp8_ring_window_workload(session_mod):
                 Kd = gs.dequant_rows(rows(layer, synth.T_K, seq, lo, t), "fp8")
                 Vd = gs.dequant_rows(rows(layer, synth.T_V, seq, lo, t), "fp8")
                 q = _np(qs[layer][seq].float()).astype(np.float64)
-                o_ref, m_ref, pav = gs.oracle_layer(q, gs.heads(Kd, w.n_kv_heads, w.head_dim),
+                o_ref, m_ref, spread = gs.oracle_layer(q, gs.heads(Kd, w.n_kv_heads, w.head_dim),
                                                     gs.heads(Vd, w.n_kv_heads, w.head_dim), np.arange(lo, t + 1), t,
                                                     w.window, None, scale, dec.geom.nb)
-                gs.close_o(_np(dec.out[layer][seq].float()), o_ref, "fp8", pav)
+                gs.close_o(_np(dec.out[layer][seq].float()), o_ref, "fp8", spread)
                 mass += m_ref
             gs.close_mass(att[seq], mass, "fp8", f"attended at step {t}")
 
@@ -477,7 +477,7 @@ def test_profiled_and_reattend_397b_full_size_sampled(session_mod):
                      torch.arange(n, dtype=torch.int32, device="cuda"))
     i = n - 1
     cur = torch.full((B,), i, dtype=torch.int32, device="cuda")
-    ws = torch.empty(api.decode_workspace_bytes(geom), dtype=torch.uint8, device="cuda")
+    ws = api.decode_workspace(geom)
     nb = geom.nb
     f32 = dict(dtype=torch.float32, device="cuda")
     q = synth.normal((B, Hq * d), (seed, 5), "cuda").reshape(B, Hq, d).to(torch.bfloat16).contiguous()
@@ -501,8 +501,8 @@ def test_profiled_and_reattend_397b_full_size_sampled(session_mod):
         Vd = gs.heads(gs.dequant_rows(_np(synth.prefill_rows(w, seed, 0, seq, synth.T_V, "cuda")), "fp8"), Hkv, d)
         qs = _np(q[seq].float()).astype(np.float64)
         o, m, hm, mx = orc.attend_profiled(qs, Kd, Vd, pos, i, 0, None, scale, nb)
-        _, _, pav = gs.oracle_layer(qs, Kd, Vd, pos, i, 0, None, scale, nb)
-        gs.close_o(_np(out[seq].float()), o, "fp8", pav)
+        _, _, spread = gs.oracle_layer(qs, Kd, Vd, pos, i, 0, None, scale, nb)
+        gs.close_o(_np(out[seq].float()), o, "fp8", spread)
         gs.close_mass(_np(mass[seq]), m, "fp8", f"sequence {seq} masses")
         gs.close_mass(_np(head_mass[seq]), hm, "fp8", f"sequence {seq} per-head masses")
         gs.close_mass(_np(mass_max[seq]), mx, "fp8", f"sequence {seq} max over heads")
@@ -510,8 +510,8 @@ def test_profiled_and_reattend_397b_full_size_sampled(session_mod):
         o2, m2 = orc.reattend_blocks(q2s, Kd, Vd, pos, i, ids[seq], scale, nb)
         alive = np.zeros(nb, dtype=bool)
         alive[ids[seq]] = True
-        _, _, pav2 = gs.oracle_layer(q2s, Kd, Vd, pos, i, 0, alive, scale, nb)
-        gs.close_o(_np(out2[seq].float()), o2, "fp8", pav2)
+        _, _, spread2 = gs.oracle_layer(q2s, Kd, Vd, pos, i, 0, alive, scale, nb)
+        gs.close_o(_np(out2[seq].float()), o2, "fp8", spread2)
         gs.close_mass(_np(mass2[seq]), m2, "fp8", f"sequence {seq} re-attend masses")
         assert not _np(mass2[seq])[~alive].any()
 
@@ -561,7 +561,7 @@ def test_compact_blocks_397b_full_size_sampled(session_mod):
     q = synth.normal((B, Hq * d), (seed, 8), "cuda").reshape(B, Hq, d).to(torch.bfloat16).contiguous()
     out = torch.empty_like(q)
     mass = torch.zeros((B, nb), dtype=torch.float32, device="cuda")
-    ws = torch.empty(api.decode_workspace_bytes(geom), dtype=torch.uint8, device="cuda")
+    ws = api.decode_workspace(geom)
     api.decode_attn_scored(cache, q, gs.to_dev(cur2), out, ws, mass_accum=mass)
     torch.cuda.synchronize()
     got_k, got_v = raw(cache.k), raw(cache.v)
@@ -580,9 +580,9 @@ def test_compact_blocks_397b_full_size_sampled(session_mod):
         Vd = gs.heads(gs.dequant_rows(_np(synth.prefill_rows(w, seed, 0, s, synth.T_V, "cuda")), "fp8"), Hkv, d)
         alive = np.zeros(nb, dtype=bool)
         alive[keep] = True
-        o_ref, m_ref, pav = gs.oracle_layer(_np(q[s].float()).astype(np.float64), Kd, Vd, np.arange(n), i, 0,
+        o_ref, m_ref, spread = gs.oracle_layer(_np(q[s].float()).astype(np.float64), Kd, Vd, np.arange(n), i, 0,
                                             alive, scale, nb)
-        gs.close_o(_np(out[s].float()), o_ref, "fp8", pav)
+        gs.close_o(_np(out[s].float()), o_ref, "fp8", spread)
         m_new = np.zeros(nb)
         m_new[:len(keep)] = m_ref[keep]
         gs.close_mass(_np(mass[s]), m_new, "fp8", f"sequence {s} compacted masses")
