@@ -27,6 +27,7 @@ TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8
 
 EXPORTED = (
     "kvs_cache_bytes", "kvs_encode_fp8", "kvs_append_kv", "kvs_decode_workspace_bytes",
+    "kvs_decode_workspace_init",
     "kvs_decode_attn_scored", "kvs_decode_partial", "kvs_decode_combine", "kvs_append_decode_attn",
     "kvs_append_decode_partial", "kvs_decode_attn_tap", "kvs_append_decode_attn_tap", "kvs_tap_masses",
     "kvs_decode_attn_profiled",
@@ -68,6 +69,7 @@ def _load():
         "kvs_encode_fp8": [P, I32, I64, I32, P, P, P],
         "kvs_append_kv": [G, P, P, I32, I32, P, P, P, P, P, P, P, P],
         "kvs_decode_workspace_bytes": [G, SZP],
+        "kvs_decode_workspace_init": [G, P, SZ, P],
         "kvs_decode_attn_scored": [G, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "kvs_decode_partial": [G, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "kvs_decode_combine": [G, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
@@ -182,6 +184,22 @@ def decode_workspace_bytes(geom: CacheGeom) -> int:
     _check(LIB.kvs_decode_workspace_bytes(ctypes.byref(geom.c()), ctypes.byref(n)),
            "kvs_decode_workspace_bytes")
     return n.value
+
+
+def decode_workspace_init(geom: CacheGeom, workspace: torch.Tensor, stream=None):
+    """kvs_decode_workspace_init: ready ``workspace`` for calls with ``geom``
+    (needed once after allocation and again after use with another geometry)."""
+    _device_check(workspace)
+    _check(LIB.kvs_decode_workspace_init(ctypes.byref(geom.c()), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(stream)),
+           "kvs_decode_workspace_init")
+    return workspace
+
+
+def decode_workspace(geom: CacheGeom, device="cuda", stream=None) -> torch.Tensor:
+    """A new decode workspace for ``geom``, initialised on the stream."""
+    ws = torch.empty(decode_workspace_bytes(geom), dtype=torch.uint8, device=device)
+    return decode_workspace_init(geom, ws, stream)
 
 
 def encode_fp8(src: torch.Tensor, codes: torch.Tensor | None = None, scales: torch.Tensor | None = None,

@@ -4,8 +4,6 @@
 #include <math.h>
 #include <stdint.h>
 
-#include <atomic>
-
 #include "../../include/kvs.h"
 #include "kvs_internal.h"
 
@@ -127,17 +125,6 @@ Plan make_plan(const kvs_geom* g) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? KVS_OK : KVS_EHIP; }
 
-// Per-call token for the partial kernel's completion flags (never 0, so a
-// cleared or zero-filled flag is never taken for a set one).
-uint32_t next_token() {
-  static std::atomic<uint32_t> counter{0};
-  uint32_t t;
-  do {
-    t = counter.fetch_add(1, std::memory_order_relaxed) + 1;
-  } while (t == 0);
-  return t;
-}
-
 }  // namespace
 
 extern "C" {
@@ -213,9 +200,32 @@ int kvs_decode_workspace_bytes(const kvs_geom* g, size_t* bytes) {
   return KVS_OK;
 }
 
+int kvs_decode_workspace_init(const kvs_geom* g, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_geom(g);
+  if (st) return st;
+  if (!workspace) return KVS_EINVAL;
+  if (!aligned16(workspace)) return KVS_EALIGN;
+  const Plan p = make_plan(g);
+  if (workspace_bytes < p.total) return KVS_EWS;
+  return hip_status(kvs::launch_fill_u32((uint32_t*)workspace, p.total / 4, 0u, (hipStream_t)stream));
+}
+
 }  // extern "C"
 
 namespace {
+
+// Points the decode arguments at the plan's regions of the workspace ws; the
+// completion flags go to flags, or to the plan's own region when flags is
+// NULL.
+void bind_workspace(const Plan& p, char* ws, uint32_t* flags, kvs::PartialArgs* a, kvs::CombineArgs* c) {
+  a->ws_m = (float*)(ws + p.off_m); a->ws_l = (float*)(ws + p.off_l);
+  a->ws_o = (float*)(ws + p.off_o); a->ws_e = (float*)(ws + p.off_e);
+  a->ws_bnd = (int*)(ws + p.off_bnd); a->ws_time = (float*)(ws + p.off_time);
+  a->ws_w = (float*)(ws + p.off_w);
+  a->pair_flag = flags ? flags : (uint32_t*)(ws + p.off_cnt);
+  a->rates = (const float*)(ws + p.off_rates);
+  c->lws[0] = ws;
+}
 
 // Shared argument checks and setup of the two decode phases.
 int decode_setup(const kvs_geom* g, const void* q, const void* k_cache, const void* v_cache,
@@ -237,25 +247,18 @@ int decode_setup(const kvs_geom* g, const void* q, const void* k_cache, const vo
   if (p.lds_partial > kLdsMaxBytes) return KVS_ENOTIMPL;  // partition bookkeeping beyond LDS
   if (workspace_bytes < p.total) return KVS_EWS;
   *plan = p;
-  char* ws = (char*)workspace;
   *a = kvs::PartialArgs{};
+  *c = kvs::CombineArgs{};
   a->q = q; a->k = k_cache; a->v = v_cache; a->ks = k_scale; a->vs = v_scale;
   a->pos_of_slot = pos_of_slot; a->cur_pos = cur_pos; a->keep = keep_mask;
-  a->ws_m = (float*)(ws + p.off_m); a->ws_l = (float*)(ws + p.off_l);
-  a->ws_o = (float*)(ws + p.off_o); a->ws_e = (float*)(ws + p.off_e);
-  a->ws_bnd = (int*)(ws + p.off_bnd); a->ws_time = (float*)(ws + p.off_time);
-  a->ws_w = (float*)(ws + p.off_w);
-  a->pair_flag = (uint32_t*)(ws + p.off_cnt);
-  a->token = next_token();
+  bind_workspace(p, (char*)workspace, nullptr, a, c);
   a->out = out;
-  a->rates = (const float*)(ws + p.off_rates);
   a->B = g->batch; a->Hq = g->n_q_heads; a->Hkv = g->n_kv_heads; a->G = p.G; a->C = g->capacity;
   a->NT = p.NT; a->window = g->window; a->nbmax = g->n_blocks_max;
   a->kwords = (g->n_blocks_max + 31) / 32; a->tpp = p.tpp; a->nparts = p.nparts;
   a->dyn = g->deterministic ? 0 : 1; a->tl_cap = p.tl_cap; a->adapt = p.adapt;
   a->scale_log2 = g->softmax_scale * 1.4426950408889634f;
-  *c = kvs::CombineArgs{};
-  c->lws[0] = ws; c->n_layers = 1; c->layers_per_chunk = 1;
+  c->n_layers = 1; c->layers_per_chunk = 1;
   c->off_w = p.off_w; c->off_e = p.off_e; c->off_bnd = p.off_bnd;
   c->off_time = p.off_time; c->off_rates = p.off_rates;
   c->cur_pos = cur_pos; c->n_wg = p.n_wg;

@@ -20,6 +20,24 @@ __device__ __forceinline__ float block_max256(float v, float* red) {
   return r;
 }
 
+// Word fill: each thread stores 16 bytes, the tail word by word.
+__global__ __launch_bounds__(256) void kvs_fill_u32(uint32_t* dst, size_t n_words, uint32_t value) {
+  const size_t n4 = n_words / 4;
+  const size_t stride = (size_t)gridDim.x * 256;
+  const u32x4 v = {value, value, value, value};
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) ((u32x4*)dst)[i] = v;
+  const size_t t = 4 * n4 + (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (t < n_words) dst[t] = value;
+}
+
+hipError_t launch_fill_u32(uint32_t* dst, size_t n_words, uint32_t value, hipStream_t st) {
+  if (n_words == 0) return hipSuccess;
+  const size_t n4 = (n_words + 3) / 4;
+  const int blocks = (int)(n4 < (size_t)1024 * 256 ? (n4 + 255) / 256 : 1024);
+  hipLaunchKernelGGL(kvs_fill_u32, dim3(blocks), dim3(256), 0, st, dst, n_words, value);
+  return hipGetLastError();
+}
+
 // One workgroup per row.
 __global__ __launch_bounds__(256) void kvs_encode_rows(const void* src, int src_bf16, int row_len,
                                                         uint8_t* codes, float* scales) {

@@ -47,11 +47,11 @@ struct PartialArgs {
   const void* app_k;
   const void* app_v;
   int app_bf16;
-  // Output merge in the kernel: the partition of a (sequence, KV head) that
-  // finds every partition's flag (pair_flag[B][Hkv][P]) set to this call's
-  // token merges the group's partials into out.
+  // Output merge in the kernel: every partition of a (sequence, KV head) sets
+  // its flag (pair_flag[B][Hkv][P], zero at entry) to 1 once its partial is
+  // in memory; the one that finds all flags set merges the group's partials
+  // into out and clears the flags.
   uint32_t* pair_flag;
-  uint32_t token;
   void* out;
 };
 
@@ -87,6 +87,10 @@ hipError_t launch_combine(const CombineArgs& a, bool ring, hipStream_t st);
 // The layer-parallel form (no per-head masses); its LDS must fit kCombineLdsBytes.
 size_t combine_layers_lds_bytes(int Hq, int Hkv, int P, int L, bool ring);
 hipError_t launch_combine_layers(const CombineArgs& a, bool ring, hipStream_t st);
+
+// Fills n_words 32-bit words at dst (16-byte aligned) with value, on the
+// stream (a kernel, not a memset node).
+hipError_t launch_fill_u32(uint32_t* dst, size_t n_words, uint32_t value, hipStream_t st);
 
 hipError_t launch_encode_fp8(const void* src, int src_bf16, int64_t n_rows, int row_len,
                              uint8_t* codes, float* scales, hipStream_t st);

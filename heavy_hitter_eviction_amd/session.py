@@ -49,10 +49,9 @@ class ScoredDecoder:
         self.geom = geom_of(w)
         self.n_layers = w.n_layers if layers is None else layers
         self.caches = [api.KVCache(self.geom, device) for _ in range(self.n_layers)]
-        ws = api.decode_workspace_bytes(self.geom)
-        self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
+        self.workspace = api.decode_workspace(self.geom, device)
         # tap mode: one workspace per layer, read once per step by tap_masses
-        self.workspaces = ([torch.empty(ws, dtype=torch.uint8, device=device) for _ in range(self.n_layers)]
+        self.workspaces = ([api.decode_workspace(self.geom, device) for _ in range(self.n_layers)]
                            if tap else [])
         B, nb = w.batch, self.geom.nb
         f32 = dict(dtype=torch.float32, device=device)

@@ -8,8 +8,9 @@
  * frees or synchronises: the caller owns every buffer. Unless stated
  * otherwise a pointer argument is a DEVICE pointer and must be 16-byte
  * aligned. Calls return KVS_OK (0) or a negative kvs_status; when a call
- * returns an error nothing has been launched. No global mutable state: calls
- * are re-entrant and may be made from several host threads.
+ * returns an error nothing has been launched. Calls are re-entrant and may be
+ * made from several host threads: the library keeps no process-wide mutable
+ * state, every call works on caller-owned buffers only.
  *
  * Terms. B sequences; Hq query heads and Hkv KV heads with G = Hq / Hkv
  * query heads reading each KV head (query head h reads KV head h / G); head
@@ -154,6 +155,19 @@ KVS_API int kvs_append_kv(const kvs_geom* geom, const void* k_rows, const void* 
 KVS_API int kvs_decode_workspace_bytes(const kvs_geom* geom, size_t* bytes);
 
 /*
+ * kvs_decode_workspace_init -- make a decode workspace ready: fills its first
+ * kvs_decode_workspace_bytes() bytes with zeros, on the stream, with a fill
+ * kernel (no memset node, so it may be captured in a HIP graph). The decode
+ * calls need the workspace's per-partition completion flags to be zero when
+ * they start and leave them zero when they end, so this is needed once after
+ * allocation (a zero-filled buffer is equally valid) and again before the
+ * workspace is used with another geometry (the flags then sit elsewhere).
+ * Errors: KVS_EINVAL (bad geometry or NULL), KVS_EALIGN, KVS_EWS.
+ */
+KVS_API int kvs_decode_workspace_init(const kvs_geom* geom, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+/*
  * kvs_decode_attn_scored -- one layer of the scored decode step.
  *
  * For every sequence b the current token's K/V are already in the cache
@@ -188,13 +202,16 @@ KVS_API int kvs_decode_workspace_bytes(const kvs_geom* geom, size_t* bytes);
  *   out         [B][Hq][d] q_dtype
  *   mass_accum  [B][NBmax] float or NULL
  *   workspace   device scratch of at least kvs_decode_workspace_bytes(),
- *               owned by the caller; calls that share one must not overlap.
- *               Besides per-call partials it keeps, from call to call, the
- *               streaming rate measured for each of the GPU's dispatch
- *               classes (workgroup id mod 8); in dynamic mode the next call
- *               splits each sequence's tiles over its workgroups by those
- *               rates. Any initial content is valid (unreadable rates count
- *               as equal); the rates never change a result beyond rounding.
+ *               owned by the caller and initialised for this geometry with
+ *               kvs_decode_workspace_init (or zero-filled); calls that share
+ *               one must not overlap. Its per-partition completion flags are
+ *               zero when a call starts and zero again when it ends. Besides
+ *               per-call partials it keeps, from call to call, the streaming
+ *               rate measured for each of the GPU's dispatch classes
+ *               (workgroup id mod 8); in dynamic mode the next call splits
+ *               each sequence's tiles over its workgroups by those rates
+ *               (unreadable rates count as equal); the rates never change a
+ *               result beyond rounding.
  *
  * Preconditions the library cannot check (unspecified results, never a
  * fault): the current token is readable (so no row is all-masked); a ring

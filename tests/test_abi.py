@@ -257,3 +257,16 @@ def test_snapkv_rejects_bad_arguments():
     assert sk(g, q=None) == api.KVS_EINVAL
     assert sk(g, ts=vp(0x2004)) == api.KVS_EALIGN
     assert sk(g, ws_bytes=0) == api.KVS_EWS
+
+
+def test_workspace_init_rejects_bad_arguments():
+    api = _lib()
+    g = _geom(api)
+    need = ctypes.c_size_t()
+    assert api.LIB.kvs_decode_workspace_bytes(ctypes.byref(g), ctypes.byref(need)) == 0
+    init = api.LIB.kvs_decode_workspace_init
+    assert init(ctypes.byref(g), None, need.value, None) == api.KVS_EINVAL
+    assert init(ctypes.byref(g), ctypes.c_void_p(0x7008), need.value, None) == api.KVS_EALIGN
+    assert init(ctypes.byref(g), ctypes.c_void_p(0x7000), need.value - 16, None) == api.KVS_EWS
+    bad = _geom(api, capacity=250)
+    assert init(ctypes.byref(bad), ctypes.c_void_p(0x7000), need.value, None) == api.KVS_EINVAL

@@ -50,9 +50,8 @@ def test_tap_masses_equal_per_layer_scored_calls(api, case):
     ref = [_prefill(api, geom, K, V, src_dt, start) for _ in range(L)]
     tap = [_prefill(api, geom, K, V, src_dt, start) for _ in range(L)]
     qdt = torch.float32 if kv == "f32" else torch.bfloat16
-    ws_bytes = api.decode_workspace_bytes(geom)
-    ws_ref = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-    ws_tap = [torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") for _ in range(L)]
+    ws_ref = api.decode_workspace(geom)
+    ws_tap = [api.decode_workspace(geom) for _ in range(L)]
     f32 = dict(dtype=torch.float32, device="cuda")
     mass_r, mass_t = torch.zeros((B, geom.nb), **f32), torch.zeros((B, geom.nb), **f32)
     hm_r, hm_t = torch.zeros((B, Hq, geom.nb), **f32), torch.zeros((B, Hq, geom.nb), **f32)
