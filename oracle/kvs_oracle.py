@@ -177,6 +177,21 @@ def key_visible(p: int, i: int, window: int) -> bool:
     return window == 0 or p >= i - window + 1
 
 
+def visible_mask(positions, i: int, window: int, alive=None) -> np.ndarray:
+    """``key_visible(p, i, window)`` and ``block_alive(alive, p // 16)`` for
+    every entry of ``positions`` at once (boolean array of the same shape)."""
+    if window < 0:
+        raise ValueError("invalid window")
+    p = np.asarray(positions, dtype=np.int64)
+    vis = (p >= 0) & (p <= i)
+    if window:
+        vis &= p >= i - window + 1
+    if alive is not None:
+        alive = np.asarray(alive, dtype=bool)
+        vis &= alive[np.clip(p // BLOCK_TOKENS, 0, len(alive) - 1)]
+    return vis
+
+
 def block_of(position: int) -> int:
     """Per-Head Attention as a Scoring Signal: the unit is a 16-token block."""
     return position // BLOCK_TOKENS
@@ -215,12 +230,12 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
     G = Hq // Hkv
     o = np.zeros((Hq, d))
     p = np.zeros((Hq, n))
-    for h in range(Hq):
-        g = h // G
-        s = (K[g] @ q[h]) * scale
-        e = np.exp(s - np.max(s))
-        p[h] = e / np.sum(e)
-        o[h] = p[h] @ V[g]
+    for g in range(Hkv):
+        hs = slice(g * G, (g + 1) * G)        # the query heads that read KV head g
+        s = (q[hs] @ K[g].T) * scale          # their logits, [G, n]
+        e = np.exp(s - np.max(s, axis=1, keepdims=True))
+        p[hs] = e / np.sum(e, axis=1, keepdims=True)
+        o[hs] = p[hs] @ V[g]
     return o, p
 
 
@@ -260,8 +275,7 @@ def attend_profiled(q, K_all, V_all, positions, i, window, alive, scale, n_block
     """attend_scored plus the per-head profile and its max over heads:
     ``(o, mass, head_mass [Hq, n_blocks], mass_max [n_blocks])``."""
     positions = np.asarray(positions, dtype=np.int64)
-    sel = np.array([key_visible(int(p), i, window) and block_alive(alive, block_of(int(p)))
-                    for p in positions], dtype=bool)
+    sel = visible_mask(positions, i, window, alive)
     o, p = attend(q, np.asarray(K_all)[:, sel], np.asarray(V_all)[:, sel], scale)
     hm = block_mass_per_head(p, positions[sel], n_blocks)
     return o, block_mass(p, positions[sel], n_blocks), hm, max_over_heads(hm)
@@ -275,8 +289,7 @@ def attend_scored(q, K_all, V_all, positions, i, window, alive, scale, n_blocks)
     read when it is visible (window rule) and its block is alive. Returns
     ``(o [Hq, d], mass [n_blocks])`` with the mass summed over query heads."""
     positions = np.asarray(positions, dtype=np.int64)
-    sel = np.array([key_visible(int(p), i, window) and block_alive(alive, block_of(int(p)))
-                    for p in positions], dtype=bool)
+    sel = visible_mask(positions, i, window, alive)
     o, p = attend(q, np.asarray(K_all)[:, sel], np.asarray(V_all)[:, sel], scale)
     return o, block_mass(p, positions[sel], n_blocks)
 

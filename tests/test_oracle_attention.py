@@ -67,6 +67,30 @@ def test_window_rule_golden():
         orc.key_visible(0, 0, -1)
 
 
+def test_visible_mask_follows_the_window_rule():
+    """The vectorised mask gives the page's window examples (golden file) and
+    agrees with the scalar rule, alive blocks included, on random cases."""
+    for line in open(GOLD):
+        line = line.split("#")[0].strip()
+        if not line or not line.startswith("visible"):
+            continue
+        _, i, w, rest = [s.strip() for s in line.split("|")]
+        i, w = int(i), int(w)
+        got = np.flatnonzero(orc.visible_mask(np.arange(i + 1), i, w)).tolist()
+        assert got == [int(x) for x in rest.split()], line
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        i = int(rng.integers(0, 300))
+        w = int(rng.choice([0, 1, 4, int(rng.integers(1, 300))]))
+        pos = rng.integers(-3, 320, 64)
+        alive = rng.random(21) < 0.6 if rng.random() < 0.5 else None
+        want = [orc.key_visible(int(p), i, w) and (int(p) < 0 or orc.block_alive(alive, orc.block_of(int(p))))
+                for p in pos]
+        assert orc.visible_mask(pos, i, w, alive).tolist() == want
+    with pytest.raises(ValueError):
+        orc.visible_mask(np.arange(3), 2, -1)
+
+
 def test_window_one_returns_current_value():
     rng = np.random.default_rng(19)
     n, i = 40, 33
