@@ -103,25 +103,22 @@ def e4m3_encode(y: np.ndarray) -> np.ndarray:
     +-448 (the pages clip before quantising). The sign is kept, so -0 gives
     0x80. Inputs must be finite.
 
-    Step by step: clip |y| to 448; find its binade ``2**e`` (at least 2**-6,
-    the subnormal binade shares the quantum of the lowest normal binade); the
-    grid there has spacing ``2**(e-3)``; ``n = round_half_even(|y| / spacing)``
-    is in [0, 16]; the code is ``(e + 7) * 8 + n - 8``, which also covers the
-    subnormals (e = -6, n < 8 gives code n) and the carry into the next binade
-    (n = 16)."""
+    Step by step: clip |y| to 448; the non-negative finite values of the
+    format (codes 0x00 .. 0x7E, ascending) and the midpoints between
+    neighbours are taken from the format definition (``e4m3_table``); the
+    number of midpoints strictly below |y| is the code of the nearest value,
+    unless |y| sits exactly on a midpoint, where the tie goes to the even one
+    of the two codes; the sign bit is then set for negative inputs."""
     y = np.asarray(y, dtype=np.float64)
     if not np.all(np.isfinite(y)):
         raise ValueError("E4M3 encode: non-finite input is outside the contract")
     sign = np.signbit(y)
     a = np.minimum(np.abs(y), E4M3_MAX)
-    _, ex = np.frexp(a)                      # a = f * 2**ex, f in [0.5, 1)
-    e = np.maximum(ex.astype(np.int64) - 1, 1 - E4M3_BIAS)
-    spacing = np.ldexp(1.0, (e - 3).astype(np.int64))
-    n = np.rint(a / spacing)                 # exact division by a power of 2
-    code = (e + E4M3_BIAS) * 8 + n.astype(np.int64) - 8
-    code = np.where(a == 0.0, 0, code)
-    code = code | (sign.astype(np.int64) << 7)
-    return code.astype(np.uint8)
+    values = e4m3_table()[:0x7F]                              # 0, subnormals, normals .. 448
+    mids = np.append((values[:-1] + values[1:]) / 2, np.inf)  # exact in float64
+    code = np.searchsorted(mids, a, side="left")               # midpoints strictly below |y|
+    code = code + ((a == mids[code]) & (code % 2 == 1))        # a tie goes to the even code
+    return (code | (sign.astype(np.int64) << 7)).astype(np.uint8)
 
 
 def fp8_encode_rows(x: np.ndarray):
