@@ -135,13 +135,17 @@ def fp8_encode_rows(x: np.ndarray):
     x2 = np.atleast_2d(x)
     if not np.all(np.isfinite(x2)):
         raise ValueError("FP8 encode: non-finite input is outside the contract")
-    absmax = np.max(np.abs(x2.astype(np.float64)), axis=1)
-    scales = (absmax / FP8_SCALE_DIVISOR).astype(np.float32)
     codes = np.zeros(x2.shape, dtype=np.uint8)
-    nz = scales > 0
-    if np.any(nz):
-        y = (x2[nz].astype(np.float64) / scales[nz, None].astype(np.float64)).astype(np.float32)
-        codes[nz] = e4m3_encode(y.astype(np.float64))
+    scales = np.zeros(x2.shape[0], dtype=np.float32)
+    for r0 in range(0, x2.shape[0], 64):       # every row on its own; 64 at a time
+        xr = x2[r0:r0 + 64].astype(np.float64)
+        absmax = np.max(np.abs(xr), axis=1)
+        s = (absmax / FP8_SCALE_DIVISOR).astype(np.float32)
+        scales[r0:r0 + 64] = s
+        nz = s > 0
+        if np.any(nz):
+            y = (xr[nz] / s[nz, None].astype(np.float64)).astype(np.float32)
+            codes[r0:r0 + 64][nz] = e4m3_encode(y.astype(np.float64))
     return codes.reshape(x.shape), scales
 
 
