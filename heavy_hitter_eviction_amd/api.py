@@ -20,7 +20,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvs.so")
 
-KVS_OK, KVS_EINVAL, KVS_EDTYPE, KVS_EALIGN, KVS_EWS, KVS_EHIP, KVS_ENOTIMPL = 0, -1, -2, -3, -4, -5, -6
+KVS_OK, KVS_EINVAL, KVS_EDTYPE, KVS_EALIGN, KVS_EWS, KVS_EHIP, KVS_ENOTIMPL, KVS_ESCRATCH = 0, -1, -2, -3, -4, -5, -6, -7
+NOALLOC_SCRATCH_BYTES = 16 << 20
 KVS_F32, KVS_BF16, KVS_FP8_E4M3 = 0, 1, 2
 DTYPE_CODES = {"f32": KVS_F32, "bf16": KVS_BF16, "fp8": KVS_FP8_E4M3}
 TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
@@ -28,7 +29,7 @@ TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8
 EXPORTED = (
     "kvs_cache_bytes", "kvs_encode_fp8", "kvs_append_kv", "kvs_decode_workspace_bytes",
     "kvs_decode_workspace_init",
-    "kvs_decode_attn_scored", "kvs_decode_partial", "kvs_decode_combine", "kvs_append_decode_attn",
+    "kvs_decode_attn_scored", "kvs_decode_attn_scored_noalloc", "kvs_decode_partial", "kvs_decode_combine", "kvs_append_decode_attn",
     "kvs_append_decode_partial", "kvs_decode_attn_tap", "kvs_append_decode_attn_tap", "kvs_tap_masses",
     "kvs_decode_attn_profiled",
     "kvs_reattend_blocks",
@@ -71,6 +72,7 @@ def _load():
         "kvs_decode_workspace_bytes": [G, SZP],
         "kvs_decode_workspace_init": [G, P, SZ, P],
         "kvs_decode_attn_scored": [G, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "kvs_decode_attn_scored_noalloc": [G, P, P, P, P, P, P, P, P, P, P, P],
         "kvs_decode_partial": [G, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "kvs_decode_combine": [G, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "kvs_append_decode_attn": [G, P, P, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
@@ -281,6 +283,34 @@ def decode_attn_scored(cache: KVCache, q: torch.Tensor, cur_pos: torch.Tensor, o
               _ptr(cache.v_scale), _ptr(cache.pos_of_slot), _ptr(cur_pos), _ptr(keep_mask), _ptr(out),
               _ptr(mass_accum), _ptr(workspace), ws_bytes, _stream(stream)),
            f"kvs_decode ({phase})")
+    return out
+
+
+def decode_attn_scored_noalloc(cache: KVCache, q: torch.Tensor, cur_pos: torch.Tensor, out: torch.Tensor,
+                               mass_accum: torch.Tensor | None = None, keep_mask: torch.Tensor | None = None,
+                               stream=None):
+    """kvs_decode_attn_scored_noalloc: decode_attn_scored with the library's
+    static per-GPU scratch as workspace (no allocation; overlapping calls on
+    one GPU race)."""
+    g = cache.geom
+    _device_check(q, cur_pos, out, mass_accum, keep_mask)
+    qdt = TORCH_DTYPES[g.q_dtype]
+    if q.dtype != qdt or out.dtype != qdt:
+        raise TypeError("q and out must have the geometry's q dtype")
+    if q.shape != (g.batch, g.n_q_heads, g.head_dim) or out.shape != q.shape:
+        raise ValueError("q/out must be [B, Hq, d]")
+    if cur_pos.dtype != torch.int32 or cur_pos.numel() != g.batch:
+        raise ValueError("cur_pos must be int32 [B]")
+    if mass_accum is not None and (mass_accum.dtype != torch.float32 or mass_accum.numel() != g.batch * g.nb):
+        raise ValueError("mass_accum must be float32 [B, NBmax]")
+    if keep_mask is not None and (keep_mask.dtype != torch.int32 or keep_mask.numel() != g.batch * g.words):
+        raise ValueError("keep_mask must be int32 (bit words) [B, W]")
+    gc = g.c()
+    _check(LIB.kvs_decode_attn_scored_noalloc(ctypes.byref(gc), _ptr(q), _ptr(cache.k), _ptr(cache.v),
+                                              _ptr(cache.k_scale), _ptr(cache.v_scale), _ptr(cache.pos_of_slot),
+                                              _ptr(cur_pos), _ptr(keep_mask), _ptr(out), _ptr(mass_accum),
+                                              _stream(stream)),
+           "kvs_decode_attn_scored_noalloc")
     return out
 
 

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/kvs.h"
 #include "kvs_internal.h"
 
@@ -140,6 +142,7 @@ const char* kvs_status_str(int s) {
     case KVS_EWS: return "workspace too small";
     case KVS_EHIP: return "HIP launch failure";
     case KVS_ENOTIMPL: return "not implemented for this combination";
+    case KVS_ESCRATCH: return "geometry needs more than the static scratch maximum (KVS_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -633,6 +636,79 @@ int kvs_update_sidecar_select(float* mass_accum, float* attended, float* ema, fl
   a.mass = mass_accum; a.att = attended; a.ema = ema; a.cum = cum; a.traj = traj;
   a.traj_cap = traj_cap; a.slot = (int)(step % traj_cap); a.alpha = alpha; a.score_src = score_source;
   return hip_status(kvs::launch_select(a, (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// kvs_decode_attn_scored_noalloc: the decode workspace in a static device
+// array instead of a caller buffer.
+// ---------------------------------------------------------------------------
+namespace {
+
+// The array's first part holds the completion flags, at the same place for
+// every geometry: each call leaves the flags it used at zero (its merging
+// workgroups clear them), so they are zero at the start of every call,
+// whatever geometry the previous call had. The rest holds one call's
+// workspace regions (partials, block records, boundaries, merge weights,
+// clock records and the per-class rates, which are sanitised on read).
+constexpr size_t kNoallocFlagBytes = 64 * 1024;  // 16384 flags: B * Hkv * partitions
+constexpr size_t kNoallocWsBytes = (size_t)KVS_NOALLOC_SCRATCH_BYTES - kNoallocFlagBytes;
+constexpr int kMaxDevices = 64;
+
+// One copy per GPU, zero when the code object is loaded; held until the
+// process ends. Host code never uses its name as an address: the device
+// address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) __attribute__((used)) unsigned char scratch[KVS_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+char* g_scratch[kMaxDevices];  // device address of scratch, per device (nullptr: not set up)
+
+// The current device's scratch address. At its first use on a device (that
+// device current) the address is looked up and the flag region is cleared
+// once more on the caller's stream (a fill kernel, no memset node).
+int scratch_of_current_device(hipStream_t s, char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KVS_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return KVS_EHIP;
+    if (kvs::launch_fill_u32((uint32_t*)ptr, kNoallocFlagBytes / 4, 0u, s) != hipSuccess) return KVS_EHIP;
+    g_scratch[dev] = (char*)ptr;
+  }
+  *out = g_scratch[dev];
+  return KVS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvs_decode_attn_scored_noalloc(const kvs_geom* g, const void* q, const void* k_cache, const void* v_cache,
+                                   const float* k_scale, const float* v_scale, const int32_t* pos_of_slot,
+                                   const int32_t* cur_pos, const uint32_t* keep_mask, void* out,
+                                   float* mass_accum, void* stream) {
+  Plan p;
+  kvs::PartialArgs a;
+  kvs::CombineArgs c;
+  int kv;
+  // every argument check first, against a stand-in workspace address of the
+  // largest size (nothing is launched or dereferenced before the rebinding)
+  void* const stand_in = (void*)(uintptr_t)256;
+  int st = decode_setup(g, q, k_cache, v_cache, k_scale, v_scale, pos_of_slot, cur_pos, keep_mask, out,
+                        mass_accum, stand_in, kNoallocWsBytes, &p, &a, &c, &kv);
+  if (st == KVS_EWS) return KVS_ESCRATCH;
+  if (st) return st;
+  if ((size_t)g->batch * g->n_kv_heads * p.nparts * 4 > kNoallocFlagBytes) return KVS_ESCRATCH;
+  hipStream_t s = (hipStream_t)stream;
+  char* base = nullptr;
+  st = scratch_of_current_device(s, &base);
+  if (st) return st;
+  bind_workspace(p, base + kNoallocFlagBytes, (uint32_t*)base, &a, &c);
+  hipError_t e = kvs::launch_partial(kv, g->head_dim, a, mass_accum != nullptr, g->ring != 0, p.lds_partial, s);
+  if (e != hipSuccess) return KVS_EHIP;
+  return hip_status(kvs::launch_combine(c, g->ring != 0, s));
 }
 
 }  // extern "C"

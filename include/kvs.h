@@ -9,8 +9,10 @@
  * otherwise a pointer argument is a DEVICE pointer and must be 16-byte
  * aligned. Calls return KVS_OK (0) or a negative kvs_status; when a call
  * returns an error nothing has been launched. Calls are re-entrant and may be
- * made from several host threads: the library keeps no process-wide mutable
- * state, every call works on caller-owned buffers only.
+ * made from several host threads. The only process-wide state is that of
+ * kvs_decode_attn_scored_noalloc: a static device scratch array per GPU and
+ * the host table of its per-device addresses (guarded by a mutex); every
+ * other call works on caller-owned buffers only.
  *
  * Terms. B sequences; Hq query heads and Hkv KV heads with G = Hq / Hkv
  * query heads reading each KV head (query head h reads KV head h / G); head
@@ -40,7 +42,8 @@ typedef enum {
   KVS_EALIGN = -3,   /* a pointer is not 16-byte aligned                       */
   KVS_EWS = -4,      /* workspace smaller than kvs_decode_workspace_bytes      */
   KVS_EHIP = -5,     /* the HIP runtime refused a launch                       */
-  KVS_ENOTIMPL = -6  /* a combination this build does not provide              */
+  KVS_ENOTIMPL = -6, /* a combination this build does not provide              */
+  KVS_ESCRATCH = -7  /* geometry needs more than KVS_NOALLOC_SCRATCH_BYTES     */
 } kvs_status;
 
 typedef enum {
@@ -222,6 +225,35 @@ KVS_API int kvs_decode_attn_scored(const kvs_geom* geom, const void* q, const vo
                            const int32_t* pos_of_slot, const int32_t* cur_pos,
                            const uint32_t* keep_mask, void* out, float* mass_accum,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kvs_decode_attn_scored_noalloc -- kvs_decode_attn_scored without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc). The
+ * call allocates nothing: its workspace is a static device array of
+ * KVS_NOALLOC_SCRATCH_BYTES in the library, one per GPU, held until the
+ * process ends. Results are those of kvs_decode_attn_scored (bit for bit with
+ * geom.deterministic = 1). The caller still passes inputs and outputs, as
+ * there; the stream must belong to the current device.
+ *
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (on different streams, or from several host threads without ordering) race
+ * and give unspecified results. Each call leaves the array's completion flags
+ * zero, so consecutive calls of any geometries need nothing in between. The
+ * first call on each device looks up the array's address (with that device
+ * current) and clears its flag region on the call's stream.
+ *
+ * Errors: as kvs_decode_attn_scored; KVS_ESCRATCH when the geometry's
+ * workspace (kvs_decode_workspace_bytes) does not fit the array beside its
+ * 64 KiB flag region, or needs more than 16384 completion flags
+ * (B * Hkv * partitions); KVS_EHIP when the array's address cannot be found.
+ */
+#define KVS_NOALLOC_SCRATCH_BYTES (16u << 20)
+KVS_API int kvs_decode_attn_scored_noalloc(const kvs_geom* geom, const void* q, const void* k_cache,
+                                           const void* v_cache, const float* k_scale, const float* v_scale,
+                                           const int32_t* pos_of_slot, const int32_t* cur_pos,
+                                           const uint32_t* keep_mask, void* out, float* mass_accum,
+                                           void* stream);
 
 /*
  * kvs_decode_attn_tap, kvs_append_decode_attn_tap, kvs_tap_masses -- the

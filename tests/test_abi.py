@@ -270,3 +270,22 @@ def test_workspace_init_rejects_bad_arguments():
     assert init(ctypes.byref(g), ctypes.c_void_p(0x7000), need.value - 16, None) == api.KVS_EWS
     bad = _geom(api, capacity=250)
     assert init(ctypes.byref(bad), ctypes.c_void_p(0x7000), need.value, None) == api.KVS_EINVAL
+
+
+def test_noalloc_rejects_geometries_beyond_its_scratch_before_any_launch():
+    """kvs_decode_attn_scored_noalloc checks every argument, and that the
+    geometry's workspace fits its static scratch, before touching the GPU."""
+    api = _lib()
+    P = ctypes.c_void_p
+    big = _geom(api, batch=64, n_q_heads=32, n_kv_heads=8, capacity=131072, n_blocks_max=8192,
+                kv_dtype=api.KVS_FP8_E4M3)
+    need = ctypes.c_size_t()
+    assert api.LIB.kvs_decode_workspace_bytes(ctypes.byref(big), ctypes.byref(need)) == 0
+    assert need.value > api.NOALLOC_SCRATCH_BYTES
+    fn = api.LIB.kvs_decode_attn_scored_noalloc
+    args = [P(0x1000), P(0x2000), P(0x3000), P(0x8000), P(0x9000), None, P(0x4000), None, P(0x5000), P(0x6000), None]
+    assert fn(ctypes.byref(big), *args) == api.KVS_ESCRATCH
+    assert api.status_str(api.KVS_ESCRATCH).startswith("geometry needs more than the static scratch")
+    small = _geom(api, kv_dtype=api.KVS_FP8_E4M3)
+    assert fn(ctypes.byref(small), *args[:2], None, *args[3:]) == api.KVS_EINVAL     # no V cache
+    assert fn(ctypes.byref(small), P(0x1008), *args[1:]) == api.KVS_EALIGN
