@@ -421,8 +421,8 @@ def run_compact(args, w):
 
 
 def run_snapkv(args, w):
-    """SnapKV-style prefill scoring (Context views at marginal cost, section 3,
-    Fact 1) after the prefill: per layer, the last 32 prompt positions' queries
+    """SnapKV-style prefill scoring (Context views at marginal cost, section 7,
+    SOTA grounding, per-system reductions) after the prefill: per layer, the last 32 prompt positions' queries
     score every prompt token per head, max-pooled with kernel 7 into block
     scores. Two passes over K."""
     import torch

@@ -1,6 +1,6 @@
 // Block compaction of a linear cache (Context Optimization, "H2O KV Cache
 // Eviction / How It Works in Flash-MoE", step 4: surviving entries move to
-// contiguous positions so later kernels see a shorter, contiguous sequence),
+// contiguous positions, and later passes read one shorter run of positions),
 // here at 16-slot block granularity: kept block ids[k] becomes block k.
 //
 // In place. Ids outside the cache move nothing. With ids ascending, the destination k of a move can only coincide

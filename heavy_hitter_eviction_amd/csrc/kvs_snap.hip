@@ -1,9 +1,10 @@
-// SnapKV-style prefill scoring (Context views at marginal cost, section 3,
-// Fact 1: one-shot at the end of prefill, the attention of the last N prompt
-// queries -- the observation window -- is pooled into one score per prompt
-// token per head, then max-pooled with kernel 7 so that a kept key drags its
-// neighbours), placed per 16-token block (Per-Head Attention as a Scoring
-// Signal: score per head, place per block).
+// SnapKV-style prefill scoring (Context views at marginal cost, section 7,
+// SOTA grounding, per-system reductions: once, when the prompt is done, the
+// weights the last N prompt queries -- the observation window -- give each
+// prompt token are added up per head, and that per-token score is replaced by
+// its maximum over a 7-token neighbourhood, so the neighbours of a
+// high-scoring key score high too), placed per 16-token block (Per-Head
+// Attention as a Scoring Signal, "Fix: score per head, place per block").
 //
 // Column n of a (KV head, sequence) is (window query w, head h of the group),
 // n = w*G + h; query w sits at position n_prompt - W + w and reads keys at or

@@ -1,7 +1,9 @@
 // Side-car views over the per-block table (Context views at marginal cost,
-// section 3, "Pure side-car vs. materialized": views are filters of the score
-// table, and the threshold is both a query predicate and a storage GC policy;
-// section 3 Fact 1: Scissorhands keeps how often a token exceeds a threshold).
+// section 3, "Pure side-car vs. materialized": a view filters the score table,
+// and one threshold serves both to answer queries and to decide which
+// fine-grained history is worth storing; section 7, SOTA grounding,
+// per-system reductions: Scissorhands counts the turns a token's attention
+// passes a threshold).
 //
 // kvs_counters: per block, the Scissorhands count of turns whose Attended
 // exceeded hot_theta, and the number of consecutive turns the EMA has stayed
@@ -9,7 +11,7 @@
 // is cleared (its fine-grained history dropped, Cumulative kept).
 //
 // kvs_filter: per sequence, the ascending ids of the existing, alive blocks
-// whose score exceeds theta -- the span refs a threshold view returns.
+// whose score exceeds theta -- the set of spans a threshold view answers with.
 
 #include "kvs_device.h"
 #include "kvs_internal.h"

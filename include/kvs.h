@@ -120,8 +120,9 @@ KVS_API int kvs_cache_bytes(const kvs_geom* geom, size_t* kv_bytes, size_t* scal
 
 /*
  * kvs_encode_fp8 -- per-row FP8 E4M3 encoding (Context Optimization,
- * "FP8 KV Cache / How It Works": per position, scale = absmax / 240, values
- * clipped to +-448 and quantised to 8 bits, scale stored separately).
+ * "FP8 KV Cache / How It Works": per position, scale = absmax / 240, each
+ * value divided by it, clipped to +-448 and rounded to an 8-bit code, the
+ * scale kept apart from the codes).
  *
  * For each row r of ``src`` ([n_rows][row_len], KVS_F32 or KVS_BF16, bf16
  * widened exactly): a = max |x|; s = a / 240 rounded once to float32;
@@ -174,7 +175,7 @@ KVS_API int kvs_decode_workspace_init(const kvs_geom* geom, void* workspace, siz
  * kvs_decode_attn_scored -- one layer of the scored decode step.
  *
  * For every sequence b the current token's K/V are already in the cache
- * (write, then attend: the window includes the current token) and
+ * (write, then attend: a position is inside its own window) and
  * i = cur_pos[b] is its absolute position. Key slot t is read when its
  * absolute position p (t if linear, pos_of_slot[b][t] if ring) satisfies
  * p >= 0, p <= i, p >= i - w + 1 when window w > 0, and, when keep_mask is
@@ -355,9 +356,9 @@ KVS_API int kvs_append_decode_partial(const kvs_geom* geom, const void* k_new, c
  * kvs_decode_attn_profiled -- kvs_decode_attn_scored with the per-axis views
  * of the block masses (Context views at marginal cost, section 4: the
  * observer's layer and head axes kept as a reduced per-span profile, not the
- * matrix; section 5, "within layer L" / "within head H"; Per-Head Attention as
- * a Scoring Signal, "Fix: score per head, place per block": a block stays
- * resident if any head still weights it).
+ * matrix; the per-layer and per-head rows of its views table; Per-Head
+ * Attention as a Scoring Signal, "Fix: score per head, place per block": a
+ * block is kept while at least one head gives it weight).
  *
  * Same arguments and checks as kvs_decode_attn_scored, plus two optional
  * outputs (NULL skips each; all three mass outputs may be NULL):
@@ -379,10 +380,10 @@ KVS_API int kvs_decode_attn_profiled(const kvs_geom* geom, const void* q, const 
 /*
  * kvs_reattend_blocks -- one layer of attention for a new query over a chosen
  * set of cached blocks only (Context views at marginal cost, "Tier 2 —
- * RE-ATTEND" and "Fact 3": a relevance question about stored spans is asked by
- * running the new query against the cached keys of the candidate spans and
- * reading the resulting distribution; the keys and values are reused, and the
- * read costs O(selected tokens)).
+ * RE-ATTEND" and "Fact 3": to ask how relevant stored spans are to a new
+ * query, that query attends over the cached keys of those spans only and the
+ * distribution it produces is read; cached keys and values are reused as
+ * they are, and the cost grows with the number of selected tokens).
  *
  * Exactly kvs_decode_attn_scored on a linear cache (ring == 0, window == 0,
  * else KVS_EINVAL) with the keep mask replaced by a list: key slot t is read
@@ -423,12 +424,13 @@ KVS_API int kvs_update_sidecar(float* mass_accum, float* attended, float* ema, f
 
 /*
  * kvs_snapkv_scores -- prefill scoring from an observation window (Context
- * views at marginal cost, section 3, Fact 1, SnapKV: one-shot at the end of
- * prefill, the attention of the last W prompt queries is pooled into one
- * score per prompt token per head, then max-pooled with an odd kernel --
- * 7 on the page -- so a kept key drags its neighbours), placed per 16-token
- * block (Per-Head Attention as a Scoring Signal: score per head, place per
- * block).
+ * views at marginal cost, section 7, SOTA grounding, per-system reductions,
+ * SnapKV: once, when the prompt is done, the weights the last W prompt
+ * queries give each prompt token are added up per head, and each token's
+ * score becomes the maximum over an odd neighbourhood -- 7 tokens on the page
+ * -- so the neighbours of a high-scoring key score high too), placed per
+ * 16-token block (Per-Head Attention as a Scoring Signal, "Fix: score per
+ * head, place per block").
  *
  * For sequence b with n = n_prompt[b] prompt tokens in a linear cache and
  * window query w (0 <= w < W) of head h at position n - W + w, reading keys
@@ -468,7 +470,7 @@ typedef struct {
  * kvs_compact_blocks -- move the kept blocks of a linear cache to the front,
  * in order (Context Optimization, "H2O KV Cache Eviction / How It Works in
  * Flash-MoE", step 4: survivors are moved to contiguous positions so later
- * kernels see a shorter, contiguous sequence), at 16-slot block granularity
+ * passes read one shorter run of positions), at 16-slot block granularity
  * (Per-Head Attention as a Scoring Signal: the block is the unit kept).
  *
  * For each sequence b and k < n_keep[b] (clamped to ids_stride and C/16),
@@ -496,11 +498,12 @@ KVS_API int kvs_compact_blocks(const kvs_geom* geom, void* k_cache, void* v_cach
 
 /*
  * kvs_update_counters -- side-car counters for threshold views, once per turn
- * after kvs_update_sidecar (Context views at marginal cost, section 3: views
- * are filters of the score table and the threshold doubles as a storage GC
- * policy; a span whose EMA stays below the threshold for K turns drops its
- * fine-grained trajectory and keeps its cumulative scalar. Section 3, Fact 1:
- * Scissorhands keeps how often a token exceeds a threshold). Per block x of
+ * after kvs_update_sidecar (Context views at marginal cost, section 3: a view
+ * filters the score table, and the same threshold decides which history is
+ * kept: a span whose EMA has been under it for K turns loses its per-turn
+ * trajectory and keeps only its Cumulative value; section 7, SOTA grounding,
+ * per-system reductions: Scissorhands counts the turns a token's attention
+ * passes a threshold). Per block x of
  * every sequence (all n_blocks_max entries):
  *   hot_count[x]  += (attended[x] > hot_theta)                (NULL: skipped)
  *   cold_turns[x]  = ema[x] < cold_theta ? cold_turns[x] + 1 : 0  (NULL: skipped)
@@ -520,8 +523,9 @@ KVS_API int kvs_update_counters(const float* attended, const float* ema, int32_t
 
 /*
  * kvs_filter_blocks -- a threshold view (Context views at marginal cost,
- * section 3: "filter(a_s > θ)", computed lazily at query time; the result is a
- * set of span refs). For each sequence b with i = cur_pos[b], the ascending
+ * section 3: the spans whose score is above a threshold, worked out when the
+ * query comes, returned as a set of spans). For each sequence b with
+ * i = cur_pos[b], the ascending
  * ids of the existing blocks (0 .. i/16, below NBmax) that are alive (bit set
  * in alive[b], or every block when alive is NULL) and whose score exceeds
  * theta. n_ids[b] is the number of such blocks; ids[b] holds the first

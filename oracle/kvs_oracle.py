@@ -11,8 +11,8 @@ in the order the source pages state them:
 
 * Context Optimization (Flash-MoE docs), "FP8 KV Cache / How It Works":
   E4M3 with 1 sign, 4 exponent and 3 mantissa bits, bias 7, range +-448; a
-  per-position scale ``absmax / 240``; values clipped and quantised to 8 bits;
-  the scale is kept next to the codes.
+  per-position scale ``absmax / 240``; every value divided by it, clipped and
+  rounded to an 8-bit code; the scale stored beside the codes.
 * Context Optimization, "Sliding Window Attention / Design": the write slot of
   a circular cache is ``position mod capacity``.
 * LLM mechanics III (four-slot cache), sections 1, 3 and 5: position ``i``
@@ -20,23 +20,27 @@ in the order the source pages state them:
   absolute position, never by slot; processed count, absolute positions and
   slots are three separate indices.
 * Context views at marginal cost, section 2 (Tier 0 and Tier 1): the
-  post-softmax weights are reduced per span with one add per (row, span); the
-  side-car keeps Attended (this turn), EMA, Cumulative and a 64-turn trajectory
-  ring, O(1) per span per turn.
+  post-softmax weights are summed per span as the pass makes them, a single
+  addition for each weight; the side-car keeps Attended (this turn), EMA,
+  Cumulative and a 64-turn trajectory ring, a constant amount of work per span
+  and turn.
 * Per-Head Attention as a Scoring Signal, "Scoring granularity, not eviction
   granularity": the unit that is scored and kept is a (sequence, 16-token
   block); heads are only a scoring input. "Fix: score per head, place per
-  block": a block stays resident if any head still weights it (the max over
-  heads of the per-head masses).
+  block": a block is kept while at least one head gives it weight (the max
+  over heads of the per-head masses).
 * Context views at marginal cost, section 4: the observer's layer and head
   axes may be kept as a reduced per-span profile instead of being summed.
 * Context views at marginal cost, "Tier 2 — RE-ATTEND" and "Fact 3": a new
   query is run against the cached keys of a chosen subset of spans, and the
   resulting distribution is read; cached keys and values are reused as they
   are.
-* Context views at marginal cost, section 3, Fact 1: SnapKV pools the
-  attention of the last N prompt queries into one score per prompt token per
-  head, then max-pools it with kernel 7.
+* Context views at marginal cost, section 7, SOTA grounding, per-system
+  reductions: SnapKV adds up, per head, the weights the last N prompt queries
+  give each prompt token, then replaces each token's score by the maximum
+  over its 7-token neighbourhood; Scissorhands counts the turns a token's
+  attention passes a threshold; TOVA evicts the block the latest query
+  weights least.
 * Context Optimization, "H2O KV Cache Eviction": post-softmax scores are summed
   over all query heads (GQA-aware) and over steps; sinks and recent tokens are
   kept unconditionally and the top scorers among the rest survive.
@@ -62,9 +66,9 @@ import math
 
 import numpy as np
 
-# Per-Head Attention as a Scoring Signal: "(sequence, token block) of 16 tokens".
+# Per-Head Attention as a Scoring Signal: the placed unit is a 16-token block of one sequence.
 BLOCK_TOKENS = 16
-# Context views at marginal cost, section 2 Tier 1: "trajCap = 64 turns".
+# Context views at marginal cost, section 2 Tier 1: the trajectory ring holds 64 turns.
 TRAJ_CAP = 64
 # Context Optimization, FP8 KV Cache: bias 7, range [-448, 448], scale absmax/240.
 E4M3_BIAS = 7
@@ -77,8 +81,8 @@ FP8_SCALE_DIVISOR = 240.0
 # ---------------------------------------------------------------------------
 
 def e4m3_to_float(code: int) -> float:
-    """Value of one E4M3 byte from the format definition: 1 sign bit, 4
-    exponent bits with bias 7, 3 mantissa bits. Exponent field 0 holds the
+    """Value of one E4M3 byte from the format definition: the top bit is the
+    sign, the next four the exponent (bias 7), the low three the mantissa. Exponent field 0 holds the
     subnormals ``(m/8) * 2**(1-7)``; otherwise ``(1 + m/8) * 2**(e-7)``. The
     pair exponent 15 / mantissa 7 is NaN (the range stops at 448, so there is no
     infinity)."""
@@ -242,7 +246,7 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
 
 def block_mass(p: np.ndarray, positions: np.ndarray, n_blocks: int) -> np.ndarray:
     """Tier 0 reduction: for every block ``b``, the sum over heads and over the
-    block's visible keys of the post-softmax weight (one add per row and span).
+    block's visible keys of the post-softmax weight.
     ``positions`` are the absolute positions of the columns of ``p``."""
     p = np.asarray(p, dtype=np.float64)
     blocks = np.asarray(positions, dtype=np.int64) // BLOCK_TOKENS
@@ -266,8 +270,8 @@ def block_mass_per_head(p: np.ndarray, positions: np.ndarray, n_blocks: int) -> 
 
 
 def max_over_heads(head_mass: np.ndarray) -> np.ndarray:
-    """Per-Head Attention as a Scoring Signal, "score per head, place per
-    block": a block stays resident if any head still weights it, so the
+    """Per-Head Attention as a Scoring Signal, "Fix: score per head, place per
+    block": a block is kept while at least one head gives it weight, so the
     block's score is the largest of its per-head masses."""
     return np.max(np.asarray(head_mass, dtype=np.float64), axis=0)
 
@@ -393,8 +397,9 @@ class SideCar:
 # ---------------------------------------------------------------------------
 
 def hot_count_update(count: np.ndarray, attended: np.ndarray, theta: float) -> np.ndarray:
-    """Scissorhands (section 3, Fact 1): per span, the number of turns whose
-    attention exceeded the threshold; one increment per turn above it."""
+    """Scissorhands (section 7, SOTA grounding, per-system reductions): per
+    span, the number of turns whose attention exceeded the threshold; one
+    increment per turn above it."""
     return np.asarray(count) + (np.asarray(attended) > theta).astype(np.asarray(count).dtype)
 
 
@@ -488,14 +493,14 @@ def keep_mask_after(keep_ids, i, n_blocks):
 # ---------------------------------------------------------------------------
 
 # ---------------------------------------------------------------------------
-# SnapKV-style prefill scoring (Context views at marginal cost, section 3,
-# Fact 1)
+# SnapKV-style prefill scoring (Context views at marginal cost, section 7,
+# SOTA grounding, per-system reductions)
 # ---------------------------------------------------------------------------
 
 def snapkv_token_scores(q_window: np.ndarray, K: np.ndarray, n_prompt: int, scale: float) -> np.ndarray:
-    """One-shot at the end of prefill: the attention of the last W prompt
-    queries (the observation window) pooled into one score per prompt token
-    per head, ``score[h][j] = sum_w p_{w,h,j}``. ``q_window`` is
+    """Once, when the prompt is done: each prompt token's score for head h is
+    the sum of the weights the last W prompt queries (the observation window)
+    give it, ``score[h][j] = sum_w p_{w,h,j}``. ``q_window`` is
     ``[W, Hq, d]``, query w at position ``n_prompt - W + w`` reading keys at or
     before it; ``K`` is ``[Hkv, >= n_prompt, d]``. Returns ``[Hq, n_prompt]``."""
     q_window = np.asarray(q_window, dtype=np.float64)
@@ -573,7 +578,8 @@ def compacted_position(i: int, n_keep: int) -> int:
 
 def kv_cache_bytes(n_layers, n_kv_heads, head_dim, bytes_per_elem, positions,
                    scale_bytes_per_position_per_cache=0):
-    """``layers x 2 (K+V) x kv_heads x head_dim x bytes x positions``, plus the
+    """Elements ``n_layers * 2 * n_kv_heads * head_dim * positions`` (K and V)
+    times their size in bytes, plus the
     FP8 scale overhead of one scale per position per cache (K and V of each
     layer)."""
     elems = n_layers * 2 * n_kv_heads * head_dim * positions

@@ -539,7 +539,7 @@ SNAP_CASES = [
 @pytest.mark.parametrize("case", SNAP_CASES, ids=lambda c: "-".join(map(str, c[:6] + c[7:])))
 def test_snapkv_scores_match_oracle(api, case):
     """SnapKV-style prefill scoring (Context views at marginal cost, section
-    3, Fact 1): window scores per (token, head) and max-pooled block scores
+    7, SOTA grounding): window scores per (token, head) and max-pooled block scores
     added onto a non-zero start; prompts shorter than the window, pooling
     kernels from 1 to 33, GQA groups 1 to 16."""
     kv, d, Hq, Hkv, C, W, n_prompt, pool = case

@@ -476,8 +476,8 @@ def test_compact_mode_equals_evict_mode(session_mod, wname, every):
 # ---------------------------------------------------------------- SnapKV at full size
 
 def test_snapkv_397b_full_size_sampled(session_mod):
-    """SnapKV-style prefill scoring (Context views at marginal cost, section 3,
-    Fact 1) at the benchmark's shape and launch configuration: 16 sequences,
+    """SnapKV-style prefill scoring (Context views at marginal cost, section 7,
+    SOTA grounding) at the benchmark's shape and launch configuration: 16 sequences,
     32 query / 8 KV heads, FP8, a 32768-token prompt, window 32, pooling
     kernel 7, one layer's cache. The oracle checks sampled outputs one by one:
     every token score of every head of sequence 11 and the block scores built

@@ -232,8 +232,8 @@ def _sdpa_over(q, K, V, cols, scale):
 
 
 def test_reattend_matches_sdpa_over_gathered_blocks():
-    """Context views at marginal cost, Tier 2: the new query against the cached
-    keys of the chosen spans only. Pinned against torch attention over the
+    """Context views at marginal cost, Tier 2: the new query attends over the
+    cached keys of the chosen spans only. Pinned against torch attention over the
     gathered columns and an explicit per-block loop for the distribution."""
     rng = np.random.default_rng(23)
     Hq, Hkv, d, n, nb = 8, 2, 32, 150, 12

@@ -148,7 +148,7 @@ def test_fp8_scale_overhead_reading():
 # ---------------------------------------------------------------- threshold views and counters
 
 def test_hot_count_is_the_number_of_turns_above_threshold():
-    """Scissorhands (Context views at marginal cost, section 3, Fact 1): the
+    """Scissorhands (Context views at marginal cost, section 7, SOTA grounding): the
     count of turns whose attention exceeded the threshold; strict inequality."""
     rng = np.random.default_rng(2)
     nb, turns, theta = 9, 40, 0.35
@@ -208,7 +208,7 @@ def test_filter_blocks_brute_force_and_boundaries():
 
 
 def test_selection_on_attended_is_tova():
-    """TOVA (section 3, Fact 1): the latest query's head-summed weight, evict
+    """TOVA (Context views at marginal cost, section 7, SOTA grounding): the latest query's head-summed weight, evict
     the minimum. Selecting on Attended with one block less than the candidates
     drops exactly the least-attended candidate."""
     rng = np.random.default_rng(12)
