@@ -218,7 +218,7 @@ int kvs_decode_workspace_init(const kvs_geom* g, void* workspace, size_t workspa
 namespace {
 
 // Points the decode arguments at the plan's regions of the workspace ws; the
-// completion flags go to flags, or to the plan's own region when flags is
+// completion counters go to flags, or to the plan's own region when flags is
 // NULL.
 void bind_workspace(const Plan& p, char* ws, uint32_t* flags, kvs::PartialArgs* a, kvs::CombineArgs* c) {
   a->ws_m = (float*)(ws + p.off_m); a->ws_l = (float*)(ws + p.off_l);
@@ -646,13 +646,13 @@ int kvs_update_sidecar_select(float* mass_accum, float* attended, float* ema, fl
 // ---------------------------------------------------------------------------
 namespace {
 
-// The array's first part holds the completion flags, at the same place for
-// every geometry: each call leaves the flags it used at zero (its merging
-// workgroups clear them), so they are zero at the start of every call,
+// The array's first part holds the completion counters, at the same place for
+// every geometry: each call leaves the counters it used at zero (its merging
+// workgroups reset them), so they are zero at the start of every call,
 // whatever geometry the previous call had. The rest holds one call's
 // workspace regions (partials, block records, boundaries, merge weights,
 // clock records and the per-class rates, which are sanitised on read).
-constexpr size_t kNoallocFlagBytes = 64 * 1024;  // 16384 flags: B * Hkv * partitions
+constexpr size_t kNoallocFlagBytes = 64 * 1024;  // counter region: B * Hkv * partitions words
 constexpr size_t kNoallocWsBytes = (size_t)KVS_NOALLOC_SCRATCH_BYTES - kNoallocFlagBytes;
 constexpr int kMaxDevices = 64;
 

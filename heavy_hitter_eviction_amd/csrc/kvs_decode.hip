@@ -966,15 +966,14 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
 
   // ---- the last partition of this (sequence, KV head) to finish merges the
   // group's outputs, so the output needs no further launch. Each partition,
-  // once its partial is in memory, sets its flag word (zero at entry: the
-  // workspace contract) to 1 and then reads the pair's flags: the partition
-  // whose flag lands last sees them all set and merges (two whose flags land
-  // together may both merge: they read the same partials in the same order
-  // and write the same values). A merging workgroup clears the flags
-  // afterwards, after every flag of the pair was seen set, so each call ends
-  // with the flags zero again (the next call, or a graph replay, starts
-  // clean). One round trip to memory, where a shared counter took one per
-  // partition finishing at the same time. ----
+  // once its partial is in memory, adds 1 to the pair's completion counter
+  // (zero at entry: the workspace contract) with one system-scope atomic,
+  // performed at memory past every XCD's L2; the partition that reads back
+  // nparts - 1 is the last and merges, then puts the counter back to zero, so
+  // each call ends with it zero again (the next call, or a graph replay,
+  // starts clean). One round trip to memory per partition and no retries
+  // (a compare-and-swap took one retry per partition finishing at the same
+  // time; a flag per partition took a store and then a load). ----
   // The partials are write-through stores; once every wave has them
   // acknowledged (vmcnt 0) they are in memory, so the flag needs no cache
   // writeback, and the merging workgroup reads them past its caches.
@@ -987,19 +986,14 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   } else {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores acknowledged
     __syncthreads();
-    uint32_t* fl = a.pair_flag + ((size_t)b * a.Hkv + g) * a.nparts;
+    uint32_t* fl = a.pair_flag + ((size_t)b * a.Hkv + g) * a.nparts;  // word 0: the pair's counter
     if (wave != 0) {
       if constexpr (SCORED) store_records(64, NTH - 64);
     } else {
       // system scope: performed at memory, past every XCD's L2
-      if (lane == 0) __hip_atomic_store(fl + part, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // the flag is in memory before the others are read
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      bool set = true;
-      for (int x = lane; x < a.nparts; x += 64)
-        set = set && __hip_atomic_load(fl + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0u;
-      const bool all = __builtin_amdgcn_ballot_w64(!set) == 0;
-      if (lane == 0) misc[6] = all ? 1 : 0;
+      uint32_t old = 0u;
+      if (lane == 0) old = __hip_atomic_fetch_add(fl, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      if (lane == 0) misc[6] = old == (uint32_t)(a.nparts - 1) ? 1 : 0;
     }
     __syncthreads();
     if (misc[6] == 1) {
@@ -1046,7 +1040,7 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
         else
           ((float*)a.out)[oi] = sum;
       }
-      for (int x = threadIdx.x; x < P; x += NTH) __hip_atomic_store(fl + x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      if (threadIdx.x == 0) __hip_atomic_store(fl, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
   }
 }

@@ -47,10 +47,11 @@ struct PartialArgs {
   const void* app_k;
   const void* app_v;
   int app_bf16;
-  // Output merge in the kernel: every partition of a (sequence, KV head) sets
-  // its flag (pair_flag[B][Hkv][P], zero at entry) to 1 once its partial is
-  // in memory; the one that finds all flags set merges the group's partials
-  // into out and clears the flags.
+  // Output merge in the kernel: every partition of a (sequence, KV head) adds
+  // 1 to the pair's counter (pair_flag[(b * Hkv + g) * P], zero at entry;
+  // the region holds B * Hkv * P words) once its partial is in memory; the
+  // one that reads back P - 1 merges the group's partials into out and puts
+  // the counter back to zero.
   uint32_t* pair_flag;
   void* out;
 };

@@ -162,10 +162,11 @@ KVS_API int kvs_decode_workspace_bytes(const kvs_geom* geom, size_t* bytes);
  * kvs_decode_workspace_init -- make a decode workspace ready: fills its first
  * kvs_decode_workspace_bytes() bytes with zeros, on the stream, with a fill
  * kernel (no memset node, so it may be captured in a HIP graph). The decode
- * calls need the workspace's per-partition completion flags to be zero when
- * they start and leave them zero when they end, so this is needed once after
- * allocation (a zero-filled buffer is equally valid) and again before the
- * workspace is used with another geometry (the flags then sit elsewhere).
+ * calls need the workspace's completion counters (one per sequence and KV
+ * head) to be zero when they start and leave them zero when they end, so this
+ * is needed once after allocation (a zero-filled buffer is equally valid) and
+ * again before the workspace is used with another geometry (the counters then
+ * sit elsewhere).
  * Errors: KVS_EINVAL (bad geometry or NULL), KVS_EALIGN, KVS_EWS.
  */
 KVS_API int kvs_decode_workspace_init(const kvs_geom* geom, void* workspace, size_t workspace_bytes,
@@ -208,8 +209,8 @@ KVS_API int kvs_decode_workspace_init(const kvs_geom* geom, void* workspace, siz
  *   workspace   device scratch of at least kvs_decode_workspace_bytes(),
  *               owned by the caller and initialised for this geometry with
  *               kvs_decode_workspace_init (or zero-filled); calls that share
- *               one must not overlap. Its per-partition completion flags are
- *               zero when a call starts and zero again when it ends. Besides
+ *               one must not overlap. Its completion counters are zero when a
+ *               call starts and zero again when it ends. Besides
  *               per-call partials it keeps, from call to call, the streaming
  *               rate measured for each of the GPU's dispatch classes
  *               (workgroup id mod 8); in dynamic mode the next call splits
@@ -239,15 +240,15 @@ KVS_API int kvs_decode_attn_scored(const kvs_geom* geom, const void* q, const vo
  *
  * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
  * (on different streams, or from several host threads without ordering) race
- * and give unspecified results. Each call leaves the array's completion flags
- * zero, so consecutive calls of any geometries need nothing in between. The
- * first call on each device looks up the array's address (with that device
- * current) and clears its flag region on the call's stream.
+ * and give unspecified results. Each call leaves the array's completion
+ * counters zero, so consecutive calls of any geometries need nothing in
+ * between. The first call on each device looks up the array's address (with
+ * that device current) and clears its counter region on the call's stream.
  *
  * Errors: as kvs_decode_attn_scored; KVS_ESCRATCH when the geometry's
  * workspace (kvs_decode_workspace_bytes) does not fit the array beside its
- * 64 KiB flag region, or needs more than 16384 completion flags
- * (B * Hkv * partitions); KVS_EHIP when the array's address cannot be found.
+ * 64 KiB counter region, or its counters (B * Hkv * partitions words) do not
+ * fit that region; KVS_EHIP when the array's address cannot be found.
  */
 #define KVS_NOALLOC_SCRATCH_BYTES (16u << 20)
 KVS_API int kvs_decode_attn_scored_noalloc(const kvs_geom* geom, const void* q, const void* k_cache,
