@@ -59,6 +59,10 @@ def parse():
                          "of inside the partial kernel (kvs_append_decode_attn)")
     ap.add_argument("--compact-every", type=int, default=64,
                     help="compact mode: steps between physical compactions (evicted blocks are masked between)")
+    ap.add_argument("--graph", action="store_true",
+                    help="decode mode: replay each timed step from HIP graphs recorded before timing "
+                         "(two graphs per step: the layers' partial launches, then the mass combine, "
+                         "side-car and selection) instead of launching it from Python")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
                          "(a reference for hardware byte counters)")
@@ -207,13 +211,31 @@ def run_gpu(args, w):
     sev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     keep = None
+    use_graph = args.graph and fused and not profiled
+    captured = []
     for t in range(n_steps):
         if t == args.warmup:
+            if use_graph:
+                # every timed step recorded now (after the eager warm-up steps
+                # have loaded the kernels); nothing runs while recording
+                torch.cuda.synchronize()
+                for tt in range(args.warmup, n_steps):
+                    captured.append(dec.capture_step([Q[l][tt] for l in range(L)], [K[l][tt] for l in range(L)],
+                                                     [V[l][tt] for l in range(L)], cur[tt], step_index=tt,
+                                                     split=True))
+                log(f"recorded {len(captured)} steps as HIP graphs")
             torch.cuda.synchronize()
             start.record()
         timed = t >= args.warmup
         if timed:
             sev[t - args.warmup].record()
+        if timed and use_graph:
+            i = t - args.warmup
+            ev[i][0].record()
+            captured[i].replay_layers()
+            ev[i][1].record()
+            captured[i].replay_rest()
+            continue
         keep = dec.keep if (args.evict and not w.window) else None
         for layer in range(L):
             if not fused:
@@ -593,6 +615,8 @@ def main():
             **({"timed_positions": [w.context + s0 + args.warmup, w.context + s0 + args.warmup + args.steps - 1],
                 "ring_state": "full (steady state)"} if w.ring else {}),
             "append": "separate launch" if args.separate_append else "in the partial kernel",
+            "launch": "HIP graph per step" if (args.graph and args.mode == "decode" and not args.separate_append)
+                      else "eager from Python",
             "masses": "per layer" if args.separate_append else "once per step, all layers",
             **({"outputs": "per-head block masses [B][Hq][NBmax] and max over heads and layers"}
                if args.mode == "profiled" else {}),

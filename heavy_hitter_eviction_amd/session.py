@@ -26,15 +26,17 @@ from . import api
 from .workloads import Workload
 
 
-def geom_of(w: Workload) -> api.CacheGeom:
+def geom_of(w: Workload, deterministic: bool = False) -> api.CacheGeom:
     return api.CacheGeom(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
                          head_dim=w.head_dim, capacity=w.capacity, window=w.window, ring=w.ring,
-                         n_blocks_max=w.n_blocks_max, kv_dtype=w.kv_dtype, q_dtype=w.q_dtype)
+                         n_blocks_max=w.n_blocks_max, kv_dtype=w.kv_dtype, q_dtype=w.q_dtype,
+                         deterministic=deterministic)
 
 
 class ScoredDecoder:
     def __init__(self, w: Workload, evict: bool = False, device="cuda", layers: int | None = None,
-                 compact: bool = False, compact_every: int = 1, fused: bool = True, tap: bool = True):
+                 compact: bool = False, compact_every: int = 1, fused: bool = True, tap: bool = True,
+                 deterministic: bool = False):
         if compact and (w.ring or w.window or not w.select):
             raise ValueError("compaction needs a linear cache with selection and no window")
         if compact_every < 1:
@@ -46,7 +48,7 @@ class ScoredDecoder:
         self.fused = fused
         self.tap = tap
         self.device = torch.device(device)
-        self.geom = geom_of(w)
+        self.geom = geom_of(w, deterministic)
         self.n_layers = w.n_layers if layers is None else layers
         self.caches = [api.KVCache(self.geom, device) for _ in range(self.n_layers)]
         self.workspace = api.decode_workspace(self.geom, device)
@@ -90,6 +92,42 @@ class ScoredDecoder:
             self.append_attend_layer(l, q_layers[l], k_layers[l], v_layers[l], cur_pos)
         self.finish_masses(cur_pos)
         self.close_turn(cur_pos)
+
+    def capture_step(self, q_layers, k_layers, v_layers, cur_pos: torch.Tensor, step_index: int | None = None,
+                     split: bool = False):
+        """Record one whole decode step as HIP graphs, without running it:
+        every layer's append and scored attention, the mass combine, the
+        side-car update and the selection, exactly the launches ``step``
+        makes, with the trajectory slot of turn ``step_index`` (default: the
+        next turn). Returns a ``CapturedStep``; its ``replay()`` performs the
+        step on the tensors given here (their contents may change, their
+        addresses may not). With ``split`` the layers' launches and the rest
+        of the step are two graphs (``replay_layers``, ``replay_rest``), so a
+        caller can time the layers alone. The step makes no allocation,
+        memset or synchronisation, so the graphs hold kernel nodes only."""
+        idx = self.step_index if step_index is None else step_index
+        keep_idx = self.step_index
+        graphs = []
+        try:
+            self.step_index = idx
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for l in range(self.n_layers):
+                    self.append_attend_layer(l, q_layers[l], k_layers[l], v_layers[l], cur_pos)
+                if not split:
+                    self.finish_masses(cur_pos)
+                    self.close_turn(cur_pos)
+            graphs.append(g)
+            if split:
+                self.step_index = idx
+                g2 = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g2):
+                    self.finish_masses(cur_pos)
+                    self.close_turn(cur_pos)
+                graphs.append(g2)
+        finally:
+            self.step_index = keep_idx
+        return CapturedStep(self, graphs, idx)
 
     def finish_masses(self, cur_pos: torch.Tensor):
         """Tap mode: add every layer's block masses into ``mass`` (one call)."""
@@ -161,3 +199,32 @@ class ScoredDecoder:
             api.update_sidecar(self.mass, self.attended, self.ema, self.cum, self.traj,
                                self.step_index, self.w.alpha)
         self.step_index += 1
+
+
+class CapturedStep:
+    """One decode step recorded by ``ScoredDecoder.capture_step``. Replay it
+    once, when the decoder is at the turn it was recorded for; the decoder's
+    turn count then advances as after ``step``."""
+
+    def __init__(self, dec: ScoredDecoder, graphs, step_index: int):
+        self.dec, self.graphs, self.step_index = dec, graphs, step_index
+
+    def _check(self):
+        if self.dec.step_index != self.step_index:
+            raise RuntimeError(f"step recorded for turn {self.step_index}, decoder is at turn {self.dec.step_index}")
+
+    def replay(self):
+        self._check()
+        for g in self.graphs:
+            g.replay()
+        self.dec.step_index += 1
+
+    def replay_layers(self):
+        """Split recordings: the layers' launches only (follow with replay_rest)."""
+        self._check()
+        self.graphs[0].replay()
+
+    def replay_rest(self):
+        self._check()
+        self.graphs[1].replay()
+        self.dec.step_index += 1
