@@ -76,7 +76,7 @@ Plan make_plan(const kvs_geom* g) {
   // partition, the block-sum records and the kept-tile list in LDS: bound the
   // partition so that part stays <= 64 KiB
   const int nw = kvs::kPartialWaves;
-  const int lds_fixed = nw * 256 + 8 + 2 * nw * 16 + p.NT / 32 + 1;  // + the keep bitmap
+  const int lds_fixed = nw * 256 + kvs::kAppRowFloats + 8 + 2 * nw * 16 + p.NT / 32 + 1;  // + the keep bitmap
   const int per_tile = p.G * (p.nsub + 1) + 1;
   const int tpp_lds = (kLdsBudgetFloats - lds_fixed) / per_tile;
   if (tpp > tpp_lds) tpp = tpp_lds < 4 ? 4 : tpp_lds;

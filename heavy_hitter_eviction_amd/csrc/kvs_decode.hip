@@ -263,14 +263,16 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   const int app_cand_tile = app_cand >= 0 ? app_cand / kTile : -1;
 
   // LDS carve-up (16-byte aligned parts first): per-wave side data (FP8
-  // scales, ring positions of the claimed tiles), then the kept-tile count,
-  // the claim counter, the append flag, the list entry of the appended tile
-  // and the list split point, each wave's final max and sum per head, the
-  // block-sum records of every list entry (sums per sub-block and head, and
-  // the running max they are relative to), the list of kept tiles and the
-  // keep bitmap. The waves' outputs are staged over the records at the end.
+  // scales, ring positions of the claimed tiles), the appended row of this KV
+  // head as the cache holds it (K and V values, then the FP8 scales), then
+  // the kept-tile count, the claim counter, the appended row's flag and the
+  // list split point, each wave's final max and sum per head, the block-sum
+  // records of every list entry (sums per sub-block and head, and the running
+  // max they are relative to), the list of kept tiles and the keep bitmap.
+  // The waves' outputs are staged over the records at the end.
   float* side_area = lds;                               // [NW][64 quads][4]
-  int* misc = (int*)(side_area + NW * 256);             // [8]
+  uint8_t* app_lds = (uint8_t*)(side_area + NW * 256);  // [2][D * eb] bytes; the scales in its last 2 floats
+  int* misc = (int*)(side_area + NW * 256 + kAppRowFloats);  // [8]
   float* mw = (float*)(misc + 8);                       // [NW][16]
   float* lw = mw + NW * 16;                             // [NW][16]
   float* e_rec = lw + NW * 16;                          // [tl_cap][NSUB][G]
@@ -283,7 +285,6 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   if (threadIdx.x == 0) {
     misc[1] = NW;  // claim counter: batches 0 .. NW - 1 are the waves' first
     misc[2] = 0;
-    misc[3] = -1;
   }
 
   // With a keep mask, or a list of block ids to re-attend, on a linear cache
@@ -388,7 +389,6 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
       if (kept) {
         const int e = n + __popcll(m & ((1ull << lane) - 1ull));
         tlist[e] = t;
-        if (t == app_cand_tile) misc[3] = e;
       }
       n += __popcll(m);
     }
@@ -410,9 +410,6 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   // a per-lane loop
   const int n_items = __builtin_amdgcn_readfirstlane(use_list ? misc[0] : te - tb);
   const int n_batches = (n_items + BATCH - 1) / BATCH;
-  // batch holding the appended tile (-1: none here, or not read)
-  const int app_entry = app_tile < 0 ? -1 : use_list ? misc[3] : app_tile - tb;
-  const int app_batch = __builtin_amdgcn_readfirstlane(app_entry < 0 ? -1 : app_entry / BATCH);
   auto tile_of = [&](int e) -> int {  // tile of list entry e < n_items (wave-uniform e)
     if (use_list) return __builtin_amdgcn_readfirstlane(tlist[e]);
     return tb + e;
@@ -433,11 +430,6 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
       v = wave + NW * n_claimed;
     }
     ++n_claimed;
-    // the batch with the appended tile is read only once the row is written
-    if (v == app_batch) {
-      while (__hip_atomic_load(&misc[2], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
-        __builtin_amdgcn_s_sleep(1);
-    }
     return v;
   };
 
@@ -528,6 +520,73 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
     if constexpr (SIDE) *(u32x4*)(side_w + 4 * lane) = pf;
   };
 
+  // ---- the slot appended in this call ----
+  // The appending wave publishes the values the cache will hold for it (this
+  // KV head's K and V, the FP8 scales) in LDS and raises misc[2] before it
+  // writes the cache, so a wave that reads the tile takes the slot from LDS
+  // and never waits for those writes (what its tile load brought for the
+  // slot, old or new, is replaced). K of slot t sits in the lanes with
+  // lane % 16 == t (16 bytes per chunk); V of slot t in the 16 lanes of group
+  // t / 4, interleaved with the three other slots of the group (element n of
+  // dim group j at byte (4 n + t % 4) eb of its chunk).
+  const int app_ts = app_slot & (kTile - 1);
+  auto patch_appended = [&](TileRegs<KV, D>& t, f32x4& ks, f32x4& vs, int4& cpos) {
+    while (__hip_atomic_load(&misc[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
+      __builtin_amdgcn_s_sleep(1);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    constexpr int NCH = TileRegs<KV, D>::NCH;
+    if ((lane & 15) == app_ts) {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) t.k[i] = *(const u32x4*)(app_lds + 64 * i + 16 * kg);
+    }
+    if (kg == (app_ts >> 2)) {
+      const int e = app_ts & 3;
+      const uint8_t* vrow = app_lds + D * eb;
+      const int x0 = (lane & 15) * (D / 16);
+      constexpr int EPV = 4 / eb;  // values of one slot per 16-byte chunk
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+#pragma unroll
+        for (int w = 0; w < EPV; ++w) {
+          const int x = x0 + EPV * i + w;
+          const int bo = (4 * w + e) * eb;       // byte of the chunk
+          const int dw = bo >> 2;                 // its dword (e is uniform)
+          const uint32_t sh = 8u * (uint32_t)(bo & 3);
+          uint32_t val, keep_mask;
+          if constexpr (eb == 1) {
+            val = (uint32_t)vrow[x] << sh;
+            keep_mask = ~(0xFFu << sh);
+          } else if constexpr (eb == 2) {
+            val = (uint32_t)((const uint16_t*)vrow)[x] << sh;
+            keep_mask = ~(0xFFFFu << sh);
+          } else {
+            val = ((const uint32_t*)vrow)[x];
+            keep_mask = 0u;
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (q == dw) t.v[i][q] = (t.v[i][q] & keep_mask) | val;
+        }
+      }
+      const int r = e;  // the slot's row among this lane's four
+      if constexpr (KV == KV_FP8) {
+        const float sk = ((const float*)app_lds)[kAppRowFloats - 2];
+        const float sv = ((const float*)app_lds)[kAppRowFloats - 1];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (q == r) ks[q] = sk;
+          if (q == r) vs[q] = sv;
+        }
+      }
+      if constexpr (RING) {
+        if (r == 0) cpos.x = i_cur;
+        if (r == 1) cpos.y = i_cur;
+        if (r == 2) cpos.z = i_cur;
+        if (r == 3) cpos.w = i_cur;
+      }
+    }
+  };
+
   // ---- one tile: online softmax, block sums, PV ----
   auto process = [&](TileRegs<KV, D>& cur, const int tile, const int tau, const int ent) {
     f32x4 ks = {0.f, 0.f, 0.f, 0.f}, vs = {0.f, 0.f, 0.f, 0.f};
@@ -537,6 +596,7 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
       vs = *(const f32x4*)(side_w + (tau * QPT + 4 + kg) * 4);
     }
     if constexpr (RING) cpos = *(const int4*)(side_w + (tau * QPT + 8 + kg) * 4);
+    if (tile == app_tile) patch_appended(cur, ks, vs, cpos);
     bool valid[4];
     int sub[4];
     bool all_valid, any_valid;
@@ -766,23 +826,62 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
       sk = fp8_scale_of(mk);
       sv = fp8_scale_of(mv);
     }
+    // this KV head's values as the cache holds them (codes, bf16 or f32
+    // bits), dims lane and lane + 64: first into LDS for the waves that read
+    // the tile in this call (they patch the slot from there), then the flag,
+    // then the cache writes, which no wave of this call waits for
+    constexpr int XPL = D > 64 ? D / 64 : 1;  // dims per lane
+    uint32_t kbits[XPL], vbits[XPL];
+#pragma unroll
+    for (int c = 0; c < XPL; ++c) {
+      const int x = lane + 64 * c;
+      if (x >= D) continue;
+      const size_t i = rb + (size_t)g * D + x;
+      if constexpr (KV == KV_FP8) {
+        kbits[c] = encode_with_scale(load_src(a.app_k, i, sbf), sk);
+        vbits[c] = encode_with_scale(load_src(a.app_v, i, sbf), sv);
+        app_lds[x] = (uint8_t)kbits[c];
+        app_lds[D + x] = (uint8_t)vbits[c];
+      } else if constexpr (KV == KV_BF16) {
+        kbits[c] = ((const uint16_t*)a.app_k)[i];
+        vbits[c] = ((const uint16_t*)a.app_v)[i];
+        ((uint16_t*)app_lds)[x] = (uint16_t)kbits[c];
+        ((uint16_t*)app_lds)[D + x] = (uint16_t)vbits[c];
+      } else {
+        kbits[c] = ((const uint32_t*)a.app_k)[i];
+        vbits[c] = ((const uint32_t*)a.app_v)[i];
+        ((uint32_t*)app_lds)[x] = kbits[c];
+        ((uint32_t*)app_lds)[D + x] = vbits[c];
+      }
+    }
+    if (lane == 0) {
+      ((float*)app_lds)[kAppRowFloats - 2] = sk;
+      ((float*)app_lds)[kAppRowFloats - 1] = sv;
+    }
+    // the wave's LDS writes are done (lgkmcnt 0, no wait on memory) before
+    // the flag is raised
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (lane == 0) __hip_atomic_store(&misc[2], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     const int t = app_slot & (kTile - 1);
     const size_t base = (((size_t)b * a.Hkv + g) * (size_t)(a.C / kTile) + app_tile) * tile_bytes;
     char* kc = (char*)const_cast<void*>(a.k) + base;
     char* vc = (char*)const_cast<void*>(a.v) + base;
-    for (int x = lane; x < D; x += 64) {
-      const size_t i = rb + (size_t)g * D + x;
+#pragma unroll
+    for (int c = 0; c < XPL; ++c) {
+      const int x = lane + 64 * c;
+      if (x >= D) continue;
       char* kp = kc + k_tile_offset(t, x, eb);
       char* vp = vc + v_tile_offset(t, x, D, eb);
       if constexpr (KV == KV_FP8) {
-        *(uint8_t*)kp = (uint8_t)encode_with_scale(load_src(a.app_k, i, sbf), sk);
-        *(uint8_t*)vp = (uint8_t)encode_with_scale(load_src(a.app_v, i, sbf), sv);
+        *(uint8_t*)kp = (uint8_t)kbits[c];
+        *(uint8_t*)vp = (uint8_t)vbits[c];
       } else if constexpr (KV == KV_BF16) {
-        *(uint16_t*)kp = ((const uint16_t*)a.app_k)[i];
-        *(uint16_t*)vp = ((const uint16_t*)a.app_v)[i];
+        *(uint16_t*)kp = (uint16_t)kbits[c];
+        *(uint16_t*)vp = (uint16_t)vbits[c];
       } else {
-        *(float*)kp = ((const float*)a.app_k)[i];
-        *(float*)vp = ((const float*)a.app_v)[i];
+        *(uint32_t*)kp = kbits[c];
+        *(uint32_t*)vp = vbits[c];
       }
     }
     if (lane == 0) {
@@ -794,13 +893,12 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
     }
   };
   // First batch of this wave: its own index, its side data and first tiles
-  // requested before the workgroup's first barrier (without a keep list).
-  // The batch holding the appended row is requested once the row is written.
+  // requested before the workgroup's first barrier (without a keep list),
+  // the batch holding the appended slot too (the slot is patched from LDS).
   TileRegs<KV, D> buf[NBUF];
   int cur = wave;
   ++n_claimed;
-  const bool early = cur < n_batches && cur != app_batch;
-  if (early) {
+  if (cur < n_batches) {
     gather(cur);
 #pragma unroll
     for (int i = 0; i < NBUF - 1; ++i) load_tile<KV, D, RING>(buf[i], ad, soff_of(cur, i));
@@ -808,23 +906,9 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   // the claim counter and the append flag are initialised (with a keep list
   // the list's barrier has seen to that)
   if (!use_list) __syncthreads();
-  if (app_slot >= 0 && wave == NW - 1) {
-    append_row();
-    // release: the wave's stores complete (vmcnt 0) before the flag is seen;
-    // the workgroup-scope release alone relies on the CU's in-order memory
-    // pipeline, the explicit wait does not
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    if (lane == 0) __hip_atomic_store(&misc[2], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-  }
+  if (app_slot >= 0 && wave == NW - 1) append_row();
 
   int n_done = 0;  // tiles this wave processed
-  if (!early && cur < n_batches) {
-    while (__hip_atomic_load(&misc[2], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
-      __builtin_amdgcn_s_sleep(1);
-    gather(cur);
-#pragma unroll
-    for (int i = 0; i < NBUF - 1; ++i) load_tile<KV, D, RING>(buf[i], ad, soff_of(cur, i));
-  }
   if (cur < n_batches) {
     convert_q();
     while (true) {
@@ -1272,12 +1356,23 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
     // ---- tables of layers [l0, l0 + lc) ----
     if (l0 > 0) __syncthreads();  // the previous chunk's tables are done with
     const int n_st = lc * (n_ml + n_bnd);
+    // four values per thread in flight per round (one round trip each)
+    auto stage_rest = [&](int la, int x_first) {
+      for (int x0 = x_first; x0 < n_st; x0 += 4 * 256) {
+        float v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = stage_src(la, min(x0 + tid + 256 * k, n_st - 1));
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (x0 + tid + 256 * k < n_st) *stage_dst(x0 + tid + 256 * k) = v[k];
+      }
+    };
     if (l0 == 0) {
       if (tid < n_st) *stage_dst(tid) = pre0;
       if (tid + 256 < n_st) *stage_dst(tid + 256) = pre1;
-      for (int x = tid + 512; x < n_st; x += 256) *stage_dst(x) = stage_src(0, x);
+      stage_rest(0, 512);
     } else {
-      for (int x = tid; x < n_st; x += 256) *stage_dst(x) = stage_src(l0, x);
+      stage_rest(l0, 0);
     }
     __syncthreads();
     if (!m_live) continue;
@@ -1568,15 +1663,20 @@ void kvs_combine_layers(CombineArgs a) {
     for (int l = l0 + 2 * ls; l < L; l += ls)
       for (int r = lane; r < per; r += 64) t_wp(l)[r] = tab_val(l, r);
   } else {
-    for (int l = 0; l < L; ++l) {
-      for (int r0 = 0; r0 < per; r0 += 4 * NTH) {
-        float v[4];
+    // every layer's tables in one flat index (layer-major, as in LDS), four
+    // values per thread in flight: one memory round trip for up to 2048
+    // values, not one per layer
+    const int n_tab = L * per;
+    for (int x0 = 0; x0 < n_tab; x0 += 4 * NTH) {
+      float v[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = tab_val(l, r0 + tid + k * NTH);
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          if (r0 + tid + k * NTH < per) t_wp(l)[r0 + tid + k * NTH] = v[k];
+      for (int k = 0; k < 4; ++k) {
+        const int x = min(x0 + tid + k * NTH, n_tab - 1);
+        v[k] = tab_val(x / per, x % per);
       }
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (x0 + tid + k * NTH < n_tab) lds[x0 + tid + k * NTH] = v[k];
     }
     __syncthreads();
   }

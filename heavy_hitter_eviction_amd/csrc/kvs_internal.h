@@ -11,6 +11,10 @@ enum : int { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
 
 // Waves per decode (partial) workgroup; one such workgroup per compute unit.
 constexpr int kPartialWaves = 8;
+// LDS floats the decode kernel keeps for the appended row of its KV head:
+// K and V values as the cache holds them (at most 2 x 128 x 4 bytes), then
+// the two FP8 scales in the last two floats.
+constexpr int kAppRowFloats = 260;
 
 struct PartialArgs {
   const void* q;
