@@ -47,13 +47,15 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=("decode", "profiled", "reattend", "compact", "snapkv"), default="decode",
+    ap.add_argument("--mode", choices=("decode", "profiled", "reattend", "compact", "snapkv", "stream"),
+                    default="decode",
                     help="decode: the scored decode step (headline); profiled: the same step also "
                          "keeping per-head block masses and their max over heads and layers; "
                          "reattend: Tier 2, a new query over the blocks the selection kept; "
                          "compact: evict mode that moves the kept blocks to the front after each "
                          "selection (H2O compaction) and decodes the shorter cache; snapkv: prefill "
-                         "scoring from the last 32 prompt queries, max-pooled per block")
+                         "scoring from the last 32 prompt queries, max-pooled per block; stream: the "
+                         "streaming-read probe (kvs_stream_read) over sizes and workgroup counts")
     ap.add_argument("--separate-append", action="store_true",
                     help="decode/profiled modes: append with its own launch (kvs_append_kv) instead "
                          "of inside the partial kernel (kvs_append_decode_attn)")
@@ -492,6 +494,52 @@ def run_snapkv(args, w):
     }
 
 
+def stream_ceiling(nbytes, workgroups=256, reps=20):
+    """The streaming-read probe (kvs_stream_read) over a buffer of ``nbytes``
+    (rounded down to KiB): every byte read once with the decode kernel's kind
+    of load, ``workgroups`` 8-wave workgroups; GB/s from the mean of one HIP
+    event pair per launch, on the stream the probe runs on."""
+    import torch
+
+    from heavy_hitter_eviction_amd import api
+    n = max(1024, nbytes // 1024 * 1024)
+    # launches rotate over buffers that together exceed the 256 MB Infinity
+    # Cache, as the decode step's layers do, so every read comes from HBM
+    nbuf = max(1, -(-(640 << 20) // n))
+    bufs = [torch.ones(n // 4, dtype=torch.int32, device="cuda") for _ in range(nbuf)]
+    sums = torch.zeros(workgroups, dtype=torch.int32, device="cuda")
+    for k in range(nbuf + 1):
+        api.stream_read(bufs[k % nbuf], sums, workgroups)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for k, (a, b) in enumerate(evs):
+        a.record()
+        api.stream_read(bufs[k % nbuf], sums, workgroups)
+        b.record()
+    torch.cuda.synchronize()
+    us = sum(a.elapsed_time(b) for a, b in evs) / reps * 1e3
+    # every dword is 1: each workgroup's sum counts its dwords
+    assert int(sums.sum().item()) == n // 4, "probe sums do not cover the buffer"
+    del bufs, sums
+    return {"kernel": "kvs_stream_read", "gbs": round(n / (us * 1e-6) / 1e9, 2), "bytes": n, "buffers": nbuf,
+            "workgroups": workgroups, "avg_launch_us": round(us, 2)}
+
+
+def run_stream(args):
+    """The probe alone: sizes from 64 MiB to 4 GiB, 256 to 2048 workgroups."""
+    rows = []
+    for mib in (64, 256, 1028, 4096):
+        for wgs in (256, 512, 1024, 2048):
+            r = stream_ceiling(mib << 20, wgs, reps=args.steps)
+            rows.append(r)
+            log(f"{mib} MiB, {wgs} workgroups: {r['gbs']} GB/s ({r['avg_launch_us']} us)")
+    best = max(rows, key=lambda r: r["gbs"])
+    return {"metric": "streaming-read probe: GB/s, every byte read once with the decode kernel's loads",
+            "value": best["gbs"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": 2,
+            "ms_per_step": round(best["avg_launch_us"] / 1e3, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "u32", "data": "synthetic", "config": {"workload": "stream probe"},
+            "pct_hbm_peak": round(100.0 * best["gbs"] / HBM_PEAK_GBS, 2), "runs": rows}
+
+
 def oracle_baseline(w, seed, seconds):
     """Time the float64 oracle (as it stands) on (sequence, layer) units of the
     same workload at the first timed step: FP8 decode (or bf16 widening) of the
@@ -550,12 +598,44 @@ def oracle_baseline(w, seed, seconds):
         done += 1
     unit_bytes = n * w.kv_bytes_per_key()
     gbs = done * unit_bytes / elapsed / 1e9
+    per_unit = elapsed / done
+    # side-car update and selection of one step for every sequence (a4, a5),
+    # on masses of the same size: the oracle's SideCar and select_blocks
+    nb = w.n_blocks_max
+    rng = np.random.default_rng(seed)
+    A = rng.random((w.batch, nb)) * (w.n_layers * w.n_q_heads / max(1, i // 16 + 1))
+    cars = [orc.SideCar(nb, w.traj_cap) for _ in range(w.batch)]
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        for b in range(w.batch):
+            cars[b].update(A[b], w.alpha)
+            if w.select:
+                orc.select_blocks(cars[b].cum, None, i, w.budget_blocks, w.recent_tokens, w.sink_tokens)
+        reps += 1
+        if time.perf_counter() - t0 > min(3.0, 0.2 * seconds):
+            break
+    side_s = (time.perf_counter() - t0) / reps
+    step_s = per_unit * w.batch * w.n_layers + side_s
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} (sequence, layer) units at position {i} ({n} keys each, "
                       f"{unit_bytes / 1e6:.1f} MB of KV per unit): dequantise + float64 attention + "
                       f"block mass, {elapsed:.1f} s timed (FP8 encode of the history not timed); "
-                      f"a full step is {w.batch * w.n_layers} units",
-            "seconds_per_unit": round(elapsed / done, 4)}
+                      f"then the side-car update and selection of every sequence, {reps} steps timed",
+            "cpu_model": cpu,
+            "seconds_per_unit": round(per_unit, 4),
+            "sidecar_select_seconds_per_step": round(side_s, 6),
+            "full_step_seconds_extrapolated": round(step_s, 3),
+            "full_step_note": f"extrapolated: {w.batch * w.n_layers} units x seconds_per_unit + one side-car "
+                              f"and selection step"}
 
 
 def main():
@@ -580,6 +660,9 @@ def main():
         return
     if args.mode == "snapkv":
         print(json.dumps(run_snapkv(args, w)), flush=True)
+        return
+    if args.mode == "stream":
+        print(json.dumps(run_stream(args)), flush=True)
         return
 
     dec, total_ms, part_ms, step_ms = run_gpu(args, w)
@@ -638,6 +721,11 @@ def main():
         },
     }
     del dec
+    # the same launch shape as the partial kernel (one 8-wave workgroup per
+    # CU) reading as many bytes as one of its launches
+    ceiling = stream_ceiling(int(bytes_launch))
+    res["stream_ceiling"] = ceiling
+    res["pct_of_stream_ceiling"] = round(100.0 * achieved / ceiling["gbs"], 2)
     if args.calibration_copy_mib:
         import torch
         n = args.calibration_copy_mib << 20

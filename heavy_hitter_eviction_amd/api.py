@@ -34,7 +34,7 @@ EXPORTED = (
     "kvs_decode_attn_profiled",
     "kvs_reattend_blocks",
     "kvs_update_sidecar", "kvs_update_counters", "kvs_filter_blocks", "kvs_select_blocks",
-    "kvs_update_sidecar_select", "kvs_compact_blocks", "kvs_snapkv_workspace_bytes", "kvs_snapkv_scores", "kvs_status_str",
+    "kvs_update_sidecar_select", "kvs_compact_blocks", "kvs_stream_read", "kvs_snapkv_workspace_bytes", "kvs_snapkv_scores", "kvs_status_str",
     "kvs_version",
 )
 
@@ -89,6 +89,7 @@ def _load():
         "kvs_snapkv_workspace_bytes": [G, I32, SZP],
         "kvs_snapkv_scores": [G, P, I32, P, P, P, P, P, I32, P, SZ, P],
         "kvs_select_blocks": [P, P, P, I32, I32, I32, I32, I32, P, P, P, P],
+        "kvs_stream_read": [P, SZ, P, I32, P],
         "kvs_update_sidecar_select": [P, P, P, P, P, I32, I32, I32, I64, F, I32, P, P, I32, I32, I32, P, P, P, P],
     }
     for name, args in sig.items():
@@ -624,3 +625,13 @@ def update_sidecar_select(mass_accum, attended, ema, cum, traj, step: int, alpha
                                          _stream(stream)),
            "kvs_update_sidecar_select")
     return keep_mask, sel_ids, n_sel
+
+
+def stream_read(buf: torch.Tensor, sums: torch.Tensor, workgroups: int, stream=None):
+    """kvs_stream_read: read every byte of ``buf`` once (the streaming-read
+    probe); ``sums`` is uint32/int32 [workgroups]."""
+    _device_check(buf, sums)
+    if sums.numel() < workgroups or sums.element_size() != 4:
+        raise ValueError("sums must hold one 32-bit word per workgroup")
+    _check(LIB.kvs_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sums), workgroups,
+                               _stream(stream)), "kvs_stream_read")

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libkvs.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["kvs_api.hip", "kvs_decode.hip", "kvs_cache.hip", "kvs_select.hip", "kvs_views.hip", "kvs_compact.hip", "kvs_snap.hip"]
+SOURCES = ["kvs_api.hip", "kvs_decode.hip", "kvs_cache.hip", "kvs_select.hip", "kvs_views.hip", "kvs_compact.hip", "kvs_snap.hip", "kvs_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("KVS_OFFLOAD_ARCH", "gfx950")

@@ -614,6 +614,13 @@ int kvs_select_blocks(const float* score, const uint32_t* alive, const int32_t* 
   return hip_status(kvs::launch_select(a, (hipStream_t)stream));
 }
 
+int kvs_stream_read(const void* buf, size_t bytes, uint32_t* sums, int32_t workgroups, void* stream) {
+  if (!buf || !sums || workgroups < 1 || workgroups > 65536) return KVS_EINVAL;
+  if (bytes == 0 || bytes % 1024 != 0 || (size_t)workgroups > bytes / 1024) return KVS_EINVAL;
+  if (!aligned16(buf) || !aligned16(sums)) return KVS_EALIGN;
+  return hip_status(kvs::launch_stream_read(buf, bytes, sums, workgroups, (hipStream_t)stream));
+}
+
 int kvs_update_sidecar_select(float* mass_accum, float* attended, float* ema, float* cum, float* traj,
                               int32_t batch, int32_t n_blocks_max, int32_t traj_cap, int64_t step,
                               float alpha, int32_t score_source, const uint32_t* alive,

@@ -190,4 +190,8 @@ struct SnapArgs {
 };
 hipError_t launch_snap(int kv, int d, const SnapArgs& a, hipStream_t st);
 
+// Streaming-read probe: bytes (a multiple of 1024) read once by `workgroups`
+// 8-wave workgroups, each storing one sum to sums[workgroup].
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sums, int workgroups, hipStream_t st);
+
 }  // namespace kvs

@@ -588,6 +588,23 @@ KVS_API int kvs_update_sidecar_select(float* mass_accum, float* attended, float*
                                       int32_t sink_tokens, uint32_t* keep_mask, int32_t* sel_ids,
                                       int32_t* n_sel, void* stream);
 
+/*
+ * kvs_stream_read -- a measurement helper, not part of the decode step: the
+ * streaming-read ceiling that the decode kernel's KV scan is compared with
+ * (Context views at marginal cost, section 7, Fact 3: the read of the cached
+ * keys by the query is the cost that cannot be avoided). Reads every byte of
+ * buf once with the decode kernel's kind of load (non-temporal 16-byte buffer
+ * loads, 1 KiB of consecutive bytes per wave instruction), split into
+ * `workgroups` equal slices of whole KiB, one 8-wave workgroup each, and
+ * stores the 32-bit wrapping sum of each slice's dwords in sums[workgroup]
+ * (so no load can be skipped). Time it with events on the stream.
+ *   buf   device, 16-byte aligned, bytes > 0 and a multiple of 1024
+ *   sums  device uint32 [workgroups], 16-byte aligned
+ *   1 <= workgroups <= min(65536, bytes / 1024)
+ * Errors: KVS_EINVAL, KVS_EALIGN, KVS_EHIP.
+ */
+KVS_API int kvs_stream_read(const void* buf, size_t bytes, uint32_t* sums, int32_t workgroups, void* stream);
+
 /* Static text for a status code. */
 KVS_API const char* kvs_status_str(int status);
 

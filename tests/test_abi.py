@@ -289,3 +289,14 @@ def test_noalloc_rejects_geometries_beyond_its_scratch_before_any_launch():
     small = _geom(api, kv_dtype=api.KVS_FP8_E4M3)
     assert fn(ctypes.byref(small), *args[:2], None, *args[3:]) == api.KVS_EINVAL     # no V cache
     assert fn(ctypes.byref(small), P(0x1008), *args[1:]) == api.KVS_EALIGN
+
+
+def test_stream_read_rejects_bad_arguments():
+    api = _lib()
+    f = api.LIB.kvs_stream_read
+    P = ctypes.c_void_p
+    assert f(None, 1024, P(0x2000), 1, None) == api.KVS_EINVAL
+    assert f(P(0x1000), 1000, P(0x2000), 1, None) == api.KVS_EINVAL          # not whole KiB
+    assert f(P(0x1000), 2048, P(0x2000), 3, None) == api.KVS_EINVAL          # fewer runs than workgroups
+    assert f(P(0x1000), 2048, P(0x2000), 0, None) == api.KVS_EINVAL
+    assert f(P(0x1008), 2048, P(0x2000), 1, None) == api.KVS_EALIGN
