@@ -476,13 +476,15 @@ struct SnapPlan {
   int tpp, nparts;
   size_t off_part, off_m, off_l, total;
 };
-// Partitions of the prefill scoring passes: about 1024 workgroups of 4 waves
-// (four per CU at up to 128 VGPRs).
+// Partitions of the prefill scoring passes: one round of workgroups of 4
+// waves, about 1024 for bf16 keys (four per CU at up to 128 VGPRs) and 512 for
+// FP8 keys (two per CU at up to 256 VGPRs).
 SnapPlan snap_plan(const kvs_geom* g, int window) {
   SnapPlan p{};
   const int NT = g->capacity / kTileSlots;
   const int pairs = g->batch * g->n_kv_heads;
-  int pt = (1024 + pairs - 1) / pairs;
+  const int target = g->kv_dtype == KVS_FP8_E4M3 ? 512 : 1024;
+  int pt = (target + pairs - 1) / pairs;
   if (pt < 1) pt = 1;
   p.tpp = (NT + pt - 1) / pt;
   if (p.tpp < 1) p.tpp = 1;
