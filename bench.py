@@ -71,17 +71,23 @@ def parse():
     return ap.parse_args()
 
 
-TRAFFIC_NOTE = "profiles/kvs_partial_397b_fp8_32k_traffic.md"
+# committed HBM-traffic notes of the partial kernel, per workload
+TRAFFIC_NOTES = {"397b_fp8": "profiles/kvs_partial_397b_fp8_32k_traffic.md",
+                 "docqa_128k": "profiles/kvs_partial_128k_bf16_traffic.md"}
+# non-packed fp32 VALU lane-ops per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+VALU_PEAK_GOPS = 256 * 4 * 16 * 2.4
 
 
 def measured_traffic(root, workload_key):
-    """HBM bytes per partial launch from the committed FETCH_SIZE/WRITE_SIZE
-    summary, or None when it does not describe the kernel as built now (its
-    source hash differs) or another workload is being measured."""
+    """HBM bytes per partial launch from the committed counter summary of this
+    workload (raw TCC EA request counts), or None when there is none or it
+    does not describe the kernel as built now (its source hash differs)."""
     import hashlib
     import re
-    path = os.path.join(root, TRAFFIC_NOTE)
-    if workload_key != "397b_fp8" or not os.path.exists(path):
+    if workload_key not in TRAFFIC_NOTES:
+        return None
+    path = os.path.join(root, TRAFFIC_NOTES[workload_key])
+    if not os.path.exists(path):
         return None
     text = open(path).read()
     m_val = re.search(r"^traffic_bytes_per_launch: (\d+)$", text, re.M)
@@ -479,6 +485,12 @@ def run_snapkv(args, w):
     kbytes = w.batch * w.context * w.n_kv_heads * w.head_dim * (1 if w.kv_dtype == "fp8" else 2) \
         + (w.batch * w.context * 4 if w.kv_dtype == "fp8" else 0)
     gbs = 2 * kbytes / (us / 1e6) / 1e9
+    # The passes are bound by VALU work, not HBM: per score element and pass
+    # one exponential (quarter rate: 4 fp32 lane-op slots) and two fp32 ops.
+    # Peak: non-packed fp32 lane-ops, 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.
+    elems = w.batch * w.n_q_heads * W * w.context
+    ops = 2 * elems * (4 + 2)
+    gops = ops / (us / 1e6) / 1e9
     return {
         "metric": "SnapKV prefill scoring: K GB/s over its two passes, per layer call",
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": 1,
@@ -487,10 +499,12 @@ def run_snapkv(args, w):
         "config": {"workload": w.name, "mode": "snapkv", "window": W, "pool_kernel": 7, "layers": L,
                    "prompt_tokens": w.context},
         "us_per_layer": round(us, 2),
-        "roofline": {"kernel": "kvs_snap_pass x2 + merge + pool (one call)", "bound": "hbm",
-                     "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "avg_launch_us": round(us, 2),
-                     "bytes_per_launch": int(2 * kbytes)},
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "roofline": {"kernel": "SnapKV pass 0 + merge + pass 1 + pool (one call)", "bound": "alu",
+                     "achieved": round(gops, 1), "peak": VALU_PEAK_GOPS, "unit": "Gop/s",
+                     "frac": round(gops / VALU_PEAK_GOPS, 4), "traffic": None, "avg_launch_us": round(us, 2),
+                     "ops_per_launch": int(ops), "bytes_per_launch": int(2 * kbytes),
+                     "ops_note": "fp32 lane-op slots: per score element and pass one exp2 (4) + two fp32 ops"},
     }
 
 
