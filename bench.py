@@ -73,7 +73,9 @@ def parse():
 
 # committed HBM-traffic notes of the partial kernel, per workload
 TRAFFIC_NOTES = {"397b_fp8": "profiles/kvs_partial_397b_fp8_32k_traffic.md",
-                 "docqa_128k": "profiles/kvs_partial_128k_bf16_traffic.md"}
+                 "docqa_128k": "profiles/kvs_partial_128k_bf16_traffic.md",
+                 "35b_bf16": "profiles/kvs_partial_35b_bf16_4k_traffic.md",
+                 "35b_fp8_ring": "profiles/kvs_partial_35b_fp8_ring_4k_traffic.md"}
 # non-packed fp32 VALU lane-ops per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
 VALU_PEAK_GOPS = 256 * 4 * 16 * 2.4
 
