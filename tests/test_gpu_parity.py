@@ -533,6 +533,10 @@ SNAP_CASES = [
     ("fp8", 64, 16, 2, 256, 16, (255, 40), 33),
     ("bf16", 128, 4, 4, 528, 5, (520, 3), 9),      # G = 1: 5 columns, 11 of padding
     ("fp8", 128, 16, 1, 784, 8, (777, 300), 7),    # G = 16
+    # FP8 with padding columns (pass 1 takes 32-column blocks, pass 2 16-column ones)
+    ("fp8", 128, 16, 4, 1040, 5, (1040, 3), 9),    # 20 columns; a prompt shorter than the window
+    ("fp8", 64, 8, 4, 656, 24, (650, 97), 5),      # 48 columns, d 64
+    ("fp8", 128, 8, 8, 528, 3, (528, 1), 3),       # G = 1: 3 columns; a one-token prompt
 ]
 
 
