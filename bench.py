@@ -223,6 +223,10 @@ def run_gpu(args, w):
     keep = None
     use_graph = args.graph and fused and not profiled
     captured = []
+    # per-step lists of the layers' inputs, made before timing
+    q_at = [[Q[l][t] for l in range(L)] for t in range(n_steps)]
+    k_at = [[K[l][t] for l in range(L)] for t in range(n_steps)]
+    v_at = [[V[l][t] for l in range(L)] for t in range(n_steps)]
     for t in range(n_steps):
         if t == args.warmup:
             if use_graph:
@@ -247,21 +251,27 @@ def run_gpu(args, w):
             captured[i].replay_rest()
             continue
         keep = dec.keep if (args.evict and not w.window) else None
+        if fused:
+            # one library call for the layers (each layer's append, attention
+            # and output merge in one kernel; the block sums stay in the
+            # layers' workspaces), then the step's one mass combine and the
+            # side-car with the selection
+            if timed:
+                ev[t - args.warmup][0].record()
+            dec.attend_layers(q_at[t], k_at[t], v_at[t], cur[t])
+            if timed:
+                ev[t - args.warmup][1].record()
+            if profiled:
+                api.tap_masses(dec.geom, dec.workspaces, cur[t], mass_accum=dec.mass, head_mass=head_mass,
+                               mass_max=mass_max)
+            else:
+                api.tap_masses(dec.geom, dec.workspaces, cur[t], mass_accum=dec.mass)
+            dec.close_turn(cur[t])
+            continue
         for layer in range(L):
             if not fused:
                 dec.caches[layer].append(K[layer][t], V[layer][t], dec.row_seq, cur[t])
             ev_here = timed and layer == (t - args.warmup) % L
-            if fused:
-                # one kernel per layer: the append, the attention and its output
-                # merge; the layer's block sums stay in its workspace for the
-                # step's one tap_masses call
-                if timed and layer == 0:
-                    ev[t - args.warmup][0].record()
-                api.decode_attn_tap(dec.caches[layer], Q[layer][t], cur[t], dec.out[layer], dec.workspaces[layer],
-                                    keep_mask=keep, k_new=K[layer][t], v_new=V[layer][t])
-                if timed and layer == L - 1:
-                    ev[t - args.warmup][1].record()
-                continue
             if ev_here:
                 ev[t - args.warmup][0].record()
             if profiled:
@@ -278,12 +288,6 @@ def run_gpu(args, w):
                 ev[t - args.warmup][1].record()
             api.decode_attn_scored(dec.caches[layer], Q[layer][t], cur[t], dec.out[layer], dec.workspace,
                                    mass_accum=dec.mass, keep_mask=keep, phase="combine")
-        if fused:
-            if profiled:
-                api.tap_masses(dec.geom, dec.workspaces, cur[t], mass_accum=dec.mass, head_mass=head_mass,
-                               mass_max=mass_max)
-            else:
-                api.tap_masses(dec.geom, dec.workspaces, cur[t], mass_accum=dec.mass)
         dec.close_turn(cur[t])
     sev[args.steps].record()
     end.record()

@@ -34,7 +34,7 @@ EXPORTED = (
     "kvs_decode_attn_profiled",
     "kvs_reattend_blocks",
     "kvs_update_sidecar", "kvs_update_counters", "kvs_filter_blocks", "kvs_select_blocks",
-    "kvs_update_sidecar_select", "kvs_compact_blocks", "kvs_stream_read", "kvs_snapkv_workspace_bytes", "kvs_snapkv_scores", "kvs_status_str",
+    "kvs_update_sidecar_select", "kvs_decode_step", "kvs_compact_blocks", "kvs_stream_read", "kvs_snapkv_workspace_bytes", "kvs_snapkv_scores", "kvs_status_str",
     "kvs_version",
 )
 
@@ -56,6 +56,24 @@ class Geom(ctypes.Structure):
         ("ring", ctypes.c_int32), ("n_blocks_max", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
         ("q_dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("deterministic", ctypes.c_int32),
     ]
+
+
+class LayerBufs(ctypes.Structure):
+    """``kvs_layer_bufs``: one layer's device buffers for kvs_decode_step."""
+    _fields_ = [("q", ctypes.c_void_p), ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p),
+                ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p), ("pos_of_slot", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p)]
+
+
+class TurnArgs(ctypes.Structure):
+    """``kvs_turn_args``: the side-car update (and selection) closing a step."""
+    _fields_ = [("attended", ctypes.c_void_p), ("ema", ctypes.c_void_p), ("cum", ctypes.c_void_p),
+                ("traj", ctypes.c_void_p), ("traj_cap", ctypes.c_int32), ("select", ctypes.c_int32),
+                ("step", ctypes.c_int64), ("alpha", ctypes.c_float), ("score_source", ctypes.c_int32),
+                ("alive", ctypes.c_void_p), ("budget_blocks", ctypes.c_int32), ("recent_tokens", ctypes.c_int32),
+                ("sink_tokens", ctypes.c_int32), ("keep_out", ctypes.c_void_p), ("sel_ids", ctypes.c_void_p),
+                ("n_sel", ctypes.c_void_p)]
 
 
 def _load():
@@ -91,6 +109,7 @@ def _load():
         "kvs_select_blocks": [P, P, P, I32, I32, I32, I32, I32, P, P, P, P],
         "kvs_stream_read": [P, SZ, P, I32, P],
         "kvs_update_sidecar_select": [P, P, P, P, P, I32, I32, I32, I64, F, I32, P, P, I32, I32, I32, P, P, P, P],
+        "kvs_decode_step": [G, I32, ctypes.POINTER(LayerBufs), I32, P, P, SZ, P, ctypes.POINTER(TurnArgs), P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -160,11 +179,16 @@ class CacheGeom:
     deterministic: bool = False
 
     def c(self) -> Geom:
-        nb = self.n_blocks_max or self.capacity // 16
-        scale = self.softmax_scale or float(torch.tensor(self.head_dim, dtype=torch.float64).rsqrt())
-        return Geom(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim, self.capacity,
-                    self.window, int(self.ring), nb, DTYPE_CODES[self.kv_dtype],
-                    DTYPE_CODES[self.q_dtype], scale, int(self.deterministic))
+        """The ``kvs_geom`` struct (built once; the library only reads it)."""
+        g = self.__dict__.get("_c")
+        if g is None:
+            nb = self.n_blocks_max or self.capacity // 16
+            scale = self.softmax_scale or float(torch.tensor(self.head_dim, dtype=torch.float64).rsqrt())
+            g = Geom(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim, self.capacity,
+                     self.window, int(self.ring), nb, DTYPE_CODES[self.kv_dtype],
+                     DTYPE_CODES[self.q_dtype], scale, int(self.deterministic))
+            object.__setattr__(self, "_c", g)  # frozen dataclass: a cache, not a field
+        return g
 
     @property
     def nb(self) -> int:
@@ -410,6 +434,126 @@ def tap_masses(geom: CacheGeom, workspaces, cur_pos: torch.Tensor, mass_accum: t
     gc = geom.c()
     _check(LIB.kvs_tap_masses(ctypes.byref(gc), arr, len(workspaces), ws_bytes, _ptr(cur_pos), _ptr(mass_accum),
                               _ptr(head_mass), _ptr(mass_max), _stream(stream)), "kvs_tap_masses")
+
+
+@dataclass
+class Turn:
+    """The side-car arrays and selection arguments that close a decode step
+    (``kvs_turn_args``); ``select=False`` updates the side-car only."""
+    attended: torch.Tensor
+    ema: torch.Tensor
+    cum: torch.Tensor
+    traj: torch.Tensor | None
+    step: int
+    alpha: float
+    select: bool = True
+    budget_blocks: int = 0
+    recent_tokens: int = 1
+    sink_tokens: int = 0
+    score: str = "cumulative"
+    alive: torch.Tensor | None = None
+    keep_out: torch.Tensor | None = None
+    sel_ids: torch.Tensor | None = None
+    n_sel: torch.Tensor | None = None
+
+
+def _turn_args(turn: Turn, B: int, nb: int) -> TurnArgs:
+    words = (nb + 31) // 32
+    for t in (turn.attended, turn.ema, turn.cum):
+        if t.device.type != "cuda" or t.dtype != torch.float32 or t.numel() != B * nb:
+            raise ValueError("side-car arrays must be float32 [B, NBmax] device tensors")
+    traj_cap = 1
+    if turn.traj is not None:
+        if turn.traj.device.type != "cuda" or turn.traj.dtype != torch.float32 or turn.traj.dim() != 3 \
+                or turn.traj.shape[0] != B or turn.traj.shape[2] != nb:
+            raise ValueError("traj must be float32 [B, traj_cap, NBmax]")
+        traj_cap = turn.traj.shape[1]
+    a = TurnArgs()
+    a.attended, a.ema, a.cum = turn.attended.data_ptr(), turn.ema.data_ptr(), turn.cum.data_ptr()
+    a.traj = turn.traj.data_ptr() if turn.traj is not None else None
+    a.traj_cap, a.step, a.alpha, a.select = traj_cap, int(turn.step), float(turn.alpha), int(bool(turn.select))
+    if turn.select:
+        if turn.score not in SCORE_SOURCES:
+            raise ValueError(f"score must be one of {sorted(SCORE_SOURCES)}")
+        for t, n in ((turn.keep_out, B * words), (turn.sel_ids, B * nb), (turn.n_sel, B)):
+            if t is None or t.device.type != "cuda" or t.dtype != torch.int32 or t.numel() != n:
+                raise ValueError("keep_out [B, W], sel_ids [B, NBmax] and n_sel [B] must be int32 device tensors")
+        if turn.alive is not None and (turn.alive.device.type != "cuda" or turn.alive.dtype != torch.int32
+                                       or turn.alive.numel() != B * words):
+            raise ValueError("alive must be int32 bit words [B, W]")
+        a.score_source = SCORE_SOURCES[turn.score]
+        a.alive = turn.alive.data_ptr() if turn.alive is not None else None
+        a.budget_blocks, a.recent_tokens, a.sink_tokens = int(turn.budget_blocks), int(turn.recent_tokens), \
+            int(turn.sink_tokens)
+        a.keep_out, a.sel_ids, a.n_sel = turn.keep_out.data_ptr(), turn.sel_ids.data_ptr(), turn.n_sel.data_ptr()
+    return a
+
+
+def decode_step(caches, q_layers, cur_pos: torch.Tensor, outs, workspaces, k_new=None, v_new=None,
+                keep_mask: torch.Tensor | None = None, mass_accum: torch.Tensor | None = None,
+                turn: Turn | None = None, stream=None):
+    """kvs_decode_step: for every layer ``l`` the append of ``k_new[l]`` /
+    ``v_new[l]`` (lists, or None: nothing appended) and the scored attention
+    of ``q_layers[l]`` into ``outs[l]``, leaving its block sums in
+    ``workspaces[l]``; then, with ``mass_accum``, the masses of all layers
+    added once; then, with ``turn``, the side-car update and selection. One
+    library call: the same launches and results as the per-layer calls,
+    tap_masses and update_sidecar(_select)."""
+    L = len(caches)
+    if L < 1 or not (len(q_layers) == len(outs) == len(workspaces) == L):
+        raise ValueError("one query, output and workspace per layer")
+    if (k_new is None) != (v_new is None) or (k_new is not None and (len(k_new) != L or len(v_new) != L)):
+        raise ValueError("k_new and v_new: both None or one row tensor per layer each")
+    g = caches[0].geom
+    qdt = TORCH_DTYPES[g.q_dtype]
+    qshape = (g.batch, g.n_q_heads, g.head_dim)
+    rshape = (g.batch, g.n_kv_heads * g.head_dim)
+    if cur_pos.device.type != "cuda" or cur_pos.dtype != torch.int32 or cur_pos.numel() != g.batch:
+        raise ValueError("cur_pos must be an int32 [B] device tensor")
+    if keep_mask is not None and (keep_mask.device.type != "cuda" or keep_mask.dtype != torch.int32
+                                  or keep_mask.numel() != g.batch * g.words):
+        raise ValueError("keep_mask must be int32 (bit words) [B, W]")
+    if mass_accum is not None and (mass_accum.device.type != "cuda" or mass_accum.dtype != torch.float32
+                                   or mass_accum.numel() != g.batch * g.nb):
+        raise ValueError("mass_accum must be float32 [B, NBmax]")
+    src = KVS_F32
+    if k_new is not None:
+        src = {torch.float32: KVS_F32, torch.bfloat16: KVS_BF16}.get(k_new[0].dtype)
+        if src is None:
+            raise TypeError("new rows must be float32 or bfloat16")
+    arr = (LayerBufs * L)()
+    ws_bytes = None
+    for l in range(L):
+        c, q, o, w = caches[l], q_layers[l], outs[l], workspaces[l]
+        if c.geom != g:
+            raise ValueError("every layer's cache must have the same geometry")
+        for t in (q, o, w):
+            if t.device.type != "cuda" or not t.is_contiguous():
+                raise ValueError("q, out and workspace must be contiguous device tensors")
+        if q.dtype != qdt or o.dtype != qdt or q.shape != qshape or o.shape != qshape:
+            raise ValueError("q and out must be [B, Hq, d] of the geometry's q dtype")
+        b = arr[l]
+        b.q, b.out, b.workspace = q.data_ptr(), o.data_ptr(), w.data_ptr()
+        nbytes = w.numel() * w.element_size()
+        ws_bytes = nbytes if ws_bytes is None else min(ws_bytes, nbytes)
+        b.k_cache, b.v_cache = c.k.data_ptr(), c.v.data_ptr()
+        b.k_scale = c.k_scale.data_ptr() if c.k_scale is not None else None
+        b.v_scale = c.v_scale.data_ptr() if c.v_scale is not None else None
+        b.pos_of_slot = c.pos_of_slot.data_ptr() if c.pos_of_slot is not None else None
+        if k_new is not None:
+            kn, vn = k_new[l], v_new[l]
+            for t in (kn, vn):
+                if t.device.type != "cuda" or not t.is_contiguous() or t.shape != rshape \
+                        or t.dtype != k_new[0].dtype:
+                    raise ValueError("new rows must be contiguous [B, Hkv*d] device tensors of one dtype")
+            b.k_new, b.v_new = kn.data_ptr(), vn.data_ptr()
+    targs = None
+    if turn is not None:
+        if mass_accum is None:
+            raise ValueError("closing the turn needs mass_accum")
+        targs = ctypes.byref(_turn_args(turn, g.batch, g.nb))
+    _check(LIB.kvs_decode_step(ctypes.byref(g.c()), L, arr, src, _ptr(cur_pos), _ptr(keep_mask), ws_bytes,
+                               _ptr(mass_accum), targs, _stream(stream)), "kvs_decode_step")
 
 
 def decode_attn_profiled(cache: KVCache, q: torch.Tensor, cur_pos: torch.Tensor, out: torch.Tensor,

@@ -399,8 +399,15 @@ int kvs_append_decode_attn_tap(const kvs_geom* g, const void* k_new, const void*
   return hip_status(kvs::launch_partial(kv, g->head_dim, a, true, g->ring != 0, p.lds_partial, s));
 }
 
-int kvs_tap_masses(const kvs_geom* g, void* const* workspaces, int32_t n_layers, size_t workspace_bytes,
-                   const int32_t* cur_pos, float* mass_accum, float* head_mass, float* mass_max, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks and arguments of kvs_tap_masses; *parallel: the layer-parallel
+// combine applies.
+int tap_setup(const kvs_geom* g, void* const* workspaces, int32_t n_layers, size_t workspace_bytes,
+              const int32_t* cur_pos, float* mass_accum, float* head_mass, float* mass_max,
+              kvs::CombineArgs* cp, bool* parallel) {
   int st = check_geom(g);
   if (st) return st;
   if (n_layers < 1 || n_layers > kvs::kMaxTapLayers || !workspaces || !cur_pos) return KVS_EINVAL;
@@ -409,7 +416,8 @@ int kvs_tap_masses(const kvs_geom* g, void* const* workspaces, int32_t n_layers,
     if (ptr && !aligned16(ptr)) return KVS_EALIGN;
   const Plan p = make_plan(g);
   if (workspace_bytes < p.total) return KVS_EWS;
-  kvs::CombineArgs c{};
+  kvs::CombineArgs& c = *cp;
+  c = kvs::CombineArgs{};
   for (int l = 0; l < n_layers; ++l) {
     if (!workspaces[l]) return KVS_EINVAL;
     if (!aligned16(workspaces[l])) return KVS_EALIGN;
@@ -428,10 +436,27 @@ int kvs_tap_masses(const kvs_geom* g, void* const* workspaces, int32_t n_layers,
   c.n_mass_chunks = (p.NT + 255) / 256;
   // without per-head masses, and when every layer's tables fit the LDS at
   // once, the layers are summed in parallel (same values, bit for bit)
-  if (!head_mass && kvs::combine_layers_lds_bytes(g->n_q_heads, g->n_kv_heads, p.nparts, n_layers, g->ring != 0) <=
-                        kvs::kCombineLdsBytes)
-    return hip_status(kvs::launch_combine_layers(c, g->ring != 0, (hipStream_t)stream));
-  return hip_status(kvs::launch_combine(c, g->ring != 0, (hipStream_t)stream));
+  *parallel = !head_mass && kvs::combine_layers_lds_bytes(g->n_q_heads, g->n_kv_heads, p.nparts, n_layers,
+                                                          g->ring != 0) <= kvs::kCombineLdsBytes;
+  return KVS_OK;
+}
+
+hipError_t launch_tap(const kvs::CombineArgs& c, bool parallel, bool ring, hipStream_t s) {
+  return parallel ? kvs::launch_combine_layers(c, ring, s) : kvs::launch_combine(c, ring, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvs_tap_masses(const kvs_geom* g, void* const* workspaces, int32_t n_layers, size_t workspace_bytes,
+                   const int32_t* cur_pos, float* mass_accum, float* head_mass, float* mass_max, void* stream) {
+  kvs::CombineArgs c;
+  bool parallel = false;
+  const int st = tap_setup(g, workspaces, n_layers, workspace_bytes, cur_pos, mass_accum, head_mass, mass_max, &c,
+                           &parallel);
+  if (st) return st;
+  return hip_status(launch_tap(c, parallel, g->ring != 0, (hipStream_t)stream));
 }
 
 int kvs_reattend_blocks(const kvs_geom* g, const void* q, const void* k_cache, const void* v_cache,
@@ -458,15 +483,31 @@ int kvs_reattend_blocks(const kvs_geom* g, const void* q, const void* k_cache, c
   return hip_status(kvs::launch_combine(c, false, s));
 }
 
-int kvs_update_sidecar(float* mass_accum, float* attended, float* ema, float* cum, float* traj,
-                       int32_t batch, int32_t n_blocks_max, int32_t traj_cap, int64_t step,
-                       float alpha, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int sidecar_check(const float* mass_accum, const float* attended, const float* ema, const float* cum,
+                  const float* traj, int32_t batch, int32_t n_blocks_max, int32_t traj_cap, int64_t step,
+                  float alpha) {
   if (batch < 1 || n_blocks_max < 1 || traj_cap < 1 || step < 0) return KVS_EINVAL;
   if (!(alpha >= 0.0f && alpha <= 1.0f)) return KVS_EINVAL;
   if (!mass_accum || !attended || !ema || !cum) return KVS_EINVAL;
   const void* ptrs[] = {mass_accum, attended, ema, cum, traj};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return KVS_EALIGN;
+  return KVS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvs_update_sidecar(float* mass_accum, float* attended, float* ema, float* cum, float* traj,
+                       int32_t batch, int32_t n_blocks_max, int32_t traj_cap, int64_t step,
+                       float alpha, void* stream) {
+  const int st = sidecar_check(mass_accum, attended, ema, cum, traj, batch, n_blocks_max, traj_cap, step, alpha);
+  if (st) return st;
   return hip_status(kvs::launch_sidecar(mass_accum, attended, ema, cum, traj, batch, n_blocks_max,
                                         traj_cap, step, alpha, (hipStream_t)stream));
 }
@@ -623,12 +664,15 @@ int kvs_stream_read(const void* buf, size_t bytes, uint32_t* sums, int32_t workg
   return hip_status(kvs::launch_stream_read(buf, bytes, sums, workgroups, (hipStream_t)stream));
 }
 
-int kvs_update_sidecar_select(float* mass_accum, float* attended, float* ema, float* cum, float* traj,
-                              int32_t batch, int32_t n_blocks_max, int32_t traj_cap, int64_t step,
-                              float alpha, int32_t score_source, const uint32_t* alive,
-                              const int32_t* cur_pos, int32_t budget_blocks, int32_t recent_tokens,
-                              int32_t sink_tokens, uint32_t* keep_mask, int32_t* sel_ids, int32_t* n_sel,
-                              void* stream) {
+}  // extern "C"
+
+namespace {
+
+int sidecar_select_setup(float* mass_accum, float* attended, float* ema, float* cum, float* traj,
+                         int32_t batch, int32_t n_blocks_max, int32_t traj_cap, int64_t step, float alpha,
+                         int32_t score_source, const uint32_t* alive, const int32_t* cur_pos,
+                         int32_t budget_blocks, int32_t recent_tokens, int32_t sink_tokens, uint32_t* keep_mask,
+                         int32_t* sel_ids, int32_t* n_sel, kvs::SelectArgs* out) {
   if (batch < 1 || n_blocks_max < 1 || traj_cap < 1 || step < 0) return KVS_EINVAL;
   if (!(alpha >= 0.0f && alpha <= 1.0f)) return KVS_EINVAL;
   if (score_source < KVS_SCORE_CUMULATIVE || score_source > KVS_SCORE_ATTENDED) return KVS_EINVAL;
@@ -644,7 +688,100 @@ int kvs_update_sidecar_select(float* mass_accum, float* attended, float* ema, fl
   a.budget = budget_blocks; a.recent = recent_tokens; a.sinks = sink_tokens;
   a.mass = mass_accum; a.att = attended; a.ema = ema; a.cum = cum; a.traj = traj;
   a.traj_cap = traj_cap; a.slot = (int)(step % traj_cap); a.alpha = alpha; a.score_src = score_source;
+  *out = a;
+  return KVS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvs_update_sidecar_select(float* mass_accum, float* attended, float* ema, float* cum, float* traj,
+                              int32_t batch, int32_t n_blocks_max, int32_t traj_cap, int64_t step,
+                              float alpha, int32_t score_source, const uint32_t* alive,
+                              const int32_t* cur_pos, int32_t budget_blocks, int32_t recent_tokens,
+                              int32_t sink_tokens, uint32_t* keep_mask, int32_t* sel_ids, int32_t* n_sel,
+                              void* stream) {
+  kvs::SelectArgs a;
+  const int st = sidecar_select_setup(mass_accum, attended, ema, cum, traj, batch, n_blocks_max, traj_cap, step,
+                                      alpha, score_source, alive, cur_pos, budget_blocks, recent_tokens,
+                                      sink_tokens, keep_mask, sel_ids, n_sel, &a);
+  if (st) return st;
   return hip_status(kvs::launch_select(a, (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// The arguments of layer l's partial launch in kvs_decode_step.
+int step_layer_setup(const kvs_geom* g, const kvs_layer_bufs& L, int32_t src_dtype, const int32_t* cur_pos,
+                     const uint32_t* keep_mask, size_t workspace_bytes, Plan* p, kvs::PartialArgs* a, int* kv) {
+  kvs::CombineArgs unused;
+  int st = decode_setup(g, L.q, L.k_cache, L.v_cache, L.k_scale, L.v_scale, L.pos_of_slot, cur_pos, keep_mask, L.out,
+                        nullptr, L.workspace, workspace_bytes, p, a, &unused, kv);
+  if (st) return st;
+  if ((L.k_new == nullptr) != (L.v_new == nullptr)) return KVS_EINVAL;
+  return L.k_new ? append_args(g, L.k_new, L.v_new, src_dtype, a) : KVS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+// One whole decode step: every check first (layer by layer), then the
+// launches, each layer's arguments set up again (a few integer operations)
+// rather than kept, so the call needs no storage.
+int kvs_decode_step(const kvs_geom* g, int32_t n_layers, const kvs_layer_bufs* layers, int32_t src_dtype,
+                    const int32_t* cur_pos, const uint32_t* keep_mask, size_t workspace_bytes,
+                    float* mass_accum, const kvs_turn_args* turn, void* stream) {
+  if (!g || !layers || n_layers < 1 || n_layers > kvs::kMaxTapLayers) return KVS_EINVAL;
+  void* ws[kvs::kMaxTapLayers];
+  for (int l = 0; l < n_layers; ++l) {
+    Plan p;
+    kvs::PartialArgs a;
+    int kv;
+    const int st = step_layer_setup(g, layers[l], src_dtype, cur_pos, keep_mask, workspace_bytes, &p, &a, &kv);
+    if (st) return st;
+    ws[l] = layers[l].workspace;
+  }
+  // without mass_accum the block sums stay in the workspaces (for a later
+  // kvs_tap_masses) and there is no turn to close
+  if (!mass_accum && turn) return KVS_EINVAL;
+  kvs::CombineArgs c;
+  bool parallel = false;
+  int st = mass_accum ? tap_setup(g, ws, n_layers, workspace_bytes, cur_pos, mass_accum, nullptr, nullptr, &c,
+                                  &parallel)
+                      : KVS_OK;
+  if (st) return st;
+  kvs::SelectArgs sa{};
+  if (turn) {
+    if (turn->select != 0 && turn->select != 1) return KVS_EINVAL;
+    if (turn->select) {
+      st = sidecar_select_setup(mass_accum, turn->attended, turn->ema, turn->cum, turn->traj, g->batch,
+                                g->n_blocks_max, turn->traj_cap, turn->step, turn->alpha, turn->score_source,
+                                turn->alive, cur_pos, turn->budget_blocks, turn->recent_tokens, turn->sink_tokens,
+                                turn->keep_out, turn->sel_ids, turn->n_sel, &sa);
+    } else {
+      st = sidecar_check(mass_accum, turn->attended, turn->ema, turn->cum, turn->traj, g->batch, g->n_blocks_max,
+                         turn->traj_cap, turn->step, turn->alpha);
+    }
+    if (st) return st;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  for (int l = 0; l < n_layers; ++l) {
+    Plan p;
+    kvs::PartialArgs a;
+    int kv;
+    step_layer_setup(g, layers[l], src_dtype, cur_pos, keep_mask, workspace_bytes, &p, &a, &kv);
+    if (kvs::launch_partial(kv, g->head_dim, a, true, g->ring != 0, p.lds_partial, s) != hipSuccess) return KVS_EHIP;
+  }
+  if (!mass_accum) return KVS_OK;
+  if (launch_tap(c, parallel, g->ring != 0, s) != hipSuccess) return KVS_EHIP;
+  if (!turn) return KVS_OK;
+  if (turn->select) return hip_status(kvs::launch_select(sa, s));
+  return hip_status(kvs::launch_sidecar(mass_accum, turn->attended, turn->ema, turn->cum, turn->traj, g->batch,
+                                        g->n_blocks_max, turn->traj_cap, turn->step, turn->alpha, s));
 }
 
 }  // extern "C"

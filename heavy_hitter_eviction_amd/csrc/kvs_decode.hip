@@ -166,21 +166,48 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   const uint64_t clk0 = __builtin_amdgcn_s_memrealtime();
   const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int wg_id = part + a.nparts * (g + a.Hkv * b);  // dispatch order: XCD = id mod 8
-  // fused append: the appending wave fetches the first 512 values of the new
-  // K and V rows right away (their address needs no cur_pos); it is decided
-  // further down whether this workgroup appends at all
+  // fused append: the appending wave fetches the new K and V rows right away
+  // (their address needs no cur_pos), before any tile load, so the append
+  // never waits behind its own tile loads (vector loads complete in order);
+  // it is decided further down whether this workgroup appends at all. FP8
+  // takes the scale from the whole row: values 8 lane .. 8 lane + 7 (and, for
+  // bf16 rows, 512 + 8 lane ..) come here, the rest in the append itself.
+  // This KV head's values (dims lane, lane + 64) come separately.
   const int app_n = a.Hkv * D;
   const size_t app_rb = (size_t)b * app_n;
-  u32x4 app_k0[2], app_v0[2];  // 8 values per lane: bf16 in [0], f32 in [0..1]
-  if (KV == KV_FP8 && a.app_k != nullptr && wave == NW - 1 && 8 * lane < app_n) {
-    if (a.app_bf16) {
-      app_k0[0] = *(const u32x4*)((const uint16_t*)a.app_k + app_rb + 8 * lane);
-      app_v0[0] = *(const u32x4*)((const uint16_t*)a.app_v + app_rb + 8 * lane);
-    } else {
+  constexpr int XPL = D > 64 ? D / 64 : 1;  // appended dims per lane
+  u32x4 app_k0[2], app_v0[2];  // bf16 rows: [r] holds values 512 r + 8 lane ..; f32 rows: [0..1] values 8 lane ..
+  uint32_t app_hk[XPL], app_hv[XPL];  // this head's values as stored in the row (bf16 or f32 bits)
+  const bool app_wave = a.app_k != nullptr && wave == NW - 1;
+  if (app_wave) {
+    if constexpr (KV == KV_FP8) {
+      if (a.app_bf16) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        app_k0[c] = *(const u32x4*)((const float*)a.app_k + app_rb + 8 * lane + 4 * c);
-        app_v0[c] = *(const u32x4*)((const float*)a.app_v + app_rb + 8 * lane + 4 * c);
+        for (int r = 0; r < 2; ++r) {
+          if (512 * r + 8 * lane < app_n) {
+            app_k0[r] = *(const u32x4*)((const uint16_t*)a.app_k + app_rb + 512 * r + 8 * lane);
+            app_v0[r] = *(const u32x4*)((const uint16_t*)a.app_v + app_rb + 512 * r + 8 * lane);
+          }
+        }
+      } else if (8 * lane < app_n) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          app_k0[c] = *(const u32x4*)((const float*)a.app_k + app_rb + 8 * lane + 4 * c);
+          app_v0[c] = *(const u32x4*)((const float*)a.app_v + app_rb + 8 * lane + 4 * c);
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < XPL; ++c) {
+      const int x = lane + 64 * c;
+      if (x >= D) continue;
+      const size_t i = app_rb + (size_t)g * D + x;
+      if (KV == KV_F32 || !a.app_bf16) {
+        app_hk[c] = ((const uint32_t*)a.app_k)[i];
+        app_hv[c] = ((const uint32_t*)a.app_v)[i];
+      } else {
+        app_hk[c] = ((const uint16_t*)a.app_k)[i];
+        app_hv[c] = ((const uint16_t*)a.app_v)[i];
       }
     }
   }
@@ -208,14 +235,27 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   // before)
   const bool use_rates = !RING && a.dyn && a.adapt && a.rates != nullptr;
   const float r_lane = use_rates && lane < 8 ? a.rates[lane] : 1.0f;
-  const int i_cur = __builtin_amdgcn_readfirstlane(a.cur_pos[b]);  // uniform, as are the tile offsets from it
+  // The current position. A linear cache's partition range depends on it: a
+  // vector load, waited for together with the rates. A ring's does not, so a
+  // ring reads it once its first tile loads are out, with a scalar load
+  // (a wait counter of its own, so it does not wait for those tiles).
+  int i_cur = RING ? 0 : __builtin_amdgcn_readfirstlane(a.cur_pos[b]);
   float wcls[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     const float r = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r_lane), c));
     wcls[c] = (r >= 0.5f && r <= 2.0f) ? fminf(fmaxf(r, 1.0f / 1.2f), 1.2f) : 1.0f;  // NaN -> 1
   }
-  const int lo = a.window > 0 ? i_cur - a.window + 1 : (int)0x80000000;
+  // from the position: the first readable one (window) and the slot this
+  // call appends (the workgroup whose tiles hold it writes this KV head's
+  // part of the row there before anyone reads that tile)
+  int lo = 0, app_cand = -1, app_cand_tile = -1;
+  auto set_position = [&]() {
+    lo = a.window > 0 ? i_cur - a.window + 1 : (int)0x80000000;
+    app_cand = (a.app_k != nullptr && i_cur >= 0 && (RING || i_cur < a.C)) ? (RING ? i_cur % a.C : i_cur) : -1;
+    app_cand_tile = app_cand >= 0 ? app_cand / kTile : -1;
+  };
+  if constexpr (!RING) set_position();
   const int cls0 = (a.nparts * (g + a.Hkv * b)) & 7;  // class of partition 0
   // weight of partitions [0, k): partition q belongs to class (cls0 + q) mod 8
   auto wprefix = [&](int k) -> float {
@@ -256,11 +296,6 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
     t0 = __builtin_amdgcn_readfirstlane(gtb + split_at(part, gte - gtb));
     t1 = __builtin_amdgcn_readfirstlane(gtb + split_at(part + 1, gte - gtb));
   }
-
-  // Fused append: the workgroup whose tiles hold the new position's slot
-  // writes this KV head's part of the row there before anyone reads that tile.
-  const int app_cand = (a.app_k != nullptr && i_cur >= 0 && (RING || i_cur < a.C)) ? (RING ? i_cur % a.C : i_cur) : -1;
-  const int app_cand_tile = app_cand >= 0 ? app_cand / kTile : -1;
 
   // LDS carve-up (16-byte aligned parts first): per-wave side data (FP8
   // scales, ring positions of the claimed tiles), the appended row of this KV
@@ -403,8 +438,9 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   }
   // Tiles that can hold a readable key.
   const int tb = t0, te = t1;
-  const int app_slot = (app_cand_tile >= tb && app_cand_tile < te) ? app_cand : -1;
-  const int app_tile = app_slot >= 0 ? app_cand_tile : -1;
+  // the appended slot if this workgroup's tiles hold it (set once the
+  // position is known)
+  int app_slot = -1, app_tile = -1;
   // uniform (readfirstlane): the tile offsets derived from these are scalar
   // operands of the buffer loads, which the compiler would otherwise wrap in
   // a per-lane loop
@@ -470,8 +506,7 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
 
   // Ring laps: positions read at step i lie in [i - C + 1, i], so at most two
   // laps (i / C and i / C - 1) share a tile; their parity names the sub-block.
-  const int lap_i = RING ? i_cur / a.C : 0;
-  const int lap_base = lap_i * a.C;
+  int lap_i = 0, lap_base = 0;  // (set with the position)
 
   TileAddr ad;
   {
@@ -498,8 +533,10 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   u32x4 pf = {0u, 0u, 0u, 0u};
   auto gather = [&](int bi) {
     if constexpr (SIDE) {
-      const int e = min(BATCH * bi + lane / QPT, n_items - 1);  // clamped: always a real slot
-      const int t = use_list ? tlist[e] : tb + e;
+      // clamped to a real slot, also for a batch past the list (the first
+      // batch is requested unconditionally)
+      const int e = max(0, min(BATCH * bi + lane / QPT, n_items - 1));
+      const int t = min(max(use_list ? tlist[e] : tb + e, 0), a.NT - 1);
       const int q = lane % QPT;
       const size_t base = (size_t)t * kTile;
       const void* src;
@@ -529,7 +566,7 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   // lane % 16 == t (16 bytes per chunk); V of slot t in the 16 lanes of group
   // t / 4, interleaved with the three other slots of the group (element n of
   // dim group j at byte (4 n + t % 4) eb of its chunk).
-  const int app_ts = app_slot & (kTile - 1);
+  int app_ts = 0;
   auto patch_appended = [&](TileRegs<KV, D>& t, f32x4& ks, f32x4& vs, int4& cpos) {
     while (__hip_atomic_load(&misc[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
       __builtin_amdgcn_s_sleep(1);
@@ -790,10 +827,10 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
       float mk = 0.0f, mv = 0.0f;
       for (int i = 8 * lane; i < n; i += 8 * 64) {  // 8 values per lane and load (n % 8 == 0)
         float xk[8], xv[8];
-        const bool pre = i < 512;  // fetched at kernel entry
+        const bool pre = i < (sbf ? 1024 : 512);  // fetched at kernel entry
         if (sbf) {
-          const u32x4 wk = pre ? app_k0[0] : *(const u32x4*)((const uint16_t*)a.app_k + rb + i);
-          const u32x4 wv = pre ? app_v0[0] : *(const u32x4*)((const uint16_t*)a.app_v + rb + i);
+          const u32x4 wk = pre ? app_k0[i >= 512] : *(const u32x4*)((const uint16_t*)a.app_k + rb + i);
+          const u32x4 wv = pre ? app_v0[i >= 512] : *(const u32x4*)((const uint16_t*)a.app_v + rb + i);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             xk[2 * e] = bf16_lo(wk[e]);
@@ -827,29 +864,30 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
       sv = fp8_scale_of(mv);
     }
     // this KV head's values as the cache holds them (codes, bf16 or f32
-    // bits), dims lane and lane + 64: first into LDS for the waves that read
-    // the tile in this call (they patch the slot from there), then the flag,
-    // then the cache writes, which no wave of this call waits for
-    constexpr int XPL = D > 64 ? D / 64 : 1;  // dims per lane
+    // bits), dims lane and lane + 64, from the values fetched at entry: first
+    // into LDS for the waves that read the tile in this call (they patch the
+    // slot from there), then the flag, then the cache writes, which no wave
+    // of this call waits for
     uint32_t kbits[XPL], vbits[XPL];
 #pragma unroll
     for (int c = 0; c < XPL; ++c) {
       const int x = lane + 64 * c;
       if (x >= D) continue;
-      const size_t i = rb + (size_t)g * D + x;
       if constexpr (KV == KV_FP8) {
-        kbits[c] = encode_with_scale(load_src(a.app_k, i, sbf), sk);
-        vbits[c] = encode_with_scale(load_src(a.app_v, i, sbf), sv);
+        const float xk = sbf ? bf16_lo(app_hk[c]) : bits_to_f32(app_hk[c]);
+        const float xv = sbf ? bf16_lo(app_hv[c]) : bits_to_f32(app_hv[c]);
+        kbits[c] = encode_with_scale(xk, sk);
+        vbits[c] = encode_with_scale(xv, sv);
         app_lds[x] = (uint8_t)kbits[c];
         app_lds[D + x] = (uint8_t)vbits[c];
       } else if constexpr (KV == KV_BF16) {
-        kbits[c] = ((const uint16_t*)a.app_k)[i];
-        vbits[c] = ((const uint16_t*)a.app_v)[i];
+        kbits[c] = app_hk[c];
+        vbits[c] = app_hv[c];
         ((uint16_t*)app_lds)[x] = (uint16_t)kbits[c];
         ((uint16_t*)app_lds)[D + x] = (uint16_t)vbits[c];
       } else {
-        kbits[c] = ((const uint32_t*)a.app_k)[i];
-        vbits[c] = ((const uint32_t*)a.app_v)[i];
+        kbits[c] = app_hk[c];
+        vbits[c] = app_hv[c];
         ((uint32_t*)app_lds)[x] = kbits[c];
         ((uint32_t*)app_lds)[D + x] = vbits[c];
       }
@@ -895,14 +933,26 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   // First batch of this wave: its own index, its side data and first tiles
   // requested before the workgroup's first barrier (without a keep list),
   // the batch holding the appended slot too (the slot is patched from LDS).
+  // They are requested even when the wave has no batch (side data of a real
+  // slot, tile loads past the buffer's range: zeros without a memory
+  // access): a conditional request would make the compiler's wait counts
+  // assume the shorter queue, so the append below would wait for these
+  // tiles instead of only for the row fetched at entry.
   TileRegs<KV, D> buf[NBUF];
   int cur = wave;
   ++n_claimed;
-  if (cur < n_batches) {
-    gather(cur);
+  gather(cur);
 #pragma unroll
-    for (int i = 0; i < NBUF - 1; ++i) load_tile<KV, D, RING>(buf[i], ad, soff_of(cur, i));
+  for (int i = 0; i < NBUF - 1; ++i) load_tile<KV, D, RING>(buf[i], ad, soff_of(cur, i));
+  if constexpr (RING) {
+    i_cur = scalar_load_i32(a.cur_pos + b);
+    set_position();
+    lap_i = i_cur / a.C;
+    lap_base = lap_i * a.C;
   }
+  app_slot = (app_cand_tile >= tb && app_cand_tile < te) ? app_cand : -1;
+  app_tile = app_slot >= 0 ? app_cand_tile : -1;
+  app_ts = app_slot & (kTile - 1);
   // the claim counter and the append flag are initialised (with a keep list
   // the list's barrier has seen to that)
   if (!use_list) __syncthreads();

@@ -87,11 +87,38 @@ class ScoredDecoder:
     def step(self, q_layers, k_layers, v_layers, cur_pos: torch.Tensor):
         """One decode step. ``q_layers[l]`` is [B, Hq, d]; ``k_layers[l]`` and
         ``v_layers[l]`` are the new position's rows [B, Hkv*d]; ``cur_pos`` is
-        the int32 [B] absolute position being written and read."""
+        the int32 [B] absolute position being written and read. Fused tap
+        mode makes it one library call (kvs_decode_step)."""
+        if self.fused and self.tap:
+            api.decode_step(self.caches, q_layers, cur_pos, self.out, self.workspaces, k_new=k_layers,
+                            v_new=v_layers, keep_mask=self._attn_keep(), mass_accum=self.mass,
+                            turn=self.turn_args())
+            self.step_index += 1
+            return
         for l in range(self.n_layers):
             self.append_attend_layer(l, q_layers[l], k_layers[l], v_layers[l], cur_pos)
         self.finish_masses(cur_pos)
         self.close_turn(cur_pos)
+
+    def attend_layers(self, q_layers, k_layers, v_layers, cur_pos: torch.Tensor):
+        """Fused tap mode: every layer's append and scored attention in one
+        library call, the block sums left in the layers' workspaces; the step
+        goes on with ``finish_masses`` and ``close_turn``."""
+        if not (self.fused and self.tap):
+            raise RuntimeError("attend_layers needs fused tap mode")
+        api.decode_step(self.caches, q_layers, cur_pos, self.out, self.workspaces, k_new=k_layers,
+                        v_new=v_layers, keep_mask=self._attn_keep())
+
+    def _attn_keep(self):
+        return self.keep if (self.evict and not self.w.window) else None
+
+    def turn_args(self) -> api.Turn:
+        """The side-car (and selection) arguments closing the current turn."""
+        w = self.w
+        return api.Turn(self.attended, self.ema, self.cum, self.traj, step=self.step_index, alpha=w.alpha,
+                        select=bool(w.select), budget_blocks=w.budget_blocks, recent_tokens=w.recent_tokens,
+                        sink_tokens=w.sink_tokens, alive=self.keep if self.evict else None,
+                        keep_out=self.keep, sel_ids=self.sel_ids, n_sel=self.n_sel)
 
     def capture_step(self, q_layers, k_layers, v_layers, cur_pos: torch.Tensor, step_index: int | None = None,
                      split: bool = False):
@@ -112,8 +139,11 @@ class ScoredDecoder:
             self.step_index = idx
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                for l in range(self.n_layers):
-                    self.append_attend_layer(l, q_layers[l], k_layers[l], v_layers[l], cur_pos)
+                if self.fused and self.tap:
+                    self.attend_layers(q_layers, k_layers, v_layers, cur_pos)
+                else:
+                    for l in range(self.n_layers):
+                        self.append_attend_layer(l, q_layers[l], k_layers[l], v_layers[l], cur_pos)
                 if not split:
                     self.finish_masses(cur_pos)
                     self.close_turn(cur_pos)

@@ -589,6 +589,81 @@ KVS_API int kvs_update_sidecar_select(float* mass_accum, float* attended, float*
                                       int32_t* n_sel, void* stream);
 
 /*
+ * kvs_decode_step -- one whole scored decode step in one call: for every
+ * layer the append of the new position and the scored attention, then the
+ * block masses of all layers added once, then the turn's side-car update (and
+ * the heavy-hitter selection). It is the per-turn loop of Context views at
+ * marginal cost (Tier 0: the tap during the forward pass; section 2: the
+ * side-car updated once per turn from the summed masses) with the selection
+ * of Context Optimization, "H2O KV Cache Eviction" (steps 2 and 3), made by
+ * the library instead of by one host call per layer: the launches and every
+ * result are exactly those of
+ *   for l in 0 .. n_layers - 1:
+ *     kvs_append_decode_attn_tap(geom, layers[l].k_new, layers[l].v_new,
+ *         src_dtype, layers[l].q, layers[l].k_cache, ..., cur_pos, keep_mask,
+ *         layers[l].out, layers[l].workspace, workspace_bytes, stream)
+ *     (kvs_decode_attn_tap when layers[l].k_new is NULL: nothing appended)
+ *   if mass_accum: kvs_tap_masses(geom, {layers[l].workspace}, n_layers,
+ *                  workspace_bytes, cur_pos, mass_accum, NULL, NULL, stream)
+ *   if turn: kvs_update_sidecar_select(mass_accum, turn->attended, ...,
+ *            geom->batch, geom->n_blocks_max, ...) when turn->select is 1,
+ *            else kvs_update_sidecar(mass_accum, turn->attended, ...).
+ *
+ *   layers      HOST array of n_layers kvs_layer_bufs (1 <= n_layers <= 128);
+ *               the pointers in it are device pointers, as in the calls above;
+ *               every layer has its own workspace (workspace_bytes each)
+ *   src_dtype   KVS_F32 or KVS_BF16: the new rows' dtype (as in
+ *               kvs_append_decode_attn_tap)
+ *   cur_pos, keep_mask: shared by all layers, as in the per-layer calls
+ *   mass_accum  [B][NBmax] float32 the masses are added into (read by the
+ *               side-car), or NULL: the layers only, their block sums left
+ *               in the workspaces for a later kvs_tap_masses (turn must then
+ *               be NULL)
+ *   turn        HOST pointer to the turn's arguments, or NULL: no side-car
+ *               update. turn->alive may be turn->keep_out (evict mode feeds
+ *               the mask back); the trajectory slot is turn->step mod traj_cap.
+ * The library keeps no pointer after the call returns. Errors: those of the
+ * calls above; every argument of every layer is checked before the first
+ * launch, so an error launches nothing.
+ */
+typedef struct kvs_layer_bufs {
+  const void* q;          /* [B][Hq][d], the geometry's q dtype */
+  const void* k_new;      /* [B][Hkv*d] new K row of each sequence, src_dtype; NULL: no append */
+  const void* v_new;      /* [B][Hkv*d] new V row; NULL exactly when k_new is */
+  void* k_cache;
+  void* v_cache;
+  float* k_scale;         /* FP8 caches only, else NULL */
+  float* v_scale;
+  int32_t* pos_of_slot;   /* ring caches only, else NULL */
+  void* out;              /* [B][Hq][d] */
+  void* workspace;        /* this layer's decode workspace */
+} kvs_layer_bufs;
+
+typedef struct kvs_turn_args {
+  float* attended;        /* [B][NBmax] side-car arrays, as in kvs_update_sidecar */
+  float* ema;
+  float* cum;
+  float* traj;            /* [B][traj_cap][NBmax], or NULL */
+  int32_t traj_cap;
+  int32_t select;         /* 1: update and select in one launch; 0: update only */
+  int64_t step;           /* the turn index */
+  float alpha;            /* EMA weight in [0, 1] */
+  int32_t score_source;   /* KVS_SCORE_*, with select */
+  const uint32_t* alive;  /* [B][W] or NULL, with select */
+  int32_t budget_blocks;  /* with select, as in kvs_select_blocks */
+  int32_t recent_tokens;
+  int32_t sink_tokens;
+  uint32_t* keep_out;     /* [B][W] keep mask written by the selection */
+  int32_t* sel_ids;       /* [B][NBmax] */
+  int32_t* n_sel;         /* [B] */
+} kvs_turn_args;
+
+KVS_API int kvs_decode_step(const kvs_geom* geom, int32_t n_layers, const kvs_layer_bufs* layers,
+                            int32_t src_dtype, const int32_t* cur_pos, const uint32_t* keep_mask,
+                            size_t workspace_bytes, float* mass_accum, const kvs_turn_args* turn,
+                            void* stream);
+
+/*
  * kvs_stream_read -- a measurement helper, not part of the decode step: the
  * streaming-read ceiling that the decode kernel's KV scan is compared with
  * (Context views at marginal cost, section 7, Fact 3: the read of the cached

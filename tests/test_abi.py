@@ -300,3 +300,89 @@ def test_stream_read_rejects_bad_arguments():
     assert f(P(0x1000), 2048, P(0x2000), 3, None) == api.KVS_EINVAL          # fewer runs than workgroups
     assert f(P(0x1000), 2048, P(0x2000), 0, None) == api.KVS_EINVAL
     assert f(P(0x1008), 2048, P(0x2000), 1, None) == api.KVS_EALIGN
+
+
+def test_decode_step_structs_match_the_header(tmp_path):
+    """kvs_layer_bufs and kvs_turn_args as the C compiler lays them out
+    (sizes and field offsets) equal the binding's ctypes mirrors."""
+    import shutil
+    import subprocess
+    api = _lib()
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    fields = {"kvs_layer_bufs": api.LayerBufs, "kvs_turn_args": api.TurnArgs}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "kvs.h"', "int main(void) {"]
+    for cname, cls in fields.items():
+        lines.append(f'  printf("{cname} %zu\\n", sizeof({cname}));')
+        for f, _ in cls._fields_:
+            lines.append(f'  printf("{cname}.{f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c99", f"-I{os.path.join(ROOT, 'include')}", str(src), "-o", str(exe)], check=True)
+    out = dict(line.split() for line in subprocess.run([str(exe)], check=True, capture_output=True,
+                                                       text=True).stdout.splitlines())
+    for cname, cls in fields.items():
+        assert int(out[cname]) == ctypes.sizeof(cls), cname
+        for f, _ in cls._fields_:
+            assert int(out[f"{cname}.{f}"]) == getattr(cls, f).offset, f"{cname}.{f}"
+
+
+def test_decode_step_rejects_bad_arguments():
+    """kvs_decode_step: every layer's checks, the mass and turn checks, all
+    before the first launch (a bad last layer is reported, not launched
+    around); every call below fails one check."""
+    api = _lib()
+    L = api.LIB
+    vp = ctypes.c_void_p
+    g = _geom(api)                                         # bf16 linear cache, 16 blocks
+
+    def layer(**kw):
+        d = dict(q=0x1000, k_new=0x8000, v_new=0x9000, k_cache=0x2000, v_cache=0x3000, k_scale=None,
+                 v_scale=None, pos_of_slot=None, out=0x5000, workspace=0x7000)
+        d.update(kw)
+        b = api.LayerBufs()
+        for f, v in d.items():
+            setattr(b, f, v)
+        return b
+
+    def turn(**kw):
+        t = api.TurnArgs()
+        d = dict(attended=0xa000, ema=0xb000, cum=0xc000, traj=0xd000, traj_cap=64, select=1, step=0, alpha=0.5,
+                 score_source=0, alive=None, budget_blocks=4, recent_tokens=16, sink_tokens=0, keep_out=0xe000,
+                 sel_ids=0xf000, n_sel=0x10000)
+        d.update(kw)
+        for f, v in d.items():
+            setattr(t, f, v)
+        return t
+
+    def step(layers, geom=g, src=api.KVS_BF16, ws=1 << 20, mass=0x6000, trn=None, n=None, cur=0x4000):
+        arr = (api.LayerBufs * len(layers))(*layers)
+        return L.kvs_decode_step(ctypes.byref(geom), len(layers) if n is None else n, arr, src,
+                                 vp(cur) if cur else None, None, ws, vp(mass) if mass else None,
+                                 ctypes.byref(trn) if trn is not None else None, None)
+
+    ok = [layer(), layer(), layer()]
+    assert step(ok, n=0) == api.KVS_EINVAL
+    assert step(ok, n=129) == api.KVS_EINVAL
+    assert step(ok, geom=_geom(api, n_q_heads=15)) == api.KVS_EINVAL
+    assert step(ok, ws=16) == api.KVS_EWS
+    assert step(ok, cur=0) == api.KVS_EINVAL
+    assert step(ok, mass=0x6004) == api.KVS_EALIGN
+    assert step(ok, src=api.KVS_F32) == api.KVS_EDTYPE              # f32 rows into a bf16 cache
+    assert step(ok[:2] + [layer(q=0x1004)]) == api.KVS_EALIGN        # the last layer's error, nothing launched
+    assert step(ok[:2] + [layer(v_new=None)]) == api.KVS_EINVAL      # K without V
+    assert step(ok[:2] + [layer(out=None)]) == api.KVS_EINVAL
+    assert step(ok[:2] + [layer(k_scale=0x11000)]) == api.KVS_EINVAL  # scales on a bf16 cache
+    assert step(ok, mass=0, trn=turn()) == api.KVS_EINVAL             # a turn needs the masses
+    assert step(ok, trn=turn(alpha=1.5)) == api.KVS_EINVAL
+    assert step(ok, trn=turn(select=2)) == api.KVS_EINVAL
+    assert step(ok, trn=turn(score_source=3)) == api.KVS_EINVAL
+    assert step(ok, trn=turn(recent_tokens=0)) == api.KVS_EINVAL
+    assert step(ok, trn=turn(keep_out=None)) == api.KVS_EINVAL
+    assert step(ok, trn=turn(traj=0xd008)) == api.KVS_EALIGN
+    assert step(ok, trn=turn(select=0, keep_out=None, traj_cap=0)) == api.KVS_EINVAL
+    fp8 = _geom(api, kv_dtype=api.KVS_FP8_E4M3)
+    assert step(ok, geom=fp8) == api.KVS_EINVAL                       # FP8 cache without scales
