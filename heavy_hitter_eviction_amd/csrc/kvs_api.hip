@@ -117,10 +117,11 @@ Plan make_plan(const kvs_geom* g) {
   p.total = round256(p.off_cnt + (size_t)pairs * p.nparts * 4);
   // LDS: the fixed part and the records, then (16-byte aligned) one output
   // slot per wave, rows padded by 4 floats; at the end the output merge of a
-  // (sequence, KV head) stages 3 G nparts + 2 G floats from the records on
+  // (sequence, KV head) stages 3 G nparts floats from the output slots on
   const size_t rec_end = (size_t)lds_fixed + (size_t)p.tl_cap * per_tile;
-  const size_t o_end = ((rec_end + 3) & ~(size_t)3) + (size_t)nw * p.G * (g->head_dim + 4);
-  const size_t merge_end = (size_t)lds_fixed + 3 * (size_t)p.G * p.nparts + 2 * (size_t)p.G;
+  const size_t o_start = (rec_end + 3) & ~(size_t)3;
+  const size_t o_end = o_start + (size_t)nw * p.G * (g->head_dim + 4);
+  const size_t merge_end = o_start + 3 * (size_t)p.G * p.nparts;
   p.lds_partial = 4 * (o_end > merge_end ? o_end : merge_end);
   return p;
 }

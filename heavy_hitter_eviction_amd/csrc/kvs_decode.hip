@@ -99,27 +99,37 @@ __device__ __forceinline__ int qk_dim(int t, int kg) {
 
 // ---- merging partitions (shared by kvs_combine and the partial kernel's
 // own merge of a (sequence, KV head)'s outputs) ----
-// One head's merge weights from its partitions' maxima m[p] and sums l[p]:
-// M = max_p m_p, L = sum_p l_p 2^(m_p - M) in ascending p, w_p = 2^(m_p - M) / L
-// (stored at w[p * wst]; 0 for an empty partition). Branch-free: guarded LDS
-// reads would each be waited for on their own.
-__device__ __forceinline__ void merge_weights(const float* m, const float* l, int P, float* w, int wst,
-                                              float* M_out, float* inv_out) {
+// Partition p's merge weight for one head from the partitions' maxima m[q]
+// and sums l[q] (in LDS): M = max_q m_q, L = sum_q l_q 2^(m_q - M) in
+// ascending q, w_p = 2^(m_p - M) / L (0 for an empty partition). Every
+// thread of a head computes the same M and L. The values are read eight at
+// a time with clamped indices (terms past P are +0), so each batch of LDS
+// reads is waited for once.
+__device__ __forceinline__ float merge_weight(const float* m, const float* l, int P, int p) {
   float M = -__builtin_inff();
-  for (int x = 0; x < P; ++x) M = fmaxf(M, m[x]);
+  for (int q0 = 0; q0 < P; q0 += 8) {
+    float mv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mv[i] = m[min(q0 + i, P - 1)];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) M = fmaxf(M, mv[i]);
+  }
   const bool none = M == -__builtin_inff();
   float L = 0.0f;
-  for (int x = 0; x < P; ++x) {
-    const float mx = m[x];
-    L += (none || mx == -__builtin_inff()) ? 0.0f : l[x] * fast_exp2(mx - M);
+  for (int q0 = 0; q0 < P; q0 += 8) {
+    float mv[8], lv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      mv[i] = m[min(q0 + i, P - 1)];
+      lv[i] = l[min(q0 + i, P - 1)];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      L += (q0 + i >= P || none || mv[i] == -__builtin_inff()) ? 0.0f : lv[i] * fast_exp2(mv[i] - M);
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  *M_out = M;
-  *inv_out = inv;
-  for (int x = 0; x < P; ++x) {
-    const float mx = m[x];
-    w[x * wst] = (mx == -__builtin_inff() || inv == 0.0f) ? 0.0f : fast_exp2(mx - M) * inv;
-  }
+  const float mp = m[p];
+  return (mp == -__builtin_inff() || inv == 0.0f) ? 0.0f : fast_exp2(mp - M) * inv;
 }
 
 // sum_p o_p w_p over P partitions with four accumulators (p mod 4) in
@@ -983,21 +993,29 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
     mw[wave * 16 + h] = m_run;
     lw[wave * 16 + h] = l_run;
   }
-  // tiles and clock ticks (100 MHz) of this wave, for the split of later launches
-  if (a.ws_time != nullptr && lane == 0) {
-    float* tm = a.ws_time + ((size_t)wg_id * NW + wave) * 2;
-    tm[0] = (float)n_done;
-    tm[1] = (float)(__builtin_amdgcn_s_memrealtime() - clk0);
-  }
-  if constexpr (SCORED) {
-    // boundaries of a linear range: partition q writes its start, the last
-    // one the end too
-    if (!RING && threadIdx.x == 0) {
-      int* bd = a.ws_bnd + ((size_t)b * a.Hkv + g) * (a.nparts + 1);
-      bd[part] = t0;
-      if (part == a.nparts - 1) bd[a.nparts] = t1;
+  // this wave's streaming time (clock ticks, 100 MHz), stored with its tile
+  // count after the handshake below, for the split of later launches
+  const float wave_ticks = (float)(__builtin_amdgcn_s_memrealtime() - clk0);
+  // Stores that nothing in this launch reads (clock records, a linear
+  // range's boundaries, block records) go out after the partial's
+  // handshake: vector-memory completions count in issue order, so a store
+  // issued before the partial would be waited for with it.
+  auto store_side = [&]() {
+    if (a.ws_time != nullptr && lane == 0) {
+      float* tm = a.ws_time + ((size_t)wg_id * NW + wave) * 2;
+      tm[0] = (float)n_done;
+      tm[1] = wave_ticks;
     }
-  }
+    if constexpr (SCORED) {
+      // boundaries of a linear range: partition q writes its start, the
+      // last one the end too
+      if (!RING && threadIdx.x == 0) {
+        int* bd = a.ws_bnd + ((size_t)b * a.Hkv + g) * (a.nparts + 1);
+        bd[part] = t0;
+        if (part == a.nparts - 1) bd[a.nparts] = t1;
+      }
+    }
+  };
   __syncthreads();
   auto wg_max = [&](int hh) -> float {
     float M = -__builtin_inff();
@@ -1050,13 +1068,17 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
 
   // The waves' outputs merge in LDS (a slot per wave in an area of its own,
   // rows padded by 4 floats against bank conflicts) into one partial per
-  // workgroup: each output sums the waves in a fixed order, rescaled to the
-  // workgroup max.
+  // workgroup. Each wave first scales its output and sum to the workgroup
+  // max of its head (factor 2^(m_wave - M), 0 for a wave that read nothing:
+  // its output and sum are zero), so the merge is a plain sum over the
+  // waves in a fixed order: one batch of LDS reads per output, no waits
+  // between the waves' terms.
   const size_t pbase = (size_t)b * a.Hq + hq0;  // first head of the group
   auto store_partial = [&]() {
     constexpr int DP = D + 4;
-    // ow: [NW][G][DP]
+    // ow: [NW][G][DP]; lw becomes each wave's scaled sum
     if (hreal) {
+      const float f = m_run == -__builtin_inff() ? 0.0f : fast_exp2(m_run - wg_max(h));
       float* dst = ow + (wave * G + h) * DP;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -1064,22 +1086,24 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
         if constexpr (NC % 4 == 0) {
 #pragma unroll
           for (int n0 = 0; n0 < NC; n0 += 4)
-            *(f32x4*)(dst + d0 + n0) = f32x4{oacc[n0][r], oacc[n0 + 1][r], oacc[n0 + 2][r], oacc[n0 + 3][r]};
+            *(f32x4*)(dst + d0 + n0) =
+                f32x4{oacc[n0][r] * f, oacc[n0 + 1][r] * f, oacc[n0 + 2][r] * f, oacc[n0 + 3][r] * f};
         } else {
 #pragma unroll
-          for (int n = 0; n < NC; ++n) dst[d0 + n] = oacc[n][r];
+          for (int n = 0; n < NC; ++n) dst[d0 + n] = oacc[n][r] * f;
         }
       }
+      if (kg == 0) lw[wave * 16 + h] = l_run * f;
     }
     __syncthreads();
     for (int x = threadIdx.x; x < G * D; x += NTH) {
       const int hh = x / D, dd = x % D;
+      float t[NW];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) t[w] = ow[(w * G + hh) * DP + dd];
       float o = 0.0f;
-      const float M = wg_max(hh);
-      for (int w = 0; w < NW; ++w) {
-        const float m = mw[w * 16 + hh];
-        if (m != -__builtin_inff()) o += ow[(w * G + hh) * DP + dd] * fast_exp2(m - M);
-      }
+#pragma unroll
+      for (int w = 0; w < NW; ++w) o += t[w];
       // the partials go to memory past the (per-XCD, non-coherent) L2, for
       // the merge below: relaxed system-scope stores are written through
       __hip_atomic_store(&a.ws_o[((pbase + hh) * a.nparts + part) * D + dd], o, __ATOMIC_RELAXED,
@@ -1087,11 +1111,12 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
     }
     for (int hh = threadIdx.x; hh < G; hh += NTH) {
       const float M = wg_max(hh);
+      float t[NW];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) t[w] = lw[w * 16 + hh];
       float l = 0.0f;
-      for (int w = 0; w < NW; ++w) {
-        const float m = mw[w * 16 + hh];
-        if (m != -__builtin_inff()) l += lw[w * 16 + hh] * fast_exp2(m - M);
-      }
+#pragma unroll
+      for (int w = 0; w < NW; ++w) l += t[w];
       __hip_atomic_store(&a.ws_m[(pbase + hh) * a.nparts + part], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       __hip_atomic_store(&a.ws_l[(pbase + hh) * a.nparts + part], l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
@@ -1116,67 +1141,115 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   // The other waves store the block records meanwhile: the completion count
   // is per wave, so wave 0's waits for its flag do not wait for them.
   if (a.pair_flag == nullptr) {
+    store_side();
     if constexpr (SCORED) store_records(0, NTH);
-  } else {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores acknowledged
-    __syncthreads();
-    uint32_t* fl = a.pair_flag + ((size_t)b * a.Hkv + g) * a.nparts;  // word 0: the pair's counter
-    if (wave != 0) {
-      if constexpr (SCORED) store_records(64, NTH - 64);
-    } else {
-      // system scope: performed at memory, past every XCD's L2
-      uint32_t old = 0u;
-      if (lane == 0) old = __hip_atomic_fetch_add(fl, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      if (lane == 0) misc[6] = old == (uint32_t)(a.nparts - 1) ? 1 : 0;
-    }
-    __syncthreads();
-    if (misc[6] == 1) {
-      const int P = a.nparts;
-      auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM); };
-      float* mT = e_rec;          // [G][P] partition maxima   (record area, free now)
-      float* lT = mT + G * P;     // [G][P] partition sums
-      float* wT = lT + G * P;     // [P][G] weights
-      float* hMt = wT + G * P;    // [G]
-      float* hIt = hMt + G;       // [G]
-      // a thread's first output: its partitions' values are requested with
-      // the maxima and sums, so both arrive in one round trip
-      float ov0[8];
-      if (threadIdx.x < G * D) {
-        const float* o_src = a.ws_o + (pbase + threadIdx.x / D) * P * D + threadIdx.x % D;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) ov0[k] = ld(o_src + (size_t)min(k, P - 1) * D);
-      }
-      for (int x = threadIdx.x; x < G * P; x += NTH) {
-        mT[x] = ld(a.ws_m + pbase * P + x);
-        lT[x] = ld(a.ws_l + pbase * P + x);
-      }
-      __syncthreads();
-      for (int hh = threadIdx.x; hh < G; hh += NTH) merge_weights(mT + hh * P, lT + hh * P, P, wT + hh, G, &hMt[hh], &hIt[hh]);
-      __syncthreads();
-      // the same weights scale the block records in the mass combine
-      for (int x = threadIdx.x; x < G * P; x += NTH)
-        a.ws_w[((size_t)b * P + x / G) * a.Hq + hq0 + x % G] = wT[x];
-      for (int x = threadIdx.x; x < G * D; x += NTH) {
-        const int hh = x / D, dd = x % D;
-        const float* o_src = a.ws_o + (pbase + hh) * P * D + dd;
-        float ov[8];
-        if (x == (int)threadIdx.x) {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) ov[k] = ov0[k];
-        } else {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) ov[k] = ld(o_src + (size_t)min(k, P - 1) * D);
-        }
-        const float sum = merge_o(ov, [&](int p) { return ld(o_src + (size_t)p * D); }, wT + hh, G, P);
-        const size_t oi = (pbase + hh) * D + dd;
-        if constexpr (KV != KV_F32)
-          ((uint16_t*)a.out)[oi] = f32_to_bf16_rne(sum);
-        else
-          ((float*)a.out)[oi] = sum;
-      }
-      if (threadIdx.x == 0) __hip_atomic_store(fl, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    }
+    return;
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores acknowledged
+  __syncthreads();
+  if (wave != 0) {
+    store_side();
+    if constexpr (SCORED) store_records(64, NTH - 64);
+    return;
+  }
+  // Wave 0 alone from here: it counts the partition and, if last, merges
+  // (it stores no records, so its loads wait for nothing else; no barrier
+  // follows, and the merge tables sit in the waves' output area, which the
+  // other waves no longer use).
+  uint32_t* fl = a.pair_flag + ((size_t)b * a.Hkv + g) * a.nparts;  // word 0: the pair's counter
+  uint32_t old = 0u;
+  // system scope: performed at memory, past every XCD's L2
+  if (lane == 0) old = __hip_atomic_fetch_add(fl, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  old = (uint32_t)__builtin_amdgcn_readfirstlane((int)old);
+  if (old == (uint32_t)(a.nparts - 1)) {
+    const int P = a.nparts;
+    auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM); };
+    float* mT = ow;             // [G][P] partition maxima
+    float* lT = mT + G * P;     // [G][P] partition sums
+    float* wT = lT + G * P;     // [P][G] weights
+    // The outputs in groups of 4 dims: group q is head 4q / D, dims 4q % D
+    // .. + 3; lane takes groups lane, lane + 64, ... The partials of the
+    // lane's first two groups (first 8 partitions) are requested with the
+    // maxima and sums, 16-byte loads past the caches (system coherent, as
+    // the partials were written through), so all arrive in one round trip.
+    const int n_grp = G * D / 4;
+    const __amdgpu_buffer_rsrc_t orsrc =
+        make_rsrc(a.ws_o + pbase * P * D, (uint32_t)((size_t)G * P * D * 4));
+    constexpr int kSysCoherent = 1 | 16;  // sc0 sc1
+    auto ld4 = [&](int grp, int p) -> f32x4 {
+      const int hh = 4 * grp / D, d0 = 4 * grp % D;
+      return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           orsrc, (int)((((size_t)hh * P + p) * D + d0) * 4), 0, kSysCoherent));
+    };
+    f32x4 pre[2][8];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) pre[gi][k] = ld4(min(lane + 64 * gi, n_grp - 1), min(k, P - 1));
+    for (int x0 = 0; x0 < G * P; x0 += 64) {
+      const int x = x0 + lane;
+      const float mv = x < G * P ? ld(a.ws_m + pbase * P + x) : 0.0f;
+      const float lv = x < G * P ? ld(a.ws_l + pbase * P + x) : 0.0f;
+      if (x < G * P) {
+        mT[x] = mv;
+        lT[x] = lv;
+      }
+    }
+    // the tables are read by other lanes of this wave: LDS operations of a
+    // wave complete in order; the fence keeps the compiler from reordering
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    // one lane per (head, partition); the same weights scale the block
+    // records in the mass combine
+    for (int x = lane; x < G * P; x += 64) {
+      const int hh = x / P, p = x % P;
+      const float w = merge_weight(mT + hh * P, lT + hh * P, P, p);
+      wT[p * G + hh] = w;
+      a.ws_w[((size_t)b * P + p) * a.Hq + hq0 + hh] = w;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    // sum_p o_p w_p with four accumulators (p mod 4) in ascending p; first:
+    // the group's partials of partitions 0 .. 7
+    auto out_group = [&](int grp, const f32x4 (&first)[8]) {
+      const int hh = 4 * grp / D;
+      f32x4 acc[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const f32x4 t = first[k] * wT[min(k, P - 1) * G + hh];
+        if (k < P) acc[k & 3] += t;
+      }
+      for (int p0 = 8; p0 < P; p0 += 8) {
+        f32x4 ov[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) ov[k] = ld4(grp, min(p0 + k, P - 1));
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const f32x4 t = ov[k] * wT[min(p0 + k, P - 1) * G + hh];
+          if (p0 + k < P) acc[k & 3] += t;
+        }
+      }
+      const f32x4 sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      const size_t oi = (pbase + hh) * D + 4 * grp % D;
+      if constexpr (KV != KV_F32) {
+        uint32_t* dst = (uint32_t*)((uint16_t*)a.out + oi);
+        dst[0] = (uint32_t)f32_to_bf16_rne(sum[0]) | ((uint32_t)f32_to_bf16_rne(sum[1]) << 16);
+        dst[1] = (uint32_t)f32_to_bf16_rne(sum[2]) | ((uint32_t)f32_to_bf16_rne(sum[3]) << 16);
+      } else {
+        *(f32x4*)((float*)a.out + oi) = sum;
+      }
+    };
+    if (lane < n_grp) out_group(lane, pre[0]);
+    if (lane + 64 < n_grp) out_group(lane + 64, pre[1]);
+    for (int grp = lane + 128; grp < n_grp; grp += 64) {
+      f32x4 fr[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) fr[k] = ld4(grp, min(k, P - 1));
+      out_group(grp, fr);
+    }
+    if (lane == 0) __hip_atomic_store(fl, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+  store_side();
 }
 
 // ---- block records for the mass combines ----
