@@ -56,7 +56,7 @@ int check_geom(const kvs_geom* g) {
 
 struct Plan {
   int NT, tpp, nparts, nsub, G, S, tl_cap, n_wg, adapt;
-  size_t off_m, off_l, off_o, off_e, off_bnd, off_w, off_time, off_rates, off_cnt, total;
+  size_t off_m, off_l, off_o, off_e, off_pid, off_w, off_time, off_rates, off_cnt, total;
   size_t lds_partial;
 };
 
@@ -80,7 +80,7 @@ Plan make_plan(const kvs_geom* g) {
   const int per_tile = p.G * (p.nsub + 1) + 1;
   const int tpp_lds = (kLdsBudgetFloats - lds_fixed) / per_tile;
   if (tpp > tpp_lds) tpp = tpp_lds < 4 ? 4 : tpp_lds;
-  // the mass combine keeps a layer's record weights and partition boundaries
+  // the mass combine keeps a layer's record weights
   // in LDS: bound them to 48 KiB
   while (true) {
     const int np = (p.NT + tpp - 1) / tpp;
@@ -109,8 +109,8 @@ Plan make_plan(const kvs_geom* g) {
   p.off_l = round256(p.off_m + bh * p.S * 4);
   p.off_o = round256(p.off_l + bh * p.S * 4);
   p.off_e = round256(p.off_o + bh * p.S * g->head_dim * 4);
-  p.off_bnd = round256(p.off_e + (size_t)g->batch * p.NT * p.nsub * g->n_q_heads * 4);
-  p.off_w = round256(p.off_bnd + (size_t)pairs * (p.nparts + 1) * 4);
+  p.off_pid = round256(p.off_e + (size_t)g->batch * p.NT * p.nsub * g->n_q_heads * 4);
+  p.off_w = round256(p.off_pid + (size_t)pairs * p.NT * 4);
   p.off_time = round256(p.off_w + bh * p.nparts * 4);
   p.off_rates = round256(p.off_time + (size_t)p.n_wg * nw * 2 * 4);
   p.off_cnt = round256(p.off_rates + 8 * 4);
@@ -224,7 +224,7 @@ namespace {
 void bind_workspace(const Plan& p, char* ws, uint32_t* flags, kvs::PartialArgs* a, kvs::CombineArgs* c) {
   a->ws_m = (float*)(ws + p.off_m); a->ws_l = (float*)(ws + p.off_l);
   a->ws_o = (float*)(ws + p.off_o); a->ws_e = (float*)(ws + p.off_e);
-  a->ws_bnd = (int*)(ws + p.off_bnd); a->ws_time = (float*)(ws + p.off_time);
+  a->ws_pid = (int*)(ws + p.off_pid); a->ws_time = (float*)(ws + p.off_time);
   a->ws_w = (float*)(ws + p.off_w);
   a->pair_flag = flags ? flags : (uint32_t*)(ws + p.off_cnt);
   a->rates = (const float*)(ws + p.off_rates);
@@ -263,7 +263,7 @@ int decode_setup(const kvs_geom* g, const void* q, const void* k_cache, const vo
   a->dyn = g->deterministic ? 0 : 1; a->tl_cap = p.tl_cap; a->adapt = p.adapt;
   a->scale_log2 = g->softmax_scale * 1.4426950408889634f;
   c->n_layers = 1; c->layers_per_chunk = 1;
-  c->off_w = p.off_w; c->off_e = p.off_e; c->off_bnd = p.off_bnd;
+  c->off_w = p.off_w; c->off_e = p.off_e; c->off_pid = p.off_pid;
   c->off_time = p.off_time; c->off_rates = p.off_rates;
   c->cur_pos = cur_pos; c->n_wg = p.n_wg;
   c->mass = mass_accum;
@@ -428,7 +428,7 @@ int tap_setup(const kvs_geom* g, void* const* workspaces, int32_t n_layers, size
   const size_t per_layer = kvs::combine_layer_floats(g->n_q_heads, g->n_kv_heads, p.nparts) * 4;
   const int fit = (int)(kvs::kCombineLdsBytes / per_layer);
   c.layers_per_chunk = fit < 1 ? 1 : (fit < n_layers ? fit : n_layers);
-  c.off_w = p.off_w; c.off_e = p.off_e; c.off_bnd = p.off_bnd;
+  c.off_w = p.off_w; c.off_e = p.off_e; c.off_pid = p.off_pid;
   c.off_time = p.off_time; c.off_rates = p.off_rates;
   c.n_wg = p.n_wg; c.cur_pos = cur_pos;
   c.mass = mass_accum; c.head_mass = head_mass; c.mass_max = mass_max;
@@ -797,7 +797,7 @@ namespace {
 // every geometry: each call leaves the counters it used at zero (its merging
 // workgroups reset them), so they are zero at the start of every call,
 // whatever geometry the previous call had. The rest holds one call's
-// workspace regions (partials, block records, boundaries, merge weights,
+// workspace regions (partials, block records, partition map, merge weights,
 // clock records and the per-class rates, which are sanitised on read).
 constexpr size_t kNoallocFlagBytes = 64 * 1024;  // counter region: B * Hkv * partitions words
 constexpr size_t kNoallocWsBytes = (size_t)KVS_NOALLOC_SCRATCH_BYTES - kNoallocFlagBytes;

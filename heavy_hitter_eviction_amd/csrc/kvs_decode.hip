@@ -996,8 +996,8 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   // this wave's streaming time (clock ticks, 100 MHz), stored with its tile
   // count after the handshake below, for the split of later launches
   const float wave_ticks = (float)(__builtin_amdgcn_s_memrealtime() - clk0);
-  // Stores that nothing in this launch reads (clock records, a linear
-  // range's boundaries, block records) go out after the partial's
+  // Stores that nothing in this launch reads (clock records, block records
+  // and a linear range's partition map) go out after the partial's
   // handshake: vector-memory completions count in issue order, so a store
   // issued before the partial would be waited for with it.
   auto store_side = [&]() {
@@ -1005,15 +1005,6 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
       float* tm = a.ws_time + ((size_t)wg_id * NW + wave) * 2;
       tm[0] = (float)n_done;
       tm[1] = wave_ticks;
-    }
-    if constexpr (SCORED) {
-      // boundaries of a linear range: partition q writes its start, the
-      // last one the end too
-      if (!RING && threadIdx.x == 0) {
-        int* bd = a.ws_bnd + ((size_t)b * a.Hkv + g) * (a.nparts + 1);
-        bd[part] = t0;
-        if (part == a.nparts - 1) bd[a.nparts] = t1;
-      }
     }
   };
   __syncthreads();
@@ -1064,6 +1055,11 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
         if (!((kb[rb >> 5] >> (rb & 31)) & 1u)) a.ws_e[e_index(tb + tl, 0, 0) + (x - tl * per_e)] = 0.0f;
       }
     }
+    // a linear range's partition map: this partition's index at each of its
+    // tiles, for the mass combine to find the tile's merge weights (a ring's
+    // partitions are fixed ranges of tpp tiles)
+    if constexpr (!RING)
+      for (int x = tid; x < te - tb; x += nth) a.ws_pid[rec_row + tb + x] = part;
   };
 
   // The waves' outputs merge in LDS (a slot per wave in an area of its own,
@@ -1292,6 +1288,27 @@ __device__ __forceinline__ void load_rec(float (&ev)[NSUB][HC], __amdgpu_buffer_
   }
 }
 
+// Partition that produced tile tc's records for the KV heads of a record
+// chunk (heads hc .. hc + HC - 1, one entry per 4-head group with V4, else
+// per head): a ring's partitions are fixed ranges of tpp tiles; a linear
+// range's come from the partition map the partial kernel stored
+// ([B][Hkv][NT] ints, map = this sequence's rows), loaded with the chunk's
+// records (clamped to 0 .. P - 1 where used).
+template <int HC, bool V4, bool RING>
+__device__ __forceinline__ void load_pid(int (&pv)[V4 ? HC / 4 : HC], __amdgpu_buffer_rsrc_t map, int tc, int hc,
+                                         int Hq, int G, int NT, int P, int tpp) {
+  constexpr int PG = V4 ? 4 : 1;
+#pragma unroll
+  for (int i = 0; i < HC / PG; ++i) {
+    if constexpr (RING) {
+      pv[i] = min(tc / tpp, P - 1);
+    } else {
+      const int gg = min(hc + PG * i, Hq - PG) / G;
+      pv[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(map, tc * 4, (int)((uint32_t)gg * NT * 4), 0);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Combine: grid (n_mass_chunks + n_layers, B), 256 threads: the block masses
 // of n_layers calls (one for kvs_decode_combine, a whole step's layers for
@@ -1362,7 +1379,7 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
 
   // Each workgroup first issues the global loads that need nothing from the
   // shared tables (the first layer's records of its tile, the current
-  // masses, the first layers' record weights and boundaries), then
+  // masses, the first layers' record weights), then
   // builds the tables and finishes, the next layer's records loading while
   // one layer is summed. Loads are unconditional (indices clamped into
   // range, unused values masked later): conditional loads make the compiler
@@ -1371,29 +1388,18 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
   constexpr int HC = RING ? 16 : 32;   // heads per record chunk
   const int G = a.Hq / a.Hkv;
   const int n_ml = a.Hq * P;                 // record weights per layer
-  const int n_bnd = a.Hkv * (P + 1);         // boundaries per layer
   const int lc0 = min(L, a.layers_per_chunk);
   // layer-table block of layer slot s in LDS
   const int per_layer = (int)combine_layer_floats(a.Hq, a.Hkv, P);
   auto t_wp = [&](int s_) { return lds + (size_t)s_ * per_layer; };          // [P][Hq]
-  auto t_bd = [&](int s_) { return (int*)(t_wp(s_) + n_ml); };               // [Hkv][P + 1]
-  // the first chunk's weights/boundaries: two per thread prefetched
-  const int n_stage = lc0 * (n_ml + n_bnd);
+  // the first chunk's weights: two per thread prefetched
+  const int n_stage = lc0 * n_ml;
   auto stage_src = [&](int l0, int x) -> float {
-    // value x of the staged tables of layers [l0, l0 + lc): per layer
-    // n_ml weights, then n_bnd boundaries (bit patterns)
-    const int per = n_ml + n_bnd;
-    const int l = l0 + x / per, r = x % per;
-    if (r < n_ml) return ws_f(l, a.off_w)[(size_t)b * n_ml + r];
-    if constexpr (RING) return 0.0f;
-    return __builtin_bit_cast(float, ((const int*)(a.lws[l] + a.off_bnd))[(size_t)b * n_bnd + r - n_ml]);
+    // value x of the staged weights of layers [l0, l0 + lc)
+    const int l = l0 + x / n_ml, r = x % n_ml;
+    return ws_f(l, a.off_w)[(size_t)b * n_ml + r];
   };
-  auto stage_dst = [&](int x) -> float* {
-    const int per = n_ml + n_bnd;
-    const int s_ = x / per, r = x % per;
-    if (r < n_ml) return t_wp(s_) + r;
-    return (float*)t_bd(s_) + (r - n_ml);
-  };
+  auto stage_dst = [&](int x) -> float* { return t_wp(x / n_ml) + x % n_ml; };
   const float pre0 = stage_src(0, min(tid, n_stage - 1));
   const float pre1 = stage_src(0, min(tid + 256, n_stage - 1));
 
@@ -1416,12 +1422,17 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
   // this sequence's records of layer l; the tile's byte offset
   const uint32_t rec_bytes = (uint32_t)a.Hkv * a.NT * NSUB * G * 4;
   const uint32_t rec_vo = (uint32_t)tc * NSUB * G * 4;
-  auto load_records = [&](int l, int hc, float (&ev)[NSUB][HC]) {
+  constexpr int PV = V4 ? HC / 4 : HC;
+  const uint32_t map_bytes = (uint32_t)a.Hkv * a.NT * 4;
+  auto load_records = [&](int l, int hc, float (&ev)[NSUB][HC], int (&pv)[PV]) {
     const char* base = a.lws[l] + a.off_e + (size_t)b * rec_bytes;
     load_rec<NSUB, HC, V4>(ev, make_rsrc(base, rec_bytes), rec_vo, hc, a.Hq, G, a.NT);
+    load_pid<HC, V4, RING>(pv, make_rsrc(a.lws[l] + a.off_pid + (size_t)b * map_bytes, map_bytes), tc, hc, a.Hq, G,
+                           a.NT, P, a.tpp);
   };
   float ev[NSUB][HC], ev_next[NSUB][HC];
-  load_records(0, 0, ev);
+  int pv[PV], pv_next[PV];
+  load_records(0, 0, ev, pv);
   float mass_run[NSUB], max_run[NSUB];
   if constexpr (!RING) {
     // a linear cache's block is the tile: its index needs no cur_pos
@@ -1478,7 +1489,7 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
     const int lc = min(lc0, L - l0);
     // ---- tables of layers [l0, l0 + lc) ----
     if (l0 > 0) __syncthreads();  // the previous chunk's tables are done with
-    const int n_st = lc * (n_ml + n_bnd);
+    const int n_st = lc * n_ml;
     // four values per thread in flight per round (one round trip each)
     auto stage_rest = [&](int la, int x_first) {
       for (int x0 = x_first; x0 < n_st; x0 += 4 * 256) {
@@ -1503,24 +1514,6 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
     for (int s_ = 0; s_ < lc; ++s_) {
       const int l = l0 + s_;
       const float* wp = t_wp(s_);
-      const int* bnd = t_bd(s_);
-      // partition that produced tile tc's records for KV head gg: a ring
-      // splits evenly; a linear range at the stored boundaries (the last one
-      // at or below tc; boundary 0 is the range start)
-      auto part_of = [&](int gg) -> int {
-        if constexpr (RING) {
-          return min(tc / a.tpp, P - 1);
-        } else {
-          const int* bg = bnd + gg * (P + 1);
-          int base = 0;
-          for (int n = P; n > 1;) {
-            const int half = n >> 1;
-            base = bg[base + half] <= tc ? base + half : base;
-            n -= half;
-          }
-          return base;
-        }
-      };
       float acc[NSUB], mx[NSUB];
 #pragma unroll
       for (int sb = 0; sb < NSUB; ++sb) {
@@ -1532,10 +1525,10 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
       // alongside when asked for. Every tile of the range has records from
       // this layer's call, relative to its partition's max.
       for (int hc = 0; hc < a.Hq; hc += HC) {
-        if (hc > 0) load_records(l, hc, ev);
+        if (hc > 0) load_records(l, hc, ev, pv);
         // the next layer's first records load while this chunk is summed
         const bool prefetch = hc + HC >= a.Hq && l + 1 < L;
-        if (prefetch) load_records(l + 1, 0, ev_next);
+        if (prefetch) load_records(l + 1, 0, ev_next, pv_next);
         // the chunk's products E w, in place of its records: a group's four
         // weights read from LDS (unconditional, clamped) as they are used,
         // heads in ascending order per sub-block; heads past Hq add +0 (sums
@@ -1544,7 +1537,7 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
 #pragma unroll
           for (int q = 0; q < HC / 4; ++q) {
             const int hh = min(hc + 4 * q, a.Hq - 4);
-            const f32x4 w4 = *(const f32x4*)(wp + part_of(hh / G) * a.Hq + hh);
+            const f32x4 w4 = *(const f32x4*)(wp + min(max(pv[q], 0), P - 1) * a.Hq + hh);
 #pragma unroll
             for (int sb = 0; sb < NSUB; ++sb)
 #pragma unroll
@@ -1559,7 +1552,7 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
 #pragma unroll
           for (int k = 0; k < HC; ++k) {
             const int hh = min(hc + k, a.Hq - 1);
-            const float w = wp[part_of(hh / G) * a.Hq + hh];
+            const float w = wp[min(max(pv[k], 0), P - 1) * a.Hq + hh];
 #pragma unroll
             for (int sb = 0; sb < NSUB; ++sb) {
               const float v = hc + k < a.Hq ? ev[sb][k] * w : 0.0f;
@@ -1600,6 +1593,8 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
           for (int sb = 0; sb < NSUB; ++sb)
 #pragma unroll
             for (int k = 0; k < HC; ++k) ev[sb][k] = ev_next[sb][k];
+#pragma unroll
+          for (int i = 0; i < PV; ++i) pv[i] = pv_next[i];
         }
       }
 #pragma unroll
@@ -1633,7 +1628,7 @@ __global__ __launch_bounds__(256) void kvs_combine(CombineArgs a) {
 // and layers w / TG, w / TG + 8 / TG, ... (TG = 1 from 8 layers up), keeping
 // each (tile, layer)'s sum over heads, computed exactly as kvs_combine does,
 // in LDS; then one lane per tile adds them in layer order to the current
-// mass, so the result equals the layer-by-layer sum bit for bit. A wave stages only its own layers' weights and boundaries, loaded
+// mass, so the result equals the layer-by-layer sum bit for bit. A wave stages only its own layers' weights, loaded
 // together with its records, so the one barrier is before the final sums.
 // ---------------------------------------------------------------------------
 constexpr int kCmbTiles = 64;
@@ -1710,10 +1705,8 @@ void kvs_combine_layers(CombineArgs a) {
   }
 
   const int G = a.Hq / a.Hkv;
-  const int n_ml = a.Hq * P, n_bnd = a.Hkv * (P + 1);
-  const int per = n_ml + n_bnd;  // one layer's table: weights [P][Hq], boundaries [Hkv][P + 1]
+  const int per = a.Hq * P;  // one layer's table: the record weights [P][Hq]
   auto t_wp = [&](int l) { return lds + (size_t)l * per; };
-  auto t_bd = [&](int l) { return (int*)(t_wp(l) + n_ml); };
   float* cl = lds + (size_t)L * per;  // [tpw][L][NSUB][2]: sum and max over heads
   // this wave: tile group tg, layers l0, l0 + ls, ...
   const int tg = wv % TG, l0 = wv / TG, ls = kCmbWaves / TG;
@@ -1733,9 +1726,13 @@ void kvs_combine_layers(CombineArgs a) {
   const int tc = min(max(t, 0), a.NT - 1);
   const uint32_t rec_bytes = (uint32_t)a.Hkv * a.NT * NSUB * G * 4;
   const uint32_t rec_vo = (uint32_t)tc * NSUB * G * 4;
-  auto load_records = [&](int l, int hc, float (&ev)[NSUB][HC]) {
-    const char* base = a.lws[min(l, L - 1)] + a.off_e + (size_t)b * rec_bytes;
-    load_rec<NSUB, HC, V4>(ev, make_rsrc(base, rec_bytes), rec_vo, hc, a.Hq, G, a.NT);
+  constexpr int PV = V4 ? HC / 4 : HC;
+  const uint32_t map_bytes = (uint32_t)a.Hkv * a.NT * 4;
+  auto load_records = [&](int l, int hc, float (&ev)[NSUB][HC], int (&pv)[PV]) {
+    const char* lw = a.lws[min(l, L - 1)];
+    load_rec<NSUB, HC, V4>(ev, make_rsrc(lw + a.off_e + (size_t)b * rec_bytes, rec_bytes), rec_vo, hc, a.Hq, G, a.NT);
+    load_pid<HC, V4, RING>(pv, make_rsrc(lw + a.off_pid + (size_t)b * map_bytes, map_bytes), tc, hc, a.Hq, G, a.NT,
+                           P, a.tpp);
   };
   // Tables of up to 128 values per layer (the usual case): each wave stages
   // those of its own layers and reads only those (waves of a layer's tile
@@ -1745,10 +1742,7 @@ void kvs_combine_layers(CombineArgs a) {
   // them waits for nothing else. Larger tables (many partitions) are staged
   // by the whole workgroup, four values per thread in flight, then a barrier.
   auto tab_val = [&](int l, int r) -> float {
-    const char* base = a.lws[min(l, L - 1)];
-    const int rc = min(r, per - 1);
-    return rc < n_ml ? ((const float*)(base + a.off_w))[(size_t)b * n_ml + rc]
-                     : ((const float*)(base + a.off_bnd))[(size_t)b * n_bnd + (rc - n_ml)];  // a ring's are unused
+    return ((const float*)(a.lws[min(l, L - 1)] + a.off_w))[(size_t)b * per + min(r, per - 1)];
   };
   const bool coop = per > 128;
   float tv[2][2];
@@ -1760,8 +1754,9 @@ void kvs_combine_layers(CombineArgs a) {
   }
   asm volatile("" ::: "memory");
   float ev[NSUB][HC], ev_next[NSUB][HC];
-  load_records(l0, 0, ev);
-  load_records(l0 + ls, 0, ev_next);
+  int pv[PV], pv_next[PV];
+  load_records(l0, 0, ev, pv);
+  load_records(l0 + ls, 0, ev_next, pv_next);
   // a linear cache's block is the tile: the first wave of each tile group
   // fetches the current masses it adds to now (a ring's blocks depend on
   // cur_pos, read at the end)
@@ -1809,26 +1804,8 @@ void kvs_combine_layers(CombineArgs a) {
   // head chunk given in ev (further chunks, when Hq > HC, loaded into ev here).
   // Heads in ascending order per sub-block; each group's four weights are read
   // from LDS as they are used.
-  auto sum_layer = [&](int l, float (&ev)[NSUB][HC]) {
+  auto sum_layer = [&](int l, float (&ev)[NSUB][HC], int (&pv)[PV]) {
     const float* wp = t_wp(l);
-    const int* bnd = t_bd(l);
-    // partition that produced tile tc's records for KV head gg: a ring splits
-    // evenly; a linear range at the stored boundaries (the last one at or
-    // below tc; boundary 0 is the range start)
-    auto part_of = [&](int gg) -> int {
-      if constexpr (RING) {
-        return min(tc / a.tpp, P - 1);
-      } else {
-        const int* bg = bnd + gg * (P + 1);
-        int base = 0;
-        for (int n = P; n > 1;) {
-          const int half = n >> 1;
-          base = bg[base + half] <= tc ? base + half : base;
-          n -= half;
-        }
-        return base;
-      }
-    };
     float acc[NSUB], mx[NSUB];
 #pragma unroll
     for (int sb = 0; sb < NSUB; ++sb) {
@@ -1836,13 +1813,13 @@ void kvs_combine_layers(CombineArgs a) {
       mx[sb] = 0.0f;
     }
     for (int hc = 0; hc < a.Hq; hc += HC) {
-      if (hc > 0) load_records(l, hc, ev);
+      if (hc > 0) load_records(l, hc, ev, pv);
       // heads past Hq add +0 (sums and maxima are >= 0: no change)
       if constexpr (V4) {
 #pragma unroll
         for (int q = 0; q < HC / 4; ++q) {
           const int hh = min(hc + 4 * q, a.Hq - 4);
-          const f32x4 w4 = *(const f32x4*)(wp + part_of(hh / G) * a.Hq + hh);
+          const f32x4 w4 = *(const f32x4*)(wp + min(max(pv[q], 0), P - 1) * a.Hq + hh);
 #pragma unroll
           for (int sb = 0; sb < NSUB; ++sb)
 #pragma unroll
@@ -1856,7 +1833,7 @@ void kvs_combine_layers(CombineArgs a) {
 #pragma unroll
         for (int k = 0; k < HC; ++k) {
           const int hh = min(hc + k, a.Hq - 1);
-          const float w = wp[part_of(hh / G) * a.Hq + hh];
+          const float w = wp[min(max(pv[k], 0), P - 1) * a.Hq + hh];
 #pragma unroll
           for (int sb = 0; sb < NSUB; ++sb) {
             const float v = hc + k < a.Hq ? ev[sb][k] * w : 0.0f;
@@ -1873,11 +1850,11 @@ void kvs_combine_layers(CombineArgs a) {
     }
   };
   // the first two layers' first chunks are in flight since the start
-  if (l0 < L) sum_layer(l0, ev);
-  if (l0 + ls < L) sum_layer(l0 + ls, ev_next);
+  if (l0 < L) sum_layer(l0, ev, pv);
+  if (l0 + ls < L) sum_layer(l0 + ls, ev_next, pv_next);
   for (int l = l0 + 2 * ls; l < L; l += ls) {
-    load_records(l, 0, ev);
-    sum_layer(l, ev);
+    load_records(l, 0, ev, pv);
+    sum_layer(l, ev, pv);
   }
   __syncthreads();
 

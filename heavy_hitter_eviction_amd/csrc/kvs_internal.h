@@ -33,7 +33,8 @@ struct PartialArgs {
   float* ws_o;     // [B][Hq][P][D] unnormalised output
   float* ws_e;     // [B][Hkv][NT][NSUB][G] per-tile block sums, relative to the
                    // max of the partition's workgroup (its waves' ws_m)
-  int* ws_bnd;     // [B][Hkv][P + 1] partition boundaries of a linear range
+  int* ws_pid;     // [B][Hkv][NT] partition map of a linear range: the index of
+                   // the partition that read each tile of the range
   float* ws_w;     // [B][P][Hq] merge weights 2^(m_p - M) / L per partition and
                    // head, written by the workgroup that merges the outputs
   float* ws_time;  // [workgroups][kPartialWaves][2] tiles processed, clock ticks
@@ -67,7 +68,7 @@ constexpr int kMaxTapLayers = 128;
 // workspace starts at lws[l]; every layer has the same plan (offsets).
 struct CombineArgs {
   const char* lws[kMaxTapLayers];
-  size_t off_w, off_e, off_bnd, off_time, off_rates;
+  size_t off_w, off_e, off_pid, off_time, off_rates;
   int n_layers;
   int layers_per_chunk;  // layers whose tables fit the LDS at once
   int n_wg;       // partial workgroups per layer that wrote clock records
@@ -79,10 +80,10 @@ struct CombineArgs {
 };
 
 // LDS floats one layer's combine tables take: the per (partition, head)
-// record weights and the partition boundaries. A combine workgroup also needs
-// 16 floats for rates.
+// record weights. A combine workgroup also needs 16 floats for rates.
 __host__ __device__ inline size_t combine_layer_floats(int Hq, int Hkv, int P) {
-  return (size_t)Hq * P + (size_t)Hkv * (P + 1);
+  (void)Hkv;
+  return (size_t)Hq * P;
 }
 constexpr size_t kCombineLdsBytes = 49152;
 
