@@ -97,55 +97,54 @@ __device__ __forceinline__ int qk_dim(int t, int kg) {
   return (t / EPC) * 4 * EPC + kg * EPC + t % EPC;
 }
 
-// ---- merging partitions (shared by kvs_combine and the partial kernel's
-// own merge of a (sequence, KV head)'s outputs) ----
+// ---- merging partitions (the partial kernel's own merge of a (sequence,
+// KV head)'s outputs) ----
 // Partition p's merge weight for one head from the partitions' maxima m[q]
 // and sums l[q] (in LDS): M = max_q m_q, L = sum_q l_q 2^(m_q - M) in
 // ascending q, w_p = 2^(m_p - M) / L (0 for an empty partition). Every
-// thread of a head computes the same M and L. The values are read eight at
-// a time with clamped indices (terms past P are +0), so each batch of LDS
-// reads is waited for once.
+// lane of a head computes the same M and L. Up to eight partitions come in
+// one batch of LDS reads (indices clamped, terms past P are +0); more take a
+// batch per eight partitions for the maximum and again for the sum.
 __device__ __forceinline__ float merge_weight(const float* m, const float* l, int P, int p) {
+  const float mp = m[p];
   float M = -__builtin_inff();
-  for (int q0 = 0; q0 < P; q0 += 8) {
-    float mv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) mv[i] = m[min(q0 + i, P - 1)];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) M = fmaxf(M, mv[i]);
-  }
-  const bool none = M == -__builtin_inff();
   float L = 0.0f;
-  for (int q0 = 0; q0 < P; q0 += 8) {
+  if (P <= 8) {
     float mv[8], lv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      mv[i] = m[min(q0 + i, P - 1)];
-      lv[i] = l[min(q0 + i, P - 1)];
+      mv[i] = m[min(i, P - 1)];
+      lv[i] = l[min(i, P - 1)];
     }
 #pragma unroll
+    for (int i = 0; i < 8; ++i) M = fmaxf(M, mv[i]);
+    const bool none = M == -__builtin_inff();
+#pragma unroll
     for (int i = 0; i < 8; ++i)
-      L += (q0 + i >= P || none || mv[i] == -__builtin_inff()) ? 0.0f : lv[i] * fast_exp2(mv[i] - M);
+      L += (i >= P || none || mv[i] == -__builtin_inff()) ? 0.0f : lv[i] * fast_exp2(mv[i] - M);
+  } else {
+    for (int q0 = 0; q0 < P; q0 += 8) {
+      float mv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mv[i] = m[min(q0 + i, P - 1)];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) M = fmaxf(M, mv[i]);
+    }
+    const bool none = M == -__builtin_inff();
+    for (int q0 = 0; q0 < P; q0 += 8) {
+      float mv[8], lv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        mv[i] = m[min(q0 + i, P - 1)];
+        lv[i] = l[min(q0 + i, P - 1)];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        L += (q0 + i >= P || none || mv[i] == -__builtin_inff()) ? 0.0f : lv[i] * fast_exp2(mv[i] - M);
+    }
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  const float mp = m[p];
   return (mp == -__builtin_inff() || inv == 0.0f) ? 0.0f : fast_exp2(mp - M) * inv;
-}
-
-// sum_p o_p w_p over P partitions with four accumulators (p mod 4) in
-// ascending p; the first OPF values are given (loaded with clamped indices,
-// terms past P are +0), the rest come from ldo(p). Every partition writes its
-// partial each launch (zeros when it read nothing), so all are finite.
-template <int OPF, class LdO>
-__device__ __forceinline__ float merge_o(const float (&ov)[OPF], LdO ldo, const float* w, int wst, int P) {
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int k = 0; k < OPF; ++k) {
-    const float wk = w[min(k, P - 1) * wst];
-    acc[k & 3] += k < P ? ov[k] * wk : 0.0f;
-  }
-  for (int p = OPF; p < P; ++p) acc[p & 3] += ldo(p) * w[p * wst];
-  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
 template <int KV>
@@ -1205,24 +1204,33 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     // sum_p o_p w_p with four accumulators (p mod 4) in ascending p; first:
     // the group's partials of partitions 0 .. 7
+    // (eight weights read in one batch and terms past P selected away, not
+    // branched over: a read under a branch is waited for on its own)
     auto out_group = [&](int grp, const f32x4 (&first)[8]) {
       const int hh = 4 * grp / D;
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
       f32x4 acc[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < 4; ++k) acc[k] = zero;
+      float wk[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) wk[k] = wT[min(k, P - 1) * G + hh];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const f32x4 t = first[k] * wT[min(k, P - 1) * G + hh];
-        if (k < P) acc[k & 3] += t;
+        const f32x4 t = first[k] * wk[k];
+        acc[k & 3] += k < P ? t : zero;
       }
       for (int p0 = 8; p0 < P; p0 += 8) {
         f32x4 ov[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) ov[k] = ld4(grp, min(p0 + k, P - 1));
+        for (int k = 0; k < 8; ++k) {
+          ov[k] = ld4(grp, min(p0 + k, P - 1));
+          wk[k] = wT[min(p0 + k, P - 1) * G + hh];
+        }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const f32x4 t = ov[k] * wT[min(p0 + k, P - 1) * G + hh];
-          if (p0 + k < P) acc[k & 3] += t;
+          const f32x4 t = ov[k] * wk[k];
+          acc[k & 3] += p0 + k < P ? t : zero;
         }
       }
       const f32x4 sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
