@@ -329,6 +329,7 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   if (threadIdx.x == 0) {
     misc[1] = NW;  // claim counter: batches 0 .. NW - 1 are the waves' first
     misc[2] = 0;
+    misc[6] = -1;  // the partition count, once wave 0 has it
   }
 
   // With a keep mask, or a list of block ids to re-attend, on a linear cache
@@ -1022,7 +1023,27 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   auto store_records = [&](int th0, int nth) {
     const int per_e = NSUB * G;
     const int tid = threadIdx.x - th0;
-    if (nth % per_e == 0) {
+    if (G % 4 == 0 && nth % (per_e / 4) == 0) {
+      // four heads of one sub-block per 16-byte piece (an entry's records
+      // and maxima are contiguous per head): a thread keeps piece c of every
+      // (nth / pieces)-th entry, with its four heads' workgroup maxima
+      const int cpe = per_e / 4;
+      const int r0 = 4 * (tid % cpe), h0 = r0 % G;
+      float M[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) M[i] = wg_max(h0 + i);
+      const int estep = nth / cpe;
+      for (int e = tid / cpe; e < n_items; e += estep) {
+        const f32x4 ev = *(const f32x4*)(e_rec + e * per_e + r0);
+        const f32x4 mr = *(const f32x4*)(m_rec + e * G + h0);
+        f32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v[i] = (M[i] == -__builtin_inff() || mr[i] == -__builtin_inff()) ? 0.0f : ev[i] * fast_exp2(mr[i] - M[i]);
+        const int t = use_list ? tlist[e] : tb + e;
+        *(f32x4*)(a.ws_e + e_index(t, 0, 0) + r0) = v;
+      }
+    } else if (nth % per_e == 0) {
       // the usual case: a thread keeps one (sub-block, head) r of every
       // (nth / per_e)-th entry, so its head's workgroup max is taken once
       const int r = tid % per_e, hh = r % G;
@@ -1046,7 +1067,16 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
         a.ws_e[e_index(t, 0, 0) + (x - e * per_e)] = v;
       }
     }
-    if (use_list) {
+    if (use_list && G % 4 == 0) {
+      // tiles of the range that were not kept: zero records (16-byte pieces)
+      const int cpe = per_e / 4;
+      for (int x = tid; x < (te - tb) * cpe; x += nth) {
+        const int tl = x / cpe;
+        const int rb = tb + tl - r_lo;
+        if (!((kb[rb >> 5] >> (rb & 31)) & 1u))
+          *(f32x4*)(a.ws_e + e_index(tb + tl, 0, 0) + 4 * (x - tl * cpe)) = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    } else if (use_list) {
       // tiles of the range that were not kept: zero records
       for (int x = tid; x < (te - tb) * per_e; x += nth) {
         const int tl = x / per_e;
@@ -1118,6 +1148,76 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   };
   store_partial();
 
+  // Head hh's output merge by one wave, for at most eight partitions: lane p
+  // takes partition p's maximum and sum (past P: -inf and 0), M and L come
+  // from reductions over lanes 0 .. 7, lane p's weight w_p = 2^(m_p - M) / L
+  // (0 for an empty partition) is stored for the mass combines and read into
+  // a scalar register, and each lane sums sum_p w_p o_p for its DPL
+  // consecutive dims with four accumulators (p mod 4) in ascending p. All
+  // loads are system coherent (the partials were written through) and go out
+  // together.
+  auto merge_head = [&](int hh) {
+    const int P = a.nparts;
+    constexpr int DPL = D >= 64 ? D / 64 : 1;  // dims per lane
+    const size_t row = (pbase + hh) * P;        // this head's partitions
+    constexpr int kSysCoherent = 1 | 16;        // sc0 sc1
+    const __amdgpu_buffer_rsrc_t orsrc = make_rsrc(a.ws_o + row * D, (uint32_t)((size_t)P * D * 4));
+    const int d0 = min(lane * DPL, D - DPL);
+    float ov[8][DPL];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (k >= P) continue;  // (wave-uniform: every load is waited for at once below)
+      const int off = (k * D + d0) * 4;
+      if constexpr (DPL == 2) {
+        const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(orsrc, off, 0, kSysCoherent));
+        ov[k][0] = bits_to_f32(v[0]);
+        ov[k][1] = bits_to_f32(v[1]);
+      } else {
+        ov[k][0] = bits_to_f32(__builtin_amdgcn_raw_buffer_load_b32(orsrc, off, 0, kSysCoherent));
+      }
+    }
+    const int pl = min(lane & 7, P - 1);
+    const float m_raw = __hip_atomic_load(a.ws_m + row + pl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const float l_raw = __hip_atomic_load(a.ws_l + row + pl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const bool mine = (lane & 7) < P;
+    const float mp = mine ? m_raw : -__builtin_inff();
+    const float M = oct_max(mp);
+    const float ep = (M == -__builtin_inff() || mp == -__builtin_inff()) ? 0.0f : fast_exp2(mp - M);
+    const float L = oct_sum(mine ? l_raw * ep : 0.0f);
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    const float w = (mp == -__builtin_inff() || inv == 0.0f) ? 0.0f : ep * inv;
+    if (lane < P) a.ws_w[((size_t)b * P + lane) * a.Hq + hq0 + hh] = w;
+    float acc[4][DPL];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[k][e] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (k >= P) continue;
+      const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[k & 3][e] += ov[k][e] * wk;
+    }
+    if (lane * DPL < D) {
+      float o[DPL];
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o[e] = (acc[0][e] + acc[1][e]) + (acc[2][e] + acc[3][e]);
+      const size_t oi = (pbase + hh) * D + lane * DPL;
+      if constexpr (KV != KV_F32) {
+        if constexpr (DPL == 2) {
+          *(uint32_t*)((uint16_t*)a.out + oi) =
+              (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
+        } else {
+          ((uint16_t*)a.out)[oi] = f32_to_bf16_rne(o[0]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) ((float*)a.out)[oi + e] = o[e];
+      }
+    }
+  };
+
   // ---- the last partition of this (sequence, KV head) to finish merges the
   // group's outputs, so the output needs no further launch. Each partition,
   // once its partial is in memory, adds 1 to the pair's completion counter
@@ -1133,8 +1233,13 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   // writeback, and the merging workgroup reads them past its caches.
   // (Device-scope fences here write back the whole L2 per workgroup and
   // cost tens of microseconds per launch.)
-  // The other waves store the block records meanwhile: the completion count
-  // is per wave, so wave 0's waits for its flag do not wait for them.
+  // With at most eight partitions and no more heads than waves, wave 0
+  // counts, waves 1 .. G - 1 wait for the count in LDS, and in the last
+  // partition wave h merges head h, while waves G .. NW - 1 store the block
+  // records (with G = NW every wave stores its share after the merge: the
+  // completion count is per wave, so records stored first would be waited
+  // for with the merge's loads). Otherwise wave 0 counts and merges alone
+  // while the other waves store the records.
   if (a.pair_flag == nullptr) {
     store_side();
     if constexpr (SCORED) store_records(0, NTH);
@@ -1142,6 +1247,38 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores acknowledged
   __syncthreads();
+  if (a.nparts <= 8 && G <= NW) {
+    const int P = a.nparts;
+    if (wave >= G) {
+      store_side();
+      if constexpr (SCORED) store_records(64 * G, NTH - 64 * G);
+      return;
+    }
+    uint32_t* fl = a.pair_flag + ((size_t)b * a.Hkv + g) * P;  // word 0: the pair's counter
+    int cnt;
+    if (wave == 0) {
+      uint32_t old = 0u;
+      // system scope: performed at memory, past every XCD's L2
+      if (lane == 0) old = __hip_atomic_fetch_add(fl, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      // (non-negative even for a counter that did not start at zero)
+      cnt = __builtin_amdgcn_readfirstlane((int)min(old, 0x7FFFFFFFu));
+      if (lane == 0) __hip_atomic_store(&misc[6], cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    } else {
+      // misc[6] is -1 from entry until wave 0 has the count (a round trip)
+      while ((cnt = __hip_atomic_load(&misc[6], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) < 0)
+        __builtin_amdgcn_s_sleep(1);
+      cnt = __builtin_amdgcn_readfirstlane(cnt);
+    }
+    const bool last = cnt == P - 1;
+    if (last) merge_head(wave);
+    // every partition has counted: back to zero for the next call (after the
+    // merge's loads, which would otherwise wait for this store)
+    if (last && wave == 0 && lane == 0) __hip_atomic_store(fl, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    store_side();
+    if constexpr (SCORED)
+      if (G == NW) store_records(0, NTH);
+    return;
+  }
   if (wave != 0) {
     store_side();
     if constexpr (SCORED) store_records(64, NTH - 64);

@@ -52,6 +52,30 @@ __device__ __forceinline__ float rows_sum(float x) {
   return bits_to_f32(b[0]) + bits_to_f32(b[1]);
 }
 
+// Reductions over each group of eight consecutive lanes (l ^ 1 and l ^ 2
+// within a quad by DPP quad permutes, then lane 7 - l of the group by the
+// half-row mirror). The pairs combine in the same order in every lane up to
+// commutation, so all eight lanes of a group hold bit-identical results.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return bits_to_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)f32_bits(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror
+
+__device__ __forceinline__ float oct_max(float x) {
+  x = fmaxf(x, dpp_f32<kDppXor1>(x));
+  x = fmaxf(x, dpp_f32<kDppXor2>(x));
+  return fmaxf(x, dpp_f32<kDppHalfMirror>(x));
+}
+
+__device__ __forceinline__ float oct_sum(float x) {
+  x = x + dpp_f32<kDppXor1>(x);
+  x = x + dpp_f32<kDppXor2>(x);
+  return x + dpp_f32<kDppHalfMirror>(x);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Wave-uniform "any lane" / "all lanes" votes.
