@@ -313,7 +313,7 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   // list split point, each wave's final max and sum per head, the block-sum
   // records of every list entry (sums per sub-block and head, and the running
   // max they are relative to), the list of kept tiles and the keep bitmap.
-  // The waves' outputs are staged over the records at the end.
+  // The waves' final outputs go to an area of their own after the bitmap.
   float* side_area = lds;                               // [NW][64 quads][4]
   uint8_t* app_lds = (uint8_t*)(side_area + NW * 256);  // [2][D * eb] bytes; the scales in its last 2 floats
   int* misc = (int*)(side_area + NW * 256 + kAppRowFloats);  // [8]
@@ -989,9 +989,29 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   }
 
   // ---- end of the partition: records, then the workgroup's partial ----
-  if (hreal && kg == 0) {
-    mw[wave * 16 + h] = m_run;
-    lw[wave * 16 + h] = l_run;
+  // This wave's running max, sum and output (unscaled) per head go to LDS
+  // for the workgroup's merge; the outputs in an area of their own that no
+  // wave uses while streaming, [NW][G][DP] with rows padded by 4 floats
+  // against bank conflicts.
+  constexpr int DP = D + 4;
+  if (hreal) {
+    if (kg == 0) {
+      mw[wave * 16 + h] = m_run;
+      lw[wave * 16 + h] = l_run;
+    }
+    float* dst = ow + (wave * G + h) * DP;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int d0 = NC * (4 * kg + r);  // lane's dims d0 .. d0 + NC - 1
+      if constexpr (NC % 4 == 0) {
+#pragma unroll
+        for (int n0 = 0; n0 < NC; n0 += 4)
+          *(f32x4*)(dst + d0 + n0) = f32x4{oacc[n0][r], oacc[n0 + 1][r], oacc[n0 + 2][r], oacc[n0 + 3][r]};
+      } else {
+#pragma unroll
+        for (int n = 0; n < NC; ++n) dst[d0 + n] = oacc[n][r];
+      }
+    }
   }
   // this wave's streaming time (clock ticks, 100 MHz), stored with its tile
   // count after the handshake below, for the split of later launches
@@ -1091,59 +1111,47 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
       for (int x = tid; x < te - tb; x += nth) a.ws_pid[rec_row + tb + x] = part;
   };
 
-  // The waves' outputs merge in LDS (a slot per wave in an area of its own,
-  // rows padded by 4 floats against bank conflicts) into one partial per
-  // workgroup. Each wave first scales its output and sum to the workgroup
-  // max of its head (factor 2^(m_wave - M), 0 for a wave that read nothing:
-  // its output and sum are zero), so the merge is a plain sum over the
-  // waves in a fixed order: one batch of LDS reads per output, no waits
-  // between the waves' terms.
+  // The waves' outputs merge into one partial per workgroup, after the one
+  // barrier above: the thread of output (head hh, dim dd) scales each wave's
+  // output by 2^(m_wave - M), M the workgroup max of the head (0 for a wave
+  // that read nothing: its output and sum are zero), and adds the terms in
+  // wave order; the thread of dim 0 does the same for the sums and stores
+  // M and the sum. One batch of LDS reads per output, no further barrier.
   const size_t pbase = (size_t)b * a.Hq + hq0;  // first head of the group
   auto store_partial = [&]() {
-    constexpr int DP = D + 4;
-    // ow: [NW][G][DP]; lw becomes each wave's scaled sum
-    if (hreal) {
-      const float f = m_run == -__builtin_inff() ? 0.0f : fast_exp2(m_run - wg_max(h));
-      float* dst = ow + (wave * G + h) * DP;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int d0 = NC * (4 * kg + r);  // lane's dims d0 .. d0 + NC - 1
-        if constexpr (NC % 4 == 0) {
-#pragma unroll
-          for (int n0 = 0; n0 < NC; n0 += 4)
-            *(f32x4*)(dst + d0 + n0) =
-                f32x4{oacc[n0][r] * f, oacc[n0 + 1][r] * f, oacc[n0 + 2][r] * f, oacc[n0 + 3][r] * f};
-        } else {
-#pragma unroll
-          for (int n = 0; n < NC; ++n) dst[d0 + n] = oacc[n][r] * f;
-        }
-      }
-      if (kg == 0) lw[wave * 16 + h] = l_run * f;
-    }
-    __syncthreads();
     for (int x = threadIdx.x; x < G * D; x += NTH) {
       const int hh = x / D, dd = x % D;
-      float t[NW];
+      float mv[NW], t[NW];
 #pragma unroll
-      for (int w = 0; w < NW; ++w) t[w] = ow[(w * G + hh) * DP + dd];
+      for (int w = 0; w < NW; ++w) {
+        mv[w] = mw[w * 16 + hh];
+        t[w] = ow[(w * G + hh) * DP + dd];
+      }
+      float M = -__builtin_inff();
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, mv[w]);
+      float f[NW];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) f[w] = mv[w] == -__builtin_inff() ? 0.0f : fast_exp2(mv[w] - M);
       float o = 0.0f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) o += t[w];
+      for (int w = 0; w < NW; ++w) o += t[w] * f[w];
       // the partials go to memory past the (per-XCD, non-coherent) L2, for
       // the merge below: relaxed system-scope stores are written through
       __hip_atomic_store(&a.ws_o[((pbase + hh) * a.nparts + part) * D + dd], o, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_SYSTEM);
-    }
-    for (int hh = threadIdx.x; hh < G; hh += NTH) {
-      const float M = wg_max(hh);
-      float t[NW];
+      if (dd == 0) {
+        float lt[NW];
 #pragma unroll
-      for (int w = 0; w < NW; ++w) t[w] = lw[w * 16 + hh];
-      float l = 0.0f;
+        for (int w = 0; w < NW; ++w) lt[w] = lw[w * 16 + hh];
+        float l = 0.0f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) l += t[w];
-      __hip_atomic_store(&a.ws_m[(pbase + hh) * a.nparts + part], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      __hip_atomic_store(&a.ws_l[(pbase + hh) * a.nparts + part], l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        for (int w = 0; w < NW; ++w) l += lt[w] * f[w];
+        __hip_atomic_store(&a.ws_m[(pbase + hh) * a.nparts + part], M, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_SYSTEM);
+        __hip_atomic_store(&a.ws_l[(pbase + hh) * a.nparts + part], l, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_SYSTEM);
+      }
     }
   };
   store_partial();
