@@ -866,10 +866,8 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
           mv = fmaxf(mv, fabsf(xv[e]));
         }
       }
-      for (int off = 32; off > 0; off >>= 1) {
-        mk = fmaxf(mk, __shfl_xor(mk, off, 64));
-        mv = fmaxf(mv, __shfl_xor(mv, off, 64));
-      }
+      mk = wave_max(mk);
+      mv = wave_max(mv);
       sk = fp8_scale_of(mk);
       sv = fp8_scale_of(mv);
     }

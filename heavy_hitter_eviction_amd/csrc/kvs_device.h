@@ -63,6 +63,7 @@ __device__ __forceinline__ float dpp_f32(float x) {
 constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
 constexpr int kDppHalfMirror = 0x141;  // row_half_mirror
+constexpr int kDppRowMirror = 0x140;   // row_mirror
 
 __device__ __forceinline__ float oct_max(float x) {
   x = fmaxf(x, dpp_f32<kDppXor1>(x));
@@ -74,6 +75,15 @@ __device__ __forceinline__ float oct_sum(float x) {
   x = x + dpp_f32<kDppXor1>(x);
   x = x + dpp_f32<kDppXor2>(x);
   return x + dpp_f32<kDppHalfMirror>(x);
+}
+
+// Maximum over the whole wave, in every lane: groups of eight, then each
+// 16-lane row (lane 15 - l), then the four rows. fmaxf is exact and drops
+// NaNs in any order, so the result does not depend on the order.
+__device__ __forceinline__ float wave_max(float x) {
+  x = oct_max(x);
+  x = fmaxf(x, dpp_f32<kDppRowMirror>(x));
+  return rows_max(x);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
