@@ -147,6 +147,10 @@ __device__ __forceinline__ float merge_weight(const float* m, const float* l, in
   return (mp == -__builtin_inff() || inv == 0.0f) ? 0.0f : fast_exp2(mp - M) * inv;
 }
 
+// Largest log2 of an exponential term of the partial kernel's online
+// softmax (see the reference rule in its tile step).
+constexpr float kLazyLog2 = 8.0f;
+
 template <int KV>
 struct Pipe {
   // tile buffers per wave (depth - 1 tiles in flight); also the tiles a wave
@@ -738,7 +742,12 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
     }
     float mx = fmaxf(fmaxf(tl[0], tl[1]), fmaxf(tl[2], tl[3]));
     mx = rows_max(mx);
-    const float m_new = fmaxf(m_run, mx);
+    // The reference the exponentials are taken against moves only when the
+    // tile's max passes it by more than kLazyLog2 (or there is none yet): the
+    // terms stay at most 2^kLazyLog2, and the output and sum are rescaled
+    // rarely rather than at nearly every tile of a short range. Any
+    // reference gives the same softmax up to rounding.
+    const float m_new = mx > m_run + kLazyLog2 ? mx : m_run;
     const float alpha = fast_exp2(m_run - m_new);
     float p[4];
 #pragma unroll
