@@ -651,7 +651,26 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
     bool valid[4];
     int sub[4];
     bool all_valid, any_valid;
+    // a ring tile whose slots are all readable and of one lap (the usual
+    // case) skips the per-slot masks and sub-block split; its sub-block sums
+    // come out bit for bit as the general path's
+    int one_lap = -1;  // that lap's sub-block, or -1
     if constexpr (RING) {
+      const int pmin = min(min(cpos.x, cpos.y), min(cpos.z, cpos.w));
+      const int pmax = max(max(cpos.x, cpos.y), max(cpos.z, cpos.w));
+      if (keep_b == nullptr && wave_all(pmin >= max(lo, 0) && pmax <= i_cur)) {
+        if (wave_all(pmin >= lap_base)) one_lap = lap_i & 1;
+        else if (wave_all(pmax < lap_base)) one_lap = (lap_i - 1) & 1;
+      }
+    }
+    if (RING && one_lap >= 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        valid[r] = true;
+        sub[r] = one_lap;
+      }
+      all_valid = any_valid = true;
+    } else if constexpr (RING) {
       const int pr[4] = {cpos.x, cpos.y, cpos.z, cpos.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -755,13 +774,23 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
 
     float esub0 = 0.f, esub1 = 0.f;
     if constexpr (NSUB == 2) {
+      if (one_lap >= 0) {
+        // the same sums as below with every slot in sub-block one_lap
+        float e = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        esub0 += sub[r] ? 0.0f : p[r];
-        esub1 += sub[r] ? p[r] : 0.0f;
+        for (int r = 0; r < 4; ++r) e += p[r];
+        e = rows_sum(e);
+        esub0 = one_lap ? 0.0f : e;
+        esub1 = one_lap ? e : 0.0f;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          esub0 += sub[r] ? 0.0f : p[r];
+          esub1 += sub[r] ? p[r] : 0.0f;
+        }
+        esub0 = rows_sum(esub0);
+        esub1 = rows_sum(esub1);
       }
-      esub0 = rows_sum(esub0);
-      esub1 = rows_sum(esub1);
     } else {
       esub0 = rows_sum((p[0] + p[1]) + (p[2] + p[3]));
     }
