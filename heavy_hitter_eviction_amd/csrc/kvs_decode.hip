@@ -192,6 +192,10 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   u32x4 app_k0[2], app_v0[2];  // bf16 rows: [r] holds values 512 r + 8 lane ..; f32 rows: [0..1] values 8 lane ..
   uint32_t app_hk[XPL], app_hv[XPL];  // this head's values as stored in the row (bf16 or f32 bits)
   const bool app_wave = a.app_k != nullptr && wave == NW - 1;
+  // a ring's position: requested first (a vector load, so waiting for it
+  // waits for nothing issued later), used once the first tile loads are out
+  int ring_pos = 0;
+  if constexpr (RING) ring_pos = a.cur_pos[b];
   if (app_wave) {
     if constexpr (KV == KV_FP8) {
       if (a.app_bf16) {
@@ -249,9 +253,9 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   const bool use_rates = !RING && a.dyn && a.adapt && a.rates != nullptr;
   const float r_lane = use_rates && lane < 8 ? a.rates[lane] : 1.0f;
   // The current position. A linear cache's partition range depends on it: a
-  // vector load, waited for together with the rates. A ring's does not, so a
-  // ring reads it once its first tile loads are out, with a scalar load
-  // (a wait counter of its own, so it does not wait for those tiles).
+  // vector load, waited for together with the rates. A ring's does not: its
+  // position was requested at entry and is read once the first tile loads
+  // are out.
   int i_cur = RING ? 0 : __builtin_amdgcn_readfirstlane(a.cur_pos[b]);
   float wcls[8];
 #pragma unroll
@@ -862,15 +866,17 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
     // a scalar operand of the loads: uniform, and marked so
     return (uint32_t)__builtin_amdgcn_readfirstlane((int)(e < n_items ? (uint32_t)tile_of(e) * tile_bytes : oob));
   };
-  // ---- fused append (last wave, before its first claim) ----
+  // ---- fused append (last wave, before its first claim; a ring's row
+  // before the first barrier) ----
   // Same encoding as kvs_append_rows: the FP8 scale covers every KV head of
   // the position, so each workgroup of the sequence derives it from the whole
   // row (identical values); this workgroup writes its own head's codes.
-  auto append_row = [&]() {
+  uint32_t kbits[XPL], vbits[XPL];
+  float sk = 0.0f, sv = 0.0f;
+  auto encode_row = [&]() {
     const int n = app_n;
     const size_t rb = app_rb;
     const int sbf = a.app_bf16;
-    float sk = 0.0f, sv = 0.0f;
     if constexpr (KV == KV_FP8) {
       float mk = 0.0f, mv = 0.0f;
       for (int i = 8 * lane; i < n; i += 8 * 64) {  // 8 values per lane and load (n % 8 == 0)
@@ -914,7 +920,6 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
     // into LDS for the waves that read the tile in this call (they patch the
     // slot from there), then the flag, then the cache writes, which no wave
     // of this call waits for
-    uint32_t kbits[XPL], vbits[XPL];
 #pragma unroll
     for (int c = 0; c < XPL; ++c) {
       const int x = lane + 64 * c;
@@ -942,6 +947,8 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
       ((float*)app_lds)[kAppRowFloats - 2] = sk;
       ((float*)app_lds)[kAppRowFloats - 1] = sv;
     }
+  };
+  auto publish_row = [&]() {
     // the wave's LDS writes are done (lgkmcnt 0, no wait on memory) before
     // the flag is raised
     __builtin_amdgcn_s_waitcnt(0xC07F);
@@ -991,7 +998,7 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
 #pragma unroll
   for (int i = 0; i < NBUF - 1; ++i) load_tile<KV, D, RING>(buf[i], ad, soff_of(cur, i));
   if constexpr (RING) {
-    i_cur = scalar_load_i32(a.cur_pos + b);
+    i_cur = __builtin_amdgcn_readfirstlane(ring_pos);
     set_position();
     lap_i = i_cur / a.C;
     lap_base = lap_i * a.C;
@@ -999,10 +1006,16 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   app_slot = (app_cand_tile >= tb && app_cand_tile < te) ? app_cand : -1;
   app_tile = app_slot >= 0 ? app_cand_tile : -1;
   app_ts = app_slot & (kTile - 1);
+  // A ring's appending wave encodes the new row into LDS now, while the
+  // first tiles are on their way; it publishes it after the barrier.
+  if (RING && app_slot >= 0 && wave == NW - 1) encode_row();
   // the claim counter and the append flag are initialised (with a keep list
   // the list's barrier has seen to that)
   if (!use_list) __syncthreads();
-  if (app_slot >= 0 && wave == NW - 1) append_row();
+  if (app_slot >= 0 && wave == NW - 1) {
+    if constexpr (!RING) encode_row();
+    publish_row();
+  }
 
   int n_done = 0;  // tiles this wave processed
   if (cur < n_batches) {

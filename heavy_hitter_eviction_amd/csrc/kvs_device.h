@@ -117,14 +117,6 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
   return code | sign;
 }
 
-// A 32-bit value that every lane reads at one address, with a scalar load: it
-// completes on the scalar counter, so waiting for it does not wait for the
-// vector loads issued before it, and later vector loads do not wait for it.
-// Only for memory the kernel does not write.
-__device__ __forceinline__ int scalar_load_i32(const int32_t* p) {
-  return *(const __attribute__((address_space(4))) int32_t*)(uintptr_t)p;
-}
-
 // absmax / 240, correctly rounded (the pages' per-position scale).
 __device__ __forceinline__ float fp8_scale_of(float absmax) { return __fdiv_rn(absmax, 240.0f); }
 
