@@ -254,8 +254,9 @@ def run_gpu(args, w):
         if fused:
             # one library call for the layers (each layer's append, attention
             # and output merge in one kernel; the block sums stay in the
-            # layers' workspaces), then the step's one mass combine and the
-            # side-car with the selection
+            # layers' workspaces), then one for the step's mass combine and
+            # the side-car with the selection (without selection the side-car
+            # update runs in the combine's launch)
             if timed:
                 ev[t - args.warmup][0].record()
             dec.attend_layers(q_at[t], k_at[t], v_at[t], cur[t])
@@ -264,9 +265,9 @@ def run_gpu(args, w):
             if profiled:
                 api.tap_masses(dec.geom, dec.workspaces, cur[t], mass_accum=dec.mass, head_mass=head_mass,
                                mass_max=mass_max)
+                dec.close_turn(cur[t])
             else:
-                api.tap_masses(dec.geom, dec.workspaces, cur[t], mass_accum=dec.mass)
-            dec.close_turn(cur[t])
+                dec.finish_step(cur[t])
             continue
         for layer in range(L):
             if not fused:

@@ -34,7 +34,7 @@ EXPORTED = (
     "kvs_decode_attn_profiled",
     "kvs_reattend_blocks",
     "kvs_update_sidecar", "kvs_update_counters", "kvs_filter_blocks", "kvs_select_blocks",
-    "kvs_update_sidecar_select", "kvs_decode_step", "kvs_compact_blocks", "kvs_stream_read", "kvs_snapkv_workspace_bytes", "kvs_snapkv_scores", "kvs_status_str",
+    "kvs_update_sidecar_select", "kvs_decode_step", "kvs_close_step", "kvs_compact_blocks", "kvs_stream_read", "kvs_snapkv_workspace_bytes", "kvs_snapkv_scores", "kvs_status_str",
     "kvs_version",
 )
 
@@ -110,6 +110,7 @@ def _load():
         "kvs_stream_read": [P, SZ, P, I32, P],
         "kvs_update_sidecar_select": [P, P, P, P, P, I32, I32, I32, I64, F, I32, P, P, I32, I32, I32, P, P, P, P],
         "kvs_decode_step": [G, I32, ctypes.POINTER(LayerBufs), I32, P, P, SZ, P, ctypes.POINTER(TurnArgs), P],
+        "kvs_close_step": [G, P, I32, SZ, P, P, ctypes.POINTER(TurnArgs), P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -554,6 +555,27 @@ def decode_step(caches, q_layers, cur_pos: torch.Tensor, outs, workspaces, k_new
         targs = ctypes.byref(_turn_args(turn, g.batch, g.nb))
     _check(LIB.kvs_decode_step(ctypes.byref(g.c()), L, arr, src, _ptr(cur_pos), _ptr(keep_mask), ws_bytes,
                                _ptr(mass_accum), targs, _stream(stream)), "kvs_decode_step")
+
+
+def close_step(geom: CacheGeom, workspaces, cur_pos: torch.Tensor, mass_accum: torch.Tensor, turn: Turn,
+               stream=None):
+    """kvs_close_step: the layers' block masses (left in ``workspaces`` by a
+    layers-only decode_step or the per-layer tap calls) added into
+    ``mass_accum``, then the turn closed: the results of tap_masses followed
+    by update_sidecar(_select), the side-car update in the combine's launch
+    where it can."""
+    _device_check(cur_pos, mass_accum, *workspaces)
+    if not workspaces:
+        raise ValueError("need at least one layer workspace")
+    if cur_pos.dtype != torch.int32 or cur_pos.numel() != geom.batch:
+        raise ValueError("cur_pos must be int32 [B]")
+    if mass_accum.dtype != torch.float32 or mass_accum.numel() != geom.batch * geom.nb:
+        raise ValueError("mass_accum must be float32 [B, NBmax]")
+    ws_bytes = min(w.numel() * w.element_size() for w in workspaces)
+    arr = (ctypes.c_void_p * len(workspaces))(*[w.data_ptr() for w in workspaces])
+    targs = _turn_args(turn, geom.batch, geom.nb)
+    _check(LIB.kvs_close_step(ctypes.byref(geom.c()), arr, len(workspaces), ws_bytes, _ptr(cur_pos),
+                              _ptr(mass_accum), ctypes.byref(targs), _stream(stream)), "kvs_close_step")
 
 
 def decode_attn_profiled(cache: KVCache, q: torch.Tensor, cur_pos: torch.Tensor, out: torch.Tensor,

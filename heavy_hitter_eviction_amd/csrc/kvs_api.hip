@@ -446,6 +446,7 @@ hipError_t launch_tap(const kvs::CombineArgs& c, bool parallel, bool ring, hipSt
   return parallel ? kvs::launch_combine_layers(c, ring, s) : kvs::launch_combine(c, ring, s);
 }
 
+
 }  // namespace
 
 extern "C" {
@@ -726,6 +727,53 @@ int step_layer_setup(const kvs_geom* g, const kvs_layer_bufs& L, int32_t src_dty
   return L.k_new ? append_args(g, L.k_new, L.v_new, src_dtype, a) : KVS_OK;
 }
 
+
+// The end of a step: the layers' masses added into mass_accum, then the turn
+// (if any) closed. Without selection, and when the layer-parallel combine
+// applies, the side-car update runs in the combine's launch (the same
+// arithmetic on the same masses: bit for bit the two calls).
+struct CloseStep {
+  kvs::CombineArgs c;
+  bool parallel = false;
+  kvs::SelectArgs sa{};
+};
+
+int close_setup(const kvs_geom* g, void* const* workspaces, int32_t n_layers, size_t workspace_bytes,
+                const int32_t* cur_pos, float* mass_accum, const kvs_turn_args* turn, CloseStep* cs) {
+  int st = tap_setup(g, workspaces, n_layers, workspace_bytes, cur_pos, mass_accum, nullptr, nullptr, &cs->c,
+                     &cs->parallel);
+  if (st) return st;
+  if (!turn) return KVS_OK;
+  if (turn->select != 0 && turn->select != 1) return KVS_EINVAL;
+  if (turn->select)
+    return sidecar_select_setup(mass_accum, turn->attended, turn->ema, turn->cum, turn->traj, g->batch,
+                                g->n_blocks_max, turn->traj_cap, turn->step, turn->alpha, turn->score_source,
+                                turn->alive, cur_pos, turn->budget_blocks, turn->recent_tokens, turn->sink_tokens,
+                                turn->keep_out, turn->sel_ids, turn->n_sel, &cs->sa);
+  st = sidecar_check(mass_accum, turn->attended, turn->ema, turn->cum, turn->traj, g->batch, g->n_blocks_max,
+                     turn->traj_cap, turn->step, turn->alpha);
+  if (st) return st;
+  if (cs->parallel) {
+    kvs::CombineArgs& c = cs->c;
+    c.sc_att = turn->attended;
+    c.sc_ema = turn->ema;
+    c.sc_cum = turn->cum;
+    c.sc_traj = turn->traj;
+    c.sc_traj_cap = turn->traj_cap;
+    c.sc_slot = (int)(turn->step % turn->traj_cap);
+    c.sc_alpha = turn->alpha;
+  }
+  return KVS_OK;
+}
+
+int close_launch(const kvs_geom* g, const CloseStep& cs, const kvs_turn_args* turn, hipStream_t s) {
+  if (launch_tap(cs.c, cs.parallel, g->ring != 0, s) != hipSuccess) return KVS_EHIP;
+  if (!turn || cs.c.sc_att) return hip_status(hipGetLastError());
+  if (turn->select) return hip_status(kvs::launch_select(cs.sa, s));
+  return hip_status(kvs::launch_sidecar(cs.c.mass, turn->attended, turn->ema, turn->cum, turn->traj, g->batch,
+                                        g->n_blocks_max, turn->traj_cap, turn->step, turn->alpha, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -749,24 +797,9 @@ int kvs_decode_step(const kvs_geom* g, int32_t n_layers, const kvs_layer_bufs* l
   // without mass_accum the block sums stay in the workspaces (for a later
   // kvs_tap_masses) and there is no turn to close
   if (!mass_accum && turn) return KVS_EINVAL;
-  kvs::CombineArgs c;
-  bool parallel = false;
-  int st = mass_accum ? tap_setup(g, ws, n_layers, workspace_bytes, cur_pos, mass_accum, nullptr, nullptr, &c,
-                                  &parallel)
-                      : KVS_OK;
-  if (st) return st;
-  kvs::SelectArgs sa{};
-  if (turn) {
-    if (turn->select != 0 && turn->select != 1) return KVS_EINVAL;
-    if (turn->select) {
-      st = sidecar_select_setup(mass_accum, turn->attended, turn->ema, turn->cum, turn->traj, g->batch,
-                                g->n_blocks_max, turn->traj_cap, turn->step, turn->alpha, turn->score_source,
-                                turn->alive, cur_pos, turn->budget_blocks, turn->recent_tokens, turn->sink_tokens,
-                                turn->keep_out, turn->sel_ids, turn->n_sel, &sa);
-    } else {
-      st = sidecar_check(mass_accum, turn->attended, turn->ema, turn->cum, turn->traj, g->batch, g->n_blocks_max,
-                         turn->traj_cap, turn->step, turn->alpha);
-    }
+  CloseStep cs;
+  if (mass_accum) {
+    const int st = close_setup(g, ws, n_layers, workspace_bytes, cur_pos, mass_accum, turn, &cs);
     if (st) return st;
   }
   hipStream_t s = (hipStream_t)stream;
@@ -778,11 +811,16 @@ int kvs_decode_step(const kvs_geom* g, int32_t n_layers, const kvs_layer_bufs* l
     if (kvs::launch_partial(kv, g->head_dim, a, true, g->ring != 0, p.lds_partial, s) != hipSuccess) return KVS_EHIP;
   }
   if (!mass_accum) return KVS_OK;
-  if (launch_tap(c, parallel, g->ring != 0, s) != hipSuccess) return KVS_EHIP;
-  if (!turn) return KVS_OK;
-  if (turn->select) return hip_status(kvs::launch_select(sa, s));
-  return hip_status(kvs::launch_sidecar(mass_accum, turn->attended, turn->ema, turn->cum, turn->traj, g->batch,
-                                        g->n_blocks_max, turn->traj_cap, turn->step, turn->alpha, s));
+  return close_launch(g, cs, turn, s);
+}
+
+int kvs_close_step(const kvs_geom* g, void* const* workspaces, int32_t n_layers, size_t workspace_bytes,
+                   const int32_t* cur_pos, float* mass_accum, const kvs_turn_args* turn, void* stream) {
+  if (!mass_accum || !turn) return KVS_EINVAL;
+  CloseStep cs;
+  const int st = close_setup(g, workspaces, n_layers, workspace_bytes, cur_pos, mass_accum, turn, &cs);
+  if (st) return st;
+  return close_launch(g, cs, turn, (hipStream_t)stream);
 }
 
 }  // extern "C"

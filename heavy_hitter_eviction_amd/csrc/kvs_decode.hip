@@ -1862,6 +1862,37 @@ void kvs_combine_layers(CombineArgs a) {
   const int TG = cmb_groups(L);
   const int tpw = kCmbTiles * TG;  // tiles per workgroup
   const int n_chunks = (a.NT + tpw - 1) / tpw;
+  // The blocks [c_lo, c_hi) of sequence b that the mass workgroups reach:
+  // a linear cache's readable tiles, a ring's two laps (i / C and
+  // i / C - 1) of every tile.
+  auto reached = [&](int& c_lo, int& c_hi) {
+    const int ic = a.cur_pos[b];
+    if constexpr (RING) {
+      const int lap_i = ic / a.C;
+      c_lo = max(lap_i - 1, 0) * a.NT;
+      c_hi = (lap_i + 1) * a.NT;
+    } else {
+      c_hi = max(0, min(a.NT, ic / kTile + 1));
+      c_lo = a.window > 0 ? min(c_hi, max(ic - a.window + 1, 0) / kTile) : 0;
+    }
+    c_hi = min(c_hi, a.nbmax);
+    c_lo = min(c_lo, c_hi);
+  };
+  if ((int)blockIdx.x >= n_chunks + L) {
+    // ---- side-car columns: the turn's update of the blocks the mass
+    // workgroups do not reach (their masses are this turn's as they stand)
+    if (a.sc_att == nullptr) return;
+    int c_lo, c_hi;
+    reached(c_lo, c_hi);
+    const int col = blockIdx.x - n_chunks - L;
+    for (int blk = col * NTH + tid; blk < a.nbmax; blk += kCmbSidecarCols * NTH) {
+      if (blk >= c_lo && blk < c_hi) continue;
+      const size_t x = (size_t)b * a.nbmax + blk;
+      sidecar_block(a.mass, a.sc_att, a.sc_ema, a.sc_cum, a.sc_traj, x, b, blk, a.nbmax, a.sc_traj_cap,
+                    a.sc_slot, a.sc_alpha, a.mass[x]);
+    }
+    return;
+  }
   if ((int)blockIdx.x >= n_chunks) {
     // rates: the same per-layer refresh as in kvs_combine
     const int l = blockIdx.x - n_chunks;
@@ -2085,7 +2116,11 @@ void kvs_combine_layers(CombineArgs a) {
       mass_run = mass_run + cl[((tl * L + l) * NSUB + sb) * 2];
       max_run = fmaxf(max_run, cl[((tl * L + l) * NSUB + sb) * 2 + 1]);
     }
-    if (a.mass != nullptr) a.mass[mi] = mass_run;
+    if (a.sc_att != nullptr)  // the turn's side-car update with this mass
+      sidecar_block(a.mass, a.sc_att, a.sc_ema, a.sc_cum, a.sc_traj, mi, b, blk, a.nbmax, a.sc_traj_cap,
+                    a.sc_slot, a.sc_alpha, mass_run);
+    else if (a.mass != nullptr)
+      a.mass[mi] = mass_run;
     if (a.mass_max != nullptr) a.mass_max[mi] = max_run;
   }
 }
@@ -2099,7 +2134,7 @@ hipError_t launch_combine_layers(const CombineArgs& a, bool ring, hipStream_t st
   if (!(a.mass || a.mass_max)) return hipSuccess;
   const int tpw = kCmbTiles * cmb_groups(a.n_layers);
   const int n_chunks = (a.NT + tpw - 1) / tpw;
-  dim3 grid(n_chunks + a.n_layers, a.B), block(64 * kCmbWaves);
+  dim3 grid(n_chunks + a.n_layers + (a.sc_att ? kCmbSidecarCols : 0), a.B), block(64 * kCmbWaves);
   size_t lds = combine_layers_lds_bytes(a.Hq, a.Hkv, a.nparts, a.n_layers, ring);
   if (lds < 16 * sizeof(float)) lds = 16 * sizeof(float);
   // four heads of a group per 16-byte record load when the group size allows

@@ -77,7 +77,31 @@ struct CombineArgs {
   float* head_mass;  // [B][Hq][nbmax] per-head block masses (+=), or NULL
   float* mass_max;   // [B][nbmax] running max over heads (and calls), or NULL
   int B, Hq, Hkv, C, NT, nbmax, tpp, nparts, n_mass_chunks, window;
+  // the turn's side-car update in the same launch (kvs_combine_layers only;
+  // sc_att NULL: none): the arrays of kvs_update_sidecar, the trajectory
+  // slot and the EMA weight
+  float *sc_att, *sc_ema, *sc_cum, *sc_traj;
+  int sc_traj_cap, sc_slot;
+  float sc_alpha;
 };
+
+// Side-car columns of the layer combine (sweeping the blocks its tiles do
+// not reach), per sequence.
+constexpr int kCmbSidecarCols = 4;
+
+// One block's side-car update, the arithmetic of kvs_update_sidecar: with A
+// the turn's mass of block blk of sequence b (x = b * nbmax + blk),
+// attended = A, ema = alpha A + (1 - alpha) ema, cum += A, the trajectory
+// slot = A, and the mass back to zero.
+__device__ __forceinline__ void sidecar_block(float* mass, float* att, float* ema, float* cum, float* traj,
+                                              size_t x, int b, int blk, int nbmax, int traj_cap, int slot,
+                                              float alpha, float A) {
+  att[x] = A;
+  ema[x] = alpha * A + (1.0f - alpha) * ema[x];
+  cum[x] = cum[x] + A;
+  if (traj) traj[((size_t)b * traj_cap + slot) * nbmax + blk] = A;
+  mass[x] = 0.0f;
+}
 
 // LDS floats one layer's combine tables take: the per (partition, head)
 // record weights. A combine workgroup also needs 16 floats for rates.

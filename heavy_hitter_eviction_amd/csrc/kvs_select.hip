@@ -22,15 +22,8 @@ __global__ __launch_bounds__(256) void kvs_sidecar(float* mass, float* att, floa
                                                     int slot, float alpha) {
   const size_t n = (size_t)B * nbmax;
   for (size_t x = (size_t)blockIdx.x * 256 + threadIdx.x; x < n; x += (size_t)gridDim.x * 256) {
-    const float A = mass[x];
-    att[x] = A;
-    ema[x] = alpha * A + (1.0f - alpha) * ema[x];
-    cum[x] = cum[x] + A;
-    if (traj) {
-      const size_t b = x / nbmax, blk = x - b * nbmax;
-      traj[(b * traj_cap + slot) * nbmax + blk] = A;
-    }
-    mass[x] = 0.0f;
+    const size_t b = x / nbmax, blk = x - b * nbmax;
+    sidecar_block(mass, att, ema, cum, traj, x, (int)b, (int)blk, nbmax, traj_cap, slot, alpha, mass[x]);
   }
 }
 

@@ -97,13 +97,12 @@ class ScoredDecoder:
             return
         for l in range(self.n_layers):
             self.append_attend_layer(l, q_layers[l], k_layers[l], v_layers[l], cur_pos)
-        self.finish_masses(cur_pos)
-        self.close_turn(cur_pos)
+        self._finish(cur_pos)
 
     def attend_layers(self, q_layers, k_layers, v_layers, cur_pos: torch.Tensor):
         """Fused tap mode: every layer's append and scored attention in one
         library call, the block sums left in the layers' workspaces; the step
-        goes on with ``finish_masses`` and ``close_turn``."""
+        goes on with ``finish_step``."""
         if not (self.fused and self.tap):
             raise RuntimeError("attend_layers needs fused tap mode")
         api.decode_step(self.caches, q_layers, cur_pos, self.out, self.workspaces, k_new=k_layers,
@@ -145,15 +144,13 @@ class ScoredDecoder:
                     for l in range(self.n_layers):
                         self.append_attend_layer(l, q_layers[l], k_layers[l], v_layers[l], cur_pos)
                 if not split:
-                    self.finish_masses(cur_pos)
-                    self.close_turn(cur_pos)
+                    self._finish(cur_pos)
             graphs.append(g)
             if split:
                 self.step_index = idx
                 g2 = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g2):
-                    self.finish_masses(cur_pos)
-                    self.close_turn(cur_pos)
+                    self._finish(cur_pos)
                 graphs.append(g2)
         finally:
             self.step_index = keep_idx
@@ -163,6 +160,15 @@ class ScoredDecoder:
         """Tap mode: add every layer's block masses into ``mass`` (one call)."""
         if self.tap:
             api.tap_masses(self.geom, self.workspaces, cur_pos, mass_accum=self.mass)
+
+    def finish_step(self, cur_pos: torch.Tensor):
+        """Tap mode: ``finish_masses`` then ``close_turn`` as one library call
+        (kvs_close_step: without selection the side-car update runs in the
+        mass combine's launch)."""
+        if not self.tap:
+            raise RuntimeError("finish_step needs tap mode")
+        api.close_step(self.geom, self.workspaces, cur_pos, self.mass, self.turn_args())
+        self.step_index += 1
 
     def append_attend_layer(self, layer: int, q, k_rows, v_rows, cur_pos: torch.Tensor,
                             keep: torch.Tensor | None = None, use_own_keep: bool = True):
@@ -216,6 +222,13 @@ class ScoredDecoder:
         self.keep.fill_(-1)                      # every block of the compacted cache is alive
         # the current block is always kept last: same offset inside it
         self.pos = ((self.n_sel - 1) * 16 + cur % 16 + 1).to(torch.int32)
+
+    def _finish(self, cur_pos: torch.Tensor):
+        if self.tap:
+            self.finish_step(cur_pos)
+        else:
+            self.finish_masses(cur_pos)
+            self.close_turn(cur_pos)
 
     def close_turn(self, cur_pos: torch.Tensor):
         if self.w.select:

@@ -664,6 +664,26 @@ KVS_API int kvs_decode_step(const kvs_geom* geom, int32_t n_layers, const kvs_la
                             void* stream);
 
 /*
+ * kvs_close_step -- the end of a step whose layers ran without mass_accum
+ * (kvs_decode_step with mass_accum NULL, or the per-layer _tap calls): the
+ * layers' block masses added into mass_accum, then the turn closed, with
+ * every result exactly that of
+ *   kvs_tap_masses(geom, workspaces, n_layers, workspace_bytes, cur_pos,
+ *                  mass_accum, NULL, NULL, stream)
+ *   kvs_update_sidecar_select(...) when turn->select is 1, else
+ *   kvs_update_sidecar(mass_accum, turn->attended, ...)
+ * (Context views at marginal cost, section 2: the side-car is updated once
+ * per turn from the summed masses). Without selection the side-car update
+ * runs in the mass combine's launch when the combine sums the layers in
+ * parallel (every layer's merge tables fit its LDS), else in a launch of its
+ * own. Arguments as in the calls above; turn is a HOST pointer, not NULL.
+ * Errors: those of the calls above, checked before the first launch.
+ */
+KVS_API int kvs_close_step(const kvs_geom* geom, void* const* workspaces, int32_t n_layers,
+                           size_t workspace_bytes, const int32_t* cur_pos, float* mass_accum,
+                           const kvs_turn_args* turn, void* stream);
+
+/*
  * kvs_stream_read -- a measurement helper, not part of the decode step: the
  * streaming-read ceiling that the decode kernel's KV scan is compared with
  * (Context views at marginal cost, section 7, Fact 3: the read of the cached

@@ -7,7 +7,8 @@ agree bit for bit after each step, on linear, windowed, keep-masked
 (evict-mode feedback: the keep words the selection writes are read by the
 next step) and ring caches, with and without the selection, and in the
 layers-only form (masses left in the workspaces for a separate
-kvs_tap_masses). The per-layer calls are checked against the float64 oracle
+kvs_tap_masses, or closed by kvs_close_step, whose side-car update without
+selection runs in the mass combine's launch). The per-layer calls are checked against the float64 oracle
 by the other parity tests, and the workload tests run the session, which
 takes this call, against the oracle too."""
 
@@ -32,7 +33,8 @@ def api():
 
 
 # a FUSED_CASES entry, the layer count, the turn ("select", "sidecar",
-# "layers": masses added by a separate tap_masses, no turn), appended rows
+# "layers": masses added by a separate tap_masses, no turn; "close-...": a
+# layers-only step closed by kvs_close_step), appended rows
 STEP_CASES = [
     (FUSED_CASES[0], 3, "select", True),
     (FUSED_CASES[1], 2, "sidecar", True),
@@ -43,6 +45,12 @@ STEP_CASES = [
     (FUSED_CASES[6], 3, "sidecar", True),    # FP8 ring
     (FUSED_CASES[7], 2, "select", True),     # bf16 ring with a window
     (FUSED_CASES[8], 2, "layers", True),
+    # layers-only step, then kvs_close_step (the side-car in the combine's
+    # launch without selection)
+    (FUSED_CASES[1], 2, "close-sidecar", True),
+    (FUSED_CASES[6], 3, "close-sidecar", True),  # FP8 ring
+    (FUSED_CASES[7], 2, "close-sidecar", True),  # bf16 ring with a window
+    (FUSED_CASES[2], 2, "close-select", True),   # keep words fed back every step
 ]
 STEPS = 5
 
@@ -96,23 +104,27 @@ def test_decode_step_equals_the_calls_it_stands_for(api, case):
             else:
                 api.decode_attn_tap(ref[l], qs[l], cur, o_r[l], ws_r[l], keep_mask=sr.keep if evict else None)
         api.tap_masses(geom, ws_r, cur, mass_accum=sr.mass)
-        if mode == "select":
+        if mode in ("select", "close-select"):
             api.update_sidecar_select(sr.mass, sr.att, sr.ema, sr.cum, sr.traj, t, 0.5, cur, budget, recent, sinks,
                                       alive=sr.keep if evict else None, keep_mask=sr.keep, sel_ids=sr.sel,
                                       n_sel=sr.n_sel)
-        elif mode == "sidecar":
+        elif mode in ("sidecar", "close-sidecar"):
             api.update_sidecar(sr.mass, sr.att, sr.ema, sr.cum, sr.traj, t, 0.5)
         # the one call (two in the layers-only form)
         turn = None
         if mode != "layers":
-            turn = api.Turn(ss.att, ss.ema, ss.cum, ss.traj, step=t, alpha=0.5, select=mode == "select",
-                            budget_blocks=budget, recent_tokens=recent, sink_tokens=sinks,
-                            alive=ss.keep if evict else None, keep_out=ss.keep, sel_ids=ss.sel, n_sel=ss.n_sel)
+            turn = api.Turn(ss.att, ss.ema, ss.cum, ss.traj, step=t, alpha=0.5,
+                            select=mode in ("select", "close-select"), budget_blocks=budget,
+                            recent_tokens=recent, sink_tokens=sinks, alive=ss.keep if evict else None,
+                            keep_out=ss.keep, sel_ids=ss.sel, n_sel=ss.n_sel)
+        layers_only = mode == "layers" or mode.startswith("close")
         api.decode_step(stp, qs, cur, o_s, ws_s, k_new=[krow] * L if append else None,
                         v_new=[vrow] * L if append else None, keep_mask=ss.keep if evict else None,
-                        mass_accum=None if mode == "layers" else ss.mass, turn=turn)
+                        mass_accum=None if layers_only else ss.mass, turn=None if layers_only else turn)
         if mode == "layers":
             api.tap_masses(geom, ws_s, cur, mass_accum=ss.mass)
+        elif mode.startswith("close"):
+            api.close_step(geom, ws_s, cur, ss.mass, turn)
         torch.cuda.synchronize()
         iv = torch.int16 if kv != "f32" else torch.int32
         for l in range(L):
