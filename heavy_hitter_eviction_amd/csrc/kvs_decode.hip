@@ -490,29 +490,27 @@ __global__ __launch_bounds__(64 * kPartialWaves, 1) void kvs_partial(PartialArgs
   float qf[QN];
   bf16x8 qb[D / 32 > 0 ? D / 32 : 1];
   auto convert_q = [&]() {
+    if constexpr (KV == KV_F32) {
 #pragma unroll
-    for (int r = 0; r < QN / EPC; ++r) {
+      for (int r = 0; r < QN / EPC; ++r) {
 #pragma unroll
-      for (int c = 0; c < QRUN; ++c) {
-        const u32x4 w = qraw[r][c];
+        for (int c = 0; c < QRUN; ++c) {
+          const u32x4 w = qraw[r][c];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if constexpr (QE == 4) {
-            qf[r * EPC + 4 * c + e] = bits_to_f32(w[e]);
-          } else {
-            qf[r * EPC + 8 * c + 2 * e] = bf16_lo(w[e]);
-            qf[r * EPC + 8 * c + 2 * e + 1] = bf16_hi(w[e]);
-          }
+          for (int e = 0; e < 4; ++e) qf[r * EPC + 4 * c + e] = hreal ? bits_to_f32(w[e]) : 0.0f;
         }
       }
-    }
+    } else {
+      // the B operand of MFMA c is the lane's bf16 values 8 c .. 8 c + 7,
+      // which are one 16-byte run as loaded (zeros for padding heads)
 #pragma unroll
-    for (int t = 0; t < QN; ++t) qf[t] = hreal ? qf[t] : 0.0f;
-    if constexpr (KV != KV_F32) {
+      for (int c = 0; c < D / 32; ++c) {
+        const u32x4 w = qraw[(8 * c) / EPC][((8 * c) % EPC) / 8];
+        u32x4 m;
 #pragma unroll
-      for (int c = 0; c < D / 32; ++c)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qb[c][e] = (__bf16)qf[8 * c + e];  // exact: Q is bf16
+        for (int e = 0; e < 4; ++e) m[e] = hreal ? w[e] : 0u;
+        qb[c] = __builtin_bit_cast(bf16x8, m);
+      }
     }
   };
 
