@@ -665,7 +665,7 @@ def oracle_baseline(w, seed, seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     root = os.path.dirname(os.path.abspath(__file__))

@@ -42,7 +42,7 @@ typedef enum {
   KVS_EALIGN = -3,   /* a pointer is not 16-byte aligned                       */
   KVS_EWS = -4,      /* workspace smaller than kvs_decode_workspace_bytes      */
   KVS_EHIP = -5,     /* the HIP runtime refused a launch                       */
-  KVS_ENOTIMPL = -6, /* a combination this build does not provide              */
+  KVS_ENOTIMPL = -6, /* a combination the library does not provide             */
   KVS_ESCRATCH = -7  /* geometry needs more than KVS_NOALLOC_SCRATCH_BYTES     */
 } kvs_status;
 
