@@ -652,9 +652,10 @@ def test_filter_blocks_matches_oracle_exactly(api):
 
 
 # (seed, blocks per sequence or None for a random 40..2999): the wider ones
-# take 8 and 16 keys per thread, and past 16384 blocks the memory-reading kernel
+# take 4, 6, 9, 12 and 16 keys per thread (each instantiated slice count, at
+# and just past the edges), and past 16384 blocks the memory-reading kernel
 SELECT_CASES = [(s, None) for s in range(6)] + [(6, 8193), (7, 16384), (8, 16385), (9, 40000)] + \
-    [(s, None) for s in range(10, 20)]
+    [(s, None) for s in range(10, 20)] + [(20, 3073), (21, 4096), (22, 6144), (23, 9216), (24, 9217), (25, 12288)]
 
 
 @pytest.mark.parametrize("seed,nb_fixed", SELECT_CASES)
@@ -671,7 +672,7 @@ def test_select_matches_oracle_exactly(api, seed, nb_fixed):
         score = (np.round(rng.random((B, nb)) * 50) / 50).astype(np.float32)   # many exact ties
     cur = rng.integers(0, nb * 16, B).astype(np.int32)
     budget, recent, sinks = int(rng.integers(0, 200)), int(rng.integers(1, 900)), int(rng.integers(0, 40))
-    if seed >= 16:
+    if 16 <= seed < 20:
         budget = nb + 5  # more than the candidates: every alive block is kept
     alive = rng.random((B, nb)) < 0.7 if seed % 2 else None
     alive_t = None
@@ -696,6 +697,26 @@ def test_select_matches_oracle_exactly(api, seed, nb_fixed):
         assert np.array_equal(bits, mask)
 
 
+@pytest.mark.parametrize("nb", [64, 3000, 9000])
+def test_select_all_scores_equal(api, nb):
+    """Every existing block has the same score: no digit separates them, so
+    the budget takes the lowest block indices among the candidates."""
+    B = 2
+    score = np.full((B, nb), 0.375, dtype=np.float32)
+    cur = np.array([nb * 16 - 1, nb * 8], dtype=np.int32)
+    budget, recent, sinks = nb // 5, 100, 16
+    keep, ids, n = api.select_blocks(gs.to_dev(score), gs.to_dev(cur), budget, recent, sinks)
+    torch.cuda.synchronize()
+    keep, ids, n = keep.cpu().numpy(), ids.cpu().numpy(), n.cpu().numpy()
+    for b in range(B):
+        i = int(cur[b])
+        ref = orc.select_blocks(score[b], None, i, budget, recent, sinks)
+        assert n[b] == len(ref)
+        assert np.array_equal(ids[b, :n[b]], ref)
+        bits = np.array([(int(keep[b, x >> 5]) >> (x & 31)) & 1 for x in range(nb)], dtype=bool)
+        assert np.array_equal(bits, orc.keep_mask_after(ref, i, nb))
+
+
 def test_select_ties_lowest_index(api):
     score = np.zeros((1, 64), dtype=np.float32)
     score[0, [3, 9, 20, 33]] = 2.0
@@ -706,6 +727,7 @@ def test_select_ties_lowest_index(api):
 
 @pytest.mark.parametrize("nb,score,evict", [(300, "cumulative", False), (8193, "cumulative", True),
                                             (2049, "ema", False), (700, "attended", True),
+                                            (4000, "ema", True), (11000, "cumulative", False),
                                             (20000, "cumulative", True)])
 def test_sidecar_select_equals_the_two_calls(api, nb, score, evict):
     """kvs_update_sidecar_select against kvs_update_sidecar then
