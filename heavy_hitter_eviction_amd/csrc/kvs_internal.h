@@ -211,6 +211,7 @@ struct SnapArgs {
   float* token_score;        // [B][Hq][C]
   float* block_score;        // [B][nbmax] (+=) or NULL
   int B, Hq, Hkv, G, C, NT, nbmax, W, tpp, nparts, pool;
+  int nparts0;               // the first pass's partitions (what the second pass merges)
   float scale_log2;
 };
 hipError_t launch_snap(int kv, int d, const SnapArgs& a, hipStream_t st);

@@ -12,7 +12,8 @@
 //   pass 0 (kvs_snap_pass<.., 0>; for FP8 keys kvs_snap_pass0_f8): per
 //     partition of tiles, each column's reference M and sum of 2^(s - M)
 //     (S^T = K Q^T on MFMA);
-//   kvs_snap_merge: per-column M and L over the partitions;
+//   kvs_snap_merge: per-column M and L over the partitions (with at most
+//     8 partitions, the second pass merges them itself);
 //   kvs_snap_pass<.., 1>: p = 2^(s - M) / L, summed over the window's queries
 //     per (token, head): token_score[b][h][token];
 //   kvs_snap_pool: per head, max over tokens j-R .. j+R (R = kernel/2) inside
@@ -40,6 +41,9 @@ __device__ __forceinline__ int snap_dim(int t, int kg) {  // as the decode kerne
 }
 
 constexpr int kSnapMaxCB = 8;  // column blocks of 16 (W*G <= 128)
+// Up to this many first-pass partitions the second pass merges their column
+// statistics itself; past it kvs_snap_merge does, once per column.
+constexpr int kSnapFoldParts = 8;
 
 // Sum of 16 values as a balanced tree (independent adds, short dependency chains).
 __device__ __forceinline__ float tree_sum16(const float* x) {
@@ -94,8 +98,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   if constexpr (PASS == 1) {
     if (tid < NCOL) {
       const size_t ci = ((size_t)b * a.Hkv + g) * NCOL + tid;
-      const float L = a.col_l[ci];
-      if (L > 0.0f) ml_in = f32x2{a.col_m[ci], 1.0f / L};
+      float M, L;
+      if (a.nparts0 <= kSnapFoldParts) {
+        // few first-pass partitions: their (reference, sum) pairs are merged
+        // here, in kvs_snap_merge's arithmetic and order, instead of by a
+        // launch of their own
+        const float* pm = a.part_ml + ci * a.nparts0 * 2;
+        float pmv[2 * kSnapFoldParts];
+#pragma unroll
+        for (int q = 0; q < kSnapFoldParts; ++q)
+          if (q < a.nparts0) {
+            pmv[2 * q] = pm[2 * q];
+            pmv[2 * q + 1] = pm[2 * q + 1];
+          }
+        M = -__builtin_inff();
+#pragma unroll
+        for (int q = 0; q < kSnapFoldParts; ++q)
+          if (q < a.nparts0) M = fmaxf(M, pmv[2 * q]);
+        L = 0.0f;
+        if (M != -__builtin_inff()) {
+#pragma unroll
+          for (int q = 0; q < kSnapFoldParts; ++q)
+            if (q < a.nparts0) L += pmv[2 * q + 1] * fast_exp2(pmv[2 * q] - M);
+        }
+      } else {
+        M = a.col_m[ci];
+        L = a.col_l[ci];
+      }
+      if (L > 0.0f) ml_in = f32x2{M, 1.0f / L};
     }
   }
   if constexpr (F8) {
@@ -858,11 +888,14 @@ static hipError_t launch_snap_t(const SnapArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((kvs_snap_pass<KV, D, 0>), dim3(a.nparts, a.Hkv, a.B), dim3(256), lds16, st, a);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(kvs_snap_merge, dim3((a.Hkv * ncol + 255) / 256, a.B), dim3(256), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.nparts > kSnapFoldParts) {
+    hipLaunchKernelGGL(kvs_snap_merge, dim3((a.Hkv * ncol + 255) / 256, a.B), dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   // pass 1 (16x16 kernel, four waves per SIMD) takes its own partition of the
   // tiles: about 1024 workgroups
   SnapArgs a1 = a;
+  a1.nparts0 = a.nparts;
   const int pairs = a.B * a.Hkv;
   const int pt = max(1, (1024 + pairs - 1) / pairs);
   a1.tpp = max(1, (a.NT + pt - 1) / pt);

@@ -537,6 +537,9 @@ SNAP_CASES = [
     ("fp8", 128, 16, 4, 1040, 5, (1040, 3), 9),    # 20 columns; a prompt shorter than the window
     ("fp8", 64, 8, 4, 656, 24, (650, 97), 5),      # 48 columns, d 64
     ("fp8", 128, 8, 8, 528, 3, (528, 1), 3),       # G = 1: 3 columns; a one-token prompt
+    # at most 8 first-pass partitions: the second pass merges the column statistics itself
+    ("fp8", 128, 32, 8, 128, 32, (128, 50), 7),
+    ("bf16", 64, 16, 4, 112, 8, (100, 5), 5),
 ]
 
 
